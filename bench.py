@@ -1,0 +1,219 @@
+"""Benchmark of the QJL KV-cache hot path on one MI355X.
+
+One step = the serving step of one layer: quantize the newly generated token's key (1-bit JL sketch
++ fp16 norms + outlier sketch) and value (token-wise 2-bit) of every sequence into slot N-1 of the
+cache, then decode attention of every query head over all N cached tokens (query projection,
+estimator scores, online softmax, value aggregation, split merge).  The cache of the first N-1
+tokens is built by the library's own prefill quantization before timing; inputs are resident in HBM.
+
+Prints ONE JSON line.  value = keys scored per second = B * Hq * N / step time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import seeded_inputs as si  # noqa: E402
+
+METRIC = "decode keys scored/sec (QJL attention) + % of MI355X HBM peak; quantize tok/s"
+HBM_PEAK_GBS = 8000.0              # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0     # MI355X dense bf16
+BYTES_PER_TOKEN_HEAD = 104          # 64 B signs + 4 B norms + 32 B codes + 4 B (min, step)
+DECODE_SOURCE = os.path.join(ROOT, "bit_kv_cache_qjl_amd", "csrc", "qjl_decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama2_7b_traffic.json")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(bytes_alg: float):
+    """HBM bytes per decode launch from committed rocprofv3 counters, if they match this source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("decode_source_sha256_16") != source_hash(DECODE_SOURCE):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w: si.Workload, budget_s: float) -> dict:
+    """The oracle, as it stands, on a bounded sample of the same workload: whole (sequence, KV head)
+    units (quantize their keys and values, then decode every query head of the unit), until the
+    time budget is spent."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
+    except Exception:  # pragma: no cover
+        threads = 1
+    oidx = si.outlier_channels(w)
+    S_in, S_out = si.jl_matrices(w)
+    Q = si.queries(w)
+    g = w.g
+    done_units = 0
+    t_start = time.perf_counter()
+    units = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
+    for b, h in units:
+        k = si.key_slice(w, b, h, oidx)
+        v = si.value_slice(w, b, h)
+        kq = oracle.quantize_key_vectors(k, S_in, S_out, oidx[h])
+        codes, meta = oracle.quantize_value_vectors(v, w.nbits)
+        vhat = oracle.dequantize_value_vectors(codes, meta)
+        for i in range(g):
+            sq_in, sq_out = oracle.project_query(Q[b, h * g + i], S_in, S_out, oidx[h])
+            s = oracle.estimator_scores(sq_in, sq_out, kq["bits"], kq["norms"])
+            oracle.attend(s, vhat, 1.0 / math.sqrt(w.d))
+        done_units += 1
+        if time.perf_counter() - t_start >= budget_s and done_units >= 2:
+            break
+    elapsed = time.perf_counter() - t_start
+    keys = done_units * g * w.N
+    return {"value": keys / elapsed, "unit": "keys/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done_units} of {w.B * w.Hkv} (sequence, KV head) units of {w.name} "
+                      f"(key + value quantization and decode of all {g} query heads over N={w.N}), "
+                      f"{elapsed:.1f} s"}
+
+
+def bench_quantize(qjl, torch, steps: int) -> dict:
+    """Prefill key-quantize stream: 65536 tokens x 8 KV heads, m = m_out = 512."""
+    w = si.WORKLOADS["prefill_quantize_64k"]
+    oidx = si.outlier_channels(w)
+    S_in, S_out = si.jl_matrices(w)
+    K = torch.from_numpy(si.keys(w, oidx)).cuda().to(torch.bfloat16)
+    Si = torch.from_numpy(S_in).cuda().to(torch.bfloat16)
+    So = torch.from_numpy(S_out).cuda().to(torch.bfloat16)
+    od = torch.from_numpy(oidx).cuda()
+    cache = qjl.alloc_cache(w.B, w.Hkv, w.N, w.m, w.m_out, w.nbits)
+    for _ in range(3):
+        qjl.quantize_keys(K, Si, So, od, cache.bits, cache.norms)
+    torch.cuda.synchronize()
+    qjl.timer_enable(True)
+    qjl.timer_read("quantize_keys")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        qjl.quantize_keys(K, Si, So, od, cache.bits, cache.norms)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    n, ms = qjl.timer_read("quantize_keys")
+    qjl.timer_enable(False)
+    kern_s = ms / 1e3 / max(n, 1)
+    tokens = w.B * w.N
+    flops = 2.0 * w.d * w.m * tokens * w.Hkv          # inlier (d - n_out) m + outlier n_out m_out = d m MACs
+    return {"workload": f"{w.name}: B={w.B} T={w.N} Hkv={w.Hkv} d={w.d} m=m_out={w.m} n_out={w.n_out}",
+            "tok_per_s": tokens / kern_s, "key_vectors_per_s": tokens * w.Hkv / kern_s,
+            "kernel_ms": kern_s * 1e3, "wall_ms_per_call": wall * 1e3,
+            "mfma": {"bound": "mfma", "achieved": flops / kern_s / 1e12, "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": flops / kern_s / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                     "flops_per_launch": flops}}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama2_7b_decode",
+                    choices=["llama2_7b_decode", "llama3_8b_gqa_decode", "llama31_70b_gqa_decode"])
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0 = skip)")
+    ap.add_argument("--no-quantize", action="store_true", help="skip the prefill quantize measurement")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "sharding across GPUs is described in the design notes but not built", file=sys.stderr)
+        return 2
+
+    import torch
+    import bit_kv_cache_qjl_amd as qjl
+
+    w = si.WORKLOADS[args.workload]
+    N = w.N
+    log(f"bench: {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={N}; generating inputs")
+    oidx = si.outlier_channels(w)
+    S_in_np, S_out_np = si.jl_matrices(w)
+    K = torch.from_numpy(si.keys(w, oidx)).cuda().to(torch.bfloat16)
+    V = torch.from_numpy(si.values(w)).cuda().to(torch.bfloat16)
+    Q = torch.from_numpy(si.queries(w)).cuda().to(torch.bfloat16)
+    S_in = torch.from_numpy(S_in_np).cuda().to(torch.bfloat16)
+    S_out = torch.from_numpy(S_out_np).cuda().to(torch.bfloat16)
+    od = torch.from_numpy(oidx).cuda()
+    cache = qjl.alloc_cache(w.B, w.Hkv, N, w.m, w.m_out, w.nbits)
+    qjl.quantize_keys(K[:, : N - 1], S_in, S_out, od, cache.bits, cache.norms, t0=0)
+    qjl.quantize_values(V[:, : N - 1], w.nbits, cache.codes, cache.meta, t0=0)
+    k_new, v_new = K[:, N - 1:], V[:, N - 1:]
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(qjl.decode_workspace_size(w.B, w.Hq, w.Hkv, N, w.m, w.m_out), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        qjl.quantize_keys(k_new, S_in, S_out, od, cache.bits, cache.norms, t0=N - 1)
+        qjl.quantize_values(v_new, w.nbits, cache.codes, cache.meta, t0=N - 1)
+        qjl.decode_attention(Q, S_in, S_out, od, cache.bits, cache.norms, N, out, codes=cache.codes,
+                             meta=cache.meta, nbits=w.nbits, workspace=ws)
+
+    log(f"bench: warmup {args.warmup}, timed {args.steps}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    qjl.timer_enable(True)
+    for k in ("decode", "quantize_keys", "quantize_values", "query_project", "combine"):
+        qjl.timer_read(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernels = {k: qjl.timer_read(k) for k in ("decode", "quantize_keys", "quantize_values", "query_project", "combine")}
+    qjl.timer_enable(False)
+    ms_per_step = elapsed / args.steps * 1e3
+    keys_scored = w.B * w.Hq * N
+    value = keys_scored / (ms_per_step / 1e3)
+    n_dec, ms_dec = kernels["decode"]
+    dec_s = ms_dec / 1e3 / max(n_dec, 1)
+    bytes_alg = float(BYTES_PER_TOKEN_HEAD) * w.B * w.Hkv * N
+    achieved = bytes_alg / dec_s / 1e9
+    log("bench: kernel ms/launch " + ", ".join(f"{k}={v[1] / max(v[0], 1):.4f}" for k, v in kernels.items()))
+
+    result = {
+        "metric": METRIC, "value": value, "unit": "keys/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "N": N, "m": w.m,
+                   "m_out": w.m_out, "n_out": w.n_out, "outlier_scale": w.outlier_scale, "value_bits": w.nbits,
+                   "step": "append 1 token per sequence (key sketch + value codes) + decode attention over N"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(bytes_alg),
+                     "kernel": "decode", "kernel_ms": dec_s * 1e3, "algorithmic_bytes": bytes_alg},
+        "kernel_ms_per_launch": {k: v[1] / max(v[0], 1) for k, v in kernels.items()},
+    }
+    if not args.no_quantize:
+        log("bench: prefill quantize stream")
+        del K, V
+        torch.cuda.empty_cache()
+        result["quantize"] = bench_quantize(qjl, torch, max(5, args.steps // 2))
+    if args.cpu_budget > 0:
+        log(f"bench: oracle on the host (~{args.cpu_budget:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

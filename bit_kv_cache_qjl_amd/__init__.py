@@ -1,0 +1,184 @@
+"""Python binding of libqjl (1-bit QJL KV-cache keys on MI355X).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of libqjl.so, reached
+through its C ABI (include/qjl.h).  PyTorch supplies device memory and the current stream.  The
+library must be built first (python -m bit_kv_cache_qjl_amd.build); importing this package without
+it raises, and there is no other implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqjl.so")
+
+QJL_OK = 0
+QJL_ERR_INVALID_ARG = -1
+QJL_ERR_UNSUPPORTED = -2
+QJL_ERR_MISALIGNED = -3
+QJL_ERR_WORKSPACE = -4
+QJL_ERR_HIP = -5
+QJL_BF16 = 0
+QJL_F32 = 1
+QJL_V_CODES = 0
+QJL_V_F32 = 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_kv_cache_qjl_amd.build`")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_i, _i64, _p, _f, _sz = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+
+lib.qjl_quantize_keys.restype = _i
+lib.qjl_quantize_keys.argtypes = [_p, _i, _i, _i64, _i, _i, _i64, _i64, _i64, _p, _i, _p, _i, _p, _i,
+                                  _p, _p, _i64, _i64, _p]
+lib.qjl_quantize_values.restype = _i
+lib.qjl_quantize_values.argtypes = [_p, _i, _i, _i64, _i, _i, _i64, _i64, _i64, _i, _p, _p, _i64, _i64, _p]
+lib.qjl_decode_workspace_size.restype = _sz
+lib.qjl_decode_workspace_size.argtypes = [_i, _i, _i, _i, _i64, _i, _i, _i]
+lib.qjl_decode_attention.restype = _i
+lib.qjl_decode_attention.argtypes = [_p, _i, _i, _i, _i, _i, _i64, _p, _i, _p, _i, _p, _i, _p, _p, _i64,
+                                     _i, _p, _p, _p, _i, _f, _p, _p, _i, _p, _sz, _p]
+lib.qjl_status_string.restype = ctypes.c_char_p
+lib.qjl_status_string.argtypes = [_i]
+lib.qjl_last_error.restype = ctypes.c_char_p
+lib.qjl_last_error.argtypes = []
+lib.qjl_timer_enable.restype = _i
+lib.qjl_timer_enable.argtypes = [_i]
+lib.qjl_timer_read.restype = _i
+lib.qjl_timer_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double)]
+
+
+class QJLError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib.qjl_status_string(status).decode()} ({status}): "
+                         f"{lib.qjl_last_error().decode()}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != QJL_OK:
+        raise QJLError(status, where)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return QJL_BF16
+    if t.dtype == torch.float32:
+        return QJL_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def status_string(status: int) -> str:
+    return lib.qjl_status_string(status).decode()
+
+
+def last_error() -> str:
+    return lib.qjl_last_error().decode()
+
+
+@dataclass
+class Cache:
+    """Device arrays of one layer's compressed KV cache (layout in include/qjl.h)."""
+
+    bits: object      # int32 view of uint32 [B, Hkv, Ncap, W]
+    norms: object     # float16 [B, Hkv, Ncap, 2]
+    codes: object     # uint8 [B, Hkv, Ncap, d*nbits/8]
+    meta: object      # float16 [B, Hkv, Ncap, 2]
+    m: int
+    m_out: int
+    nbits: int
+
+    @property
+    def Ncap(self) -> int:
+        return int(self.bits.shape[2])
+
+
+def alloc_cache(B: int, Hkv: int, Ncap: int, m: int, m_out: int, nbits: int = 2, d: int = 128,
+                device="cuda") -> Cache:
+    import torch
+    W = (m + m_out) // 32
+    return Cache(bits=torch.zeros((B, Hkv, Ncap, W), dtype=torch.int32, device=device),
+                 norms=torch.zeros((B, Hkv, Ncap, 2), dtype=torch.float16, device=device),
+                 codes=torch.zeros((B, Hkv, Ncap, d * nbits // 8), dtype=torch.uint8, device=device),
+                 meta=torch.zeros((B, Hkv, Ncap, 2), dtype=torch.float16, device=device),
+                 m=m, m_out=m_out, nbits=nbits)
+
+
+def quantize_keys(K, S_in, S_out, outlier_idx, bits, norms, t0: int = 0, stream=None) -> None:
+    """qjl_quantize_keys on torch tensors.  K [B, T, Hkv, d] (any strides with d contiguous)."""
+    B, T, Hkv, d = K.shape
+    if K.stride(3) != 1:
+        raise ValueError("the d channels of K must be contiguous")
+    m = S_in.shape[0]
+    m_out = 0 if S_out is None else S_out.shape[0]
+    n_out = 0 if outlier_idx is None or outlier_idx.numel() == 0 else outlier_idx.shape[1]
+    _check(lib.qjl_quantize_keys(_ptr(K), _dtype_code(K), B, T, Hkv, d, K.stride(0), K.stride(1), K.stride(2),
+                                 _ptr(S_in), m, _ptr(S_out) if m_out else 0, m_out,
+                                 _ptr(outlier_idx) if n_out else 0, n_out, _ptr(bits), _ptr(norms),
+                                 bits.shape[2], t0, _stream(stream)), "qjl_quantize_keys")
+
+
+def quantize_values(V, nbits: int, codes, meta, t0: int = 0, stream=None) -> None:
+    """qjl_quantize_values on torch tensors.  V [B, T, Hkv, d] (d contiguous)."""
+    B, T, Hkv, d = V.shape
+    if V.stride(3) != 1:
+        raise ValueError("the d channels of V must be contiguous")
+    _check(lib.qjl_quantize_values(_ptr(V), _dtype_code(V), B, T, Hkv, d, V.stride(0), V.stride(1), V.stride(2),
+                                   nbits, _ptr(codes), _ptr(meta), codes.shape[2], t0, _stream(stream)),
+           "qjl_quantize_values")
+
+
+def decode_workspace_size(B: int, Hq: int, Hkv: int, N: int, m: int, m_out: int, nsplit: int = 0,
+                          d: int = 128) -> int:
+    return int(lib.qjl_decode_workspace_size(B, Hq, Hkv, d, N, m, m_out, nsplit))
+
+
+def decode_attention(Q, S_in, S_out, outlier_idx, bits, norms, N: int, out, *, codes=None, meta=None,
+                     V_f32=None, nbits: int = 2, sm_scale: float = 0.0, scores_dbg=None, nsplit: int = 0,
+                     workspace=None, stream=None) -> None:
+    """qjl_decode_attention on torch tensors.  Q [B, Hq, d] contiguous; out [B, Hq, d] fp32."""
+    B, Hq, d = Q.shape
+    if not Q.is_contiguous():
+        raise ValueError("Q must be contiguous [B, Hq, d]")
+    Hkv = bits.shape[1]
+    m = S_in.shape[0]
+    m_out = 0 if S_out is None else S_out.shape[0]
+    n_out = 0 if outlier_idx is None or outlier_idx.numel() == 0 else outlier_idx.shape[1]
+    vmode = QJL_V_F32 if V_f32 is not None else QJL_V_CODES
+    if workspace is None:
+        import torch
+        workspace = torch.empty(max(1, decode_workspace_size(B, Hq, Hkv, N, m, m_out, nsplit, d)),
+                                dtype=torch.uint8, device=Q.device)
+    _check(lib.qjl_decode_attention(_ptr(Q), _dtype_code(Q), B, Hq, Hkv, d, N, _ptr(S_in), m,
+                                    _ptr(S_out) if m_out else 0, m_out, _ptr(outlier_idx) if n_out else 0, n_out,
+                                    _ptr(bits), _ptr(norms), bits.shape[2], vmode, _ptr(codes), _ptr(meta),
+                                    _ptr(V_f32), nbits, sm_scale, _ptr(out), _ptr(scores_dbg), nsplit,
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)), "qjl_decode_attention")
+
+
+def timer_enable(on: bool) -> None:
+    _check(lib.qjl_timer_enable(1 if on else 0), "qjl_timer_enable")
+
+
+def timer_read(kernel: str) -> tuple[int, float]:
+    """(launches, total milliseconds) of one kernel since the last read; clears the record."""
+    n = _i64(0)
+    ms = ctypes.c_double(0.0)
+    _check(lib.qjl_timer_read(kernel.encode(), ctypes.byref(n), ctypes.byref(ms)), "qjl_timer_read")
+    return int(n.value), float(ms.value)

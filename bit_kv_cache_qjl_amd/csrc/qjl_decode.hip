@@ -1,0 +1,408 @@
+// Decode attention over the 1-bit key sketch: query projection, estimator scores, online softmax,
+// dequantized-value aggregation, split-context log-sum-exp merge.
+//
+// Method: "QJL: 1-Bit Quantized JL Transform for KV Cache Quantization with Zero Overhead",
+// "Approach" (the query is JL-projected without quantization; the asymmetric estimator
+// sqrt(pi/2)/m * |k| * <S q, sign(S k)> is unbiased); softmax attention with a weighted sum of the
+// dequantized values ("Your Brain Already Runs on 1-Bit Keys", "Keys Select. Values Deliver.").
+//
+// Kernels
+//   qproj   one workgroup per (sequence, query head): Sq = S q (fp32) pre-multiplied by
+//           sqrt(pi/2)/m (inlier part) and sqrt(pi/2)/m_out (outlier part).
+//   decode  one workgroup (8 waves, 512 threads) per (sequence, KV head, query head, context chunk).
+//           The projected query is expanded in LDS into byte tables: entry [p][beta] is the signed
+//           sum of the 8 Sq values of byte position p under the sign pattern beta, so one LDS read
+//           replaces eight +-1 accumulations.  Per tile of 512 tokens:
+//             score  thread = token: coalesced 128-bit loads of the token's sign words, one table
+//                    read per byte, s = |k_in| * sum_in + |k_out| * sum_out;
+//             softmax block-wide running max (log2 domain), p = 2^(z - M), running sums;
+//             value  thread = (16-channel slice, token pair): the 2-bit codes of two tokens become
+//                    fp16 pairs 1 + code/4 with one and-or, and v_dot2_f32_f16 accumulates
+//                    p*step for both tokens at once; the constant 1 is removed at the end
+//                    (sum p*step*(1 + code/4) - sum p*step = sum p*step*code/4), and the
+//                    min term sum p*min is carried separately.
+//           The partial (M, sum p, unnormalized o) of the chunk goes to the workspace.
+//   combine one workgroup per (sequence, query head): log-sum-exp merge of the chunk partials.
+#include <math.h>
+
+#include "qjl_common.h"
+
+namespace qjl {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = kDecodeTile;   // 512
+constexpr int kWaves = kThreads / 64;
+
+// ------------------------------------------------------------------------------------ qproj
+template <typename QT>
+__device__ __forceinline__ float load_elem(const QT* p, size_t i);
+template <>
+__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, size_t i) {
+    return __uint_as_float((uint32_t)p[i] << 16);
+}
+template <>
+__device__ __forceinline__ float load_elem<float>(const float* p, size_t i) { return p[i]; }
+
+template <typename QT>
+__global__ __launch_bounds__(256) void qproj_kernel(DecodeArgs a) {
+    __shared__ float qin[kD];
+    __shared__ float qo[kMaxOutliers];
+    __shared__ int so[kMaxOutliers];
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x;
+    const int hq = bh % a.Hq;
+    const int h = hq / a.g;
+    const QT* Q = static_cast<const QT*>(a.Q);
+    if (tid < a.n_out) so[tid] = a.oidx[h * a.n_out + tid] & (kD - 1);   // never index outside a row
+    if (tid < kD) qin[tid] = load_elem<QT>(Q, (size_t)bh * kD + tid);
+    __syncthreads();
+    if (tid < a.n_out) qo[tid] = qin[so[tid]];
+    __syncthreads();
+    if (tid < a.n_out) qin[so[tid]] = 0.f;
+    __syncthreads();
+    const QT* Sin = static_cast<const QT*>(a.S_in);
+    const QT* Sout = static_cast<const QT*>(a.S_out);
+    float* dst = a.sq + (size_t)bh * (a.m + a.m_out);
+    const float c_in = kSqrtHalfPi / (float)a.m;
+    for (int j = tid; j < a.m; j += 256) {
+        float acc = 0.f;
+        for (int c = 0; c < kD; ++c) acc = fmaf(load_elem<QT>(Sin, (size_t)j * kD + c), qin[c], acc);
+        dst[j] = acc * c_in;
+    }
+    if (a.m_out) {
+        const float c_out = kSqrtHalfPi / (float)a.m_out;
+        for (int j = tid; j < a.m_out; j += 256) {
+            float acc = 0.f;
+            for (int i = 0; i < a.n_out; ++i) acc = fmaf(load_elem<QT>(Sout, (size_t)j * kD + so[i]), qo[i], acc);
+            dst[a.m + j] = acc * c_out;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------ decode
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
+    uint32_t r;
+    asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(o));
+    return r;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// VM = 0: 2-bit codes + (min, step) meta;  VM = 1: fp32 values.
+template <int WIN, int WOUT, int VM>
+__global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a, int groups) {
+    constexpr int WB = WIN + WOUT;
+    constexpr int P = 4 * WB;                    // byte positions = tables
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    float* lut = lds;                            // [P][256]
+    __shared__ float sq_s[8 * P];
+    __shared__ __attribute__((aligned(16))) float wts[kThreads];   // fp16 pairs (VM 0) or fp32 weights (VM 1)
+    __shared__ float red[kWaves][4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    // XCD-aware placement: blocks L, L+8, L+16, ... share an XCD (and its L2); the query heads of one
+    // (KV head, chunk) are consecutive slots of the same XCD so their re-reads of the chunk hit L2.
+    const int lin = blockIdx.x;
+    const int xcd = lin & 7;
+    const int slot = lin >> 3;
+    const int hg = slot % a.g;
+    const int64_t us = (int64_t)(slot / a.g) * 8 + xcd;
+    if (us >= (int64_t)groups) return;
+    const int split = (int)(us % a.nsplit);
+    const int unit = (int)(us / a.nsplit);       // b * Hkv + h
+    const int b = unit / a.Hkv;
+    const int h = unit - b * a.Hkv;
+    const int hq = h * a.g + hg;
+    const int bhq = b * a.Hq + hq;
+
+    const int64_t t_begin = (int64_t)split * a.chunk;
+    const int64_t t_end = min(a.N, t_begin + a.chunk);
+
+    // ---- byte tables of the projected query
+    for (int i = tid; i < 8 * P; i += kThreads) sq_s[i] = a.sq[(size_t)bhq * (8 * P) + i];
+    __syncthreads();
+    for (int idx = tid; idx < P * 256; idx += kThreads) {
+        const int p = idx >> 8, beta = idx & 255;
+        float v = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float s = sq_s[8 * p + i];
+            v += ((beta >> i) & 1) ? s : -s;
+        }
+        lut[idx] = v;
+    }
+    __syncthreads();
+
+    const uint32_t* bits = a.bits + (size_t)unit * a.Ncap * WB;
+    const uint32_t* norms = reinterpret_cast<const uint32_t*>(a.norms) + (size_t)unit * a.Ncap;
+    const uint32_t* meta = reinterpret_cast<const uint32_t*>(a.meta) + (size_t)unit * a.Ncap;
+    const uint32_t* codes = reinterpret_cast<const uint32_t*>(a.codes) + (size_t)unit * a.Ncap * 8;
+    const float* vf = a.V_f32 + (size_t)unit * a.Ncap * kD;
+    float* sdbg = a.scores_dbg ? a.scores_dbg + (size_t)bhq * a.N : nullptr;
+
+    const int jv = tid & 7;          // value role: 16-channel slice
+    const int pg = tid >> 3;         // value role: token-pair group (0..63)
+
+    float m_run = -INFINITY;
+    float l_t = 0.f, mn_t = 0.f, sw_t = 0.f;   // per-thread partial sums (score role)
+    float acc[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) acc[c] = 0.f;
+
+    for (int64_t tile0 = t_begin; tile0 < t_end; tile0 += kThreads) {
+        const int64_t t = tile0 + tid;
+        const bool valid = t < t_end;
+
+        // value operands of this thread's token pairs, issued early
+        uint32_t xv[8];
+        if (VM == 0) {
+#pragma unroll
+            for (int pass = 0; pass < 4; ++pass) {
+                const int64_t t1 = tile0 + 2 * (pg + 64 * pass);
+                xv[2 * pass] = t1 < t_end ? codes[t1 * 8 + jv] : 0u;
+                xv[2 * pass + 1] = t1 + 1 < t_end ? codes[(t1 + 1) * 8 + jv] : 0u;
+            }
+        }
+
+        // ---- scores (thread = token)
+        uint32_t wv[WB];
+        uint32_t nrm = 0, mt = 0;
+        if (valid) {
+            const uint4* src = reinterpret_cast<const uint4*>(bits + t * WB);
+#pragma unroll
+            for (int q = 0; q < WB / 4; ++q) {
+                const uint4 x = src[q];
+                wv[4 * q] = x.x; wv[4 * q + 1] = x.y; wv[4 * q + 2] = x.z; wv[4 * q + 3] = x.w;
+            }
+            nrm = norms[t];
+            if (VM == 0) mt = meta[t];
+        } else {
+#pragma unroll
+            for (int q = 0; q < WB; ++q) wv[q] = 0u;
+        }
+        float s_in = 0.f, s_out = 0.f;
+#pragma unroll
+        for (int w = 0; w < WB; ++w) {
+            const uint32_t x = wv[w];
+            float part = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) part += lut[(4 * w + k) * 256 + ((x >> (8 * k)) & 0xFFu)];
+            if (w < WIN) s_in += part; else s_out += part;
+        }
+        const float n_in = (float)__builtin_bit_cast(_Float16, (uint16_t)(nrm & 0xFFFFu));
+        const float n_out = (float)__builtin_bit_cast(_Float16, (uint16_t)(nrm >> 16));
+        const float score = WOUT ? fmaf(n_out, s_out, n_in * s_in) : n_in * s_in;
+        if (sdbg && valid) sdbg[t] = score;
+        const float z = valid ? score * a.z_scale : -INFINITY;
+
+        // ---- online softmax (block-wide max, log2 domain)
+        const float wm = wave_max(z);
+        if (lane == 0) red[wave][0] = wm;
+        __syncthreads();
+        float tmax = red[0][0];
+#pragma unroll
+        for (int i = 1; i < kWaves; ++i) tmax = fmaxf(tmax, red[i][0]);
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+        const float p = valid ? exp2f(z - m_new) : 0.f;
+        m_run = m_new;
+        l_t = fmaf(l_t, alpha, p);
+        if (VM == 0) {
+            const float mn = (float)__builtin_bit_cast(_Float16, (uint16_t)(mt & 0xFFFFu));
+            const float step = (float)__builtin_bit_cast(_Float16, (uint16_t)(mt >> 16));
+            const _Float16 w16 = (_Float16)(p * step);
+            mn_t = fmaf(mn_t, alpha, p * mn);
+            sw_t = fmaf(sw_t, alpha, (float)w16);
+            reinterpret_cast<_Float16*>(wts)[tid] = w16;
+        } else {
+            wts[tid] = p;
+        }
+        if (alpha != 1.f) {
+#pragma unroll
+            for (int c = 0; c < 16; ++c) acc[c] *= alpha;
+        }
+        __syncthreads();
+
+        // ---- values (thread = 16-channel slice x token pairs)
+        if (VM == 0) {
+            const uint32_t base = 0x3C003C00u, mask = 0x03000300u;
+#pragma unroll
+            for (int pass = 0; pass < 4; ++pass) {
+                const int pr = pg + 64 * pass;
+                const half2_t wp = __builtin_bit_cast(half2_t, reinterpret_cast<const uint32_t*>(wts)[pr]);
+                const uint32_t x1 = xv[2 * pass], x2 = xv[2 * pass + 1];
+                const uint32_t ylo = __builtin_amdgcn_perm(x2, x1, 0x05040100u);
+                const uint32_t yhi = __builtin_amdgcn_perm(x2, x1, 0x07060302u);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const uint32_t sl = c <= 4 ? (ylo << (8 - 2 * c)) : (ylo >> (2 * c - 8));
+                    const uint32_t sh = c <= 4 ? (yhi << (8 - 2 * c)) : (yhi >> (2 * c - 8));
+                    acc[c] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, and_or(sl, mask, base)), wp, acc[c], false);
+                    acc[8 + c] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, and_or(sh, mask, base)), wp, acc[8 + c], false);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int pass = 0; pass < 4; ++pass) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int tl = 2 * (pg + 64 * pass) + e;
+                    const int64_t tt = tile0 + tl;
+                    if (tt < t_end) {
+                        const float w = wts[tl];
+                        const float4* src = reinterpret_cast<const float4*>(vf + tt * kD + 16 * jv);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float4 x = src[q];
+                            acc[4 * q] = fmaf(w, x.x, acc[4 * q]);
+                            acc[4 * q + 1] = fmaf(w, x.y, acc[4 * q + 1]);
+                            acc[4 * q + 2] = fmaf(w, x.z, acc[4 * q + 2]);
+                            acc[4 * q + 3] = fmaf(w, x.w, acc[4 * q + 3]);
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();   // wts and red are rewritten by the next tile
+    }
+
+    // ---- chunk partial: block sums, channel reduction over the 64 token-pair groups
+    const float l_sum = wave_sum(l_t), mn_sum = wave_sum(mn_t), sw_sum = wave_sum(sw_t);
+    if (lane == 0) {
+        red[wave][0] = l_sum;
+        red[wave][1] = mn_sum;
+        red[wave][2] = sw_sum;
+    }
+    float* rbuf = lds;   // reuse the tables: [64 groups][128 channels]
+#pragma unroll
+    for (int c = 0; c < 16; ++c) rbuf[pg * kD + 16 * jv + c] = acc[c];
+    __syncthreads();
+    if (tid < kD) {
+        float tot = 0.f;
+        for (int i = 0; i < kThreads / 8; ++i) tot += rbuf[i * kD + tid];
+        float L = 0.f, MN = 0.f, SW = 0.f;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) {
+            L += red[i][0];
+            MN += red[i][1];
+            SW += red[i][2];
+        }
+        const float o = VM == 0 ? fmaf(4.f, tot - SW, MN) : tot;
+        float* dst = a.part + ((size_t)bhq * a.nsplit + split) * (kD + 2);
+        dst[2 + tid] = o;
+        if (tid == 0) {
+            dst[0] = m_run;
+            dst[1] = L;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------ combine
+__global__ __launch_bounds__(kD) void combine_kernel(DecodeArgs a) {
+    const int bhq = blockIdx.x;
+    const int c = threadIdx.x;
+    const float* src = a.part + (size_t)bhq * a.nsplit * (kD + 2);
+    float mmax = -INFINITY;
+    for (int i = 0; i < a.nsplit; ++i) mmax = fmaxf(mmax, src[(size_t)i * (kD + 2)]);
+    float l = 0.f, o = 0.f;
+    if (mmax != -INFINITY) {
+        for (int i = 0; i < a.nsplit; ++i) {
+            const float* pp = src + (size_t)i * (kD + 2);
+            const float mi = pp[0];
+            if (mi == -INFINITY) continue;
+            const float sc = exp2f(mi - mmax);
+            l = fmaf(sc, pp[1], l);
+            o = fmaf(sc, pp[2 + c], o);
+        }
+    }
+    a.out[(size_t)bhq * kD + c] = l > 0.f ? o / l : 0.f;
+}
+
+template <int WIN, int WOUT, int VM>
+hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
+    // dynamic LDS: the byte tables, also reused for the final channel reduction [64][128] floats
+    size_t lut_bytes = (size_t)4 * (WIN + WOUT) * 256 * sizeof(float);
+    if (lut_bytes < (size_t)(kThreads / 8) * kD * sizeof(float)) lut_bytes = (size_t)(kThreads / 8) * kD * sizeof(float);
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<WIN, WOUT, VM>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lut_bytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int groups = a.B * a.Hkv * a.nsplit;
+    const int slots = (groups + 7) / 8;
+    const unsigned nblocks = (unsigned)slots * 8u * (unsigned)a.g;
+    timer_begin(TK_DECODE, s);
+    hipLaunchKernelGGL((decode_kernel<WIN, WOUT, VM>), dim3(nblocks), dim3(kThreads), lut_bytes, s, a, groups);
+    timer_end(TK_DECODE, s);
+    return hipGetLastError();
+}
+
+template <int WIN, int WOUT>
+hipError_t launch_decode_v(const DecodeArgs& a, int vmode, hipStream_t s) {
+    return vmode == 0 ? launch_decode_t<WIN, WOUT, 0>(a, s) : launch_decode_t<WIN, WOUT, 1>(a, s);
+}
+
+}  // namespace
+
+int decode_pick_nsplit(int B, int Hkv, int g, int64_t N, int m, int m_out) {
+    (void)m;
+    (void)m_out;
+    const int64_t units = (int64_t)B * Hkv * g;
+    const int64_t target = 1024;                       // ~4 workgroups per CU on 256 CUs
+    int64_t ns = (target + units - 1) / units;
+    const int64_t max_ns = (N + kDecodeTile - 1) / kDecodeTile;
+    if (ns > max_ns) ns = max_ns;
+    if (ns < 1) ns = 1;
+    return (int)ns;
+}
+
+int64_t decode_chunk(int64_t N, int nsplit) {
+    const int64_t per = (N + nsplit - 1) / nsplit;
+    return ((per + kDecodeTile - 1) / kDecodeTile) * kDecodeTile;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int qdt, int vmode, hipStream_t s) {
+    timer_begin(TK_QPROJ, s);
+    if (qdt == 0) hipLaunchKernelGGL(qproj_kernel<uint16_t>, dim3(a.B * a.Hq), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(qproj_kernel<float>, dim3(a.B * a.Hq), dim3(256), 0, s, a);
+    timer_end(TK_QPROJ, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int win = a.m >> 5, wout = a.m_out >> 5;
+    if (win == 4 && wout == 0) e = launch_decode_v<4, 0>(a, vmode, s);
+    else if (win == 4 && wout == 4) e = launch_decode_v<4, 4>(a, vmode, s);
+    else if (win == 8 && wout == 0) e = launch_decode_v<8, 0>(a, vmode, s);
+    else if (win == 8 && wout == 8) e = launch_decode_v<8, 8>(a, vmode, s);
+    else if (win == 16 && wout == 0) e = launch_decode_v<16, 0>(a, vmode, s);
+    else if (win == 16 && wout == 16) e = launch_decode_v<16, 16>(a, vmode, s);
+    else return hipErrorInvalidValue;
+    if (e != hipSuccess) return e;
+    timer_begin(TK_COMBINE, s);
+    hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.Hq), dim3(kD), 0, s, a);
+    timer_end(TK_COMBINE, s);
+    return hipGetLastError();
+}
+
+bool decode_shape_supported(int m, int m_out) {
+    const int win = m >> 5, wout = m_out >> 5;
+    return (win == 4 || win == 8 || win == 16) && (wout == 0 || wout == win);
+}
+
+}  // namespace qjl

@@ -1,0 +1,285 @@
+// Key quantization: JL projection on the matrix cores, sign extraction and bit packing fused into
+// the epilogue, fp16 norms.
+//
+// Method: "QJL: 1-Bit Quantized JL Transform for KV Cache Quantization with Zero Overhead",
+// "Approach" (Gaussian JL transform of each key, keep the signs plus the key norm, outlier channels
+// through a separate quantizer copy); 16-bit norm from "Your Brain Already Runs on 1-Bit Keys",
+// "But Wait. Don't the Small Dims Overpower?".
+//
+// bf16 kernel layout (gfx950, wave64, v_mfma_f32_32x32x16_bf16):
+//   * one workgroup = 8 waves; it owns one (sequence, KV head) and a range of tokens, walked in
+//     chunks of 32 tokens (the MFMA N dimension);
+//   * the JL matrix is stationary: each wave keeps its share of 32-row tiles of S_in (K = 128, eight
+//     K steps) and of the outlier-channel columns of S_out (K = 16, one step) in VGPRs for the whole
+//     workgroup lifetime;
+//   * the key chunk is staged in LDS with the outlier channels zeroed (inlier operand) and the
+//     outlier channels gathered into a 16-wide row (outlier operand); the loader threads also form
+//     the two sums of squares for the norms;
+//   * D = S_tile x K_chunk^T puts 16 projections of one token in each lane; the sign bits are shifted
+//     into a word with v_alignbit, the two half-waves are merged with one cross-lane exchange, and
+//     the S rows are permuted when loaded so that bit b of the word is projection 32*tile + b;
+//   * words are staged in LDS and written with coalesced stores.
+#include "qjl_common.h"
+
+namespace qjl {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kTok = 32;        // tokens per chunk
+constexpr int kKRow = 136;      // LDS row of one key in bf16 elements (272 B: conflict-free b128 reads)
+constexpr int kGRow = 24;       // LDS row of the gathered outlier channels (48 B)
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
+
+// MFMA output row i (0..31) of a 32x32 tile holds projection tile_row(i) of that tile.  Lane l
+// holds rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15; the packing loop leaves the sign of
+// register r in bit 15 - r of the lane's half-word, and the half-wave l >= 32 supplies bits 16..31.
+__device__ __forceinline__ int tile_row(int i) {
+    const int half = (i >> 2) & 1;
+    const int r = 4 * (i >> 3) + (i & 3);
+    return 15 - r + 16 * half;
+}
+
+// Signs of one 32x32 tile -> one packed word per token (valid in lanes 0..31, lane = token).
+// Bit = 1 iff the projection is >= 0: the sign bit of each accumulator is shifted in, then inverted.
+__device__ __forceinline__ uint32_t pack_signs(const f32x16& acc, int lane) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) w = __builtin_amdgcn_alignbit(w, __float_as_uint(acc[r]), 31);
+    const uint32_t other = __shfl_xor(w, 32);
+    const uint32_t lo = lane < 32 ? w : other;
+    const uint32_t hi = lane < 32 ? other : w;
+    return ~(lo | (hi << 16));
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+template <int TPW>
+__global__ __launch_bounds__(kThreads, 1) void quantize_keys_bf16_kernel(KeyQuantArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t kl[kTok * kKRow];
+    __shared__ __attribute__((aligned(16))) uint16_t gl[kTok * kGRow];
+    __shared__ uint32_t ol[kTok * (kMaxBits / 32 + 1)];
+    __shared__ int s_oidx[kMaxOutliers];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int h = blockIdx.y;
+    const int b = blockIdx.z;
+    const int64_t t_begin = (int64_t)blockIdx.x * a.tokens_per_block;
+    const int64_t t_end = min(a.T, t_begin + (int64_t)a.tokens_per_block);
+    const int n_out = a.n_out;
+    const int Win = a.m >> 5;
+    const int Wout = a.m_out >> 5;
+    const int W = a.W;
+    const int orow = W + 1;
+
+    if (tid < n_out) s_oidx[tid] = a.oidx[h * n_out + tid] & (kD - 1);   // never index outside a row
+    for (int i = tid; i < kTok * kGRow / 2; i += kThreads) reinterpret_cast<uint32_t*>(gl)[i] = 0u;
+    __syncthreads();
+
+    // loader role: token tt of the chunk, channels 8*cg .. 8*cg+7
+    const int tt = tid >> 4;
+    const int cg = tid & 15;
+    uint32_t omask = 0;
+    for (int i = 0; i < n_out; ++i) {
+        const int c = s_oidx[i];
+        if ((c >> 3) == cg) omask |= 1u << (c & 7);
+    }
+
+    // stationary JL fragments of this wave
+    const uint16_t* Sin = static_cast<const uint16_t*>(a.S_in);
+    const uint16_t* Sout = static_cast<const uint16_t*>(a.S_out);
+    const int prow = tile_row(lane & 31);
+    const int khalf = (lane >> 5) * 8;
+    uint4 sin_frag[TPW][8];
+    uint4 sout_frag[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int j = wave + kWaves * i;
+        if (j < Win) {
+            const uint16_t* row = Sin + (size_t)(32 * j + prow) * kD + khalf;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) sin_frag[i][s] = *reinterpret_cast<const uint4*>(row + 16 * s);
+        } else {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) sin_frag[i][s] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        uint32_t g[4] = {0u, 0u, 0u, 0u};
+        if (j < Wout) {
+            const uint16_t* row = Sout + (size_t)(32 * j + prow) * kD;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int k = khalf + e;
+                const uint32_t v = k < n_out ? row[s_oidx[k]] : 0u;
+                g[e >> 1] |= v << (16 * (e & 1));
+            }
+        }
+        sout_frag[i] = make_uint4(g[0], g[1], g[2], g[3]);
+    }
+
+    const uint16_t* K = static_cast<const uint16_t*>(a.K);
+    const int64_t head_row0 = ((int64_t)b * a.Hkv + h) * a.Ncap + a.t0;
+
+    for (int64_t c0 = t_begin; c0 < t_end; c0 += kTok) {
+        const int nvalid = (int)min((int64_t)kTok, t_end - c0);
+
+        // ---- stage the chunk: mask, gather outlier channels, sums of squares
+        uint4 kv = make_uint4(0u, 0u, 0u, 0u);
+        if (tt < nvalid)
+            kv = *reinterpret_cast<const uint4*>(K + b * a.sKb + (c0 + tt) * a.sKt + h * a.sKh + 8 * cg);
+        uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+        float ss_in = 0.f, ss_out = 0.f;
+        uint32_t mw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = kw[q] & 0xFFFFu, hi = kw[q] >> 16;
+            const float flo = bf16_to_f32(lo), fhi = bf16_to_f32(hi);
+            const bool olo = (omask >> (2 * q)) & 1u, ohi = (omask >> (2 * q + 1)) & 1u;
+            if (olo) ss_out = fmaf(flo, flo, ss_out); else ss_in = fmaf(flo, flo, ss_in);
+            if (ohi) ss_out = fmaf(fhi, fhi, ss_out); else ss_in = fmaf(fhi, fhi, ss_in);
+            mw[q] = (olo ? 0u : lo) | ((ohi ? 0u : hi) << 16);
+        }
+        if (omask) {
+            for (int i = 0; i < n_out; ++i) {
+                const int c = s_oidx[i];
+                if ((c >> 3) == cg) {
+                    const int e = c & 7;
+                    gl[tt * kGRow + i] = (uint16_t)((kw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                }
+            }
+        }
+        *reinterpret_cast<uint4*>(kl + tt * kKRow + 8 * cg) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) {
+            ss_in += __shfl_xor(ss_in, o);
+            ss_out += __shfl_xor(ss_out, o);
+        }
+        if (cg == 0 && tt < nvalid) {
+            const _Float16 ni = (_Float16)sqrtf(ss_in);
+            const _Float16 no = (_Float16)sqrtf(ss_out);
+            const uint32_t packed = (uint32_t)__builtin_bit_cast(uint16_t, ni) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, no) << 16);
+            reinterpret_cast<uint32_t*>(a.norms)[head_row0 + c0 + tt] = packed;
+        }
+        __syncthreads();
+
+        // ---- projections on the matrix cores, signs packed in registers
+        uint4 bfrag[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            bfrag[s] = *reinterpret_cast<const uint4*>(kl + (lane & 31) * kKRow + 16 * s + khalf);
+        const uint4 gfrag = *reinterpret_cast<const uint4*>(gl + (lane & 31) * kGRow + khalf);
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int j = wave + kWaves * i;
+            if (j < Win) {
+                f32x16 acc = {};
+#pragma unroll
+                for (int s = 0; s < 8; ++s)
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sin_frag[i][s]), as_bf16x8(bfrag[s]),
+                                                                  acc, 0, 0, 0);
+                const uint32_t w = pack_signs(acc, lane);
+                if (lane < 32) ol[lane * orow + j] = w;
+            }
+            if (j < Wout) {
+                f32x16 acc = {};
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sout_frag[i]), as_bf16x8(gfrag), acc, 0, 0, 0);
+                const uint32_t w = pack_signs(acc, lane);
+                if (lane < 32) ol[lane * orow + Win + j] = w;
+            }
+        }
+        __syncthreads();
+
+        // ---- coalesced store of the packed words of the chunk
+        uint32_t* dst = a.bits + (head_row0 + c0) * W;
+        for (int i = tid; i < nvalid * W; i += kThreads) {
+            const int tok = i / W;
+            dst[i] = ol[tok * orow + (i - tok * W)];
+        }
+    }
+}
+
+// fp32 keys and JL matrix (VALU, one wave per key): exact fp32 fused multiply-adds in channel order.
+constexpr int kF32Tok = 4;
+
+__global__ __launch_bounds__(256) void quantize_keys_f32_kernel(KeyQuantArgs a) {
+    __shared__ float kin[kF32Tok][kD];
+    __shared__ float kout[kF32Tok][kD];
+    __shared__ int s_oidx[kMaxOutliers];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int64_t t = (int64_t)blockIdx.x * kF32Tok + wave;
+    const bool valid = t < a.T;
+    if (tid < a.n_out) s_oidx[tid] = a.oidx[h * a.n_out + tid] & (kD - 1);
+    __syncthreads();
+    const float* K = static_cast<const float*>(a.K);
+    float ss_in = 0.f, ss_out = 0.f;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int c = 2 * lane + q;
+        const float v = valid ? K[b * a.sKb + t * a.sKt + h * a.sKh + c] : 0.f;
+        bool is_out = false;
+        for (int i = 0; i < a.n_out; ++i) is_out |= (s_oidx[i] == c);
+        kin[wave][c] = is_out ? 0.f : v;
+        kout[wave][c] = is_out ? v : 0.f;
+        if (is_out) ss_out = fmaf(v, v, ss_out); else ss_in = fmaf(v, v, ss_in);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        ss_in += __shfl_xor(ss_in, o);
+        ss_out += __shfl_xor(ss_out, o);
+    }
+    __syncthreads();
+    if (!valid) return;
+    const int64_t row = ((int64_t)b * a.Hkv + h) * a.Ncap + a.t0 + t;
+    if (lane == 0) {
+        const _Float16 ni = (_Float16)sqrtf(ss_in), no = (_Float16)sqrtf(ss_out);
+        reinterpret_cast<uint32_t*>(a.norms)[row] =
+            (uint32_t)__builtin_bit_cast(uint16_t, ni) | ((uint32_t)__builtin_bit_cast(uint16_t, no) << 16);
+    }
+    const float* Sin = static_cast<const float*>(a.S_in);
+    const float* Sout = static_cast<const float*>(a.S_out);
+    const int total = a.m + a.m_out;
+    for (int g = 0; 64 * g < total; ++g) {
+        const int r = 64 * g + lane;
+        float p = 0.f;
+        if (r < a.m) {
+            const float* srow = Sin + (size_t)r * kD;
+            for (int c = 0; c < kD; ++c) p = fmaf(srow[c], kin[wave][c], p);
+        } else if (r < total) {
+            const float* srow = Sout + (size_t)(r - a.m) * kD;
+            for (int c = 0; c < kD; ++c) p = fmaf(srow[c], kout[wave][c], p);
+        }
+        const uint64_t bal = __ballot(r < total && p >= 0.f);
+        if (lane == 0) {
+            uint32_t* dst = a.bits + row * a.W;
+            if (2 * g < a.W) dst[2 * g] = (uint32_t)bal;
+            if (2 * g + 1 < a.W) dst[2 * g + 1] = (uint32_t)(bal >> 32);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_keys_bf16(const KeyQuantArgs& a, int B, hipStream_t s) {
+    const int tiles = (a.m >> 5) > (a.m_out >> 5) ? (a.m >> 5) : (a.m_out >> 5);
+    const int tpw = (tiles + kWaves - 1) / kWaves;
+    dim3 grid((unsigned)((a.T + a.tokens_per_block - 1) / a.tokens_per_block), (unsigned)a.Hkv, (unsigned)B);
+    if (tpw <= 1) hipLaunchKernelGGL(quantize_keys_bf16_kernel<1>, grid, dim3(kThreads), 0, s, a);
+    else if (tpw == 2) hipLaunchKernelGGL(quantize_keys_bf16_kernel<2>, grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL(quantize_keys_bf16_kernel<4>, grid, dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_keys_f32(const KeyQuantArgs& a, int B, hipStream_t s) {
+    dim3 grid((unsigned)((a.T + kF32Tok - 1) / kF32Tok), (unsigned)a.Hkv, (unsigned)B);
+    hipLaunchKernelGGL(quantize_keys_f32_kernel, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace qjl

@@ -1,0 +1,178 @@
+/*
+ * qjl.h - C ABI of libqjl: 1-bit QJL KV-cache key compression and decode attention on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (page "QJL: 1-Bit Quantized JL Transform for KV Cache Quantization with Zero
+ * Overhead", sections "Approach" and "Surprising findings"): every key k is projected with a
+ * Gaussian JL matrix S (m x d) and only the signs of S k are kept, plus the key norm; outlier
+ * channels go through a separate copy of the quantizer; the query is projected without
+ * quantization, and the inner product is estimated by the unbiased asymmetric estimator
+ *
+ *     score(q, k) = sqrt(pi/2)/m * |k_in| * <S_in q_in, sign(S_in k_in)>
+ *                 + sqrt(pi/2)/m_out * |k_out| * <S_out q_out, sign(S_out k_out)>
+ *
+ * where x_in / x_out are x with its outlier channels / its other channels set to zero.  Values use
+ * token-wise min/max quantization (same page, "Limitations"; page "2 numbers out of 128 destroy the
+ * entire KV cache", section "The Obvious Fix: Use Fewer Bits").  Decode attention is softmax over
+ * sm_scale * score followed by the weighted sum of the dequantized values.
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers owned by the caller; the library never allocates,
+ *     frees, or synchronizes.  Work is enqueued on `stream` (0 = the null stream) and returns
+ *     immediately; results are valid once the stream reaches that point.
+ *   - Argument errors are detected on the host before anything is enqueued and returned as a
+ *     negative qjl_status; nothing is written then.  A failed launch returns QJL_ERR_HIP.
+ *     qjl_last_error() gives a human-readable detail of the last error on the calling thread.
+ *   - Supported shapes: head dimension d = 128; m and m_out multiples of 32 with 32 <= m,
+ *     0 <= m_out, m + m_out <= 1024; 0 <= n_out <= 16 outlier channels per KV head, n_out > 0 only
+ *     with m_out > 0; Hq a multiple of Hkv.  Query head hq reads KV head hq / (Hq / Hkv).
+ *   - Every device pointer must be 16-byte aligned, and the model-layout strides must keep every
+ *     d-vector 16-byte aligned (QJL_ERR_MISALIGNED otherwise).
+ *   - Stateless and thread-safe; calls on different streams may overlap.
+ *
+ * Cache layout in HBM (per sequence b, KV head h, token position t < Ncap):
+ *   bits  uint32 [B][Hkv][Ncap][W], W = (m + m_out) / 32: bit i of word w is 1 iff projection
+ *         32 w + i is >= 0 (sign(0) taken as +1); words 0 .. m/32-1 hold the inlier sketch,
+ *         words m/32 .. W-1 the outlier sketch.
+ *   norms fp16  [B][Hkv][Ncap][2]: (|k_in|, |k_out|) as IEEE binary16 round-to-nearest-even.
+ *   codes uint8 [B][Hkv][Ncap][d*nbits/8]: the value codes of one token as an LSB-first bit
+ *         stream, code of channel c in bits [nbits*c, nbits*c + nbits).
+ *   meta  fp16  [B][Hkv][Ncap][2]: (min, step) of the token's value vector.
+ */
+#ifndef QJL_H
+#define QJL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QJL_OK = 0,
+    QJL_ERR_INVALID_ARG = -1,  /* null pointer, negative size, inconsistent shapes, bad enum   */
+    QJL_ERR_UNSUPPORTED = -2,  /* valid request outside the supported shapes listed above      */
+    QJL_ERR_MISALIGNED = -3,   /* a pointer or stride breaks the 16-byte alignment rule       */
+    QJL_ERR_WORKSPACE = -4,    /* decode workspace missing or smaller than required            */
+    QJL_ERR_HIP = -5           /* the HIP runtime reported an error at launch                  */
+} qjl_status;
+
+typedef enum { QJL_BF16 = 0, QJL_F32 = 1 } qjl_dtype;
+
+typedef enum {
+    QJL_V_CODES = 0,  /* values as token-wise codes + (min, step) meta                         */
+    QJL_V_F32 = 1     /* values kept unquantized, fp32 [B][Hkv][Ncap][d]                       */
+} qjl_vmode;
+
+/*
+ * qjl_quantize_keys - sketch T new keys per (sequence, KV head) into the cache at positions
+ * [t0, t0 + T).
+ *
+ * Defined by "QJL: 1-Bit Quantized JL Transform ..." ("Approach"): Gaussian JL transform, keep the
+ * sign bits plus the key norm; outlier channels through a separate quantizer copy; the norm is
+ * 16-bit (page "Your Brain Already Runs on 1-Bit Keys", "But Wait. Don't the Small Dims
+ * Overpower?").  Per key k of KV head h with outlier set O_h:
+ *     bits  = sign(S_in k_in) then sign(S_out k_out), packed as described above;
+ *     norms = fp16(|k_in|), fp16(|k_out|).
+ *
+ *   K           keys in the model layout, element (b, t, h, c) at K[b*sK_b + t*sK_t + h*sK_h + c]
+ *               (element strides; the d channels are contiguous); dtype kdt (bf16 or fp32).
+ *   S_in        [m][d] row-major, dtype kdt.  S_out [m_out][d] row-major, dtype kdt (may be NULL
+ *               when m_out == 0).  The caller draws S (i.i.d. N(0,1)) and keeps it for decode.
+ *   outlier_idx int32 [Hkv][n_out]: distinct channels in [0, d) per KV head (NULL if n_out == 0).
+ *   bits, norms the cache arrays (layout above) with capacity Ncap tokens; t0 + T <= Ncap.
+ * Projections accumulate in fp32 (bf16 keys on the matrix cores); a sign bit can differ from the
+ * exact sign only where |S k| is within fp32 accumulation error of zero.  T == 0 or B == 0 is a
+ * no-op.
+ */
+int qjl_quantize_keys(const void* K, int kdt, int B, int64_t T, int Hkv, int d,
+                      int64_t sK_b, int64_t sK_t, int64_t sK_h,
+                      const void* S_in, int m, const void* S_out, int m_out,
+                      const int32_t* outlier_idx, int n_out,
+                      uint32_t* bits, uint16_t* norms, int64_t Ncap, int64_t t0,
+                      hipStream_t stream);
+
+/*
+ * qjl_quantize_values - token-wise min/max quantization of T new values per (sequence, KV head)
+ * into the cache at positions [t0, t0 + T).
+ *
+ * Defined by "2 numbers out of 128 destroy the entire KV cache" ("The Obvious Fix: Use Fewer Bits":
+ * find the range, divide it into equally spaced values, round to the nearest) and the QJL summary
+ * ("Limitations": values use token-wise quantization).  Per value vector v (d channels), in IEEE
+ * fp32 with L = 2^nbits - 1:
+ *     mn = min v; mx = max v; step = fp16_rne((mx - mn) / L); mn16 = fp16_rne(mn);
+ *     code_c = clamp(rint((v_c - mn16) / step), 0, L)   (rint ties to even; all 0 if step == 0);
+ *     dequantized value = mn16 + step * code.
+ *   V      values in the model layout with element strides (sV_b, sV_t, sV_h), dtype vdt.
+ *   nbits  2, 3 or 4.
+ *   codes  uint8 [B][Hkv][Ncap][d*nbits/8]; meta fp16 [B][Hkv][Ncap][2] = (mn16, step).
+ */
+int qjl_quantize_values(const void* V, int vdt, int B, int64_t T, int Hkv, int d,
+                        int64_t sV_b, int64_t sV_t, int64_t sV_h, int nbits,
+                        uint8_t* codes, uint16_t* meta, int64_t Ncap, int64_t t0,
+                        hipStream_t stream);
+
+/*
+ * qjl_decode_workspace_size - bytes of device workspace qjl_decode_attention needs for these
+ * sizes and this nsplit (nsplit <= 0: the library's own choice, the same one the decode call makes).
+ */
+size_t qjl_decode_workspace_size(int B, int Hq, int Hkv, int d, int64_t N, int m, int m_out,
+                                 int nsplit);
+
+/*
+ * qjl_decode_attention - one decode step: each query attends over the first N cached tokens of
+ * its KV head.
+ *
+ * Defined by the QJL summary ("Approach": the query is JL-projected without quantization, and the
+ * asymmetric estimator is unbiased for the inner product) and by softmax attention over the
+ * estimated scores with a weighted sum of the dequantized values (page "Your Brain Already Runs on
+ * 1-Bit Keys", "Keys Select. Values Deliver.").  Per (b, hq) with h = hq / (Hq/Hkv):
+ *     Sq_in = S_in q_in, Sq_out = S_out q_out                         (fp32, unquantized)
+ *     s_t   = score(q, k_t) from the sketch bits and fp16 norms      (formula at the top)
+ *     out   = sum_t softmax(sm_scale * s)_t * v_t                    (fp32 accumulation)
+ * where v_t = mn16 + step * code (QJL_V_CODES) or the fp32 value itself (QJL_V_F32).
+ *   Q           [B][Hq][d] contiguous, dtype qdt; S_in / S_out / outlier_idx as for quantize (S in
+ *               dtype qdt).
+ *   bits, norms the key cache (capacity Ncap >= N).
+ *   vmode       QJL_V_CODES: codes + meta (nbits must be 2), V_f32 ignored;
+ *               QJL_V_F32: V_f32 [B][Hkv][Ncap][d] fp32, codes/meta ignored.
+ *   sm_scale    softmax scale; <= 0 selects 1/sqrt(d).
+ *   out         fp32 [B][Hq][d].  N == 0 writes zeros.
+ *   scores_dbg  optional fp32 [B][Hq][N] receiving the raw estimator scores s_t (NULL to skip).
+ *   nsplit      number of context chunks per (b, KV head) merged by log-sum-exp (<= 0: auto).
+ *   workspace   device scratch of at least qjl_decode_workspace_size(...) bytes (same nsplit);
+ *               owned by the caller, contents undefined on return, must not be shared by calls
+ *               that overlap in time.
+ */
+int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, int64_t N,
+                         const void* S_in, int m, const void* S_out, int m_out,
+                         const int32_t* outlier_idx, int n_out,
+                         const uint32_t* bits, const uint16_t* norms, int64_t Ncap,
+                         int vmode, const uint8_t* codes, const uint16_t* meta, const float* V_f32,
+                         int nbits, float sm_scale, float* out, float* scores_dbg, int nsplit,
+                         void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* qjl_status_string(int status);
+
+/* Detail of the last error reported on the calling thread ("" if none). */
+const char* qjl_last_error(void);
+
+/*
+ * Kernel timing for measurement harnesses.  While enabled, every launch of the named kernel
+ * ("decode", "quantize_keys", "quantize_values", "query_project", "combine") is bracketed by HIP
+ * events recorded on the launch stream.  qjl_timer_read synchronizes on the recorded events and
+ * returns the number of launches timed and their total duration in milliseconds, then clears the
+ * record.  Disabled by default; enabling it does not change results.
+ */
+int qjl_timer_enable(int on);
+int qjl_timer_read(const char* kernel, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QJL_H */

@@ -1,0 +1,132 @@
+"""Shared helpers of the GPU parity tests: uploads, library calls, comparisons against the oracle."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+
+import oracle
+import seeded_inputs as si
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def to_dev(x: np.ndarray, dtype: str, device="cuda"):
+    """fp32 numpy array holding storage-type values -> device tensor of the storage type (exact)."""
+    torch = torch_mod()
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def inputs(w: si.Workload, T: int | None = None):
+    oidx = si.outlier_channels(w)
+    S_in, S_out = si.jl_matrices(w)
+    K = si.keys(w, oidx, T)
+    V = si.values(w, T)
+    Q = si.queries(w)
+    return dict(oidx=oidx, S_in=S_in, S_out=S_out, K=K, V=V, Q=Q)
+
+
+def gpu_quantize_keys(qjl, w, K, S_in, S_out, oidx, Ncap=None, t0=0, Kdev=None):
+    torch = torch_mod()
+    B, T, Hkv, d = K.shape
+    Ncap = T + t0 if Ncap is None else Ncap
+    Kd = to_dev(K, w.dtype) if Kdev is None else Kdev
+    cache = qjl.alloc_cache(B, Hkv, Ncap, w.m, w.m_out, w.nbits)
+    qjl.quantize_keys(Kd, to_dev(S_in, w.dtype), to_dev(S_out, w.dtype) if w.m_out else None,
+                      torch.from_numpy(oidx).cuda() if w.n_out else None, cache.bits, cache.norms, t0=t0)
+    torch.cuda.synchronize()
+    return cache
+
+
+def bits_np(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def compare_bits(gpu_bits: np.ndarray, ref: dict, what: str, nbits_total: int):
+    """Bit-exact except where the oracle flags |S k| < 1e-5 |k|; returns (mismatches, flagged)."""
+    g = oracle.unpack_bits(gpu_bits, nbits_total)
+    r = oracle.unpack_bits(ref["bits"], nbits_total)
+    diff = g != r
+    flagged = ref["near_zero"]
+    bad = diff & ~flagged
+    if bad.any():
+        idx = np.argwhere(bad)[0]
+        tok = tuple(idx[:-1])
+        raise AssertionError(f"{what}: {int(bad.sum())} unflagged bit mismatches of {diff.size}; first at {tuple(idx)}; "
+                             f"gpu words {gpu_bits[tok][:4]} oracle words {ref['bits'][tok][:4]}")
+    log(f"  {what}: bits ok, {int(diff.sum())} mismatches all within {int(flagged.sum())} near-zero flags "
+        f"of {diff.size}")
+    return int(diff.sum()), int(flagged.sum())
+
+
+def compare_norms(gpu: np.ndarray, ref: np.ndarray, what: str):
+    """Within one fp16 ulp (norms are non-negative, so adjacent values differ by 1 in the pattern)."""
+    a = gpu.view(np.uint16).astype(np.int64)
+    b = ref.view(np.uint16).astype(np.int64)
+    d = np.abs(a - b)
+    assert d.max() <= 1, f"{what}: norm differs by {d.max()} fp16 ulps"
+    log(f"  {what}: norms ok ({int((d == 1).sum())} of {d.size} one ulp apart)")
+
+
+def score_tolerance(sq_in, sq_out, norms, m, m_out):
+    """1e-3 relative to the estimator's magnitude scale sqrt(pi/2)(n_in |Sq_in|_1/m + n_out |Sq_out|_1/m_out)."""
+    n_in = norms[:, 0].astype(np.float64)
+    n_out = norms[:, 1].astype(np.float64)
+    scale = n_in * np.abs(sq_in).sum() / m
+    if m_out:
+        scale = scale + n_out * np.abs(sq_out).sum() / m_out
+    return 1e-3 * math.sqrt(math.pi / 2) * scale
+
+
+def run_decode(qjl, w, Q, S_in, S_out, oidx, cache_np: dict, N: int, *, nsplit=0, with_scores=True, V_f32=None):
+    """Upload an oracle-built cache, run the library decode, return (out, scores) as numpy."""
+    torch = torch_mod()
+    B, Hq, d = Q.shape
+    bits = torch.from_numpy(cache_np["bits"].view(np.int32)).cuda()
+    norms = torch.from_numpy(cache_np["norms"]).cuda()
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    scores = torch.full((B, Hq, max(N, 1)), float("nan"), dtype=torch.float32, device="cuda") if with_scores else None
+    kw = {}
+    if V_f32 is not None:
+        kw["V_f32"] = torch.from_numpy(np.ascontiguousarray(V_f32, dtype=np.float32)).cuda()
+    else:
+        kw["codes"] = torch.from_numpy(cache_np["codes"]).cuda()
+        kw["meta"] = torch.from_numpy(cache_np["meta"]).cuda()
+    qjl.decode_attention(to_dev(Q, w.dtype), to_dev(S_in, w.dtype), to_dev(S_out, w.dtype) if w.m_out else None,
+                         torch.from_numpy(oidx).cuda() if w.n_out else None, bits, norms, N, out,
+                         nbits=w.nbits, scores_dbg=scores, nsplit=nsplit, **kw)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), (scores.cpu().numpy()[:, :, :N] if with_scores else None)
+
+
+def check_decode(w, Q, S_in, S_out, oidx, cache_np, N, out_gpu, scores_gpu, units, V_f32=None, what=""):
+    """Compare sampled (b, hq) outputs (2e-3 max-abs) and scores (1e-3 of the estimator scale)."""
+    ref = oracle.decode_attention(Q, S_in, S_out, oidx, cache_np["bits"], cache_np["norms"], N,
+                                  codes=cache_np.get("codes"), meta=cache_np.get("meta"), V_f32=V_f32,
+                                  nbits=w.nbits, units=units)
+    worst_o, worst_s = 0.0, 0.0
+    g = w.Hq // w.Hkv
+    for b, hq in units:
+        h = hq // g
+        err = np.abs(out_gpu[b, hq] - ref["out"][b, hq]).max()
+        worst_o = max(worst_o, float(err))
+        assert err <= 2e-3, f"{what} out (b={b}, hq={hq}) max-abs {err:.3g} > 2e-3"
+        if scores_gpu is not None and N:
+            sq_in, sq_out = oracle.project_query(Q[b, hq], S_in, S_out, oidx[h] if oidx.size else [])
+            tol = score_tolerance(sq_in, sq_out, cache_np["norms"][b, h, :N], w.m, w.m_out)
+            ds = np.abs(scores_gpu[b, hq] - ref["scores"][b, hq])
+            ratio = float((ds / tol).max())
+            worst_s = max(worst_s, ratio)
+            assert ratio <= 1.0, f"{what} scores (b={b}, hq={hq}) exceed tolerance by x{ratio:.3g}"
+    log(f"  {what}: out max-abs {worst_o:.2e} (<= 2e-3); worst score error {worst_s:.2e} of tolerance")
+    return worst_o, worst_s

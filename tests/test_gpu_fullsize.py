@@ -1,0 +1,119 @@
+"""GPU <-> oracle parity at the full workload sizes, in the launch configuration the benchmark times.
+
+The GPU processes the whole workload; the oracle recomputes sampled units one by one:
+  * decode workloads: the cache is built by the library (prefill of N-1 tokens, then the one-token
+    append of the serving step); sampled (sequence, KV head) units are re-quantized by the oracle
+    and compared, then overwritten with the oracle's cache so that both sides attend over identical
+    inputs, and the outputs of every query head of those units are compared; the appended token is
+    compared for every unit;
+  * the prefill quantize stream: sampled (token, KV head) rows of the full output.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+from gpu_util import check_decode, compare_bits, compare_norms, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+qjl = pytest.importorskip("bit_kv_cache_qjl_amd")
+
+
+def _units(w, count, seed):
+    rng = np.random.default_rng(seed)
+    picks = {(0, 0), (w.B - 1, w.Hkv - 1)}
+    while len(picks) < count:
+        picks.add((int(rng.integers(w.B)), int(rng.integers(w.Hkv))))
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("name", ["llama2_7b_decode", "llama3_8b_gqa_decode", "llama31_70b_gqa_decode"])
+def test_full_size_decode_step(name):
+    w = si.WORKLOADS[name]
+    N = w.N
+    log(f"[full decode] {name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={N}: generating inputs")
+    oidx = si.outlier_channels(w)
+    S_in_np, S_out_np = si.jl_matrices(w)
+    Q_np = si.queries(w)
+    K = to_dev(si.keys(w, oidx), w.dtype)
+    V = to_dev(si.values(w), w.dtype)
+    S_in, S_out = to_dev(S_in_np, w.dtype), to_dev(S_out_np, w.dtype)
+    od = torch.from_numpy(oidx).cuda()
+    cache = qjl.alloc_cache(w.B, w.Hkv, N, w.m, w.m_out, w.nbits)
+    log("  prefill N-1 tokens, append the last one")
+    qjl.quantize_keys(K[:, : N - 1], S_in, S_out, od, cache.bits, cache.norms, t0=0)
+    qjl.quantize_values(V[:, : N - 1], w.nbits, cache.codes, cache.meta, t0=0)
+    qjl.quantize_keys(K[:, N - 1:], S_in, S_out, od, cache.bits, cache.norms, t0=N - 1)
+    qjl.quantize_values(V[:, N - 1:], w.nbits, cache.codes, cache.meta, t0=N - 1)
+    torch.cuda.synchronize()
+
+    # the appended token of every unit
+    last_k = K[:, N - 1:].float().cpu().numpy()
+    last_v = V[:, N - 1:].float().cpu().numpy()
+    rk = oracle.quantize_keys(last_k, S_in_np, S_out_np, oidx)
+    rv = oracle.quantize_values(last_v, w.nbits)
+    compare_bits(cache.bits[:, :, N - 1:].cpu().numpy().view(np.uint32), rk, "appended token", w.m + w.m_out)
+    compare_norms(cache.norms[:, :, N - 1:].cpu().numpy(), rk["norms"], "appended token")
+    np.testing.assert_array_equal(cache.codes[:, :, N - 1:].cpu().numpy(), rv["codes"])
+    np.testing.assert_array_equal(cache.meta[:, :, N - 1:].cpu().numpy().view(np.uint16), rv["meta"].view(np.uint16))
+
+    units = _units(w, 2, w.seed)
+    ref_cache = {}
+    for b, h in units:
+        log(f"  oracle unit b={b} h={h}")
+        kbh = si.key_slice(w, b, h, oidx)
+        assert np.array_equal(kbh, K[b, :, h].float().cpu().numpy()), "device keys differ from the generator"
+        r = oracle.quantize_key_vectors(kbh, S_in_np, S_out_np, oidx[h])
+        codes, meta = oracle.quantize_value_vectors(si.value_slice(w, b, h), w.nbits)
+        packed = oracle.pack_codes(codes, w.nbits)
+        compare_bits(cache.bits[b, h].cpu().numpy().view(np.uint32), {"bits": r["bits"], "near_zero": r["near_zero"]},
+                     f"unit ({b},{h}) bits", w.m + w.m_out)
+        compare_norms(cache.norms[b, h].cpu().numpy(), r["norms"], f"unit ({b},{h})")
+        np.testing.assert_array_equal(cache.codes[b, h].cpu().numpy(), packed)
+        np.testing.assert_array_equal(cache.meta[b, h].cpu().numpy().view(np.uint16), meta.view(np.uint16))
+        # identical decode inputs on both sides
+        cache.bits[b, h] = torch.from_numpy(r["bits"].view(np.int32)).cuda()
+        cache.norms[b, h] = torch.from_numpy(r["norms"]).cuda()
+        ref_cache[(b, h)] = (r["bits"], r["norms"], packed, meta)
+
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    scores = torch.empty((w.B, w.Hq, N), dtype=torch.float32, device="cuda")
+    log("  decode (library's own split choice)")
+    qjl.decode_attention(to_dev(Q_np, w.dtype), S_in, S_out, od, cache.bits, cache.norms, N, out,
+                         codes=cache.codes, meta=cache.meta, nbits=w.nbits, scores_dbg=scores)
+    torch.cuda.synchronize()
+    out_np = out.cpu().numpy()
+    g = w.g
+    ws = w.scaled(B=1, Hq=g, Hkv=1)
+    for (b, h), (rb, rn, rc, rm) in ref_cache.items():
+        sub = {"bits": rb[None, None], "norms": rn[None, None], "codes": rc[None, None], "meta": rm[None, None]}
+        sl = slice(h * g, (h + 1) * g)
+        sc = scores[b, sl].cpu().numpy()[None]
+        check_decode(ws, Q_np[b:b + 1, sl], S_in_np, S_out_np, oidx[h:h + 1], sub, N, out_np[b:b + 1, sl], sc,
+                     [(0, i) for i in range(g)], what=f"{name} unit ({b},{h})")
+
+
+def test_full_size_prefill_quantize():
+    w = si.WORKLOADS["prefill_quantize_64k"]
+    log(f"[full quantize] {w.name} T={w.N} Hkv={w.Hkv} m={w.m} m_out={w.m_out}")
+    oidx = si.outlier_channels(w)
+    S_in_np, S_out_np = si.jl_matrices(w)
+    K_np = si.keys(w, oidx)
+    K = to_dev(K_np, w.dtype)
+    cache = qjl.alloc_cache(w.B, w.Hkv, w.N, w.m, w.m_out, w.nbits)
+    qjl.quantize_keys(K, to_dev(S_in_np, w.dtype), to_dev(S_out_np, w.dtype), torch.from_numpy(oidx).cuda(),
+                      cache.bits, cache.norms)
+    torch.cuda.synchronize()
+    bits = cache.bits.cpu().numpy().view(np.uint32)
+    norms = cache.norms.cpu().numpy()
+    rng = np.random.default_rng(3)
+    for h in range(w.Hkv):
+        ts = np.sort(rng.choice(w.N, size=512, replace=False))
+        ts[0], ts[-1] = 0, w.N - 1
+        r = oracle.quantize_key_vectors(K_np[0, ts, h, :], S_in_np, S_out_np, oidx[h])
+        compare_bits(bits[0, h, ts], r, f"head {h} sampled rows", w.m + w.m_out)
+        compare_norms(norms[0, h, ts], r["norms"], f"head {h}")

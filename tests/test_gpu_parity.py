@@ -1,0 +1,204 @@
+"""GPU <-> oracle parity at sizes the oracle finishes in seconds (several tiles plus a ragged tail).
+
+Bar (BASELINE the benchmark spec): sign bits and value codes bit-exact, except sign bits whose projection
+magnitude is below 1e-5 |k| (counted and reported); norms within one fp16 ulp; scores within 1e-3 of
+the estimator's magnitude scale; attention outputs within 2e-3 max-abs.  Decode parity feeds both
+sides the same oracle-built cache.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+from gpu_util import (bits_np, check_decode, compare_bits, compare_norms, gpu_quantize_keys, inputs, log,
+                      run_decode, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+qjl = pytest.importorskip("bit_kv_cache_qjl_amd")
+
+W = si.WORKLOADS
+
+# scaled-down copies of every workload: same recipe and seed, small B / heads / context, ragged T
+SCALED = {
+    "tiny_fp32": W["tiny_fp32"],
+    "llama2_7b_decode": W["llama2_7b_decode"].scaled(B=2, Hq=3, Hkv=3, N=1500),
+    "llama3_8b_gqa_decode": W["llama3_8b_gqa_decode"].scaled(B=2, Hq=8, Hkv=2, N=1100),
+    "prefill_quantize_64k": W["prefill_quantize_64k"].scaled(B=1, Hq=2, Hkv=2, N=1000),
+    "llama31_70b_gqa_decode": W["llama31_70b_gqa_decode"].scaled(B=1, Hq=16, Hkv=2, N=777),
+}
+
+
+@pytest.mark.parametrize("name", list(SCALED))
+def test_quantize_keys_parity(name):
+    w = SCALED[name]
+    log(f"[quantize_keys] {name} B={w.B} T={w.N} Hkv={w.Hkv} m={w.m} m_out={w.m_out} n_out={w.n_out} {w.dtype}")
+    x = inputs(w)
+    cache = gpu_quantize_keys(qjl, w, x["K"], x["S_in"], x["S_out"], x["oidx"])
+    ref = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
+    compare_bits(bits_np(cache.bits), ref, name, w.m + w.m_out)
+    compare_norms(cache.norms.cpu().numpy(), ref["norms"], name)
+
+
+def test_quantize_keys_append_offset_and_strides():
+    """Write T tokens at t0 of a larger cache from a strided (non-contiguous) key view."""
+    w = SCALED["llama2_7b_decode"].scaled(N=70)
+    x = inputs(w)
+    big = np.zeros((w.B, w.N, 2 * w.Hkv, w.d), dtype=np.float32)
+    big[:, :, ::2, :] = x["K"]
+    Kdev = to_dev(big, w.dtype)[:, :, ::2, :]
+    assert not Kdev.is_contiguous()
+    t0, Ncap = 37, 37 + w.N + 11
+    log(f"[quantize_keys] strided view, t0={t0}, Ncap={Ncap}")
+    cache = gpu_quantize_keys(qjl, w, x["K"], x["S_in"], x["S_out"], x["oidx"], Ncap=Ncap, t0=t0, Kdev=Kdev)
+    ref = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
+    bits = bits_np(cache.bits)
+    compare_bits(bits[:, :, t0:t0 + w.N], ref, "append", w.m + w.m_out)
+    compare_norms(cache.norms.cpu().numpy()[:, :, t0:t0 + w.N], ref["norms"], "append")
+    assert not bits[:, :, :t0].any() and not bits[:, :, t0 + w.N:].any(), "wrote outside [t0, t0 + T)"
+    assert not cache.norms[:, :, :t0].any() and not cache.norms[:, :, t0 + w.N:].any()
+
+
+def test_quantize_keys_special_keys():
+    """Zero keys (every projection 0 -> all bits 1, norms 0), keys living only on the outlier
+    channels (inlier bits all 1), and negated keys (complemented bits away from near-zero)."""
+    w = SCALED["llama31_70b_gqa_decode"].scaled(N=64)
+    x = inputs(w)
+    K = x["K"].copy()
+    K[:, :16] = 0.0
+    only_out = np.zeros_like(K[:, 16:32])
+    for h in range(w.Hkv):
+        only_out[:, :, h, x["oidx"][h]] = K[:, 16:32, h, x["oidx"][h]]
+    K[:, 16:32] = only_out
+    K[:, 48:64] = -K[:, 32:48]
+    log("[quantize_keys] special keys")
+    cache = gpu_quantize_keys(qjl, w, K, x["S_in"], x["S_out"], x["oidx"])
+    bits = bits_np(cache.bits)
+    norms = cache.norms.cpu().numpy()
+    assert np.all(bits[:, :, :16] == 0xFFFFFFFF) and np.all(norms[:, :, :16] == 0)
+    assert np.all(bits[:, :, 16:32, : w.m // 32] == 0xFFFFFFFF) and np.all(norms[:, :, 16:32, 0] == 0)
+    ref = oracle.quantize_keys(K, x["S_in"], x["S_out"], x["oidx"])
+    compare_bits(bits, ref, "special", w.m + w.m_out)
+    nz = ~(ref["near_zero"][:, :, 32:48] | ref["near_zero"][:, :, 48:64])
+    a = oracle.unpack_bits(bits[:, :, 32:48], w.m + w.m_out)
+    b = oracle.unpack_bits(bits[:, :, 48:64], w.m + w.m_out)
+    assert np.all(a[nz] != b[nz])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("nbits", [2, 3, 4])
+def test_quantize_values_parity(dtype, nbits):
+    w = SCALED["llama3_8b_gqa_decode"].scaled(dtype=dtype, nbits=nbits, N=333)
+    log(f"[quantize_values] {dtype} nbits={nbits} B={w.B} T={w.N} Hkv={w.Hkv}")
+    V = si.values(w)
+    V[0, 0, 0, :] = 1.25                       # constant vector: step 0, all codes 0
+    V[0, 1, 0, :5] = [3.0, -3.0, 0.0, 1.0, 2.0]
+    torch_v = to_dev(V, dtype)
+    cache = qjl.alloc_cache(w.B, w.Hkv, w.N + 3, w.m, w.m_out, nbits)
+    qjl.quantize_values(torch_v, nbits, cache.codes, cache.meta, t0=3)
+    torch.cuda.synchronize()
+    ref = oracle.quantize_values(V, nbits)
+    codes = cache.codes.cpu().numpy()[:, :, 3:]
+    meta = cache.meta.cpu().numpy()[:, :, 3:]
+    np.testing.assert_array_equal(meta.view(np.uint16), ref["meta"].view(np.uint16))
+    np.testing.assert_array_equal(codes, ref["codes"])
+    assert not cache.codes[:, :, :3].any()
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama2_7b_decode", "llama3_8b_gqa_decode", "llama31_70b_gqa_decode"])
+@pytest.mark.parametrize("nsplit", [0, 1, 3])
+def test_decode_parity(name, nsplit):
+    w = SCALED[name]
+    log(f"[decode] {name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} nsplit={nsplit}")
+    x = inputs(w)
+    kq = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
+    cache = {"bits": kq["bits"], "norms": kq["norms"]}
+    V_f32 = None
+    if w.vmode == "codes":
+        cache.update(oracle.quantize_values(x["V"], w.nbits))
+    else:
+        V_f32 = np.ascontiguousarray(x["V"].transpose(0, 2, 1, 3))       # [B, Hkv, N, d]
+    out, scores = run_decode(qjl, w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, w.N, nsplit=nsplit, V_f32=V_f32)
+    units = [(b, hq) for b in range(w.B) for hq in range(w.Hq)]
+    check_decode(w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, w.N, out, scores, units, V_f32=V_f32, what=name)
+
+
+@pytest.mark.parametrize("N", [0, 1, 511, 513])
+def test_decode_edge_lengths(N):
+    w = SCALED["llama3_8b_gqa_decode"].scaled(N=600)
+    log(f"[decode] edge N={N}")
+    x = inputs(w)
+    kq = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
+    cache = {"bits": kq["bits"], "norms": kq["norms"], **oracle.quantize_values(x["V"], w.nbits)}
+    out, scores = run_decode(qjl, w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, N, nsplit=0)
+    if N == 0:
+        assert np.all(out == 0)
+        return
+    units = [(b, hq) for b in range(w.B) for hq in range(w.Hq)]
+    check_decode(w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, N, out, scores, units, what=f"N={N}")
+    if N == 1:
+        vhat = oracle.dequantize_value_vectors(oracle.unpack_codes(cache["codes"][:, :, :1], 2, w.d), cache["meta"][:, :, :1])
+        g = w.Hq // w.Hkv
+        for b in range(w.B):
+            for hq in range(w.Hq):
+                np.testing.assert_allclose(out[b, hq], vhat[b, hq // g, 0], atol=2e-3)
+
+
+def test_decode_many_splits_and_equal_scores():
+    """More splits than tiles (empty chunks) and a cache whose keys are all equal (uniform softmax:
+    the output is the mean of the dequantized values)."""
+    w = SCALED["llama2_7b_decode"].scaled(N=700)
+    x = inputs(w)
+    K = np.repeat(x["K"][:, :1], w.N, axis=1)
+    kq = oracle.quantize_keys(K, x["S_in"], x["S_out"], x["oidx"])
+    cache = {"bits": kq["bits"], "norms": kq["norms"], **oracle.quantize_values(x["V"], w.nbits)}
+    log("[decode] equal keys, nsplit=40")
+    out, scores = run_decode(qjl, w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, w.N, nsplit=40)
+    vhat = oracle.dequantize_value_vectors(oracle.unpack_codes(cache["codes"], 2, w.d), cache["meta"])
+    for b in range(w.B):
+        for hq in range(w.Hq):
+            np.testing.assert_allclose(out[b, hq], vhat[b, hq].mean(axis=0), atol=2e-3)
+            assert np.all(scores[b, hq] == scores[b, hq, 0])
+
+
+def test_decode_step_append_then_attend():
+    """The serving step: quantize the new token's key and value into slot N-1 of a cache built by
+    prefill, then attend over all N tokens; compared with the oracle on the same inputs."""
+    w = SCALED["llama31_70b_gqa_decode"].scaled(N=900)
+    x = inputs(w)
+    N = w.N
+    log("[pipeline] prefill N-1 tokens, append 1, decode")
+    cache = qjl.alloc_cache(w.B, w.Hkv, N, w.m, w.m_out, w.nbits)
+    Kd, Vd = to_dev(x["K"], w.dtype), to_dev(x["V"], w.dtype)
+    S_in, S_out = to_dev(x["S_in"], w.dtype), to_dev(x["S_out"], w.dtype)
+    oidx = torch.from_numpy(x["oidx"]).cuda()
+    qjl.quantize_keys(Kd[:, : N - 1], S_in, S_out, oidx, cache.bits, cache.norms, t0=0)
+    qjl.quantize_values(Vd[:, : N - 1], w.nbits, cache.codes, cache.meta, t0=0)
+    qjl.quantize_keys(Kd[:, N - 1:], S_in, S_out, oidx, cache.bits, cache.norms, t0=N - 1)
+    qjl.quantize_values(Vd[:, N - 1:], w.nbits, cache.codes, cache.meta, t0=N - 1)
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    qjl.decode_attention(to_dev(x["Q"], w.dtype), S_in, S_out, oidx, cache.bits, cache.norms, N, out,
+                         codes=cache.codes, meta=cache.meta, nbits=w.nbits)
+    torch.cuda.synchronize()
+    kq = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
+    vq = oracle.quantize_values(x["V"], w.nbits)
+    compare_bits(bits_np(cache.bits), kq, "pipeline", w.m + w.m_out)
+    np.testing.assert_array_equal(cache.codes.cpu().numpy(), vq["codes"])
+    # decode input must be identical on both sides: use the oracle cache where a near-zero bit differs
+    gbits = bits_np(cache.bits)
+    if np.array_equal(gbits, kq["bits"]) and np.array_equal(cache.norms.cpu().numpy().view(np.uint16),
+                                                             kq["norms"].view(np.uint16)):
+        cache_np = {"bits": kq["bits"], "norms": kq["norms"], **vq}
+        units = [(b, hq) for b in range(w.B) for hq in range(w.Hq)]
+        check_decode(w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache_np, N, out.cpu().numpy(), None, units,
+                     what="pipeline")
+    else:
+        log("  pipeline: GPU cache differs from the oracle's in near-zero bits or a norm ulp; "
+            "decode parity re-run on the oracle cache")
+        cache_np = {"bits": kq["bits"], "norms": kq["norms"], **vq}
+        o2, s2 = run_decode(qjl, w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache_np, N)
+        units = [(b, hq) for b in range(w.B) for hq in range(w.Hq)]
+        check_decode(w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache_np, N, o2, s2, units, what="pipeline")
