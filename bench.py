@@ -30,7 +30,7 @@ HBM_PEAK_GBS = 8000.0              # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0     # MI355X dense bf16
 BYTES_PER_TOKEN_HEAD = 104          # 64 B signs + 4 B norms + 32 B codes + 4 B (min, step)
 DECODE_SOURCE = os.path.join(ROOT, "bit_kv_cache_qjl_amd", "csrc", "qjl_decode.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama2_7b_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_{}_traffic.json")
 
 
 def log(msg: str) -> None:
@@ -42,15 +42,63 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(bytes_alg: float):
+def measured_traffic(workload: str):
     """HBM bytes per decode launch from committed rocprofv3 counters, if they match this source."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILE.format(workload)
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         t = json.load(f)
     if t.get("decode_source_sha256_16") != source_hash(DECODE_SOURCE):
         return None
     return t.get("bytes_per_launch")
+
+
+CALIB_BYTES = 1 << 30               # plain copy kernel used to scale FETCH_SIZE / WRITE_SIZE
+
+
+def _counter_rows(path: str):
+    import csv
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            yield row
+
+
+def _per_dispatch(path: str, counter: str, name_part: str) -> list[float]:
+    """Counter value (KiB) of every dispatch whose kernel name contains name_part."""
+    acc: dict[str, float] = {}
+    for row in _counter_rows(path):
+        if row.get("Counter_Name") != counter or name_part not in row.get("Kernel_Name", ""):
+            continue
+        key = row.get("Dispatch_Id") or row.get("Correlation_Id")
+        acc[key] = acc.get(key, 0.0) + float(row["Counter_Value"])
+    return list(acc.values())
+
+
+def write_traffic(fetch_csv: str, write_csv: str, workload: str) -> int:
+    """HBM bytes per decode launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the decode kernel,
+    each scaled by what the same counter reads for the plain copy of CALIB_BYTES bytes."""
+    import statistics
+    copy_f = _per_dispatch(fetch_csv, "FETCH_SIZE", "copy")
+    copy_w = _per_dispatch(write_csv, "WRITE_SIZE", "copy")
+    big_f = max(copy_f)
+    big_w = max(copy_w)
+    kf = CALIB_BYTES / (big_f * 1024.0)
+    kw = CALIB_BYTES / (big_w * 1024.0)
+    dec_f = statistics.mean(_per_dispatch(fetch_csv, "FETCH_SIZE", "decode_kernel"))
+    dec_w = statistics.mean(_per_dispatch(write_csv, "WRITE_SIZE", "decode_kernel"))
+    w = si.WORKLOADS[workload]
+    rec = {"workload": workload, "decode_source_sha256_16": source_hash(DECODE_SOURCE),
+           "fetch_kib_per_launch": dec_f, "write_kib_per_launch": dec_w,
+           "copy_fetch_kib": big_f, "copy_write_kib": big_w, "copy_bytes": CALIB_BYTES,
+           "read_scale": kf, "write_scale": kw,
+           "bytes_per_launch": dec_f * 1024.0 * kf + dec_w * 1024.0 * kw,
+           "algorithmic_bytes": float(BYTES_PER_TOKEN_HEAD) * w.B * w.Hkv * w.N}
+    out = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+    return 0
 
 
 def cpu_baseline(w: si.Workload, budget_s: float) -> dict:
@@ -133,7 +181,15 @@ def main() -> int:
                     choices=["llama2_7b_decode", "llama3_8b_gqa_decode", "llama31_70b_gqa_decode"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--no-quantize", action="store_true", help="skip the prefill quantize measurement")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help=f"run one plain {CALIB_BYTES >> 20} MiB device copy first (the reference kernel that "
+                         "scales the HBM byte counters of a --pmc profile)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a --calibration-copy "
+                         "run into the traffic record under profiles/, then exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        return write_traffic(*args.traffic_from, args.workload)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "sharding across GPUs is described in the design notes but not built", file=sys.stderr)
@@ -159,6 +215,11 @@ def main() -> int:
     k_new, v_new = K[:, N - 1:], V[:, N - 1:]
     out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
     ws = torch.empty(qjl.decode_workspace_size(w.B, w.Hq, w.Hkv, N, w.m, w.m_out), dtype=torch.uint8, device="cuda")
+    if args.calibration_copy:
+        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        del src, dst
     torch.cuda.synchronize()
 
     def step():
@@ -199,7 +260,7 @@ def main() -> int:
                    "m_out": w.m_out, "n_out": w.n_out, "outlier_scale": w.outlier_scale, "value_bits": w.nbits,
                    "step": "append 1 token per sequence (key sketch + value codes) + decode attention over N"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(bytes_alg),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
                      "kernel": "decode", "kernel_ms": dec_s * 1e3, "algorithmic_bytes": bytes_alg},
         "kernel_ms_per_launch": {k: v[1] / max(v[0], 1) for k, v in kernels.items()},
     }

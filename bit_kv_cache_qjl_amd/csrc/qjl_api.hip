@@ -252,6 +252,8 @@ int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, 
         return fail(QJL_ERR_INVALID_ARG, "bad sizes B=%d Hq=%d Hkv=%d N=%lld Ncap=%lld", B, Hq, Hkv, (long long)N, (long long)Ncap);
     if (Hq % Hkv) return fail(QJL_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
     if (N > Ncap) return fail(QJL_ERR_INVALID_ARG, "N=%lld exceeds Ncap=%lld", (long long)N, (long long)Ncap);
+    if (Ncap * (int64_t)((m + m_out) / 32) >= ((int64_t)1 << 30) || Ncap * (int64_t)qjl::kD >= ((int64_t)1 << 30))
+        return fail(QJL_ERR_UNSUPPORTED, "Ncap=%lld too large for one (sequence, KV head) row (32-bit offsets)", (long long)Ncap);
     int st = check_sketch_shape(d, m, m_out, n_out);
     if (st) return st;
     if (!qjl::decode_shape_supported(m, m_out))

@@ -88,6 +88,17 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
     return r;
 }
 
+// Byte k of x, times 4 (a table offset in bytes) in one SDWA instruction.
+template <int K>
+__device__ __forceinline__ uint32_t byte_x4(uint32_t x) {
+    uint32_t r;
+    if (K == 0) asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(x));
+    if (K == 1) asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(x));
+    if (K == 2) asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(x));
+    if (K == 3) asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(x));
+    return r;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -100,15 +111,61 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+constexpr int kSlab = 64;                    // tokens per wave step
+
+// Raw buffer resource over [base, base + bytes): loads at or past the end return zero, which is how
+// the kernels treat the ragged end of a chunk (no branches, no clamped addresses).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Token data of one wave step.
+template <int WB, int VM>
+struct Slab {
+    uint32_t w[WB];      // sign words of this lane's token
+    uint32_t nrm;        // (|k_in|, |k_out|) fp16 pair
+    uint32_t mt;         // (min, step) fp16 pair
+    uint32_t xv[8];      // value role: code dwords of this lane's token pairs
+};
+
+template <int WB, int VM>
+__device__ __forceinline__ void load_slab(Slab<WB, VM>& sl, __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rn,
+                                          __amdgpu_buffer_rsrc_t rm, __amdgpu_buffer_rsrc_t rc, int s0, int lane,
+                                          int jv, int pg) {
+    const int t = s0 + lane;
+#pragma unroll
+    for (int q = 0; q < WB / 4; ++q) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rb, (t * WB + 4 * q) * 4, 0, 0);
+        sl.w[4 * q] = x[0]; sl.w[4 * q + 1] = x[1]; sl.w[4 * q + 2] = x[2]; sl.w[4 * q + 3] = x[3];
+    }
+    sl.nrm = __builtin_amdgcn_raw_buffer_load_b32(rn, t * 4, 0, 0);
+    if (VM == 0) {
+        sl.mt = __builtin_amdgcn_raw_buffer_load_b32(rm, t * 4, 0, 0);
+#pragma unroll
+        for (int pass = 0; pass < 4; ++pass) {
+            const int t1 = s0 + 2 * (pg + 8 * pass);
+            sl.xv[2 * pass] = __builtin_amdgcn_raw_buffer_load_b32(rc, (t1 * 8 + jv) * 4, 0, 0);
+            sl.xv[2 * pass + 1] = __builtin_amdgcn_raw_buffer_load_b32(rc, ((t1 + 1) * 8 + jv) * 4, 0, 0);
+        }
+    } else {
+        sl.mt = 0u;
+    }
+}
+
 // VM = 0: 2-bit codes + (min, step) meta;  VM = 1: fp32 values.
+//
+// Each wave is an independent online-softmax stream over 64-token slabs (slab i of the chunk goes
+// to wave i mod 8); the waves share only the read-only byte tables, so there is no workgroup
+// barrier inside the token loop.  The eight partial (max, sum, output) states are merged once at
+// the end of the chunk.
 template <int WIN, int WOUT, int VM>
-__global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a, int groups) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel(DecodeArgs a, int groups) {
     constexpr int WB = WIN + WOUT;
     constexpr int P = 4 * WB;                    // byte positions = tables
-    extern __shared__ __attribute__((aligned(16))) float lds[];
-    float* lut = lds;                            // [P][256]
+    constexpr int LUT_FLOATS = P * 256 > (kThreads / 8) * kD ? P * 256 : (kThreads / 8) * kD;
+    __shared__ __attribute__((aligned(16))) float lut[LUT_FLOATS];   // [P][256]; reused for the final reduction
     __shared__ float sq_s[8 * P];
-    __shared__ __attribute__((aligned(16))) float wts[kThreads];   // fp16 pairs (VM 0) or fp32 weights (VM 1)
+    __shared__ __attribute__((aligned(16))) float wts[kWaves][kSlab];   // per-wave weights of one slab
     __shared__ float red[kWaves][4];
 
     const int tid = threadIdx.x;
@@ -130,10 +187,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a, int g
     const int hq = h * a.g + hg;
     const int bhq = b * a.Hq + hq;
 
-    const int64_t t_begin = (int64_t)split * a.chunk;
-    const int64_t t_end = min(a.N, t_begin + a.chunk);
+    // token range of this chunk, as 32-bit offsets inside the (sequence, KV head) rows
+    const int t_begin = (int)((int64_t)split * a.chunk);
+    const int t_end = (int)min(a.N, (int64_t)t_begin + a.chunk);
 
-    // ---- byte tables of the projected query
+    // ---- byte tables of the projected query: entry [p][beta] = sum_i (+-) Sq[8p + i]
     for (int i = tid; i < 8 * P; i += kThreads) sq_s[i] = a.sq[(size_t)bhq * (8 * P) + i];
     __syncthreads();
     for (int idx = tid; idx < P * 256; idx += kThreads) {
@@ -148,104 +206,83 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a, int g
     }
     __syncthreads();
 
+    // the (sequence, KV head) rows, bounded at the end of this chunk
     const uint32_t* bits = a.bits + (size_t)unit * a.Ncap * WB;
     const uint32_t* norms = reinterpret_cast<const uint32_t*>(a.norms) + (size_t)unit * a.Ncap;
-    const uint32_t* meta = reinterpret_cast<const uint32_t*>(a.meta) + (size_t)unit * a.Ncap;
-    const uint32_t* codes = reinterpret_cast<const uint32_t*>(a.codes) + (size_t)unit * a.Ncap * 8;
-    const float* vf = a.V_f32 + (size_t)unit * a.Ncap * kD;
+    const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(bits, (uint32_t)t_end * WB * 4u);
+    const __amdgpu_buffer_rsrc_t rn = buffer_rsrc(norms, (uint32_t)t_end * 4u);
+    const __amdgpu_buffer_rsrc_t rm = VM == 0 ? buffer_rsrc(reinterpret_cast<const uint32_t*>(a.meta) + (size_t)unit * a.Ncap,
+                                                            (uint32_t)t_end * 4u) : rn;
+    const __amdgpu_buffer_rsrc_t rc = VM == 0 ? buffer_rsrc(a.codes + (size_t)unit * a.Ncap * 32, (uint32_t)t_end * 32u) : rn;
+    const float* vf = VM == 1 ? a.V_f32 + (size_t)unit * a.Ncap * kD : nullptr;
     float* sdbg = a.scores_dbg ? a.scores_dbg + (size_t)bhq * a.N : nullptr;
 
-    const int jv = tid & 7;          // value role: 16-channel slice
-    const int pg = tid >> 3;         // value role: token-pair group (0..63)
+    const int jv = lane & 7;         // value role: 16-channel slice
+    const int pg = lane >> 3;        // value role: token-pair group of the slab (0..7)
+    float* wl = wts[wave];
 
     float m_run = -INFINITY;
-    float l_t = 0.f, mn_t = 0.f, sw_t = 0.f;   // per-thread partial sums (score role)
+    float l_t = 0.f, mn_t = 0.f, sw_t = 0.f;   // per-lane partial sums (score role)
     float acc[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) acc[c] = 0.f;
 
-    for (int64_t tile0 = t_begin; tile0 < t_end; tile0 += kThreads) {
-        const int64_t t = tile0 + tid;
+    const char* lut_b = reinterpret_cast<const char*>(lut);
+    for (int s0 = t_begin + kSlab * wave; s0 < t_end; s0 += kSlab * kWaves) {
+        Slab<WB, VM> cur;
+        load_slab<WB, VM>(cur, rb, rn, rm, rc, s0, lane, jv, pg);
+        const int t = s0 + lane;
         const bool valid = t < t_end;
 
-        // value operands of this thread's token pairs, issued early
-        uint32_t xv[8];
-        if (VM == 0) {
-#pragma unroll
-            for (int pass = 0; pass < 4; ++pass) {
-                const int64_t t1 = tile0 + 2 * (pg + 64 * pass);
-                xv[2 * pass] = t1 < t_end ? codes[t1 * 8 + jv] : 0u;
-                xv[2 * pass + 1] = t1 + 1 < t_end ? codes[(t1 + 1) * 8 + jv] : 0u;
-            }
-        }
-
-        // ---- scores (thread = token)
-        uint32_t wv[WB];
-        uint32_t nrm = 0, mt = 0;
-        if (valid) {
-            const uint4* src = reinterpret_cast<const uint4*>(bits + t * WB);
-#pragma unroll
-            for (int q = 0; q < WB / 4; ++q) {
-                const uint4 x = src[q];
-                wv[4 * q] = x.x; wv[4 * q + 1] = x.y; wv[4 * q + 2] = x.z; wv[4 * q + 3] = x.w;
-            }
-            nrm = norms[t];
-            if (VM == 0) mt = meta[t];
-        } else {
-#pragma unroll
-            for (int q = 0; q < WB; ++q) wv[q] = 0u;
-        }
+        // ---- score of this lane's token: one table read per byte of its sign words
         float s_in = 0.f, s_out = 0.f;
 #pragma unroll
         for (int w = 0; w < WB; ++w) {
-            const uint32_t x = wv[w];
-            float part = 0.f;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) part += lut[(4 * w + k) * 256 + ((x >> (8 * k)) & 0xFFu)];
+            const uint32_t x = cur.w[w];
+            const char* tb = lut_b + (4 * w) * 1024;
+            float part = *reinterpret_cast<const float*>(tb + byte_x4<0>(x));
+            part += *reinterpret_cast<const float*>(tb + 1024 + byte_x4<1>(x));
+            part += *reinterpret_cast<const float*>(tb + 2048 + byte_x4<2>(x));
+            part += *reinterpret_cast<const float*>(tb + 3072 + byte_x4<3>(x));
             if (w < WIN) s_in += part; else s_out += part;
         }
-        const float n_in = (float)__builtin_bit_cast(_Float16, (uint16_t)(nrm & 0xFFFFu));
-        const float n_out = (float)__builtin_bit_cast(_Float16, (uint16_t)(nrm >> 16));
+        const float n_in = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur.nrm & 0xFFFFu));
+        const float n_out = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur.nrm >> 16));
         const float score = WOUT ? fmaf(n_out, s_out, n_in * s_in) : n_in * s_in;
         if (sdbg && valid) sdbg[t] = score;
         const float z = valid ? score * a.z_scale : -INFINITY;
 
-        // ---- online softmax (block-wide max, log2 domain)
-        const float wm = wave_max(z);
-        if (lane == 0) red[wave][0] = wm;
-        __syncthreads();
-        float tmax = red[0][0];
-#pragma unroll
-        for (int i = 1; i < kWaves; ++i) tmax = fmaxf(tmax, red[i][0]);
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-        const float p = valid ? exp2f(z - m_new) : 0.f;
+        // ---- online softmax of this wave's stream (log2 domain)
+        const float m_new = fmaxf(m_run, wave_max(z));
+        // v_exp_f32 directly: weights below 2^-126 contribute nothing to the sums
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // m_new is finite: lane 0 of a slab is valid
+        const float p = valid ? __builtin_amdgcn_exp2f(z - m_new) : 0.f;
         m_run = m_new;
         l_t = fmaf(l_t, alpha, p);
         if (VM == 0) {
-            const float mn = (float)__builtin_bit_cast(_Float16, (uint16_t)(mt & 0xFFFFu));
-            const float step = (float)__builtin_bit_cast(_Float16, (uint16_t)(mt >> 16));
+            const float mn = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur.mt & 0xFFFFu));
+            const float step = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur.mt >> 16));
             const _Float16 w16 = (_Float16)(p * step);
             mn_t = fmaf(mn_t, alpha, p * mn);
             sw_t = fmaf(sw_t, alpha, (float)w16);
-            reinterpret_cast<_Float16*>(wts)[tid] = w16;
+            reinterpret_cast<_Float16*>(wl)[lane] = w16;
         } else {
-            wts[tid] = p;
+            wl[lane] = p;
         }
         if (alpha != 1.f) {
 #pragma unroll
             for (int c = 0; c < 16; ++c) acc[c] *= alpha;
         }
-        __syncthreads();
+        __builtin_amdgcn_wave_barrier();   // the weights written above are read by other lanes below
 
-        // ---- values (thread = 16-channel slice x token pairs)
+        // ---- values (lane = 16-channel slice x token pairs of the slab)
         if (VM == 0) {
             const uint32_t base = 0x3C003C00u, mask = 0x03000300u;
 #pragma unroll
             for (int pass = 0; pass < 4; ++pass) {
-                const int pr = pg + 64 * pass;
-                const half2_t wp = __builtin_bit_cast(half2_t, reinterpret_cast<const uint32_t*>(wts)[pr]);
-                const uint32_t x1 = xv[2 * pass], x2 = xv[2 * pass + 1];
+                const int pr = pg + 8 * pass;
+                const half2_t wp = __builtin_bit_cast(half2_t, reinterpret_cast<const uint32_t*>(wl)[pr]);
+                const uint32_t x1 = cur.xv[2 * pass], x2 = cur.xv[2 * pass + 1];
                 const uint32_t ylo = __builtin_amdgcn_perm(x2, x1, 0x05040100u);
                 const uint32_t yhi = __builtin_amdgcn_perm(x2, x1, 0x07060302u);
 #pragma unroll
@@ -261,36 +298,42 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a, int g
             for (int pass = 0; pass < 4; ++pass) {
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
-                    const int tl = 2 * (pg + 64 * pass) + e;
-                    const int64_t tt = tile0 + tl;
+                    const int tl = 2 * (pg + 8 * pass) + e;
+                    const int tt = s0 + tl;
                     if (tt < t_end) {
-                        const float w = wts[tl];
-                        const float4* src = reinterpret_cast<const float4*>(vf + tt * kD + 16 * jv);
+                        const float wgt = wl[tl];
+                        const float4* src = reinterpret_cast<const float4*>(vf + (size_t)tt * kD + 16 * jv);
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             const float4 x = src[q];
-                            acc[4 * q] = fmaf(w, x.x, acc[4 * q]);
-                            acc[4 * q + 1] = fmaf(w, x.y, acc[4 * q + 1]);
-                            acc[4 * q + 2] = fmaf(w, x.z, acc[4 * q + 2]);
-                            acc[4 * q + 3] = fmaf(w, x.w, acc[4 * q + 3]);
+                            acc[4 * q] = fmaf(wgt, x.x, acc[4 * q]);
+                            acc[4 * q + 1] = fmaf(wgt, x.y, acc[4 * q + 1]);
+                            acc[4 * q + 2] = fmaf(wgt, x.z, acc[4 * q + 2]);
+                            acc[4 * q + 3] = fmaf(wgt, x.w, acc[4 * q + 3]);
                         }
                     }
                 }
             }
         }
-        __syncthreads();   // wts and red are rewritten by the next tile
+        __builtin_amdgcn_wave_barrier();   // next slab rewrites the weights
     }
 
-    // ---- chunk partial: block sums, channel reduction over the 64 token-pair groups
-    const float l_sum = wave_sum(l_t), mn_sum = wave_sum(mn_t), sw_sum = wave_sum(sw_t);
+    // ---- merge the eight wave streams: common max, then sums and the channel reduction
+    if (lane == 0) red[wave][3] = m_run;
+    __syncthreads();
+    float m_blk = red[0][3];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) m_blk = fmaxf(m_blk, red[i][3]);
+    const float sc = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_blk);
+    const float l_sum = wave_sum(l_t) * sc, mn_sum = wave_sum(mn_t) * sc, sw_sum = wave_sum(sw_t) * sc;
     if (lane == 0) {
         red[wave][0] = l_sum;
         red[wave][1] = mn_sum;
         red[wave][2] = sw_sum;
     }
-    float* rbuf = lds;   // reuse the tables: [64 groups][128 channels]
+    float* rbuf = lut;   // [64 = wave x pair group][128 channels]
 #pragma unroll
-    for (int c = 0; c < 16; ++c) rbuf[pg * kD + 16 * jv + c] = acc[c];
+    for (int c = 0; c < 16; ++c) rbuf[(wave * 8 + pg) * kD + 16 * jv + c] = acc[c] * sc;
     __syncthreads();
     if (tid < kD) {
         float tot = 0.f;
@@ -306,7 +349,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a, int g
         float* dst = a.part + ((size_t)bhq * a.nsplit + split) * (kD + 2);
         dst[2 + tid] = o;
         if (tid == 0) {
-            dst[0] = m_run;
+            dst[0] = m_blk;
             dst[1] = L;
         }
     }
@@ -335,21 +378,11 @@ __global__ __launch_bounds__(kD) void combine_kernel(DecodeArgs a) {
 
 template <int WIN, int WOUT, int VM>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
-    // dynamic LDS: the byte tables, also reused for the final channel reduction [64][128] floats
-    size_t lut_bytes = (size_t)4 * (WIN + WOUT) * 256 * sizeof(float);
-    if (lut_bytes < (size_t)(kThreads / 8) * kD * sizeof(float)) lut_bytes = (size_t)(kThreads / 8) * kD * sizeof(float);
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<WIN, WOUT, VM>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lut_bytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
     const int groups = a.B * a.Hkv * a.nsplit;
     const int slots = (groups + 7) / 8;
     const unsigned nblocks = (unsigned)slots * 8u * (unsigned)a.g;
     timer_begin(TK_DECODE, s);
-    hipLaunchKernelGGL((decode_kernel<WIN, WOUT, VM>), dim3(nblocks), dim3(kThreads), lut_bytes, s, a, groups);
+    hipLaunchKernelGGL((decode_kernel<WIN, WOUT, VM>), dim3(nblocks), dim3(kThreads), 0, s, a, groups);
     timer_end(TK_DECODE, s);
     return hipGetLastError();
 }

@@ -58,11 +58,58 @@ __device__ __forceinline__ uint32_t pack_signs(const f32x16& acc, int lane) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Per-thread loader role: token tt of the chunk, channels 8*cg .. 8*cg+7.  Masks the outlier
+// channels of the 8 values, gathers them into the 16-wide outlier row, stores the masked values in
+// LDS and returns the two partial sums of squares.
+__device__ __forceinline__ void stage_chunk(uint4 kv, uint32_t omask, int tt, int cg, int n_out, const int* s_oidx,
+                                            uint16_t* kl, uint16_t* gl, float& ss_in, float& ss_out) {
+    const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+    uint32_t mw[4];
+    ss_in = 0.f;
+    ss_out = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = kw[q] & 0xFFFFu, hi = kw[q] >> 16;
+        const float flo = bf16_to_f32(lo), fhi = bf16_to_f32(hi);
+        const bool olo = (omask >> (2 * q)) & 1u, ohi = (omask >> (2 * q + 1)) & 1u;
+        if (olo) ss_out = fmaf(flo, flo, ss_out); else ss_in = fmaf(flo, flo, ss_in);
+        if (ohi) ss_out = fmaf(fhi, fhi, ss_out); else ss_in = fmaf(fhi, fhi, ss_in);
+        mw[q] = (olo ? 0u : lo) | ((ohi ? 0u : hi) << 16);
+    }
+    if (omask) {
+        for (int i = 0; i < n_out; ++i) {
+            const int c = s_oidx[i];
+            if ((c >> 3) == cg) {
+                const int e = c & 7;
+                gl[tt * kGRow + i] = (uint16_t)((kw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+            }
+        }
+    }
+    *reinterpret_cast<uint4*>(kl + tt * kKRow + 8 * cg) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) {
+        ss_in += __shfl_xor(ss_in, o);
+        ss_out += __shfl_xor(ss_out, o);
+    }
+}
+
+__device__ __forceinline__ uint32_t norm_pair(float ss_in, float ss_out) {
+    const _Float16 ni = (_Float16)sqrtf(ss_in);
+    const _Float16 no = (_Float16)sqrtf(ss_out);
+    return (uint32_t)__builtin_bit_cast(uint16_t, ni) | ((uint32_t)__builtin_bit_cast(uint16_t, no) << 16);
+}
+
+// Waves per SIMD the register budget must allow: two workgroups per CU for up to 512 inlier
+// projections (TPW <= 2), one for more.
 template <int TPW>
-__global__ __launch_bounds__(kThreads, 1) void quantize_keys_bf16_kernel(KeyQuantArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t kl[kTok * kKRow];
-    __shared__ __attribute__((aligned(16))) uint16_t gl[kTok * kGRow];
-    __shared__ uint32_t ol[kTok * (kMaxBits / 32 + 1)];
+struct QKOccupancy { static constexpr int waves = TPW <= 2 ? 4 : 2; };
+
+template <int TPW>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QKOccupancy<TPW>::waves)))
+void quantize_keys_bf16_kernel(KeyQuantArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t kl[2][kTok * kKRow];
+    __shared__ __attribute__((aligned(16))) uint16_t gl[2][kTok * kGRow];
+    __shared__ uint32_t ol[2][kTok * (kMaxBits / 32 + 1)];
     __shared__ int s_oidx[kMaxOutliers];
 
     const int tid = threadIdx.x;
@@ -79,10 +126,9 @@ __global__ __launch_bounds__(kThreads, 1) void quantize_keys_bf16_kernel(KeyQuan
     const int orow = W + 1;
 
     if (tid < n_out) s_oidx[tid] = a.oidx[h * n_out + tid] & (kD - 1);   // never index outside a row
-    for (int i = tid; i < kTok * kGRow / 2; i += kThreads) reinterpret_cast<uint32_t*>(gl)[i] = 0u;
+    for (int i = tid; i < 2 * kTok * kGRow / 2; i += kThreads) reinterpret_cast<uint32_t*>(&gl[0][0])[i] = 0u;
     __syncthreads();
 
-    // loader role: token tt of the chunk, channels 8*cg .. 8*cg+7
     const int tt = tid >> 4;
     const int cg = tid & 15;
     uint32_t omask = 0;
@@ -91,7 +137,15 @@ __global__ __launch_bounds__(kThreads, 1) void quantize_keys_bf16_kernel(KeyQuan
         if ((c >> 3) == cg) omask |= 1u << (c & 7);
     }
 
-    // stationary JL fragments of this wave
+    const uint16_t* K = static_cast<const uint16_t*>(a.K);
+    const int64_t head_row0 = ((int64_t)b * a.Hkv + h) * a.Ncap + a.t0;
+    const uint16_t* krow = K + b * a.sKb + h * a.sKh + 8 * cg;
+    uint32_t* norms32 = reinterpret_cast<uint32_t*>(a.norms);
+
+    // first chunk in flight while the stationary JL fragments load
+    uint4 kv = make_uint4(0u, 0u, 0u, 0u);
+    if (t_begin + tt < t_end) kv = *reinterpret_cast<const uint4*>(krow + (t_begin + tt) * a.sKt);
+
     const uint16_t* Sin = static_cast<const uint16_t*>(a.S_in);
     const uint16_t* Sout = static_cast<const uint16_t*>(a.S_out);
     const int prow = tile_row(lane & 31);
@@ -122,85 +176,66 @@ __global__ __launch_bounds__(kThreads, 1) void quantize_keys_bf16_kernel(KeyQuan
         sout_frag[i] = make_uint4(g[0], g[1], g[2], g[3]);
     }
 
-    const uint16_t* K = static_cast<const uint16_t*>(a.K);
-    const int64_t head_row0 = ((int64_t)b * a.Hkv + h) * a.Ncap + a.t0;
+    {
+        float ss_in, ss_out;
+        stage_chunk(kv, omask, tt, cg, n_out, s_oidx, kl[0], gl[0], ss_in, ss_out);
+        if (cg == 0 && t_begin + tt < t_end) norms32[head_row0 + t_begin + tt] = norm_pair(ss_in, ss_out);
+    }
+    __syncthreads();
 
+    int buf = 0;
     for (int64_t c0 = t_begin; c0 < t_end; c0 += kTok) {
         const int nvalid = (int)min((int64_t)kTok, t_end - c0);
+        const int64_t cn = c0 + kTok;
 
-        // ---- stage the chunk: mask, gather outlier channels, sums of squares
-        uint4 kv = make_uint4(0u, 0u, 0u, 0u);
-        if (tt < nvalid)
-            kv = *reinterpret_cast<const uint4*>(K + b * a.sKb + (c0 + tt) * a.sKt + h * a.sKh + 8 * cg);
-        uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
-        float ss_in = 0.f, ss_out = 0.f;
-        uint32_t mw[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t lo = kw[q] & 0xFFFFu, hi = kw[q] >> 16;
-            const float flo = bf16_to_f32(lo), fhi = bf16_to_f32(hi);
-            const bool olo = (omask >> (2 * q)) & 1u, ohi = (omask >> (2 * q + 1)) & 1u;
-            if (olo) ss_out = fmaf(flo, flo, ss_out); else ss_in = fmaf(flo, flo, ss_in);
-            if (ohi) ss_out = fmaf(fhi, fhi, ss_out); else ss_in = fmaf(fhi, fhi, ss_in);
-            mw[q] = (olo ? 0u : lo) | ((ohi ? 0u : hi) << 16);
-        }
-        if (omask) {
-            for (int i = 0; i < n_out; ++i) {
-                const int c = s_oidx[i];
-                if ((c >> 3) == cg) {
-                    const int e = c & 7;
-                    gl[tt * kGRow + i] = (uint16_t)((kw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-                }
-            }
-        }
-        *reinterpret_cast<uint4*>(kl + tt * kKRow + 8 * cg) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) {
-            ss_in += __shfl_xor(ss_in, o);
-            ss_out += __shfl_xor(ss_out, o);
-        }
-        if (cg == 0 && tt < nvalid) {
-            const _Float16 ni = (_Float16)sqrtf(ss_in);
-            const _Float16 no = (_Float16)sqrtf(ss_out);
-            const uint32_t packed = (uint32_t)__builtin_bit_cast(uint16_t, ni) |
-                                    ((uint32_t)__builtin_bit_cast(uint16_t, no) << 16);
-            reinterpret_cast<uint32_t*>(a.norms)[head_row0 + c0 + tt] = packed;
-        }
-        __syncthreads();
+        // next chunk's keys in flight during this chunk's matrix work
+        uint4 kvn = make_uint4(0u, 0u, 0u, 0u);
+        if (cn + tt < t_end) kvn = *reinterpret_cast<const uint4*>(krow + (cn + tt) * a.sKt);
 
-        // ---- projections on the matrix cores, signs packed in registers
-        uint4 bfrag[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-            bfrag[s] = *reinterpret_cast<const uint4*>(kl + (lane & 31) * kKRow + 16 * s + khalf);
-        const uint4 gfrag = *reinterpret_cast<const uint4*>(gl + (lane & 31) * kGRow + khalf);
+        // ---- projections on the matrix cores; signs packed in registers
+        const uint16_t* klb = kl[buf] + (lane & 31) * kKRow + khalf;
+        uint32_t* olb = ol[buf];
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const int j = wave + kWaves * i;
             if (j < Win) {
                 f32x16 acc = {};
 #pragma unroll
-                for (int s = 0; s < 8; ++s)
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sin_frag[i][s]), as_bf16x8(bfrag[s]),
-                                                                  acc, 0, 0, 0);
+                for (int s = 0; s < 8; ++s) {
+                    const uint4 bf = *reinterpret_cast<const uint4*>(klb + 16 * s);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sin_frag[i][s]), as_bf16x8(bf), acc, 0, 0, 0);
+                }
                 const uint32_t w = pack_signs(acc, lane);
-                if (lane < 32) ol[lane * orow + j] = w;
+                if (lane < 32) olb[lane * orow + j] = w;
             }
+        }
+        const uint4 gfrag = *reinterpret_cast<const uint4*>(gl[buf] + (lane & 31) * kGRow + khalf);
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int j = wave + kWaves * i;
             if (j < Wout) {
-                f32x16 acc = {};
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sout_frag[i]), as_bf16x8(gfrag), acc, 0, 0, 0);
-                const uint32_t w = pack_signs(acc, lane);
-                if (lane < 32) ol[lane * orow + Win + j] = w;
+                f32x16 ao = {};
+                ao = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sout_frag[i]), as_bf16x8(gfrag), ao, 0, 0, 0);
+                const uint32_t w = pack_signs(ao, lane);
+                if (lane < 32) olb[lane * orow + Win + j] = w;
             }
+        }
+
+        // ---- stage the next chunk into the other buffer
+        if (cn < t_end) {
+            float ss_in, ss_out;
+            stage_chunk(kvn, omask, tt, cg, n_out, s_oidx, kl[buf ^ 1], gl[buf ^ 1], ss_in, ss_out);
+            if (cg == 0 && cn + tt < t_end) norms32[head_row0 + cn + tt] = norm_pair(ss_in, ss_out);
         }
         __syncthreads();
 
-        // ---- coalesced store of the packed words of the chunk
+        // ---- coalesced store of this chunk's packed words
         uint32_t* dst = a.bits + (head_row0 + c0) * W;
         for (int i = tid; i < nvalid * W; i += kThreads) {
             const int tok = i / W;
-            dst[i] = ol[tok * orow + (i - tok * W)];
+            dst[i] = olb[tok * orow + (i - tok * W)];
         }
+        buf ^= 1;
     }
 }
 
