@@ -54,6 +54,7 @@ def measured_traffic(workload: str):
     return t.get("bytes_per_launch")
 
 
+KERNELS = ("decode", "quantize_keys", "quantize_values", "query_project", "combine")
 CALIB_BYTES = 1 << 30               # plain copy kernel used to scale FETCH_SIZE / WRITE_SIZE
 
 
@@ -233,7 +234,7 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
     qjl.timer_enable(True)
-    for k in ("decode", "quantize_keys", "quantize_values", "query_project", "combine"):
+    for k in KERNELS:
         qjl.timer_read(k)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -241,7 +242,7 @@ def main() -> int:
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    kernels = {k: qjl.timer_read(k) for k in ("decode", "quantize_keys", "quantize_values", "query_project", "combine")}
+    kernels = {k: qjl.timer_read(k) for k in KERNELS}
     qjl.timer_enable(False)
     ms_per_step = elapsed / args.steps * 1e3
     keys_scored = w.B * w.Hq * N

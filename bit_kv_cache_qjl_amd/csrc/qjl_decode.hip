@@ -9,19 +9,20 @@
 // Kernels
 //   qproj   one workgroup per (sequence, query head): Sq = S q (fp32) pre-multiplied by
 //           sqrt(pi/2)/m (inlier part) and sqrt(pi/2)/m_out (outlier part).
-//   decode  one workgroup (8 waves, 512 threads) per (sequence, KV head, query head, context chunk).
-//           The projected query is expanded in LDS into byte tables: entry [p][beta] is the signed
-//           sum of the 8 Sq values of byte position p under the sign pattern beta, so one LDS read
-//           replaces eight +-1 accumulations.  Per tile of 512 tokens:
-//             score  thread = token: coalesced 128-bit loads of the token's sign words, one table
-//                    read per byte, s = |k_in| * sum_in + |k_out| * sum_out;
-//             softmax block-wide running max (log2 domain), p = 2^(z - M), running sums;
-//             value  thread = (16-channel slice, token pair): the 2-bit codes of two tokens become
+//   decode  one workgroup (8 waves) per (sequence, KV head, query head, context chunk).  The
+//           projected query is expanded in LDS into byte tables: entry [p][beta] is the signed sum of
+//           the 8 Sq values of byte position p under sign pattern beta, so one LDS read replaces
+//           eight +-1 accumulations.  Each wave is an independent online-softmax stream over
+//           64-token slabs:
+//             score  lane = token: buffer loads of the token's sign words, one table read per byte
+//                    (offset from one SDWA shift), s = |k_in| * sum_in + |k_out| * sum_out;
+//             softmax wave-wide running max (log2 domain), p = 2^(z - M), running sums;
+//             value  lane = (16-channel slice, token pair): the 2-bit codes of two tokens become
 //                    fp16 pairs 1 + code/4 with one and-or, and v_dot2_f32_f16 accumulates
 //                    p*step for both tokens at once; the constant 1 is removed at the end
-//                    (sum p*step*(1 + code/4) - sum p*step = sum p*step*code/4), and the
-//                    min term sum p*min is carried separately.
-//           The partial (M, sum p, unnormalized o) of the chunk goes to the workspace.
+//                    (sum p*step*(1 + code/4) - sum p*step = sum p*step*code/4), and the min term
+//                    sum p*min is carried separately.
+//           The eight wave states merge into the chunk's partial (max, sum, unnormalized output).
 //   combine one workgroup per (sequence, query head): log-sum-exp merge of the chunk partials.
 #include <math.h>
 
@@ -45,6 +46,34 @@ __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, size_t i
 template <>
 __device__ __forceinline__ float load_elem<float>(const float* p, size_t i) { return p[i]; }
 
+// dot of one JL row (d = 128 values of type QT) with the masked query in LDS, fp32 in channel order
+__device__ __forceinline__ float row_dot(const uint16_t* row, const float* q) {
+    float acc = 0.f;
+#pragma unroll
+    for (int v = 0; v < kD / 8; ++v) {
+        const uint4 x = reinterpret_cast<const uint4*>(row)[v];
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc = fmaf(__uint_as_float(w[e] << 16), q[8 * v + 2 * e], acc);
+            acc = fmaf(__uint_as_float(w[e] & 0xFFFF0000u), q[8 * v + 2 * e + 1], acc);
+        }
+    }
+    return acc;
+}
+__device__ __forceinline__ float row_dot(const float* row, const float* q) {
+    float acc = 0.f;
+#pragma unroll
+    for (int v = 0; v < kD / 4; ++v) {
+        const float4 x = reinterpret_cast<const float4*>(row)[v];
+        acc = fmaf(x.x, q[4 * v], acc);
+        acc = fmaf(x.y, q[4 * v + 1], acc);
+        acc = fmaf(x.z, q[4 * v + 2], acc);
+        acc = fmaf(x.w, q[4 * v + 3], acc);
+    }
+    return acc;
+}
+
 template <typename QT>
 __global__ __launch_bounds__(256) void qproj_kernel(DecodeArgs a) {
     __shared__ float qin[kD];
@@ -66,11 +95,7 @@ __global__ __launch_bounds__(256) void qproj_kernel(DecodeArgs a) {
     const QT* Sout = static_cast<const QT*>(a.S_out);
     float* dst = a.sq + (size_t)bh * (a.m + a.m_out);
     const float c_in = kSqrtHalfPi / (float)a.m;
-    for (int j = tid; j < a.m; j += 256) {
-        float acc = 0.f;
-        for (int c = 0; c < kD; ++c) acc = fmaf(load_elem<QT>(Sin, (size_t)j * kD + c), qin[c], acc);
-        dst[j] = acc * c_in;
-    }
+    for (int j = tid; j < a.m; j += 256) dst[j] = row_dot(Sin + (size_t)j * kD, qin) * c_in;
     if (a.m_out) {
         const float c_out = kSqrtHalfPi / (float)a.m_out;
         for (int j = tid; j < a.m_out; j += 256) {
@@ -112,6 +137,26 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 constexpr int kSlab = 64;                    // tokens per wave step
+
+// Log-sum-exp merge of the chunk partials (max, sum, unnormalized output) of one query head;
+// thread c writes output channel c.
+__device__ __forceinline__ void merge_partials(const DecodeArgs& a, int bhq, int c) {
+    const float* src = a.part + (size_t)bhq * a.nsplit * (kD + 2);
+    float mmax = -INFINITY;
+    for (int i = 0; i < a.nsplit; ++i) mmax = fmaxf(mmax, src[(size_t)i * (kD + 2)]);
+    float l = 0.f, o = 0.f;
+    if (mmax != -INFINITY) {
+        for (int i = 0; i < a.nsplit; ++i) {
+            const float* pp = src + (size_t)i * (kD + 2);
+            const float mi = pp[0];
+            if (mi == -INFINITY) continue;
+            const float sc = exp2f(mi - mmax);
+            l = fmaf(sc, pp[1], l);
+            o = fmaf(sc, pp[2 + c], o);
+        }
+    }
+    a.out[(size_t)bhq * kD + c] = l > 0.f ? o / l : 0.f;
+}
 
 // Raw buffer resource over [base, base + bytes): loads at or past the end return zero, which is how
 // the kernels treat the ragged end of a chunk (no branches, no clamped addresses).
@@ -356,25 +401,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 }
 
 // ------------------------------------------------------------------------------------ combine
+// One workgroup per (sequence, query head): log-sum-exp merge of the chunk partials.  A separate
+// launch: merging inside the decode kernel would need a device-scope release/acquire per workgroup,
+// which on MI355X writes back and invalidates the XCD's whole L2.
 __global__ __launch_bounds__(kD) void combine_kernel(DecodeArgs a) {
-    const int bhq = blockIdx.x;
-    const int c = threadIdx.x;
-    const float* src = a.part + (size_t)bhq * a.nsplit * (kD + 2);
-    float mmax = -INFINITY;
-    for (int i = 0; i < a.nsplit; ++i) mmax = fmaxf(mmax, src[(size_t)i * (kD + 2)]);
-    float l = 0.f, o = 0.f;
-    if (mmax != -INFINITY) {
-        for (int i = 0; i < a.nsplit; ++i) {
-            const float* pp = src + (size_t)i * (kD + 2);
-            const float mi = pp[0];
-            if (mi == -INFINITY) continue;
-            const float sc = exp2f(mi - mmax);
-            l = fmaf(sc, pp[1], l);
-            o = fmaf(sc, pp[2 + c], o);
-        }
-    }
-    a.out[(size_t)bhq * kD + c] = l > 0.f ? o / l : 0.f;
+    merge_partials(a, blockIdx.x, threadIdx.x);
 }
+
+}  // namespace
+
+namespace {
 
 template <int WIN, int WOUT, int VM>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {

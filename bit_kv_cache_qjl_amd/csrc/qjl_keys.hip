@@ -32,6 +32,7 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kTok = 32;        // tokens per chunk
 constexpr int kKRow = 136;      // LDS row of one key in bf16 elements (272 B: conflict-free b128 reads)
 constexpr int kGRow = 24;       // LDS row of the gathered outlier channels (48 B)
+constexpr int64_t kSmallAppend = 16;   // tokens per sequence at or below which the flattened-row kernel runs
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t v) { return __uint_as_float(v << 16); }
 
@@ -239,6 +240,112 @@ void quantize_keys_bf16_kernel(KeyQuantArgs a) {
     }
 }
 
+// Small appends (a few new tokens per sequence, e.g. one per decode step): every 32 key rows of any
+// (sequence, KV head, token) form one MFMA chunk.  The outlier sketch is computed with the
+// full-width S_out on the outlier-only key (zeros on the other channels), so the JL operands are
+// the same for every row and one workgroup covers rows of all heads: the JL matrices are read once
+// per 32 rows instead of once per (sequence, head).
+constexpr int kMaxTilesPerWave = 4;          // (m + m_out) / 32 / 8 waves
+
+template <int TT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void quantize_keys_rows_kernel(KeyQuantArgs a, int64_t rows) {
+    __shared__ __attribute__((aligned(16))) uint16_t kl[kTok * kKRow];   // inlier channels
+    __shared__ __attribute__((aligned(16))) uint16_t ko[kTok * kKRow];   // outlier channels
+    __shared__ uint32_t ol[kTok * (kMaxBits / 32 + 1)];
+    __shared__ int64_t s_dst[kTok];
+    extern __shared__ uint32_t s_mask[];                                   // [Hkv][4] outlier masks
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int Win = a.m >> 5, Wout = a.m_out >> 5, W = a.W, orow = W + 1;
+    const int64_t r0 = (int64_t)blockIdx.x * kTok;
+
+    for (int hh = tid; hh < a.Hkv; hh += kThreads) {
+        uint32_t mk[4] = {0u, 0u, 0u, 0u};
+        for (int i = 0; i < a.n_out; ++i) {
+            const int c = a.oidx[hh * a.n_out + i] & (kD - 1);
+            mk[c >> 5] |= 1u << (c & 31);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s_mask[hh * 4 + q] = mk[q];
+    }
+
+    // stationary JL tiles of this wave: global tile gt = wave + 8 i over [inlier tiles, outlier tiles]
+    const int prow = tile_row(lane & 31);
+    const int khalf = (lane >> 5) * 8;
+    uint4 frag[TT][8];
+#pragma unroll
+    for (int i = 0; i < TT; ++i) {
+        const int gt = wave + kWaves * i;
+        const uint16_t* row = nullptr;
+        if (gt < Win) row = static_cast<const uint16_t*>(a.S_in) + (size_t)(32 * gt + prow) * kD + khalf;
+        else if (gt < Win + Wout) row = static_cast<const uint16_t*>(a.S_out) + (size_t)(32 * (gt - Win) + prow) * kD + khalf;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) frag[i][s] = row ? *reinterpret_cast<const uint4*>(row + 16 * s) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();
+
+    // ---- stage 32 rows: split into inlier / outlier halves, norms
+    const int tt = tid >> 4, cg = tid & 15;
+    const int64_t r = r0 + tt;
+    uint4 kv = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t om = 0;
+    if (r < rows) {
+        const int64_t t = r % a.T, bh = r / a.T;
+        const int h = (int)(bh % a.Hkv);
+        const int64_t b = bh / a.Hkv;
+        kv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.K) + b * a.sKb + t * a.sKt + h * a.sKh + 8 * cg);
+        om = (s_mask[h * 4 + (cg >> 2)] >> (8 * (cg & 3))) & 0xFFu;
+        if (cg == 0) s_dst[tt] = ((int64_t)b * a.Hkv + h) * a.Ncap + a.t0 + t;
+    }
+    {
+        const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+        uint32_t win[4], wout[4];
+        float ss_in = 0.f, ss_out = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = kw[q] & 0xFFFFu, hi = kw[q] >> 16;
+            const float flo = bf16_to_f32(lo), fhi = bf16_to_f32(hi);
+            const bool olo = (om >> (2 * q)) & 1u, ohi = (om >> (2 * q + 1)) & 1u;
+            if (olo) ss_out = fmaf(flo, flo, ss_out); else ss_in = fmaf(flo, flo, ss_in);
+            if (ohi) ss_out = fmaf(fhi, fhi, ss_out); else ss_in = fmaf(fhi, fhi, ss_in);
+            win[q] = (olo ? 0u : lo) | ((ohi ? 0u : hi) << 16);
+            wout[q] = (olo ? lo : 0u) | ((ohi ? hi : 0u) << 16);
+        }
+        *reinterpret_cast<uint4*>(kl + tt * kKRow + 8 * cg) = make_uint4(win[0], win[1], win[2], win[3]);
+        *reinterpret_cast<uint4*>(ko + tt * kKRow + 8 * cg) = make_uint4(wout[0], wout[1], wout[2], wout[3]);
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) {
+            ss_in += __shfl_xor(ss_in, o);
+            ss_out += __shfl_xor(ss_out, o);
+        }
+        __syncthreads();
+        if (cg == 0 && r < rows) reinterpret_cast<uint32_t*>(a.norms)[s_dst[tt]] = norm_pair(ss_in, ss_out);
+    }
+
+    // ---- projections and sign packing
+#pragma unroll
+    for (int i = 0; i < TT; ++i) {
+        const int gt = wave + kWaves * i;
+        if (gt < Win + Wout) {
+            const uint16_t* src = (gt < Win ? kl : ko) + (lane & 31) * kKRow + khalf;
+            f32x16 acc = {};
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(frag[i][s]),
+                                                              as_bf16x8(*reinterpret_cast<const uint4*>(src + 16 * s)), acc, 0, 0, 0);
+            const uint32_t w = pack_signs(acc, lane);
+            if (lane < 32) ol[lane * orow + gt] = w;
+        }
+    }
+    __syncthreads();
+    const int nvalid = (int)min((int64_t)kTok, rows - r0);
+    for (int i = tid; i < nvalid * W; i += kThreads) {
+        const int tok = i / W, w = i - tok * W;
+        a.bits[s_dst[tok] * W + w] = ol[tok * orow + w];
+    }
+}
+
 // fp32 keys and JL matrix (VALU, one wave per key): exact fp32 fused multiply-adds in channel order.
 constexpr int kF32Tok = 4;
 
@@ -302,6 +409,17 @@ __global__ __launch_bounds__(256) void quantize_keys_f32_kernel(KeyQuantArgs a) 
 }  // namespace
 
 hipError_t launch_quantize_keys_bf16(const KeyQuantArgs& a, int B, hipStream_t s) {
+    if (a.T <= kSmallAppend) {
+        // few tokens per sequence: flattened rows, one JL load per 32 rows of all heads
+        const int64_t rows = (int64_t)B * a.Hkv * a.T;
+        const int tt = ((a.m >> 5) + (a.m_out >> 5) + kWaves - 1) / kWaves;
+        const dim3 grid((unsigned)((rows + kTok - 1) / kTok));
+        const size_t lds = (size_t)a.Hkv * 4 * sizeof(uint32_t);
+        if (tt <= 1) hipLaunchKernelGGL(quantize_keys_rows_kernel<1>, grid, dim3(kThreads), lds, s, a, rows);
+        else if (tt == 2) hipLaunchKernelGGL(quantize_keys_rows_kernel<2>, grid, dim3(kThreads), lds, s, a, rows);
+        else hipLaunchKernelGGL(quantize_keys_rows_kernel<4>, grid, dim3(kThreads), lds, s, a, rows);
+        return hipGetLastError();
+    }
     const int tiles = (a.m >> 5) > (a.m_out >> 5) ? (a.m >> 5) : (a.m_out >> 5);
     const int tpw = (tiles + kWaves - 1) / kWaves;
     dim3 grid((unsigned)((a.T + a.tokens_per_block - 1) / a.tokens_per_block), (unsigned)a.Hkv, (unsigned)B);

@@ -43,6 +43,27 @@ def test_quantize_keys_parity(name):
     compare_norms(cache.norms.cpu().numpy(), ref["norms"], name)
 
 
+@pytest.mark.parametrize("name,T,m,m_out", [
+    ("llama2_7b_decode", 1, 256, 256),
+    ("llama31_70b_gqa_decode", 5, 256, 256),
+    ("prefill_quantize_64k", 16, 512, 512),
+    ("prefill_quantize_64k", 17, 512, 512),
+    ("llama3_8b_gqa_decode", 3, 128, 128),
+    ("llama3_8b_gqa_decode", 2, 1024, 0),
+])
+def test_quantize_keys_small_append(name, T, m, m_out):
+    """A few tokens per sequence (the decode-step append): the flattened-row kernel for T <= 16."""
+    w = SCALED[name].scaled(N=T, m=m, m_out=m_out, n_out=SCALED[name].n_out if m_out else 0)
+    log(f"[quantize_keys] small append {name} T={T} m={m} m_out={m_out} B={w.B} Hkv={w.Hkv}")
+    x = inputs(w)
+    cache = gpu_quantize_keys(qjl, w, x["K"], x["S_in"], x["S_out"], x["oidx"], Ncap=T + 9, t0=9)
+    ref = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
+    bits = bits_np(cache.bits)
+    compare_bits(bits[:, :, 9:], ref, f"append T={T}", w.m + w.m_out)
+    compare_norms(cache.norms.cpu().numpy()[:, :, 9:], ref["norms"], f"append T={T}")
+    assert not bits[:, :, :9].any()
+
+
 def test_quantize_keys_append_offset_and_strides():
     """Write T tokens at t0 of a larger cache from a strided (non-contiguous) key view."""
     w = SCALED["llama2_7b_decode"].scaled(N=70)
