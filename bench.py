@@ -182,6 +182,7 @@ def main() -> int:
                     choices=["llama2_7b_decode", "llama3_8b_gqa_decode", "llama31_70b_gqa_decode"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--no-quantize", action="store_true", help="skip the prefill quantize measurement")
+    ap.add_argument("--quantize-only", action="store_true", help="only the prefill quantize measurement (profiling)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help=f"run one plain {CALIB_BYTES >> 20} MiB device copy first (the reference kernel that "
                          "scales the HBM byte counters of a --pmc profile)")
@@ -198,6 +199,10 @@ def main() -> int:
 
     import torch
     import bit_kv_cache_qjl_amd as qjl
+
+    if args.quantize_only:
+        print(json.dumps(bench_quantize(qjl, torch, args.steps)), flush=True)
+        return 0
 
     w = si.WORKLOADS[args.workload]
     N = w.N

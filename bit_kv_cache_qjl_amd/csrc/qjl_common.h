@@ -12,6 +12,56 @@ constexpr int kMaxBits = 1024;       // m + m_out
 constexpr float kSqrtHalfPi = 1.2533141373155002f;   // sqrt(pi / 2)
 constexpr float kLog2e = 1.4426950408889634f;
 
+// ---- cross-lane reductions on the VALU (DPP row permutes and gfx950 permlane swaps; no LDS
+//      crossbar round trip)
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// sum over each row of 16 lanes, result in every lane of the row
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v);   // row_half_mirror
+    v += dpp_mov<0x140>(v);   // row_mirror
+    return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_mov<0xB1>(v));
+    v = fmaxf(v, dpp_mov<0x4E>(v));
+    v = fmaxf(v, dpp_mov<0x141>(v));
+    v = fmaxf(v, dpp_mov<0x140>(v));
+    return v;
+}
+__device__ __forceinline__ float row16_min(float v) {
+    v = fminf(v, dpp_mov<0xB1>(v));
+    v = fminf(v, dpp_mov<0x4E>(v));
+    v = fminf(v, dpp_mov<0x141>(v));
+    v = fminf(v, dpp_mov<0x140>(v));
+    return v;
+}
+// value held by lane l ^ 16 (neighbouring row) and by lane l ^ 32 (other half-wave)
+__device__ __forceinline__ uint32_t lane_xor16(uint32_t v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return ((__lane_id() >> 4) & 1) ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t lane_xor32(uint32_t v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (__lane_id() >= 32) ? r[0] : r[1];
+}
+__device__ __forceinline__ float wave64_sum(float v) {
+    v = row16_sum(v);
+    v += __uint_as_float(lane_xor16(__float_as_uint(v)));
+    v += __uint_as_float(lane_xor32(__float_as_uint(v)));
+    return v;
+}
+__device__ __forceinline__ float wave64_max(float v) {
+    v = row16_max(v);
+    v = fmaxf(v, __uint_as_float(lane_xor16(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(lane_xor32(__float_as_uint(v))));
+    return v;
+}
+
 // Launch descriptors filled by the host layer (qjl_api.hip) and consumed by the kernels.
 struct KeyQuantArgs {
     const void* K;

@@ -124,17 +124,8 @@ __device__ __forceinline__ uint32_t byte_x4(uint32_t x) {
     return r;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
+__device__ __forceinline__ float wave_max(float v) { return wave64_max(v); }
+__device__ __forceinline__ float wave_sum(float v) { return wave64_sum(v); }
 
 constexpr int kSlab = 64;                    // tokens per wave step
 
@@ -239,15 +230,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     // ---- byte tables of the projected query: entry [p][beta] = sum_i (+-) Sq[8p + i]
     for (int i = tid; i < 8 * P; i += kThreads) sq_s[i] = a.sq[(size_t)bhq * (8 * P) + i];
     __syncthreads();
-    for (int idx = tid; idx < P * 256; idx += kThreads) {
-        const int p = idx >> 8, beta = idx & 255;
-        float v = 0.f;
+    // one task = (position p, high nibble): 16 entries from the high-nibble sum and two
+    // 4-entry tables of the low bit pairs
+    for (int idx = tid; idx < P * 16; idx += kThreads) {
+        const int p = idx >> 4, bh = idx & 15;
+        const float* sv = sq_s + 8 * p;
+        float hi = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float s = sq_s[8 * p + i];
-            v += ((beta >> i) & 1) ? s : -s;
+        for (int i = 0; i < 4; ++i) hi += ((bh >> i) & 1) ? sv[4 + i] : -sv[4 + i];
+        const float t01[4] = {-sv[0] - sv[1], sv[0] - sv[1], -sv[0] + sv[1], sv[0] + sv[1]};
+        const float t23[4] = {-sv[2] - sv[3], sv[2] - sv[3], -sv[2] + sv[3], sv[2] + sv[3]};
+        float4* dst = reinterpret_cast<float4*>(lut + p * 256 + bh * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float h2 = hi + t23[q];
+            dst[q] = make_float4(h2 + t01[0], h2 + t01[1], h2 + t01[2], h2 + t01[3]);
         }
-        lut[idx] = v;
     }
     __syncthreads();
 

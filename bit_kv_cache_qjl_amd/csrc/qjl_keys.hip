@@ -51,7 +51,7 @@ __device__ __forceinline__ uint32_t pack_signs(const f32x16& acc, int lane) {
     uint32_t w = 0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) w = __builtin_amdgcn_alignbit(w, __float_as_uint(acc[r]), 31);
-    const uint32_t other = __shfl_xor(w, 32);
+    const uint32_t other = lane_xor32(w);
     const uint32_t lo = lane < 32 ? w : other;
     const uint32_t hi = lane < 32 ? other : w;
     return ~(lo | (hi << 16));
@@ -59,45 +59,15 @@ __device__ __forceinline__ uint32_t pack_signs(const f32x16& acc, int lane) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Per-thread loader role: token tt of the chunk, channels 8*cg .. 8*cg+7.  Masks the outlier
-// channels of the 8 values, gathers them into the 16-wide outlier row, stores the masked values in
-// LDS and returns the two partial sums of squares.
-__device__ __forceinline__ void stage_chunk(uint4 kv, uint32_t omask, int tt, int cg, int n_out, const int* s_oidx,
-                                            uint16_t* kl, uint16_t* gl, float& ss_in, float& ss_out) {
-    const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
-    uint32_t mw[4];
-    ss_in = 0.f;
-    ss_out = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = kw[q] & 0xFFFFu, hi = kw[q] >> 16;
-        const float flo = bf16_to_f32(lo), fhi = bf16_to_f32(hi);
-        const bool olo = (omask >> (2 * q)) & 1u, ohi = (omask >> (2 * q + 1)) & 1u;
-        if (olo) ss_out = fmaf(flo, flo, ss_out); else ss_in = fmaf(flo, flo, ss_in);
-        if (ohi) ss_out = fmaf(fhi, fhi, ss_out); else ss_in = fmaf(fhi, fhi, ss_in);
-        mw[q] = (olo ? 0u : lo) | ((ohi ? 0u : hi) << 16);
-    }
-    if (omask) {
-        for (int i = 0; i < n_out; ++i) {
-            const int c = s_oidx[i];
-            if ((c >> 3) == cg) {
-                const int e = c & 7;
-                gl[tt * kGRow + i] = (uint16_t)((kw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-            }
-        }
-    }
-    *reinterpret_cast<uint4*>(kl + tt * kKRow + 8 * cg) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) {
-        ss_in += __shfl_xor(ss_in, o);
-        ss_out += __shfl_xor(ss_out, o);
-    }
-}
-
 __device__ __forceinline__ uint32_t norm_pair(float ss_in, float ss_out) {
     const _Float16 ni = (_Float16)sqrtf(ss_in);
     const _Float16 no = (_Float16)sqrtf(ss_out);
     return (uint32_t)__builtin_bit_cast(uint16_t, ni) | ((uint32_t)__builtin_bit_cast(uint16_t, no) << 16);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
 // Waves per SIMD the register budget must allow: two workgroups per CU for up to 512 inlier
@@ -105,13 +75,17 @@ __device__ __forceinline__ uint32_t norm_pair(float ss_in, float ss_out) {
 template <int TPW>
 struct QKOccupancy { static constexpr int waves = TPW <= 2 ? 4 : 2; };
 
+// One workgroup = one (sequence, KV head) and a token range.  The outlier columns of the
+// stationary S_in fragments are zeroed once, so S_in k = S_in k_in and the key chunk is staged in
+// LDS unmasked; the outlier operand (k gathered on the head's outlier channels, K = 16) is read
+// back from the staged chunk.
 template <int TPW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QKOccupancy<TPW>::waves)))
 void quantize_keys_bf16_kernel(KeyQuantArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t kl[2][kTok * kKRow];
-    __shared__ __attribute__((aligned(16))) uint16_t gl[2][kTok * kGRow];
     __shared__ uint32_t ol[2][kTok * (kMaxBits / 32 + 1)];
     __shared__ int s_oidx[kMaxOutliers];
+    __shared__ uint4 sout_l[TPW][kWaves][64];                            // gathered S_out fragments
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -127,15 +101,15 @@ void quantize_keys_bf16_kernel(KeyQuantArgs a) {
     const int orow = W + 1;
 
     if (tid < n_out) s_oidx[tid] = a.oidx[h * n_out + tid] & (kD - 1);   // never index outside a row
-    for (int i = tid; i < 2 * kTok * kGRow / 2; i += kThreads) reinterpret_cast<uint32_t*>(&gl[0][0])[i] = 0u;
     __syncthreads();
 
+    // loader role: token tt of the chunk, channels 8*cg .. 8*cg+7; keep masks of its 8 channels
     const int tt = tid >> 4;
     const int cg = tid & 15;
-    uint32_t omask = 0;
+    uint32_t keep_out[4] = {0u, 0u, 0u, 0u};
     for (int i = 0; i < n_out; ++i) {
         const int c = s_oidx[i];
-        if ((c >> 3) == cg) omask |= 1u << (c & 7);
+        if ((c >> 3) == cg) keep_out[(c & 7) >> 1] |= (c & 1) ? 0xFFFF0000u : 0x0000FFFFu;
     }
 
     const uint16_t* K = static_cast<const uint16_t*>(a.K);
@@ -152,7 +126,6 @@ void quantize_keys_bf16_kernel(KeyQuantArgs a) {
     const int prow = tile_row(lane & 31);
     const int khalf = (lane >> 5) * 8;
     uint4 sin_frag[TPW][8];
-    uint4 sout_frag[TPW];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
         const int j = wave + kWaves * i;
@@ -174,16 +147,48 @@ void quantize_keys_bf16_kernel(KeyQuantArgs a) {
                 g[e >> 1] |= v << (16 * (e & 1));
             }
         }
-        sout_frag[i] = make_uint4(g[0], g[1], g[2], g[3]);
+        sout_l[i][wave][lane] = make_uint4(g[0], g[1], g[2], g[3]);
+    }
+    for (int i = 0; i < n_out; ++i) {       // S_in k = S_in k_in: zero the outlier columns
+        const int c = s_oidx[i];
+        const int s = c >> 4, off = c & 15;
+        if ((off >> 3) == (khalf >> 3)) {
+            const int e = off & 7;
+            const uint32_t m = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int ss = 0; ss < 8; ++ss)
+                    if (ss == s) {
+                        uint32_t* f = reinterpret_cast<uint32_t*>(&sin_frag[t][ss]);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (q == (e >> 1)) f[q] &= m;
+                    }
+        }
     }
 
-    {
-        float ss_in, ss_out;
-        stage_chunk(kv, omask, tt, cg, n_out, s_oidx, kl[0], gl[0], ss_in, ss_out);
-        if (cg == 0 && t_begin + tt < t_end) norms32[head_row0 + t_begin + tt] = norm_pair(ss_in, ss_out);
-    }
+    // stage one chunk: unmasked keys to LDS, the two sums of squares, norms
+    auto stage = [&](uint4 v, uint16_t* dst, int64_t c0s) {
+        *reinterpret_cast<uint4*>(dst + tt * kKRow + 8 * cg) = v;
+        const uint32_t kw[4] = {v.x, v.y, v.z, v.w};
+        float ss_in = 0.f, ss_out = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t o = kw[q] & keep_out[q];
+            const uint32_t n = kw[q] & ~keep_out[q];
+            ss_out = dot2_bf16(o, o, ss_out);
+            ss_in = dot2_bf16(n, n, ss_in);
+        }
+        ss_in = row16_sum(ss_in);       // the 16 loader lanes of a token are one DPP row
+        ss_out = row16_sum(ss_out);
+        if (cg == 0 && c0s + tt < t_end) norms32[head_row0 + c0s + tt] = norm_pair(ss_in, ss_out);
+    };
+
+    stage(kv, kl[0], t_begin);
     __syncthreads();
 
+    const int my_tok = lane & 31;
     int buf = 0;
     for (int64_t c0 = t_begin; c0 < t_end; c0 += kTok) {
         const int nvalid = (int)min((int64_t)kTok, t_end - c0);
@@ -193,8 +198,9 @@ void quantize_keys_bf16_kernel(KeyQuantArgs a) {
         uint4 kvn = make_uint4(0u, 0u, 0u, 0u);
         if (cn + tt < t_end) kvn = *reinterpret_cast<const uint4*>(krow + (cn + tt) * a.sKt);
 
-        // ---- projections on the matrix cores; signs packed in registers
-        const uint16_t* klb = kl[buf] + (lane & 31) * kKRow + khalf;
+        // ---- projections on the matrix cores (one live accumulator: the register budget holds
+        //      two workgroups per CU)
+        const uint16_t* klb = kl[buf] + my_tok * kKRow + khalf;
         uint32_t* olb = ol[buf];
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
@@ -202,40 +208,44 @@ void quantize_keys_bf16_kernel(KeyQuantArgs a) {
             if (j < Win) {
                 f32x16 acc = {};
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const uint4 bf = *reinterpret_cast<const uint4*>(klb + 16 * s);
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sin_frag[i][s]), as_bf16x8(bf), acc, 0, 0, 0);
-                }
+                for (int s = 0; s < 8; ++s)
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sin_frag[i][s]),
+                                                                  as_bf16x8(*reinterpret_cast<const uint4*>(klb + 16 * s)), acc, 0, 0, 0);
                 const uint32_t w = pack_signs(acc, lane);
                 if (lane < 32) olb[lane * orow + j] = w;
             }
         }
-        const uint4 gfrag = *reinterpret_cast<const uint4*>(gl[buf] + (lane & 31) * kGRow + khalf);
+        if (Wout > wave) {
+            // outlier operand: this lane's token, gathered on the head's outlier channels
+            uint32_t g[4] = {0u, 0u, 0u, 0u};
+            const uint16_t* krw = kl[buf] + my_tok * kKRow;
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int j = wave + kWaves * i;
-            if (j < Wout) {
-                f32x16 ao = {};
-                ao = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sout_frag[i]), as_bf16x8(gfrag), ao, 0, 0, 0);
-                const uint32_t w = pack_signs(ao, lane);
-                if (lane < 32) olb[lane * orow + Win + j] = w;
+            for (int e = 0; e < 8; ++e) {
+                const int k = khalf + e;
+                if (k < n_out) g[e >> 1] |= (uint32_t)krw[s_oidx[k]] << (16 * (e & 1));
+            }
+            const uint4 gfrag = make_uint4(g[0], g[1], g[2], g[3]);
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int j = wave + kWaves * i;
+                if (j < Wout) {
+                    f32x16 ao = {};
+                    ao = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sout_l[i][wave][lane]), as_bf16x8(gfrag), ao, 0, 0, 0);
+                    const uint32_t w = pack_signs(ao, lane);
+                    if (lane < 32) olb[lane * orow + Win + j] = w;
+                }
             }
         }
 
         // ---- stage the next chunk into the other buffer
-        if (cn < t_end) {
-            float ss_in, ss_out;
-            stage_chunk(kvn, omask, tt, cg, n_out, s_oidx, kl[buf ^ 1], gl[buf ^ 1], ss_in, ss_out);
-            if (cg == 0 && cn + tt < t_end) norms32[head_row0 + cn + tt] = norm_pair(ss_in, ss_out);
-        }
+        if (cn < t_end) stage(kvn, kl[buf ^ 1], cn);
         __syncthreads();
 
-        // ---- coalesced store of this chunk's packed words
+        // ---- coalesced store of this chunk's packed words (lanes 0..W-1 of each 32-lane row)
         uint32_t* dst = a.bits + (head_row0 + c0) * W;
-        for (int i = tid; i < nvalid * W; i += kThreads) {
-            const int tok = i / W;
-            dst[i] = olb[tok * orow + (i - tok * W)];
-        }
+        const int w = tid & 31;
+        if (w < W)
+            for (int tok = tid >> 5; tok < nvalid; tok += kThreads / 32) dst[tok * W + w] = olb[tok * orow + w];
         buf ^= 1;
     }
 }
@@ -314,11 +324,8 @@ void quantize_keys_rows_kernel(KeyQuantArgs a, int64_t rows) {
         }
         *reinterpret_cast<uint4*>(kl + tt * kKRow + 8 * cg) = make_uint4(win[0], win[1], win[2], win[3]);
         *reinterpret_cast<uint4*>(ko + tt * kKRow + 8 * cg) = make_uint4(wout[0], wout[1], wout[2], wout[3]);
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) {
-            ss_in += __shfl_xor(ss_in, o);
-            ss_out += __shfl_xor(ss_out, o);
-        }
+        ss_in = row16_sum(ss_in);
+        ss_out = row16_sum(ss_out);
         __syncthreads();
         if (cg == 0 && r < rows) reinterpret_cast<uint32_t*>(a.norms)[s_dst[tt]] = norm_pair(ss_in, ss_out);
     }

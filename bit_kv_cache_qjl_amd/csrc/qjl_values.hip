@@ -57,11 +57,8 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(ValueQuantArgs a) 
         mn = fminf(mn, v[q]);
         mx = fmaxf(mx, v[q]);
     }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) {
-        mn = fminf(mn, __shfl_xor(mn, o));
-        mx = fmaxf(mx, __shfl_xor(mx, o));
-    }
+    mn = row16_min(mn);   // the 16 lanes of a vector are one DPP row; min/max are exact
+    mx = row16_max(mx);
     constexpr int L = (1 << NBITS) - 1;
     const float range = mx - mn;
     const float stepf = range / (float)L;
