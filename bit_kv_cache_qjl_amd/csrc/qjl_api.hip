@@ -181,12 +181,12 @@ int qjl_quantize_keys(const void* K, int kdt, int B, int64_t T, int Hkv, int d, 
     a.m_out = m_out;
     a.n_out = n_out;
     a.W = (m + m_out) / 32;
-    // ~2 workgroups per CU over 256 CUs, in whole 32-token chunks
+    // ~2 workgroups per CU over 256 CUs, in whole 64-token chunks
     int64_t per = ((int64_t)B * Hkv * T + 511) / 512;
-    per = ((per + 31) / 32) * 32;
-    if (per < 32) per = 32;
+    per = ((per + 63) / 64) * 64;
+    if (per < 64) per = 64;
     if (per > 8192) per = 8192;
-    if (per > ((T + 31) / 32) * 32) per = ((T + 31) / 32) * 32;
+    if (per > ((T + 63) / 64) * 64) per = ((T + 63) / 64) * 64;
     a.tokens_per_block = (int)per;
     qjl::timer_begin(qjl::TK_QUANT_KEYS, stream);
     hipError_t e = kdt == QJL_BF16 ? qjl::launch_quantize_keys_bf16(a, B, stream) : qjl::launch_quantize_keys_f32(a, B, stream);

@@ -79,13 +79,17 @@ struct QKOccupancy { static constexpr int waves = TPW <= 2 ? 4 : 2; };
 // stationary S_in fragments are zeroed once, so S_in k = S_in k_in and the key chunk is staged in
 // LDS unmasked; the outlier operand (k gathered on the head's outlier channels, K = 16) is read
 // back from the staged chunk.
+constexpr int kTokH = 64;        // tokens per chunk of the per-head kernel (two MFMA N tiles)
+
 template <int TPW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QKOccupancy<TPW>::waves)))
 void quantize_keys_bf16_kernel(KeyQuantArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t kl[2][kTok * kKRow];
-    __shared__ uint32_t ol[2][kTok * (kMaxBits / 32 + 1)];
+    constexpr int NW = kWaves;
+    constexpr int NT = kThreads;
+    __shared__ __attribute__((aligned(16))) uint16_t kl[2][kTokH * kKRow];
+    __shared__ uint32_t ol[2][kTokH * (kMaxBits / 32 + 1)];
     __shared__ int s_oidx[kMaxOutliers];
-    __shared__ uint4 sout_l[TPW][kWaves][64];                            // gathered S_out fragments
+    __shared__ uint4 sout_l[TPW][NW][64];                            // gathered S_out fragments
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -103,7 +107,7 @@ void quantize_keys_bf16_kernel(KeyQuantArgs a) {
     if (tid < n_out) s_oidx[tid] = a.oidx[h * n_out + tid] & (kD - 1);   // never index outside a row
     __syncthreads();
 
-    // loader role: token tt of the chunk, channels 8*cg .. 8*cg+7; keep masks of its 8 channels
+    // loader role: tokens tt and tt + 32 of the chunk, channels 8*cg .. 8*cg+7
     const int tt = tid >> 4;
     const int cg = tid & 15;
     uint32_t keep_out[4] = {0u, 0u, 0u, 0u};
@@ -118,8 +122,9 @@ void quantize_keys_bf16_kernel(KeyQuantArgs a) {
     uint32_t* norms32 = reinterpret_cast<uint32_t*>(a.norms);
 
     // first chunk in flight while the stationary JL fragments load
-    uint4 kv = make_uint4(0u, 0u, 0u, 0u);
-    if (t_begin + tt < t_end) kv = *reinterpret_cast<const uint4*>(krow + (t_begin + tt) * a.sKt);
+    uint4 kv0 = make_uint4(0u, 0u, 0u, 0u), kv1 = make_uint4(0u, 0u, 0u, 0u);
+    if (t_begin + tt < t_end) kv0 = *reinterpret_cast<const uint4*>(krow + (t_begin + tt) * a.sKt);
+    if (t_begin + tt + 32 < t_end) kv1 = *reinterpret_cast<const uint4*>(krow + (t_begin + tt + 32) * a.sKt);
 
     const uint16_t* Sin = static_cast<const uint16_t*>(a.S_in);
     const uint16_t* Sout = static_cast<const uint16_t*>(a.S_out);
@@ -128,7 +133,7 @@ void quantize_keys_bf16_kernel(KeyQuantArgs a) {
     uint4 sin_frag[TPW][8];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-        const int j = wave + kWaves * i;
+        const int j = wave + NW * i;
         if (j < Win) {
             const uint16_t* row = Sin + (size_t)(32 * j + prow) * kD + khalf;
 #pragma unroll
@@ -168,9 +173,9 @@ void quantize_keys_bf16_kernel(KeyQuantArgs a) {
         }
     }
 
-    // stage one chunk: unmasked keys to LDS, the two sums of squares, norms
-    auto stage = [&](uint4 v, uint16_t* dst, int64_t c0s) {
-        *reinterpret_cast<uint4*>(dst + tt * kKRow + 8 * cg) = v;
+    // stage one token row: unmasked key to LDS, the two sums of squares, its norms
+    auto stage = [&](uint4 v, uint16_t* dst, int tok, int64_t tglob) {
+        *reinterpret_cast<uint4*>(dst + tok * kKRow + 8 * cg) = v;
         const uint32_t kw[4] = {v.x, v.y, v.z, v.w};
         float ss_in = 0.f, ss_out = 0.f;
 #pragma unroll
@@ -182,70 +187,81 @@ void quantize_keys_bf16_kernel(KeyQuantArgs a) {
         }
         ss_in = row16_sum(ss_in);       // the 16 loader lanes of a token are one DPP row
         ss_out = row16_sum(ss_out);
-        if (cg == 0 && c0s + tt < t_end) norms32[head_row0 + c0s + tt] = norm_pair(ss_in, ss_out);
+        if (cg == 0 && tglob < t_end) norms32[head_row0 + tglob] = norm_pair(ss_in, ss_out);
     };
 
-    stage(kv, kl[0], t_begin);
+    stage(kv0, kl[0], tt, t_begin + tt);
+    stage(kv1, kl[0], tt + 32, t_begin + tt + 32);
     __syncthreads();
 
     const int my_tok = lane & 31;
     int buf = 0;
-    for (int64_t c0 = t_begin; c0 < t_end; c0 += kTok) {
-        const int nvalid = (int)min((int64_t)kTok, t_end - c0);
-        const int64_t cn = c0 + kTok;
+    for (int64_t c0 = t_begin; c0 < t_end; c0 += kTokH) {
+        const int nvalid = (int)min((int64_t)kTokH, t_end - c0);
+        const int64_t cn = c0 + kTokH;
 
         // next chunk's keys in flight during this chunk's matrix work
-        uint4 kvn = make_uint4(0u, 0u, 0u, 0u);
-        if (cn + tt < t_end) kvn = *reinterpret_cast<const uint4*>(krow + (cn + tt) * a.sKt);
+        uint4 kn0 = make_uint4(0u, 0u, 0u, 0u), kn1 = make_uint4(0u, 0u, 0u, 0u);
+        if (cn + tt < t_end) kn0 = *reinterpret_cast<const uint4*>(krow + (cn + tt) * a.sKt);
+        if (cn + tt + 32 < t_end) kn1 = *reinterpret_cast<const uint4*>(krow + (cn + tt + 32) * a.sKt);
 
-        // ---- projections on the matrix cores (one live accumulator: the register budget holds
-        //      two workgroups per CU)
-        const uint16_t* klb = kl[buf] + my_tok * kKRow + khalf;
-        uint32_t* olb = ol[buf];
+        // ---- projections on the matrix cores
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
-            const int j = wave + kWaves * i;
+            const int j = wave + NW * i;
             if (j < Win) {
-                f32x16 acc = {};
+                {
 #pragma unroll
-                for (int s = 0; s < 8; ++s)
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sin_frag[i][s]),
-                                                                  as_bf16x8(*reinterpret_cast<const uint4*>(klb + 16 * s)), acc, 0, 0, 0);
-                const uint32_t w = pack_signs(acc, lane);
-                if (lane < 32) olb[lane * orow + j] = w;
-            }
-        }
-        if (Wout > wave) {
-            // outlier operand: this lane's token, gathered on the head's outlier channels
-            uint32_t g[4] = {0u, 0u, 0u, 0u};
-            const uint16_t* krw = kl[buf] + my_tok * kKRow;
+                    for (int nh = 0; nh < 2; ++nh) {
+                        const uint16_t* klb = kl[buf] + (32 * nh + my_tok) * kKRow + khalf;
+                        f32x16 acc = {};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int k = khalf + e;
-                if (k < n_out) g[e >> 1] |= (uint32_t)krw[s_oidx[k]] << (16 * (e & 1));
-            }
-            const uint4 gfrag = make_uint4(g[0], g[1], g[2], g[3]);
-#pragma unroll
-            for (int i = 0; i < TPW; ++i) {
-                const int j = wave + kWaves * i;
-                if (j < Wout) {
-                    f32x16 ao = {};
-                    ao = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sout_l[i][wave][lane]), as_bf16x8(gfrag), ao, 0, 0, 0);
-                    const uint32_t w = pack_signs(ao, lane);
-                    if (lane < 32) olb[lane * orow + Win + j] = w;
+                        for (int s = 0; s < 8; ++s)
+                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sin_frag[i][s]),
+                                                                          as_bf16x8(*reinterpret_cast<const uint4*>(klb + 16 * s)), acc, 0, 0, 0);
+                        const uint32_t w = pack_signs(acc, lane);
+                        if (lane < 32) ol[buf][(32 * nh + lane) * orow + j] = w;
+                    }
                 }
             }
         }
-
-        // ---- stage the next chunk into the other buffer
-        if (cn < t_end) stage(kvn, kl[buf ^ 1], cn);
+        if (Wout > wave) {
+#pragma unroll
+            for (int nh = 0; nh < 2; ++nh) {
+                // outlier operand: this lane's token, gathered on the head's outlier channels
+                uint32_t g[4] = {0u, 0u, 0u, 0u};
+                const uint16_t* krw = kl[buf] + (32 * nh + my_tok) * kKRow;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int k = khalf + e;
+                    if (k < n_out) g[e >> 1] |= (uint32_t)krw[s_oidx[k]] << (16 * (e & 1));
+                }
+                const uint4 gfrag = make_uint4(g[0], g[1], g[2], g[3]);
+#pragma unroll
+                for (int i = 0; i < TPW; ++i) {
+                    const int j = wave + NW * i;
+                    if (j < Wout) {
+                        f32x16 ao = {};
+                        ao = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(sout_l[i][wave][lane]), as_bf16x8(gfrag), ao, 0, 0, 0);
+                        const uint32_t w = pack_signs(ao, lane);
+                        if (lane < 32) ol[buf][(32 * nh + lane) * orow + Win + j] = w;
+                    }
+                }
+            }
+        }
+        // ---- stage the next chunk into the other buffer (its last readers passed the previous barrier)
+        if (cn < t_end) {
+            stage(kn0, kl[buf ^ 1], tt, cn + tt);
+            stage(kn1, kl[buf ^ 1], tt + 32, cn + tt + 32);
+        }
         __syncthreads();
 
-        // ---- coalesced store of this chunk's packed words (lanes 0..W-1 of each 32-lane row)
+        // ---- coalesced store of this chunk's packed words
         uint32_t* dst = a.bits + (head_row0 + c0) * W;
+        const uint32_t* olb = ol[buf];
         const int w = tid & 31;
         if (w < W)
-            for (int tok = tid >> 5; tok < nvalid; tok += kThreads / 32) dst[tok * W + w] = olb[tok * orow + w];
+            for (int tok = tid >> 5; tok < nvalid; tok += NT / 32) dst[tok * W + w] = olb[tok * orow + w];
         buf ^= 1;
     }
 }
@@ -428,10 +444,9 @@ hipError_t launch_quantize_keys_bf16(const KeyQuantArgs& a, int B, hipStream_t s
         return hipGetLastError();
     }
     const int tiles = (a.m >> 5) > (a.m_out >> 5) ? (a.m >> 5) : (a.m_out >> 5);
-    const int tpw = (tiles + kWaves - 1) / kWaves;
     dim3 grid((unsigned)((a.T + a.tokens_per_block - 1) / a.tokens_per_block), (unsigned)a.Hkv, (unsigned)B);
-    if (tpw <= 1) hipLaunchKernelGGL(quantize_keys_bf16_kernel<1>, grid, dim3(kThreads), 0, s, a);
-    else if (tpw == 2) hipLaunchKernelGGL(quantize_keys_bf16_kernel<2>, grid, dim3(kThreads), 0, s, a);
+    if (tiles <= 8) hipLaunchKernelGGL(quantize_keys_bf16_kernel<1>, grid, dim3(kThreads), 0, s, a);
+    else if (tiles <= 16) hipLaunchKernelGGL(quantize_keys_bf16_kernel<2>, grid, dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL(quantize_keys_bf16_kernel<4>, grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
