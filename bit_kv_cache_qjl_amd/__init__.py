@@ -11,6 +11,8 @@ import ctypes
 import os
 from dataclasses import dataclass
 
+from . import layout  # noqa: F401  (host-side views of the cache layout)
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqjl.so")
 
@@ -97,7 +99,7 @@ class Cache:
 
     bits: object      # int32 view of uint32 [B, Hkv, Ncap, W]
     norms: object     # float16 [B, Hkv, Ncap, 2]
-    codes: object     # uint8 [B, Hkv, Ncap, d*nbits/8]
+    codes: object     # int32 view of uint32 code tiles [B, Hkv, ceil(Ncap/32), d, nbits]
     meta: object      # float16 [B, Hkv, Ncap, 2]
     m: int
     m_out: int
@@ -108,13 +110,18 @@ class Cache:
         return int(self.bits.shape[2])
 
 
+def code_tiles(Ncap: int) -> int:
+    """Number of 32-position code tiles of a cache with capacity Ncap."""
+    return (Ncap + 31) // 32
+
+
 def alloc_cache(B: int, Hkv: int, Ncap: int, m: int, m_out: int, nbits: int = 2, d: int = 128,
                 device="cuda") -> Cache:
     import torch
     W = (m + m_out) // 32
     return Cache(bits=torch.zeros((B, Hkv, Ncap, W), dtype=torch.int32, device=device),
                  norms=torch.zeros((B, Hkv, Ncap, 2), dtype=torch.float16, device=device),
-                 codes=torch.zeros((B, Hkv, Ncap, d * nbits // 8), dtype=torch.uint8, device=device),
+                 codes=torch.zeros((B, Hkv, code_tiles(Ncap), d, nbits), dtype=torch.int32, device=device),
                  meta=torch.zeros((B, Hkv, Ncap, 2), dtype=torch.float16, device=device),
                  m=m, m_out=m_out, nbits=nbits)
 
@@ -134,12 +141,16 @@ def quantize_keys(K, S_in, S_out, outlier_idx, bits, norms, t0: int = 0, stream=
 
 
 def quantize_values(V, nbits: int, codes, meta, t0: int = 0, stream=None) -> None:
-    """qjl_quantize_values on torch tensors.  V [B, T, Hkv, d] (d contiguous)."""
+    """qjl_quantize_values on torch tensors.  V [B, T, Hkv, d] (d contiguous); codes are the code
+    tiles of a cache whose capacity is meta.shape[2]."""
     B, T, Hkv, d = V.shape
     if V.stride(3) != 1:
         raise ValueError("the d channels of V must be contiguous")
+    Ncap = meta.shape[2]
+    if codes.numel() * codes.element_size() < B * Hkv * code_tiles(Ncap) * d * nbits * 4:
+        raise ValueError("codes is smaller than the code tiles of a cache of this capacity")
     _check(lib.qjl_quantize_values(_ptr(V), _dtype_code(V), B, T, Hkv, d, V.stride(0), V.stride(1), V.stride(2),
-                                   nbits, _ptr(codes), _ptr(meta), codes.shape[2], t0, _stream(stream)),
+                                   nbits, _ptr(codes), _ptr(meta), Ncap, t0, _stream(stream)),
            "qjl_quantize_values")
 
 

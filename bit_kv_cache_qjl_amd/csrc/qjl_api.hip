@@ -195,7 +195,7 @@ int qjl_quantize_keys(const void* K, int kdt, int B, int64_t T, int Hkv, int d, 
 }
 
 int qjl_quantize_values(const void* V, int vdt, int B, int64_t T, int Hkv, int d, int64_t sV_b, int64_t sV_t,
-                        int64_t sV_h, int nbits, uint8_t* codes, uint16_t* meta, int64_t Ncap, int64_t t0,
+                        int64_t sV_h, int nbits, uint32_t* codes, uint16_t* meta, int64_t Ncap, int64_t t0,
                         hipStream_t stream) {
     g_last_error.clear();
     if (vdt != QJL_BF16 && vdt != QJL_F32) return fail(QJL_ERR_INVALID_ARG, "vdt=%d is not a qjl_dtype", vdt);
@@ -242,7 +242,7 @@ size_t qjl_decode_workspace_size(int B, int Hq, int Hkv, int d, int64_t N, int m
 
 int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, int64_t N, const void* S_in, int m,
                          const void* S_out, int m_out, const int32_t* outlier_idx, int n_out, const uint32_t* bits,
-                         const uint16_t* norms, int64_t Ncap, int vmode, const uint8_t* codes, const uint16_t* meta,
+                         const uint16_t* norms, int64_t Ncap, int vmode, const uint32_t* codes, const uint16_t* meta,
                          const float* V_f32, int nbits, float sm_scale, float* out, float* scores_dbg, int nsplit,
                          void* workspace, size_t ws_bytes, hipStream_t stream) {
     g_last_error.clear();

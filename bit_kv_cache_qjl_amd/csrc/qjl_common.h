@@ -76,10 +76,15 @@ struct KeyQuantArgs {
     int tokens_per_block;            // multiple of 32
 };
 
+// Value codes live in tiles of kCodeTile consecutive positions: for each channel, the codes of the
+// tile's tokens as an LSB-first bit stream of nbits 32-bit words.
+constexpr int kCodeTile = 32;
+__host__ __device__ constexpr int64_t code_tiles(int64_t Ncap) { return (Ncap + kCodeTile - 1) / kCodeTile; }
+
 struct ValueQuantArgs {
     const void* V;
     int64_t sVb, sVt, sVh;
-    uint8_t* codes;
+    uint32_t* codes;                 // [B*Hkv][code_tiles(Ncap)][kD][nbits]
     uint16_t* meta;
     int64_t T, Ncap, t0;
     int B, Hkv, nbits;
@@ -92,7 +97,7 @@ struct DecodeArgs {
     const int32_t* oidx;
     const uint32_t* bits;
     const uint16_t* norms;
-    const uint8_t* codes;
+    const uint32_t* codes;            // 2-bit code tiles [B*Hkv][code_tiles(Ncap)][kD][2]
     const uint16_t* meta;
     const float* V_f32;
     float* out;

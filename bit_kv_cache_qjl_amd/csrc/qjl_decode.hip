@@ -17,11 +17,12 @@
 //             score  lane = token: buffer loads of the token's sign words, one table read per byte
 //                    (offset from one SDWA shift), s = |k_in| * sum_in + |k_out| * sum_out;
 //             softmax wave-wide running max (log2 domain), p = 2^(z - M), running sums;
-//             value  lane = (16-channel slice, token pair): the 2-bit codes of two tokens become
-//                    fp16 pairs 1 + code/4 with one and-or, and v_dot2_f32_f16 accumulates
-//                    p*step for both tokens at once; the constant 1 is removed at the end
-//                    (sum p*step*(1 + code/4) - sum p*step = sum p*step*code/4), and the min term
-//                    sum p*min is carried separately.
+//             value  lane = two channels: one 16-byte load per 32-token code tile brings the code
+//                    words of both channels; the 2-bit codes of tokens (t, t + 8) of a word become
+//                    an fp16 pair 1 + code/4 with one shift and one and-or, and v_dot2_f32_f16
+//                    accumulates p*step for both tokens at once; the constant 1 is removed at the
+//                    end (sum p*step*(1 + code/4) - sum p*step = sum p*step*code/4), and the min
+//                    term sum p*min is carried separately.
 //           The eight wave states merge into the chunk's partial (max, sum, unnormalized output).
 //   combine one workgroup per (sequence, query head): log-sum-exp merge of the chunk partials.
 #include <math.h>
@@ -161,13 +162,12 @@ struct Slab {
     uint32_t w[WB];      // sign words of this lane's token
     uint32_t nrm;        // (|k_in|, |k_out|) fp16 pair
     uint32_t mt;         // (min, step) fp16 pair
-    uint32_t xv[8];      // value role: code dwords of this lane's token pairs
+    uint32_t xv[8];      // value role: code words of this lane's channel pair in the slab's two tiles
 };
 
 template <int WB, int VM>
 __device__ __forceinline__ void load_slab(Slab<WB, VM>& sl, __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rn,
-                                          __amdgpu_buffer_rsrc_t rm, __amdgpu_buffer_rsrc_t rc, int s0, int lane,
-                                          int jv, int pg) {
+                                          __amdgpu_buffer_rsrc_t rm, __amdgpu_buffer_rsrc_t rc, int s0, int lane) {
     const int t = s0 + lane;
 #pragma unroll
     for (int q = 0; q < WB / 4; ++q) {
@@ -177,11 +177,11 @@ __device__ __forceinline__ void load_slab(Slab<WB, VM>& sl, __amdgpu_buffer_rsrc
     sl.nrm = __builtin_amdgcn_raw_buffer_load_b32(rn, t * 4, 0, 0);
     if (VM == 0) {
         sl.mt = __builtin_amdgcn_raw_buffer_load_b32(rm, t * 4, 0, 0);
+        // tile = [128 channels][2 words] (1 KiB); this lane's channels 2 lane, 2 lane + 1 are 16 bytes
 #pragma unroll
-        for (int pass = 0; pass < 4; ++pass) {
-            const int t1 = s0 + 2 * (pg + 8 * pass);
-            sl.xv[2 * pass] = __builtin_amdgcn_raw_buffer_load_b32(rc, (t1 * 8 + jv) * 4, 0, 0);
-            sl.xv[2 * pass + 1] = __builtin_amdgcn_raw_buffer_load_b32(rc, ((t1 + 1) * 8 + jv) * 4, 0, 0);
+        for (int q = 0; q < 2; ++q) {
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(rc, (s0 / kCodeTile + q) * 1024 + lane * 16, 0, 0);
+            sl.xv[4 * q] = x[0]; sl.xv[4 * q + 1] = x[1]; sl.xv[4 * q + 2] = x[2]; sl.xv[4 * q + 3] = x[3];
         }
     } else {
         sl.mt = 0u;
@@ -256,24 +256,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const __amdgpu_buffer_rsrc_t rn = buffer_rsrc(norms, (uint32_t)t_end * 4u);
     const __amdgpu_buffer_rsrc_t rm = VM == 0 ? buffer_rsrc(reinterpret_cast<const uint32_t*>(a.meta) + (size_t)unit * a.Ncap,
                                                             (uint32_t)t_end * 4u) : rn;
-    const __amdgpu_buffer_rsrc_t rc = VM == 0 ? buffer_rsrc(a.codes + (size_t)unit * a.Ncap * 32, (uint32_t)t_end * 32u) : rn;
+    // code tiles of this (sequence, KV head), bounded at the tile holding the chunk's last token
+    const __amdgpu_buffer_rsrc_t rc = VM == 0 ? buffer_rsrc(a.codes + (size_t)unit * code_tiles(a.Ncap) * (kD * 2),
+                                                            (uint32_t)code_tiles(t_end) * 1024u) : rn;
     const float* vf = VM == 1 ? a.V_f32 + (size_t)unit * a.Ncap * kD : nullptr;
     float* sdbg = a.scores_dbg ? a.scores_dbg + (size_t)bhq * a.N : nullptr;
 
-    const int jv = lane & 7;         // value role: 16-channel slice
-    const int pg = lane >> 3;        // value role: token-pair group of the slab (0..7)
+    const int jv = lane & 7;         // fp32 value role: 16-channel slice
+    const int pg = lane >> 3;        // fp32 value role: token-pair group of the slab (0..7)
     float* wl = wts[wave];
+    // code role: the weight of token tau sits in fp16 pair 8 (tau / 16) + tau % 8, half (tau / 8) % 2,
+    // next to the token 8 positions away that shares its code word
+    const int wslot = 2 * (8 * (lane >> 4) + (lane & 7)) + ((lane >> 3) & 1);
 
     float m_run = -INFINITY;
     float l_t = 0.f, mn_t = 0.f, sw_t = 0.f;   // per-lane partial sums (score role)
-    float acc[16];
+    constexpr int NACC = VM == 0 ? 8 : 16;      // codes: 2 channels x 4 partial sums; fp32: 16 channels
+    float acc[NACC];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) acc[c] = 0.f;
+    for (int c = 0; c < NACC; ++c) acc[c] = 0.f;
 
     const char* lut_b = reinterpret_cast<const char*>(lut);
     for (int s0 = t_begin + kSlab * wave; s0 < t_end; s0 += kSlab * kWaves) {
         Slab<WB, VM> cur;
-        load_slab<WB, VM>(cur, rb, rn, rm, rc, s0, lane, jv, pg);
+        load_slab<WB, VM>(cur, rb, rn, rm, rc, s0, lane);
         const int t = s0 + lane;
         const bool valid = t < t_end;
 
@@ -308,32 +314,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             const _Float16 w16 = (_Float16)(p * step);
             mn_t = fmaf(mn_t, alpha, p * mn);
             sw_t = fmaf(sw_t, alpha, (float)w16);
-            reinterpret_cast<_Float16*>(wl)[lane] = w16;
+            reinterpret_cast<_Float16*>(wl)[wslot] = w16;
         } else {
             wl[lane] = p;
         }
         if (alpha != 1.f) {
 #pragma unroll
-            for (int c = 0; c < 16; ++c) acc[c] *= alpha;
+            for (int c = 0; c < NACC; ++c) acc[c] *= alpha;
         }
         __builtin_amdgcn_wave_barrier();   // the weights written above are read by other lanes below
 
-        // ---- values (lane = 16-channel slice x token pairs of the slab)
+        // ---- values
         if (VM == 0) {
+            // lane = channels 2 lane, 2 lane + 1; word G % 2 of tile G / 2 holds tokens 16 G .. 16 G + 15
             const uint32_t base = 0x3C003C00u, mask = 0x03000300u;
+            const uint4* wq = reinterpret_cast<const uint4*>(wl);
 #pragma unroll
-            for (int pass = 0; pass < 4; ++pass) {
-                const int pr = pg + 8 * pass;
-                const half2_t wp = __builtin_bit_cast(half2_t, reinterpret_cast<const uint32_t*>(wl)[pr]);
-                const uint32_t x1 = cur.xv[2 * pass], x2 = cur.xv[2 * pass + 1];
-                const uint32_t ylo = __builtin_amdgcn_perm(x2, x1, 0x05040100u);
-                const uint32_t yhi = __builtin_amdgcn_perm(x2, x1, 0x07060302u);
+            for (int G = 0; G < 4; ++G) {
+                const uint4 wa = wq[2 * G], wb = wq[2 * G + 1];   // pairs (t, t + 8), t = 0..7
+                const uint32_t wpair[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const uint32_t sl = c <= 4 ? (ylo << (8 - 2 * c)) : (ylo >> (2 * c - 8));
-                    const uint32_t sh = c <= 4 ? (yhi << (8 - 2 * c)) : (yhi >> (2 * c - 8));
-                    acc[c] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, and_or(sl, mask, base)), wp, acc[c], false);
-                    acc[8 + c] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, and_or(sh, mask, base)), wp, acc[8 + c], false);
+                for (int ch = 0; ch < 2; ++ch) {
+                    const uint32_t x = cur.xv[4 * (G >> 1) + 2 * ch + (G & 1)];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const uint32_t y = t <= 4 ? (x << (8 - 2 * t)) : (x >> (2 * t - 8));
+                        acc[4 * ch + (t & 3)] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, and_or(y, mask, base)),
+                                                                       __builtin_bit_cast(half2_t, wpair[t]),
+                                                                       acc[4 * ch + (t & 3)], false);
+                    }
                 }
             }
         } else {
@@ -374,13 +383,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         red[wave][1] = mn_sum;
         red[wave][2] = sw_sum;
     }
-    float* rbuf = lut;   // [64 = wave x pair group][128 channels]
+    float* rbuf = lut;
+    int nrows;
+    if (VM == 0) {   // [8 waves][128 channels]
 #pragma unroll
-    for (int c = 0; c < 16; ++c) rbuf[(wave * 8 + pg) * kD + 16 * jv + c] = acc[c] * sc;
+        for (int ch = 0; ch < 2; ++ch)
+            rbuf[wave * kD + 2 * lane + ch] = ((acc[4 * ch] + acc[4 * ch + 1]) + (acc[4 * ch + 2] + acc[4 * ch + 3])) * sc;
+        nrows = kWaves;
+    } else {         // [64 = wave x pair group][128 channels]
+#pragma unroll
+        for (int c = 0; c < 16; ++c) rbuf[(wave * 8 + pg) * kD + 16 * jv + c] = acc[c] * sc;
+        nrows = kThreads / 8;
+    }
     __syncthreads();
     if (tid < kD) {
         float tot = 0.f;
-        for (int i = 0; i < kThreads / 8; ++i) tot += rbuf[i * kD + tid];
+        for (int i = 0; i < nrows; ++i) tot += rbuf[i * kD + tid];
         float L = 0.f, MN = 0.f, SW = 0.f;
 #pragma unroll
         for (int i = 0; i < kWaves; ++i) {

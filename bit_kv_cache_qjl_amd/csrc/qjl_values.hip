@@ -4,15 +4,23 @@
 // (take the range of the vector, divide it into 2^b equally spaced values, round each number to the
 // nearest) and the QJL summary, "Limitations" (values use token-wise quantization).
 //
-// Sixteen threads own one value vector (8 channels each): a 16-lane min/max butterfly, then every
-// thread emits 8 codes (nbits bytes).  The decisions are IEEE fp32 operations with no contraction:
-// subtract, correctly rounded divide, fp16 round-to-nearest-even, rint (ties to even).
+// One workgroup per (sequence, KV head, 32-token code tile) touched by the append.  Phase 1: sixteen
+// threads own one value vector (8 channels each): a 16-lane min/max butterfly, the (min, step) meta,
+// and the codes of 8 channels into LDS.  Phase 2: one thread per channel packs the tile's 32 codes of
+// its channel into nbits words (the channel-major tile the decode kernels read as matrix-core
+// operands).  A tile wholly inside the append is stored; a tile the append covers only in part is
+// merged bit-exactly with two atomics per word (clear the appended fields, then set them), so tokens
+// outside [t0, t0 + T) keep their codes.
+//
+// The decisions are IEEE fp32 operations with no contraction: subtract, correctly rounded divide,
+// fp16 round-to-nearest-even, rint (ties to even).
 #include "qjl_common.h"
 
 namespace qjl {
 namespace {
 
-constexpr int kRowsPerBlock = 16;
+constexpr int kValThreads = kCodeTile * 16;   // 512
+constexpr int kRowPitch = kCodeTile + 4;      // bytes per channel row of the LDS code tile
 
 template <typename VT>
 __device__ __forceinline__ void load8(const VT* p, float (&v)[8]);
@@ -37,20 +45,21 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
 }
 
 template <typename VT, int NBITS>
-__global__ __launch_bounds__(256) void quantize_values_kernel(ValueQuantArgs a) {
+__global__ __launch_bounds__(kValThreads) void quantize_values_kernel(ValueQuantArgs a, int64_t tile_first, int ntiles) {
 #pragma clang fp contract(off)
+    __shared__ __attribute__((aligned(16))) uint8_t cs[kD * kRowPitch];   // [channel][token of the tile]
     const int tid = threadIdx.x;
     const int sub = tid & 15;
-    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (tid >> 4);
-    const int64_t rows = (int64_t)a.B * a.T * a.Hkv;
-    const bool valid = row < rows;
-    const int h = (int)(row % a.Hkv);
-    const int64_t bt = row / a.Hkv;
-    const int64_t t = bt % a.T;
-    const int64_t b = bt / a.T;
+    const int tk = tid >> 4;
+    const int64_t bh = blockIdx.x / ntiles;           // b * Hkv + h
+    const int64_t tile = tile_first + (int)(blockIdx.x % ntiles);
+    const int h = (int)(bh % a.Hkv);
+    const int64_t b = bh / a.Hkv;
+    const int64_t pos = tile * kCodeTile + tk;        // cache position of this thread's token
+    const bool valid = pos >= a.t0 && pos < a.t0 + a.T;
 
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (valid) load8<VT>(static_cast<const VT*>(a.V) + b * a.sVb + t * a.sVt + h * a.sVh + 8 * sub, v);
+    if (valid) load8<VT>(static_cast<const VT*>(a.V) + b * a.sVb + (pos - a.t0) * a.sVt + h * a.sVh + 8 * sub, v);
     float mn = v[0], mx = v[0];
 #pragma unroll
     for (int q = 1; q < 8; ++q) {
@@ -66,7 +75,6 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(ValueQuantArgs a) 
     const _Float16 mn16 = (_Float16)mn;
     const float step = (float)step16;
     const float base = (float)mn16;
-    uint32_t packed = 0;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         uint32_t code = 0;
@@ -75,33 +83,65 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(ValueQuantArgs a) 
             const float r = rintf(diff / step);
             code = (uint32_t)fminf(fmaxf(r, 0.f), (float)L);
         }
-        packed |= code << (NBITS * q);
+        cs[(8 * sub + q) * kRowPitch + tk] = (uint8_t)code;
     }
-    if (!valid) return;
-    const int64_t cache_row = ((int64_t)b * a.Hkv + h) * a.Ncap + a.t0 + t;
-    uint8_t* dst = a.codes + cache_row * (16 * NBITS) + sub * NBITS;
-    if (NBITS == 2) {
-        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
-    } else if (NBITS == 4) {
-        *reinterpret_cast<uint32_t*>(dst) = packed;
+    if (valid && sub == 0) {
+        reinterpret_cast<uint32_t*>(a.meta)[bh * a.Ncap + pos] =
+            (uint32_t)__builtin_bit_cast(uint16_t, mn16) | ((uint32_t)__builtin_bit_cast(uint16_t, step16) << 16);
+    }
+    __syncthreads();
+
+    if (tid >= kD) return;
+    const int c = tid;
+    uint32_t wd[NBITS], msk[NBITS];
+#pragma unroll
+    for (int k = 0; k < NBITS; ++k) wd[k] = msk[k] = 0u;
+    const int64_t p0 = tile * kCodeTile;
+    const uint32_t* row = reinterpret_cast<const uint32_t*>(cs + c * kRowPitch);
+#pragma unroll
+    for (int q = 0; q < kCodeTile / 4; ++q) {
+        const uint32_t four = row[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 4 * q + e;
+            const uint32_t code = (four >> (8 * e)) & 0xFFu;
+            const bool in = p0 + i >= a.t0 && p0 + i < a.t0 + a.T;
+            constexpr uint32_t fm = (1u << NBITS) - 1u;
+            const int bp = NBITS * i;
+            wd[bp >> 5] |= code << (bp & 31);
+            if (in) msk[bp >> 5] |= fm << (bp & 31);
+            if ((bp & 31) + NBITS > 32) {   // the field continues in the next word
+                wd[(bp >> 5) + 1] |= code >> (32 - (bp & 31));
+                if (in) msk[(bp >> 5) + 1] |= fm >> (32 - (bp & 31));
+            }
+        }
+    }
+    uint32_t* dst = a.codes + ((size_t)bh * code_tiles(a.Ncap) + tile) * (kD * NBITS) + c * NBITS;
+    const bool full = p0 >= a.t0 && p0 + kCodeTile <= a.t0 + a.T;
+    if (full) {
+#pragma unroll
+        for (int k = 0; k < NBITS; ++k) dst[k] = wd[k];
     } else {
 #pragma unroll
-        for (int q = 0; q < NBITS; ++q) dst[q] = (uint8_t)(packed >> (8 * q));
-    }
-    if (sub == 0) {
-        reinterpret_cast<uint32_t*>(a.meta)[cache_row] =
-            (uint32_t)__builtin_bit_cast(uint16_t, mn16) | ((uint32_t)__builtin_bit_cast(uint16_t, step16) << 16);
+        for (int k = 0; k < NBITS; ++k) {
+            if (msk[k]) {
+                atomicAnd(dst + k, ~msk[k]);
+                atomicOr(dst + k, wd[k] & msk[k]);
+            }
+        }
     }
 }
 
 template <typename VT>
 hipError_t launch_typed(const ValueQuantArgs& a, hipStream_t s) {
-    const int64_t rows = (int64_t)a.B * a.T * a.Hkv;
-    const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+    const int64_t first = a.t0 / kCodeTile;
+    const int64_t last = (a.t0 + a.T - 1) / kCodeTile;
+    const int ntiles = (int)(last - first + 1);
+    const dim3 grid((unsigned)((int64_t)a.B * a.Hkv * ntiles));
     switch (a.nbits) {
-        case 2: hipLaunchKernelGGL((quantize_values_kernel<VT, 2>), grid, dim3(256), 0, s, a); break;
-        case 3: hipLaunchKernelGGL((quantize_values_kernel<VT, 3>), grid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((quantize_values_kernel<VT, 4>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((quantize_values_kernel<VT, 2>), grid, dim3(kValThreads), 0, s, a, first, ntiles); break;
+        case 3: hipLaunchKernelGGL((quantize_values_kernel<VT, 3>), grid, dim3(kValThreads), 0, s, a, first, ntiles); break;
+        default: hipLaunchKernelGGL((quantize_values_kernel<VT, 4>), grid, dim3(kValThreads), 0, s, a, first, ntiles); break;
     }
     return hipGetLastError();
 }

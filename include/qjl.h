@@ -35,8 +35,11 @@
  *         32 w + i is >= 0 (sign(0) taken as +1); words 0 .. m/32-1 hold the inlier sketch,
  *         words m/32 .. W-1 the outlier sketch.
  *   norms fp16  [B][Hkv][Ncap][2]: (|k_in|, |k_out|) as IEEE binary16 round-to-nearest-even.
- *   codes uint8 [B][Hkv][Ncap][d*nbits/8]: the value codes of one token as an LSB-first bit
- *         stream, code of channel c in bits [nbits*c, nbits*c + nbits).
+ *   codes uint32 [B][Hkv][Ncap32/32][d][nbits], Ncap32 = Ncap rounded up to a multiple of 32: the
+ *         positions are grouped in tiles of 32 (tile i covers positions 32 i .. 32 i + 31); for each
+ *         channel c, in order, a tile holds the codes of its 32 positions as an LSB-first bit stream
+ *         of nbits words (position 32 i + j in bits [nbits*j, nbits*j + nbits) of the stream).
+ *         Channel-major tiles let the decode kernels feed the codes to the matrix cores directly.
  *   meta  fp16  [B][Hkv][Ncap][2]: (min, step) of the token's value vector.
  */
 #ifndef QJL_H
@@ -108,11 +111,15 @@ int qjl_quantize_keys(const void* K, int kdt, int B, int64_t T, int Hkv, int d,
  *     dequantized value = mn16 + step * code.
  *   V      values in the model layout with element strides (sV_b, sV_t, sV_h), dtype vdt.
  *   nbits  2, 3 or 4.
- *   codes  uint8 [B][Hkv][Ncap][d*nbits/8]; meta fp16 [B][Hkv][Ncap][2] = (mn16, step).
+ *   codes  the code tiles (layout above) of a cache with capacity Ncap; meta fp16 [B][Hkv][Ncap][2]
+ *          = (mn16, step).  Only the code fields and meta of positions [t0, t0 + T) are written;
+ *          every other position keeps its contents (a tile the append covers in part is merged
+ *          with atomic and/or on its words, so appends to disjoint positions of one tile must not
+ *          run concurrently on different streams).
  */
 int qjl_quantize_values(const void* V, int vdt, int B, int64_t T, int Hkv, int d,
                         int64_t sV_b, int64_t sV_t, int64_t sV_h, int nbits,
-                        uint8_t* codes, uint16_t* meta, int64_t Ncap, int64_t t0,
+                        uint32_t* codes, uint16_t* meta, int64_t Ncap, int64_t t0,
                         hipStream_t stream);
 
 /*
@@ -151,7 +158,7 @@ int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, 
                          const void* S_in, int m, const void* S_out, int m_out,
                          const int32_t* outlier_idx, int n_out,
                          const uint32_t* bits, const uint16_t* norms, int64_t Ncap,
-                         int vmode, const uint8_t* codes, const uint16_t* meta, const float* V_f32,
+                         int vmode, const uint32_t* codes, const uint16_t* meta, const float* V_f32,
                          int nbits, float sm_scale, float* out, float* scores_dbg, int nsplit,
                          void* workspace, size_t ws_bytes, hipStream_t stream);
 

@@ -52,6 +52,19 @@ def bits_np(t):
     return t.cpu().numpy().view(np.uint32)
 
 
+def code_tiles_of_rows(rows: np.ndarray, nbits: int, ncap: int | None = None, d: int = 128) -> np.ndarray:
+    """Oracle codes (per-token LSB-first bytes [..., n, d*nbits/8]) -> the library's code tiles."""
+    from bit_kv_cache_qjl_amd import layout
+    return layout.tiles_from_codes(oracle.unpack_codes(rows, nbits, d), nbits, ncap)
+
+
+def code_rows_of_tiles(tiles, nbits: int, n: int) -> np.ndarray:
+    """The library's code tiles (device tensor or array) -> oracle-format rows [..., n, d*nbits/8]."""
+    from bit_kv_cache_qjl_amd import layout
+    t = tiles.cpu().numpy() if hasattr(tiles, "cpu") else tiles
+    return oracle.pack_codes(layout.codes_from_tiles(t, nbits, n), nbits)
+
+
 def compare_bits(gpu_bits: np.ndarray, ref: dict, what: str, nbits_total: int):
     """Bit-exact except where the oracle flags |S k| < 1e-5 |k|; returns (mismatches, flagged)."""
     g = oracle.unpack_bits(gpu_bits, nbits_total)
@@ -100,7 +113,8 @@ def run_decode(qjl, w, Q, S_in, S_out, oidx, cache_np: dict, N: int, *, nsplit=0
     if V_f32 is not None:
         kw["V_f32"] = torch.from_numpy(np.ascontiguousarray(V_f32, dtype=np.float32)).cuda()
     else:
-        kw["codes"] = torch.from_numpy(cache_np["codes"]).cuda()
+        tiles = code_tiles_of_rows(cache_np["codes"], w.nbits, bits.shape[2], w.d)
+        kw["codes"] = torch.from_numpy(tiles.view(np.int32)).cuda()
         kw["meta"] = torch.from_numpy(cache_np["meta"]).cuda()
     qjl.decode_attention(to_dev(Q, w.dtype), to_dev(S_in, w.dtype), to_dev(S_out, w.dtype) if w.m_out else None,
                          torch.from_numpy(oidx).cuda() if w.n_out else None, bits, norms, N, out,

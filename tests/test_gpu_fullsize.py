@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import seeded_inputs as si
-from gpu_util import check_decode, compare_bits, compare_norms, log, to_dev
+from gpu_util import check_decode, code_rows_of_tiles, compare_bits, compare_norms, log, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -58,7 +58,8 @@ def test_full_size_decode_step(name):
     rv = oracle.quantize_values(last_v, w.nbits)
     compare_bits(cache.bits[:, :, N - 1:].cpu().numpy().view(np.uint32), rk, "appended token", w.m + w.m_out)
     compare_norms(cache.norms[:, :, N - 1:].cpu().numpy(), rk["norms"], "appended token")
-    np.testing.assert_array_equal(cache.codes[:, :, N - 1:].cpu().numpy(), rv["codes"])
+    last_tile = code_rows_of_tiles(cache.codes[:, :, (N - 1) // 32: (N - 1) // 32 + 1], w.nbits, 32)
+    np.testing.assert_array_equal(last_tile[:, :, (N - 1) % 32:(N - 1) % 32 + 1], rv["codes"])
     np.testing.assert_array_equal(cache.meta[:, :, N - 1:].cpu().numpy().view(np.uint16), rv["meta"].view(np.uint16))
 
     units = _units(w, 2, w.seed)
@@ -73,7 +74,7 @@ def test_full_size_decode_step(name):
         compare_bits(cache.bits[b, h].cpu().numpy().view(np.uint32), {"bits": r["bits"], "near_zero": r["near_zero"]},
                      f"unit ({b},{h}) bits", w.m + w.m_out)
         compare_norms(cache.norms[b, h].cpu().numpy(), r["norms"], f"unit ({b},{h})")
-        np.testing.assert_array_equal(cache.codes[b, h].cpu().numpy(), packed)
+        np.testing.assert_array_equal(code_rows_of_tiles(cache.codes[b, h], w.nbits, N), packed)
         np.testing.assert_array_equal(cache.meta[b, h].cpu().numpy().view(np.uint16), meta.view(np.uint16))
         # identical decode inputs on both sides
         cache.bits[b, h] = torch.from_numpy(r["bits"].view(np.int32)).cuda()

@@ -10,8 +10,8 @@ import pytest
 
 import oracle
 import seeded_inputs as si
-from gpu_util import (bits_np, check_decode, compare_bits, compare_norms, gpu_quantize_keys, inputs, log,
-                      run_decode, to_dev)
+from gpu_util import (bits_np, check_decode, code_rows_of_tiles, compare_bits, compare_norms, gpu_quantize_keys,
+                      inputs, log, run_decode, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -122,11 +122,35 @@ def test_quantize_values_parity(dtype, nbits):
     qjl.quantize_values(torch_v, nbits, cache.codes, cache.meta, t0=3)
     torch.cuda.synchronize()
     ref = oracle.quantize_values(V, nbits)
-    codes = cache.codes.cpu().numpy()[:, :, 3:]
+    rows = code_rows_of_tiles(cache.codes, nbits, w.N + 3)
     meta = cache.meta.cpu().numpy()[:, :, 3:]
     np.testing.assert_array_equal(meta.view(np.uint16), ref["meta"].view(np.uint16))
-    np.testing.assert_array_equal(codes, ref["codes"])
-    assert not cache.codes[:, :, :3].any()
+    np.testing.assert_array_equal(rows[:, :, 3:], ref["codes"])
+    assert not rows[:, :, :3].any(), "wrote codes before t0"
+    assert not cache.meta[:, :, :3].any(), "wrote meta before t0"
+
+
+@pytest.mark.parametrize("nbits", [2, 3])
+def test_quantize_values_appends_keep_neighbours(nbits):
+    """Appends that start and end inside code tiles (single tokens, short runs, a run across tiles)
+    merge into the tiles without touching other positions; the result equals one bulk quantize."""
+    w = SCALED["llama2_7b_decode"].scaled(nbits=nbits, N=150)
+    V = si.values(w)
+    Vd = to_dev(V, w.dtype)
+    cache = qjl.alloc_cache(w.B, w.Hkv, w.N, w.m, w.m_out, nbits)
+    cache.codes.fill_(-1)                                  # garbage everywhere: only writes may change it
+    log(f"[quantize_values] piecewise appends nbits={nbits}")
+    for a, b in [(0, 1), (1, 5), (5, 31), (31, 33), (33, 34), (34, 97), (97, 149), (149, 150)]:
+        qjl.quantize_values(Vd[:, a:b], nbits, cache.codes, cache.meta, t0=a)
+    torch.cuda.synchronize()
+    ref = oracle.quantize_values(V, nbits)
+    rows = code_rows_of_tiles(cache.codes, nbits, w.N)
+    np.testing.assert_array_equal(rows, ref["codes"])
+    np.testing.assert_array_equal(cache.meta.cpu().numpy().view(np.uint16), ref["meta"].view(np.uint16))
+    # the tail of the last tile (positions 150..159) was never appended: still all ones
+    from bit_kv_cache_qjl_amd import layout
+    tail = layout.codes_from_tiles(cache.codes.cpu().numpy(), nbits, 160)[:, :, 150:]
+    assert np.all(tail == 2 ** nbits - 1)
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "llama2_7b_decode", "llama3_8b_gqa_decode", "llama31_70b_gqa_decode"])
@@ -207,7 +231,7 @@ def test_decode_step_append_then_attend():
     kq = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
     vq = oracle.quantize_values(x["V"], w.nbits)
     compare_bits(bits_np(cache.bits), kq, "pipeline", w.m + w.m_out)
-    np.testing.assert_array_equal(cache.codes.cpu().numpy(), vq["codes"])
+    np.testing.assert_array_equal(code_rows_of_tiles(cache.codes, w.nbits, N), vq["codes"])
     # decode input must be identical on both sides: use the oracle cache where a near-zero bit differs
     gbits = bits_np(cache.bits)
     if np.array_equal(gbits, kq["bits"]) and np.array_equal(cache.norms.cpu().numpy().view(np.uint16),
