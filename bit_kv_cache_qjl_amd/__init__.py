@@ -76,6 +76,13 @@ def _stream(stream) -> int:
     return int(s.cuda_stream)
 
 
+def _contiguous(**tensors) -> None:
+    """The C ABI takes row-major arrays: refuse strided views instead of reading the wrong bytes."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor (row-major layout of include/qjl.h)")
+
+
 def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.bfloat16:
@@ -131,6 +138,7 @@ def quantize_keys(K, S_in, S_out, outlier_idx, bits, norms, t0: int = 0, stream=
     B, T, Hkv, d = K.shape
     if K.stride(3) != 1:
         raise ValueError("the d channels of K must be contiguous")
+    _contiguous(S_in=S_in, S_out=S_out, outlier_idx=outlier_idx, bits=bits, norms=norms)
     m = S_in.shape[0]
     m_out = 0 if S_out is None else S_out.shape[0]
     n_out = 0 if outlier_idx is None or outlier_idx.numel() == 0 else outlier_idx.shape[1]
@@ -146,6 +154,7 @@ def quantize_values(V, nbits: int, codes, meta, t0: int = 0, stream=None) -> Non
     B, T, Hkv, d = V.shape
     if V.stride(3) != 1:
         raise ValueError("the d channels of V must be contiguous")
+    _contiguous(codes=codes, meta=meta)
     Ncap = meta.shape[2]
     if codes.numel() * codes.element_size() < B * Hkv * code_tiles(Ncap) * d * nbits * 4:
         raise ValueError("codes is smaller than the code tiles of a cache of this capacity")
@@ -166,6 +175,8 @@ def decode_attention(Q, S_in, S_out, outlier_idx, bits, norms, N: int, out, *, c
     B, Hq, d = Q.shape
     if not Q.is_contiguous():
         raise ValueError("Q must be contiguous [B, Hq, d]")
+    _contiguous(S_in=S_in, S_out=S_out, outlier_idx=outlier_idx, bits=bits, norms=norms, out=out, codes=codes,
+                meta=meta, V_f32=V_f32, scores_dbg=scores_dbg, workspace=workspace)
     Hkv = bits.shape[1]
     m = S_in.shape[0]
     m_out = 0 if S_out is None else S_out.shape[0]

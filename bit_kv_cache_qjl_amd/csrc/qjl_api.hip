@@ -41,7 +41,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int check_sketch_shape(int d, int m, int m_out, int n_out) {
     if (m <= 0 || m_out < 0 || n_out < 0) return fail(QJL_ERR_INVALID_ARG, "m=%d m_out=%d n_out=%d must be >= 0 (m > 0)", m, m_out, n_out);
     if (d != qjl::kD) return fail(QJL_ERR_UNSUPPORTED, "d=%d unsupported (only d=128)", d);
-    if (m % 32 || m_out % 32) return fail(QJL_ERR_UNSUPPORTED, "m=%d and m_out=%d must be multiples of 32", m, m_out);
+    if (m % 128 || m_out % 128) return fail(QJL_ERR_UNSUPPORTED, "m=%d and m_out=%d must be multiples of 128", m, m_out);
     if (m + m_out > qjl::kMaxBits) return fail(QJL_ERR_UNSUPPORTED, "m + m_out = %d exceeds %d", m + m_out, qjl::kMaxBits);
     if (n_out > qjl::kMaxOutliers) return fail(QJL_ERR_UNSUPPORTED, "n_out=%d exceeds %d", n_out, qjl::kMaxOutliers);
     if (n_out > 0 && m_out == 0) return fail(QJL_ERR_INVALID_ARG, "n_out=%d outlier channels need an outlier sketch (m_out > 0)", n_out);
@@ -236,7 +236,7 @@ size_t qjl_decode_workspace_size(int B, int Hq, int Hkv, int d, int64_t N, int m
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || N < 0 || m <= 0 || m_out < 0 || d <= 0) return 0;
     const int g = Hq / Hkv;
     const int ns = nsplit > 0 ? nsplit : qjl::decode_pick_nsplit(B, Hkv, g, N, m, m_out);
-    return align256((size_t)B * Hq * (m + m_out) * sizeof(float)) +
+    return align256((size_t)B * Hq * (m + m_out) * sizeof(float)) + align256((size_t)B * Hq * 4 * sizeof(float)) +
            align256((size_t)B * Hq * ns * (d + 2) * sizeof(float));
 }
 
@@ -268,6 +268,7 @@ int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, 
         (vmode == QJL_V_CODES && (!aligned16(codes) || !aligned16(meta))) || (vmode == QJL_V_F32 && !aligned16(V_f32)))
         return fail(QJL_ERR_MISALIGNED, "device pointers must be 16-byte aligned");
     const int g = Hq / Hkv;
+    if (nsplit > qjl::kMaxSplits) return fail(QJL_ERR_UNSUPPORTED, "nsplit=%d exceeds %d", nsplit, qjl::kMaxSplits);
     const int ns = nsplit > 0 ? nsplit : qjl::decode_pick_nsplit(B, Hkv, g, N, m, m_out);
     const size_t need = qjl_decode_workspace_size(B, Hq, Hkv, d, N, m, m_out, ns);
     if (!workspace || ws_bytes < need)
@@ -285,7 +286,9 @@ int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, 
     a.out = out;
     a.scores_dbg = scores_dbg;
     a.sq = static_cast<float*>(workspace);
-    a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)B * Hq * (m + m_out) * sizeof(float)));
+    const size_t sq_bytes = align256((size_t)B * Hq * (m + m_out) * sizeof(float));
+    a.qconst = reinterpret_cast<float*>(static_cast<char*>(workspace) + sq_bytes);
+    a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + sq_bytes + align256((size_t)B * Hq * 4 * sizeof(float)));
     a.N = N;
     a.Ncap = Ncap;
     a.B = B;

@@ -76,10 +76,30 @@ struct KeyQuantArgs {
     int tokens_per_block;            // multiple of 32
 };
 
+// Sign words of a token row: natural word w holds projections 32 w .. 32 w + 31 (inlier words
+// 0 .. win-1, outlier words win .. win+wout-1).  The row is stored as 4 groups of (win + wout)/4
+// words; group j holds inlier words j win/4 .. (j+1) win/4 - 1, then outlier words
+// win + j wout/4 .. win + (j+1) wout/4 - 1 (win and wout multiples of 4).  One 4-, 8- or 16-byte load
+// then gives each lane group of a matrix-core operand its inlier and outlier words.
+__host__ __device__ constexpr int bits_slot(int w, int win, int wout) {
+    return w < win ? (w / (win >> 2)) * ((win + wout) >> 2) + w % (win >> 2)
+                   : ((w - win) / (wout >> 2)) * ((win + wout) >> 2) + (win >> 2) + (w - win) % (wout >> 2);
+}
+// natural word held by stored slot s (inverse of bits_slot)
+__host__ __device__ constexpr int bits_word(int s, int win, int wout) {
+    return (s % ((win + wout) >> 2)) < (win >> 2)
+               ? (s / ((win + wout) >> 2)) * (win >> 2) + s % ((win + wout) >> 2)
+               : win + (s / ((win + wout) >> 2)) * (wout >> 2) + (s % ((win + wout) >> 2)) - (win >> 2);
+}
+
 // Value codes live in tiles of kCodeTile consecutive positions: for each channel, the codes of the
-// tile's tokens as an LSB-first bit stream of nbits 32-bit words.
+// tile's tokens as an LSB-first bit stream of nbits 32-bit words.  The 128 channel streams of a tile
+// are stored in the order slot p = 8 (c % 16) + c / 16 (channel c = 16 (p % 8) + p / 8), so the
+// channels 16 cg + t (cg = 0..7) of one matrix-core column t are 8 consecutive streams.
 constexpr int kCodeTile = 32;
 __host__ __device__ constexpr int64_t code_tiles(int64_t Ncap) { return (Ncap + kCodeTile - 1) / kCodeTile; }
+__host__ __device__ constexpr int code_slot(int c) { return 8 * (c & 15) + (c >> 4); }
+__host__ __device__ constexpr int code_channel(int p) { return 16 * (p & 7) + (p >> 3); }
 
 struct ValueQuantArgs {
     const void* V;
@@ -102,7 +122,9 @@ struct DecodeArgs {
     const float* V_f32;
     float* out;
     float* scores_dbg;
-    float* sq;                        // workspace: projected queries [B*Hq][m + m_out]
+    float* sq;                        // workspace: projected queries [B*Hq][m + m_out] (table path), or
+                                      // the matrix-core query operand, 4 (m + m_out) bytes per head
+    float* qconst;                    // workspace: per-head constants [B*Hq][4] of the matrix-core path
     float* part;                      // workspace: partials [B*Hq][nsplit][d + 2]
     int64_t N, Ncap;
     int B, Hq, Hkv, g, m, m_out, n_out, nsplit;
@@ -118,11 +140,16 @@ hipError_t launch_quantize_keys_bf16(const KeyQuantArgs& a, int B, hipStream_t s
 hipError_t launch_quantize_keys_f32(const KeyQuantArgs& a, int B, hipStream_t s);
 hipError_t launch_quantize_values(const ValueQuantArgs& a, int vdt, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int qdt, int vmode, hipStream_t s);
+// query operand + matrix-core decode kernel (partials only; launch_decode adds the merge)
+hipError_t launch_decode_mfma(const DecodeArgs& a, int qdt, hipStream_t s);
 
 // Decode geometry shared by the workspace-size query and the launcher.
 constexpr int kDecodeTile = 512;     // tokens per tile = threads per decode block
+constexpr int kMaxSplits = 4096;     // context chunks per (sequence, query head)
 int decode_pick_nsplit(int B, int Hkv, int g, int64_t N, int m, int m_out);
 int64_t decode_chunk(int64_t N, int nsplit);
+// True when decode runs on the matrix-core path (2-bit value codes, W = (m + m_out)/32 <= 16).
+bool decode_uses_mfma(int m, int m_out, int vmode, int nbits);
 
 // Launch timer hooks (no-ops unless enabled).
 void timer_begin(TimedKernel k, hipStream_t s);

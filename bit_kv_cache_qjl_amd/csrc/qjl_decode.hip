@@ -18,7 +18,7 @@
 //                    (offset from one SDWA shift), s = |k_in| * sum_in + |k_out| * sum_out;
 //             softmax wave-wide running max (log2 domain), p = 2^(z - M), running sums;
 //             value  lane = two channels: one 16-byte load per 32-token code tile brings the code
-//                    words of both channels; the 2-bit codes of tokens (t, t + 8) of a word become
+//                    words of both channel streams; the 2-bit codes of tokens (t, t + 8) of a word become
 //                    an fp16 pair 1 + code/4 with one shift and one and-or, and v_dot2_f32_f16
 //                    accumulates p*step for both tokens at once; the constant 1 is removed at the
 //                    end (sum p*step*(1 + code/4) - sum p*step = sum p*step*code/4), and the min
@@ -27,7 +27,7 @@
 //   combine one workgroup per (sequence, query head): log-sum-exp merge of the chunk partials.
 #include <math.h>
 
-#include "qjl_common.h"
+#include "qjl_decode_common.h"
 
 namespace qjl {
 namespace {
@@ -38,43 +38,6 @@ constexpr int kThreads = kDecodeTile;   // 512
 constexpr int kWaves = kThreads / 64;
 
 // ------------------------------------------------------------------------------------ qproj
-template <typename QT>
-__device__ __forceinline__ float load_elem(const QT* p, size_t i);
-template <>
-__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, size_t i) {
-    return __uint_as_float((uint32_t)p[i] << 16);
-}
-template <>
-__device__ __forceinline__ float load_elem<float>(const float* p, size_t i) { return p[i]; }
-
-// dot of one JL row (d = 128 values of type QT) with the masked query in LDS, fp32 in channel order
-__device__ __forceinline__ float row_dot(const uint16_t* row, const float* q) {
-    float acc = 0.f;
-#pragma unroll
-    for (int v = 0; v < kD / 8; ++v) {
-        const uint4 x = reinterpret_cast<const uint4*>(row)[v];
-        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc = fmaf(__uint_as_float(w[e] << 16), q[8 * v + 2 * e], acc);
-            acc = fmaf(__uint_as_float(w[e] & 0xFFFF0000u), q[8 * v + 2 * e + 1], acc);
-        }
-    }
-    return acc;
-}
-__device__ __forceinline__ float row_dot(const float* row, const float* q) {
-    float acc = 0.f;
-#pragma unroll
-    for (int v = 0; v < kD / 4; ++v) {
-        const float4 x = reinterpret_cast<const float4*>(row)[v];
-        acc = fmaf(x.x, q[4 * v], acc);
-        acc = fmaf(x.y, q[4 * v + 1], acc);
-        acc = fmaf(x.z, q[4 * v + 2], acc);
-        acc = fmaf(x.w, q[4 * v + 3], acc);
-    }
-    return acc;
-}
-
 template <typename QT>
 __global__ __launch_bounds__(256) void qproj_kernel(DecodeArgs a) {
     __shared__ float qin[kD];
@@ -130,39 +93,13 @@ __device__ __forceinline__ float wave_sum(float v) { return wave64_sum(v); }
 
 constexpr int kSlab = 64;                    // tokens per wave step
 
-// Log-sum-exp merge of the chunk partials (max, sum, unnormalized output) of one query head;
-// thread c writes output channel c.
-__device__ __forceinline__ void merge_partials(const DecodeArgs& a, int bhq, int c) {
-    const float* src = a.part + (size_t)bhq * a.nsplit * (kD + 2);
-    float mmax = -INFINITY;
-    for (int i = 0; i < a.nsplit; ++i) mmax = fmaxf(mmax, src[(size_t)i * (kD + 2)]);
-    float l = 0.f, o = 0.f;
-    if (mmax != -INFINITY) {
-        for (int i = 0; i < a.nsplit; ++i) {
-            const float* pp = src + (size_t)i * (kD + 2);
-            const float mi = pp[0];
-            if (mi == -INFINITY) continue;
-            const float sc = exp2f(mi - mmax);
-            l = fmaf(sc, pp[1], l);
-            o = fmaf(sc, pp[2 + c], o);
-        }
-    }
-    a.out[(size_t)bhq * kD + c] = l > 0.f ? o / l : 0.f;
-}
-
-// Raw buffer resource over [base, base + bytes): loads at or past the end return zero, which is how
-// the kernels treat the ragged end of a chunk (no branches, no clamped addresses).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
 // Token data of one wave step.
 template <int WB, int VM>
 struct Slab {
     uint32_t w[WB];      // sign words of this lane's token
     uint32_t nrm;        // (|k_in|, |k_out|) fp16 pair
     uint32_t mt;         // (min, step) fp16 pair
-    uint32_t xv[8];      // value role: code words of this lane's channel pair in the slab's two tiles
+    uint32_t xv[8];      // value role: code words of this lane's two channel streams in the slab's two tiles
 };
 
 template <int WB, int VM>
@@ -177,7 +114,7 @@ __device__ __forceinline__ void load_slab(Slab<WB, VM>& sl, __amdgpu_buffer_rsrc
     sl.nrm = __builtin_amdgcn_raw_buffer_load_b32(rn, t * 4, 0, 0);
     if (VM == 0) {
         sl.mt = __builtin_amdgcn_raw_buffer_load_b32(rm, t * 4, 0, 0);
-        // tile = [128 channels][2 words] (1 KiB); this lane's channels 2 lane, 2 lane + 1 are 16 bytes
+        // tile = [128 stream slots][2 words] (1 KiB); this lane's stream slots 2 lane, 2 lane + 1
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const auto x = __builtin_amdgcn_raw_buffer_load_b128(rc, (s0 / kCodeTile + q) * 1024 + lane * 16, 0, 0);
@@ -227,14 +164,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int t_begin = (int)((int64_t)split * a.chunk);
     const int t_end = (int)min(a.N, (int64_t)t_begin + a.chunk);
 
-    // ---- byte tables of the projected query: entry [p][beta] = sum_i (+-) Sq[8p + i]
+    // ---- byte tables of the projected query: entry [p][beta] = sum_i (+-) Sq[8p' + i] for stored
+    //      byte p of a row (slot p/4, natural word w = bits_word(p/4), p' = 4 w + p % 4)
     for (int i = tid; i < 8 * P; i += kThreads) sq_s[i] = a.sq[(size_t)bhq * (8 * P) + i];
     __syncthreads();
     // one task = (position p, high nibble): 16 entries from the high-nibble sum and two
     // 4-entry tables of the low bit pairs
     for (int idx = tid; idx < P * 16; idx += kThreads) {
         const int p = idx >> 4, bh = idx & 15;
-        const float* sv = sq_s + 8 * p;
+        const float* sv = sq_s + 32 * bits_word(p >> 2, WIN, WOUT) + 8 * (p & 3);
         float hi = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) hi += ((bh >> i) & 1) ? sv[4 + i] : -sv[4 + i];
@@ -293,7 +231,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             part += *reinterpret_cast<const float*>(tb + 1024 + byte_x4<1>(x));
             part += *reinterpret_cast<const float*>(tb + 2048 + byte_x4<2>(x));
             part += *reinterpret_cast<const float*>(tb + 3072 + byte_x4<3>(x));
-            if (w < WIN) s_in += part; else s_out += part;
+            if (w % (WB / 4) < WIN / 4) s_in += part; else s_out += part;   // stored slot w
         }
         const float n_in = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur.nrm & 0xFFFFu));
         const float n_out = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur.nrm >> 16));
@@ -388,7 +326,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (VM == 0) {   // [8 waves][128 channels]
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch)
-            rbuf[wave * kD + 2 * lane + ch] = ((acc[4 * ch] + acc[4 * ch + 1]) + (acc[4 * ch + 2] + acc[4 * ch + 3])) * sc;
+            rbuf[wave * kD + code_channel(2 * lane + ch)] = ((acc[4 * ch] + acc[4 * ch + 1]) + (acc[4 * ch + 2] + acc[4 * ch + 3])) * sc;
         nrows = kWaves;
     } else {         // [64 = wave x pair group][128 channels]
 #pragma unroll
@@ -417,11 +355,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 }
 
 // ------------------------------------------------------------------------------------ combine
-// One workgroup per (sequence, query head): log-sum-exp merge of the chunk partials.  A separate
-// launch: merging inside the decode kernel would need a device-scope release/acquire per workgroup,
-// which on MI355X writes back and invalidates the XCD's whole L2.
-__global__ __launch_bounds__(kD) void combine_kernel(DecodeArgs a) {
-    merge_partials(a, blockIdx.x, threadIdx.x);
+// One workgroup (256 threads) per (sequence, query head): log-sum-exp merge of the chunk partials
+// (max, sum, unnormalized output).  The split maxima and their scale factors go through LDS first,
+// so the output pass issues independent loads (two threads per channel, alternate splits).  A
+// separate launch: merging inside the decode kernel would need a device-scope release/acquire per
+// workgroup, which on MI355X writes back and invalidates the XCD's whole L2.
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
+    __shared__ float sc[kMaxSplits];
+    __shared__ float red[2][4];
+    __shared__ float ohalf[kD];
+    const int tid = threadIdx.x;
+    const int bhq = blockIdx.x;
+    const int ns = a.nsplit;
+    const float* src = a.part + (size_t)bhq * ns * (kD + 2);
+    float mx = -INFINITY;
+    for (int i = tid; i < ns; i += 256) mx = fmaxf(mx, src[(size_t)i * (kD + 2)]);
+    mx = wave64_max(mx);
+    if ((tid & 63) == 0) red[0][tid >> 6] = mx;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    float l = 0.f;
+    for (int i = tid; i < ns; i += 256) {
+        const float mi = src[(size_t)i * (kD + 2)];
+        const float f = (mi == -INFINITY) ? 0.f : exp2f(mi - M);   // M is finite when any mi is
+        sc[i] = f;
+        l = fmaf(f, src[(size_t)i * (kD + 2) + 1], l);
+    }
+    l = wave64_sum(l);
+    if ((tid & 63) == 0) red[1][tid >> 6] = l;
+    __syncthreads();
+    const float L = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+    const int c = tid & (kD - 1);
+    const int half = tid >> 7;
+    float o = 0.f;
+#pragma unroll 4
+    for (int i = half; i < ns; i += 2) o = fmaf(sc[i], src[(size_t)i * (kD + 2) + 2 + c], o);
+    if (half) ohalf[c] = o;
+    __syncthreads();
+    if (!half) a.out[(size_t)bhq * kD + c] = L > 0.f ? (o + ohalf[c]) / L : 0.f;
 }
 
 }  // namespace
@@ -444,12 +415,27 @@ hipError_t launch_decode_v(const DecodeArgs& a, int vmode, hipStream_t s) {
     return vmode == 0 ? launch_decode_t<WIN, WOUT, 0>(a, s) : launch_decode_t<WIN, WOUT, 1>(a, s);
 }
 
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
+    timer_begin(TK_COMBINE, s);
+    hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.Hq), dim3(256), 0, s, a);
+    timer_end(TK_COMBINE, s);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+bool decode_uses_mfma(int m, int m_out, int vmode, int nbits) {
+    const int win = m >> 5, wout = m_out >> 5;
+    return vmode == 0 && nbits == 2 && (win == 4 || win == 8 || win == 16) && (wout == 0 || wout == win) &&
+           win + wout <= 16;
+}
 
 int decode_pick_nsplit(int B, int Hkv, int g, int64_t N, int m, int m_out) {
     (void)m;
     (void)m_out;
-    const int64_t units = (int64_t)B * Hkv * g;
+    // one workgroup per (sequence, KV head, group of 4 query heads, chunk) on the matrix-core path,
+    // per (sequence, query head, chunk) on the table path; both aim at ~1024 workgroups
+    const int64_t units = (int64_t)B * Hkv * ((g + 3) / 4);
     const int64_t target = 1024;                       // ~4 workgroups per CU on 256 CUs
     int64_t ns = (target + units - 1) / units;
     const int64_t max_ns = (N + kDecodeTile - 1) / kDecodeTile;
@@ -464,13 +450,18 @@ int64_t decode_chunk(int64_t N, int nsplit) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int qdt, int vmode, hipStream_t s) {
+    const int win = a.m >> 5, wout = a.m_out >> 5;
+    if (decode_uses_mfma(a.m, a.m_out, vmode, 2)) {
+        const hipError_t e = launch_decode_mfma(a, qdt, s);
+        if (e != hipSuccess) return e;
+        return launch_combine(a, s);
+    }
     timer_begin(TK_QPROJ, s);
     if (qdt == 0) hipLaunchKernelGGL(qproj_kernel<uint16_t>, dim3(a.B * a.Hq), dim3(256), 0, s, a);
     else hipLaunchKernelGGL(qproj_kernel<float>, dim3(a.B * a.Hq), dim3(256), 0, s, a);
     timer_end(TK_QPROJ, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int win = a.m >> 5, wout = a.m_out >> 5;
     if (win == 4 && wout == 0) e = launch_decode_v<4, 0>(a, vmode, s);
     else if (win == 4 && wout == 4) e = launch_decode_v<4, 4>(a, vmode, s);
     else if (win == 8 && wout == 0) e = launch_decode_v<8, 0>(a, vmode, s);
@@ -479,10 +470,7 @@ hipError_t launch_decode(const DecodeArgs& a, int qdt, int vmode, hipStream_t s)
     else if (win == 16 && wout == 16) e = launch_decode_v<16, 16>(a, vmode, s);
     else return hipErrorInvalidValue;
     if (e != hipSuccess) return e;
-    timer_begin(TK_COMBINE, s);
-    hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.Hq), dim3(kD), 0, s, a);
-    timer_end(TK_COMBINE, s);
-    return hipGetLastError();
+    return launch_combine(a, s);
 }
 
 bool decode_shape_supported(int m, int m_out) {

@@ -1,0 +1,480 @@
+// Decode attention on the matrix cores: estimator scores and the value aggregation of up to four
+// query heads per instruction.
+//
+// Method: "QJL: 1-Bit Quantized JL Transform for KV Cache Quantization with Zero Overhead",
+// "Approach" (asymmetric estimator sqrt(pi/2)/m * |k| * <S q, sign(S k)> with the query projected
+// unquantized) and softmax attention over the estimated scores with the dequantized values ("Your
+// Brain Already Runs on 1-Bit Keys", "Keys Select. Values Deliver.").
+//
+// Scores on v_mfma_scale_f32_16x16x128_f8f6f4 (A fp8 e4m3, B fp4 e2m1): 16 tokens x 4 query heads
+// per instruction, 128 sign positions of one kind (inlier or outlier) per instruction.
+//   B (sign bits): with b = 1 for a non-negative projection, a 32-bit sign word x gives four fp4
+//     operand words x & 0x11111111, x & 0x22222222, x & 0x44444444, (x >> 1) & 0x44444444: nibble n
+//     of plane word i holds bit 4n + i with the value 0.5, 1, 2, 2 (e2m1 0001, 0010, 0100, 0100) or 0.
+//   A (query): x_k = 2 z_scale sqrt(pi/2)/m (S q)_k divided by its plane's bit value and scaled by a
+//     per-head power of two, split into three e4m3 pieces (each rounded to nearest, 4 significant
+//     bits, so the residual is below 2^-12 of the value); rows = (query head, piece), the fourth row
+//     of a head is zero, and the instruction's E8M0 row scales undo the powers of two.
+//   sign = 2b - 1, so <S q, sign> = 2 <S q, b> - sum (S q): the accumulator starts at -sum_k x_k / 2
+//     and z = |k_in| D_in + |k_out| D_out is the token's base-2 softmax logit.
+// Values on the same instruction: rows = (query head, piece) of the weight p * step, columns = 16
+// channels, K = 128 tokens; B = the 2-bit codes of a code tile as x & 0x33333333 and
+// (x >> 2) & 0x33333333 (e2m1 nibble 00cc = code / 2).  The weights of a 128-token block are scaled
+// by 2^(8 - E), 2^E > the block's largest step, split into three e4m3 pieces, and transposed to the
+// A-operand order through LDS.  Each wave is an independent online-softmax stream over 128-token
+// blocks; the four waves of a workgroup merge at the end of the chunk.
+#include <math.h>
+
+#include "qjl_decode_common.h"
+
+namespace qjl {
+namespace {
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMThreads = 256;               // 4 waves
+constexpr int kMWaves = kMThreads / 64;
+constexpr int kMBlock = 128;                 // tokens per wave step
+constexpr int kWPitch = 144;                 // bytes per row of a wave's weight tile (16-byte aligned;
+                                             // rows of different heads land on different LDS banks)
+
+// 4 fp8 e4m3 bytes: a, b in the low half-word and c, d in the high one, rounded to nearest even
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+    const uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)r, true);
+}
+// r[i] = (r[i] - value of byte i of k) * 16: the residual after an e4m3 piece, rescaled for the next
+__device__ __forceinline__ void next_piece(float (&r)[4], uint32_t k) {
+    r[0] = (r[0] - __builtin_amdgcn_cvt_f32_fp8((int)k, 0)) * 16.f;
+    r[1] = (r[1] - __builtin_amdgcn_cvt_f32_fp8((int)k, 1)) * 16.f;
+    r[2] = (r[2] - __builtin_amdgcn_cvt_f32_fp8((int)k, 2)) * 16.f;
+    r[3] = (r[3] - __builtin_amdgcn_cvt_f32_fp8((int)k, 3)) * 16.f;
+}
+
+// The four fp4 operand words of a sign word (plane i = bit 4n + i of x in nibble n).
+__device__ __forceinline__ v8i_t sign_planes(uint32_t x) {
+    return v8i_t{(int)(x & 0x11111111u), (int)(x & 0x22222222u), (int)(x & 0x44444444u),
+                 (int)((x >> 1) & 0x44444444u), 0, 0, 0, 0};
+}
+
+// ---------------------------------------------------------------------------- query operand
+// One workgroup per (sequence, query head): S q as in the byte-table path, then the A-operand bytes
+// in the order the decode kernel loads them, [K block kb][piece][lane group ga][32 bytes]: byte ea of
+// lane group ga is K index k = 16 ga + ea % 16 + 64 (ea / 16) of the instruction, and K index k pairs
+// with bit 4n + i (n = (k % 32) % 8, i = (k % 32) / 8) of the sign word that B lane group k / 32
+// supplies.  Also the per-head constants [-sum x_in / 2, -sum x_out / 2, e_in, e_out].
+template <typename QT>
+__global__ __launch_bounds__(256) void qproj_mfma_kernel(DecodeArgs a, int win4, int wout4) {
+    __shared__ float qin[kD];
+    __shared__ float qo[kMaxOutliers];
+    __shared__ int so[kMaxOutliers];
+    __shared__ float xs[kMaxBits];
+    __shared__ float red[4][4];
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x;
+    const int hq = bh % a.Hq;
+    const int h = hq / a.g;
+    const QT* Q = static_cast<const QT*>(a.Q);
+    if (tid < a.n_out) so[tid] = a.oidx[h * a.n_out + tid] & (kD - 1);   // never index outside a row
+    if (tid < kD) qin[tid] = load_elem<QT>(Q, (size_t)bh * kD + tid);
+    __syncthreads();
+    if (tid < a.n_out) qo[tid] = qin[so[tid]];
+    __syncthreads();
+    if (tid < a.n_out) qin[so[tid]] = 0.f;
+    __syncthreads();
+    const QT* Sin = static_cast<const QT*>(a.S_in);
+    const QT* Sout = static_cast<const QT*>(a.S_out);
+    // |x| divided by the bit value of its plane (0.5, 1, 2, 2 for position % 4 = 0, 1, 2, 3)
+    auto plane_abs = [](float x, int pos) {
+        const int i = pos & 3;
+        return fabsf(x) * (i == 0 ? 2.f : (i == 1 ? 1.f : 0.5f));
+    };
+    const float c_in = 2.f * a.z_scale * kSqrtHalfPi / (float)a.m;
+    float sum_in = 0.f, sum_out = 0.f, mx_in = 0.f, mx_out = 0.f;
+    for (int j = tid; j < a.m; j += 256) {
+        const float x = row_dot(Sin + (size_t)j * kD, qin) * c_in;
+        xs[j] = x;
+        sum_in += x;
+        mx_in = fmaxf(mx_in, plane_abs(x, j));
+    }
+    if (a.m_out) {
+        const float c_out = 2.f * a.z_scale * kSqrtHalfPi / (float)a.m_out;
+        for (int j = tid; j < a.m_out; j += 256) {
+            float acc = 0.f;
+            for (int i = 0; i < a.n_out; ++i) acc = fmaf(load_elem<QT>(Sout, (size_t)j * kD + so[i]), qo[i], acc);
+            const float x = acc * c_out;
+            xs[a.m + j] = x;
+            sum_out += x;
+            mx_out = fmaxf(mx_out, plane_abs(x, a.m + j));
+        }
+    }
+    sum_in = wave64_sum(sum_in);
+    sum_out = wave64_sum(sum_out);
+    mx_in = wave64_max(mx_in);
+    mx_out = wave64_max(mx_out);
+    if ((tid & 63) == 0) {
+        red[0][tid >> 6] = sum_in;
+        red[1][tid >> 6] = sum_out;
+        red[2][tid >> 6] = mx_in;
+        red[3][tid >> 6] = mx_out;
+    }
+    __syncthreads();
+    const float tot_in = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+    const float tot_out = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+    const float max_in = fmaxf(fmaxf(red[2][0], red[2][1]), fmaxf(red[2][2], red[2][3]));
+    const float max_out = fmaxf(fmaxf(red[3][0], red[3][1]), fmaxf(red[3][2], red[3][3]));
+    // the power of two that takes the largest operand value into [128, 256), kept within the E8M0
+    // range of the row scales 127 - e - 4 piece
+    auto pick_exp = [](float mx) {
+        if (!(mx > 0.f)) return 0;
+        const int e = 8 - __builtin_amdgcn_frexp_expf(mx);
+        return e > 114 ? 114 : (e < -120 ? -120 : e);
+    };
+    const int e_in = pick_exp(max_in), e_out = pick_exp(max_out);
+    if (tid == 0) {
+        float* c = a.qconst + (size_t)bh * 4;
+        c[0] = -0.5f * tot_in;
+        c[1] = -0.5f * tot_out;
+        c[2] = __int_as_float(e_in);
+        c[3] = __int_as_float(e_out);
+    }
+    // operand bytes, one 32-bit word (4 bytes of one (kb, piece, ga)) per thread and step
+    const int W = 4 * (win4 + wout4);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(a.sq) + (size_t)bh * (32 * W);
+    for (int idx = tid; idx < 32 * W; idx += 256) {
+        const int kb = idx >> 7;                 // 128 words per K block
+        const int piece = (idx >> 5) & 3;
+        const int ga = (idx >> 3) & 3;
+        const int e0 = (idx & 7) * 4;            // first byte of this word
+        const bool out = kb >= win4;
+        const int e = out ? e_out : e_in;
+        float y[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int ea = e0 + q;
+            const int k = 16 * ga + (ea & 15) + 64 * (ea >> 4);
+            const int gb = k >> 5, eb = k & 31;
+            const int plane = eb >> 3, n = eb & 7;
+            const int word = out ? 4 * win4 + gb * wout4 + (kb - win4) : gb * win4 + kb;
+            // divided by the plane's bit value and scaled by the head's power of two (exact)
+            float v = ldexpf(xs[32 * word + 4 * n + plane], e + (plane == 0 ? 1 : (plane == 1 ? 0 : -1)));
+            for (int r = 0; r < piece; ++r) {   // v = p0 + p1 / 16 + p2 / 256 + residual
+                const float pr = __builtin_amdgcn_cvt_f32_fp8(__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.f, 0, false), 0);
+                v = (v - pr) * 16.f;
+            }
+            y[q] = piece == 3 ? 0.f : v;
+        }
+        dst[idx] = fp8x4(y[0], y[1], y[2], y[3]);
+    }
+}
+
+// ---------------------------------------------------------------------------- decode
+// Token of sub-step s (0..7) of a 128-token block in B column t, chosen so that the four sub-steps
+// 4q..4q+3 of one column land on four consecutive bytes of the value operand (one 32-bit LDS store
+// per piece): tau = 32 (2q + t3) + 16 t2 + 2 (4 t1 + i) + t0 for s = 4q + i, t = (t3 t2 t1 t0) in bits.
+__device__ __forceinline__ int mfma_token(int s, int t) {
+    return 32 * (2 * (s >> 2) + ((t >> 3) & 1)) + 16 * ((t >> 2) & 1) + 2 * (4 * ((t >> 1) & 1) + (s & 3)) + (t & 1);
+}
+
+// Token data of one 128-token block for one lane: the stored quarter-row (lane group hh) of the sign
+// words of its token for each sub-step, the (norm, meta) pairs of tokens 2 lane and 2 lane + 1 (staged
+// through LDS before use), and the code words of channels 16 cg + t in code tile s0/32 + hh.
+template <int WIN4, int WOUT4>
+struct MBlock {
+    uint32_t w[8][WIN4 + WOUT4];
+    uint32_t nm[4];
+    uint32_t cx[8][2];
+};
+
+template <int WIN4, int WOUT4>
+__device__ __forceinline__ void load_mblock(MBlock<WIN4, WOUT4>& bl, __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rn,
+                                            __amdgpu_buffer_rsrc_t rm, __amdgpu_buffer_rsrc_t rc, int s0, int t, int hh,
+                                            int lane) {
+    constexpr int Q = WIN4 + WOUT4;              // words per quarter-row
+    constexpr int WB = 4 * Q;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const int off = ((s0 + mfma_token(s, t)) * WB + hh * Q) * 4;
+        if constexpr (Q == 1) {
+            bl.w[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rb, off, 0, 0);
+        } else if constexpr (Q == 2) {
+            const auto x = __builtin_amdgcn_raw_buffer_load_b64(rb, off, 0, 0);
+            bl.w[s][0] = x[0]; bl.w[s][1 % Q] = x[1];
+        } else {
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+            bl.w[s][0] = x[0]; bl.w[s][1 % Q] = x[1]; bl.w[s][2 % Q] = x[2]; bl.w[s][3 % Q] = x[3];
+        }
+    }
+    const auto n2 = __builtin_amdgcn_raw_buffer_load_b64(rn, (s0 + 2 * lane) * 4, 0, 0);
+    const auto m2 = __builtin_amdgcn_raw_buffer_load_b64(rm, (s0 + 2 * lane) * 4, 0, 0);
+    bl.nm[0] = n2[0]; bl.nm[1] = m2[0]; bl.nm[2] = n2[1]; bl.nm[3] = m2[1];
+    // code tile s0/32 + hh = [128 stream slots][2 words]: slots 8 t .. 8 t + 7 = channels 16 cg + t
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rc, (s0 / kCodeTile + hh) * 1024 + t * 64 + q * 16, 0, 0);
+        bl.cx[2 * q][0] = x[0]; bl.cx[2 * q][1] = x[1];
+        bl.cx[2 * q + 1][0] = x[2]; bl.cx[2 * q + 1][1] = x[3];
+    }
+}
+
+template <int WIN4, int WOUT4>
+__global__ __launch_bounds__(kMThreads, 2) void decode_mfma_kernel(DecodeArgs a, int groups, int hgroups) {
+    constexpr int W4 = WIN4 + WOUT4;             // instructions (K blocks of 128 sign positions) per token
+    constexpr int WB = 4 * W4;                   // sign words per token
+    __shared__ __attribute__((aligned(16))) uint8_t wtile[kMWaves][16 * kWPitch];   // weight pieces
+    __shared__ __attribute__((aligned(16))) uint32_t nmt[kMWaves][2 * kMBlock];     // (norm, meta) per token
+    __shared__ float red_m[kMWaves][4], red_l[kMWaves][4], red_mn[kMWaves][4];
+    __shared__ __attribute__((aligned(16))) float red_o[kMWaves][4][kD];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int t = lane & 15;                     // B column: token slot (scores) / channel (values)
+    const int hh = lane >> 4;                    // lane group: D rows 4 hh .. 4 hh + 3 = query head hh
+
+    // XCD-aware placement: the head groups of one (KV head, chunk) run on one XCD (shared L2)
+    const int lin = blockIdx.x;
+    const int xcd = lin & 7;
+    const int slot = lin >> 3;
+    const int hg = slot % hgroups;
+    const int64_t us = (int64_t)(slot / hgroups) * 8 + xcd;
+    if (us >= (int64_t)groups) return;
+    const int split = (int)(us % a.nsplit);
+    const int unit = (int)(us / a.nsplit);       // b * Hkv + h
+    const int b = unit / a.Hkv;
+    const int h = unit - b * a.Hkv;
+    const int t_begin = (int)((int64_t)split * a.chunk);
+    const int t_end = (int)min(a.N, (int64_t)t_begin + a.chunk);
+
+    // ---- score A operands and scales: this lane's A row is (head rh, piece pc), K slice hh
+    const int rh = t >> 2, pc = lane & 3;
+    const int qa_head = 4 * hg + rh;
+    v8i_t sA[W4];
+    int sc_in = 127, sc_out = 127;
+    if (qa_head < a.g) {
+        const int bhq = b * a.Hq + h * a.g + qa_head;
+        const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.sq) + (size_t)bhq * (128 * WB));
+#pragma unroll
+        for (int kb = 0; kb < W4; ++kb) {
+            const uint4 lo = src[kb * 32 + (pc * 4 + hh) * 2], hi = src[kb * 32 + (pc * 4 + hh) * 2 + 1];
+            sA[kb] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+        const float* c = a.qconst + (size_t)bhq * 4;
+        sc_in = 127 - __float_as_int(c[2]) - 4 * pc;
+        sc_out = 127 - __float_as_int(c[3]) - 4 * pc;
+    } else {
+#pragma unroll
+        for (int kb = 0; kb < W4; ++kb) sA[kb] = v8i_t{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    // ---- D-side constants: lane group hh is query head 4 hg + hh of the KV head
+    const int dhead = 4 * hg + hh;
+    const bool head_ok = dhead < a.g;
+    const int bhq_d = b * a.Hq + h * a.g + (head_ok ? dhead : 0);
+    float cin = 0.f, cout = 0.f;
+    if (head_ok) {
+        cin = a.qconst[(size_t)bhq_d * 4];
+        cout = a.qconst[(size_t)bhq_d * 4 + 1];
+    }
+
+    // zero this wave's weight tile once (the rows of piece 3 are never written again)
+    uint8_t* wt = wtile[wave];
+    for (int i = lane; i < 16 * kWPitch / 16; i += 64) reinterpret_cast<uint4*>(wt)[i] = make_uint4(0, 0, 0, 0);
+    __builtin_amdgcn_wave_barrier();
+
+    // this lane's byte offset in the weight tile for sub-steps 4q..4q+3 (row and 16 q added later)
+    const int woff = 32 * (2 * ((t >> 3) & 1) + ((t >> 2) & 1)) + 8 * (t & 1) + 4 * ((t >> 1) & 1);
+
+    const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(a.bits + (size_t)unit * a.Ncap * WB, (uint32_t)t_end * WB * 4u);
+    const __amdgpu_buffer_rsrc_t rn = buffer_rsrc(reinterpret_cast<const uint32_t*>(a.norms) + (size_t)unit * a.Ncap,
+                                                  (uint32_t)t_end * 4u);
+    const __amdgpu_buffer_rsrc_t rm = buffer_rsrc(reinterpret_cast<const uint32_t*>(a.meta) + (size_t)unit * a.Ncap,
+                                                  (uint32_t)t_end * 4u);
+    const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(a.codes + (size_t)unit * code_tiles(a.Ncap) * (kD * 2),
+                                                  (uint32_t)code_tiles(t_end) * 1024u);
+    float* sdbg = (a.scores_dbg && head_ok) ? a.scores_dbg + (size_t)bhq_d * a.N : nullptr;
+    const float inv_z = 1.0f / a.z_scale;
+
+    float m_run = -INFINITY, l_acc = 0.f, mn_acc = 0.f;
+    v4f_t dv[8];
+#pragma unroll
+    for (int cg = 0; cg < 8; ++cg) dv[cg] = v4f_t{0.f, 0.f, 0.f, 0.f};
+
+    // ---- the block loop, software-pipelined: block i + 1 is in flight while block i is computed
+    //      (loads past the chunk end fall outside the buffer ranges and return zeros)
+    MBlock<WIN4, WOUT4> cur, nxt;
+    const int s_first = t_begin + kMBlock * wave;
+    load_mblock(cur, rb, rn, rm, rc, s_first, t, hh, lane);
+    uint32_t* nmw = nmt[wave];
+    for (int s0 = s_first; s0 < t_end; s0 += kMBlock * kMWaves) {
+        load_mblock(nxt, rb, rn, rm, rc, s0 + kMBlock * kMWaves, t, hh, lane);
+        // (norm, meta) of the block's tokens to LDS (the previous block's reads are done: LDS
+        // operations of a wave complete in order)
+        *reinterpret_cast<uint4*>(nmw + 4 * lane) = make_uint4(cur.nm[0], cur.nm[1], cur.nm[2], cur.nm[3]);
+        __builtin_amdgcn_wave_barrier();
+        uint32_t nrm[8], mt[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const uint2 v = *reinterpret_cast<const uint2*>(nmw + 2 * mfma_token(s, t));
+            nrm[s] = v.x;
+            mt[s] = v.y;
+        }
+
+        // ---- scores (base-2 logits) of the 8 sub-steps
+        float z[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            v4f_t din = v4f_t{cin, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < WIN4; ++kb)
+                din = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sA[kb], sign_planes(cur.w[s][kb]), din, 0, 4, 0,
+                                                                       sc_in, 0, 127);
+            const float n_in = (float)__builtin_bit_cast(_Float16, (uint16_t)(nrm[s] & 0xFFFFu));
+            float zz = n_in * ((din[0] + din[1]) + din[2]);
+            if constexpr (WOUT4 > 0) {
+                v4f_t dout = v4f_t{cout, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < WOUT4; ++kb)
+                    dout = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sA[WIN4 + kb], sign_planes(cur.w[s][WIN4 + kb]),
+                                                                            dout, 0, 4, 0, sc_out, 0, 127);
+                const float n_out = (float)__builtin_bit_cast(_Float16, (uint16_t)(nrm[s] >> 16));
+                zz = fmaf(n_out, (dout[0] + dout[1]) + dout[2], zz);
+            }
+            const int P = s0 + mfma_token(s, t);
+            const bool valid = P < t_end;
+            if (sdbg && valid) sdbg[P] = zz * inv_z;
+            z[s] = valid ? zz : -INFINITY;
+        }
+
+        // ---- online softmax over the block (per head = per row of 16 lanes)
+        float mx = z[0];
+#pragma unroll
+        for (int s = 1; s < 8; ++s) mx = fmaxf(mx, z[s]);
+        mx = row16_max(mx);
+        const float m_new = fmaxf(m_run, mx);            // finite: token s0 of the block is valid
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        float mxs = 0.f, stp[8], mnv[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            mnv[s] = (float)__builtin_bit_cast(_Float16, (uint16_t)(mt[s] & 0xFFFFu));
+            stp[s] = (float)__builtin_bit_cast(_Float16, (uint16_t)(mt[s] >> 16));
+            mxs = fmaxf(mxs, stp[s]);
+        }
+        mxs = row16_max(mxs);
+        const int E = mxs > 0.f ? __builtin_amdgcn_frexp_expf(mxs) : 0;   // every step of the block < 2^E
+        l_acc *= alpha;
+        mn_acc *= alpha;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            float w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = 4 * q + i;
+                const float p = __builtin_amdgcn_exp2f(z[s] - m_new);
+                l_acc += p;
+                mn_acc = fmaf(p, mnv[s], mn_acc);
+                w[i] = p * ldexpf(stp[s], 8 - E);             // in [0, 256)
+            }
+            // three e4m3 pieces: w = p0 + p1 / 16 + p2 / 256 + residual
+            const uint32_t k0 = fp8x4(w[0], w[1], w[2], w[3]);
+            next_piece(w, k0);
+            const uint32_t k1 = fp8x4(w[0], w[1], w[2], w[3]);
+            next_piece(w, k1);
+            const uint32_t k2 = fp8x4(w[0], w[1], w[2], w[3]);
+            uint8_t* row = wt + (4 * hh) * kWPitch + woff + 16 * q;
+            *reinterpret_cast<uint32_t*>(row) = k0;
+            *reinterpret_cast<uint32_t*>(row + kWPitch) = k1;
+            *reinterpret_cast<uint32_t*>(row + 2 * kWPitch) = k2;
+        }
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+            for (int cg = 0; cg < 8; ++cg) dv[cg] *= alpha;
+        }
+        __builtin_amdgcn_wave_barrier();   // the weight tile written above is read across lanes below
+
+        // ---- values: A = weight pieces (row t = (head, piece), K slice hh), B = code tile hh
+        const uint4 alo = *reinterpret_cast<const uint4*>(wt + t * kWPitch + 32 * hh);
+        const uint4 ahi = *reinterpret_cast<const uint4*>(wt + t * kWPitch + 32 * hh + 16);
+        const v8i_t aw = v8i_t{(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
+        const int sc_w = 120 + E - 4 * pc;   // 2^(E - 8 - 4 piece), times 2 for the nibble = code / 2
+#pragma unroll
+        for (int cg = 0; cg < 8; ++cg) {
+            const uint32_t x0 = cur.cx[cg][0], x1 = cur.cx[cg][1];
+            const v8i_t bv = v8i_t{(int)(x0 & 0x33333333u), (int)((x0 >> 2) & 0x33333333u), (int)(x1 & 0x33333333u),
+                                   (int)((x1 >> 2) & 0x33333333u), 0, 0, 0, 0};
+            dv[cg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, bv, dv[cg], 0, 4, 0, sc_w, 0, 127);
+        }
+        __builtin_amdgcn_wave_barrier();   // the next block rewrites the weight tile
+        cur = nxt;
+    }
+
+    // ---- merge the four wave streams of each head
+    const float l_sum = row16_sum(l_acc), mn_sum = row16_sum(mn_acc);
+    if (t == 0) {
+        red_m[wave][hh] = m_run;
+        red_l[wave][hh] = l_sum;
+        red_mn[wave][hh] = mn_sum;
+    }
+#pragma unroll
+    for (int cg = 0; cg < 8; ++cg) red_o[wave][hh][16 * cg + t] = (dv[cg][0] + dv[cg][1]) + dv[cg][2];
+    __syncthreads();
+    const int oh = tid >> 6;                 // head of the group handled by this thread
+    const int c0 = 2 * (tid & 63);           // channels c0, c0 + 1
+    if (4 * hg + oh >= a.g) return;
+    float M = red_m[0][oh];
+#pragma unroll
+    for (int w = 1; w < kMWaves; ++w) M = fmaxf(M, red_m[w][oh]);
+    float L = 0.f, o0 = 0.f, o1 = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < kMWaves; ++w) {
+            const float mw = red_m[w][oh];
+            if (mw == -INFINITY) continue;
+            const float sc = exp2f(mw - M);
+            L = fmaf(sc, red_l[w][oh], L);
+            o0 = fmaf(sc, red_o[w][oh][c0] + red_mn[w][oh], o0);
+            o1 = fmaf(sc, red_o[w][oh][c0 + 1] + red_mn[w][oh], o1);
+        }
+    }
+    const int bhq = b * a.Hq + h * a.g + 4 * hg + oh;
+    float* dst = a.part + ((size_t)bhq * a.nsplit + split) * (kD + 2);
+    dst[2 + c0] = o0;
+    dst[3 + c0] = o1;
+    if ((tid & 63) == 0) {
+        dst[0] = M;
+        dst[1] = L;
+    }
+}
+
+template <int WIN4, int WOUT4>
+hipError_t launch_decode_mfma_t(const DecodeArgs& a, hipStream_t s) {
+    const int hgroups = (a.g + 3) / 4;
+    const int groups = a.B * a.Hkv * a.nsplit;
+    const int slots = (groups + 7) / 8;
+    const unsigned nblocks = (unsigned)slots * 8u * (unsigned)hgroups;
+    timer_begin(TK_DECODE, s);
+    hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4>), dim3(nblocks), dim3(kMThreads), 0, s, a, groups, hgroups);
+    timer_end(TK_DECODE, s);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int qdt, hipStream_t s) {
+    const int win4 = a.m >> 7, wout4 = a.m_out >> 7;
+    timer_begin(TK_QPROJ, s);
+    if (qdt == 0) hipLaunchKernelGGL(qproj_mfma_kernel<uint16_t>, dim3(a.B * a.Hq), dim3(256), 0, s, a, win4, wout4);
+    else hipLaunchKernelGGL(qproj_mfma_kernel<float>, dim3(a.B * a.Hq), dim3(256), 0, s, a, win4, wout4);
+    timer_end(TK_QPROJ, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (win4 == 1 && wout4 == 0) return launch_decode_mfma_t<1, 0>(a, s);
+    if (win4 == 1 && wout4 == 1) return launch_decode_mfma_t<1, 1>(a, s);
+    if (win4 == 2 && wout4 == 0) return launch_decode_mfma_t<2, 0>(a, s);
+    if (win4 == 2 && wout4 == 2) return launch_decode_mfma_t<2, 2>(a, s);
+    if (win4 == 4 && wout4 == 0) return launch_decode_mfma_t<4, 0>(a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace qjl

@@ -260,8 +260,10 @@ void quantize_keys_bf16_kernel(KeyQuantArgs a) {
         uint32_t* dst = a.bits + (head_row0 + c0) * W;
         const uint32_t* olb = ol[buf];
         const int w = tid & 31;
-        if (w < W)
-            for (int tok = tid >> 5; tok < nvalid; tok += NT / 32) dst[tok * W + w] = olb[tok * orow + w];
+        if (w < W) {
+            const int slot = bits_slot(w, Win, Wout);
+            for (int tok = tid >> 5; tok < nvalid; tok += NT / 32) dst[tok * W + slot] = olb[tok * orow + w];
+        }
         buf ^= 1;
     }
 }
@@ -365,7 +367,7 @@ void quantize_keys_rows_kernel(KeyQuantArgs a, int64_t rows) {
     const int nvalid = (int)min((int64_t)kTok, rows - r0);
     for (int i = tid; i < nvalid * W; i += kThreads) {
         const int tok = i / W, w = i - tok * W;
-        a.bits[s_dst[tok] * W + w] = ol[tok * orow + w];
+        a.bits[s_dst[tok] * W + bits_slot(w, Win, Wout)] = ol[tok * orow + w];
     }
 }
 
@@ -423,8 +425,9 @@ __global__ __launch_bounds__(256) void quantize_keys_f32_kernel(KeyQuantArgs a) 
         const uint64_t bal = __ballot(r < total && p >= 0.f);
         if (lane == 0) {
             uint32_t* dst = a.bits + row * a.W;
-            if (2 * g < a.W) dst[2 * g] = (uint32_t)bal;
-            if (2 * g + 1 < a.W) dst[2 * g + 1] = (uint32_t)(bal >> 32);
+            const int win = a.m >> 5, wout = a.m_out >> 5;
+            if (2 * g < a.W) dst[bits_slot(2 * g, win, wout)] = (uint32_t)bal;
+            if (2 * g + 1 < a.W) dst[bits_slot(2 * g + 1, win, wout)] = (uint32_t)(bal >> 32);
         }
     }
 }

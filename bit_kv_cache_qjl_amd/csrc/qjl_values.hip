@@ -8,7 +8,7 @@
 // threads own one value vector (8 channels each): a 16-lane min/max butterfly, the (min, step) meta,
 // and the codes of 8 channels into LDS.  Phase 2: one thread per channel packs the tile's 32 codes of
 // its channel into nbits words (the channel-major tile the decode kernels read as matrix-core
-// operands).  A tile wholly inside the append is stored; a tile the append covers only in part is
+// operands; channel c is stream slot 8 (c % 16) + c / 16 of the tile).  A tile wholly inside the append is stored; a tile the append covers only in part is
 // merged bit-exactly with two atomics per word (clear the appended fields, then set them), so tokens
 // outside [t0, t0 + T) keep their codes.
 //
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kValThreads) void quantize_values_kernel(ValueQuant
             }
         }
     }
-    uint32_t* dst = a.codes + ((size_t)bh * code_tiles(a.Ncap) + tile) * (kD * NBITS) + c * NBITS;
+    uint32_t* dst = a.codes + ((size_t)bh * code_tiles(a.Ncap) + tile) * (kD * NBITS) + code_slot(c) * NBITS;
     const bool full = p0 >= a.t0 && p0 + kCodeTile <= a.t0 + a.T;
     if (full) {
 #pragma unroll

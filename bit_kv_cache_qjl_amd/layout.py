@@ -1,15 +1,55 @@
 """Host-side views of the cache layout documented in include/qjl.h (numpy only, no device work).
 
-Value codes are stored channel-major in tiles of 32 positions: for each channel, the codes of a
-tile's 32 positions form an LSB-first bit stream of nbits 32-bit words.  These helpers convert
-between that layout and plain integer codes [..., position, channel], e.g. to inspect a cache or to
-build one on the host.
+Sign words: natural word w of a token holds projections 32 w .. 32 w + 31 (inlier words first); a
+row stores them as 4 groups of W/4 words, group j = inlier words j Win/4 .. then outlier words
+Win + j Wout/4 ...  Value codes are stored channel-major in tiles of 32 positions: for each channel,
+the codes of a tile's 32 positions form an LSB-first bit stream of nbits 32-bit words, channel c in
+stream slot 8 (c % 16) + c // 16.  These helpers convert between the stored layout and the natural
+one (sign words in projection order, integer codes [..., position, channel]), e.g. to inspect a
+cache or to build one on the host.
 """
 from __future__ import annotations
 
 import numpy as np
 
 TILE = 32
+
+
+def bits_slots(m: int, m_out: int) -> np.ndarray:
+    """Stored row slot of each natural sign word (index = natural word)."""
+    win, wout = m // 32, m_out // 32
+    if m % 128 or m_out % 128:
+        raise ValueError("m and m_out must be multiples of 128")
+    q = (win + wout) // 4
+    slots = np.empty(win + wout, dtype=np.int64)
+    for w in range(win):
+        slots[w] = (w // (win // 4)) * q + w % (win // 4)
+    for j in range(wout):
+        slots[win + j] = (j // (wout // 4)) * q + win // 4 + j % (wout // 4)
+    return slots
+
+
+def bits_to_stored(words: np.ndarray, m: int, m_out: int) -> np.ndarray:
+    """Sign words in natural order [..., W] -> the stored row order."""
+    w = np.asarray(words)
+    out = np.empty(w.shape, dtype=w.dtype)                   # C order
+    out[..., bits_slots(m, m_out)] = w
+    return out
+
+
+def bits_from_stored(stored: np.ndarray, m: int, m_out: int) -> np.ndarray:
+    """Stored rows [..., W] -> sign words in natural order (word w = projections 32 w .. 32 w + 31)."""
+    return np.ascontiguousarray(np.asarray(stored)[..., bits_slots(m, m_out)])
+
+
+def code_slot_of_channel(d: int = 128) -> np.ndarray:
+    c = np.arange(d)
+    return 8 * (c % 16) + c // 16
+
+
+def code_channel_of_slot(d: int = 128) -> np.ndarray:
+    p = np.arange(d)
+    return 16 * (p % 8) + p // 8
 
 
 def codes_from_tiles(tiles: np.ndarray, nbits: int, n: int) -> np.ndarray:
@@ -20,9 +60,10 @@ def codes_from_tiles(tiles: np.ndarray, nbits: int, n: int) -> np.ndarray:
         raise ValueError(f"tiles of shape {t.shape} do not hold {n} positions of {nbits}-bit codes")
     bits = (t[..., None] >> np.arange(32, dtype=np.uint32)) & np.uint32(1)       # [..., nt, d, nbits, 32]
     fields = bits.reshape(*lead, nt, d, TILE, nbits).astype(np.int64)            # stream bit nbits*j + k
-    codes = (fields << np.arange(nbits, dtype=np.int64)).sum(axis=-1)              # [..., nt, d, 32]
+    codes = (fields << np.arange(nbits, dtype=np.int64)).sum(axis=-1)              # [..., nt, slot, 32]
+    codes = codes[..., code_slot_of_channel(d), :]                                  # [..., nt, channel, 32]
     codes = np.swapaxes(codes, -1, -2).reshape(*lead, nt * TILE, d)
-    return codes[..., :n, :]
+    return np.ascontiguousarray(codes[..., :n, :])
 
 
 def tiles_from_codes(codes: np.ndarray, nbits: int, ncap: int | None = None) -> np.ndarray:
@@ -36,8 +77,9 @@ def tiles_from_codes(codes: np.ndarray, nbits: int, ncap: int | None = None) -> 
     nt = (ncap + TILE - 1) // TILE
     full = np.zeros((*lead, nt * TILE, d), dtype=np.int64)
     full[..., :n, :] = c
-    per = np.swapaxes(full.reshape(*lead, nt, TILE, d), -1, -2)                    # [..., nt, d, 32]
+    per = np.swapaxes(full.reshape(*lead, nt, TILE, d), -1, -2)                    # [..., nt, channel, 32]
+    per = per[..., code_channel_of_slot(d), :]                                      # [..., nt, slot, 32]
     bits = (per[..., None] >> np.arange(nbits, dtype=np.int64)) & 1                 # [..., nt, d, 32, nbits]
     stream = bits.reshape(*lead, nt, d, nbits, 32).astype(np.uint64)                 # stream bit 32*w + i
     words = (stream << np.arange(32, dtype=np.uint64)).sum(axis=-1)
-    return words.astype(np.uint32)
+    return np.ascontiguousarray(words, dtype=np.uint32)     # row-major bytes, as a device copy expects

@@ -23,7 +23,7 @@
  *   - Argument errors are detected on the host before anything is enqueued and returned as a
  *     negative qjl_status; nothing is written then.  A failed launch returns QJL_ERR_HIP.
  *     qjl_last_error() gives a human-readable detail of the last error on the calling thread.
- *   - Supported shapes: head dimension d = 128; m and m_out multiples of 32 with 32 <= m,
+ *   - Supported shapes: head dimension d = 128; m and m_out multiples of 128 with 128 <= m,
  *     0 <= m_out, m + m_out <= 1024; 0 <= n_out <= 16 outlier channels per KV head, n_out > 0 only
  *     with m_out > 0; Hq a multiple of Hkv.  Query head hq reads KV head hq / (Hq / Hkv).
  *   - Every device pointer must be 16-byte aligned, and the model-layout strides must keep every
@@ -31,15 +31,22 @@
  *   - Stateless and thread-safe; calls on different streams may overlap.
  *
  * Cache layout in HBM (per sequence b, KV head h, token position t < Ncap):
- *   bits  uint32 [B][Hkv][Ncap][W], W = (m + m_out) / 32: bit i of word w is 1 iff projection
- *         32 w + i is >= 0 (sign(0) taken as +1); words 0 .. m/32-1 hold the inlier sketch,
- *         words m/32 .. W-1 the outlier sketch.
+ *   bits  uint32 [B][Hkv][Ncap][W], W = (m + m_out) / 32.  Sign word w (w < W) has bit i set iff
+ *         projection 32 w + i is >= 0 (sign(0) taken as +1); words 0 .. Win-1 (Win = m/32) hold the
+ *         inlier sketch, words Win .. W-1 (Wout = m_out/32 of them) the outlier sketch.  A token's
+ *         row stores its W words as 4 groups of W/4: group j (j = 0..3) holds inlier words
+ *         j Win/4 .. (j+1) Win/4 - 1 followed by outlier words Win + j Wout/4 .. Win + (j+1) Wout/4 - 1,
+ *         so row slot j W/4 + r holds inlier word j Win/4 + r for r < Win/4 and outlier word
+ *         Win + j Wout/4 + r - Win/4 otherwise.  (Each quarter of a row is what one lane group of a
+ *         matrix-core operand consumes; one load per token and lane.)
  *   norms fp16  [B][Hkv][Ncap][2]: (|k_in|, |k_out|) as IEEE binary16 round-to-nearest-even.
  *   codes uint32 [B][Hkv][Ncap32/32][d][nbits], Ncap32 = Ncap rounded up to a multiple of 32: the
- *         positions are grouped in tiles of 32 (tile i covers positions 32 i .. 32 i + 31); for each
- *         channel c, in order, a tile holds the codes of its 32 positions as an LSB-first bit stream
- *         of nbits words (position 32 i + j in bits [nbits*j, nbits*j + nbits) of the stream).
- *         Channel-major tiles let the decode kernels feed the codes to the matrix cores directly.
+ *         positions are grouped in tiles of 32 (tile i covers positions 32 i .. 32 i + 31).  For each
+ *         channel c a tile holds the codes of its 32 positions as an LSB-first bit stream of nbits
+ *         words (position 32 i + j in bits [nbits*j, nbits*j + nbits) of the stream); the stream of
+ *         channel c is stream slot 8 (c mod 16) + floor(c / 16) of the tile (slot p holds channel
+ *         16 (p mod 8) + floor(p / 8)).  Channel-major tiles let the decode kernels feed the codes
+ *         to the matrix cores directly, 8 channels per 64-byte load.
  *   meta  fp16  [B][Hkv][Ncap][2]: (min, step) of the token's value vector.
  */
 #ifndef QJL_H

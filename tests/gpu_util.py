@@ -48,8 +48,16 @@ def gpu_quantize_keys(qjl, w, K, S_in, S_out, oidx, Ncap=None, t0=0, Kdev=None):
     return cache
 
 
-def bits_np(t):
-    return t.cpu().numpy().view(np.uint32)
+def bits_np(t, m: int, m_out: int):
+    """Device sign-word rows -> numpy uint32 words in natural order (word w = projections 32w..32w+31)."""
+    from bit_kv_cache_qjl_amd import layout
+    return layout.bits_from_stored(t.cpu().numpy().view(np.uint32), m, m_out)
+
+
+def bits_dev(words: np.ndarray, m: int, m_out: int):
+    """Natural-order sign words (the oracle's) -> a device tensor in the library's row order."""
+    from bit_kv_cache_qjl_amd import layout
+    return torch_mod().from_numpy(np.ascontiguousarray(layout.bits_to_stored(words, m, m_out)).view(np.int32)).cuda()
 
 
 def code_tiles_of_rows(rows: np.ndarray, nbits: int, ncap: int | None = None, d: int = 128) -> np.ndarray:
@@ -105,7 +113,7 @@ def run_decode(qjl, w, Q, S_in, S_out, oidx, cache_np: dict, N: int, *, nsplit=0
     """Upload an oracle-built cache, run the library decode, return (out, scores) as numpy."""
     torch = torch_mod()
     B, Hq, d = Q.shape
-    bits = torch.from_numpy(cache_np["bits"].view(np.int32)).cuda()
+    bits = bits_dev(cache_np["bits"], w.m, w.m_out)
     norms = torch.from_numpy(cache_np["norms"]).cuda()
     out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
     scores = torch.full((B, Hq, max(N, 1)), float("nan"), dtype=torch.float32, device="cuda") if with_scores else None

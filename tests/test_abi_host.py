@@ -114,6 +114,7 @@ def decode_call(ws_bytes=None, **kw):
     (dict(vmode=7), qjl.QJL_ERR_INVALID_ARG),
     (dict(out=MIS), qjl.QJL_ERR_MISALIGNED),
     (dict(scores=MIS), qjl.QJL_ERR_MISALIGNED),
+    (dict(nsplit=5000, ws_bytes=1 << 30), qjl.QJL_ERR_UNSUPPORTED),
     (dict(), qjl.QJL_ERR_WORKSPACE),                    # 4 bytes short
     (dict(ws=0), qjl.QJL_ERR_WORKSPACE),
 ])
@@ -126,9 +127,10 @@ def test_decode_workspace_size_formula():
     for nsplit in (1, 4, 7):
         ws = qjl.decode_workspace_size(B, Hq, Hkv, N, m, m_out, nsplit)
         sq = B * Hq * (m + m_out) * 4
+        qconst = B * Hq * 4 * 4
         part = B * Hq * nsplit * 130 * 4
         r = lambda x: (x + 255) // 256 * 256
-        assert ws == r(sq) + r(part)
+        assert ws == r(sq) + r(qconst) + r(part)
     assert qjl.decode_workspace_size(B, Hq, Hkv, N, m, m_out, 0) >= qjl.decode_workspace_size(B, Hq, Hkv, N, m, m_out, 1)
     assert qjl.decode_workspace_size(B, 9, 2, N, m, m_out) == 0
 

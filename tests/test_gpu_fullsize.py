@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import seeded_inputs as si
-from gpu_util import check_decode, code_rows_of_tiles, compare_bits, compare_norms, log, to_dev
+from gpu_util import bits_dev, bits_np, check_decode, code_rows_of_tiles, compare_bits, compare_norms, log, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -56,7 +56,7 @@ def test_full_size_decode_step(name):
     last_v = V[:, N - 1:].float().cpu().numpy()
     rk = oracle.quantize_keys(last_k, S_in_np, S_out_np, oidx)
     rv = oracle.quantize_values(last_v, w.nbits)
-    compare_bits(cache.bits[:, :, N - 1:].cpu().numpy().view(np.uint32), rk, "appended token", w.m + w.m_out)
+    compare_bits(bits_np(cache.bits[:, :, N - 1:], w.m, w.m_out), rk, "appended token", w.m + w.m_out)
     compare_norms(cache.norms[:, :, N - 1:].cpu().numpy(), rk["norms"], "appended token")
     last_tile = code_rows_of_tiles(cache.codes[:, :, (N - 1) // 32: (N - 1) // 32 + 1], w.nbits, 32)
     np.testing.assert_array_equal(last_tile[:, :, (N - 1) % 32:(N - 1) % 32 + 1], rv["codes"])
@@ -71,13 +71,13 @@ def test_full_size_decode_step(name):
         r = oracle.quantize_key_vectors(kbh, S_in_np, S_out_np, oidx[h])
         codes, meta = oracle.quantize_value_vectors(si.value_slice(w, b, h), w.nbits)
         packed = oracle.pack_codes(codes, w.nbits)
-        compare_bits(cache.bits[b, h].cpu().numpy().view(np.uint32), {"bits": r["bits"], "near_zero": r["near_zero"]},
+        compare_bits(bits_np(cache.bits[b, h], w.m, w.m_out), {"bits": r["bits"], "near_zero": r["near_zero"]},
                      f"unit ({b},{h}) bits", w.m + w.m_out)
         compare_norms(cache.norms[b, h].cpu().numpy(), r["norms"], f"unit ({b},{h})")
         np.testing.assert_array_equal(code_rows_of_tiles(cache.codes[b, h], w.nbits, N), packed)
         np.testing.assert_array_equal(cache.meta[b, h].cpu().numpy().view(np.uint16), meta.view(np.uint16))
         # identical decode inputs on both sides
-        cache.bits[b, h] = torch.from_numpy(r["bits"].view(np.int32)).cuda()
+        cache.bits[b, h] = bits_dev(r["bits"], w.m, w.m_out)
         cache.norms[b, h] = torch.from_numpy(r["norms"]).cuda()
         ref_cache[(b, h)] = (r["bits"], r["norms"], packed, meta)
 
@@ -109,7 +109,7 @@ def test_full_size_prefill_quantize():
     qjl.quantize_keys(K, to_dev(S_in_np, w.dtype), to_dev(S_out_np, w.dtype), torch.from_numpy(oidx).cuda(),
                       cache.bits, cache.norms)
     torch.cuda.synchronize()
-    bits = cache.bits.cpu().numpy().view(np.uint32)
+    bits = bits_np(cache.bits, w.m, w.m_out)
     norms = cache.norms.cpu().numpy()
     rng = np.random.default_rng(3)
     for h in range(w.Hkv):

@@ -30,6 +30,8 @@ SCALED = {
     "prefill_quantize_64k": W["prefill_quantize_64k"].scaled(B=1, Hq=2, Hkv=2, N=1000),
     "llama31_70b_gqa_decode": W["llama31_70b_gqa_decode"].scaled(B=1, Hq=16, Hkv=2, N=777),
 }
+# a 1024-bit sketch (m = m_out = 512): decode takes the byte-table path for such wide sketches
+WIDE = W["llama3_8b_gqa_decode"].scaled(B=2, Hq=6, Hkv=3, N=900, m=512, m_out=512)
 
 
 @pytest.mark.parametrize("name", list(SCALED))
@@ -39,7 +41,7 @@ def test_quantize_keys_parity(name):
     x = inputs(w)
     cache = gpu_quantize_keys(qjl, w, x["K"], x["S_in"], x["S_out"], x["oidx"])
     ref = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
-    compare_bits(bits_np(cache.bits), ref, name, w.m + w.m_out)
+    compare_bits(bits_np(cache.bits, w.m, w.m_out), ref, name, w.m + w.m_out)
     compare_norms(cache.norms.cpu().numpy(), ref["norms"], name)
 
 
@@ -58,7 +60,7 @@ def test_quantize_keys_small_append(name, T, m, m_out):
     x = inputs(w)
     cache = gpu_quantize_keys(qjl, w, x["K"], x["S_in"], x["S_out"], x["oidx"], Ncap=T + 9, t0=9)
     ref = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
-    bits = bits_np(cache.bits)
+    bits = bits_np(cache.bits, w.m, w.m_out)
     compare_bits(bits[:, :, 9:], ref, f"append T={T}", w.m + w.m_out)
     compare_norms(cache.norms.cpu().numpy()[:, :, 9:], ref["norms"], f"append T={T}")
     assert not bits[:, :, :9].any()
@@ -76,7 +78,7 @@ def test_quantize_keys_append_offset_and_strides():
     log(f"[quantize_keys] strided view, t0={t0}, Ncap={Ncap}")
     cache = gpu_quantize_keys(qjl, w, x["K"], x["S_in"], x["S_out"], x["oidx"], Ncap=Ncap, t0=t0, Kdev=Kdev)
     ref = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
-    bits = bits_np(cache.bits)
+    bits = bits_np(cache.bits, w.m, w.m_out)
     compare_bits(bits[:, :, t0:t0 + w.N], ref, "append", w.m + w.m_out)
     compare_norms(cache.norms.cpu().numpy()[:, :, t0:t0 + w.N], ref["norms"], "append")
     assert not bits[:, :, :t0].any() and not bits[:, :, t0 + w.N:].any(), "wrote outside [t0, t0 + T)"
@@ -97,7 +99,7 @@ def test_quantize_keys_special_keys():
     K[:, 48:64] = -K[:, 32:48]
     log("[quantize_keys] special keys")
     cache = gpu_quantize_keys(qjl, w, K, x["S_in"], x["S_out"], x["oidx"])
-    bits = bits_np(cache.bits)
+    bits = bits_np(cache.bits, w.m, w.m_out)
     norms = cache.norms.cpu().numpy()
     assert np.all(bits[:, :, :16] == 0xFFFFFFFF) and np.all(norms[:, :, :16] == 0)
     assert np.all(bits[:, :, 16:32, : w.m // 32] == 0xFFFFFFFF) and np.all(norms[:, :, 16:32, 0] == 0)
@@ -153,10 +155,11 @@ def test_quantize_values_appends_keep_neighbours(nbits):
     assert np.all(tail == 2 ** nbits - 1)
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "llama2_7b_decode", "llama3_8b_gqa_decode", "llama31_70b_gqa_decode"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama2_7b_decode", "llama3_8b_gqa_decode", "llama31_70b_gqa_decode",
+                                  "wide_sketch"])
 @pytest.mark.parametrize("nsplit", [0, 1, 3])
 def test_decode_parity(name, nsplit):
-    w = SCALED[name]
+    w = WIDE if name == "wide_sketch" else SCALED[name]
     log(f"[decode] {name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} nsplit={nsplit}")
     x = inputs(w)
     kq = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
@@ -230,10 +233,10 @@ def test_decode_step_append_then_attend():
     torch.cuda.synchronize()
     kq = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
     vq = oracle.quantize_values(x["V"], w.nbits)
-    compare_bits(bits_np(cache.bits), kq, "pipeline", w.m + w.m_out)
+    compare_bits(bits_np(cache.bits, w.m, w.m_out), kq, "pipeline", w.m + w.m_out)
     np.testing.assert_array_equal(code_rows_of_tiles(cache.codes, w.nbits, N), vq["codes"])
     # decode input must be identical on both sides: use the oracle cache where a near-zero bit differs
-    gbits = bits_np(cache.bits)
+    gbits = bits_np(cache.bits, w.m, w.m_out)
     if np.array_equal(gbits, kq["bits"]) and np.array_equal(cache.norms.cpu().numpy().view(np.uint16),
                                                              kq["norms"].view(np.uint16)):
         cache_np = {"bits": kq["bits"], "norms": kq["norms"], **vq}

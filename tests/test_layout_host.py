@@ -29,8 +29,11 @@ def test_tiles_match_the_documented_layout(nbits):
     assert tiles.shape == (3, d, nbits) and tiles.dtype == np.uint32
     for tile in range(3):
         for ch in (0, 1, 17, 64, 127):
-            assert [int(x) for x in tiles[tile, ch]] == tile_words_by_hand(codes, nbits, tile, ch)
+            slot = 8 * (ch % 16) + ch // 16
+            assert [int(x) for x in tiles[tile, slot]] == tile_words_by_hand(codes, nbits, tile, ch)
     np.testing.assert_array_equal(layout.codes_from_tiles(tiles, nbits, n), codes)
+    # device copies take the bytes as they lie: every helper returns C-contiguous arrays
+    assert tiles.flags.c_contiguous and layout.codes_from_tiles(tiles, nbits, n).flags.c_contiguous
 
 
 def test_two_bit_tile_by_example():
@@ -39,12 +42,14 @@ def test_two_bit_tile_by_example():
     codes[0, 0] = 3          # bits 0, 1 of word 0
     codes[15, 0] = 2         # bit 31 of word 0
     codes[16, 0] = 1         # bit 0 of word 1
-    codes[5, 1] = 1          # channel 1: bit 10 of its word 0
+    codes[5, 1] = 1          # channel 1 (stream slot 8): bit 10 of its word 0
+    codes[31, 16] = 3        # channel 16 (stream slot 1): bits 30, 31 of its word 1
     t = layout.tiles_from_codes(codes, 2)
     assert t.shape == (1, 128, 2)
     assert int(t[0, 0, 0]) == 0x80000003 and int(t[0, 0, 1]) == 0x1
-    assert int(t[0, 1, 0]) == 1 << 10 and int(t[0, 1, 1]) == 0
-    assert not t[0, 2:].any()
+    assert int(t[0, 8, 0]) == 1 << 10 and int(t[0, 8, 1]) == 0
+    assert int(t[0, 1, 0]) == 0 and int(t[0, 1, 1]) == 0xC0000000
+    assert not t[0, 2:8].any() and not t[0, 9:].any()
 
 
 def test_round_trip_with_leading_dims_and_int32_views():
@@ -55,3 +60,25 @@ def test_round_trip_with_leading_dims_and_int32_views():
     np.testing.assert_array_equal(back, codes)
     with pytest.raises(ValueError):
         layout.codes_from_tiles(t, 2, 65)
+
+
+def test_sign_word_row_order():
+    """m = m_out = 256 (8 + 8 words): row = 4 groups of (2 inlier, 2 outlier) words."""
+    slots = layout.bits_slots(256, 256)
+    # natural words 0..7 inlier, 8..15 outlier; group j holds inlier 2j, 2j+1 and outlier 8+2j, 9+2j
+    expect_row = [0, 1, 8, 9, 2, 3, 10, 11, 4, 5, 12, 13, 6, 7, 14, 15]
+    for slot, word in enumerate(expect_row):
+        assert slots[word] == slot
+    assert list(layout.bits_slots(128, 0)) == [0, 1, 2, 3]          # no outlier sketch: natural order
+    assert list(layout.bits_slots(512, 0)) == list(range(16))
+    # m = m_out = 128: row = inlier 0, outlier 0, inlier 1, outlier 1, ...
+    assert list(layout.bits_slots(128, 128)) == [0, 2, 4, 6, 1, 3, 5, 7]
+    rng = np.random.default_rng(3)
+    words = rng.integers(0, 2 ** 32, size=(2, 5, 32), dtype=np.uint64).astype(np.uint32)
+    for m, m_out in [(512, 512), (1024, 0), (256, 128 * 2)]:
+        w = words[..., : (m + m_out) // 32]
+        st = layout.bits_to_stored(w, m, m_out)
+        np.testing.assert_array_equal(layout.bits_from_stored(st, m, m_out), w)
+        assert st.flags.c_contiguous and layout.bits_from_stored(st, m, m_out).flags.c_contiguous
+    with pytest.raises(ValueError):
+        layout.bits_slots(96, 0)
