@@ -187,38 +187,49 @@ struct MBlock {
     uint32_t cx[8][2];
 };
 
+// Per-lane parts of the block loads (the block start enters as a scalar offset).
+struct MOffsets {
+    int bits;    // sign quarter-row of sub-step 0
+    int nm;      // (norm, meta) of tokens 2 lane, 2 lane + 1
+    int codes;   // channel streams 8 t .. 8 t + 7 of code tile hh
+};
+
 template <int WIN4, int WOUT4>
 __device__ __forceinline__ void load_mblock(MBlock<WIN4, WOUT4>& bl, __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rn,
-                                            __amdgpu_buffer_rsrc_t rm, __amdgpu_buffer_rsrc_t rc, int s0, int t, int hh,
-                                            int lane) {
+                                            __amdgpu_buffer_rsrc_t rm, __amdgpu_buffer_rsrc_t rc, const MOffsets& o, int s0) {
     constexpr int Q = WIN4 + WOUT4;              // words per quarter-row
     constexpr int WB = 4 * Q;
+    // one address add per stream and block; the sub-step offsets are instruction immediates
+    const int vb0 = o.bits + s0 * WB * 4;                       // sub-steps 0..3
+    const int vb1 = vb0 + 64 * WB * 4;                          // sub-steps 4..7
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        const int off = ((s0 + mfma_token(s, t)) * WB + hh * Q) * 4;
+        // token of sub-step s = token of sub-step 0 + 64 (s / 4) + 2 (s % 4)
+        const int voff = (s < 4 ? vb0 : vb1) + 2 * (s & 3) * WB * 4;
         if constexpr (Q == 1) {
-            bl.w[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rb, off, 0, 0);
+            bl.w[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rb, voff, 0, 0);
         } else if constexpr (Q == 2) {
-            const auto x = __builtin_amdgcn_raw_buffer_load_b64(rb, off, 0, 0);
+            const auto x = __builtin_amdgcn_raw_buffer_load_b64(rb, voff, 0, 0);
             bl.w[s][0] = x[0]; bl.w[s][1 % Q] = x[1];
         } else {
-            const auto x = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(rb, voff, 0, 0);
             bl.w[s][0] = x[0]; bl.w[s][1 % Q] = x[1]; bl.w[s][2 % Q] = x[2]; bl.w[s][3 % Q] = x[3];
         }
     }
-    const auto n2 = __builtin_amdgcn_raw_buffer_load_b64(rn, (s0 + 2 * lane) * 4, 0, 0);
-    const auto m2 = __builtin_amdgcn_raw_buffer_load_b64(rm, (s0 + 2 * lane) * 4, 0, 0);
+    const int vn = o.nm + s0 * 4;
+    const auto n2 = __builtin_amdgcn_raw_buffer_load_b64(rn, vn, 0, 0);
+    const auto m2 = __builtin_amdgcn_raw_buffer_load_b64(rm, vn, 0, 0);
     bl.nm[0] = n2[0]; bl.nm[1] = m2[0]; bl.nm[2] = n2[1]; bl.nm[3] = m2[1];
-    // code tile s0/32 + hh = [128 stream slots][2 words]: slots 8 t .. 8 t + 7 = channels 16 cg + t
+    const int vc = o.codes + s0 * (kD * 2 * 4 / kCodeTile);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rc, (s0 / kCodeTile + hh) * 1024 + t * 64 + q * 16, 0, 0);
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rc, vc + 16 * q, 0, 0);
         bl.cx[2 * q][0] = x[0]; bl.cx[2 * q][1] = x[1];
         bl.cx[2 * q + 1][0] = x[2]; bl.cx[2 * q + 1][1] = x[3];
     }
 }
 
-template <int WIN4, int WOUT4>
+template <int WIN4, int WOUT4, bool DBG>
 __global__ __launch_bounds__(kMThreads, 2) void decode_mfma_kernel(DecodeArgs a, int groups, int hgroups) {
     constexpr int W4 = WIN4 + WOUT4;             // instructions (K blocks of 128 sign positions) per token
     constexpr int WB = 4 * W4;                   // sign words per token
@@ -229,7 +240,7 @@ __global__ __launch_bounds__(kMThreads, 2) void decode_mfma_kernel(DecodeArgs a,
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t = lane & 15;                     // B column: token slot (scores) / channel (values)
     const int hh = lane >> 4;                    // lane group: D rows 4 hh .. 4 hh + 3 = query head hh
 
@@ -292,22 +303,18 @@ __global__ __launch_bounds__(kMThreads, 2) void decode_mfma_kernel(DecodeArgs a,
                                                   (uint32_t)t_end * 4u);
     const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(a.codes + (size_t)unit * code_tiles(a.Ncap) * (kD * 2),
                                                   (uint32_t)code_tiles(t_end) * 1024u);
-    float* sdbg = (a.scores_dbg && head_ok) ? a.scores_dbg + (size_t)bhq_d * a.N : nullptr;
+    const MOffsets offs{(mfma_token(0, t) * WB + hh * W4) * 4, 8 * lane, hh * 1024 + t * 64};
+    float* sdbg = DBG && head_ok ? a.scores_dbg + (size_t)bhq_d * a.N : nullptr;
     const float inv_z = 1.0f / a.z_scale;
 
     float m_run = -INFINITY, l_acc = 0.f, mn_acc = 0.f;
     v4f_t dv[8];
 #pragma unroll
     for (int cg = 0; cg < 8; ++cg) dv[cg] = v4f_t{0.f, 0.f, 0.f, 0.f};
-
-    // ---- the block loop, software-pipelined: block i + 1 is in flight while block i is computed
-    //      (loads past the chunk end fall outside the buffer ranges and return zeros)
-    MBlock<WIN4, WOUT4> cur, nxt;
-    const int s_first = t_begin + kMBlock * wave;
-    load_mblock(cur, rb, rn, rm, rc, s_first, t, hh, lane);
     uint32_t* nmw = nmt[wave];
-    for (int s0 = s_first; s0 < t_end; s0 += kMBlock * kMWaves) {
-        load_mblock(nxt, rb, rn, rm, rc, s0 + kMBlock * kMWaves, t, hh, lane);
+
+    // ---- one 128-token block
+    auto process = [&](const MBlock<WIN4, WOUT4>& cur, int s0) {
         // (norm, meta) of the block's tokens to LDS (the previous block's reads are done: LDS
         // operations of a wave complete in order)
         *reinterpret_cast<uint4*>(nmw + 4 * lane) = make_uint4(cur.nm[0], cur.nm[1], cur.nm[2], cur.nm[3]);
@@ -320,7 +327,7 @@ __global__ __launch_bounds__(kMThreads, 2) void decode_mfma_kernel(DecodeArgs a,
             mt[s] = v.y;
         }
 
-        // ---- scores (base-2 logits) of the 8 sub-steps
+        // scores (base-2 logits) of the 8 sub-steps
         float z[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
@@ -342,11 +349,13 @@ __global__ __launch_bounds__(kMThreads, 2) void decode_mfma_kernel(DecodeArgs a,
             }
             const int P = s0 + mfma_token(s, t);
             const bool valid = P < t_end;
-            if (sdbg && valid) sdbg[P] = zz * inv_z;
+            if constexpr (DBG) {
+                if (sdbg && valid) sdbg[P] = zz * inv_z;
+            }
             z[s] = valid ? zz : -INFINITY;
         }
 
-        // ---- online softmax over the block (per head = per row of 16 lanes)
+        // online softmax over the block (per head = per row of 16 lanes)
         float mx = z[0];
 #pragma unroll
         for (int s = 1; s < 8; ++s) mx = fmaxf(mx, z[s]);
@@ -393,7 +402,7 @@ __global__ __launch_bounds__(kMThreads, 2) void decode_mfma_kernel(DecodeArgs a,
         }
         __builtin_amdgcn_wave_barrier();   // the weight tile written above is read across lanes below
 
-        // ---- values: A = weight pieces (row t = (head, piece), K slice hh), B = code tile hh
+        // values: A = weight pieces (row t = (head, piece), K slice hh), B = code tile hh
         const uint4 alo = *reinterpret_cast<const uint4*>(wt + t * kWPitch + 32 * hh);
         const uint4 ahi = *reinterpret_cast<const uint4*>(wt + t * kWPitch + 32 * hh + 16);
         const v8i_t aw = v8i_t{(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
@@ -406,7 +415,20 @@ __global__ __launch_bounds__(kMThreads, 2) void decode_mfma_kernel(DecodeArgs a,
             dv[cg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, bv, dv[cg], 0, 4, 0, sc_w, 0, 127);
         }
         __builtin_amdgcn_wave_barrier();   // the next block rewrites the weight tile
-        cur = nxt;
+    };
+
+    // ---- the block loop, software-pipelined over two buffers: block i + 1 is in flight while block i
+    //      is computed (loads past the chunk end fall outside the buffer ranges and return zeros)
+    constexpr int kStep = kMBlock * kMWaves;
+    MBlock<WIN4, WOUT4> ba, bb;
+    const int s_first = t_begin + kMBlock * wave;
+    load_mblock(ba, rb, rn, rm, rc, offs, s_first);
+    for (int s0 = s_first; s0 < t_end; s0 += 2 * kStep) {
+        load_mblock(bb, rb, rn, rm, rc, offs, s0 + kStep);
+        process(ba, s0);
+        if (s0 + kStep >= t_end) break;
+        load_mblock(ba, rb, rn, rm, rc, offs, s0 + 2 * kStep);
+        process(bb, s0 + kStep);
     }
 
     // ---- merge the four wave streams of each head
@@ -454,7 +476,10 @@ hipError_t launch_decode_mfma_t(const DecodeArgs& a, hipStream_t s) {
     const int slots = (groups + 7) / 8;
     const unsigned nblocks = (unsigned)slots * 8u * (unsigned)hgroups;
     timer_begin(TK_DECODE, s);
-    hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4>), dim3(nblocks), dim3(kMThreads), 0, s, a, groups, hgroups);
+    if (a.scores_dbg)
+        hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, true>), dim3(nblocks), dim3(kMThreads), 0, s, a, groups, hgroups);
+    else
+        hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, false>), dim3(nblocks), dim3(kMThreads), 0, s, a, groups, hgroups);
     timer_end(TK_DECODE, s);
     return hipGetLastError();
 }
