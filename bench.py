@@ -29,7 +29,9 @@ METRIC = "decode keys scored/sec (QJL attention) + % of MI355X HBM peak; quantiz
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0     # MI355X dense bf16
 BYTES_PER_TOKEN_HEAD = 104          # 64 B signs + 4 B norms + 32 B codes + 4 B (min, step)
-DECODE_SOURCE = os.path.join(ROOT, "bit_kv_cache_qjl_amd", "csrc", "qjl_decode.hip")
+DECODE_SOURCES = [os.path.join(ROOT, "bit_kv_cache_qjl_amd", "csrc", f) for f in
+                  ("qjl_decode.hip", "qjl_decode_mfma.hip", "qjl_decode_common.h", "qjl_common.h")]
+DECODE_KERNEL = "decode_mfma_kernel"   # the dominant kernel of the 2-bit value decode workloads
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_{}_traffic.json")
 
 
@@ -37,9 +39,12 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
@@ -49,13 +54,14 @@ def measured_traffic(workload: str):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("decode_source_sha256_16") != source_hash(DECODE_SOURCE):
+    if t.get("decode_source_sha256_16") != source_hash(DECODE_SOURCES):
         return None
     return t.get("bytes_per_launch")
 
 
 KERNELS = ("decode", "quantize_keys", "quantize_values", "query_project", "combine")
 CALIB_BYTES = 1 << 30               # plain copy kernel used to scale FETCH_SIZE / WRITE_SIZE
+MALL_BYTES = 256 << 20              # MI355X last-level (Infinity) cache
 
 
 def _counter_rows(path: str):
@@ -80,16 +86,16 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str) -> int:
     """HBM bytes per decode launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the decode kernel,
     each scaled by what the same counter reads for the plain copy of CALIB_BYTES bytes."""
     import statistics
-    copy_f = _per_dispatch(fetch_csv, "FETCH_SIZE", "copy")
-    copy_w = _per_dispatch(write_csv, "WRITE_SIZE", "copy")
+    copy_f = _per_dispatch(fetch_csv, "FETCH_SIZE", "copyBuffer")      # the runtime's device-to-device blit
+    copy_w = _per_dispatch(write_csv, "WRITE_SIZE", "copyBuffer")
     big_f = max(copy_f)
     big_w = max(copy_w)
     kf = CALIB_BYTES / (big_f * 1024.0)
     kw = CALIB_BYTES / (big_w * 1024.0)
-    dec_f = statistics.mean(_per_dispatch(fetch_csv, "FETCH_SIZE", "decode_kernel"))
-    dec_w = statistics.mean(_per_dispatch(write_csv, "WRITE_SIZE", "decode_kernel"))
+    dec_f = statistics.mean(_per_dispatch(fetch_csv, "FETCH_SIZE", DECODE_KERNEL))
+    dec_w = statistics.mean(_per_dispatch(write_csv, "WRITE_SIZE", DECODE_KERNEL))
     w = si.WORKLOADS[workload]
-    rec = {"workload": workload, "decode_source_sha256_16": source_hash(DECODE_SOURCE),
+    rec = {"workload": workload, "kernel": DECODE_KERNEL, "decode_source_sha256_16": source_hash(DECODE_SOURCES),
            "fetch_kib_per_launch": dec_f, "write_kib_per_launch": dec_w,
            "copy_fetch_kib": big_f, "copy_write_kib": big_w, "copy_bytes": CALIB_BYTES,
            "read_scale": kf, "write_scale": kw,
@@ -182,6 +188,12 @@ def main() -> int:
                     choices=["llama2_7b_decode", "llama3_8b_gqa_decode", "llama31_70b_gqa_decode"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0 = skip)")
     ap.add_argument("--no-quantize", action="store_true", help="skip the prefill quantize measurement")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the step captured once in a HIP graph and replayed (after checking that a replay "
+                         "reproduces the eager result) instead of eager launches")
+    ap.add_argument("--cache-copies", type=int, default=0,
+                    help="independent caches the steps rotate through (0: enough that consecutive steps never "
+                         f"find their cache in the {MALL_BYTES >> 20} MiB last-level cache)")
     ap.add_argument("--quantize-only", action="store_true", help="only the prefill quantize measurement (profiling)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help=f"run one plain {CALIB_BYTES >> 20} MiB device copy first (the reference kernel that "
@@ -215,9 +227,15 @@ def main() -> int:
     S_in = torch.from_numpy(S_in_np).cuda().to(torch.bfloat16)
     S_out = torch.from_numpy(S_out_np).cuda().to(torch.bfloat16)
     od = torch.from_numpy(oidx).cuda()
-    cache = qjl.alloc_cache(w.B, w.Hkv, N, w.m, w.m_out, w.nbits)
-    qjl.quantize_keys(K[:, : N - 1], S_in, S_out, od, cache.bits, cache.norms, t0=0)
-    qjl.quantize_values(V[:, : N - 1], w.nbits, cache.codes, cache.meta, t0=0)
+    cache_bytes = BYTES_PER_TOKEN_HEAD * w.B * w.Hkv * N
+    copies = args.cache_copies or max(1, math.ceil(3 * MALL_BYTES / cache_bytes))
+    caches = []
+    for _ in range(copies):
+        cache = qjl.alloc_cache(w.B, w.Hkv, N, w.m, w.m_out, w.nbits)
+        qjl.quantize_keys(K[:, : N - 1], S_in, S_out, od, cache.bits, cache.norms, t0=0)
+        qjl.quantize_values(V[:, : N - 1], w.nbits, cache.codes, cache.meta, t0=0)
+        caches.append(cache)
+    log(f"bench: {copies} cache cop{'y' if copies == 1 else 'ies'} of {cache_bytes / 1e6:.0f} MB (steps rotate)")
     k_new, v_new = K[:, N - 1:], V[:, N - 1:]
     out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
     ws = torch.empty(qjl.decode_workspace_size(w.B, w.Hq, w.Hkv, N, w.m, w.m_out), dtype=torch.uint8, device="cuda")
@@ -228,7 +246,11 @@ def main() -> int:
         del src, dst
     torch.cuda.synchronize()
 
+    turn = [0]
+
     def step():
+        cache = caches[turn[0] % copies]
+        turn[0] += 1
         qjl.quantize_keys(k_new, S_in, S_out, od, cache.bits, cache.norms, t0=N - 1)
         qjl.quantize_values(v_new, w.nbits, cache.codes, cache.meta, t0=N - 1)
         qjl.decode_attention(Q, S_in, S_out, od, cache.bits, cache.norms, N, out, codes=cache.codes,
@@ -238,18 +260,62 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    def timed(run_one) -> float:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            run_one()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / args.steps * 1e3
+
+    ms_eager = timed(step)
+    graph_ok = None
+    ms_per_step = ms_eager
+    if args.graph:
+        # the same launches captured once and replayed (no host launch overhead per kernel); a replay
+        # must reproduce the eager step bit for bit before it is timed
+        ref_out = out.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for _ in range(copies):             # one graph per cache copy, replayed in rotation
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step()
+            graphs.append(g)
+        turn_g = [0]
+
+        def replay():
+            graphs[turn_g[0] % copies].replay()
+            turn_g[0] += 1
+        for _ in range(3 * copies):
+            out.zero_()
+            torch.cuda.synchronize()
+            replay()
+            torch.cuda.synchronize()
+            graph_ok = bool(torch.equal(out, ref_out))
+            if not graph_ok:
+                break
+        if graph_ok:
+            for _ in range(args.warmup):
+                replay()
+            ms_per_step = timed(replay)
+        else:
+            log("bench: graph replay differs from the eager step; reporting eager timing")
+    # per-kernel durations (HIP events around each launch on its stream), in a separate eager pass
     qjl.timer_enable(True)
     for k in KERNELS:
         qjl.timer_read(k)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
     kernels = {k: qjl.timer_read(k) for k in KERNELS}
     qjl.timer_enable(False)
-    ms_per_step = elapsed / args.steps * 1e3
     keys_scored = w.B * w.Hq * N
     value = keys_scored / (ms_per_step / 1e3)
     n_dec, ms_dec = kernels["decode"]
@@ -267,8 +333,11 @@ def main() -> int:
                    "step": "append 1 token per sequence (key sketch + value codes) + decode attention over N"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
-                     "kernel": "decode", "kernel_ms": dec_s * 1e3, "algorithmic_bytes": bytes_alg},
+                     "kernel": DECODE_KERNEL, "kernel_ms": dec_s * 1e3, "algorithmic_bytes": bytes_alg},
         "kernel_ms_per_launch": {k: v[1] / max(v[0], 1) for k, v in kernels.items()},
+        "step_timing": {"mode": "hip_graph_replay" if (graph_ok and args.graph) else "eager",
+                        "ms_per_step_eager": ms_eager, "graph_replay_matches_eager": graph_ok,
+                        "cache_copies": copies, "cache_bytes": cache_bytes},
     }
     if not args.no_quantize:
         log("bench: prefill quantize stream")

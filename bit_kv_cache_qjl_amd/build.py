@@ -30,9 +30,15 @@ FLAGS = [
 ]
 
 
+# Per-source code-generation options.  The matrix-core decode keeps its MFMA accumulators in the
+# architectural VGPRs: with 8 query heads per workgroup its live state exceeds 256 registers, and the
+# accumulator-register form makes the compiler shuttle values between the two register files.
+EXTRA = {"qjl_decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

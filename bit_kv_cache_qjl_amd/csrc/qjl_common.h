@@ -150,6 +150,8 @@ int decode_pick_nsplit(int B, int Hkv, int g, int64_t N, int m, int m_out);
 int64_t decode_chunk(int64_t N, int nsplit);
 // True when decode runs on the matrix-core path (2-bit value codes, W = (m + m_out)/32 <= 16).
 bool decode_uses_mfma(int m, int m_out, int vmode, int nbits);
+// Row groups of 4 query heads per matrix-core workgroup: 2 (8 heads) when a KV head serves more than 4.
+__host__ __device__ constexpr int decode_mfma_rowgroups(int g) { return g > 4 ? 2 : 1; }
 
 // Launch timer hooks (no-ops unless enabled).
 void timer_begin(TimedKernel k, hipStream_t s);

@@ -433,9 +433,10 @@ bool decode_uses_mfma(int m, int m_out, int vmode, int nbits) {
 int decode_pick_nsplit(int B, int Hkv, int g, int64_t N, int m, int m_out) {
     (void)m;
     (void)m_out;
-    // one workgroup per (sequence, KV head, group of 4 query heads, chunk) on the matrix-core path,
-    // per (sequence, query head, chunk) on the table path; both aim at ~1024 workgroups
-    const int64_t units = (int64_t)B * Hkv * ((g + 3) / 4);
+    // one workgroup per (sequence, KV head, group of 4 or 8 query heads, chunk) on the matrix-core
+    // path, per (sequence, query head, chunk) on the table path; both aim at ~1024 workgroups
+    const int hpg = 4 * decode_mfma_rowgroups(g);
+    const int64_t units = (int64_t)B * Hkv * ((g + hpg - 1) / hpg);
     const int64_t target = 1024;                       // ~4 workgroups per CU on 256 CUs
     int64_t ns = (target + units - 1) / units;
     const int64_t max_ns = (N + kDecodeTile - 1) / kDecodeTile;

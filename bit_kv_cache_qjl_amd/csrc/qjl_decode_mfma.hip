@@ -9,14 +9,17 @@
 // Scores on v_mfma_scale_f32_16x16x128_f8f6f4 (A fp8 e4m3, B fp4 e2m1): 16 tokens x 4 query heads
 // per instruction, 128 sign positions of one kind (inlier or outlier) per instruction.
 //   B (sign bits): with b = 1 for a non-negative projection, a 32-bit sign word x gives four fp4
-//     operand words x & 0x11111111, x & 0x22222222, x & 0x44444444, (x >> 1) & 0x44444444: nibble n
-//     of plane word i holds bit 4n + i with the value 0.5, 1, 2, 2 (e2m1 0001, 0010, 0100, 0100) or 0.
-//   A (query): x_k = 2 z_scale sqrt(pi/2)/m (S q)_k divided by its plane's bit value and scaled by a
-//     per-head power of two, split into three e4m3 pieces (each rounded to nearest, 4 significant
-//     bits, so the residual is below 2^-12 of the value); rows = (query head, piece), the fourth row
-//     of a head is zero, and the instruction's E8M0 row scales undo the powers of two.
-//   sign = 2b - 1, so <S q, sign> = 2 <S q, b> - sum (S q): the accumulator starts at -sum_k x_k / 2
-//     and z = |k_in| D_in + |k_out| D_out is the token's base-2 softmax logit.
+//     operand words, one instruction each: x & 0x11111111, x & 0x22222222, x & 0x44444444 (nibble n
+//     holds bit 4n + i with the value 0.5 b, b, 2 b: e2m1 0001, 0010, 0100) and
+//     (x & 0x88888888) | 0x11111111 (e2m1 0001 or 1001: the value 0.5 - b of bit 4n + 3).
+//   A (query): x_k = 2 z_scale sqrt(pi/2)/m (S q)_k divided by its plane's bit coefficient (0.5, 1,
+//     2, -1) and scaled by a per-head power of two, split into three e4m3 pieces (each rounded to
+//     nearest, 4 significant bits, so the residual is below 2^-12 of the value); rows = (query head,
+//     piece), the fourth row of a head is zero, and the instruction's E8M0 row scales undo the powers
+//     of two.
+//   sign = 2b - 1, so <S q, sign> = 2 <S q, b> - sum (S q).  The plane-3 positions contribute
+//     x_k b_k - x_k / 2 by themselves; the accumulator starts at -sum x_k / 2 over the other
+//     positions, so z = |k_in| D_in + |k_out| D_out is the token's base-2 softmax logit.
 // Values on the same instruction: rows = (query head, piece) of the weight p * step, columns = 16
 // channels, K = 128 tokens; B = the 2-bit codes of a code tile as x & 0x33333333 and
 // (x >> 2) & 0x33333333 (e2m1 nibble 00cc = code / 2).  The weights of a 128-token block are scaled
@@ -52,10 +55,13 @@ __device__ __forceinline__ void next_piece(float (&r)[4], uint32_t k) {
     r[3] = (r[3] - __builtin_amdgcn_cvt_f32_fp8((int)k, 3)) * 16.f;
 }
 
-// The four fp4 operand words of a sign word (plane i = bit 4n + i of x in nibble n).
-__device__ __forceinline__ v8i_t sign_planes(uint32_t x) {
+// The four fp4 operand words of a sign word (plane i = bit 4n + i of x in nibble n).  m8 and o1 hold
+// 0x88888888 and 0x11111111 in VGPRs (VOP3 takes no literals), so the last word is one v_and_or_b32;
+// the code stays plain C, so the compiler sees every instruction that feeds the matrix core and
+// inserts its wait states.
+__device__ __forceinline__ v8i_t sign_planes(uint32_t x, uint32_t m8, uint32_t o1) {
     return v8i_t{(int)(x & 0x11111111u), (int)(x & 0x22222222u), (int)(x & 0x44444444u),
-                 (int)((x >> 1) & 0x44444444u), 0, 0, 0, 0};
+                 (int)((x & m8) | o1), 0, 0, 0, 0};
 }
 
 // ---------------------------------------------------------------------------- query operand
@@ -63,7 +69,8 @@ __device__ __forceinline__ v8i_t sign_planes(uint32_t x) {
 // in the order the decode kernel loads them, [K block kb][piece][lane group ga][32 bytes]: byte ea of
 // lane group ga is K index k = 16 ga + ea % 16 + 64 (ea / 16) of the instruction, and K index k pairs
 // with bit 4n + i (n = (k % 32) % 8, i = (k % 32) / 8) of the sign word that B lane group k / 32
-// supplies.  Also the per-head constants [-sum x_in / 2, -sum x_out / 2, e_in, e_out].
+// supplies.  Also the per-head constants [-sum x_in / 2, -sum x_out / 2 (both over the positions
+// outside plane 3), e_in, e_out].
 template <typename QT>
 __global__ __launch_bounds__(256) void qproj_mfma_kernel(DecodeArgs a, int win4, int wout4) {
     __shared__ float qin[kD];
@@ -85,17 +92,17 @@ __global__ __launch_bounds__(256) void qproj_mfma_kernel(DecodeArgs a, int win4,
     __syncthreads();
     const QT* Sin = static_cast<const QT*>(a.S_in);
     const QT* Sout = static_cast<const QT*>(a.S_out);
-    // |x| divided by the bit value of its plane (0.5, 1, 2, 2 for position % 4 = 0, 1, 2, 3)
+    // |x| divided by its plane's bit coefficient (0.5, 1, 2, -1 for position % 4 = 0, 1, 2, 3)
     auto plane_abs = [](float x, int pos) {
         const int i = pos & 3;
-        return fabsf(x) * (i == 0 ? 2.f : (i == 1 ? 1.f : 0.5f));
+        return fabsf(x) * (i == 0 ? 2.f : (i == 2 ? 0.5f : 1.f));
     };
     const float c_in = 2.f * a.z_scale * kSqrtHalfPi / (float)a.m;
     float sum_in = 0.f, sum_out = 0.f, mx_in = 0.f, mx_out = 0.f;
     for (int j = tid; j < a.m; j += 256) {
         const float x = row_dot(Sin + (size_t)j * kD, qin) * c_in;
         xs[j] = x;
-        sum_in += x;
+        if ((j & 3) != 3) sum_in += x;          // plane-3 positions carry their own -x/2
         mx_in = fmaxf(mx_in, plane_abs(x, j));
     }
     if (a.m_out) {
@@ -105,7 +112,7 @@ __global__ __launch_bounds__(256) void qproj_mfma_kernel(DecodeArgs a, int win4,
             for (int i = 0; i < a.n_out; ++i) acc = fmaf(load_elem<QT>(Sout, (size_t)j * kD + so[i]), qo[i], acc);
             const float x = acc * c_out;
             xs[a.m + j] = x;
-            sum_out += x;
+            if (((a.m + j) & 3) != 3) sum_out += x;
             mx_out = fmaxf(mx_out, plane_abs(x, a.m + j));
         }
     }
@@ -157,8 +164,9 @@ __global__ __launch_bounds__(256) void qproj_mfma_kernel(DecodeArgs a, int win4,
             const int gb = k >> 5, eb = k & 31;
             const int plane = eb >> 3, n = eb & 7;
             const int word = out ? 4 * win4 + gb * wout4 + (kb - win4) : gb * win4 + kb;
-            // divided by the plane's bit value and scaled by the head's power of two (exact)
-            float v = ldexpf(xs[32 * word + 4 * n + plane], e + (plane == 0 ? 1 : (plane == 1 ? 0 : -1)));
+            // divided by the plane's bit coefficient and scaled by the head's power of two (exact)
+            float v = ldexpf(xs[32 * word + 4 * n + plane], e + (plane == 0 ? 1 : (plane == 2 ? -1 : 0)));
+            if (plane == 3) v = -v;
             for (int r = 0; r < piece; ++r) {   // v = p0 + p1 / 16 + p2 / 256 + residual
                 const float pr = __builtin_amdgcn_cvt_f32_fp8(__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.f, 0, false), 0);
                 v = (v - pr) * 16.f;
@@ -229,20 +237,23 @@ __device__ __forceinline__ void load_mblock(MBlock<WIN4, WOUT4>& bl, __amdgpu_bu
     }
 }
 
-template <int WIN4, int WOUT4, bool DBG>
-__global__ __launch_bounds__(kMThreads, 2) void decode_mfma_kernel(DecodeArgs a, int groups, int hgroups) {
+// R = 1: one workgroup serves 4 query heads of a KV head; R = 2: 8 query heads as two row groups of
+// the same instructions' B operands (the sign and code planes are built once for both).
+template <int WIN4, int WOUT4, int R, bool DBG>
+__global__ __launch_bounds__(kMThreads, R == 1 ? 2 : 1) void decode_mfma_kernel(DecodeArgs a, int groups, int hgroups) {
     constexpr int W4 = WIN4 + WOUT4;             // instructions (K blocks of 128 sign positions) per token
     constexpr int WB = 4 * W4;                   // sign words per token
-    __shared__ __attribute__((aligned(16))) uint8_t wtile[kMWaves][16 * kWPitch];   // weight pieces
-    __shared__ __attribute__((aligned(16))) uint32_t nmt[kMWaves][2 * kMBlock];     // (norm, meta) per token
-    __shared__ float red_m[kMWaves][4], red_l[kMWaves][4], red_mn[kMWaves][4];
-    __shared__ __attribute__((aligned(16))) float red_o[kMWaves][4][kD];
+    constexpr int HPG = 4 * R;                   // query heads per workgroup
+    __shared__ __attribute__((aligned(16))) uint8_t wtile[kMWaves][R][16 * kWPitch];   // weight pieces
+    __shared__ __attribute__((aligned(16))) uint32_t nmt[kMWaves][2 * kMBlock];        // (norm, meta) per token
+    __shared__ float red_m[kMWaves][HPG], red_l[kMWaves][HPG], red_mn[kMWaves][HPG];
+    __shared__ __attribute__((aligned(16))) float red_o[kMWaves][HPG][kD];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int t = lane & 15;                     // B column: token slot (scores) / channel (values)
-    const int hh = lane >> 4;                    // lane group: D rows 4 hh .. 4 hh + 3 = query head hh
+    const int hh = lane >> 4;                    // lane group: D rows 4 hh .. 4 hh + 3 = head hh of a row group
 
     // XCD-aware placement: the head groups of one (KV head, chunk) run on one XCD (shared L2)
     const int lin = blockIdx.x;
@@ -257,43 +268,51 @@ __global__ __launch_bounds__(kMThreads, 2) void decode_mfma_kernel(DecodeArgs a,
     const int h = unit - b * a.Hkv;
     const int t_begin = (int)((int64_t)split * a.chunk);
     const int t_end = (int)min(a.N, (int64_t)t_begin + a.chunk);
+    const int head0 = b * a.Hq + h * a.g;        // (b, first query head of KV head h)
 
-    // ---- score A operands and scales: this lane's A row is (head rh, piece pc), K slice hh
+    // ---- score A operands and scales: this lane's A row in row group rg is (head 4 rg + rh, piece pc),
+    //      K slice hh
     const int rh = t >> 2, pc = lane & 3;
-    const int qa_head = 4 * hg + rh;
-    v8i_t sA[W4];
-    int sc_in = 127, sc_out = 127;
-    if (qa_head < a.g) {
-        const int bhq = b * a.Hq + h * a.g + qa_head;
-        const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.sq) + (size_t)bhq * (128 * WB));
+    v8i_t sA[R][W4];
+    int sc_in[R], sc_out[R];
 #pragma unroll
-        for (int kb = 0; kb < W4; ++kb) {
-            const uint4 lo = src[kb * 32 + (pc * 4 + hh) * 2], hi = src[kb * 32 + (pc * 4 + hh) * 2 + 1];
-            sA[kb] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    for (int rg = 0; rg < R; ++rg) {
+        const int qa_head = HPG * hg + 4 * rg + rh;
+        sc_in[rg] = sc_out[rg] = 127;
+        if (qa_head < a.g) {
+            const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.sq) +
+                                                              (size_t)(head0 + qa_head) * (128 * WB));
+#pragma unroll
+            for (int kb = 0; kb < W4; ++kb) {
+                const uint4 lo = src[kb * 32 + (pc * 4 + hh) * 2], hi = src[kb * 32 + (pc * 4 + hh) * 2 + 1];
+                sA[rg][kb] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
+            const float* c = a.qconst + (size_t)(head0 + qa_head) * 4;
+            sc_in[rg] = 127 - __float_as_int(c[2]) - 4 * pc;
+            sc_out[rg] = 127 - __float_as_int(c[3]) - 4 * pc;
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < W4; ++kb) sA[rg][kb] = v8i_t{0, 0, 0, 0, 0, 0, 0, 0};
         }
-        const float* c = a.qconst + (size_t)bhq * 4;
-        sc_in = 127 - __float_as_int(c[2]) - 4 * pc;
-        sc_out = 127 - __float_as_int(c[3]) - 4 * pc;
-    } else {
-#pragma unroll
-        for (int kb = 0; kb < W4; ++kb) sA[kb] = v8i_t{0, 0, 0, 0, 0, 0, 0, 0};
     }
-    // ---- D-side constants: lane group hh is query head 4 hg + hh of the KV head
-    const int dhead = 4 * hg + hh;
-    const bool head_ok = dhead < a.g;
-    const int bhq_d = b * a.Hq + h * a.g + (head_ok ? dhead : 0);
-    float cin = 0.f, cout = 0.f;
-    if (head_ok) {
-        cin = a.qconst[(size_t)bhq_d * 4];
-        cout = a.qconst[(size_t)bhq_d * 4 + 1];
+    // ---- D-side constants: lane group hh is query head HPG hg + 4 rg + hh of the KV head
+    float cin[R], cout[R];
+    float* sdbg[R];
+#pragma unroll
+    for (int rg = 0; rg < R; ++rg) {
+        const int dhead = HPG * hg + 4 * rg + hh;
+        const bool ok = dhead < a.g;
+        cin[rg] = ok ? a.qconst[(size_t)(head0 + dhead) * 4] : 0.f;
+        cout[rg] = ok ? a.qconst[(size_t)(head0 + dhead) * 4 + 1] : 0.f;
+        sdbg[rg] = (DBG && ok) ? a.scores_dbg + (size_t)(head0 + dhead) * a.N : nullptr;
     }
 
-    // zero this wave's weight tile once (the rows of piece 3 are never written again)
-    uint8_t* wt = wtile[wave];
-    for (int i = lane; i < 16 * kWPitch / 16; i += 64) reinterpret_cast<uint4*>(wt)[i] = make_uint4(0, 0, 0, 0);
+    // zero this wave's weight tiles once (the rows of piece 3 are never written again)
+    uint8_t* wt = &wtile[wave][0][0];
+    for (int i = lane; i < R * 16 * kWPitch / 16; i += 64) reinterpret_cast<uint4*>(wt)[i] = make_uint4(0, 0, 0, 0);
     __builtin_amdgcn_wave_barrier();
 
-    // this lane's byte offset in the weight tile for sub-steps 4q..4q+3 (row and 16 q added later)
+    // this lane's byte offset in a weight tile for sub-steps 4q..4q+3 (row and 16 q added later)
     const int woff = 32 * (2 * ((t >> 3) & 1) + ((t >> 2) & 1)) + 8 * (t & 1) + 4 * ((t >> 1) & 1);
 
     const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(a.bits + (size_t)unit * a.Ncap * WB, (uint32_t)t_end * WB * 4u);
@@ -304,14 +323,21 @@ __global__ __launch_bounds__(kMThreads, 2) void decode_mfma_kernel(DecodeArgs a,
     const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(a.codes + (size_t)unit * code_tiles(a.Ncap) * (kD * 2),
                                                   (uint32_t)code_tiles(t_end) * 1024u);
     const MOffsets offs{(mfma_token(0, t) * WB + hh * W4) * 4, 8 * lane, hh * 1024 + t * 64};
-    float* sdbg = DBG && head_ok ? a.scores_dbg + (size_t)bhq_d * a.N : nullptr;
     const float inv_z = 1.0f / a.z_scale;
 
-    float m_run = -INFINITY, l_acc = 0.f, mn_acc = 0.f;
-    v4f_t dv[8];
+    float m_run[R], l_acc[R], mn_acc[R];
+    v4f_t dv[R][8];
 #pragma unroll
-    for (int cg = 0; cg < 8; ++cg) dv[cg] = v4f_t{0.f, 0.f, 0.f, 0.f};
+    for (int rg = 0; rg < R; ++rg) {
+        m_run[rg] = -INFINITY;
+        l_acc[rg] = mn_acc[rg] = 0.f;
+#pragma unroll
+        for (int cg = 0; cg < 8; ++cg) dv[rg][cg] = v4f_t{0.f, 0.f, 0.f, 0.f};
+    }
     uint32_t* nmw = nmt[wave];
+    // plane-3 masks in VGPRs; the empty asm only hides the constants from constant folding
+    uint32_t m8 = 0x88888888u, o1 = 0x11111111u;
+    asm volatile("" : "+v"(m8), "+v"(o1));
 
     // ---- one 128-token block
     auto process = [&](const MBlock<WIN4, WOUT4>& cur, int s0) {
@@ -328,41 +354,41 @@ __global__ __launch_bounds__(kMThreads, 2) void decode_mfma_kernel(DecodeArgs a,
         }
 
         // scores (base-2 logits) of the 8 sub-steps
-        float z[8];
+        float z[R][8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            v4f_t din = v4f_t{cin, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < WIN4; ++kb)
-                din = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sA[kb], sign_planes(cur.w[s][kb]), din, 0, 4, 0,
-                                                                       sc_in, 0, 127);
             const float n_in = (float)__builtin_bit_cast(_Float16, (uint16_t)(nrm[s] & 0xFFFFu));
-            float zz = n_in * ((din[0] + din[1]) + din[2]);
-            if constexpr (WOUT4 > 0) {
-                v4f_t dout = v4f_t{cout, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb < WOUT4; ++kb)
-                    dout = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sA[WIN4 + kb], sign_planes(cur.w[s][WIN4 + kb]),
-                                                                            dout, 0, 4, 0, sc_out, 0, 127);
-                const float n_out = (float)__builtin_bit_cast(_Float16, (uint16_t)(nrm[s] >> 16));
-                zz = fmaf(n_out, (dout[0] + dout[1]) + dout[2], zz);
-            }
+            const float n_out = (float)__builtin_bit_cast(_Float16, (uint16_t)(nrm[s] >> 16));
             const int P = s0 + mfma_token(s, t);
             const bool valid = P < t_end;
-            if constexpr (DBG) {
-                if (sdbg && valid) sdbg[P] = zz * inv_z;
+            v8i_t bin[WIN4], bout[WOUT4 > 0 ? WOUT4 : 1];
+#pragma unroll
+            for (int kb = 0; kb < WIN4; ++kb) bin[kb] = sign_planes(cur.w[s][kb], m8, o1);
+#pragma unroll
+            for (int kb = 0; kb < WOUT4; ++kb) bout[kb] = sign_planes(cur.w[s][WIN4 + kb], m8, o1);
+#pragma unroll
+            for (int rg = 0; rg < R; ++rg) {
+                v4f_t din = v4f_t{cin[rg], 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < WIN4; ++kb)
+                    din = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sA[rg][kb], bin[kb], din, 0, 4, 0, sc_in[rg], 0, 127);
+                float zz = n_in * ((din[0] + din[1]) + din[2]);
+                if constexpr (WOUT4 > 0) {
+                    v4f_t dout = v4f_t{cout[rg], 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb < WOUT4; ++kb)
+                        dout = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sA[rg][WIN4 + kb], bout[kb], dout, 0, 4, 0,
+                                                                                sc_out[rg], 0, 127);
+                    zz = fmaf(n_out, (dout[0] + dout[1]) + dout[2], zz);
+                }
+                if constexpr (DBG) {
+                    if (sdbg[rg] && valid) sdbg[rg][P] = zz * inv_z;
+                }
+                z[rg][s] = valid ? zz : -INFINITY;
             }
-            z[s] = valid ? zz : -INFINITY;
         }
 
-        // online softmax over the block (per head = per row of 16 lanes)
-        float mx = z[0];
-#pragma unroll
-        for (int s = 1; s < 8; ++s) mx = fmaxf(mx, z[s]);
-        mx = row16_max(mx);
-        const float m_new = fmaxf(m_run, mx);            // finite: token s0 of the block is valid
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
+        // step scale of the block (shared by the row groups): every step of the block < 2^E
         float mxs = 0.f, stp[8], mnv[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
@@ -371,50 +397,78 @@ __global__ __launch_bounds__(kMThreads, 2) void decode_mfma_kernel(DecodeArgs a,
             mxs = fmaxf(mxs, stp[s]);
         }
         mxs = row16_max(mxs);
-        const int E = mxs > 0.f ? __builtin_amdgcn_frexp_expf(mxs) : 0;   // every step of the block < 2^E
-        l_acc *= alpha;
-        mn_acc *= alpha;
+        const int E = mxs > 0.f ? __builtin_amdgcn_frexp_expf(mxs) : 0;
+        float stpf[8];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            float w[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int s = 4 * q + i;
-                const float p = __builtin_amdgcn_exp2f(z[s] - m_new);
-                l_acc += p;
-                mn_acc = fmaf(p, mnv[s], mn_acc);
-                w[i] = p * ldexpf(stp[s], 8 - E);             // in [0, 256)
-            }
-            // three e4m3 pieces: w = p0 + p1 / 16 + p2 / 256 + residual
-            const uint32_t k0 = fp8x4(w[0], w[1], w[2], w[3]);
-            next_piece(w, k0);
-            const uint32_t k1 = fp8x4(w[0], w[1], w[2], w[3]);
-            next_piece(w, k1);
-            const uint32_t k2 = fp8x4(w[0], w[1], w[2], w[3]);
-            uint8_t* row = wt + (4 * hh) * kWPitch + woff + 16 * q;
-            *reinterpret_cast<uint32_t*>(row) = k0;
-            *reinterpret_cast<uint32_t*>(row + kWPitch) = k1;
-            *reinterpret_cast<uint32_t*>(row + 2 * kWPitch) = k2;
-        }
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-            for (int cg = 0; cg < 8; ++cg) dv[cg] *= alpha;
-        }
-        __builtin_amdgcn_wave_barrier();   // the weight tile written above is read across lanes below
+        for (int s = 0; s < 8; ++s) stpf[s] = ldexpf(stp[s], 8 - E);
+        bool rescale = false;
+        float alpha[R];
 
-        // values: A = weight pieces (row t = (head, piece), K slice hh), B = code tile hh
-        const uint4 alo = *reinterpret_cast<const uint4*>(wt + t * kWPitch + 32 * hh);
-        const uint4 ahi = *reinterpret_cast<const uint4*>(wt + t * kWPitch + 32 * hh + 16);
-        const v8i_t aw = v8i_t{(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
+        // online softmax per row group (per head = per row of 16 lanes), weights to the LDS tile
+#pragma unroll
+        for (int rg = 0; rg < R; ++rg) {
+            float mx = z[rg][0];
+#pragma unroll
+            for (int s = 1; s < 8; ++s) mx = fmaxf(mx, z[rg][s]);
+            mx = row16_max(mx);
+            const float m_new = fmaxf(m_run[rg], mx);    // finite: token s0 of the block is valid
+            alpha[rg] = __builtin_amdgcn_exp2f(m_run[rg] - m_new);
+            rescale |= alpha[rg] != 1.f;
+            m_run[rg] = m_new;
+            l_acc[rg] *= alpha[rg];
+            mn_acc[rg] *= alpha[rg];
+            uint8_t* row0 = wt + rg * 16 * kWPitch + (4 * hh) * kWPitch + woff;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                float w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int s = 4 * q + i;
+                    const float p = __builtin_amdgcn_exp2f(z[rg][s] - m_new);
+                    l_acc[rg] += p;
+                    mn_acc[rg] = fmaf(p, mnv[s], mn_acc[rg]);
+                    w[i] = p * stpf[s];                   // in [0, 256)
+                }
+                // three e4m3 pieces: w = p0 + p1 / 16 + p2 / 256 + residual
+                const uint32_t k0 = fp8x4(w[0], w[1], w[2], w[3]);
+                next_piece(w, k0);
+                const uint32_t k1 = fp8x4(w[0], w[1], w[2], w[3]);
+                next_piece(w, k1);
+                const uint32_t k2 = fp8x4(w[0], w[1], w[2], w[3]);
+                uint8_t* row = row0 + 16 * q;
+                *reinterpret_cast<uint32_t*>(row) = k0;
+                *reinterpret_cast<uint32_t*>(row + kWPitch) = k1;
+                *reinterpret_cast<uint32_t*>(row + 2 * kWPitch) = k2;
+            }
+        }
+        if (__builtin_amdgcn_ballot_w64(rescale)) {
+#pragma unroll
+            for (int rg = 0; rg < R; ++rg)
+#pragma unroll
+                for (int cg = 0; cg < 8; ++cg) dv[rg][cg] *= alpha[rg];
+        }
+        __builtin_amdgcn_wave_barrier();   // the weight tiles written above are read across lanes below
+
+        // values: A = weight pieces (row t = (head, piece), K slice hh), B = code tile hh (built once)
+        v8i_t aw[R];
+#pragma unroll
+        for (int rg = 0; rg < R; ++rg) {
+            const uint8_t* src = wt + rg * 16 * kWPitch + t * kWPitch + 32 * hh;
+            const uint4 alo = *reinterpret_cast<const uint4*>(src);
+            const uint4 ahi = *reinterpret_cast<const uint4*>(src + 16);
+            aw[rg] = v8i_t{(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
+        }
         const int sc_w = 120 + E - 4 * pc;   // 2^(E - 8 - 4 piece), times 2 for the nibble = code / 2
 #pragma unroll
         for (int cg = 0; cg < 8; ++cg) {
             const uint32_t x0 = cur.cx[cg][0], x1 = cur.cx[cg][1];
             const v8i_t bv = v8i_t{(int)(x0 & 0x33333333u), (int)((x0 >> 2) & 0x33333333u), (int)(x1 & 0x33333333u),
                                    (int)((x1 >> 2) & 0x33333333u), 0, 0, 0, 0};
-            dv[cg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw, bv, dv[cg], 0, 4, 0, sc_w, 0, 127);
+#pragma unroll
+            for (int rg = 0; rg < R; ++rg)
+                dv[rg][cg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw[rg], bv, dv[rg][cg], 0, 4, 0, sc_w, 0, 127);
         }
-        __builtin_amdgcn_wave_barrier();   // the next block rewrites the weight tile
+        __builtin_amdgcn_wave_barrier();   // the next block rewrites the weight tiles
     };
 
     // ---- the block loop, software-pipelined over two buffers: block i + 1 is in flight while block i
@@ -432,56 +486,64 @@ __global__ __launch_bounds__(kMThreads, 2) void decode_mfma_kernel(DecodeArgs a,
     }
 
     // ---- merge the four wave streams of each head
-    const float l_sum = row16_sum(l_acc), mn_sum = row16_sum(mn_acc);
-    if (t == 0) {
-        red_m[wave][hh] = m_run;
-        red_l[wave][hh] = l_sum;
-        red_mn[wave][hh] = mn_sum;
-    }
 #pragma unroll
-    for (int cg = 0; cg < 8; ++cg) red_o[wave][hh][16 * cg + t] = (dv[cg][0] + dv[cg][1]) + dv[cg][2];
-    __syncthreads();
-    const int oh = tid >> 6;                 // head of the group handled by this thread
-    const int c0 = 2 * (tid & 63);           // channels c0, c0 + 1
-    if (4 * hg + oh >= a.g) return;
-    float M = red_m[0][oh];
-#pragma unroll
-    for (int w = 1; w < kMWaves; ++w) M = fmaxf(M, red_m[w][oh]);
-    float L = 0.f, o0 = 0.f, o1 = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-        for (int w = 0; w < kMWaves; ++w) {
-            const float mw = red_m[w][oh];
-            if (mw == -INFINITY) continue;
-            const float sc = exp2f(mw - M);
-            L = fmaf(sc, red_l[w][oh], L);
-            o0 = fmaf(sc, red_o[w][oh][c0] + red_mn[w][oh], o0);
-            o1 = fmaf(sc, red_o[w][oh][c0 + 1] + red_mn[w][oh], o1);
+    for (int rg = 0; rg < R; ++rg) {
+        const float l_sum = row16_sum(l_acc[rg]), mn_sum = row16_sum(mn_acc[rg]);
+        if (t == 0) {
+            red_m[wave][4 * rg + hh] = m_run[rg];
+            red_l[wave][4 * rg + hh] = l_sum;
+            red_mn[wave][4 * rg + hh] = mn_sum;
         }
+#pragma unroll
+        for (int cg = 0; cg < 8; ++cg) red_o[wave][4 * rg + hh][16 * cg + t] = (dv[rg][cg][0] + dv[rg][cg][1]) + dv[rg][cg][2];
     }
-    const int bhq = b * a.Hq + h * a.g + 4 * hg + oh;
-    float* dst = a.part + ((size_t)bhq * a.nsplit + split) * (kD + 2);
-    dst[2 + c0] = o0;
-    dst[3 + c0] = o1;
-    if ((tid & 63) == 0) {
-        dst[0] = M;
-        dst[1] = L;
+    __syncthreads();
+    const int c0 = 2 * (tid & 63);           // channels c0, c0 + 1
+    for (int oh = tid >> 6; oh < HPG; oh += kMWaves) {
+        if (HPG * hg + oh >= a.g) break;
+        float M = red_m[0][oh];
+#pragma unroll
+        for (int w = 1; w < kMWaves; ++w) M = fmaxf(M, red_m[w][oh]);
+        float L = 0.f, o0 = 0.f, o1 = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < kMWaves; ++w) {
+                const float mw = red_m[w][oh];
+                if (mw == -INFINITY) continue;
+                const float sc = exp2f(mw - M);
+                L = fmaf(sc, red_l[w][oh], L);
+                o0 = fmaf(sc, red_o[w][oh][c0] + red_mn[w][oh], o0);
+                o1 = fmaf(sc, red_o[w][oh][c0 + 1] + red_mn[w][oh], o1);
+            }
+        }
+        float* dst = a.part + ((size_t)(head0 + HPG * hg + oh) * a.nsplit + split) * (kD + 2);
+        dst[2 + c0] = o0;
+        dst[3 + c0] = o1;
+        if ((tid & 63) == 0) {
+            dst[0] = M;
+            dst[1] = L;
+        }
     }
 }
 
-template <int WIN4, int WOUT4>
-hipError_t launch_decode_mfma_t(const DecodeArgs& a, hipStream_t s) {
-    const int hgroups = (a.g + 3) / 4;
+template <int WIN4, int WOUT4, int R>
+hipError_t launch_decode_mfma_r(const DecodeArgs& a, hipStream_t s) {
+    const int hgroups = (a.g + 4 * R - 1) / (4 * R);
     const int groups = a.B * a.Hkv * a.nsplit;
     const int slots = (groups + 7) / 8;
     const unsigned nblocks = (unsigned)slots * 8u * (unsigned)hgroups;
     timer_begin(TK_DECODE, s);
     if (a.scores_dbg)
-        hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, true>), dim3(nblocks), dim3(kMThreads), 0, s, a, groups, hgroups);
+        hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, R, true>), dim3(nblocks), dim3(kMThreads), 0, s, a, groups, hgroups);
     else
-        hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, false>), dim3(nblocks), dim3(kMThreads), 0, s, a, groups, hgroups);
+        hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, R, false>), dim3(nblocks), dim3(kMThreads), 0, s, a, groups, hgroups);
     timer_end(TK_DECODE, s);
     return hipGetLastError();
+}
+
+template <int WIN4, int WOUT4>
+hipError_t launch_decode_mfma_t(const DecodeArgs& a, hipStream_t s) {
+    return decode_mfma_rowgroups(a.g) == 2 ? launch_decode_mfma_r<WIN4, WOUT4, 2>(a, s) : launch_decode_mfma_r<WIN4, WOUT4, 1>(a, s);
 }
 
 }  // namespace
