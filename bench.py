@@ -59,7 +59,7 @@ def measured_traffic(workload: str):
     return t.get("bytes_per_launch")
 
 
-KERNELS = ("decode", "quantize_keys", "quantize_values", "query_project", "combine")
+KERNELS = ("decode", "append_project", "quantize_keys", "quantize_values", "query_project", "combine")
 CALIB_BYTES = 1 << 30               # plain copy kernel used to scale FETCH_SIZE / WRITE_SIZE
 MALL_BYTES = 256 << 20              # MI355X last-level (Infinity) cache
 
@@ -194,6 +194,9 @@ def main() -> int:
     ap.add_argument("--cache-copies", type=int, default=0,
                     help="independent caches the steps rotate through (0: enough that consecutive steps never "
                          f"find their cache in the {MALL_BYTES >> 20} MiB last-level cache)")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="run the step as three calls (quantize keys, quantize values, decode attention) instead "
+                         "of the one decode-step call")
     ap.add_argument("--quantize-only", action="store_true", help="only the prefill quantize measurement (profiling)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help=f"run one plain {CALIB_BYTES >> 20} MiB device copy first (the reference kernel that "
@@ -251,10 +254,13 @@ def main() -> int:
     def step():
         cache = caches[turn[0] % copies]
         turn[0] += 1
-        qjl.quantize_keys(k_new, S_in, S_out, od, cache.bits, cache.norms, t0=N - 1)
-        qjl.quantize_values(v_new, w.nbits, cache.codes, cache.meta, t0=N - 1)
-        qjl.decode_attention(Q, S_in, S_out, od, cache.bits, cache.norms, N, out, codes=cache.codes,
-                             meta=cache.meta, nbits=w.nbits, workspace=ws)
+        if args.separate_calls:
+            qjl.quantize_keys(k_new, S_in, S_out, od, cache.bits, cache.norms, t0=N - 1)
+            qjl.quantize_values(v_new, w.nbits, cache.codes, cache.meta, t0=N - 1)
+            qjl.decode_attention(Q, S_in, S_out, od, cache.bits, cache.norms, N, out, codes=cache.codes,
+                                 meta=cache.meta, nbits=w.nbits, workspace=ws)
+        else:
+            qjl.decode_step(Q, k_new, v_new, S_in, S_out, od, cache, N, out, workspace=ws)
 
     log(f"bench: warmup {args.warmup}, timed {args.steps}")
     for _ in range(args.warmup):
@@ -330,7 +336,9 @@ def main() -> int:
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "N": N, "m": w.m,
                    "m_out": w.m_out, "n_out": w.n_out, "outlier_scale": w.outlier_scale, "value_bits": w.nbits,
-                   "step": "append 1 token per sequence (key sketch + value codes) + decode attention over N"},
+                   "step": "append 1 token per sequence (key sketch + value codes) + decode attention over N",
+                   "entry_points": ("qjl_quantize_keys + qjl_quantize_values + qjl_decode_attention"
+                                    if args.separate_calls else "qjl_decode_step")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
                      "kernel": DECODE_KERNEL, "kernel_ms": dec_s * 1e3, "algorithmic_bytes": bytes_alg},

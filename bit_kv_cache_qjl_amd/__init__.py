@@ -2,7 +2,7 @@
 
 Argument marshalling only: every step of the path runs in the HIP kernels of libqjl.so, reached
 through its C ABI (include/qjl.h).  PyTorch supplies device memory and the current stream.  The
-library must be built first (python -m bit_kv_cache_qjl_amd.build); importing this package without
+library must be built first (python bit_kv_cache_qjl_amd/build.py); importing this package without
 it raises, and there is no other implementation to fall back to.
 """
 from __future__ import annotations
@@ -28,7 +28,7 @@ QJL_V_CODES = 0
 QJL_V_F32 = 1
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_kv_cache_qjl_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python bit_kv_cache_qjl_amd/build.py`")
 
 lib = ctypes.CDLL(LIB_PATH)
 
@@ -44,6 +44,9 @@ lib.qjl_decode_workspace_size.argtypes = [_i, _i, _i, _i, _i64, _i, _i, _i]
 lib.qjl_decode_attention.restype = _i
 lib.qjl_decode_attention.argtypes = [_p, _i, _i, _i, _i, _i, _i64, _p, _i, _p, _i, _p, _i, _p, _p, _i64,
                                      _i, _p, _p, _p, _i, _f, _p, _p, _i, _p, _sz, _p]
+lib.qjl_decode_step.restype = _i
+lib.qjl_decode_step.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _p, _i, _p, _i, _p, _i,
+                                _p, _p, _p, _p, _i64, _i, _f, _p, _p, _i, _p, _sz, _p]
 lib.qjl_status_string.restype = ctypes.c_char_p
 lib.qjl_status_string.argtypes = [_i]
 lib.qjl_last_error.restype = ctypes.c_char_p
@@ -192,6 +195,37 @@ def decode_attention(Q, S_in, S_out, outlier_idx, bits, norms, N: int, out, *, c
                                     _ptr(V_f32), nbits, sm_scale, _ptr(out), _ptr(scores_dbg), nsplit,
                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream)), "qjl_decode_attention")
+
+
+def decode_step(Q, K_new, V_new, S_in, S_out, outlier_idx, cache: Cache, N: int, out, *, sm_scale: float = 0.0,
+                scores_dbg=None, nsplit: int = 0, workspace=None, stream=None) -> None:
+    """qjl_decode_step on torch tensors: append the new token (K_new, V_new [B, 1, Hkv, d], d contiguous)
+    at position N - 1 of the cache, then decode Q [B, Hq, d] over the first N positions into out."""
+    B, Hq, d = Q.shape
+    if not Q.is_contiguous():
+        raise ValueError("Q must be contiguous [B, Hq, d]")
+    for name, t in (("K_new", K_new), ("V_new", V_new)):
+        if t.dim() != 4 or t.shape[1] != 1 or t.stride(3) != 1:
+            raise ValueError(f"{name} must be [B, 1, Hkv, d] with the d channels contiguous")
+        if t.dtype != Q.dtype:
+            raise TypeError(f"{name} must have the dtype of Q")
+    _contiguous(S_in=S_in, S_out=S_out, outlier_idx=outlier_idx, bits=cache.bits, norms=cache.norms,
+                codes=cache.codes, meta=cache.meta, out=out, scores_dbg=scores_dbg, workspace=workspace)
+    Hkv = cache.bits.shape[1]
+    m = S_in.shape[0]
+    m_out = 0 if S_out is None else S_out.shape[0]
+    n_out = 0 if outlier_idx is None or outlier_idx.numel() == 0 else outlier_idx.shape[1]
+    if workspace is None:
+        import torch
+        workspace = torch.empty(max(1, decode_workspace_size(B, Hq, Hkv, N, m, m_out, nsplit, d)),
+                                dtype=torch.uint8, device=Q.device)
+    _check(lib.qjl_decode_step(_ptr(Q), _ptr(K_new), _ptr(V_new), _dtype_code(Q), B, Hq, Hkv, d, N,
+                               K_new.stride(0), K_new.stride(2), V_new.stride(0), V_new.stride(2),
+                               _ptr(S_in), m, _ptr(S_out) if m_out else 0, m_out,
+                               _ptr(outlier_idx) if n_out else 0, n_out, _ptr(cache.bits), _ptr(cache.norms),
+                               _ptr(cache.codes), _ptr(cache.meta), cache.Ncap, cache.nbits, sm_scale, _ptr(out),
+                               _ptr(scores_dbg), nsplit, _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream)), "qjl_decode_step")
 
 
 def timer_enable(on: bool) -> None:

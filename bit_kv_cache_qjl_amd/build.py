@@ -1,6 +1,7 @@
 """Build libqjl.so in-tree with hipcc for gfx950.
 
-Usage: python -m bit_kv_cache_qjl_amd.build   (or call build()).  Always recompiles.
+Usage: python bit_kv_cache_qjl_amd/build.py   (or call build()).  The package itself is not imported:
+it needs the library this builds.  Always recompiles.
 """
 from __future__ import annotations
 

@@ -69,7 +69,8 @@ hipEvent_t pool_event() {
     return e;
 }
 
-const char* kKernelNames[qjl::TK_COUNT] = {"quantize_keys", "quantize_values", "query_project", "decode", "combine"};
+const char* kKernelNames[qjl::TK_COUNT] = {"quantize_keys", "quantize_values", "query_project", "decode", "combine",
+                                           "append_project"};
 
 }  // namespace
 
@@ -232,20 +233,25 @@ int qjl_quantize_values(const void* V, int vdt, int B, int64_t T, int Hkv, int d
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t qjl_decode_workspace_size(int B, int Hq, int Hkv, int d, int64_t N, int m, int m_out, int nsplit) {
-    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || N < 0 || m <= 0 || m_out < 0 || d <= 0) return 0;
-    const int g = Hq / Hkv;
-    const int ns = nsplit > 0 ? nsplit : qjl::decode_pick_nsplit(B, Hkv, g, N, m, m_out);
-    return align256((size_t)B * Hq * (m + m_out) * sizeof(float)) + align256((size_t)B * Hq * 4 * sizeof(float)) +
-           align256((size_t)B * Hq * ns * (d + 2) * sizeof(float));
+namespace {
+
+// workspace regions: query operands, per-head constants, chunk partials
+struct WsLayout {
+    size_t sq, qconst, part, total;
+};
+WsLayout ws_layout(int B, int Hq, int d, int m, int m_out, int ns) {
+    WsLayout w;
+    w.sq = 0;
+    w.qconst = w.sq + align256((size_t)B * Hq * (m + m_out) * sizeof(float));
+    w.part = w.qconst + align256((size_t)B * Hq * 4 * sizeof(float));
+    w.total = w.part + align256((size_t)B * Hq * ns * (d + 2) * sizeof(float));
+    return w;
 }
 
-int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, int64_t N, const void* S_in, int m,
-                         const void* S_out, int m_out, const int32_t* outlier_idx, int n_out, const uint32_t* bits,
-                         const uint16_t* norms, int64_t Ncap, int vmode, const uint32_t* codes, const uint16_t* meta,
-                         const float* V_f32, int nbits, float sm_scale, float* out, float* scores_dbg, int nsplit,
-                         void* workspace, size_t ws_bytes, hipStream_t stream) {
-    g_last_error.clear();
+// Checks shared by the decode entry points (everything but the value arguments and the pointers),
+// then the launch descriptor.
+int prepare_decode(qjl::DecodeArgs& a, int qdt, int B, int Hq, int Hkv, int d, int64_t N, int m, int m_out, int n_out,
+                   int64_t Ncap, int vmode, int nbits, float sm_scale, int nsplit, void* workspace, size_t ws_bytes) {
     if (qdt != QJL_BF16 && qdt != QJL_F32) return fail(QJL_ERR_INVALID_ARG, "qdt=%d is not a qjl_dtype", qdt);
     if (vmode != QJL_V_CODES && vmode != QJL_V_F32) return fail(QJL_ERR_INVALID_ARG, "vmode=%d is not a qjl_vmode", vmode);
     if (B < 0 || Hq <= 0 || Hkv <= 0 || N < 0 || Ncap < 0)
@@ -259,36 +265,17 @@ int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, 
     if (!qjl::decode_shape_supported(m, m_out))
         return fail(QJL_ERR_UNSUPPORTED, "decode supports m in {128, 256, 512} with m_out in {0, m}; got m=%d m_out=%d", m, m_out);
     if (vmode == QJL_V_CODES && nbits != 2) return fail(QJL_ERR_UNSUPPORTED, "decode of %d-bit value codes unsupported (2)", nbits);
-    if (B == 0) return QJL_OK;
-    if (!Q || !S_in || !bits || !norms || !out || (m_out && !S_out) || (n_out && !outlier_idx) ||
-        (vmode == QJL_V_CODES && (!codes || !meta)) || (vmode == QJL_V_F32 && !V_f32))
-        return fail(QJL_ERR_INVALID_ARG, "null device pointer");
-    if (!aligned16(Q) || !aligned16(S_in) || (m_out && !aligned16(S_out)) || !aligned16(bits) || !aligned16(norms) ||
-        !aligned16(out) || (scores_dbg && !aligned16(scores_dbg)) || !aligned16(workspace) ||
-        (vmode == QJL_V_CODES && (!aligned16(codes) || !aligned16(meta))) || (vmode == QJL_V_F32 && !aligned16(V_f32)))
-        return fail(QJL_ERR_MISALIGNED, "device pointers must be 16-byte aligned");
-    const int g = Hq / Hkv;
     if (nsplit > qjl::kMaxSplits) return fail(QJL_ERR_UNSUPPORTED, "nsplit=%d exceeds %d", nsplit, qjl::kMaxSplits);
+    const int g = Hq / Hkv;
     const int ns = nsplit > 0 ? nsplit : qjl::decode_pick_nsplit(B, Hkv, g, N, m, m_out);
-    const size_t need = qjl_decode_workspace_size(B, Hq, Hkv, d, N, m, m_out, ns);
-    if (!workspace || ws_bytes < need)
-        return fail(QJL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);
-    qjl::DecodeArgs a{};
-    a.Q = Q;
-    a.S_in = S_in;
-    a.S_out = S_out;
-    a.oidx = outlier_idx;
-    a.bits = bits;
-    a.norms = norms;
-    a.codes = codes;
-    a.meta = meta;
-    a.V_f32 = V_f32;
-    a.out = out;
-    a.scores_dbg = scores_dbg;
-    a.sq = static_cast<float*>(workspace);
-    const size_t sq_bytes = align256((size_t)B * Hq * (m + m_out) * sizeof(float));
-    a.qconst = reinterpret_cast<float*>(static_cast<char*>(workspace) + sq_bytes);
-    a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + sq_bytes + align256((size_t)B * Hq * 4 * sizeof(float)));
+    const WsLayout w = ws_layout(B, Hq, d, m, m_out, ns);
+    a.ws_need = w.total;
+    if (workspace) {
+        char* base = static_cast<char*>(workspace);
+        a.sq = reinterpret_cast<float*>(base + w.sq);
+        a.qconst = reinterpret_cast<float*>(base + w.qconst);
+        a.part = reinterpret_cast<float*>(base + w.part);
+    }
     a.N = N;
     a.Ncap = Ncap;
     a.B = B;
@@ -302,7 +289,116 @@ int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, 
     a.chunk = qjl::decode_chunk(N, ns);
     const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)d);
     a.z_scale = scale * qjl::kLog2e;
+    return QJL_OK;
+}
+
+// after the other pointer checks: the workspace the launch descriptor points into
+int check_workspace(const qjl::DecodeArgs& a, const void* workspace, size_t ws_bytes) {
+    if (!workspace || ws_bytes < a.ws_need)
+        return fail(QJL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", a.ws_need, workspace ? ws_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(QJL_ERR_MISALIGNED, "device pointers must be 16-byte aligned");
+    return QJL_OK;
+}
+
+}  // namespace
+
+size_t qjl_decode_workspace_size(int B, int Hq, int Hkv, int d, int64_t N, int m, int m_out, int nsplit) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || N < 0 || m <= 0 || m_out < 0 || d <= 0) return 0;
+    const int ns = nsplit > 0 ? nsplit : qjl::decode_pick_nsplit(B, Hkv, Hq / Hkv, N, m, m_out);
+    return ws_layout(B, Hq, d, m, m_out, ns).total;
+}
+
+int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, int64_t N, const void* S_in, int m,
+                         const void* S_out, int m_out, const int32_t* outlier_idx, int n_out, const uint32_t* bits,
+                         const uint16_t* norms, int64_t Ncap, int vmode, const uint32_t* codes, const uint16_t* meta,
+                         const float* V_f32, int nbits, float sm_scale, float* out, float* scores_dbg, int nsplit,
+                         void* workspace, size_t ws_bytes, hipStream_t stream) {
+    g_last_error.clear();
+    qjl::DecodeArgs a{};
+    int st = prepare_decode(a, qdt, B, Hq, Hkv, d, N, m, m_out, n_out, Ncap, vmode, nbits, sm_scale, nsplit, workspace,
+                            ws_bytes);
+    if (st) return st;
+    if (B == 0) return QJL_OK;
+    if (!Q || !S_in || !bits || !norms || !out || (m_out && !S_out) || (n_out && !outlier_idx) ||
+        (vmode == QJL_V_CODES && (!codes || !meta)) || (vmode == QJL_V_F32 && !V_f32))
+        return fail(QJL_ERR_INVALID_ARG, "null device pointer");
+    if (!aligned16(Q) || !aligned16(S_in) || (m_out && !aligned16(S_out)) || !aligned16(bits) || !aligned16(norms) ||
+        !aligned16(out) || (scores_dbg && !aligned16(scores_dbg)) ||
+        (vmode == QJL_V_CODES && (!aligned16(codes) || !aligned16(meta))) || (vmode == QJL_V_F32 && !aligned16(V_f32)))
+        return fail(QJL_ERR_MISALIGNED, "device pointers must be 16-byte aligned");
+    st = check_workspace(a, workspace, ws_bytes);
+    if (st) return st;
+    a.Q = Q;
+    a.S_in = S_in;
+    a.S_out = S_out;
+    a.oidx = outlier_idx;
+    a.bits = bits;
+    a.norms = norms;
+    a.codes = codes;
+    a.meta = meta;
+    a.V_f32 = V_f32;
+    a.out = out;
+    a.scores_dbg = scores_dbg;
     return hip_status(qjl::launch_decode(a, qdt, vmode, stream), "qjl_decode_attention launch");
+}
+
+int qjl_decode_step(const void* Q, const void* K_new, const void* V_new, int dt, int B, int Hq, int Hkv, int d, int64_t N,
+                    int64_t sK_b, int64_t sK_h, int64_t sV_b, int64_t sV_h, const void* S_in, int m, const void* S_out,
+                    int m_out, const int32_t* outlier_idx, int n_out, uint32_t* bits, uint16_t* norms, uint32_t* codes,
+                    uint16_t* meta, int64_t Ncap, int nbits, float sm_scale, float* out, float* scores_dbg, int nsplit,
+                    void* workspace, size_t ws_bytes, hipStream_t stream) {
+    g_last_error.clear();
+    if (N < 1) return fail(QJL_ERR_INVALID_ARG, "N=%lld: a decode step appends one token, so N >= 1", (long long)N);
+    qjl::DecodeArgs a{};
+    int st = prepare_decode(a, dt, B, Hq, Hkv, d, N, m, m_out, n_out, Ncap, QJL_V_CODES, nbits, sm_scale, nsplit, workspace,
+                            ws_bytes);
+    if (st) return st;
+    if (B == 0) return QJL_OK;
+    if (!Q || !K_new || !V_new || !S_in || !bits || !norms || !codes || !meta || !out || (m_out && !S_out) ||
+        (n_out && !outlier_idx))
+        return fail(QJL_ERR_INVALID_ARG, "null device pointer");
+    if (sK_b < 0 || sK_h < 0 || sV_b < 0 || sV_h < 0) return fail(QJL_ERR_INVALID_ARG, "negative stride");
+    const int64_t vec = dt == QJL_BF16 ? 8 : 4;
+    if (!aligned16(Q) || !aligned16(K_new) || !aligned16(V_new) || !aligned16(S_in) || (m_out && !aligned16(S_out)) ||
+        !aligned16(bits) || !aligned16(norms) || !aligned16(codes) || !aligned16(meta) || !aligned16(out) ||
+        (scores_dbg && !aligned16(scores_dbg)) || sK_b % vec || sK_h % vec || sV_b % vec || sV_h % vec)
+        return fail(QJL_ERR_MISALIGNED, "pointers must be 16-byte aligned and strides multiples of %lld elements", (long long)vec);
+    st = check_workspace(a, workspace, ws_bytes);
+    if (st) return st;
+    if (dt == QJL_BF16 && qjl::decode_uses_mfma(m, m_out, QJL_V_CODES, nbits)) {
+        a.Q = Q;
+        a.S_in = S_in;
+        a.S_out = S_out;
+        a.oidx = outlier_idx;
+        a.bits = bits;
+        a.norms = norms;
+        a.codes = codes;
+        a.meta = meta;
+        a.out = out;
+        a.scores_dbg = scores_dbg;
+        qjl::AppendArgs ap{};
+        ap.K = static_cast<const uint16_t*>(K_new);
+        ap.sKb = sK_b;
+        ap.sKh = sK_h;
+        ap.V = static_cast<const uint16_t*>(V_new);
+        ap.sVb = sV_b;
+        ap.sVh = sV_h;
+        ap.bits = bits;
+        ap.norms = norms;
+        ap.codes = codes;
+        ap.meta = meta;
+        ap.pos = N - 1;
+        return hip_status(qjl::launch_decode_step_mfma(a, ap, stream), "qjl_decode_step launch");
+    }
+    // other shapes and fp32: the three operations one after the other (arguments checked above)
+    st = qjl_quantize_keys(K_new, dt, B, 1, Hkv, d, sK_b, 0, sK_h, S_in, m, S_out, m_out, outlier_idx, n_out, bits, norms,
+                           Ncap, N - 1, stream);
+    if (st) return st;
+    st = qjl_quantize_values(V_new, dt, B, 1, Hkv, d, sV_b, 0, sV_h, nbits, codes, meta, Ncap, N - 1, stream);
+    if (st) return st;
+    return qjl_decode_attention(Q, dt, B, Hq, Hkv, d, N, S_in, m, S_out, m_out, outlier_idx, n_out, bits, norms, Ncap,
+                                QJL_V_CODES, codes, meta, nullptr, nbits, sm_scale, out, scores_dbg, nsplit, workspace,
+                                ws_bytes, stream);
 }
 
 }  // extern "C"

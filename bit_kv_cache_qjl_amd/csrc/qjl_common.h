@@ -62,6 +62,69 @@ __device__ __forceinline__ float wave64_max(float v) {
     return v;
 }
 
+// ---- per-token arithmetic of small appends, shared by the quantize kernels and the decode-step
+//      append so that every path writes the same norms, codes and meta
+
+// Eight bf16 channels c0 .. c0 + 7 of a key (kv), split into the inlier part (outlier channels
+// zeroed) and the outlier part (the other channels zeroed), and the squares of each part added in
+// channel order.  Bit i of om flags channel c0 + i as an outlier channel.
+__device__ __forceinline__ void split_key8(uint4 kv, uint32_t om, uint4& kin, uint4& kout, float& ss_in, float& ss_out) {
+    const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+    uint32_t wi[4], wo[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = kw[q] & 0xFFFFu, hi = kw[q] >> 16;
+        const float flo = __uint_as_float(lo << 16), fhi = __uint_as_float(hi << 16);
+        const bool olo = (om >> (2 * q)) & 1u, ohi = (om >> (2 * q + 1)) & 1u;
+        if (olo) ss_out = fmaf(flo, flo, ss_out); else ss_in = fmaf(flo, flo, ss_in);
+        if (ohi) ss_out = fmaf(fhi, fhi, ss_out); else ss_in = fmaf(fhi, fhi, ss_in);
+        wi[q] = (olo ? 0u : lo) | ((ohi ? 0u : hi) << 16);
+        wo[q] = (olo ? lo : 0u) | ((ohi ? hi : 0u) << 16);
+    }
+    kin = make_uint4(wi[0], wi[1], wi[2], wi[3]);
+    kout = make_uint4(wo[0], wo[1], wo[2], wo[3]);
+}
+
+// (|k_in|, |k_out|) as IEEE binary16 (round to nearest even) in one word, from the sums of squares
+__device__ __forceinline__ uint32_t norm_pair(float ss_in, float ss_out) {
+    const _Float16 ni = (_Float16)sqrtf(ss_in);
+    const _Float16 no = (_Float16)sqrtf(ss_out);
+    return (uint32_t)__builtin_bit_cast(uint16_t, ni) | ((uint32_t)__builtin_bit_cast(uint16_t, no) << 16);
+}
+
+// Token-wise quantization of one value vector held by a row of 16 lanes, 8 channels per lane (v):
+// min and max over the row, step = fp16((max - min) / L), mn16 = fp16(min), and the codes
+// clamp(rint((v - mn16) / step), 0, L) of the lane's channels (all 0 when step is 0).  IEEE fp32
+// operations with no contraction.  Returns the meta word (mn16 | step16 << 16).
+template <int NBITS>
+__device__ __forceinline__ uint32_t value_codes16(const float (&v)[8], uint32_t (&code)[8]) {
+#pragma clang fp contract(off)
+    float mn = v[0], mx = v[0];
+#pragma unroll
+    for (int q = 1; q < 8; ++q) {
+        mn = fminf(mn, v[q]);
+        mx = fmaxf(mx, v[q]);
+    }
+    mn = row16_min(mn);   // min and max are exact in any order
+    mx = row16_max(mx);
+    constexpr int L = (1 << NBITS) - 1;
+    const float stepf = (mx - mn) / (float)L;
+    const _Float16 step16 = (_Float16)stepf;
+    const _Float16 mn16 = (_Float16)mn;
+    const float step = (float)step16;
+    const float base = (float)mn16;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        uint32_t c = 0;
+        if (step != 0.f) {
+            const float r = rintf((v[q] - base) / step);
+            c = (uint32_t)fminf(fmaxf(r, 0.f), (float)L);
+        }
+        code[q] = c;
+    }
+    return (uint32_t)__builtin_bit_cast(uint16_t, mn16) | ((uint32_t)__builtin_bit_cast(uint16_t, step16) << 16);
+}
+
 // Launch descriptors filled by the host layer (qjl_api.hip) and consumed by the kernels.
 struct KeyQuantArgs {
     const void* K;
@@ -130,18 +193,37 @@ struct DecodeArgs {
     int B, Hq, Hkv, g, m, m_out, n_out, nsplit;
     int64_t chunk;                    // tokens per split (multiple of the tile)
     float z_scale;                    // sm_scale * log2(e)
+    size_t ws_need;                   // workspace bytes these sizes need (host-side check)
+};
+
+// The new token of a decode step (one per sequence, bf16, model layout) and the cache it goes to.
+struct AppendArgs {
+    const uint16_t* K;
+    int64_t sKb, sKh;                 // element strides of the new keys
+    const uint16_t* V;
+    int64_t sVb, sVh;                 // element strides of the new values
+    uint32_t* bits;
+    uint16_t* norms;
+    uint32_t* codes;                  // 2-bit code tiles
+    uint16_t* meta;
+    int64_t pos;                      // cache position of the new token (N - 1)
 };
 
 // Kernel ids of the launch timer.
-enum TimedKernel { TK_QUANT_KEYS = 0, TK_QUANT_VALUES, TK_QPROJ, TK_DECODE, TK_COMBINE, TK_COUNT };
+enum TimedKernel { TK_QUANT_KEYS = 0, TK_QUANT_VALUES, TK_QPROJ, TK_DECODE, TK_COMBINE, TK_STEP, TK_COUNT };
 
 // Host-side launchers (defined next to their kernels). They return hipSuccess or the launch error.
 hipError_t launch_quantize_keys_bf16(const KeyQuantArgs& a, int B, hipStream_t s);
 hipError_t launch_quantize_keys_f32(const KeyQuantArgs& a, int B, hipStream_t s);
 hipError_t launch_quantize_values(const ValueQuantArgs& a, int vdt, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int qdt, int vmode, hipStream_t s);
-// query operand + matrix-core decode kernel (partials only; launch_decode adds the merge)
+// query operand + matrix-core decode kernel + split merge
 hipError_t launch_decode_mfma(const DecodeArgs& a, int qdt, hipStream_t s);
+// decode step on the matrix-core path: append of the new token + query operand in one launch, then
+// the decode kernel and the split merge
+hipError_t launch_decode_step_mfma(const DecodeArgs& a, const AppendArgs& ap, hipStream_t s);
+// log-sum-exp merge of the chunk partials into out
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
 
 // Decode geometry shared by the workspace-size query and the launcher.
 constexpr int kDecodeTile = 512;     // tokens per tile = threads per decode block

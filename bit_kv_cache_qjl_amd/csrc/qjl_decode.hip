@@ -415,14 +415,14 @@ hipError_t launch_decode_v(const DecodeArgs& a, int vmode, hipStream_t s) {
     return vmode == 0 ? launch_decode_t<WIN, WOUT, 0>(a, s) : launch_decode_t<WIN, WOUT, 1>(a, s);
 }
 
+}  // namespace
+
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
     timer_begin(TK_COMBINE, s);
     hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.Hq), dim3(256), 0, s, a);
     timer_end(TK_COMBINE, s);
     return hipGetLastError();
 }
-
-}  // namespace
 
 bool decode_uses_mfma(int m, int m_out, int vmode, int nbits) {
     const int win = m >> 5, wout = m_out >> 5;
@@ -437,6 +437,7 @@ int decode_pick_nsplit(int B, int Hkv, int g, int64_t N, int m, int m_out) {
     // path, per (sequence, query head, chunk) on the table path; both aim at ~1024 workgroups
     const int hpg = 4 * decode_mfma_rowgroups(g);
     const int64_t units = (int64_t)B * Hkv * ((g + hpg - 1) / hpg);
+    if (units <= 0) return 1;                          // empty batch: nothing is launched
     const int64_t target = 1024;                       // ~4 workgroups per CU on 256 CUs
     int64_t ns = (target + units - 1) / units;
     const int64_t max_ns = (N + kDecodeTile - 1) / kDecodeTile;
@@ -452,11 +453,7 @@ int64_t decode_chunk(int64_t N, int nsplit) {
 
 hipError_t launch_decode(const DecodeArgs& a, int qdt, int vmode, hipStream_t s) {
     const int win = a.m >> 5, wout = a.m_out >> 5;
-    if (decode_uses_mfma(a.m, a.m_out, vmode, 2)) {
-        const hipError_t e = launch_decode_mfma(a, qdt, s);
-        if (e != hipSuccess) return e;
-        return launch_combine(a, s);
-    }
+    if (decode_uses_mfma(a.m, a.m_out, vmode, 2)) return launch_decode_mfma(a, qdt, s);
     timer_begin(TK_QPROJ, s);
     if (qdt == 0) hipLaunchKernelGGL(qproj_kernel<uint16_t>, dim3(a.B * a.Hq), dim3(256), 0, s, a);
     else hipLaunchKernelGGL(qproj_kernel<float>, dim3(a.B * a.Hq), dim3(256), 0, s, a);

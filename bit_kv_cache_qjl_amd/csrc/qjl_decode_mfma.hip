@@ -65,72 +65,35 @@ __device__ __forceinline__ v8i_t sign_planes(uint32_t x, uint32_t m8, uint32_t o
 }
 
 // ---------------------------------------------------------------------------- query operand
-// One workgroup per (sequence, query head): S q as in the byte-table path, then the A-operand bytes
-// in the order the decode kernel loads them, [K block kb][piece][lane group ga][32 bytes]: byte ea of
-// lane group ga is K index k = 16 ga + ea % 16 + 64 (ea / 16) of the instruction, and K index k pairs
-// with bit 4n + i (n = (k % 32) % 8, i = (k % 32) / 8) of the sign word that B lane group k / 32
-// supplies.  Also the per-head constants [-sum x_in / 2, -sum x_out / 2 (both over the positions
-// outside plane 3), e_in, e_out].
-template <typename QT>
-__global__ __launch_bounds__(256) void qproj_mfma_kernel(DecodeArgs a, int win4, int wout4) {
-    __shared__ float qin[kD];
-    __shared__ float qo[kMaxOutliers];
-    __shared__ int so[kMaxOutliers];
-    __shared__ float xs[kMaxBits];
-    __shared__ float red[4][4];
-    const int tid = threadIdx.x;
-    const int bh = blockIdx.x;
-    const int hq = bh % a.Hq;
-    const int h = hq / a.g;
-    const QT* Q = static_cast<const QT*>(a.Q);
-    if (tid < a.n_out) so[tid] = a.oidx[h * a.n_out + tid] & (kD - 1);   // never index outside a row
-    if (tid < kD) qin[tid] = load_elem<QT>(Q, (size_t)bh * kD + tid);
-    __syncthreads();
-    if (tid < a.n_out) qo[tid] = qin[so[tid]];
-    __syncthreads();
-    if (tid < a.n_out) qin[so[tid]] = 0.f;
-    __syncthreads();
-    const QT* Sin = static_cast<const QT*>(a.S_in);
-    const QT* Sout = static_cast<const QT*>(a.S_out);
+// The matrix-core operand of one query head, built by one wave from the head's projections
+// x_j = 2 z_scale sqrt(pi/2)/m (S q)_j (inlier j < m, then outlier, natural order, in LDS): the
+// A-operand bytes in the order the decode kernel loads them, [K block kb][piece][lane group ga][32
+// bytes] (byte ea of lane group ga is K index k = 16 ga + ea % 16 + 64 (ea / 16) of the instruction,
+// and K index k pairs with bit 4n + i, n = (k % 32) % 8, i = (k % 32) / 8, of the sign word that B
+// lane group k / 32 supplies), and the per-head constants [-sum x_in / 2, -sum x_out / 2 (both over
+// the positions outside plane 3), e_in, e_out].
+__device__ void query_operand_wave(const float* xs, int m, int m_out, int win4, int wout4, uint32_t* dst, float* qc,
+                                   int lane) {
     // |x| divided by its plane's bit coefficient (0.5, 1, 2, -1 for position % 4 = 0, 1, 2, 3)
     auto plane_abs = [](float x, int pos) {
         const int i = pos & 3;
         return fabsf(x) * (i == 0 ? 2.f : (i == 2 ? 0.5f : 1.f));
     };
-    const float c_in = 2.f * a.z_scale * kSqrtHalfPi / (float)a.m;
     float sum_in = 0.f, sum_out = 0.f, mx_in = 0.f, mx_out = 0.f;
-    for (int j = tid; j < a.m; j += 256) {
-        const float x = row_dot(Sin + (size_t)j * kD, qin) * c_in;
-        xs[j] = x;
-        if ((j & 3) != 3) sum_in += x;          // plane-3 positions carry their own -x/2
+    for (int j = lane; j < m; j += 64) {
+        const float x = xs[j];
+        if ((j & 3) != 3) sum_in += x;           // plane-3 positions carry their own -x/2
         mx_in = fmaxf(mx_in, plane_abs(x, j));
     }
-    if (a.m_out) {
-        const float c_out = 2.f * a.z_scale * kSqrtHalfPi / (float)a.m_out;
-        for (int j = tid; j < a.m_out; j += 256) {
-            float acc = 0.f;
-            for (int i = 0; i < a.n_out; ++i) acc = fmaf(load_elem<QT>(Sout, (size_t)j * kD + so[i]), qo[i], acc);
-            const float x = acc * c_out;
-            xs[a.m + j] = x;
-            if (((a.m + j) & 3) != 3) sum_out += x;
-            mx_out = fmaxf(mx_out, plane_abs(x, a.m + j));
-        }
+    for (int j = lane; j < m_out; j += 64) {   // m is a multiple of 4: position m + j is in plane j % 4
+        const float x = xs[m + j];
+        if ((j & 3) != 3) sum_out += x;
+        mx_out = fmaxf(mx_out, plane_abs(x, j));
     }
     sum_in = wave64_sum(sum_in);
     sum_out = wave64_sum(sum_out);
     mx_in = wave64_max(mx_in);
     mx_out = wave64_max(mx_out);
-    if ((tid & 63) == 0) {
-        red[0][tid >> 6] = sum_in;
-        red[1][tid >> 6] = sum_out;
-        red[2][tid >> 6] = mx_in;
-        red[3][tid >> 6] = mx_out;
-    }
-    __syncthreads();
-    const float tot_in = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
-    const float tot_out = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
-    const float max_in = fmaxf(fmaxf(red[2][0], red[2][1]), fmaxf(red[2][2], red[2][3]));
-    const float max_out = fmaxf(fmaxf(red[3][0], red[3][1]), fmaxf(red[3][2], red[3][3]));
     // the power of two that takes the largest operand value into [128, 256), kept within the E8M0
     // range of the row scales 127 - e - 4 piece
     auto pick_exp = [](float mx) {
@@ -138,22 +101,20 @@ __global__ __launch_bounds__(256) void qproj_mfma_kernel(DecodeArgs a, int win4,
         const int e = 8 - __builtin_amdgcn_frexp_expf(mx);
         return e > 114 ? 114 : (e < -120 ? -120 : e);
     };
-    const int e_in = pick_exp(max_in), e_out = pick_exp(max_out);
-    if (tid == 0) {
-        float* c = a.qconst + (size_t)bh * 4;
-        c[0] = -0.5f * tot_in;
-        c[1] = -0.5f * tot_out;
-        c[2] = __int_as_float(e_in);
-        c[3] = __int_as_float(e_out);
+    const int e_in = pick_exp(mx_in), e_out = pick_exp(mx_out);
+    if (lane == 0) {
+        qc[0] = -0.5f * sum_in;
+        qc[1] = -0.5f * sum_out;
+        qc[2] = __int_as_float(e_in);
+        qc[3] = __int_as_float(e_out);
     }
-    // operand bytes, one 32-bit word (4 bytes of one (kb, piece, ga)) per thread and step
+    // one task = 4 consecutive bytes e0 .. e0 + 3 of lane group ga in K block kb, all three pieces
+    // (words kb 128 + piece 32 + ga 8 + e0 / 4; the fourth piece's word is zero)
     const int W = 4 * (win4 + wout4);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(a.sq) + (size_t)bh * (32 * W);
-    for (int idx = tid; idx < 32 * W; idx += 256) {
-        const int kb = idx >> 7;                 // 128 words per K block
-        const int piece = (idx >> 5) & 3;
-        const int ga = (idx >> 3) & 3;
-        const int e0 = (idx & 7) * 4;            // first byte of this word
+    for (int task = lane; task < 8 * W; task += 64) {
+        const int kb = task >> 5;
+        const int ga = (task >> 3) & 3;
+        const int e0 = (task & 7) * 4;
         const bool out = kb >= win4;
         const int e = out ? e_out : e_in;
         float y[4];
@@ -165,15 +126,215 @@ __global__ __launch_bounds__(256) void qproj_mfma_kernel(DecodeArgs a, int win4,
             const int plane = eb >> 3, n = eb & 7;
             const int word = out ? 4 * win4 + gb * wout4 + (kb - win4) : gb * win4 + kb;
             // divided by the plane's bit coefficient and scaled by the head's power of two (exact)
-            float v = ldexpf(xs[32 * word + 4 * n + plane], e + (plane == 0 ? 1 : (plane == 2 ? -1 : 0)));
-            if (plane == 3) v = -v;
-            for (int r = 0; r < piece; ++r) {   // v = p0 + p1 / 16 + p2 / 256 + residual
-                const float pr = __builtin_amdgcn_cvt_f32_fp8(__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.f, 0, false), 0);
-                v = (v - pr) * 16.f;
-            }
-            y[q] = piece == 3 ? 0.f : v;
+            const float v = ldexpf(xs[32 * word + 4 * n + plane], e + (plane == 0 ? 1 : (plane == 2 ? -1 : 0)));
+            y[q] = plane == 3 ? -v : v;
         }
-        dst[idx] = fp8x4(y[0], y[1], y[2], y[3]);
+        // y = p0 + p1 / 16 + p2 / 256 + residual
+        const uint32_t k0 = fp8x4(y[0], y[1], y[2], y[3]);
+        next_piece(y, k0);
+        const uint32_t k1 = fp8x4(y[0], y[1], y[2], y[3]);
+        next_piece(y, k1);
+        const uint32_t k2 = fp8x4(y[0], y[1], y[2], y[3]);
+        uint32_t* d = dst + kb * 128 + ga * 8 + (task & 7);
+        d[0] = k0;
+        d[32] = k1;
+        d[64] = k2;
+        d[96] = 0u;
+    }
+}
+
+// fp32 queries and JL matrices: one workgroup per (sequence, query head), S q in fp32 on the VALU in
+// channel order, then the operand (wave 0).
+__global__ __launch_bounds__(256) void qproj_f32_kernel(DecodeArgs a, int win4, int wout4) {
+    __shared__ float qin[kD];
+    __shared__ float qo[kMaxOutliers];
+    __shared__ int so[kMaxOutliers];
+    __shared__ float xs[kMaxBits];
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x;
+    const int hq = bh % a.Hq;
+    const int h = hq / a.g;
+    const float* Q = static_cast<const float*>(a.Q);
+    if (tid < a.n_out) so[tid] = a.oidx[h * a.n_out + tid] & (kD - 1);   // never index outside a row
+    if (tid < kD) qin[tid] = Q[(size_t)bh * kD + tid];
+    __syncthreads();
+    if (tid < a.n_out) qo[tid] = qin[so[tid]];
+    __syncthreads();
+    if (tid < a.n_out) qin[so[tid]] = 0.f;
+    __syncthreads();
+    const float* Sin = static_cast<const float*>(a.S_in);
+    const float* Sout = static_cast<const float*>(a.S_out);
+    const float c_in = 2.f * a.z_scale * kSqrtHalfPi / (float)a.m;
+    for (int j = tid; j < a.m; j += 256) xs[j] = row_dot(Sin + (size_t)j * kD, qin) * c_in;
+    if (a.m_out) {
+        const float c_out = 2.f * a.z_scale * kSqrtHalfPi / (float)a.m_out;
+        for (int j = tid; j < a.m_out; j += 256) {
+            float acc = 0.f;
+            for (int i = 0; i < a.n_out; ++i) acc = fmaf(Sout[(size_t)j * kD + so[i]], qo[i], acc);
+            xs[a.m + j] = acc * c_out;
+        }
+    }
+    __syncthreads();
+    if (tid < 64)
+        query_operand_wave(xs, a.m, a.m_out, win4, wout4, reinterpret_cast<uint32_t*>(a.sq) + (size_t)bh * (128 * (win4 + wout4)),
+                           a.qconst + (size_t)bh * 4, tid);
+}
+
+// bf16: one workgroup per (sequence, KV head) projects the KV head's g query heads (and, for a decode
+// step, the new key) on the matrix cores: D (16 vectors x 16 projections) = A (vectors x channels,
+// from LDS) . B (S rows, straight from global memory), v_mfma_f32_16x16x32_bf16 (exact bf16 products,
+// fp32 sums).  Vector 0 of the first pass is the new key when APPEND; its signs are the sign bits of
+// the cache row (ballot of the D column), its norms and its value codes are computed as in the
+// quantize kernels.  Wave w owns sign words w WPW .. (w + 1) WPW - 1 (two 16-projection tiles per
+// word), so WPW = W / 4.  The query projections go to LDS, then one wave per head builds the operand.
+constexpr int kVRow = kD + 8;                // LDS row of a staged vector (bf16), 272 B
+constexpr int kMaxMfmaBits = 512;            // m + m_out on the matrix-core path
+constexpr int kXPitch = kMaxMfmaBits + 4;    // LDS row of a head's projections (floats)
+
+template <int WPW, bool APPEND>
+__global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs ap) {
+    __shared__ __attribute__((aligned(16))) uint16_t vin[16 * kVRow];    // vectors, outlier channels zeroed
+    __shared__ __attribute__((aligned(16))) uint16_t vout[16 * kVRow];   // vectors on the outlier channels only
+    __shared__ float xs[16 * kXPitch];
+    __shared__ uint32_t s_mask[4];
+    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nunits = a.B * a.Hkv;
+    if (APPEND && (int)blockIdx.x >= nunits) {
+        // ---- the new values, one (sequence, KV head) per wave in workgroups of their own (their atomic
+        //      round trips overlap the projections): a row of 16 lanes, 8 channels per lane; the 2-bit
+        //      fields are merged into the tile words of position pos with atomic and/or, the rest of the
+        //      tile is kept
+        const int vunit = 4 * ((int)blockIdx.x - nunits) + wave;
+        if (vunit >= nunits) return;
+        const int vb = vunit / a.Hkv, vh = vunit - vb * a.Hkv;
+        uint4 vv = make_uint4(0u, 0u, 0u, 0u);
+        if (lane < 16) vv = *reinterpret_cast<const uint4*>(ap.V + vb * ap.sVb + vh * ap.sVh + 8 * lane);
+        const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            v[2 * q] = __uint_as_float(w[q] << 16);
+            v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+        }
+        uint32_t code[8];
+        const uint32_t mt = value_codes16<2>(v, code);
+        if (lane < 16) {
+            if (lane == 0) reinterpret_cast<uint32_t*>(ap.meta)[(size_t)vunit * a.Ncap + ap.pos] = mt;
+            const int64_t tile = ap.pos / kCodeTile;
+            const int j = (int)(ap.pos % kCodeTile);
+            uint32_t* tw = ap.codes + ((size_t)vunit * code_tiles(a.Ncap) + tile) * (kD * 2) + (j >> 4);
+            const int sh = 2 * (j & 15);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                uint32_t* dst = tw + code_slot(8 * lane + q) * 2;
+                atomicAnd(dst, ~(3u << sh));
+                atomicOr(dst, code[q] << sh);
+            }
+        }
+        return;
+    }
+    const int unit = blockIdx.x;                 // b * Hkv + h
+    const int b = unit / a.Hkv, h = unit - b * a.Hkv;
+    const int Win = a.m >> 5, Wout = a.m_out >> 5, W = Win + Wout;
+    const int win4 = a.m >> 7, wout4 = a.m_out >> 7;
+    const int ncol = a.g + (APPEND ? 1 : 0);
+    const int64_t head0 = (int64_t)b * a.Hq + (int64_t)h * a.g;
+
+    // ---- every global load that does not depend on another is issued first: this wave's S tiles
+    //      (B operands: projection row 16 hf + lane % 16 of word wn, channels 32 s + 8 (lane / 16) ..),
+    //      the outlier channels and the first pass's vectors
+    uint4 sb[WPW][2][4];
+#pragma unroll
+    for (int u = 0; u < WPW; ++u) {
+        const int wn = WPW * wave + u;
+        const uint16_t* S = wn < Win ? static_cast<const uint16_t*>(a.S_in) + (size_t)(32 * wn) * kD
+                                     : static_cast<const uint16_t*>(a.S_out) + (size_t)(32 * (wn - Win)) * kD;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                sb[u][hf][s] = *reinterpret_cast<const uint4*>(S + (size_t)(16 * hf + (lane & 15)) * kD + 32 * s + 8 * (lane >> 4));
+    }
+    bool is_out = false;
+    if (wave < 2)
+        for (int i = 0; i < a.n_out; ++i) is_out |= (a.oidx[h * a.n_out + i] & (kD - 1)) == tid;
+    const int sv = tid >> 4, cg = tid & 15;      // staging: vector sv of a pass, channels 8 cg .. 8 cg + 7
+    auto load_vector = [&](int col) {
+        if (col >= ncol) return make_uint4(0u, 0u, 0u, 0u);
+        if (APPEND && col == 0) return *reinterpret_cast<const uint4*>(ap.K + b * ap.sKb + h * ap.sKh + 8 * cg);
+        return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Q) + (head0 + col - (APPEND ? 1 : 0)) * kD + 8 * cg);
+    };
+    uint4 xv = load_vector(sv);
+    if (wave < 2) {                              // outlier mask of the KV head, 64 channels per wave
+        const uint64_t bm = __builtin_amdgcn_ballot_w64(is_out);
+        if (lane == 0) {
+            s_mask[2 * wave] = (uint32_t)bm;
+            s_mask[2 * wave + 1] = (uint32_t)(bm >> 32);
+        }
+    }
+    __syncthreads();
+
+    const float c_in = 2.f * a.z_scale * kSqrtHalfPi / (float)a.m;
+    const float c_out = a.m_out ? 2.f * a.z_scale * kSqrtHalfPi / (float)a.m_out : 0.f;
+    for (int c0 = 0; c0 < ncol; c0 += 16) {
+        const bool key_pass = APPEND && c0 == 0;
+        // ---- stage 16 vectors, split at the outlier channels
+        {
+            if (c0) xv = load_vector(c0 + sv);
+            const uint32_t om = (s_mask[cg >> 2] >> (8 * (cg & 3))) & 0xFFu;
+            uint4 xi, xo;
+            float ss_in = 0.f, ss_out = 0.f;
+            split_key8(xv, om, xi, xo, ss_in, ss_out);
+            *reinterpret_cast<uint4*>(vin + sv * kVRow + 8 * cg) = xi;
+            *reinterpret_cast<uint4*>(vout + sv * kVRow + 8 * cg) = xo;
+            if (key_pass) {
+                // the key is vector 0: lanes 0..15 of wave 0, one DPP row (the sums of the other rows
+                // belong to query vectors and are not used)
+                ss_in = row16_sum(ss_in);
+                ss_out = row16_sum(ss_out);
+                if (tid == 0) reinterpret_cast<uint32_t*>(ap.norms)[(size_t)unit * a.Ncap + ap.pos] = norm_pair(ss_in, ss_out);
+            }
+        }
+        __syncthreads();
+
+        // ---- projections: sign word wn = WPW wave + u is the pair of 16-projection tiles 2 wn, 2 wn + 1;
+        //      D lane l holds projection 32 wn + 16 hf + l % 16 of vectors 4 (l / 16) + i
+#pragma unroll
+        for (int u = 0; u < WPW; ++u) {
+            const int wn = WPW * wave + u;
+            const bool inl = wn < Win;
+            const uint16_t* vsrc = (inl ? vin : vout) + (lane & 15) * kVRow + 8 * (lane >> 4);
+            uint32_t word = 0;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                v4f_t acc = v4f_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(vsrc + 32 * s)),
+                                                                  __builtin_bit_cast(bf16x8_t, sb[u][hf][s]), acc, 0, 0, 0);
+                if (key_pass) word |= ((uint32_t)__builtin_amdgcn_ballot_w64(acc[0] >= 0.f) & 0xFFFFu) << (16 * hf);
+                const int j = (inl ? 32 * wn : a.m + 32 * (wn - Win)) + 16 * hf + (lane & 15);
+                const float cs = inl ? c_in : c_out;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xs[(4 * (lane >> 4) + i) * kXPitch + j] = acc[i] * cs;
+            }
+            if (key_pass && lane == 0) ap.bits[((size_t)unit * a.Ncap + ap.pos) * W + bits_slot(wn, Win, Wout)] = word;
+        }
+        __syncthreads();
+
+        // ---- operands of this pass's query heads, one wave per head
+        for (int v = wave; v < 16; v += 4) {
+            const int col = c0 + v;
+            if (col >= ncol) break;
+            if (APPEND && col == 0) continue;
+            const int64_t hq = head0 + col - (APPEND ? 1 : 0);
+            query_operand_wave(xs + v * kXPitch, a.m, a.m_out, win4, wout4,
+                               reinterpret_cast<uint32_t*>(a.sq) + hq * (128 * (win4 + wout4)), a.qconst + hq * 4, lane);
+        }
+        __syncthreads();
     }
 }
 
@@ -524,6 +685,7 @@ __global__ __launch_bounds__(kMThreads, R == 1 ? 2 : 1) void decode_mfma_kernel(
             dst[1] = L;
         }
     }
+
 }
 
 template <int WIN4, int WOUT4, int R>
@@ -546,22 +708,53 @@ hipError_t launch_decode_mfma_t(const DecodeArgs& a, hipStream_t s) {
     return decode_mfma_rowgroups(a.g) == 2 ? launch_decode_mfma_r<WIN4, WOUT4, 2>(a, s) : launch_decode_mfma_r<WIN4, WOUT4, 1>(a, s);
 }
 
-}  // namespace
+template <bool APPEND>
+hipError_t launch_prologue(const DecodeArgs& a, const AppendArgs& ap, hipStream_t s) {
+    const int wpw = (a.m + a.m_out) / 128;       // sign words per wave
+    const int nunits = a.B * a.Hkv;              // + workgroups of 4 value appends
+    const dim3 grid((unsigned)(nunits + (APPEND ? (nunits + 3) / 4 : 0)));
+    if (wpw == 1) hipLaunchKernelGGL((prologue_kernel<1, APPEND>), grid, dim3(256), 0, s, a, ap);
+    else if (wpw == 2) hipLaunchKernelGGL((prologue_kernel<2, APPEND>), grid, dim3(256), 0, s, a, ap);
+    else if (wpw == 4) hipLaunchKernelGGL((prologue_kernel<4, APPEND>), grid, dim3(256), 0, s, a, ap);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int qdt, hipStream_t s) {
+hipError_t launch_decode_kernel(const DecodeArgs& a, hipStream_t s) {
     const int win4 = a.m >> 7, wout4 = a.m_out >> 7;
-    timer_begin(TK_QPROJ, s);
-    if (qdt == 0) hipLaunchKernelGGL(qproj_mfma_kernel<uint16_t>, dim3(a.B * a.Hq), dim3(256), 0, s, a, win4, wout4);
-    else hipLaunchKernelGGL(qproj_mfma_kernel<float>, dim3(a.B * a.Hq), dim3(256), 0, s, a, win4, wout4);
-    timer_end(TK_QPROJ, s);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     if (win4 == 1 && wout4 == 0) return launch_decode_mfma_t<1, 0>(a, s);
     if (win4 == 1 && wout4 == 1) return launch_decode_mfma_t<1, 1>(a, s);
     if (win4 == 2 && wout4 == 0) return launch_decode_mfma_t<2, 0>(a, s);
     if (win4 == 2 && wout4 == 2) return launch_decode_mfma_t<2, 2>(a, s);
     if (win4 == 4 && wout4 == 0) return launch_decode_mfma_t<4, 0>(a, s);
     return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int qdt, hipStream_t s) {
+    const int win4 = a.m >> 7, wout4 = a.m_out >> 7;
+    timer_begin(TK_QPROJ, s);
+    if (qdt == 0)
+        (void)launch_prologue<false>(a, AppendArgs{}, s);
+    else
+        hipLaunchKernelGGL(qproj_f32_kernel, dim3(a.B * a.Hq), dim3(256), 0, s, a, win4, wout4);
+    timer_end(TK_QPROJ, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_decode_kernel(a, s);
+    if (e != hipSuccess) return e;
+    return launch_combine(a, s);
+}
+
+hipError_t launch_decode_step_mfma(const DecodeArgs& a, const AppendArgs& ap, hipStream_t s) {
+    timer_begin(TK_STEP, s);
+    hipError_t e = launch_prologue<true>(a, ap, s);
+    timer_end(TK_STEP, s);
+    if (e != hipSuccess) return e;
+    e = launch_decode_kernel(a, s);
+    if (e != hipSuccess) return e;
+    return launch_combine(a, s);
 }
 
 }  // namespace qjl

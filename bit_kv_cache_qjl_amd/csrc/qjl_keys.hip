@@ -59,12 +59,6 @@ __device__ __forceinline__ uint32_t pack_signs(const f32x16& acc, int lane) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ uint32_t norm_pair(float ss_in, float ss_out) {
-    const _Float16 ni = (_Float16)sqrtf(ss_in);
-    const _Float16 no = (_Float16)sqrtf(ss_out);
-    return (uint32_t)__builtin_bit_cast(uint16_t, ni) | ((uint32_t)__builtin_bit_cast(uint16_t, no) << 16);
-}
-
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
@@ -327,21 +321,11 @@ void quantize_keys_rows_kernel(KeyQuantArgs a, int64_t rows) {
         if (cg == 0) s_dst[tt] = ((int64_t)b * a.Hkv + h) * a.Ncap + a.t0 + t;
     }
     {
-        const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
-        uint32_t win[4], wout[4];
+        uint4 kin, kout;
         float ss_in = 0.f, ss_out = 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t lo = kw[q] & 0xFFFFu, hi = kw[q] >> 16;
-            const float flo = bf16_to_f32(lo), fhi = bf16_to_f32(hi);
-            const bool olo = (om >> (2 * q)) & 1u, ohi = (om >> (2 * q + 1)) & 1u;
-            if (olo) ss_out = fmaf(flo, flo, ss_out); else ss_in = fmaf(flo, flo, ss_in);
-            if (ohi) ss_out = fmaf(fhi, fhi, ss_out); else ss_in = fmaf(fhi, fhi, ss_in);
-            win[q] = (olo ? 0u : lo) | ((ohi ? 0u : hi) << 16);
-            wout[q] = (olo ? lo : 0u) | ((ohi ? hi : 0u) << 16);
-        }
-        *reinterpret_cast<uint4*>(kl + tt * kKRow + 8 * cg) = make_uint4(win[0], win[1], win[2], win[3]);
-        *reinterpret_cast<uint4*>(ko + tt * kKRow + 8 * cg) = make_uint4(wout[0], wout[1], wout[2], wout[3]);
+        split_key8(kv, om, kin, kout, ss_in, ss_out);
+        *reinterpret_cast<uint4*>(kl + tt * kKRow + 8 * cg) = kin;
+        *reinterpret_cast<uint4*>(ko + tt * kKRow + 8 * cg) = kout;
         ss_in = row16_sum(ss_in);
         ss_out = row16_sum(ss_out);
         __syncthreads();

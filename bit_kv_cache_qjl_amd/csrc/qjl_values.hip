@@ -60,35 +60,11 @@ __global__ __launch_bounds__(kValThreads) void quantize_values_kernel(ValueQuant
 
     float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (valid) load8<VT>(static_cast<const VT*>(a.V) + b * a.sVb + (pos - a.t0) * a.sVt + h * a.sVh + 8 * sub, v);
-    float mn = v[0], mx = v[0];
+    uint32_t code[8];
+    const uint32_t mt = value_codes16<NBITS>(v, code);
 #pragma unroll
-    for (int q = 1; q < 8; ++q) {
-        mn = fminf(mn, v[q]);
-        mx = fmaxf(mx, v[q]);
-    }
-    mn = row16_min(mn);   // the 16 lanes of a vector are one DPP row; min/max are exact
-    mx = row16_max(mx);
-    constexpr int L = (1 << NBITS) - 1;
-    const float range = mx - mn;
-    const float stepf = range / (float)L;
-    const _Float16 step16 = (_Float16)stepf;
-    const _Float16 mn16 = (_Float16)mn;
-    const float step = (float)step16;
-    const float base = (float)mn16;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        uint32_t code = 0;
-        if (step != 0.f) {
-            const float diff = v[q] - base;
-            const float r = rintf(diff / step);
-            code = (uint32_t)fminf(fmaxf(r, 0.f), (float)L);
-        }
-        cs[(8 * sub + q) * kRowPitch + tk] = (uint8_t)code;
-    }
-    if (valid && sub == 0) {
-        reinterpret_cast<uint32_t*>(a.meta)[bh * a.Ncap + pos] =
-            (uint32_t)__builtin_bit_cast(uint16_t, mn16) | ((uint32_t)__builtin_bit_cast(uint16_t, step16) << 16);
-    }
+    for (int q = 0; q < 8; ++q) cs[(8 * sub + q) * kRowPitch + tk] = (uint8_t)code[q];
+    if (valid && sub == 0) reinterpret_cast<uint32_t*>(a.meta)[bh * a.Ncap + pos] = mt;
     __syncthreads();
 
     if (tid >= kD) return;

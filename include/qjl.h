@@ -169,6 +169,34 @@ int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, 
                          int nbits, float sm_scale, float* out, float* scores_dbg, int nsplit,
                          void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * qjl_decode_step - one step of autoregressive decoding: append the new token of every sequence to
+ * the cache at position N - 1, then decode attention over the first N positions.
+ *
+ * The operations are the ones above, in this order: qjl_quantize_keys and qjl_quantize_values with
+ * T = 1 and t0 = N - 1, then qjl_decode_attention over N tokens (the new token is quantized on the
+ * fly before the step's query attends to it, as the QJL summary describes for generated tokens,
+ * "Approach"; the cache then holds the same bits, norms, codes and meta as after the separate calls).
+ * On the matrix-core path (dt = QJL_BF16, 2-bit values, (m, m_out) in {(128, 0), (128, 128),
+ * (256, 0), (256, 256), (512, 0)}) the appends and the query projections run in one launch before the
+ * decode kernel; otherwise the three operations are enqueued one after the other.
+ *   Q           [B][Hq][d] contiguous, dtype dt.
+ *   K_new       new keys, element (b, h, c) at K_new[b*sK_b + h*sK_h + c] (the model layout of one
+ *               token: [B][1][Hkv][d] with its strides), dtype dt; V_new likewise with (sV_b, sV_h).
+ *   S_in, S_out, outlier_idx, n_out, m, m_out  as for qjl_quantize_keys (S in dtype dt).
+ *   bits, norms, codes, meta  the cache (layout at the top) of capacity Ncap >= N; nbits must be 2.
+ *   N           context length after the append (N >= 1).
+ *   sm_scale, out, scores_dbg, nsplit, workspace  as for qjl_decode_attention (same workspace size).
+ * Every argument is checked before anything is enqueued.
+ */
+int qjl_decode_step(const void* Q, const void* K_new, const void* V_new, int dt, int B, int Hq, int Hkv, int d,
+                    int64_t N, int64_t sK_b, int64_t sK_h, int64_t sV_b, int64_t sV_h,
+                    const void* S_in, int m, const void* S_out, int m_out,
+                    const int32_t* outlier_idx, int n_out,
+                    uint32_t* bits, uint16_t* norms, uint32_t* codes, uint16_t* meta, int64_t Ncap, int nbits,
+                    float sm_scale, float* out, float* scores_dbg, int nsplit,
+                    void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* qjl_status_string(int status);
 
@@ -177,7 +205,8 @@ const char* qjl_last_error(void);
 
 /*
  * Kernel timing for measurement harnesses.  While enabled, every launch of the named kernel
- * ("decode", "quantize_keys", "quantize_values", "query_project", "combine") is bracketed by HIP
+ * ("decode", "quantize_keys", "quantize_values", "query_project", "combine", "append_project": the
+ * append + query-projection launch of qjl_decode_step) is bracketed by HIP
  * events recorded on the launch stream.  qjl_timer_read synchronizes on the recorded events and
  * returns the number of launches timed and their total duration in milliseconds, then clears the
  * record.  Disabled by default; enabling it does not change results.

@@ -141,3 +141,43 @@ def test_timer_api():
     qjl.timer_enable(False)
     with pytest.raises(qjl.QJLError):
         qjl.timer_read("nope")
+
+
+def step_call(ws_bytes=None, **kw):
+    a = dict(Q=FAKE, K_new=FAKE, V_new=FAKE, dt=0, B=2, Hq=8, Hkv=2, d=128, N=1000, sK_b=2 * 128, sK_h=128,
+             sV_b=2 * 128, sV_h=128, S_in=FAKE, m=256, S_out=FAKE, m_out=256, oidx=FAKE, n_out=3, bits=FAKE,
+             norms=FAKE, codes=FAKE, meta=FAKE, Ncap=1024, nbits=2, sm_scale=0.0, out=FAKE, scores=0, nsplit=0,
+             ws=FAKE, ws_bytes=0, stream=0)
+    a.update(kw)
+    if ws_bytes is None:
+        a["ws_bytes"] = qjl.lib.qjl_decode_workspace_size(a["B"], a["Hq"], a["Hkv"], 128, a["N"], a["m"], a["m_out"],
+                                                          a["nsplit"]) - 4
+    else:
+        a["ws_bytes"] = ws_bytes
+    return qjl.lib.qjl_decode_step(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), qjl.QJL_ERR_INVALID_ARG),               # no position for the new token
+    (dict(N=1025), qjl.QJL_ERR_INVALID_ARG),
+    (dict(dt=3), qjl.QJL_ERR_INVALID_ARG),
+    (dict(Hq=9), qjl.QJL_ERR_INVALID_ARG),
+    (dict(nbits=3), qjl.QJL_ERR_UNSUPPORTED),
+    (dict(m=256, m_out=128), qjl.QJL_ERR_UNSUPPORTED),
+    (dict(K_new=0), qjl.QJL_ERR_INVALID_ARG),
+    (dict(codes=0), qjl.QJL_ERR_INVALID_ARG),
+    (dict(sK_h=-128), qjl.QJL_ERR_INVALID_ARG),
+    (dict(sV_h=130), qjl.QJL_ERR_MISALIGNED),
+    (dict(dt=1, sK_b=2 * 128 + 2), qjl.QJL_ERR_MISALIGNED),
+    (dict(meta=MIS), qjl.QJL_ERR_MISALIGNED),
+    (dict(nsplit=5000, ws_bytes=1 << 30), qjl.QJL_ERR_UNSUPPORTED),
+    (dict(), qjl.QJL_ERR_WORKSPACE),                    # 4 bytes short
+    (dict(ws=0), qjl.QJL_ERR_WORKSPACE),
+])
+def test_decode_step_rejects(kw, status):
+    assert step_call(**kw) == status
+    assert qjl.last_error() != ""
+
+
+def test_decode_step_empty_batch_is_noop():
+    assert step_call(B=0, ws=0, ws_bytes=0) == qjl.QJL_OK
