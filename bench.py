@@ -194,6 +194,8 @@ def main() -> int:
     ap.add_argument("--cache-copies", type=int, default=0,
                     help="independent caches the steps rotate through (0: enough that consecutive steps never "
                          f"find their cache in the {MALL_BYTES >> 20} MiB last-level cache)")
+    ap.add_argument("--nsplit", type=int, default=0,
+                    help="context chunks per (sequence, KV head) of the decode (0: the library's choice)")
     ap.add_argument("--separate-calls", action="store_true",
                     help="run the step as three calls (quantize keys, quantize values, decode attention) instead "
                          "of the one decode-step call")
@@ -241,7 +243,8 @@ def main() -> int:
     log(f"bench: {copies} cache cop{'y' if copies == 1 else 'ies'} of {cache_bytes / 1e6:.0f} MB (steps rotate)")
     k_new, v_new = K[:, N - 1:], V[:, N - 1:]
     out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
-    ws = torch.empty(qjl.decode_workspace_size(w.B, w.Hq, w.Hkv, N, w.m, w.m_out), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(qjl.decode_workspace_size(w.B, w.Hq, w.Hkv, N, w.m, w.m_out, args.nsplit), dtype=torch.uint8,
+                     device="cuda")
     if args.calibration_copy:
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -258,9 +261,9 @@ def main() -> int:
             qjl.quantize_keys(k_new, S_in, S_out, od, cache.bits, cache.norms, t0=N - 1)
             qjl.quantize_values(v_new, w.nbits, cache.codes, cache.meta, t0=N - 1)
             qjl.decode_attention(Q, S_in, S_out, od, cache.bits, cache.norms, N, out, codes=cache.codes,
-                                 meta=cache.meta, nbits=w.nbits, workspace=ws)
+                                 meta=cache.meta, nbits=w.nbits, nsplit=args.nsplit, workspace=ws)
         else:
-            qjl.decode_step(Q, k_new, v_new, S_in, S_out, od, cache, N, out, workspace=ws)
+            qjl.decode_step(Q, k_new, v_new, S_in, S_out, od, cache, N, out, nsplit=args.nsplit, workspace=ws)
 
     log(f"bench: warmup {args.warmup}, timed {args.steps}")
     for _ in range(args.warmup):
@@ -345,7 +348,8 @@ def main() -> int:
         "kernel_ms_per_launch": {k: v[1] / max(v[0], 1) for k, v in kernels.items()},
         "step_timing": {"mode": "hip_graph_replay" if (graph_ok and args.graph) else "eager",
                         "ms_per_step_eager": ms_eager, "graph_replay_matches_eager": graph_ok,
-                        "cache_copies": copies, "cache_bytes": cache_bytes},
+                        "cache_copies": copies, "cache_bytes": cache_bytes,
+                        "nsplit": args.nsplit or "library choice"},
     }
     if not args.no_quantize:
         log("bench: prefill quantize stream")

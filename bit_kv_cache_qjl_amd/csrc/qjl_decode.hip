@@ -433,17 +433,25 @@ bool decode_uses_mfma(int m, int m_out, int vmode, int nbits) {
 int decode_pick_nsplit(int B, int Hkv, int g, int64_t N, int m, int m_out) {
     (void)m;
     (void)m_out;
-    // one workgroup per (sequence, KV head, group of 4 or 8 query heads, chunk) on the matrix-core
-    // path, per (sequence, query head, chunk) on the table path; both aim at ~1024 workgroups
+    // Work units: (sequence, KV head, group of 4 or 8 query heads); each context chunk of a unit is
+    // one workgroup.  The chunks stream from HBM at the same rate when every CU holds the same number
+    // of them, so a step lasts about ceil(units ns / 256) chunk lengths of N / ns tokens: pick the ns
+    // that minimizes ceil(units ns / 256) / ns (the smallest such ns, for the fewest partials).
+    constexpr int64_t kCUs = 256;
     const int hpg = 4 * decode_mfma_rowgroups(g);
     const int64_t units = (int64_t)B * Hkv * ((g + hpg - 1) / hpg);
     if (units <= 0) return 1;                          // empty batch: nothing is launched
-    const int64_t target = 1024;                       // ~4 workgroups per CU on 256 CUs
-    int64_t ns = (target + units - 1) / units;
-    const int64_t max_ns = (N + kDecodeTile - 1) / kDecodeTile;
-    if (ns > max_ns) ns = max_ns;
-    if (ns < 1) ns = 1;
-    return (int)ns;
+    int64_t max_ns = (N + kDecodeTile - 1) / kDecodeTile;
+    if (max_ns > 1024) max_ns = 1024;
+    int64_t best = 1, best_rounds = (units + kCUs - 1) / kCUs;
+    for (int64_t ns = 2; ns <= max_ns; ++ns) {
+        const int64_t rounds = (units * ns + kCUs - 1) / kCUs;
+        if (rounds * best < best_rounds * ns) {        // rounds / ns < best_rounds / best
+            best = ns;
+            best_rounds = rounds;
+        }
+    }
+    return (int)best;
 }
 
 int64_t decode_chunk(int64_t N, int nsplit) {
