@@ -677,6 +677,12 @@ __global__ __launch_bounds__(kMThreads, R == 1 ? 2 : 1) void decode_mfma_kernel(
                 o1 = fmaf(sc, red_o[w][oh][c0 + 1] + red_mn[w][oh], o1);
             }
         }
+        if (a.nsplit == 1) {                 // the whole context: the output itself (no merge launch)
+            float* o = a.out + (size_t)(head0 + HPG * hg + oh) * kD;
+            o[c0] = L > 0.f ? o0 / L : 0.f;
+            o[c0 + 1] = L > 0.f ? o1 / L : 0.f;
+            continue;
+        }
         float* dst = a.part + ((size_t)(head0 + HPG * hg + oh) * a.nsplit + split) * (kD + 2);
         dst[2 + c0] = o0;
         dst[3 + c0] = o1;
@@ -743,7 +749,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int qdt, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_decode_kernel(a, s);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || a.nsplit == 1) return e;
     return launch_combine(a, s);
 }
 
@@ -753,7 +759,7 @@ hipError_t launch_decode_step_mfma(const DecodeArgs& a, const AppendArgs& ap, hi
     timer_end(TK_STEP, s);
     if (e != hipSuccess) return e;
     e = launch_decode_kernel(a, s);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || a.nsplit == 1) return e;
     return launch_combine(a, s);
 }
 
