@@ -30,6 +30,14 @@ QJL_V_F32 = 1
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python bit_kv_cache_qjl_amd/build.py`")
 
+# PyTorch ships its own HIP runtime.  Load it before libqjl so that the library's HIP calls bind to
+# the runtime instance that owns the tensors' device memory (loaded the other way round, a process
+# can hold two runtimes and the library's launches find no device).
+try:
+    import torch  # noqa: F401
+except ImportError:  # the C ABI alone (argument checks) still works without torch
+    torch = None
+
 lib = ctypes.CDLL(LIB_PATH)
 
 _i, _i64, _p, _f, _sz = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
