@@ -182,8 +182,11 @@ int qjl_quantize_keys(const void* K, int kdt, int B, int64_t T, int Hkv, int d, 
     a.m_out = m_out;
     a.n_out = n_out;
     a.W = (m + m_out) / 32;
-    // ~2 workgroups per CU over 256 CUs, in whole 64-token chunks
-    int64_t per = ((int64_t)B * Hkv * T + 511) / 512;
+    // one round of workgroups over 256 CUs (one per CU for the kernel that keeps the JL matrices in
+    // LDS, two for the other), in whole 64-token chunks
+    const int64_t slots =
+        kdt == QJL_BF16 && qjl::quantize_keys_lds_shape(m, m_out) && T * sK_t * 2 + 256 < ((int64_t)1 << 31) ? 256 : 512;
+    int64_t per = ((int64_t)B * Hkv * T + slots - 1) / slots;
     per = ((per + 63) / 64) * 64;
     if (per < 64) per = 64;
     if (per > 8192) per = 8192;

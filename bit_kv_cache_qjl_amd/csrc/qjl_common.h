@@ -62,6 +62,12 @@ __device__ __forceinline__ float wave64_max(float v) {
     return v;
 }
 
+// Raw buffer resource over [base, base + bytes): loads at or past the end return zero, which is how
+// the kernels treat ragged ends (no branches, no clamped addresses).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // ---- per-token arithmetic of small appends, shared by the quantize kernels and the decode-step
 //      append so that every path writes the same norms, codes and meta
 
@@ -214,6 +220,11 @@ enum TimedKernel { TK_QUANT_KEYS = 0, TK_QUANT_VALUES, TK_QPROJ, TK_DECODE, TK_C
 
 // Host-side launchers (defined next to their kernels). They return hipSuccess or the launch error.
 hipError_t launch_quantize_keys_bf16(const KeyQuantArgs& a, int B, hipStream_t s);
+// True when bf16 keys of this sketch shape take the kernel that keeps the JL matrices in LDS
+// (m and m_out in {0, 128, 256, 512} with m_out in {0, m}; one workgroup per CU).
+inline bool quantize_keys_lds_shape(int m, int m_out) {
+    return (m == 128 || m == 256 || m == 512) && (m_out == 0 || m_out == m);
+}
 hipError_t launch_quantize_keys_f32(const KeyQuantArgs& a, int B, hipStream_t s);
 hipError_t launch_quantize_values(const ValueQuantArgs& a, int vdt, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int qdt, int vmode, hipStream_t s);

@@ -42,10 +42,4 @@ __device__ __forceinline__ float row_dot(const float* row, const float* q) {
     return acc;
 }
 
-// Raw buffer resource over [base, base + bytes): loads at or past the end return zero, which is how
-// the kernels treat the ragged end of a chunk (no branches, no clamped addresses).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
 }  // namespace qjl

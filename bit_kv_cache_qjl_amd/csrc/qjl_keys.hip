@@ -21,6 +21,13 @@
 //   * words are staged in LDS and written with coalesced stores.
 #include "qjl_common.h"
 
+#ifndef QJL_QK_WAVES
+#define QJL_QK_WAVES 16
+#endif
+#ifndef QJL_QK_PREFETCH
+#define QJL_QK_PREFETCH 0
+#endif
+
 namespace qjl {
 namespace {
 
@@ -262,6 +269,215 @@ void quantize_keys_bf16_kernel(KeyQuantArgs a) {
     }
 }
 
+// Sketches with m <= 512 and m_out <= 512: the JL matrices stay in LDS for the whole workgroup (S_in
+// with its outlier columns zeroed; S_out gathered on the head's outlier channels in rank order, 16
+// per row), loaded once.  Each wave then streams its own 32-token blocks with no further barrier:
+// the keys of a block go from global memory straight into the MFMA B operand (lane l: token l % 32,
+// channels 16 s + 8 (l / 32) .. + 7), the A operands (32 projections x 16 channels) come from LDS,
+// and a lane stores its token's sign words quarter-row group by group (the group's words are
+// consecutive slots of the stored row).  The norms come from the same registers: |k_in|^2 with the
+// outlier channels masked out (S_in has zero columns there, so the projections need no masking),
+// |k_out|^2 from the gathered operand.
+constexpr int kOGRow = 16;                   // gathered S_out row (bf16)
+constexpr int kSRowL = kD;                   // S_in row in LDS (bf16, 256 B, swizzled)
+
+// 16-byte chunk c of row i (i = row within its 32-row tile) is stored at chunk c ^ swz(i): the 32
+// rows a matrix-core A operand reads at one chunk then fall on 16 distinct 4-bank windows, for any
+// 8 or 16 consecutive lanes.
+__device__ __forceinline__ int s_swz(int i) { return (i & 7) | (((i >> 4) & 1) << 3); }
+
+// NW waves per workgroup (one workgroup per CU: NW / 4 per SIMD); PF: the next block's keys are in
+// flight during the current one
+template <int WIN, int WOUT, int NW, bool PF>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)))
+void quantize_keys_lds_kernel(KeyQuantArgs a) {
+    constexpr int kLWaves = NW;
+    constexpr int kLThreads = 64 * NW;
+    constexpr int W = WIN + WOUT;
+    __shared__ __attribute__((aligned(16))) uint16_t sl[WIN * 32 * kSRowL];
+    __shared__ __attribute__((aligned(16))) uint16_t so[(WOUT > 0 ? WOUT : 1) * 32 * kOGRow];
+    __shared__ int s_oidx[kMaxOutliers];
+    __shared__ uint32_t s_keep[2 * 32];          // keep masks of the 32 key words of each lane half
+    __shared__ uint32_t s_goff[2 * 8];           // byte offsets of the gathered channels of each lane half
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int h = blockIdx.y;
+    const int b = blockIdx.z;
+    const int64_t t_begin = (int64_t)blockIdx.x * a.tokens_per_block;
+    const int64_t t_end = min(a.T, t_begin + (int64_t)a.tokens_per_block);
+    const int n_out = a.n_out;
+
+    if (tid < n_out) s_oidx[tid] = a.oidx[h * n_out + tid] & (kD - 1);   // never index outside a row
+    __syncthreads();
+    if (tid < 64) {
+        // word w = 4 s + q of lane half hf holds channels 16 s + 8 hf + 2 q, + 1
+        const int hf = tid >> 5, w = tid & 31;
+        const int c0 = 16 * (w >> 2) + 8 * hf + 2 * (w & 3);
+        uint32_t keep = 0xFFFFFFFFu;
+        for (int k = 0; k < n_out; ++k) {
+            if (s_oidx[k] == c0) keep &= 0xFFFF0000u;
+            if (s_oidx[k] == c0 + 1) keep &= 0x0000FFFFu;
+        }
+        s_keep[tid] = keep;
+    } else if (tid < 80) {
+        // rank r = 8 hf + e of the gathered operand: its channel, or an offset past any buffer (reads 0)
+        const int r = tid - 64;
+        s_goff[r] = r < n_out ? 2u * (uint32_t)s_oidx[r] : 0x7FFFFF00u;
+    }
+    {
+        const uint16_t* Sin = static_cast<const uint16_t*>(a.S_in);
+        for (int i = tid; i < WIN * 32 * 16; i += kLThreads) {
+            const int r = i >> 4, cgi = i & 15;
+            const uint4 v = *reinterpret_cast<const uint4*>(Sin + (size_t)r * kD + 8 * cgi);
+            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            for (int k = 0; k < n_out; ++k) {
+                const int c = s_oidx[k];
+                if ((c >> 3) == cgi) {
+                    const uint32_t m = (c & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (q == ((c & 7) >> 1)) w[q] &= m;
+                }
+            }
+            *reinterpret_cast<uint4*>(sl + r * kSRowL + 8 * (cgi ^ s_swz(r & 31))) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        const uint16_t* Sout = static_cast<const uint16_t*>(a.S_out);
+        for (int i = tid; i < WOUT * 32 * kOGRow; i += kLThreads) {
+            const int j = i / kOGRow, r = i % kOGRow;
+            // the two 8-rank halves of row j swap places when bit 4 of the row is set
+            so[j * kOGRow + (r ^ (((j >> 4) & 1) << 3))] = r < n_out ? Sout[(size_t)j * kD + s_oidx[r]] : (uint16_t)0;
+        }
+    }
+    __syncthreads();
+
+    const int tcol = lane & 31;
+    const int khalf = (lane >> 5) * 8;
+    const int prow = tile_row(lane & 31);
+    // this (sequence, head)'s key rows up to the end of the last valid token: loads of tokens past
+    // t_end (and of the unused gathered ranks) fall outside and return zeros
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(static_cast<const uint16_t*>(a.K) + b * a.sKb + h * a.sKh,
+                                                  (uint32_t)((t_end - 1) * a.sKt * 2 + kD * 2));
+    const int64_t head_row0 = ((int64_t)b * a.Hkv + h) * a.Ncap + a.t0;
+    uint32_t* norms32 = reinterpret_cast<uint32_t*>(a.norms);
+    // A fragment of tile j, K step s: chunk 2 s + khalf / 8 of row prow, at sl + 32 j kSRowL + aoff[s]
+    int aoff[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) aoff[s] = prow * kSRowL + 8 * ((2 * s + (khalf >> 3)) ^ s_swz(prow));
+    // gathered S_out fragment of tile j: orow + 32 j kOGRow
+    const uint16_t* orow = so + prow * kOGRow + 8 * ((khalf >> 3) ^ ((prow >> 4) & 1));
+    const uint32_t* keep = s_keep + (lane >> 5) * 32;
+    const uint32_t* goff = s_goff + (lane >> 5) * 8;
+
+    auto load_keys = [&](int64_t tk, const uint32_t* goffb, uint4 (&bk)[8], uint4& bg) {
+        const uint32_t voff = (uint32_t)(tk * a.sKt * 2);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(rk, voff + 2 * khalf + 32 * s, 0, 0);
+            bk[s] = make_uint4(x[0], x[1], x[2], x[3]);
+        }
+        uint32_t g[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(rk, voff + goffb[2 * q], 0, 0);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(rk, voff + goffb[2 * q + 1], 0, 0);
+            g[q] = lo | (hi << 16);
+        }
+        bg = make_uint4(g[0], g[1], g[2], g[3]);
+    };
+
+    const int64_t nblk = (t_end - t_begin + 31) / 32;
+    uint4 bk[8], bg;
+    if (PF && wave < nblk) load_keys(t_begin + 32 * wave + tcol, goff, bk, bg);
+    for (int64_t blk = wave; blk < nblk; blk += kLWaves) {
+        const int64_t t0b = t_begin + 32 * blk;
+        const int64_t tk = t0b + tcol;
+        // the mask tables are read per block, not held in registers across the loop
+        int opaque = 0;
+        asm volatile("" : "+v"(opaque));
+        const uint32_t* keepb = keep + opaque;
+        const uint32_t* goffb = goff + opaque;
+        uint4 nk[8], ng;
+        if constexpr (PF) {
+            if (blk + kLWaves < nblk) load_keys(tk + 32 * kLWaves, goffb, nk, ng);
+        } else {
+            load_keys(tk, goffb, bk, bg);
+        }
+
+        // norms: |k_in|^2 over this lane's channels outside the outlier set, |k_out|^2 over its gathered ranks
+        float si = 0.f, sg = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint4 m = *reinterpret_cast<const uint4*>(keepb + 4 * q);
+            si = dot2_bf16(bk[q].x & m.x, bk[q].x, si);
+            si = dot2_bf16(bk[q].y & m.y, bk[q].y, si);
+            si = dot2_bf16(bk[q].z & m.z, bk[q].z, si);
+            si = dot2_bf16(bk[q].w & m.w, bk[q].w, si);
+        }
+        sg = dot2_bf16(bg.x, bg.x, sg);
+        sg = dot2_bf16(bg.y, bg.y, sg);
+        sg = dot2_bf16(bg.z, bg.z, sg);
+        sg = dot2_bf16(bg.w, bg.w, sg);
+        si += __uint_as_float(lane_xor32(__float_as_uint(si)));
+        sg += __uint_as_float(lane_xor32(__float_as_uint(sg)));
+        if (lane < 32 && tk < t_end) norms32[head_row0 + tk] = norm_pair(si, sg);
+
+        // projections by quarter-row group g of the stored row (inlier words g WIN/4 .., then outlier
+        // words g WOUT/4 ..: consecutive slots g W/4 ..), two independent MFMA chains at a time
+        constexpr int GI = WIN / 4, GO = WOUT / 4;
+        uint32_t* row = a.bits + (head_row0 + tk) * W;
+#pragma unroll 1
+        for (int g = 0; g < 4; ++g) {
+            uint32_t gw[GI + GO];
+#pragma unroll
+            for (int jj = 0; jj < GI; jj += 2) {
+                const uint16_t* a0p = sl + 32 * (g * GI + jj) * kSRowL;
+                if constexpr (GI == 1) {
+                    f32x16 a0 = {};
+#pragma unroll
+                    for (int s = 0; s < 8; ++s)
+                        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const uint4*>(a0p + aoff[s])),
+                                                                     as_bf16x8(bk[s]), a0, 0, 0, 0);
+                    gw[jj] = pack_signs(a0, lane);
+                } else {
+                    f32x16 a0 = {}, a1 = {};
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) {
+                        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const uint4*>(a0p + aoff[s])),
+                                                                     as_bf16x8(bk[s]), a0, 0, 0, 0);
+                        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            as_bf16x8(*reinterpret_cast<const uint4*>(a0p + 32 * kSRowL + aoff[s])), as_bf16x8(bk[s]), a1, 0, 0, 0);
+                    }
+                    gw[jj] = pack_signs(a0, lane);
+                    gw[jj + 1] = pack_signs(a1, lane);
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < GO; ++jj) {
+                const f32x16 ao = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    as_bf16x8(*reinterpret_cast<const uint4*>(orow + 32 * (g * GO + jj) * kOGRow)), as_bf16x8(bg), f32x16{}, 0, 0, 0);
+                gw[GI + jj] = pack_signs(ao, lane);
+            }
+            if (lane < 32 && tk < t_end) {
+                uint32_t* dst = row + g * (W / 4);
+                if constexpr (GI + GO == 1) dst[0] = gw[0];
+                else if constexpr (GI + GO == 2) *reinterpret_cast<uint2*>(dst) = make_uint2(gw[0], gw[1]);
+                else {
+#pragma unroll
+                    for (int q = 0; q < GI + GO; q += 4)
+                        *reinterpret_cast<uint4*>(dst + q) = make_uint4(gw[q], gw[q + 1], gw[q + 2], gw[q + 3]);
+                }
+            }
+        }
+        if constexpr (PF) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) bk[s] = nk[s];
+            bg = ng;
+        }
+    }
+}
+
 // Small appends (a few new tokens per sequence, e.g. one per decode step): every 32 key rows of any
 // (sequence, KV head, token) form one MFMA chunk.  The outlier sketch is computed with the
 // full-width S_out on the outlier-only key (zeros on the other channels), so the JL operands are
@@ -418,6 +634,9 @@ __global__ __launch_bounds__(256) void quantize_keys_f32_kernel(KeyQuantArgs a) 
 
 }  // namespace
 
+constexpr int kQKWaves = QJL_QK_WAVES;
+constexpr bool kQKPrefetch = QJL_QK_PREFETCH;
+
 hipError_t launch_quantize_keys_bf16(const KeyQuantArgs& a, int B, hipStream_t s) {
     if (a.T <= kSmallAppend) {
         // few tokens per sequence: flattened rows, one JL load per 32 rows of all heads
@@ -432,6 +651,19 @@ hipError_t launch_quantize_keys_bf16(const KeyQuantArgs& a, int B, hipStream_t s
     }
     const int tiles = (a.m >> 5) > (a.m_out >> 5) ? (a.m >> 5) : (a.m_out >> 5);
     dim3 grid((unsigned)((a.T + a.tokens_per_block - 1) / a.tokens_per_block), (unsigned)a.Hkv, (unsigned)B);
+    // the LDS-resident kernel addresses one (sequence, head)'s key rows with 32-bit buffer offsets
+    if (quantize_keys_lds_shape(a.m, a.m_out) && a.T * a.sKt * 2 + 256 < ((int64_t)1 << 31)) {
+        const int wi = a.m >> 5, wo = a.m_out >> 5;
+#define QK_LDS(WI, WO) hipLaunchKernelGGL((quantize_keys_lds_kernel<WI, WO, kQKWaves, kQKPrefetch>), grid, dim3(64 * kQKWaves), 0, s, a)
+        if (wi == 16 && wo == 16) QK_LDS(16, 16);
+        else if (wi == 16 && wo == 0) QK_LDS(16, 0);
+        else if (wi == 8 && wo == 8) QK_LDS(8, 8);
+        else if (wi == 8 && wo == 0) QK_LDS(8, 0);
+        else if (wi == 4 && wo == 4) QK_LDS(4, 4);
+        else QK_LDS(4, 0);
+#undef QK_LDS
+        return hipGetLastError();
+    }
     if (tiles <= 8) hipLaunchKernelGGL(quantize_keys_bf16_kernel<1>, grid, dim3(kThreads), 0, s, a);
     else if (tiles <= 16) hipLaunchKernelGGL(quantize_keys_bf16_kernel<2>, grid, dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL(quantize_keys_bf16_kernel<4>, grid, dim3(kThreads), 0, s, a);
