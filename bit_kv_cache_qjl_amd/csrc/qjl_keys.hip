@@ -21,12 +21,6 @@
 //   * words are staged in LDS and written with coalesced stores.
 #include "qjl_common.h"
 
-#ifndef QJL_QK_WAVES
-#define QJL_QK_WAVES 16
-#endif
-#ifndef QJL_QK_PREFETCH
-#define QJL_QK_PREFETCH 0
-#endif
 
 namespace qjl {
 namespace {
@@ -279,20 +273,19 @@ void quantize_keys_bf16_kernel(KeyQuantArgs a) {
 // outlier channels masked out (S_in has zero columns there, so the projections need no masking),
 // |k_out|^2 from the gathered operand.
 constexpr int kOGRow = 16;                   // gathered S_out row (bf16)
-constexpr int kSRowL = kD;                   // S_in row in LDS (bf16, 256 B, swizzled)
+constexpr int kSRowL = kD + 8;               // S_in row in LDS (bf16, 272 B)
 
-// 16-byte chunk c of row i (i = row within its 32-row tile) is stored at chunk c ^ swz(i): the 32
-// rows a matrix-core A operand reads at one chunk then fall on 16 distinct 4-bank windows, for any
-// 8 or 16 consecutive lanes.
-__device__ __forceinline__ int s_swz(int i) { return (i & 7) | (((i >> 4) & 1) << 3); }
+// Projection row p of a 32-row tile sits at LDS row p ^ 8 (bit 4 of p): with the 272-byte pitch the
+// rows that 8 or 16 consecutive lanes of a matrix-core A operand read (tile_row order) then fall on
+// distinct 4-bank windows, and a fragment's offset within the row is the same for every lane.
+__device__ __forceinline__ int s_lrow(int p) { return p ^ (((p >> 4) & 1) << 3); }
 
-// NW waves per workgroup (one workgroup per CU: NW / 4 per SIMD); PF: the next block's keys are in
-// flight during the current one
-template <int WIN, int WOUT, int NW, bool PF>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4)))
+constexpr int kLWaves = 16;                  // one workgroup per CU: 4 waves per SIMD
+constexpr int kLThreads = 64 * kLWaves;
+
+template <int WIN, int WOUT>
+__global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void quantize_keys_lds_kernel(KeyQuantArgs a) {
-    constexpr int kLWaves = NW;
-    constexpr int kLThreads = 64 * NW;
     constexpr int W = WIN + WOUT;
     __shared__ __attribute__((aligned(16))) uint16_t sl[WIN * 32 * kSRowL];
     __shared__ __attribute__((aligned(16))) uint16_t so[(WOUT > 0 ? WOUT : 1) * 32 * kOGRow];
@@ -341,7 +334,7 @@ void quantize_keys_lds_kernel(KeyQuantArgs a) {
                         if (q == ((c & 7) >> 1)) w[q] &= m;
                 }
             }
-            *reinterpret_cast<uint4*>(sl + r * kSRowL + 8 * (cgi ^ s_swz(r & 31))) = make_uint4(w[0], w[1], w[2], w[3]);
+            *reinterpret_cast<uint4*>(sl + ((r & ~31) | s_lrow(r & 31)) * kSRowL + 8 * cgi) = make_uint4(w[0], w[1], w[2], w[3]);
         }
         const uint16_t* Sout = static_cast<const uint16_t*>(a.S_out);
         for (int i = tid; i < WOUT * 32 * kOGRow; i += kLThreads) {
@@ -361,10 +354,8 @@ void quantize_keys_lds_kernel(KeyQuantArgs a) {
                                                   (uint32_t)((t_end - 1) * a.sKt * 2 + kD * 2));
     const int64_t head_row0 = ((int64_t)b * a.Hkv + h) * a.Ncap + a.t0;
     uint32_t* norms32 = reinterpret_cast<uint32_t*>(a.norms);
-    // A fragment of tile j, K step s: chunk 2 s + khalf / 8 of row prow, at sl + 32 j kSRowL + aoff[s]
-    int aoff[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) aoff[s] = prow * kSRowL + 8 * ((2 * s + (khalf >> 3)) ^ s_swz(prow));
+    // A fragment of tile j, K step s: arow + 32 j kSRowL + 16 s
+    const uint16_t* arow = sl + s_lrow(prow) * kSRowL + khalf;
     // gathered S_out fragment of tile j: orow + 32 j kOGRow
     const uint16_t* orow = so + prow * kOGRow + 8 * ((khalf >> 3) ^ ((prow >> 4) & 1));
     const uint32_t* keep = s_keep + (lane >> 5) * 32;
@@ -388,8 +379,6 @@ void quantize_keys_lds_kernel(KeyQuantArgs a) {
     };
 
     const int64_t nblk = (t_end - t_begin + 31) / 32;
-    uint4 bk[8], bg;
-    if (PF && wave < nblk) load_keys(t_begin + 32 * wave + tcol, goff, bk, bg);
     for (int64_t blk = wave; blk < nblk; blk += kLWaves) {
         const int64_t t0b = t_begin + 32 * blk;
         const int64_t tk = t0b + tcol;
@@ -398,12 +387,8 @@ void quantize_keys_lds_kernel(KeyQuantArgs a) {
         asm volatile("" : "+v"(opaque));
         const uint32_t* keepb = keep + opaque;
         const uint32_t* goffb = goff + opaque;
-        uint4 nk[8], ng;
-        if constexpr (PF) {
-            if (blk + kLWaves < nblk) load_keys(tk + 32 * kLWaves, goffb, nk, ng);
-        } else {
-            load_keys(tk, goffb, bk, bg);
-        }
+        uint4 bk[8], bg;
+        load_keys(tk, goffb, bk, bg);
 
         // norms: |k_in|^2 over this lane's channels outside the outlier set, |k_out|^2 over its gathered ranks
         float si = 0.f, sg = 0.f;
@@ -432,22 +417,22 @@ void quantize_keys_lds_kernel(KeyQuantArgs a) {
             uint32_t gw[GI + GO];
 #pragma unroll
             for (int jj = 0; jj < GI; jj += 2) {
-                const uint16_t* a0p = sl + 32 * (g * GI + jj) * kSRowL;
+                const uint16_t* a0p = arow + 32 * (g * GI + jj) * kSRowL;
                 if constexpr (GI == 1) {
                     f32x16 a0 = {};
 #pragma unroll
                     for (int s = 0; s < 8; ++s)
-                        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const uint4*>(a0p + aoff[s])),
+                        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const uint4*>(a0p + 16 * s)),
                                                                      as_bf16x8(bk[s]), a0, 0, 0, 0);
                     gw[jj] = pack_signs(a0, lane);
                 } else {
                     f32x16 a0 = {}, a1 = {};
 #pragma unroll
                     for (int s = 0; s < 8; ++s) {
-                        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const uint4*>(a0p + aoff[s])),
+                        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const uint4*>(a0p + 16 * s)),
                                                                      as_bf16x8(bk[s]), a0, 0, 0, 0);
                         a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            as_bf16x8(*reinterpret_cast<const uint4*>(a0p + 32 * kSRowL + aoff[s])), as_bf16x8(bk[s]), a1, 0, 0, 0);
+                            as_bf16x8(*reinterpret_cast<const uint4*>(a0p + 32 * kSRowL + 16 * s)), as_bf16x8(bk[s]), a1, 0, 0, 0);
                     }
                     gw[jj] = pack_signs(a0, lane);
                     gw[jj + 1] = pack_signs(a1, lane);
@@ -469,11 +454,6 @@ void quantize_keys_lds_kernel(KeyQuantArgs a) {
                         *reinterpret_cast<uint4*>(dst + q) = make_uint4(gw[q], gw[q + 1], gw[q + 2], gw[q + 3]);
                 }
             }
-        }
-        if constexpr (PF) {
-#pragma unroll
-            for (int s = 0; s < 8; ++s) bk[s] = nk[s];
-            bg = ng;
         }
     }
 }
@@ -634,9 +614,6 @@ __global__ __launch_bounds__(256) void quantize_keys_f32_kernel(KeyQuantArgs a) 
 
 }  // namespace
 
-constexpr int kQKWaves = QJL_QK_WAVES;
-constexpr bool kQKPrefetch = QJL_QK_PREFETCH;
-
 hipError_t launch_quantize_keys_bf16(const KeyQuantArgs& a, int B, hipStream_t s) {
     if (a.T <= kSmallAppend) {
         // few tokens per sequence: flattened rows, one JL load per 32 rows of all heads
@@ -654,7 +631,7 @@ hipError_t launch_quantize_keys_bf16(const KeyQuantArgs& a, int B, hipStream_t s
     // the LDS-resident kernel addresses one (sequence, head)'s key rows with 32-bit buffer offsets
     if (quantize_keys_lds_shape(a.m, a.m_out) && a.T * a.sKt * 2 + 256 < ((int64_t)1 << 31)) {
         const int wi = a.m >> 5, wo = a.m_out >> 5;
-#define QK_LDS(WI, WO) hipLaunchKernelGGL((quantize_keys_lds_kernel<WI, WO, kQKWaves, kQKPrefetch>), grid, dim3(64 * kQKWaves), 0, s, a)
+#define QK_LDS(WI, WO) hipLaunchKernelGGL((quantize_keys_lds_kernel<WI, WO>), grid, dim3(kLThreads), 0, s, a)
         if (wi == 16 && wo == 16) QK_LDS(16, 16);
         else if (wi == 16 && wo == 0) QK_LDS(16, 0);
         else if (wi == 8 && wo == 8) QK_LDS(8, 8);
