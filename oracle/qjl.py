@@ -29,7 +29,11 @@ Readings taken where the pages are silent (each is also listed in the design not
   * norms are stored as IEEE binary16, round-to-nearest-even ("16-bit norm", [1BIT]);
   * value quantization is per token and KV head over the whole head dimension, min/max range with
     2^b - 1 equal steps and round-to-nearest [2NUM "The Obvious Fix"]; min and step stored as fp16;
-  * attention: z = sm_scale * score, softmax over all N keys (no mask), weighted sum of values.
+  * attention: z = sm_scale * score, softmax over all N keys (no mask), weighted sum of values;
+  * outlier channels of a KV head [2NUM "The Real Problem: Outlier Channels", HARD "The Third
+    Problem: Magnitude Outliers"]: the n_out channels with the largest mean magnitude |k_c| over all
+    keys of that head seen so far (every sequence and token of the prefill), the lower channel first
+    on equal means; returned in ascending channel order.
 """
 from __future__ import annotations
 
@@ -145,6 +149,25 @@ def quantize_keys(K: np.ndarray, S_in: np.ndarray, S_out: np.ndarray, outlier_id
             r = quantize_key_vectors(K[b, :, h, :], S_in, S_out, outlier_idx[h] if outlier_idx.size else [])
             bits[b, h], norms[b, h], near[b, h] = r["bits"], r["norms"], r["near_zero"]
     return {"bits": bits, "norms": norms, "near_zero": near}
+
+
+def select_outliers(K: np.ndarray, n_out: int) -> np.ndarray:
+    """Outlier channels of every KV head from keys K [B, T, Hkv, d] -> int32 [Hkv, n_out].
+
+    The pages describe outlier channels as the few coordinates whose magnitudes are 10-100x those of
+    the rest [2NUM "The Real Problem: Outlier Channels"; HARD "The Third Problem: Magnitude
+    Outliers": "detecting them"]; the detection statistic is not given.  Read here as the mean of
+    |k_c| over the B*T keys of the head, in fp64; the n_out largest means win, the lower channel
+    first on equal means, and the chosen channels are listed in ascending order.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    B, T, Hkv, d = K.shape
+    out = np.zeros((Hkv, n_out), dtype=np.int32)
+    for h in range(Hkv):
+        mean_abs = np.abs(K[:, :, h, :]).reshape(B * T, d).mean(axis=0) if B * T else np.zeros(d)
+        order = sorted(range(d), key=lambda c: (-mean_abs[c], c))      # largest mean, then lower channel
+        out[h] = np.sort(np.array(order[:n_out], dtype=np.int32))
+    return out
 
 
 # ----------------------------------------------------------------------------- values

@@ -378,3 +378,57 @@ def test_decode_brute_force_d8_page_vectors():
         e = [math.exp(x - mz) for x in z]
         o = [sum(e[t] * vhat[t][c] for t in range(3)) / sum(e) for c in range(8)]
         np.testing.assert_allclose(res["out"][0, 0], o, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- outlier channels
+
+def test_select_outliers_page_examples():
+    """The pages' own outlier channels: the two 100x coordinates of the 8-dim key (page 3, 'The Real
+    Problem: Outlier Channels'), the four big dims of cat/sat/mat (page 1, 'Seeing It With Real
+    Numbers') and the three ~0.8 dims among ~0.05 ones (page 5, 'The Third Problem: Magnitude
+    Outliers')."""
+    g3 = golden("page3_tokenwise.json")["three_bit_outliers"]
+    K = np.array(g3["v"], dtype=np.float64).reshape(1, 1, 1, -1)
+    assert oracle.select_outliers(K, 2)[0].tolist() == [c - 1 for c in g3["outlier_dims_printed_one_based"]]
+    g1 = golden("page1_one_bit_keys.json")
+    K = np.array([g1["keys"][t] for t in ("cat", "sat", "mat")], dtype=np.float64).reshape(1, 3, 1, -1)
+    assert oracle.select_outliers(K, 4)[0].tolist() == [c - 1 for c in g1["big_dims_printed_one_based"]]
+    g5 = golden("page5_uniform_2bit.json")["outlier_magnitudes_conceptual"]
+    rng = np.random.default_rng(7)
+    mag = np.full(g5["d"], g5["normal_magnitude"])
+    mag[g5["channels"]] = g5["outlier_magnitude"]
+    K = (mag * rng.choice([-1.0, 1.0], size=(2, 50, 1, g5["d"]))) * rng.uniform(0.5, 1.5, size=(2, 50, 1, g5["d"]))
+    assert oracle.select_outliers(K, 3)[0].tolist() == g5["channels"]
+
+
+def test_select_outliers_closed_forms_and_ties():
+    d = 16
+    # |k_c| = c + 1 for every key: the n_out highest channels
+    K = np.tile(np.arange(1.0, d + 1.0) * np.array([1, -1] * (d // 2)), (2, 3, 2, 1))
+    assert oracle.select_outliers(K, 3).tolist() == [[13, 14, 15]] * 2
+    # all magnitudes equal: the lowest channels win the ties
+    assert oracle.select_outliers(np.ones((1, 4, 1, d)), 5)[0].tolist() == [0, 1, 2, 3, 4]
+    # the statistic is the mean of |k_c| over all 8 keys of the head (not the max, not the RMS)
+    K = np.zeros((2, 4, 1, d))
+    K[1, 3, 0, 7] = 1.0                                                   # mean 0.125  (max 1,   RMS 0.354)
+    K[:, :, 0, 4] = 0.1                                                   # mean 0.1    (max 0.1, RMS 0.1)
+    K[0, 0, 0, 9] = 0.5                                                   # mean 0.0625 (max 0.5, RMS 0.177)
+    K[:, :, 0, 12] = 0.11                                                 # mean 0.11   (max 0.11, RMS 0.11)
+    assert oracle.select_outliers(K, 1)[0].tolist() == [7]
+    assert oracle.select_outliers(K, 2)[0].tolist() == [7, 12]           # by max or RMS: [7, 9]
+    assert oracle.select_outliers(K, 3)[0].tolist() == [4, 7, 12]        # by max or RMS: [7, 9, 12]
+    assert oracle.select_outliers(K, 0).shape == (1, 0)
+
+
+def test_select_outliers_invariances():
+    """Invariant under token order, signs, positive scale and splitting the keys into sequences;
+    heads are independent."""
+    rng = np.random.default_rng(3)
+    K = rng.standard_normal((2, 40, 3, 32)) * rng.uniform(0.1, 3.0, size=(1, 1, 3, 32))
+    ref = oracle.select_outliers(K, 5)
+    assert np.array_equal(oracle.select_outliers(K[:, ::-1], 5), ref)
+    assert np.array_equal(oracle.select_outliers(-2.5 * K, 5), ref)
+    assert np.array_equal(oracle.select_outliers(K.reshape(1, 80, 3, 32), 5), ref)
+    for h in range(3):
+        assert np.array_equal(oracle.select_outliers(K[:, :, h:h + 1], 5)[0], ref[h])
+    assert all(np.all(np.diff(r) > 0) for r in ref)                      # ascending, distinct
