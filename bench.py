@@ -169,6 +169,21 @@ def bench_quantize(qjl, torch, steps: int) -> dict:
     n, ms = qjl.timer_read("quantize_keys")
     qjl.timer_enable(False)
     kern_s = ms / 1e3 / max(n, 1)
+    # outlier-channel selection over the same keys (one read of K, two launches)
+    ws = torch.empty(qjl.lib.qjl_select_outliers_workspace_size(w.B, w.N, w.Hkv, w.d), dtype=torch.uint8, device="cuda")
+    sel = torch.empty((w.Hkv, w.n_out), dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        qjl.select_outliers(K, w.n_out, sel, workspace=ws)
+    torch.cuda.synchronize()
+    qjl.timer_enable(True)
+    qjl.timer_read("select_outliers")
+    for _ in range(steps):
+        qjl.select_outliers(K, w.n_out, sel, workspace=ws)
+    torch.cuda.synchronize()
+    ns, mss = qjl.timer_read("select_outliers")
+    qjl.timer_enable(False)
+    sel_s = mss / 1e3 / max(ns, 1)
+    sel_bytes = float(K.numel() * K.element_size())
     tokens = w.B * w.N
     flops = 2.0 * w.d * w.m * tokens * w.Hkv          # inlier (d - n_out) m + outlier n_out m_out = d m MACs
     return {"workload": f"{w.name}: B={w.B} T={w.N} Hkv={w.Hkv} d={w.d} m=m_out={w.m} n_out={w.n_out}",
@@ -176,7 +191,10 @@ def bench_quantize(qjl, torch, steps: int) -> dict:
             "kernel_ms": kern_s * 1e3, "wall_ms_per_call": wall * 1e3,
             "mfma": {"bound": "mfma", "achieved": flops / kern_s / 1e12, "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": flops / kern_s / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-                     "flops_per_launch": flops}}
+                     "flops_per_launch": flops},
+            "select_outliers": {"kernel_ms": sel_s * 1e3, "bound": "hbm", "achieved": sel_bytes / sel_s / 1e9,
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": sel_bytes / sel_s / 1e9 / HBM_PEAK_GBS,
+                                "bytes_per_launch": sel_bytes}}
 
 
 def main() -> int:

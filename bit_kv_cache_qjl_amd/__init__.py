@@ -55,6 +55,10 @@ lib.qjl_decode_attention.argtypes = [_p, _i, _i, _i, _i, _i, _i64, _p, _i, _p, _
 lib.qjl_decode_step.restype = _i
 lib.qjl_decode_step.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _p, _i, _p, _i, _p, _i,
                                 _p, _p, _p, _p, _i64, _i, _f, _p, _p, _i, _p, _sz, _p]
+lib.qjl_select_outliers_workspace_size.restype = _sz
+lib.qjl_select_outliers_workspace_size.argtypes = [_i, _i64, _i, _i]
+lib.qjl_select_outliers.restype = _i
+lib.qjl_select_outliers.argtypes = [_p, _i, _i, _i64, _i, _i, _i64, _i64, _i64, _i, _p, _p, _sz, _p]
 lib.qjl_status_string.restype = ctypes.c_char_p
 lib.qjl_status_string.argtypes = [_i]
 lib.qjl_last_error.restype = ctypes.c_char_p
@@ -234,6 +238,25 @@ def decode_step(Q, K_new, V_new, S_in, S_out, outlier_idx, cache: Cache, N: int,
                                _ptr(cache.codes), _ptr(cache.meta), cache.Ncap, cache.nbits, sm_scale, _ptr(out),
                                _ptr(scores_dbg), nsplit, _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)), "qjl_decode_step")
+
+
+def select_outliers(K, n_out: int, outlier_idx=None, *, workspace=None, stream=None):
+    """qjl_select_outliers on torch tensors: K [B, T, Hkv, d] (d contiguous) -> int32 [Hkv, n_out],
+    the channels with the largest mean |k_c| of each KV head, ascending."""
+    import torch
+    B, T, Hkv, d = K.shape
+    if K.stride(3) != 1:
+        raise ValueError("the d channels of K must be contiguous")
+    if outlier_idx is None:
+        outlier_idx = torch.empty((Hkv, n_out), dtype=torch.int32, device=K.device)
+    _contiguous(outlier_idx=outlier_idx, workspace=workspace)
+    if workspace is None:
+        workspace = torch.empty(max(1, int(lib.qjl_select_outliers_workspace_size(B, T, Hkv, d))), dtype=torch.uint8,
+                                device=K.device)
+    _check(lib.qjl_select_outliers(_ptr(K), _dtype_code(K), B, T, Hkv, d, K.stride(0), K.stride(1), K.stride(2), n_out,
+                                   _ptr(outlier_idx), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "qjl_select_outliers")
+    return outlier_idx
 
 
 def timer_enable(on: bool) -> None:

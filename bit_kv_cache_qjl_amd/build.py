@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqjl.so")
-SOURCES = ["qjl_api.hip", "qjl_keys.hip", "qjl_values.hip", "qjl_decode.hip", "qjl_decode_mfma.hip"]
+SOURCES = ["qjl_api.hip", "qjl_keys.hip", "qjl_values.hip", "qjl_decode.hip", "qjl_decode_mfma.hip", "qjl_outliers.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -70,7 +70,7 @@ hipEvent_t pool_event() {
 }
 
 const char* kKernelNames[qjl::TK_COUNT] = {"quantize_keys", "quantize_values", "query_project", "decode", "combine",
-                                           "append_project"};
+                                           "append_project", "select_outliers"};
 
 }  // namespace
 
@@ -402,6 +402,47 @@ int qjl_decode_step(const void* Q, const void* K_new, const void* V_new, int dt,
     return qjl_decode_attention(Q, dt, B, Hq, Hkv, d, N, S_in, m, S_out, m_out, outlier_idx, n_out, bits, norms, Ncap,
                                 QJL_V_CODES, codes, meta, nullptr, nbits, sm_scale, out, scores_dbg, nsplit, workspace,
                                 ws_bytes, stream);
+}
+
+size_t qjl_select_outliers_workspace_size(int B, int64_t T, int Hkv, int d) {
+    if (B < 0 || T < 0 || Hkv <= 0 || d != qjl::kD) return 0;
+    const int64_t nb = qjl::outlier_token_blocks(B, T, Hkv);
+    return align256((size_t)(nb > 0 ? nb : 1) * (size_t)(B > 0 ? B : 1) * Hkv * qjl::kD * sizeof(double));
+}
+
+int qjl_select_outliers(const void* K, int kdt, int B, int64_t T, int Hkv, int d, int64_t sK_b, int64_t sK_t,
+                        int64_t sK_h, int n_out, int32_t* outlier_idx, void* workspace, size_t ws_bytes,
+                        hipStream_t stream) {
+    g_last_error.clear();
+    if (kdt != QJL_BF16 && kdt != QJL_F32) return fail(QJL_ERR_INVALID_ARG, "kdt=%d is not a qjl_dtype", kdt);
+    if (B < 0 || T < 0 || Hkv <= 0 || n_out < 0)
+        return fail(QJL_ERR_INVALID_ARG, "bad sizes B=%d T=%lld Hkv=%d n_out=%d", B, (long long)T, Hkv, n_out);
+    if (d != qjl::kD) return fail(QJL_ERR_UNSUPPORTED, "d=%d unsupported (only d=128)", d);
+    if (n_out > qjl::kMaxOutliers) return fail(QJL_ERR_UNSUPPORTED, "n_out=%d exceeds %d", n_out, qjl::kMaxOutliers);
+    if (n_out == 0) return QJL_OK;
+    if (!outlier_idx || (B > 0 && T > 0 && !K)) return fail(QJL_ERR_INVALID_ARG, "null device pointer");
+    if (sK_b < 0 || sK_t < 0 || sK_h < 0) return fail(QJL_ERR_INVALID_ARG, "negative stride");
+    const int64_t vec = kdt == QJL_BF16 ? 8 : 4;
+    if ((K && !aligned16(K)) || !aligned16(outlier_idx) || sK_b % vec || sK_t % vec || sK_h % vec)
+        return fail(QJL_ERR_MISALIGNED, "pointers must be 16-byte aligned and strides multiples of %lld elements", (long long)vec);
+    const size_t need = qjl_select_outliers_workspace_size(B, T, Hkv, d);
+    if (!workspace || ws_bytes < need)
+        return fail(QJL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(QJL_ERR_MISALIGNED, "device pointers must be 16-byte aligned");
+    qjl::OutlierArgs a{};
+    a.K = K;
+    a.sKb = sK_b;
+    a.sKt = sK_t;
+    a.sKh = sK_h;
+    a.partial = static_cast<double*>(workspace);
+    a.outlier_idx = outlier_idx;
+    a.T = B > 0 ? T : 0;
+    a.Hkv = Hkv;
+    a.n_out = n_out;
+    qjl::timer_begin(qjl::TK_SELECT, stream);
+    const hipError_t e = qjl::launch_select_outliers(a, B, kdt, stream);
+    qjl::timer_end(qjl::TK_SELECT, stream);
+    return hip_status(e, "qjl_select_outliers launch");
 }
 
 }  // extern "C"

@@ -215,8 +215,19 @@ struct AppendArgs {
     int64_t pos;                      // cache position of the new token (N - 1)
 };
 
+// Outlier-channel selection over prefill keys (model layout, element strides).
+struct OutlierArgs {
+    const void* K;
+    int64_t sKb, sKt, sKh;
+    double* partial;                  // workspace: per-channel sums [B * token blocks][Hkv][kD]
+    int32_t* outlier_idx;             // [Hkv][n_out]
+    int64_t T;
+    int64_t tokens_per_block;
+    int Hkv, n_out;
+};
+
 // Kernel ids of the launch timer.
-enum TimedKernel { TK_QUANT_KEYS = 0, TK_QUANT_VALUES, TK_QPROJ, TK_DECODE, TK_COMBINE, TK_STEP, TK_COUNT };
+enum TimedKernel { TK_QUANT_KEYS = 0, TK_QUANT_VALUES, TK_QPROJ, TK_DECODE, TK_COMBINE, TK_STEP, TK_SELECT, TK_COUNT };
 
 // Host-side launchers (defined next to their kernels). They return hipSuccess or the launch error.
 hipError_t launch_quantize_keys_bf16(const KeyQuantArgs& a, int B, hipStream_t s);
@@ -235,6 +246,9 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int qdt, hipStream_t s);
 hipError_t launch_decode_step_mfma(const DecodeArgs& a, const AppendArgs& ap, hipStream_t s);
 // log-sum-exp merge of the chunk partials into out
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
+// outlier-channel selection (kdt 0: bf16 keys, 1: fp32) and its token blocks per (sequence, head)
+hipError_t launch_select_outliers(const OutlierArgs& a, int B, int kdt, hipStream_t s);
+int64_t outlier_token_blocks(int B, int64_t T, int Hkv);
 
 // Decode geometry shared by the workspace-size query and the launcher.
 constexpr int kDecodeTile = 512;     // tokens per tile = threads per decode block

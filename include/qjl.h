@@ -197,6 +197,28 @@ int qjl_decode_step(const void* Q, const void* K_new, const void* V_new, int dt,
                     float sm_scale, float* out, float* scores_dbg, int nsplit,
                     void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * qjl_select_outliers - the outlier channels of every KV head, from prefill keys.
+ *
+ * The pages describe outlier channels as the few coordinates whose values are 10-100x those of the
+ * rest ("2 numbers out of 128 destroy the entire KV cache", "The Real Problem: Outlier Channels";
+ * "Why Compressing the KV Cache Is Hard", "The Third Problem: Magnitude Outliers", which asks for
+ * detecting them); the QJL summary ("Approach") routes them through a separate quantizer copy.
+ * Here: for KV head h, the n_out channels with the largest mean |k_c| over all B*T keys of the
+ * head; equal means are ordered by the lower channel; written to outlier_idx[h][0..n_out) in
+ * ascending channel order, ready for qjl_quantize_keys / qjl_decode_attention.
+ *   K           keys in the model layout (as for qjl_quantize_keys), dtype kdt; keys must be finite.
+ *   n_out       0..16 (0 writes nothing).  B*T == 0 selects channels 0..n_out-1.
+ *   outlier_idx int32 [Hkv][n_out].
+ *   workspace   device scratch of at least qjl_select_outliers_workspace_size(B, T, Hkv, d) bytes.
+ * The magnitudes are summed in fp64 in a fixed order, so the result is deterministic; bf16 keys are
+ * summed exactly unless a channel's sum spans more than 53 bits.
+ */
+size_t qjl_select_outliers_workspace_size(int B, int64_t T, int Hkv, int d);
+int qjl_select_outliers(const void* K, int kdt, int B, int64_t T, int Hkv, int d,
+                        int64_t sK_b, int64_t sK_t, int64_t sK_h, int n_out, int32_t* outlier_idx,
+                        void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* qjl_status_string(int status);
 
@@ -206,7 +228,7 @@ const char* qjl_last_error(void);
 /*
  * Kernel timing for measurement harnesses.  While enabled, every launch of the named kernel
  * ("decode", "quantize_keys", "quantize_values", "query_project", "combine", "append_project": the
- * append + query-projection launch of qjl_decode_step) is bracketed by HIP
+ * append + query-projection launch of qjl_decode_step, "select_outliers") is bracketed by HIP
  * events recorded on the launch stream.  qjl_timer_read synchronizes on the recorded events and
  * returns the number of launches timed and their total duration in milliseconds, then clears the
  * record.  Disabled by default; enabling it does not change results.

@@ -181,3 +181,40 @@ def test_decode_step_rejects(kw, status):
 
 def test_decode_step_empty_batch_is_noop():
     assert step_call(B=0, ws=0, ws_bytes=0) == qjl.QJL_OK
+
+
+def select_call(ws_bytes=None, **kw):
+    a = dict(K=FAKE, kdt=0, B=2, T=100, Hkv=4, d=128, sK_b=100 * 4 * 128, sK_t=4 * 128, sK_h=128, n_out=4,
+             oidx=FAKE, ws=FAKE, ws_bytes=0, stream=0)
+    a.update(kw)
+    a["ws_bytes"] = (qjl.lib.qjl_select_outliers_workspace_size(a["B"], a["T"], a["Hkv"], 128) - 8
+                     if ws_bytes is None else ws_bytes)
+    return qjl.lib.qjl_select_outliers(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kdt=2), qjl.QJL_ERR_INVALID_ARG),
+    (dict(T=-1), qjl.QJL_ERR_INVALID_ARG),
+    (dict(n_out=17), qjl.QJL_ERR_UNSUPPORTED),
+    (dict(d=64), qjl.QJL_ERR_UNSUPPORTED),
+    (dict(oidx=0), qjl.QJL_ERR_INVALID_ARG),
+    (dict(K=0), qjl.QJL_ERR_INVALID_ARG),
+    (dict(sK_t=4 * 128 + 4), qjl.QJL_ERR_MISALIGNED),
+    (dict(oidx=MIS), qjl.QJL_ERR_MISALIGNED),
+    (dict(), qjl.QJL_ERR_WORKSPACE),                    # 8 bytes short
+    (dict(ws=0), qjl.QJL_ERR_WORKSPACE),
+])
+def test_select_outliers_rejects(kw, status):
+    assert select_call(**kw) == status
+    assert qjl.last_error() != ""
+
+
+def test_select_outliers_no_channels_is_noop():
+    assert select_call(n_out=0, K=0, oidx=0, ws=0) == qjl.QJL_OK
+
+
+def test_select_outliers_workspace_formula():
+    # ~1024 workgroups of >= 256 tokens over (sequence, head): one fp64 sum per channel each
+    assert qjl.lib.qjl_select_outliers_workspace_size(1, 65536, 8, 128) == 128 * 8 * 128 * 8
+    assert qjl.lib.qjl_select_outliers_workspace_size(2, 100, 4, 128) == ((1 * 2 * 4 * 128 * 8 + 255) // 256) * 256
+    assert qjl.lib.qjl_select_outliers_workspace_size(1, 10, 4, 64) == 0
