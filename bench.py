@@ -212,6 +212,8 @@ def main() -> int:
     ap.add_argument("--cache-copies", type=int, default=0,
                     help="independent caches the steps rotate through (0: enough that consecutive steps never "
                          f"find their cache in the {MALL_BYTES >> 20} MiB last-level cache)")
+    ap.add_argument("--value-bits", type=int, default=0, choices=[0, 2, 4],
+                    help="token-wise value code width (0: the workload's, 2 bits)")
     ap.add_argument("--nsplit", type=int, default=0,
                     help="context chunks per (sequence, KV head) of the decode (0: the library's choice)")
     ap.add_argument("--separate-calls", action="store_true",
@@ -240,7 +242,11 @@ def main() -> int:
         return 0
 
     w = si.WORKLOADS[args.workload]
+    if args.value_bits:
+        w = w.scaled(nbits=args.value_bits)
     N = w.N
+    # algorithmic bytes per cached token and KV head: sign words, two fp16 norms, codes, fp16 (min, step)
+    bytes_per_token_head = (w.m + w.m_out) // 8 + 4 + w.d * w.nbits // 8 + 4
     log(f"bench: {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={N}; generating inputs")
     oidx = si.outlier_channels(w)
     S_in_np, S_out_np = si.jl_matrices(w)
@@ -250,7 +256,7 @@ def main() -> int:
     S_in = torch.from_numpy(S_in_np).cuda().to(torch.bfloat16)
     S_out = torch.from_numpy(S_out_np).cuda().to(torch.bfloat16)
     od = torch.from_numpy(oidx).cuda()
-    cache_bytes = BYTES_PER_TOKEN_HEAD * w.B * w.Hkv * N
+    cache_bytes = bytes_per_token_head * w.B * w.Hkv * N
     copies = args.cache_copies or max(1, math.ceil(3 * MALL_BYTES / cache_bytes))
     caches = []
     for _ in range(copies):
@@ -347,7 +353,7 @@ def main() -> int:
     value = keys_scored / (ms_per_step / 1e3)
     n_dec, ms_dec = kernels["decode"]
     dec_s = ms_dec / 1e3 / max(n_dec, 1)
-    bytes_alg = float(BYTES_PER_TOKEN_HEAD) * w.B * w.Hkv * N
+    bytes_alg = float(bytes_per_token_head) * w.B * w.Hkv * N
     achieved = bytes_alg / dec_s / 1e9
     log("bench: kernel ms/launch " + ", ".join(f"{k}={v[1] / max(v[0], 1):.4f}" for k, v in kernels.items()))
 
@@ -361,7 +367,8 @@ def main() -> int:
                    "entry_points": ("qjl_quantize_keys + qjl_quantize_values + qjl_decode_attention"
                                     if args.separate_calls else "qjl_decode_step")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name),
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(w.name) if w.nbits == 2 else None,   # counters: 2-bit runs
                      "kernel": DECODE_KERNEL, "kernel_ms": dec_s * 1e3, "algorithmic_bytes": bytes_alg},
         "kernel_ms_per_launch": {k: v[1] / max(v[0], 1) for k, v in kernels.items()},
         "step_timing": {"mode": "hip_graph_replay" if (graph_ok and args.graph) else "eager",

@@ -426,7 +426,7 @@ hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
 
 bool decode_uses_mfma(int m, int m_out, int vmode, int nbits) {
     const int win = m >> 5, wout = m_out >> 5;
-    return vmode == 0 && nbits == 2 && (win == 4 || win == 8 || win == 16) && (wout == 0 || wout == win) &&
+    return vmode == 0 && (nbits == 2 || nbits == 4) && (win == 4 || win == 8 || win == 16) && (wout == 0 || wout == win) &&
            win + wout <= 16;
 }
 
@@ -461,7 +461,7 @@ int64_t decode_chunk(int64_t N, int nsplit) {
 
 hipError_t launch_decode(const DecodeArgs& a, int qdt, int vmode, hipStream_t s) {
     const int win = a.m >> 5, wout = a.m_out >> 5;
-    if (decode_uses_mfma(a.m, a.m_out, vmode, 2)) return launch_decode_mfma(a, qdt, s);
+    if (decode_uses_mfma(a.m, a.m_out, vmode, vmode == 0 ? a.nbits : 2)) return launch_decode_mfma(a, qdt, s);
     timer_begin(TK_QPROJ, s);
     if (qdt == 0) hipLaunchKernelGGL(qproj_kernel<uint16_t>, dim3(a.B * a.Hq), dim3(256), 0, s, a);
     else hipLaunchKernelGGL(qproj_kernel<float>, dim3(a.B * a.Hq), dim3(256), 0, s, a);

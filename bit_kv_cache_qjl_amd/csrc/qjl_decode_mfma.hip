@@ -22,7 +22,8 @@
 //     positions, so z = |k_in| D_in + |k_out| D_out is the token's base-2 softmax logit.
 // Values on the same instruction: rows = (query head, piece) of the weight p * step, columns = 16
 // channels, K = 128 tokens; B = the 2-bit codes of a code tile as x & 0x33333333 and
-// (x >> 2) & 0x33333333 (e2m1 nibble 00cc = code / 2).  The weights of a 128-token block are scaled
+// (x >> 2) & 0x33333333 (e2m1 nibble 00cc = code / 2); 4-bit codes as their two 2-bit planes, the
+// high one through a B scale of 4.  The weights of a 128-token block are scaled
 // by 2^(8 - E), 2^E > the block's largest step, split into three e4m3 pieces, and transposed to the
 // A-operand order through LDS.  Each wave is an independent online-softmax stream over 128-token
 // blocks; the four waves of a workgroup merge at the end of the chunk.
@@ -204,9 +205,9 @@ __global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs 
     const int nunits = a.B * a.Hkv;
     if (APPEND && (int)blockIdx.x >= nunits) {
         // ---- the new values, one (sequence, KV head) per wave in workgroups of their own (their atomic
-        //      round trips overlap the projections): a row of 16 lanes, 8 channels per lane; the 2-bit
-        //      fields are merged into the tile words of position pos with atomic and/or, the rest of the
-        //      tile is kept
+        //      round trips overlap the projections): a row of 16 lanes, 8 channels per lane; the 2- or
+        //      4-bit fields are merged into the tile words of position pos with atomic and/or, the rest
+        //      of the tile is kept
         const int vunit = 4 * ((int)blockIdx.x - nunits) + wave;
         if (vunit >= nunits) return;
         const int vb = vunit / a.Hkv, vh = vunit - vb * a.Hkv;
@@ -219,18 +220,20 @@ __global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs 
             v[2 * q] = __uint_as_float(w[q] << 16);
             v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
         }
+        const int nb = a.nbits;
         uint32_t code[8];
-        const uint32_t mt = value_codes16<2>(v, code);
+        const uint32_t mt = nb == 4 ? value_codes16<4>(v, code) : value_codes16<2>(v, code);
         if (lane < 16) {
             if (lane == 0) reinterpret_cast<uint32_t*>(ap.meta)[(size_t)vunit * a.Ncap + ap.pos] = mt;
             const int64_t tile = ap.pos / kCodeTile;
-            const int j = (int)(ap.pos % kCodeTile);
-            uint32_t* tw = ap.codes + ((size_t)vunit * code_tiles(a.Ncap) + tile) * (kD * 2) + (j >> 4);
-            const int sh = 2 * (j & 15);
+            const int bit = nb * code_field((int)(ap.pos % kCodeTile), nb);   // the field never crosses a word
+            uint32_t* tw = ap.codes + ((size_t)vunit * code_tiles(a.Ncap) + tile) * (kD * nb) + (bit >> 5);
+            const int sh = bit & 31;
+            const uint32_t fm = (1u << nb) - 1u;
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                uint32_t* dst = tw + code_slot(8 * lane + q) * 2;
-                atomicAnd(dst, ~(3u << sh));
+                uint32_t* dst = tw + code_slot(8 * lane + q) * nb;
+                atomicAnd(dst, ~(fm << sh));
                 atomicOr(dst, code[q] << sh);
             }
         }
@@ -348,12 +351,12 @@ __device__ __forceinline__ int mfma_token(int s, int t) {
 
 // Token data of one 128-token block for one lane: the stored quarter-row (lane group hh) of the sign
 // words of its token for each sub-step, the (norm, meta) pairs of tokens 2 lane and 2 lane + 1 (staged
-// through LDS before use), and the code words of channels 16 cg + t in code tile s0/32 + hh.
-template <int WIN4, int WOUT4>
+// through LDS before use), and the NB code words of channels 16 cg + t in code tile s0/32 + hh.
+template <int WIN4, int WOUT4, int NB>
 struct MBlock {
     uint32_t w[8][WIN4 + WOUT4];
     uint32_t nm[4];
-    uint32_t cx[8][2];
+    uint32_t cx[8][NB];
 };
 
 // Per-lane parts of the block loads (the block start enters as a scalar offset).
@@ -363,8 +366,8 @@ struct MOffsets {
     int codes;   // channel streams 8 t .. 8 t + 7 of code tile hh
 };
 
-template <int WIN4, int WOUT4>
-__device__ __forceinline__ void load_mblock(MBlock<WIN4, WOUT4>& bl, __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rn,
+template <int WIN4, int WOUT4, int NB>
+__device__ __forceinline__ void load_mblock(MBlock<WIN4, WOUT4, NB>& bl, __amdgpu_buffer_rsrc_t rb, __amdgpu_buffer_rsrc_t rn,
                                             __amdgpu_buffer_rsrc_t rm, __amdgpu_buffer_rsrc_t rc, const MOffsets& o, int s0) {
     constexpr int Q = WIN4 + WOUT4;              // words per quarter-row
     constexpr int WB = 4 * Q;
@@ -389,19 +392,24 @@ __device__ __forceinline__ void load_mblock(MBlock<WIN4, WOUT4>& bl, __amdgpu_bu
     const auto n2 = __builtin_amdgcn_raw_buffer_load_b64(rn, vn, 0, 0);
     const auto m2 = __builtin_amdgcn_raw_buffer_load_b64(rm, vn, 0, 0);
     bl.nm[0] = n2[0]; bl.nm[1] = m2[0]; bl.nm[2] = n2[1]; bl.nm[3] = m2[1];
-    const int vc = o.codes + s0 * (kD * 2 * 4 / kCodeTile);
+    const int vc = o.codes + s0 * (kD * NB * 4 / kCodeTile);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2 * NB; ++q) {
         const auto x = __builtin_amdgcn_raw_buffer_load_b128(rc, vc + 16 * q, 0, 0);
-        bl.cx[2 * q][0] = x[0]; bl.cx[2 * q][1] = x[1];
-        bl.cx[2 * q + 1][0] = x[2]; bl.cx[2 * q + 1][1] = x[3];
+        if constexpr (NB == 2) {
+            bl.cx[2 * q][0] = x[0]; bl.cx[2 * q][1 % NB] = x[1];
+            bl.cx[(2 * q + 1) % 8][0] = x[2]; bl.cx[(2 * q + 1) % 8][1 % NB] = x[3];
+        } else {
+            bl.cx[q % 8][0] = x[0]; bl.cx[q % 8][1] = x[1]; bl.cx[q % 8][2 % NB] = x[2]; bl.cx[q % 8][3 % NB] = x[3];
+        }
     }
 }
 
 // R = 1: one workgroup serves 4 query heads of a KV head; R = 2: 8 query heads as two row groups of
 // the same instructions' B operands (the sign and code planes are built once for both).
-template <int WIN4, int WOUT4, int R, bool DBG>
-__global__ __launch_bounds__(kMThreads, R == 1 ? 2 : 1) void decode_mfma_kernel(DecodeArgs a, int groups, int hgroups) {
+// Two workgroups per CU for 4 query heads and 2-bit codes; one (the whole register file) otherwise.
+template <int WIN4, int WOUT4, int R, bool DBG, int NB>
+__global__ __launch_bounds__(kMThreads, (R == 1 && NB == 2) ? 2 : 1) void decode_mfma_kernel(DecodeArgs a, int groups, int hgroups) {
     constexpr int W4 = WIN4 + WOUT4;             // instructions (K blocks of 128 sign positions) per token
     constexpr int WB = 4 * W4;                   // sign words per token
     constexpr int HPG = 4 * R;                   // query heads per workgroup
@@ -481,9 +489,9 @@ __global__ __launch_bounds__(kMThreads, R == 1 ? 2 : 1) void decode_mfma_kernel(
                                                   (uint32_t)t_end * 4u);
     const __amdgpu_buffer_rsrc_t rm = buffer_rsrc(reinterpret_cast<const uint32_t*>(a.meta) + (size_t)unit * a.Ncap,
                                                   (uint32_t)t_end * 4u);
-    const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(a.codes + (size_t)unit * code_tiles(a.Ncap) * (kD * 2),
-                                                  (uint32_t)code_tiles(t_end) * 1024u);
-    const MOffsets offs{(mfma_token(0, t) * WB + hh * W4) * 4, 8 * lane, hh * 1024 + t * 64};
+    const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(a.codes + (size_t)unit * code_tiles(a.Ncap) * (kD * NB),
+                                                  (uint32_t)code_tiles(t_end) * (kD * NB * 4u));
+    const MOffsets offs{(mfma_token(0, t) * WB + hh * W4) * 4, 8 * lane, hh * (kD * NB * 4) + t * (8 * NB * 4)};
     const float inv_z = 1.0f / a.z_scale;
 
     float m_run[R], l_acc[R], mn_acc[R];
@@ -501,7 +509,7 @@ __global__ __launch_bounds__(kMThreads, R == 1 ? 2 : 1) void decode_mfma_kernel(
     asm volatile("" : "+v"(m8), "+v"(o1));
 
     // ---- one 128-token block
-    auto process = [&](const MBlock<WIN4, WOUT4>& cur, int s0) {
+    auto process = [&](const MBlock<WIN4, WOUT4, NB>& cur, int s0) {
         // (norm, meta) of the block's tokens to LDS (the previous block's reads are done: LDS
         // operations of a wave complete in order)
         *reinterpret_cast<uint4*>(nmw + 4 * lane) = make_uint4(cur.nm[0], cur.nm[1], cur.nm[2], cur.nm[3]);
@@ -622,12 +630,27 @@ __global__ __launch_bounds__(kMThreads, R == 1 ? 2 : 1) void decode_mfma_kernel(
         const int sc_w = 120 + E - 4 * pc;   // 2^(E - 8 - 4 piece), times 2 for the nibble = code / 2
 #pragma unroll
         for (int cg = 0; cg < 8; ++cg) {
-            const uint32_t x0 = cur.cx[cg][0], x1 = cur.cx[cg][1];
-            const v8i_t bv = v8i_t{(int)(x0 & 0x33333333u), (int)((x0 >> 2) & 0x33333333u), (int)(x1 & 0x33333333u),
-                                   (int)((x1 >> 2) & 0x33333333u), 0, 0, 0, 0};
+            if constexpr (NB == 2) {
+                const uint32_t x0 = cur.cx[cg][0], x1 = cur.cx[cg][1 % NB];
+                const v8i_t bv = v8i_t{(int)(x0 & 0x33333333u), (int)((x0 >> 2) & 0x33333333u), (int)(x1 & 0x33333333u),
+                                       (int)((x1 >> 2) & 0x33333333u), 0, 0, 0, 0};
 #pragma unroll
-            for (int rg = 0; rg < R; ++rg)
-                dv[rg][cg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw[rg], bv, dv[rg][cg], 0, 4, 0, sc_w, 0, 127);
+                for (int rg = 0; rg < R; ++rg)
+                    dv[rg][cg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw[rg], bv, dv[rg][cg], 0, 4, 0, sc_w, 0, 127);
+            } else {
+                // 4-bit codes: word w holds the same tokens in its two 2-bit planes as the 2-bit
+                // planes above; code = low + 4 high, the high plane through a B scale of 2^2
+                const uint32_t x0 = cur.cx[cg][0], x1 = cur.cx[cg][1], x2 = cur.cx[cg][2 % NB], x3 = cur.cx[cg][3 % NB];
+                const v8i_t blo = v8i_t{(int)(x0 & 0x33333333u), (int)(x1 & 0x33333333u), (int)(x2 & 0x33333333u),
+                                        (int)(x3 & 0x33333333u), 0, 0, 0, 0};
+                const v8i_t bhi = v8i_t{(int)((x0 >> 2) & 0x33333333u), (int)((x1 >> 2) & 0x33333333u),
+                                        (int)((x2 >> 2) & 0x33333333u), (int)((x3 >> 2) & 0x33333333u), 0, 0, 0, 0};
+#pragma unroll
+                for (int rg = 0; rg < R; ++rg) {
+                    dv[rg][cg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw[rg], blo, dv[rg][cg], 0, 4, 0, sc_w, 0, 127);
+                    dv[rg][cg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw[rg], bhi, dv[rg][cg], 0, 4, 0, sc_w, 0, 129);
+                }
+            }
         }
         __builtin_amdgcn_wave_barrier();   // the next block rewrites the weight tiles
     };
@@ -635,7 +658,7 @@ __global__ __launch_bounds__(kMThreads, R == 1 ? 2 : 1) void decode_mfma_kernel(
     // ---- the block loop, software-pipelined over two buffers: block i + 1 is in flight while block i
     //      is computed (loads past the chunk end fall outside the buffer ranges and return zeros)
     constexpr int kStep = kMBlock * kMWaves;
-    MBlock<WIN4, WOUT4> ba, bb;
+    MBlock<WIN4, WOUT4, NB> ba, bb;
     const int s_first = t_begin + kMBlock * wave;
     load_mblock(ba, rb, rn, rm, rc, offs, s_first);
     for (int s0 = s_first; s0 < t_end; s0 += 2 * kStep) {
@@ -694,7 +717,7 @@ __global__ __launch_bounds__(kMThreads, R == 1 ? 2 : 1) void decode_mfma_kernel(
 
 }
 
-template <int WIN4, int WOUT4, int R>
+template <int WIN4, int WOUT4, int R, int NB>
 hipError_t launch_decode_mfma_r(const DecodeArgs& a, hipStream_t s) {
     const int hgroups = (a.g + 4 * R - 1) / (4 * R);
     const int groups = a.B * a.Hkv * a.nsplit;
@@ -702,16 +725,18 @@ hipError_t launch_decode_mfma_r(const DecodeArgs& a, hipStream_t s) {
     const unsigned nblocks = (unsigned)slots * 8u * (unsigned)hgroups;
     timer_begin(TK_DECODE, s);
     if (a.scores_dbg)
-        hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, R, true>), dim3(nblocks), dim3(kMThreads), 0, s, a, groups, hgroups);
+        hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, R, true, NB>), dim3(nblocks), dim3(kMThreads), 0, s, a, groups, hgroups);
     else
-        hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, R, false>), dim3(nblocks), dim3(kMThreads), 0, s, a, groups, hgroups);
+        hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, R, false, NB>), dim3(nblocks), dim3(kMThreads), 0, s, a, groups, hgroups);
     timer_end(TK_DECODE, s);
     return hipGetLastError();
 }
 
 template <int WIN4, int WOUT4>
 hipError_t launch_decode_mfma_t(const DecodeArgs& a, hipStream_t s) {
-    return decode_mfma_rowgroups(a.g) == 2 ? launch_decode_mfma_r<WIN4, WOUT4, 2>(a, s) : launch_decode_mfma_r<WIN4, WOUT4, 1>(a, s);
+    const bool r2 = decode_mfma_rowgroups(a.g) == 2;
+    if (a.nbits == 4) return r2 ? launch_decode_mfma_r<WIN4, WOUT4, 2, 4>(a, s) : launch_decode_mfma_r<WIN4, WOUT4, 1, 4>(a, s);
+    return r2 ? launch_decode_mfma_r<WIN4, WOUT4, 2, 2>(a, s) : launch_decode_mfma_r<WIN4, WOUT4, 1, 2>(a, s);
 }
 
 template <bool APPEND>

@@ -8,9 +8,10 @@
 // threads own one value vector (8 channels each): a 16-lane min/max butterfly, the (min, step) meta,
 // and the codes of 8 channels into LDS.  Phase 2: one thread per channel packs the tile's 32 codes of
 // its channel into nbits words (the channel-major tile the decode kernels read as matrix-core
-// operands; channel c is stream slot 8 (c % 16) + c / 16 of the tile).  A tile wholly inside the append is stored; a tile the append covers only in part is
-// merged bit-exactly with two atomics per word (clear the appended fields, then set them), so tokens
-// outside [t0, t0 + T) keep their codes.
+// operands; channel c is stream slot 8 (c % 16) + c / 16 of the tile; token j sits in field
+// code_field(j, nbits)).  A tile wholly inside the append is stored; a tile the append covers only in
+// part is merged bit-exactly with two atomics per word (clear the appended fields, then set them), so
+// tokens outside [t0, t0 + T) keep their codes.
 //
 // The decisions are IEEE fp32 operations with no contraction: subtract, correctly rounded divide,
 // fp16 round-to-nearest-even, rint (ties to even).
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(kValThreads) void quantize_values_kernel(ValueQuant
             const uint32_t code = (four >> (8 * e)) & 0xFFu;
             const bool in = p0 + i >= a.t0 && p0 + i < a.t0 + a.T;
             constexpr uint32_t fm = (1u << NBITS) - 1u;
-            const int bp = NBITS * i;
+            const int bp = NBITS * code_field(i, NBITS);
             wd[bp >> 5] |= code << (bp & 31);
             if (in) msk[bp >> 5] |= fm << (bp & 31);
             if ((bp & 31) + NBITS > 32) {   // the field continues in the next word

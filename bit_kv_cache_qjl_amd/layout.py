@@ -52,6 +52,18 @@ def code_channel_of_slot(d: int = 128) -> np.ndarray:
     return 16 * (p % 8) + p // 8
 
 
+def code_field_tokens(nbits: int) -> np.ndarray:
+    """Token (0..31 within its tile) of each code field of a channel stream: field f occupies bits
+    [nbits*f, nbits*f + nbits).  2- and 3-bit streams are in token order; 4-bit streams hold in word
+    w the tokens 16 (w // 2) + 2 e + (w % 2), e = 0..7 (so the 2-bit planes of a word follow the same
+    token order as a 2-bit stream)."""
+    f = np.arange(TILE)
+    if nbits != 4:
+        return f
+    w, e = f // 8, f % 8
+    return 16 * (w // 2) + 2 * e + (w % 2)
+
+
 def codes_from_tiles(tiles: np.ndarray, nbits: int, n: int) -> np.ndarray:
     """uint32 (or int32) code tiles [..., ntiles, d, nbits] -> int64 codes [..., n, d]."""
     t = np.ascontiguousarray(tiles).view(np.uint32)
@@ -60,7 +72,8 @@ def codes_from_tiles(tiles: np.ndarray, nbits: int, n: int) -> np.ndarray:
         raise ValueError(f"tiles of shape {t.shape} do not hold {n} positions of {nbits}-bit codes")
     bits = (t[..., None] >> np.arange(32, dtype=np.uint32)) & np.uint32(1)       # [..., nt, d, nbits, 32]
     fields = bits.reshape(*lead, nt, d, TILE, nbits).astype(np.int64)            # stream bit nbits*j + k
-    codes = (fields << np.arange(nbits, dtype=np.int64)).sum(axis=-1)              # [..., nt, slot, 32]
+    codes = (fields << np.arange(nbits, dtype=np.int64)).sum(axis=-1)              # [..., nt, slot, field]
+    codes = codes[..., np.argsort(code_field_tokens(nbits))]                        # [..., nt, slot, token]
     codes = codes[..., code_slot_of_channel(d), :]                                  # [..., nt, channel, 32]
     codes = np.swapaxes(codes, -1, -2).reshape(*lead, nt * TILE, d)
     return np.ascontiguousarray(codes[..., :n, :])
@@ -78,7 +91,8 @@ def tiles_from_codes(codes: np.ndarray, nbits: int, ncap: int | None = None) -> 
     full = np.zeros((*lead, nt * TILE, d), dtype=np.int64)
     full[..., :n, :] = c
     per = np.swapaxes(full.reshape(*lead, nt, TILE, d), -1, -2)                    # [..., nt, channel, 32]
-    per = per[..., code_channel_of_slot(d), :]                                      # [..., nt, slot, 32]
+    per = per[..., code_channel_of_slot(d), :]                                      # [..., nt, slot, token]
+    per = per[..., code_field_tokens(nbits)]                                        # [..., nt, slot, field]
     bits = (per[..., None] >> np.arange(nbits, dtype=np.int64)) & 1                 # [..., nt, d, 32, nbits]
     stream = bits.reshape(*lead, nt, d, nbits, 32).astype(np.uint64)                 # stream bit 32*w + i
     words = (stream << np.arange(32, dtype=np.uint64)).sum(axis=-1)

@@ -110,6 +110,7 @@ def decode_call(ws_bytes=None, **kw):
     (dict(m=384, m_out=384), qjl.QJL_ERR_UNSUPPORTED),
     (dict(m=256, m_out=128), qjl.QJL_ERR_UNSUPPORTED),
     (dict(nbits=3), qjl.QJL_ERR_UNSUPPORTED),
+    (dict(nbits=4, m=512, m_out=512), qjl.QJL_ERR_UNSUPPORTED),   # 4-bit codes: matrix-core shapes only
     (dict(vmode=1), qjl.QJL_ERR_INVALID_ARG),          # fp32 values but V_f32 is null
     (dict(vmode=7), qjl.QJL_ERR_INVALID_ARG),
     (dict(out=MIS), qjl.QJL_ERR_MISALIGNED),

@@ -8,12 +8,17 @@ layout = qjl.layout
 
 
 def tile_words_by_hand(codes, nbits, tile, ch):
-    """The nbits words of (tile, channel): position 32*tile + j in bits [nbits*j, nbits*j + nbits)
-    of an LSB-first stream; positions past the end count as code 0."""
+    """The nbits words of (tile, channel).  2 and 3 bits: position 32*tile + j in bits
+    [nbits*j, nbits*j + nbits) of an LSB-first stream.  4 bits: word w, nibble e holds position
+    32*tile + 16*(w // 2) + 2*e + (w % 2).  Positions past the end count as code 0."""
+    def code(j):
+        p = 32 * tile + j
+        return int(codes[p, ch]) if p < codes.shape[0] else 0
+    if nbits == 4:
+        return [sum(code(16 * (w // 2) + 2 * e + (w % 2)) << (4 * e) for e in range(8)) for w in range(4)]
     stream = 0
     for j in range(32):
-        p = 32 * tile + j
-        c = int(codes[p, ch]) if p < codes.shape[0] else 0
+        c = code(j)
         for k in range(nbits):
             if (c >> k) & 1:
                 stream |= 1 << (nbits * j + k)
@@ -50,6 +55,19 @@ def test_two_bit_tile_by_example():
     assert int(t[0, 8, 0]) == 1 << 10 and int(t[0, 8, 1]) == 0
     assert int(t[0, 1, 0]) == 0 and int(t[0, 1, 1]) == 0xC0000000
     assert not t[0, 2:8].any() and not t[0, 9:].any()
+
+
+def test_four_bit_tile_by_example():
+    """Channel 0 of a 4-bit tile: word 0 holds positions 0, 2, .., 14, word 1 positions 1, 3, .., 15,
+    words 2 and 3 the same for 16..31; position 2e + (w % 2) + 16 (w // 2) in nibble e of word w."""
+    codes = np.zeros((32, 128), dtype=np.int64)
+    codes[0, 0] = 0xF        # word 0, nibble 0
+    codes[14, 0] = 0x9       # word 0, nibble 7
+    codes[1, 0] = 0x3        # word 1, nibble 0
+    codes[31, 0] = 0x5       # word 3, nibble 7
+    codes[18, 0] = 0x2       # word 2, nibble 1
+    t = layout.tiles_from_codes(codes, 4)
+    assert [int(x) for x in t[0, 0]] == [0x9000000F, 0x3, 0x20, 0x50000000]
 
 
 def test_round_trip_with_leading_dims_and_int32_views():
