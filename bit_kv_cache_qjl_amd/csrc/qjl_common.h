@@ -13,10 +13,11 @@ constexpr float kSqrtHalfPi = 1.2533141373155002f;   // sqrt(pi / 2)
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---- cross-lane reductions on the VALU (DPP row permutes and gfx950 permlane swaps; no LDS
-//      crossbar round trip)
+//      crossbar round trip).  The row permutes read lanes of the same row only, so bound_ctrl (zero for
+//      invalid lanes) changes nothing and lets the compiler fold the move into the consuming instruction.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 // sum over each row of 16 lanes, result in every lane of the row
 __device__ __forceinline__ float row16_sum(float v) {
@@ -26,18 +27,20 @@ __device__ __forceinline__ float row16_sum(float v) {
     v += dpp_mov<0x140>(v);   // row_mirror
     return v;
 }
+// max / min: the IEEE maximum and minimum (v_maximum3 / v_minimum3), which agree with fmaxf / fminf
+// on non-NaN values and need no canonicalizing of the permuted operand
 __device__ __forceinline__ float row16_max(float v) {
-    v = fmaxf(v, dpp_mov<0xB1>(v));
-    v = fmaxf(v, dpp_mov<0x4E>(v));
-    v = fmaxf(v, dpp_mov<0x141>(v));
-    v = fmaxf(v, dpp_mov<0x140>(v));
+    v = __builtin_elementwise_maximum(v, dpp_mov<0xB1>(v));
+    v = __builtin_elementwise_maximum(v, dpp_mov<0x4E>(v));
+    v = __builtin_elementwise_maximum(v, dpp_mov<0x141>(v));
+    v = __builtin_elementwise_maximum(v, dpp_mov<0x140>(v));
     return v;
 }
 __device__ __forceinline__ float row16_min(float v) {
-    v = fminf(v, dpp_mov<0xB1>(v));
-    v = fminf(v, dpp_mov<0x4E>(v));
-    v = fminf(v, dpp_mov<0x141>(v));
-    v = fminf(v, dpp_mov<0x140>(v));
+    v = __builtin_elementwise_minimum(v, dpp_mov<0xB1>(v));
+    v = __builtin_elementwise_minimum(v, dpp_mov<0x4E>(v));
+    v = __builtin_elementwise_minimum(v, dpp_mov<0x141>(v));
+    v = __builtin_elementwise_minimum(v, dpp_mov<0x140>(v));
     return v;
 }
 // value held by lane l ^ 16 (neighbouring row) and by lane l ^ 32 (other half-wave)

@@ -36,6 +36,8 @@ namespace {
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v4f_t __attribute__((ext_vector_type(4)));
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+typedef short v2s_t __attribute__((ext_vector_type(2)));
 
 constexpr int kMThreads = 256;               // 4 waves
 constexpr int kMWaves = kMThreads / 64;
@@ -48,12 +50,24 @@ __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
     const uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)r, true);
 }
-// r[i] = (r[i] - value of byte i of k) * 16: the residual after an e4m3 piece, rescaled for the next
-__device__ __forceinline__ void next_piece(float (&r)[4], uint32_t k) {
-    r[0] = (r[0] - __builtin_amdgcn_cvt_f32_fp8((int)k, 0)) * 16.f;
-    r[1] = (r[1] - __builtin_amdgcn_cvt_f32_fp8((int)k, 1)) * 16.f;
-    r[2] = (r[2] - __builtin_amdgcn_cvt_f32_fp8((int)k, 2)) * 16.f;
-    r[3] = (r[3] - __builtin_amdgcn_cvt_f32_fp8((int)k, 3)) * 16.f;
+// The three e4m3 pieces of 4 values v: k[0] = e4m3(v), k[1] = e4m3(16 r1), k[2] = e4m3(256 r2), with
+// r1 = v - k[0] and r2 = r1 - k[1] / 16 exact in fp32, so v = k[0] + k[1] / 16 + k[2] / 256 + residual.
+// The scaled conversions of gfx950 divide by the scale's power of two before rounding and multiply by
+// it after decoding, two values per instruction.
+__device__ __forceinline__ void fp8_pieces(const float (&v)[4], uint32_t (&k)[3]) {
+    k[0] = fp8x4(v[0], v[1], v[2], v[3]);
+    v2f_t lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)k[0], 1.0f, false);
+    v2f_t hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)k[0], 1.0f, true);
+    float r0 = v[0] - lo[0], r1 = v[1] - lo[1], r2 = v[2] - hi[0], r3 = v[3] - hi[1];
+    v2s_t q = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s_t{0, 0}, r0, r1, 0.0625f, false);
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(q, r2, r3, 0.0625f, true);
+    k[1] = (uint32_t)(uint16_t)q[0] | ((uint32_t)(uint16_t)q[1] << 16);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)k[1], 0.0625f, false);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)k[1], 0.0625f, true);
+    r0 -= lo[0]; r1 -= lo[1]; r2 -= hi[0]; r3 -= hi[1];
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s_t{0, 0}, r0, r1, 0.00390625f, false);
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(q, r2, r3, 0.00390625f, true);
+    k[2] = (uint32_t)(uint16_t)q[0] | ((uint32_t)(uint16_t)q[1] << 16);
 }
 
 // The four fp4 operand words of a sign word (plane i = bit 4n + i of x in nibble n).  m8 and o1 hold
@@ -130,16 +144,12 @@ __device__ void query_operand_wave(const float* xs, int m, int m_out, int win4, 
             const float v = ldexpf(xs[32 * word + 4 * n + plane], e + (plane == 0 ? 1 : (plane == 2 ? -1 : 0)));
             y[q] = plane == 3 ? -v : v;
         }
-        // y = p0 + p1 / 16 + p2 / 256 + residual
-        const uint32_t k0 = fp8x4(y[0], y[1], y[2], y[3]);
-        next_piece(y, k0);
-        const uint32_t k1 = fp8x4(y[0], y[1], y[2], y[3]);
-        next_piece(y, k1);
-        const uint32_t k2 = fp8x4(y[0], y[1], y[2], y[3]);
+        uint32_t k[3];
+        fp8_pieces(y, k);
         uint32_t* d = dst + kb * 128 + ga * 8 + (task & 7);
-        d[0] = k0;
-        d[32] = k1;
-        d[64] = k2;
+        d[0] = k[0];
+        d[32] = k[1];
+        d[64] = k[2];
         d[96] = 0u;
     }
 }
@@ -528,8 +538,6 @@ __global__ __launch_bounds__(kMThreads, (R == 1 && NB == 2) ? 2 : 1) void decode
         for (int s = 0; s < 8; ++s) {
             const float n_in = (float)__builtin_bit_cast(_Float16, (uint16_t)(nrm[s] & 0xFFFFu));
             const float n_out = (float)__builtin_bit_cast(_Float16, (uint16_t)(nrm[s] >> 16));
-            const int P = s0 + mfma_token(s, t);
-            const bool valid = P < t_end;
             v8i_t bin[WIN4], bout[WOUT4 > 0 ? WOUT4 : 1];
 #pragma unroll
             for (int kb = 0; kb < WIN4; ++kb) bin[kb] = sign_planes(cur.w[s][kb], m8, o1);
@@ -551,9 +559,19 @@ __global__ __launch_bounds__(kMThreads, (R == 1 && NB == 2) ? 2 : 1) void decode
                     zz = fmaf(n_out, (dout[0] + dout[1]) + dout[2], zz);
                 }
                 if constexpr (DBG) {
-                    if (sdbg[rg] && valid) sdbg[rg][P] = zz * inv_z;
+                    const int P = s0 + mfma_token(s, t);
+                    if (sdbg[rg] && P < t_end) sdbg[rg][P] = zz * inv_z;
                 }
-                z[rg][s] = valid ? zz : -INFINITY;
+                z[rg][s] = zz;
+            }
+        }
+        if (s0 + kMBlock > t_end) {
+            // the chunk's last block: tokens past its end take no part in the softmax
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const bool past = s0 + mfma_token(s, t) >= t_end;
+#pragma unroll
+                for (int rg = 0; rg < R; ++rg) z[rg][s] = past ? -INFINITY : z[rg][s];
             }
         }
 
@@ -598,16 +616,12 @@ __global__ __launch_bounds__(kMThreads, (R == 1 && NB == 2) ? 2 : 1) void decode
                     mn_acc[rg] = fmaf(p, mnv[s], mn_acc[rg]);
                     w[i] = p * stpf[s];                   // in [0, 256)
                 }
-                // three e4m3 pieces: w = p0 + p1 / 16 + p2 / 256 + residual
-                const uint32_t k0 = fp8x4(w[0], w[1], w[2], w[3]);
-                next_piece(w, k0);
-                const uint32_t k1 = fp8x4(w[0], w[1], w[2], w[3]);
-                next_piece(w, k1);
-                const uint32_t k2 = fp8x4(w[0], w[1], w[2], w[3]);
+                uint32_t k[3];
+                fp8_pieces(w, k);
                 uint8_t* row = row0 + 16 * q;
-                *reinterpret_cast<uint32_t*>(row) = k0;
-                *reinterpret_cast<uint32_t*>(row + kWPitch) = k1;
-                *reinterpret_cast<uint32_t*>(row + 2 * kWPitch) = k2;
+                *reinterpret_cast<uint32_t*>(row) = k[0];
+                *reinterpret_cast<uint32_t*>(row + kWPitch) = k[1];
+                *reinterpret_cast<uint32_t*>(row + 2 * kWPitch) = k[2];
             }
         }
         if (__builtin_amdgcn_ballot_w64(rescale)) {
