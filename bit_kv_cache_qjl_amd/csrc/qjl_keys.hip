@@ -273,12 +273,10 @@ void quantize_keys_bf16_kernel(KeyQuantArgs a) {
 // outlier channels masked out (S_in has zero columns there, so the projections need no masking),
 // |k_out|^2 from the gathered operand.
 constexpr int kOGRow = 16;                   // gathered S_out row (bf16)
-constexpr int kSRowL = kD + 8;               // S_in row in LDS (bf16, 272 B)
+// S_in row in LDS (bf16, 272 B): the 16-byte A-fragment reads of a wave, in the MFMA's row order,
+// fall on distinct banks (measured: such a 64-lane b128 read runs at the full LDS rate)
+constexpr int kSRowL = kD + 8;
 
-// Projection row p of a 32-row tile sits at LDS row p ^ 8 (bit 4 of p): with the 272-byte pitch the
-// rows that 8 or 16 consecutive lanes of a matrix-core A operand read (tile_row order) then fall on
-// distinct 4-bank windows, and a fragment's offset within the row is the same for every lane.
-__device__ __forceinline__ int s_lrow(int p) { return p ^ (((p >> 4) & 1) << 3); }
 
 constexpr int kLWaves = 16;                  // one workgroup per CU: 4 waves per SIMD
 constexpr int kLThreads = 64 * kLWaves;
@@ -320,11 +318,30 @@ void quantize_keys_lds_kernel(KeyQuantArgs a) {
         s_goff[r] = r < n_out ? 2u * (uint32_t)s_oidx[r] : 0x7FFFFF00u;
     }
     {
+        // every load of a thread is issued before the first LDS store: one round trip to L2, not one
+        // per element
+        constexpr int NSI = WIN * 32 * 16 / kLThreads, NSO = WOUT * 32 * kOGRow / kLThreads;
+        static_assert(NSI * kLThreads == WIN * 32 * 16 && NSO * kLThreads == WOUT * 32 * kOGRow, "whole rounds");
         const uint16_t* Sin = static_cast<const uint16_t*>(a.S_in);
-        for (int i = tid; i < WIN * 32 * 16; i += kLThreads) {
+        const uint16_t* Sout = static_cast<const uint16_t*>(a.S_out);
+        uint4 v[NSI > 0 ? NSI : 1];
+        uint16_t go[NSO > 0 ? NSO : 1];
+#pragma unroll
+        for (int u = 0; u < NSI; ++u) {
+            const int i = tid + u * kLThreads;
+            v[u] = *reinterpret_cast<const uint4*>(Sin + (size_t)(i >> 4) * kD + 8 * (i & 15));
+        }
+#pragma unroll
+        for (int u = 0; u < NSO; ++u) {
+            const int i = tid + u * kLThreads;
+            const int j = i / kOGRow, r = i % kOGRow;
+            go[u] = r < n_out ? Sout[(size_t)j * kD + s_oidx[r]] : (uint16_t)0;
+        }
+#pragma unroll
+        for (int u = 0; u < NSI; ++u) {
+            const int i = tid + u * kLThreads;
             const int r = i >> 4, cgi = i & 15;
-            const uint4 v = *reinterpret_cast<const uint4*>(Sin + (size_t)r * kD + 8 * cgi);
-            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
             for (int k = 0; k < n_out; ++k) {
                 const int c = s_oidx[k];
                 if ((c >> 3) == cgi) {
@@ -334,13 +351,14 @@ void quantize_keys_lds_kernel(KeyQuantArgs a) {
                         if (q == ((c & 7) >> 1)) w[q] &= m;
                 }
             }
-            *reinterpret_cast<uint4*>(sl + ((r & ~31) | s_lrow(r & 31)) * kSRowL + 8 * cgi) = make_uint4(w[0], w[1], w[2], w[3]);
+            *reinterpret_cast<uint4*>(sl + r * kSRowL + 8 * cgi) = make_uint4(w[0], w[1], w[2], w[3]);
         }
-        const uint16_t* Sout = static_cast<const uint16_t*>(a.S_out);
-        for (int i = tid; i < WOUT * 32 * kOGRow; i += kLThreads) {
+#pragma unroll
+        for (int u = 0; u < NSO; ++u) {
+            const int i = tid + u * kLThreads;
             const int j = i / kOGRow, r = i % kOGRow;
             // the two 8-rank halves of row j swap places when bit 4 of the row is set
-            so[j * kOGRow + (r ^ (((j >> 4) & 1) << 3))] = r < n_out ? Sout[(size_t)j * kD + s_oidx[r]] : (uint16_t)0;
+            so[j * kOGRow + (r ^ (((j >> 4) & 1) << 3))] = go[u];
         }
     }
     __syncthreads();
@@ -355,7 +373,7 @@ void quantize_keys_lds_kernel(KeyQuantArgs a) {
     const int64_t head_row0 = ((int64_t)b * a.Hkv + h) * a.Ncap + a.t0;
     uint32_t* norms32 = reinterpret_cast<uint32_t*>(a.norms);
     // A fragment of tile j, K step s: arow + 32 j kSRowL + 16 s
-    const uint16_t* arow = sl + s_lrow(prow) * kSRowL + khalf;
+    const uint16_t* arow = sl + prow * kSRowL + khalf;
     // gathered S_out fragment of tile j: orow + 32 j kOGRow
     const uint16_t* orow = so + prow * kOGRow + 8 * ((khalf >> 3) ^ ((prow >> 4) & 1));
     const uint32_t* keep = s_keep + (lane >> 5) * 32;
