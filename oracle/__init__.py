@@ -11,11 +11,12 @@ cases and Monte-Carlo unbiasedness.  Every function is pinned; none is "parity u
 """
 from .qjl import (SQRT_HALF_PI, attend, decode_attention, dequantize_value_vectors, estimator_scores,
                   exact_attention, fp16, jl_project, outlier_mask, pack_bits, pack_codes, project_query,
-                  quantize_key_vectors, quantize_keys, quantize_value_vectors, quantize_values, select_outliers,
-                  softmax, two_sided_estimate, uniform_quantize, unpack_bits, unpack_codes)
+                  quantize_key_vectors, quantize_keys, quantize_value_vectors, quantize_values,
+                  rotate_sign_scores, select_outliers, softmax, two_sided_estimate, two_sided_scores,
+                  uniform_quantize, unpack_bits, unpack_codes)
 
 __all__ = ["SQRT_HALF_PI", "attend", "decode_attention", "dequantize_value_vectors", "estimator_scores",
            "exact_attention", "fp16", "jl_project", "outlier_mask", "pack_bits", "pack_codes",
            "project_query", "quantize_key_vectors", "quantize_keys", "quantize_value_vectors",
-           "quantize_values", "select_outliers", "softmax", "two_sided_estimate", "uniform_quantize", "unpack_bits",
-           "unpack_codes"]
+           "quantize_values", "rotate_sign_scores", "select_outliers", "softmax", "two_sided_estimate",
+           "two_sided_scores", "uniform_quantize", "unpack_bits", "unpack_codes"]

@@ -33,7 +33,14 @@ Readings taken where the pages are silent (each is also listed in the design not
   * outlier channels of a KV head [2NUM "The Real Problem: Outlier Channels", HARD "The Third
     Problem: Magnitude Outliers"]: the n_out channels with the largest mean magnitude |k_c| over all
     keys of that head seen so far (every sequence and token of the prefill), the lower channel first
-    on equal means; returned in ascending channel order.
+    on equal means; returned in ascending channel order;
+  * two-sided estimator [QJL "Surprising findings": signs on both sides estimate the cosine with a
+    bias]: per part, ||q_part|| * ||k_part|| / m_part * <sign(S q_part), sign(S k_part)> (the mean
+    sign agreement scaled by both norms, expectation ||q|| ||k|| (1 - 2 theta / pi)); the query
+    signs take sign(0) = +1 like the keys; the parts add as for the one-sided estimator;
+  * rotate-then-sign keys [1BIT "The 1-Bit Breakthrough", "But Wait. Don't the Small Dims
+    Overpower?"]: an orthogonal rotation R (m = d), key reconstructed as norm x signs scaled to the
+    key's norm, ||k|| sign(R k) / sqrt(d), dotted with the rotated query R q.
 """
 from __future__ import annotations
 
@@ -251,6 +258,49 @@ def estimator_scores(sq_in: np.ndarray, sq_out: np.ndarray, bits: np.ndarray, no
     return score
 
 
+def two_sided_scores(sq_in: np.ndarray, sq_out: np.ndarray, qn_in: float, qn_out: float, bits: np.ndarray,
+                     norms: np.ndarray) -> np.ndarray:
+    """Both sides quantized to signs, for every key of one KV head [QJL "Surprising findings"].
+
+    sq_in [m], sq_out [m_out]: the projected query, of which only the signs are used (sign(0) = +1);
+    qn_in, qn_out: the norms of the query's inlier and outlier parts; bits [n, W], norms [n, 2] fp16
+    from the key quantizer.  score = qn_in * ||k_in|| / m * <sign(S_in q_in), s_in> + qn_out *
+    ||k_out|| / m_out * <sign(S_out q_out), s_out>: the mean sign agreement of each part times both
+    norms, a biased estimate of <q, k> (expectation ||q|| ||k|| (1 - 2 theta / pi) per part).
+    """
+    m, m_out = sq_in.shape[0], sq_out.shape[0]
+    n = bits.shape[0]
+    qs_in = np.where(sq_in >= 0, 1.0, -1.0)
+    qs_out = np.where(sq_out >= 0, 1.0, -1.0)
+    score = np.zeros(n, dtype=np.float64)
+    for t0 in range(0, n, _SLICE):          # independent keys, evaluated a slice at a time
+        t1 = min(n, t0 + _SLICE)
+        signs = np.where(unpack_bits(bits[t0:t1], m + m_out), 1.0, -1.0)
+        n_in = norms[t0:t1, 0].astype(np.float64)
+        n_out = norms[t0:t1, 1].astype(np.float64)
+        s = qn_in * n_in / m * (signs[:, :m] @ qs_in)
+        if m_out:
+            s = s + qn_out * n_out / m_out * (signs[:, m:] @ qs_out)
+        score[t0:t1] = s
+    return score
+
+
+def rotate_sign_scores(q: np.ndarray, K: np.ndarray, R: np.ndarray) -> np.ndarray:
+    """Rotate-then-sign keys [1BIT "The 1-Bit Breakthrough": sign after a rotation; "But Wait. Don't
+    the Small Dims Overpower?": the norm is stored separately and the key is reconstructed as norm x
+    signs]: for keys K [n, d] and an orthogonal R [d, d], the reconstruction ||k|| sign(R k) / sqrt(d)
+    (scaled so that its norm is ||k||) dotted with the rotated query R q, in fp64 with the exact key
+    norms; sign(0) = +1."""
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    R = np.asarray(R, dtype=np.float64)
+    d = R.shape[1]
+    rq = R @ q
+    rk = K @ R.T
+    khat = np.linalg.norm(K, axis=1)[:, None] * np.where(rk >= 0, 1.0, -1.0) / math.sqrt(d)
+    return khat @ rq
+
+
 def softmax(z: np.ndarray) -> np.ndarray:
     """Two-pass softmax in fp64: subtract the max, exponentiate, normalise."""
     z = np.asarray(z, dtype=np.float64)
@@ -268,15 +318,19 @@ def attend(scores: np.ndarray, values: np.ndarray, sm_scale: float) -> np.ndarra
 def decode_attention(Q: np.ndarray, S_in: np.ndarray, S_out: np.ndarray, outlier_idx: np.ndarray,
                      bits: np.ndarray, norms: np.ndarray, N: int, *, codes=None, meta=None,
                      V_f32=None, nbits: int = 2, sm_scale: float | None = None,
-                     units=None) -> dict:
+                     units=None, estimator: str = "one_sided") -> dict:
     """One decode step for every sequence and query head.
 
     Q [B, Hq, d]; bits [B, Hkv, >=N, W]; norms [B, Hkv, >=N, 2]; values either as codes
     [B, Hkv, >=N, d*nbits/8] + meta [B, Hkv, >=N, 2] or unquantized V_f32 [B, Hkv, >=N, d].
     Query head hq reads KV head hq // (Hq/Hkv).  sm_scale defaults to 1/sqrt(d).
     `units` optionally restricts the work to a list of (b, hq) pairs (others stay NaN).
+    `estimator`: "one_sided" (the query unquantized, estimator_scores) or "two_sided" (the query
+    reduced to its signs as well, two_sided_scores).
     Returns out [B, Hq, d] and scores [B, Hq, N] (raw estimator scores, before sm_scale), fp64.
     """
+    if estimator not in ("one_sided", "two_sided"):
+        raise ValueError(f"unknown estimator {estimator!r}")
     B, Hq, d = Q.shape
     Hkv = bits.shape[1]
     g = Hq // Hkv
@@ -290,7 +344,13 @@ def decode_attention(Q: np.ndarray, S_in: np.ndarray, S_out: np.ndarray, outlier
         h = hq // g
         channels = outlier_idx[h] if outlier_idx.size else []
         sq_in, sq_out = project_query(Q[b, hq], S_in, S_out, channels)
-        s = estimator_scores(sq_in, sq_out, bits[b, h, :N], norms[b, h, :N])
+        if estimator == "one_sided":
+            s = estimator_scores(sq_in, sq_out, bits[b, h, :N], norms[b, h, :N])
+        else:
+            q = np.asarray(Q[b, hq], dtype=np.float64)
+            mask = outlier_mask(d, channels)
+            qn_in, qn_out = float(np.linalg.norm(q * (1.0 - mask))), float(np.linalg.norm(q * mask))
+            s = two_sided_scores(sq_in, sq_out, qn_in, qn_out, bits[b, h, :N], norms[b, h, :N])
         if (b, h) not in vcache:
             if V_f32 is not None:
                 vcache[(b, h)] = np.asarray(V_f32[b, h, :N], dtype=np.float64)

@@ -176,3 +176,10 @@ def values(w: Workload, T: int | None = None) -> np.ndarray:
 def gaussian(seed: int, shape, *key: int) -> np.ndarray:
     """Plain fp64 N(0, 1) draws for statistical tests (no storage rounding)."""
     return _rng(seed, 99, *key).standard_normal(shape)
+
+
+def random_rotation(seed: int, d: int, *key: int) -> np.ndarray:
+    """A random orthogonal d x d matrix (fp64): the QR factor of a Gaussian draw, column signs fixed
+    by the diagonal of R so that the draw is uniform over the orthogonal group."""
+    q, r = np.linalg.qr(_rng(seed, 98, *key).standard_normal((d, d)))
+    return q * np.sign(np.diag(r))[None, :]

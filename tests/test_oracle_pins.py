@@ -432,3 +432,97 @@ def test_select_outliers_invariances():
     for h in range(3):
         assert np.array_equal(oracle.select_outliers(K[:, :, h:h + 1], 5)[0], ref[h])
     assert all(np.all(np.diff(r) > 0) for r in ref)                      # ascending, distinct
+
+
+# ----------------------------------------------------------------------------- estimator variants
+
+def test_two_sided_scores_parallel_and_antiparallel_are_exact():
+    """Both sides as signs: a query parallel to the key agrees on every sign, so each part scores
+    ||q_part|| * ||k_part|| (stored fp16 norm) exactly; an antiparallel query disagrees everywhere."""
+    rng = np.random.default_rng(41)
+    d, m, ch = 32, 64, [3, 17]
+    S_in, S_out = rng.standard_normal((m, d)), rng.standard_normal((m, d))
+    k = rng.standard_normal(d)
+    kq = oracle.quantize_key_vectors(k[None, :], S_in, S_out, ch)
+    mask = oracle.outlier_mask(d, ch)
+    n16 = kq["norms"][0].astype(np.float64)
+    for c, sign in ((3.0, 1.0), (-0.5, -1.0)):
+        q = c * k
+        sq_in, sq_out = oracle.project_query(q, S_in, S_out, ch)
+        qn_in, qn_out = np.linalg.norm(q * (1 - mask)), np.linalg.norm(q * mask)
+        s = oracle.two_sided_scores(sq_in, sq_out, qn_in, qn_out, kq["bits"], kq["norms"])[0]
+        assert s == pytest.approx(sign * (qn_in * n16[0] + qn_out * n16[1]), rel=1e-14)
+
+
+def test_two_sided_scores_identity_projection_page_vectors():
+    """S = I tiled 4x (m = 32, d = 8) on the page's vectors: the sign agreement of q and k counted
+    by hand, times |q| |k|16 / 8."""
+    g = golden("page1_one_bit_keys.json")
+    q = np.array(g["query_on"])
+    S = tiled_identity(8, 32)
+    for kv in g["keys"].values():
+        kq = oracle.quantize_key_vectors(np.array([kv]), S, np.zeros((0, 8)), [])
+        sq_in, sq_out = oracle.project_query(q, S, np.zeros((0, 8)), [])
+        s = oracle.two_sided_scores(sq_in, sq_out, float(np.linalg.norm(q)), 0.0, kq["bits"], kq["norms"])[0]
+        agree = sum(1 if (a >= 0) == (b >= 0) else -1 for a, b in zip(q, kv))
+        assert s == pytest.approx(np.linalg.norm(q) * float(np.float16(np.linalg.norm(kv))) * agree / 8, rel=1e-13)
+    # the 'on' query agrees with 'cat' on all but dimension 5 (0.05 vs 0.04: same sign) -> all 8
+    assert sum((a >= 0) == (b >= 0) for a, b in zip(q, g["keys"]["cat"])) == 8
+
+
+def test_decode_attention_estimator_switch():
+    """The decode reference routes to the two scorers; an unknown estimator name is refused."""
+    rng = np.random.default_rng(5)
+    d, m, N = 16, 32, 9
+    S = rng.standard_normal((m, d))
+    K = rng.standard_normal((1, N, 1, d))
+    kq = oracle.quantize_keys(K, S, np.zeros((0, d)), np.zeros((1, 0), np.int32))
+    V = rng.standard_normal((1, 1, N, d))
+    Q = rng.standard_normal((1, 2, d))
+    one = oracle.decode_attention(Q, S, np.zeros((0, d)), np.zeros((1, 0), np.int32), kq["bits"], kq["norms"], N, V_f32=V)
+    two = oracle.decode_attention(Q, S, np.zeros((0, d)), np.zeros((1, 0), np.int32), kq["bits"], kq["norms"], N, V_f32=V,
+                                  estimator="two_sided")
+    for hq in range(2):
+        sq_in, sq_out = oracle.project_query(Q[0, hq], S, np.zeros((0, d)), [])
+        bits, norms = kq["bits"][0, 0], kq["norms"][0, 0]
+        assert np.array_equal(one["scores"][0, hq], oracle.estimator_scores(sq_in, sq_out, bits, norms))
+        assert np.array_equal(two["scores"][0, hq],
+                              oracle.two_sided_scores(sq_in, sq_out, np.linalg.norm(Q[0, hq]), 0.0, bits, norms))
+    with pytest.raises(ValueError):
+        oracle.decode_attention(Q, S, np.zeros((0, d)), np.zeros((1, 0), np.int32), kq["bits"], kq["norms"], N,
+                                V_f32=V, estimator="cosine")
+
+
+def test_rotate_sign_identity_is_norm_times_signs():
+    """R = I: the page's reconstructed key, norm x signs scaled to the key's norm, dotted with q."""
+    g = golden("page1_one_bit_keys.json")
+    q = np.array(g["query_on"])
+    K = np.array(list(g["keys"].values()))
+    s = oracle.rotate_sign_scores(q, K, np.eye(8))
+    for i, kv in enumerate(K):
+        khat = np.linalg.norm(kv) * np.sign(kv) / math.sqrt(8)
+        assert np.linalg.norm(khat) == pytest.approx(np.linalg.norm(kv), rel=1e-15)
+        assert s[i] == pytest.approx(q @ khat, rel=1e-14)
+
+
+def test_rotate_sign_closed_forms():
+    """q = k scores ||k|| ||R k||_1 / sqrt(d); permuting or negating rows of R changes no score; and
+    the one-sided estimator with S = sqrt(2d/pi) R gives the same scores up to the fp16 key norm."""
+    rng = np.random.default_rng(8)
+    d = 64
+    R = si.random_rotation(3, d)
+    assert np.allclose(R @ R.T, np.eye(d), atol=1e-12)
+    K = rng.standard_normal((5, d))
+    q = rng.standard_normal(d)
+    s_kk = oracle.rotate_sign_scores(K[0], K[:1], R)[0]
+    assert s_kk == pytest.approx(np.linalg.norm(K[0]) * np.abs(R @ K[0]).sum() / math.sqrt(d), rel=1e-13)
+    # permuting and negating rows of R changes no score (the reconstruction's terms are reordered)
+    P = np.eye(d)[rng.permutation(d)] * np.where(rng.random(d) < 0.5, -1.0, 1.0)[:, None]
+    assert np.allclose(oracle.rotate_sign_scores(q, K, P @ R), oracle.rotate_sign_scores(q, K, R), rtol=1e-12)
+    S = math.sqrt(2 * d / math.pi) * R
+    kq = oracle.quantize_key_vectors(K, S, np.zeros((0, d)), [])
+    sq_in, sq_out = oracle.project_query(q, S, np.zeros((0, d)), [])
+    one = oracle.estimator_scores(sq_in, sq_out, kq["bits"], kq["norms"])
+    ref = oracle.rotate_sign_scores(q, K, R)
+    scale = np.linalg.norm(K, axis=1) * np.abs(R @ q).sum() / math.sqrt(d)
+    assert np.all(np.abs(one - ref) <= 2 ** -11 * scale)

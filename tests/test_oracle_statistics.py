@@ -94,3 +94,30 @@ def test_two_sided_sign_estimator_is_biased_toward_the_angle():
     est = np.mean([oracle.two_sided_estimate(q, k, si.gaussian(800, (256, D), r)) for r in range(400)])
     assert est == pytest.approx(1 - 2 * theta / math.pi, abs=0.01)
     assert abs(est - math.cos(theta)) > 0.1
+
+
+def test_two_sided_decode_scores_average_to_the_angle_term():
+    """The decode-path two-sided scorer (with the outlier split) averages, over Gaussian JL draws, to
+    sum over parts of ||q_part|| ||k_part||16 (1 - 2 theta_part / pi)."""
+    q, k = _pair(31, 0.6)
+    ch = [5, 77, 100]
+    mask = oracle.outlier_mask(D, ch)
+    qi, qo, ki, ko = q * (1 - mask), q * mask, k * (1 - mask), k * mask
+
+    def angle(a, b):
+        return math.acos(float(a @ b) / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+    vals = []
+    for r in range(300):
+        S_in, S_out = si.gaussian(900, (256, D), r, 0), si.gaussian(900, (256, D), r, 1)
+        kq = oracle.quantize_key_vectors(k[None, :], S_in, S_out, ch)
+        sq_in, sq_out = oracle.project_query(q, S_in, S_out, ch)
+        vals.append(oracle.two_sided_scores(sq_in, sq_out, np.linalg.norm(qi), np.linalg.norm(qo), kq["bits"],
+                                            kq["norms"])[0])
+    n16 = kq["norms"][0].astype(np.float64)
+    expect = (np.linalg.norm(qi) * n16[0] * (1 - 2 * angle(qi, ki) / math.pi)
+              + np.linalg.norm(qo) * n16[1] * (1 - 2 * angle(qo, ko) / math.pi))
+    scale = np.linalg.norm(qi) * n16[0] + np.linalg.norm(qo) * n16[1]
+    assert np.mean(vals) == pytest.approx(expect, abs=0.01 * scale)
+    # and not the inner product: the bias of the two-sided estimate is visible
+    assert abs(np.mean(vals) - q @ k) > 0.05 * scale
