@@ -26,6 +26,8 @@ QJL_BF16 = 0
 QJL_F32 = 1
 QJL_V_CODES = 0
 QJL_V_F32 = 1
+QJL_EST_ONE_SIDED = 0
+QJL_EST_TWO_SIDED = 1
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python bit_kv_cache_qjl_amd/build.py`")
@@ -51,10 +53,10 @@ lib.qjl_decode_workspace_size.restype = _sz
 lib.qjl_decode_workspace_size.argtypes = [_i, _i, _i, _i, _i64, _i, _i, _i]
 lib.qjl_decode_attention.restype = _i
 lib.qjl_decode_attention.argtypes = [_p, _i, _i, _i, _i, _i, _i64, _p, _i, _p, _i, _p, _i, _p, _p, _i64,
-                                     _i, _p, _p, _p, _i, _f, _p, _p, _i, _p, _sz, _p]
+                                     _i, _p, _p, _p, _i, _f, _i, _p, _p, _i, _p, _sz, _p]
 lib.qjl_decode_step.restype = _i
 lib.qjl_decode_step.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _p, _i, _p, _i, _p, _i,
-                                _p, _p, _p, _p, _i64, _i, _f, _p, _p, _i, _p, _sz, _p]
+                                _p, _p, _p, _p, _i64, _i, _f, _i, _p, _p, _i, _p, _sz, _p]
 lib.qjl_select_outliers_workspace_size.restype = _sz
 lib.qjl_select_outliers_workspace_size.argtypes = [_i, _i64, _i, _i]
 lib.qjl_select_outliers.restype = _i
@@ -184,9 +186,10 @@ def decode_workspace_size(B: int, Hq: int, Hkv: int, N: int, m: int, m_out: int,
 
 
 def decode_attention(Q, S_in, S_out, outlier_idx, bits, norms, N: int, out, *, codes=None, meta=None,
-                     V_f32=None, nbits: int = 2, sm_scale: float = 0.0, scores_dbg=None, nsplit: int = 0,
-                     workspace=None, stream=None) -> None:
-    """qjl_decode_attention on torch tensors.  Q [B, Hq, d] contiguous; out [B, Hq, d] fp32."""
+                     V_f32=None, nbits: int = 2, sm_scale: float = 0.0, estimator: int = 0, scores_dbg=None,
+                     nsplit: int = 0, workspace=None, stream=None) -> None:
+    """qjl_decode_attention on torch tensors.  Q [B, Hq, d] contiguous; out [B, Hq, d] fp32.
+    estimator: QJL_EST_ONE_SIDED (0) or QJL_EST_TWO_SIDED (1)."""
     B, Hq, d = Q.shape
     if not Q.is_contiguous():
         raise ValueError("Q must be contiguous [B, Hq, d]")
@@ -204,13 +207,13 @@ def decode_attention(Q, S_in, S_out, outlier_idx, bits, norms, N: int, out, *, c
     _check(lib.qjl_decode_attention(_ptr(Q), _dtype_code(Q), B, Hq, Hkv, d, N, _ptr(S_in), m,
                                     _ptr(S_out) if m_out else 0, m_out, _ptr(outlier_idx) if n_out else 0, n_out,
                                     _ptr(bits), _ptr(norms), bits.shape[2], vmode, _ptr(codes), _ptr(meta),
-                                    _ptr(V_f32), nbits, sm_scale, _ptr(out), _ptr(scores_dbg), nsplit,
+                                    _ptr(V_f32), nbits, sm_scale, estimator, _ptr(out), _ptr(scores_dbg), nsplit,
                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream)), "qjl_decode_attention")
 
 
 def decode_step(Q, K_new, V_new, S_in, S_out, outlier_idx, cache: Cache, N: int, out, *, sm_scale: float = 0.0,
-                scores_dbg=None, nsplit: int = 0, workspace=None, stream=None) -> None:
+                estimator: int = 0, scores_dbg=None, nsplit: int = 0, workspace=None, stream=None) -> None:
     """qjl_decode_step on torch tensors: append the new token (K_new, V_new [B, 1, Hkv, d], d contiguous)
     at position N - 1 of the cache, then decode Q [B, Hq, d] over the first N positions into out."""
     B, Hq, d = Q.shape
@@ -235,7 +238,7 @@ def decode_step(Q, K_new, V_new, S_in, S_out, outlier_idx, cache: Cache, N: int,
                                K_new.stride(0), K_new.stride(2), V_new.stride(0), V_new.stride(2),
                                _ptr(S_in), m, _ptr(S_out) if m_out else 0, m_out,
                                _ptr(outlier_idx) if n_out else 0, n_out, _ptr(cache.bits), _ptr(cache.norms),
-                               _ptr(cache.codes), _ptr(cache.meta), cache.Ncap, cache.nbits, sm_scale, _ptr(out),
+                               _ptr(cache.codes), _ptr(cache.meta), cache.Ncap, cache.nbits, sm_scale, estimator, _ptr(out),
                                _ptr(scores_dbg), nsplit, _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)), "qjl_decode_step")
 

@@ -254,8 +254,11 @@ WsLayout ws_layout(int B, int Hq, int d, int m, int m_out, int ns) {
 // Checks shared by the decode entry points (everything but the value arguments and the pointers),
 // then the launch descriptor.
 int prepare_decode(qjl::DecodeArgs& a, int qdt, int B, int Hq, int Hkv, int d, int64_t N, int m, int m_out, int n_out,
-                   int64_t Ncap, int vmode, int nbits, float sm_scale, int nsplit, void* workspace, size_t ws_bytes) {
+                   int64_t Ncap, int vmode, int nbits, float sm_scale, int estimator, int nsplit, void* workspace,
+                   size_t ws_bytes) {
     if (qdt != QJL_BF16 && qdt != QJL_F32) return fail(QJL_ERR_INVALID_ARG, "qdt=%d is not a qjl_dtype", qdt);
+    if (estimator != QJL_EST_ONE_SIDED && estimator != QJL_EST_TWO_SIDED)
+        return fail(QJL_ERR_INVALID_ARG, "estimator=%d is not a qjl_estimator", estimator);
     if (vmode != QJL_V_CODES && vmode != QJL_V_F32) return fail(QJL_ERR_INVALID_ARG, "vmode=%d is not a qjl_vmode", vmode);
     if (B < 0 || Hq <= 0 || Hkv <= 0 || N < 0 || Ncap < 0)
         return fail(QJL_ERR_INVALID_ARG, "bad sizes B=%d Hq=%d Hkv=%d N=%lld Ncap=%lld", B, Hq, Hkv, (long long)N, (long long)Ncap);
@@ -296,6 +299,7 @@ int prepare_decode(qjl::DecodeArgs& a, int qdt, int B, int Hq, int Hkv, int d, i
     a.chunk = qjl::decode_chunk(N, ns);
     const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)d);
     a.z_scale = scale * qjl::kLog2e;
+    a.estimator = estimator;
     return QJL_OK;
 }
 
@@ -318,11 +322,11 @@ size_t qjl_decode_workspace_size(int B, int Hq, int Hkv, int d, int64_t N, int m
 int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, int64_t N, const void* S_in, int m,
                          const void* S_out, int m_out, const int32_t* outlier_idx, int n_out, const uint32_t* bits,
                          const uint16_t* norms, int64_t Ncap, int vmode, const uint32_t* codes, const uint16_t* meta,
-                         const float* V_f32, int nbits, float sm_scale, float* out, float* scores_dbg, int nsplit,
-                         void* workspace, size_t ws_bytes, hipStream_t stream) {
+                         const float* V_f32, int nbits, float sm_scale, int estimator, float* out, float* scores_dbg,
+                         int nsplit, void* workspace, size_t ws_bytes, hipStream_t stream) {
     g_last_error.clear();
     qjl::DecodeArgs a{};
-    int st = prepare_decode(a, qdt, B, Hq, Hkv, d, N, m, m_out, n_out, Ncap, vmode, nbits, sm_scale, nsplit, workspace,
+    int st = prepare_decode(a, qdt, B, Hq, Hkv, d, N, m, m_out, n_out, Ncap, vmode, nbits, sm_scale, estimator, nsplit, workspace,
                             ws_bytes);
     if (st) return st;
     if (B == 0) return QJL_OK;
@@ -352,12 +356,12 @@ int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, 
 int qjl_decode_step(const void* Q, const void* K_new, const void* V_new, int dt, int B, int Hq, int Hkv, int d, int64_t N,
                     int64_t sK_b, int64_t sK_h, int64_t sV_b, int64_t sV_h, const void* S_in, int m, const void* S_out,
                     int m_out, const int32_t* outlier_idx, int n_out, uint32_t* bits, uint16_t* norms, uint32_t* codes,
-                    uint16_t* meta, int64_t Ncap, int nbits, float sm_scale, float* out, float* scores_dbg, int nsplit,
-                    void* workspace, size_t ws_bytes, hipStream_t stream) {
+                    uint16_t* meta, int64_t Ncap, int nbits, float sm_scale, int estimator, float* out, float* scores_dbg,
+                    int nsplit, void* workspace, size_t ws_bytes, hipStream_t stream) {
     g_last_error.clear();
     if (N < 1) return fail(QJL_ERR_INVALID_ARG, "N=%lld: a decode step appends one token, so N >= 1", (long long)N);
     qjl::DecodeArgs a{};
-    int st = prepare_decode(a, dt, B, Hq, Hkv, d, N, m, m_out, n_out, Ncap, QJL_V_CODES, nbits, sm_scale, nsplit, workspace,
+    int st = prepare_decode(a, dt, B, Hq, Hkv, d, N, m, m_out, n_out, Ncap, QJL_V_CODES, nbits, sm_scale, estimator, nsplit, workspace,
                             ws_bytes);
     if (st) return st;
     if (B == 0) return QJL_OK;
@@ -404,7 +408,7 @@ int qjl_decode_step(const void* Q, const void* K_new, const void* V_new, int dt,
     st = qjl_quantize_values(V_new, dt, B, 1, Hkv, d, sV_b, 0, sV_h, nbits, codes, meta, Ncap, N - 1, stream);
     if (st) return st;
     return qjl_decode_attention(Q, dt, B, Hq, Hkv, d, N, S_in, m, S_out, m_out, outlier_idx, n_out, bits, norms, Ncap,
-                                QJL_V_CODES, codes, meta, nullptr, nbits, sm_scale, out, scores_dbg, nsplit, workspace,
+                                QJL_V_CODES, codes, meta, nullptr, nbits, sm_scale, estimator, out, scores_dbg, nsplit, workspace,
                                 ws_bytes, stream);
 }
 

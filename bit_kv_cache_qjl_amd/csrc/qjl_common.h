@@ -209,6 +209,7 @@ struct DecodeArgs {
     int nbits;                        // value code width (2 or 4 on the matrix-core path)
     int64_t chunk;                    // tokens per split (multiple of the tile)
     float z_scale;                    // sm_scale * log2(e)
+    int estimator;                    // 0: one-sided (query unquantized); 1: two-sided (query signs)
     size_t ws_need;                   // workspace bytes these sizes need (host-side check)
 };
 

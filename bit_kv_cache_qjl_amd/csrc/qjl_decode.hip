@@ -8,7 +8,9 @@
 //
 // Kernels
 //   qproj   one workgroup per (sequence, query head): Sq = S q (fp32) pre-multiplied by
-//           sqrt(pi/2)/m (inlier part) and sqrt(pi/2)/m_out (outlier part).
+//           sqrt(pi/2)/m (inlier part) and sqrt(pi/2)/m_out (outlier part); for the two-sided
+//           estimator (both sides as signs: "Surprising findings" of the QJL summary) sign(Sq) times
+//           |q_in|/m and |q_out|/m_out instead.
 //   decode  one workgroup (8 waves) per (sequence, KV head, query head, context chunk).  The
 //           projected query is expanded in LDS into byte tables: entry [p][beta] is the signed sum of
 //           the 8 Sq values of byte position p under sign pattern beta, so one LDS read replaces
@@ -58,14 +60,27 @@ __global__ __launch_bounds__(256) void qproj_kernel(DecodeArgs a) {
     const QT* Sin = static_cast<const QT*>(a.S_in);
     const QT* Sout = static_cast<const QT*>(a.S_out);
     float* dst = a.sq + (size_t)bh * (a.m + a.m_out);
-    const float c_in = kSqrtHalfPi / (float)a.m;
-    for (int j = tid; j < a.m; j += 256) dst[j] = row_dot(Sin + (size_t)j * kD, qin) * c_in;
+    // one-sided: Sq scaled by sqrt(pi/2)/m; two-sided: only the sign of each projection is kept, scaled
+    // by the norm of the query part over m (sign(0) = +1)
+    const bool two = a.estimator != 0;
+    float qn_in = 0.f, qn_out = 0.f;
+    if (two) {
+        for (int c = 0; c < kD; ++c) qn_in = fmaf(qin[c], qin[c], qn_in);
+        for (int i = 0; i < a.n_out; ++i) qn_out = fmaf(qo[i], qo[i], qn_out);
+        qn_in = sqrtf(qn_in);
+        qn_out = sqrtf(qn_out);
+    }
+    const float c_in = (two ? qn_in : kSqrtHalfPi) / (float)a.m;
+    for (int j = tid; j < a.m; j += 256) {
+        const float p = row_dot(Sin + (size_t)j * kD, qin);
+        dst[j] = two ? (p >= 0.f ? c_in : -c_in) : p * c_in;
+    }
     if (a.m_out) {
-        const float c_out = kSqrtHalfPi / (float)a.m_out;
+        const float c_out = (two ? qn_out : kSqrtHalfPi) / (float)a.m_out;
         for (int j = tid; j < a.m_out; j += 256) {
             float acc = 0.f;
             for (int i = 0; i < a.n_out; ++i) acc = fmaf(load_elem<QT>(Sout, (size_t)j * kD + so[i]), qo[i], acc);
-            dst[a.m + j] = acc * c_out;
+            dst[a.m + j] = two ? (acc >= 0.f ? c_out : -c_out) : acc * c_out;
         }
     }
 }

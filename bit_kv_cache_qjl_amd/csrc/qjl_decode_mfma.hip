@@ -81,7 +81,8 @@ __device__ __forceinline__ v8i_t sign_planes(uint32_t x, uint32_t m8, uint32_t o
 
 // ---------------------------------------------------------------------------- query operand
 // The matrix-core operand of one query head, built by one wave from the head's projections
-// x_j = 2 z_scale sqrt(pi/2)/m (S q)_j (inlier j < m, then outlier, natural order, in LDS): the
+// x_j = 2 z_scale sqrt(pi/2)/m (S q)_j (inlier j < m, then outlier, natural order, in LDS; for the
+// two-sided estimator x_j = 2 z_scale |q_part|/m sign((S q)_j) instead): the
 // A-operand bytes in the order the decode kernel loads them, [K block kb][piece][lane group ga][32
 // bytes] (byte ea of lane group ga is K index k = 16 ga + ea % 16 + 64 (ea / 16) of the instruction,
 // and K index k pairs with bit 4n + i, n = (k % 32) % 8, i = (k % 32) / 8, of the sign word that B
@@ -175,14 +176,26 @@ __global__ __launch_bounds__(256) void qproj_f32_kernel(DecodeArgs a, int win4, 
     __syncthreads();
     const float* Sin = static_cast<const float*>(a.S_in);
     const float* Sout = static_cast<const float*>(a.S_out);
-    const float c_in = 2.f * a.z_scale * kSqrtHalfPi / (float)a.m;
-    for (int j = tid; j < a.m; j += 256) xs[j] = row_dot(Sin + (size_t)j * kD, qin) * c_in;
+    // two-sided estimator: the sign of each projection times the norm of the query part (sign(0) = +1)
+    const bool two = a.estimator != 0;
+    float qn_in = 0.f, qn_out = 0.f;
+    if (two) {
+        for (int c = 0; c < kD; ++c) qn_in = fmaf(qin[c], qin[c], qn_in);
+        for (int i = 0; i < a.n_out; ++i) qn_out = fmaf(qo[i], qo[i], qn_out);
+        qn_in = sqrtf(qn_in);
+        qn_out = sqrtf(qn_out);
+    }
+    const float c_in = 2.f * a.z_scale * (two ? qn_in : kSqrtHalfPi) / (float)a.m;
+    for (int j = tid; j < a.m; j += 256) {
+        const float p = row_dot(Sin + (size_t)j * kD, qin);
+        xs[j] = two ? (p >= 0.f ? c_in : -c_in) : p * c_in;
+    }
     if (a.m_out) {
-        const float c_out = 2.f * a.z_scale * kSqrtHalfPi / (float)a.m_out;
+        const float c_out = 2.f * a.z_scale * (two ? qn_out : kSqrtHalfPi) / (float)a.m_out;
         for (int j = tid; j < a.m_out; j += 256) {
             float acc = 0.f;
             for (int i = 0; i < a.n_out; ++i) acc = fmaf(Sout[(size_t)j * kD + so[i]], qo[i], acc);
-            xs[a.m + j] = acc * c_out;
+            xs[a.m + j] = two ? (acc >= 0.f ? c_out : -c_out) : acc * c_out;
         }
     }
     __syncthreads();
@@ -208,6 +221,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs 
     __shared__ __attribute__((aligned(16))) uint16_t vout[16 * kVRow];   // vectors on the outlier channels only
     __shared__ float xs[16 * kXPitch];
     __shared__ uint32_t s_mask[4];
+    __shared__ float s_qn[16][2];                                         // vector norms (two-sided)
     typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -292,6 +306,8 @@ __global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs 
 
     const float c_in = 2.f * a.z_scale * kSqrtHalfPi / (float)a.m;
     const float c_out = a.m_out ? 2.f * a.z_scale * kSqrtHalfPi / (float)a.m_out : 0.f;
+    const float c2_in = 2.f * a.z_scale / (float)a.m;
+    const float c2_out = a.m_out ? 2.f * a.z_scale / (float)a.m_out : 0.f;
     for (int c0 = 0; c0 < ncol; c0 += 16) {
         const bool key_pass = APPEND && c0 == 0;
         // ---- stage 16 vectors, split at the outlier channels
@@ -303,12 +319,16 @@ __global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs 
             split_key8(xv, om, xi, xo, ss_in, ss_out);
             *reinterpret_cast<uint4*>(vin + sv * kVRow + 8 * cg) = xi;
             *reinterpret_cast<uint4*>(vout + sv * kVRow + 8 * cg) = xo;
-            if (key_pass) {
-                // the key is vector 0: lanes 0..15 of wave 0, one DPP row (the sums of the other rows
-                // belong to query vectors and are not used)
+            if (key_pass || a.estimator) {
+                // squared norms of each vector's two parts: one DPP row of 16 lanes per vector
                 ss_in = row16_sum(ss_in);
                 ss_out = row16_sum(ss_out);
-                if (tid == 0) reinterpret_cast<uint32_t*>(ap.norms)[(size_t)unit * a.Ncap + ap.pos] = norm_pair(ss_in, ss_out);
+            }
+            // the key is vector 0: lanes 0..15 of wave 0
+            if (key_pass && tid == 0) reinterpret_cast<uint32_t*>(ap.norms)[(size_t)unit * a.Ncap + ap.pos] = norm_pair(ss_in, ss_out);
+            if (a.estimator && cg == 0) {
+                s_qn[sv][0] = sqrtf(ss_in);
+                s_qn[sv][1] = sqrtf(ss_out);
             }
         }
         __syncthreads();
@@ -332,7 +352,12 @@ __global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs 
                 const int j = (inl ? 32 * wn : a.m + 32 * (wn - Win)) + 16 * hf + (lane & 15);
                 const float cs = inl ? c_in : c_out;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) xs[(4 * (lane >> 4) + i) * kXPitch + j] = acc[i] * cs;
+                for (int i = 0; i < 4; ++i) {
+                    const int vec = 4 * (lane >> 4) + i;
+                    // two-sided estimator: the projection's sign times the norm of the query part
+                    const float t = a.estimator ? s_qn[vec][inl ? 0 : 1] * (inl ? c2_in : c2_out) : 0.f;
+                    xs[vec * kXPitch + j] = a.estimator ? (acc[i] >= 0.f ? t : -t) : acc[i] * cs;
+                }
             }
             if (key_pass && lane == 0) ap.bits[((size_t)unit * a.Ncap + ap.pos) * W + bits_slot(wn, Win, Wout)] = word;
         }

@@ -79,6 +79,13 @@ typedef enum {
     QJL_V_F32 = 1     /* values kept unquantized, fp32 [B][Hkv][Ncap][d]                       */
 } qjl_vmode;
 
+/* The inner-product estimate the decode scores with (the key sketch is the same for both). */
+typedef enum {
+    QJL_EST_ONE_SIDED = 0,  /* query unquantized: sqrt(pi/2)/m |k| <S q, sign(S k)>, unbiased     */
+    QJL_EST_TWO_SIDED = 1   /* query reduced to its signs as well: |q| |k| / m <sign(S q), sign(S k)>
+                               per part, a biased estimate (expectation |q||k|(1 - 2 theta/pi))  */
+} qjl_estimator;
+
 /*
  * qjl_quantize_keys - sketch T new keys per (sequence, KV head) into the cache at positions
  * [t0, t0 + T).
@@ -156,6 +163,14 @@ size_t qjl_decode_workspace_size(int B, int Hq, int Hkv, int d, int64_t N, int m
  *   vmode       QJL_V_CODES: codes + meta (nbits 2, or 4 with m + m_out <= 512), V_f32 ignored;
  *               QJL_V_F32: V_f32 [B][Hkv][Ncap][d] fp32, codes/meta ignored.
  *   sm_scale    softmax scale; <= 0 selects 1/sqrt(d).
+ *   estimator   a qjl_estimator.  QJL_EST_TWO_SIDED is the variant the QJL summary contrasts with the
+ *               one-sided estimator ("Surprising findings": quantizing both sides gives a biased
+ *               estimate of the cosine): s_t = |q_in| n_in / m <sign(Sq_in), s_in> + |q_out| n_out /
+ *               m_out <sign(Sq_out), s_out>, with sign(0) = +1 on the query side as on the key side.
+ *               Rotate-then-sign keys ("Your Brain Already Runs on 1-Bit Keys", "The 1-Bit
+ *               Breakthrough": sign after a rotation, key = norm x signs) are the one-sided estimator
+ *               with m = d, m_out = 0 and S_in = sqrt(2d/pi) R for an orthogonal R: the score is then
+ *               <R q, |k| sign(R k) / sqrt(d)>.
  *   out         fp32 [B][Hq][d].  N == 0 writes zeros.
  *   scores_dbg  optional fp32 [B][Hq][N] receiving the raw estimator scores s_t (NULL to skip).
  *   nsplit      number of context chunks per (b, KV head) merged by log-sum-exp (<= 0: auto).
@@ -168,7 +183,7 @@ int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, 
                          const int32_t* outlier_idx, int n_out,
                          const uint32_t* bits, const uint16_t* norms, int64_t Ncap,
                          int vmode, const uint32_t* codes, const uint16_t* meta, const float* V_f32,
-                         int nbits, float sm_scale, float* out, float* scores_dbg, int nsplit,
+                         int nbits, float sm_scale, int estimator, float* out, float* scores_dbg, int nsplit,
                          void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
@@ -189,7 +204,8 @@ int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, 
  *   bits, norms, codes, meta  the cache (layout at the top) of capacity Ncap >= N; nbits 2 or 4 (as
  *               for qjl_decode_attention).
  *   N           context length after the append (N >= 1).
- *   sm_scale, out, scores_dbg, nsplit, workspace  as for qjl_decode_attention (same workspace size).
+ *   sm_scale, estimator, out, scores_dbg, nsplit, workspace  as for qjl_decode_attention (same
+ *               workspace size).
  * Every argument is checked before anything is enqueued.
  */
 int qjl_decode_step(const void* Q, const void* K_new, const void* V_new, int dt, int B, int Hq, int Hkv, int d,
@@ -197,7 +213,7 @@ int qjl_decode_step(const void* Q, const void* K_new, const void* V_new, int dt,
                     const void* S_in, int m, const void* S_out, int m_out,
                     const int32_t* outlier_idx, int n_out,
                     uint32_t* bits, uint16_t* norms, uint32_t* codes, uint16_t* meta, int64_t Ncap, int nbits,
-                    float sm_scale, float* out, float* scores_dbg, int nsplit,
+                    float sm_scale, int estimator, float* out, float* scores_dbg, int nsplit,
                     void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*

@@ -109,7 +109,26 @@ def score_tolerance(sq_in, sq_out, norms, m, m_out):
     return 1e-3 * math.sqrt(math.pi / 2) * scale
 
 
-def run_decode(qjl, w, Q, S_in, S_out, oidx, cache_np: dict, N: int, *, nsplit=0, with_scores=True, V_f32=None):
+def two_sided_tolerance(q, S_in, S_out, channels, norms, m, m_out):
+    """1e-3 relative to the two-sided estimator's magnitude scale |q_in| n_in + |q_out| n_out, plus, for
+    every query projection small enough that its sign may come out differently in the kernel's fp32
+    sums (|S_j q| <= 1e-4 sum_c |S_jc q_c|), the full swing of that sign, 2 |q_part| n_part / m_part."""
+    q = np.asarray(q, dtype=np.float64)
+    mask = oracle.outlier_mask(q.shape[0], channels)
+    qi, qo = q * (1.0 - mask), q * mask
+    n_in = norms[:, 0].astype(np.float64)
+    n_out = norms[:, 1].astype(np.float64)
+    tol = 1e-3 * (np.linalg.norm(qi) * n_in + np.linalg.norm(qo) * n_out)
+    amb_in = int(np.sum(np.abs(S_in @ qi) <= 1e-4 * (np.abs(S_in) @ np.abs(qi))))
+    tol = tol + 2.0 * amb_in * np.linalg.norm(qi) * n_in / m
+    if m_out:
+        amb_out = int(np.sum(np.abs(S_out @ qo) <= 1e-4 * (np.abs(S_out) @ np.abs(qo))))
+        tol = tol + 2.0 * amb_out * np.linalg.norm(qo) * n_out / m_out
+    return tol
+
+
+def run_decode(qjl, w, Q, S_in, S_out, oidx, cache_np: dict, N: int, *, nsplit=0, with_scores=True, V_f32=None,
+               estimator=0):
     """Upload an oracle-built cache, run the library decode, return (out, scores) as numpy."""
     torch = torch_mod()
     B, Hq, d = Q.shape
@@ -126,16 +145,17 @@ def run_decode(qjl, w, Q, S_in, S_out, oidx, cache_np: dict, N: int, *, nsplit=0
         kw["meta"] = torch.from_numpy(cache_np["meta"]).cuda()
     qjl.decode_attention(to_dev(Q, w.dtype), to_dev(S_in, w.dtype), to_dev(S_out, w.dtype) if w.m_out else None,
                          torch.from_numpy(oidx).cuda() if w.n_out else None, bits, norms, N, out,
-                         nbits=w.nbits, scores_dbg=scores, nsplit=nsplit, **kw)
+                         nbits=w.nbits, scores_dbg=scores, nsplit=nsplit, estimator=estimator, **kw)
     torch.cuda.synchronize()
     return out.cpu().numpy(), (scores.cpu().numpy()[:, :, :N] if with_scores else None)
 
 
-def check_decode(w, Q, S_in, S_out, oidx, cache_np, N, out_gpu, scores_gpu, units, V_f32=None, what=""):
+def check_decode(w, Q, S_in, S_out, oidx, cache_np, N, out_gpu, scores_gpu, units, V_f32=None, what="",
+                 estimator="one_sided"):
     """Compare sampled (b, hq) outputs (2e-3 max-abs) and scores (1e-3 of the estimator scale)."""
     ref = oracle.decode_attention(Q, S_in, S_out, oidx, cache_np["bits"], cache_np["norms"], N,
                                   codes=cache_np.get("codes"), meta=cache_np.get("meta"), V_f32=V_f32,
-                                  nbits=w.nbits, units=units)
+                                  nbits=w.nbits, units=units, estimator=estimator)
     worst_o, worst_s = 0.0, 0.0
     g = w.Hq // w.Hkv
     for b, hq in units:
@@ -144,8 +164,12 @@ def check_decode(w, Q, S_in, S_out, oidx, cache_np, N, out_gpu, scores_gpu, unit
         worst_o = max(worst_o, float(err))
         assert err <= 2e-3, f"{what} out (b={b}, hq={hq}) max-abs {err:.3g} > 2e-3"
         if scores_gpu is not None and N:
-            sq_in, sq_out = oracle.project_query(Q[b, hq], S_in, S_out, oidx[h] if oidx.size else [])
-            tol = score_tolerance(sq_in, sq_out, cache_np["norms"][b, h, :N], w.m, w.m_out)
+            channels = oidx[h] if oidx.size else []
+            if estimator == "one_sided":
+                sq_in, sq_out = oracle.project_query(Q[b, hq], S_in, S_out, channels)
+                tol = score_tolerance(sq_in, sq_out, cache_np["norms"][b, h, :N], w.m, w.m_out)
+            else:
+                tol = two_sided_tolerance(Q[b, hq], S_in, S_out, channels, cache_np["norms"][b, h, :N], w.m, w.m_out)
             ds = np.abs(scores_gpu[b, hq] - ref["scores"][b, hq])
             ratio = float((ds / tol).max())
             worst_s = max(worst_s, ratio)

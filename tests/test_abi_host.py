@@ -94,7 +94,7 @@ def test_quantize_values_rejects(kw, status):
 def decode_call(ws_bytes=None, **kw):
     a = dict(Q=FAKE, qdt=0, B=2, Hq=8, Hkv=2, d=128, N=1000, S_in=FAKE, m=256, S_out=FAKE, m_out=256, oidx=FAKE,
              n_out=3, bits=FAKE, norms=FAKE, Ncap=1024, vmode=0, codes=FAKE, meta=FAKE, V_f32=0, nbits=2,
-             sm_scale=0.0, out=FAKE, scores=0, nsplit=0, ws=FAKE, ws_bytes=0, stream=0)
+             sm_scale=0.0, estimator=0, out=FAKE, scores=0, nsplit=0, ws=FAKE, ws_bytes=0, stream=0)
     a.update(kw)
     if ws_bytes is None:
         a["ws_bytes"] = qjl.lib.qjl_decode_workspace_size(a["B"], a["Hq"], a["Hkv"], 128, a["N"], a["m"], a["m_out"],
@@ -113,6 +113,8 @@ def decode_call(ws_bytes=None, **kw):
     (dict(nbits=4, m=512, m_out=512), qjl.QJL_ERR_UNSUPPORTED),   # 4-bit codes: matrix-core shapes only
     (dict(vmode=1), qjl.QJL_ERR_INVALID_ARG),          # fp32 values but V_f32 is null
     (dict(vmode=7), qjl.QJL_ERR_INVALID_ARG),
+    (dict(estimator=2), qjl.QJL_ERR_INVALID_ARG),
+    (dict(estimator=-1), qjl.QJL_ERR_INVALID_ARG),
     (dict(out=MIS), qjl.QJL_ERR_MISALIGNED),
     (dict(scores=MIS), qjl.QJL_ERR_MISALIGNED),
     (dict(nsplit=5000, ws_bytes=1 << 30), qjl.QJL_ERR_UNSUPPORTED),
@@ -147,8 +149,8 @@ def test_timer_api():
 def step_call(ws_bytes=None, **kw):
     a = dict(Q=FAKE, K_new=FAKE, V_new=FAKE, dt=0, B=2, Hq=8, Hkv=2, d=128, N=1000, sK_b=2 * 128, sK_h=128,
              sV_b=2 * 128, sV_h=128, S_in=FAKE, m=256, S_out=FAKE, m_out=256, oidx=FAKE, n_out=3, bits=FAKE,
-             norms=FAKE, codes=FAKE, meta=FAKE, Ncap=1024, nbits=2, sm_scale=0.0, out=FAKE, scores=0, nsplit=0,
-             ws=FAKE, ws_bytes=0, stream=0)
+             norms=FAKE, codes=FAKE, meta=FAKE, Ncap=1024, nbits=2, sm_scale=0.0, estimator=0, out=FAKE, scores=0,
+             nsplit=0, ws=FAKE, ws_bytes=0, stream=0)
     a.update(kw)
     if ws_bytes is None:
         a["ws_bytes"] = qjl.lib.qjl_decode_workspace_size(a["B"], a["Hq"], a["Hkv"], 128, a["N"], a["m"], a["m_out"],
@@ -163,6 +165,7 @@ def step_call(ws_bytes=None, **kw):
     (dict(N=1025), qjl.QJL_ERR_INVALID_ARG),
     (dict(dt=3), qjl.QJL_ERR_INVALID_ARG),
     (dict(Hq=9), qjl.QJL_ERR_INVALID_ARG),
+    (dict(estimator=5), qjl.QJL_ERR_INVALID_ARG),
     (dict(nbits=3), qjl.QJL_ERR_UNSUPPORTED),
     (dict(m=256, m_out=128), qjl.QJL_ERR_UNSUPPORTED),
     (dict(K_new=0), qjl.QJL_ERR_INVALID_ARG),

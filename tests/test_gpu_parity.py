@@ -1,10 +1,12 @@
 """GPU <-> oracle parity at sizes the oracle finishes in seconds (several tiles plus a ragged tail).
 
-Bar (BASELINE the benchmark spec): sign bits and value codes bit-exact, except sign bits whose projection
+Bar: sign bits and value codes bit-exact, except sign bits whose projection
 magnitude is below 1e-5 |k| (counted and reported); norms within one fp16 ulp; scores within 1e-3 of
 the estimator's magnitude scale; attention outputs within 2e-3 max-abs.  Decode parity feeds both
 sides the same oracle-built cache.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -186,6 +188,67 @@ def test_decode_parity_four_bit_values(name, nsplit):
     out, scores = run_decode(qjl, w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, w.N, nsplit=nsplit)
     units = [(b, hq) for b in range(w.B) for hq in range(w.Hq)]
     check_decode(w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, w.N, out, scores, units, what=f"{name} 4-bit")
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama2_7b_decode", "llama3_8b_gqa_decode", "llama31_70b_gqa_decode",
+                                  "wide_sketch", "fp32_queries"])
+@pytest.mark.parametrize("nsplit", [0, 3])
+def test_decode_parity_two_sided(name, nsplit):
+    """The two-sided estimator (query reduced to its signs too) on every query-projection kernel: the
+    matrix-core prologue (bf16), the fp32 projection of the matrix-core path, and the VALU path
+    (fp32 values, and a sketch wider than the matrix-core shapes)."""
+    if name == "wide_sketch":
+        w = WIDE
+    elif name == "fp32_queries":
+        w = SCALED["llama3_8b_gqa_decode"].scaled(dtype="f32")
+    else:
+        w = SCALED[name]
+    log(f"[decode two-sided] {name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} nsplit={nsplit}")
+    x = inputs(w)
+    kq = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
+    cache = {"bits": kq["bits"], "norms": kq["norms"]}
+    V_f32 = None
+    if w.vmode == "codes":
+        cache.update(oracle.quantize_values(x["V"], w.nbits))
+    else:
+        V_f32 = np.ascontiguousarray(x["V"].transpose(0, 2, 1, 3))
+    out, scores = run_decode(qjl, w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, w.N, nsplit=nsplit, V_f32=V_f32,
+                             estimator=qjl.QJL_EST_TWO_SIDED)
+    units = [(b, hq) for b in range(w.B) for hq in range(w.Hq)]
+    check_decode(w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, w.N, out, scores, units, V_f32=V_f32,
+                 what=f"{name} two-sided", estimator="two_sided")
+
+
+def test_decode_rotate_then_sign():
+    """Rotate-then-sign keys: m = d = 128, no outlier copy, S_in = sqrt(2d/pi) R for an orthogonal R
+    (stored in bf16); the one-sided decode then scores <R q, |k| sign(R k)/sqrt(d)>, which the oracle
+    computes from R directly (R = S_in / sqrt(2d/pi), the exact rotation the kernels' signs come from)."""
+    w = SCALED["llama3_8b_gqa_decode"].scaled(m=128, m_out=0, n_out=0, N=700)
+    log(f"[decode rotate-then-sign] B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N}")
+    x = inputs(w)
+    alpha = math.sqrt(2 * w.d / math.pi)
+    S = si.round_bf16((alpha * si.random_rotation(17, w.d)).astype(np.float32))
+    R = S.astype(np.float64) / alpha
+    oidx = np.zeros((w.Hkv, 0), np.int32)
+    empty = np.zeros((0, w.d), np.float32)
+    kq = oracle.quantize_keys(x["K"], S, empty, oidx)
+    cache = {"bits": kq["bits"], "norms": kq["norms"], **oracle.quantize_values(x["V"], w.nbits)}
+    out, scores = run_decode(qjl, w, x["Q"], S, empty, oidx, cache, w.N)
+    g = w.Hq // w.Hkv
+    worst = 0.0
+    for b in range(w.B):
+        for hq in range(w.Hq):
+            h = hq // g
+            K = x["K"][b, :, h]
+            ref = oracle.rotate_sign_scores(x["Q"][b, hq], K, R)
+            # the kernels use the fp16-rounded key norm: tolerance 1e-3 of the scale plus the norm rounding
+            scale = np.linalg.norm(K, axis=1) * np.abs(R @ x["Q"][b, hq]).sum() / math.sqrt(w.d)
+            err = np.abs(scores[b, hq] - ref)
+            worst = max(worst, float((err / scale).max()))
+            assert np.all(err <= (1e-3 + 2 ** -11) * scale), f"rotate-then-sign scores (b={b}, hq={hq})"
+    log(f"  rotate-then-sign: worst score error {worst:.2e} of the scale")
+    units = [(b, hq) for b in range(w.B) for hq in range(w.Hq)]
+    check_decode(w, x["Q"], S, empty, oidx, cache, w.N, out, scores, units, what="rotate-then-sign")
 
 
 @pytest.mark.parametrize("N", [0, 1, 511, 513])

@@ -86,14 +86,14 @@ def check_row(w, cache, kq, vq, pos: int, Ncap: int, what: str):
     return same
 
 
-def run_step(w, x, cache, N, *, nsplit=0, scores=None, ws=None):
+def run_step(w, x, cache, N, *, nsplit=0, scores=None, ws=None, estimator=0):
     B = w.B
     Kd, Vd = to_dev(x["K"], w.dtype), to_dev(x["V"], w.dtype)
     out = torch.full((B, w.Hq, w.d), float("nan"), dtype=torch.float32, device="cuda")
     qjl.decode_step(to_dev(x["Q"], w.dtype), Kd[:, N - 1:N], Vd[:, N - 1:N], to_dev(x["S_in"], w.dtype),
                     to_dev(x["S_out"], w.dtype) if w.m_out else None,
                     torch.from_numpy(x["oidx"]).cuda() if w.n_out else None, cache, N, out,
-                    scores_dbg=scores, nsplit=nsplit, workspace=ws)
+                    scores_dbg=scores, nsplit=nsplit, workspace=ws, estimator=estimator)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -143,6 +143,28 @@ def test_decode_step_parity(name):
     else:
         log(f"  {name}: appended row differs from the oracle's in a near-zero bit or a norm ulp; "
             "output compared with the separate calls only")
+
+
+@pytest.mark.parametrize("name", ["llama2_mha", "llama3_gqa", "llama31_70b_gqa", "group16", "fp32_separate_calls"])
+def test_decode_step_two_sided(name):
+    """The two-sided estimator through the decode step: the fused prologue takes the query signs and
+    part norms (bf16), the separate calls the fp32 projection; the appended row is unchanged."""
+    w = CASES[name]
+    N = w.N
+    Ncap = N + 5
+    log(f"[decode_step two-sided] {name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={N} {w.dtype}")
+    x = inputs(w)
+    kq = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
+    vq = oracle.quantize_values(x["V"], w.nbits)
+    cache = dev_cache(w, kq, vq, N - 1, Ncap)
+    scores = torch.full((w.B, w.Hq, N), float("nan"), dtype=torch.float32, device="cuda")
+    out = run_step(w, x, cache, N, scores=scores, estimator=qjl.QJL_EST_TWO_SIDED)
+    if check_row(w, cache, kq, vq, N - 1, Ncap, f"{name} two-sided"):
+        units = [(b, hq) for b in range(w.B) for hq in range(w.Hq)]
+        check_decode(w, x["Q"], x["S_in"], x["S_out"], x["oidx"], {"bits": kq["bits"], "norms": kq["norms"], **vq},
+                     N, out, scores.cpu().numpy(), units, what=f"{name} two-sided step", estimator="two_sided")
+    else:
+        pytest.skip("appended row differs from the oracle's in a near-zero bit or a norm ulp")
 
 
 @pytest.mark.parametrize("nsplit", [1, 7])
