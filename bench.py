@@ -212,7 +212,7 @@ def main() -> int:
     ap.add_argument("--cache-copies", type=int, default=0,
                     help="independent caches the steps rotate through (0: enough that consecutive steps never "
                          f"find their cache in the {MALL_BYTES >> 20} MiB last-level cache)")
-    ap.add_argument("--value-bits", type=int, default=0, choices=[0, 2, 4],
+    ap.add_argument("--value-bits", type=int, default=0, choices=[0, 2, 3, 4],
                     help="token-wise value code width (0: the workload's, 2 bits)")
     ap.add_argument("--nsplit", type=int, default=0,
                     help="context chunks per (sequence, KV head) of the decode (0: the library's choice)")

@@ -270,10 +270,11 @@ int prepare_decode(qjl::DecodeArgs& a, int qdt, int B, int Hq, int Hkv, int d, i
     if (st) return st;
     if (!qjl::decode_shape_supported(m, m_out))
         return fail(QJL_ERR_UNSUPPORTED, "decode supports m in {128, 256, 512} with m_out in {0, m}; got m=%d m_out=%d", m, m_out);
-    if (vmode == QJL_V_CODES && nbits != 2 && nbits != 4)
-        return fail(QJL_ERR_UNSUPPORTED, "decode of %d-bit value codes unsupported (2 or 4)", nbits);
-    if (vmode == QJL_V_CODES && nbits == 4 && !qjl::decode_uses_mfma(m, m_out, QJL_V_CODES, 4))
-        return fail(QJL_ERR_UNSUPPORTED, "decode of 4-bit value codes needs m + m_out <= 512 (got m=%d m_out=%d)", m, m_out);
+    if (vmode == QJL_V_CODES && (nbits < 2 || nbits > 4))
+        return fail(QJL_ERR_UNSUPPORTED, "decode of %d-bit value codes unsupported (2, 3 or 4)", nbits);
+    if (vmode == QJL_V_CODES && nbits != 2 && !qjl::decode_uses_mfma(m, m_out, QJL_V_CODES, nbits))
+        return fail(QJL_ERR_UNSUPPORTED, "decode of %d-bit value codes needs m + m_out <= 512 (got m=%d m_out=%d)", nbits, m,
+                    m_out);
     if (nsplit > qjl::kMaxSplits) return fail(QJL_ERR_UNSUPPORTED, "nsplit=%d exceeds %d", nsplit, qjl::kMaxSplits);
     const int g = Hq / Hkv;
     const int ns = nsplit > 0 ? nsplit : qjl::decode_pick_nsplit(B, Hkv, g, N, m, m_out);

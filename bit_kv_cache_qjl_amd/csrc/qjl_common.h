@@ -171,12 +171,17 @@ __host__ __device__ constexpr int bits_word(int s, int win, int wout) {
 constexpr int kCodeTile = 32;
 __host__ __device__ constexpr int64_t code_tiles(int64_t Ncap) { return (Ncap + kCodeTile - 1) / kCodeTile; }
 __host__ __device__ constexpr int code_slot(int c) { return 8 * (c & 15) + (c >> 4); }
-// Field of token j (0..31) in a channel stream: fields are nbits wide, LSB first.  2- and 3-bit
-// streams are in token order; a 4-bit stream holds in word w the tokens 16 (w / 2) + 2 e + (w % 2)
-// (nibble e), so the two 2-bit planes of each word follow the token order of a 2-bit stream.
+// Field of token j (0..31) in a channel stream: fields are nbits wide, LSB first.  2-bit streams are
+// in token order; a 4-bit stream holds in word w the tokens 16 (w / 2) + 2 e + (w % 2) (nibble e), so
+// the two 2-bit planes of each word follow the token order of a 2-bit stream.  3-bit streams are two
+// planes instead: words 0 and 1 hold the low two bits of every code where a 2-bit stream holds its
+// code (field j), word 2 the high bits, token j at bit hi3_bit(j); then nibble n of
+// (word 2 >> k) & 0x11111111 belongs to the same token as nibble n of the k-th 2-bit plane word
+// (word 0 & 0x33333333, (word 0 >> 2) & .., word 1 & .., (word 1 >> 2) & ..).
 __host__ __device__ constexpr int code_field(int j, int nbits) {
     return nbits == 4 ? 8 * (2 * (j >> 4) + (j & 1)) + ((j & 15) >> 1) : j;
 }
+__host__ __device__ constexpr int hi3_bit(int j) { return 4 * ((j & 15) >> 1) + 2 * (j >> 4) + (j & 1); }
 __host__ __device__ constexpr int code_channel(int p) { return 16 * (p & 7) + (p >> 3); }
 
 struct ValueQuantArgs {
@@ -206,7 +211,7 @@ struct DecodeArgs {
     float* part;                      // workspace: partials [B*Hq][nsplit][d + 2]
     int64_t N, Ncap;
     int B, Hq, Hkv, g, m, m_out, n_out, nsplit;
-    int nbits;                        // value code width (2 or 4 on the matrix-core path)
+    int nbits;                        // value code width (2, 3 or 4 on the matrix-core path)
     int64_t chunk;                    // tokens per split (multiple of the tile)
     float z_scale;                    // sm_scale * log2(e)
     int estimator;                    // 0: one-sided (query unquantized); 1: two-sided (query signs)
@@ -221,7 +226,7 @@ struct AppendArgs {
     int64_t sVb, sVh;                 // element strides of the new values
     uint32_t* bits;
     uint16_t* norms;
-    uint32_t* codes;                  // 2- or 4-bit code tiles
+    uint32_t* codes;                  // 2-, 3- or 4-bit code tiles
     uint16_t* meta;
     int64_t pos;                      // cache position of the new token (N - 1)
 };
@@ -266,7 +271,7 @@ constexpr int kDecodeTile = 512;     // tokens per tile = threads per decode blo
 constexpr int kMaxSplits = 4096;     // context chunks per (sequence, query head)
 int decode_pick_nsplit(int B, int Hkv, int g, int64_t N, int m, int m_out);
 int64_t decode_chunk(int64_t N, int nsplit);
-// True when decode runs on the matrix-core path (2- or 4-bit value codes, W = (m + m_out)/32 <= 16).
+// True when decode runs on the matrix-core path (2-, 3- or 4-bit value codes, W = (m + m_out)/32 <= 16).
 bool decode_uses_mfma(int m, int m_out, int vmode, int nbits);
 // Row groups of 4 query heads per matrix-core workgroup: 2 (8 heads) when a KV head serves more than 4.
 __host__ __device__ constexpr int decode_mfma_rowgroups(int g) { return g > 4 ? 2 : 1; }

@@ -441,7 +441,7 @@ hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
 
 bool decode_uses_mfma(int m, int m_out, int vmode, int nbits) {
     const int win = m >> 5, wout = m_out >> 5;
-    return vmode == 0 && (nbits == 2 || nbits == 4) && (win == 4 || win == 8 || win == 16) && (wout == 0 || wout == win) &&
+    return vmode == 0 && (nbits >= 2 && nbits <= 4) && (win == 4 || win == 8 || win == 16) && (wout == 0 || wout == win) &&
            win + wout <= 16;
 }
 

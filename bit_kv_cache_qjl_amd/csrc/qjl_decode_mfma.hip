@@ -246,19 +246,26 @@ __global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs 
         }
         const int nb = a.nbits;
         uint32_t code[8];
-        const uint32_t mt = nb == 4 ? value_codes16<4>(v, code) : value_codes16<2>(v, code);
+        const uint32_t mt = nb == 4 ? value_codes16<4>(v, code) : (nb == 3 ? value_codes16<3>(v, code) : value_codes16<2>(v, code));
         if (lane < 16) {
             if (lane == 0) reinterpret_cast<uint32_t*>(ap.meta)[(size_t)vunit * a.Ncap + ap.pos] = mt;
             const int64_t tile = ap.pos / kCodeTile;
-            const int bit = nb * code_field((int)(ap.pos % kCodeTile), nb);   // the field never crosses a word
-            uint32_t* tw = ap.codes + ((size_t)vunit * code_tiles(a.Ncap) + tile) * (kD * nb) + (bit >> 5);
+            const int j = (int)(ap.pos % kCodeTile);
+            // a 2- or 4-bit field never crosses a word; 3-bit codes: the low two bits at the 2-bit
+            // field, the high bit in word 2 (two planes)
+            const int bit = nb == 3 ? 2 * j : nb * code_field(j, nb);
+            uint32_t* tw = ap.codes + ((size_t)vunit * code_tiles(a.Ncap) + tile) * (kD * nb);
             const int sh = bit & 31;
-            const uint32_t fm = (1u << nb) - 1u;
+            const uint32_t fm = nb == 3 ? 3u : (1u << nb) - 1u;
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 uint32_t* dst = tw + code_slot(8 * lane + q) * nb;
-                atomicAnd(dst, ~(fm << sh));
-                atomicOr(dst, code[q] << sh);
+                atomicAnd(dst + (bit >> 5), ~(fm << sh));
+                atomicOr(dst + (bit >> 5), (code[q] & fm) << sh);
+                if (nb == 3) {
+                    atomicAnd(dst + 2, ~(1u << hi3_bit(j)));
+                    atomicOr(dst + 2, (code[q] >> 2) << hi3_bit(j));
+                }
             }
         }
         return;
@@ -428,15 +435,13 @@ __device__ __forceinline__ void load_mblock(MBlock<WIN4, WOUT4, NB>& bl, __amdgp
     const auto m2 = __builtin_amdgcn_raw_buffer_load_b64(rm, vn, 0, 0);
     bl.nm[0] = n2[0]; bl.nm[1] = m2[0]; bl.nm[2] = n2[1]; bl.nm[3] = m2[1];
     const int vc = o.codes + s0 * (kD * NB * 4 / kCodeTile);
+    // the 8 channels' NB words each are 8 NB consecutive words: word 4 q + e is word (4 q + e) % NB of
+    // channel group (4 q + e) / NB
 #pragma unroll
     for (int q = 0; q < 2 * NB; ++q) {
         const auto x = __builtin_amdgcn_raw_buffer_load_b128(rc, vc + 16 * q, 0, 0);
-        if constexpr (NB == 2) {
-            bl.cx[2 * q][0] = x[0]; bl.cx[2 * q][1 % NB] = x[1];
-            bl.cx[(2 * q + 1) % 8][0] = x[2]; bl.cx[(2 * q + 1) % 8][1 % NB] = x[3];
-        } else {
-            bl.cx[q % 8][0] = x[0]; bl.cx[q % 8][1] = x[1]; bl.cx[q % 8][2 % NB] = x[2]; bl.cx[q % 8][3 % NB] = x[3];
-        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bl.cx[(4 * q + e) / NB][(4 * q + e) % NB] = x[e];
     }
 }
 
@@ -676,10 +681,23 @@ __global__ __launch_bounds__(kMThreads, (R == 1 && NB == 2) ? 2 : 1) void decode
 #pragma unroll
                 for (int rg = 0; rg < R; ++rg)
                     dv[rg][cg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw[rg], bv, dv[rg][cg], 0, 4, 0, sc_w, 0, 127);
+            } else if constexpr (NB == 3) {
+                // 3-bit codes: the 2-bit planes of words 0 and 1 as above, the high bits of word 2 as
+                // four 1-bit planes in the same token order; code = low + 4 high (B scale 2^2)
+                const uint32_t x0 = cur.cx[cg][0], x1 = cur.cx[cg][1 % NB], hb = cur.cx[cg][2 % NB];
+                const v8i_t blo = v8i_t{(int)(x0 & 0x33333333u), (int)((x0 >> 2) & 0x33333333u), (int)(x1 & 0x33333333u),
+                                        (int)((x1 >> 2) & 0x33333333u), 0, 0, 0, 0};
+                const v8i_t bhi = v8i_t{(int)(hb & 0x11111111u), (int)((hb >> 1) & 0x11111111u),
+                                        (int)((hb >> 2) & 0x11111111u), (int)((hb >> 3) & 0x11111111u), 0, 0, 0, 0};
+#pragma unroll
+                for (int rg = 0; rg < R; ++rg) {
+                    dv[rg][cg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw[rg], blo, dv[rg][cg], 0, 4, 0, sc_w, 0, 127);
+                    dv[rg][cg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw[rg], bhi, dv[rg][cg], 0, 4, 0, sc_w, 0, 129);
+                }
             } else {
                 // 4-bit codes: word w holds the same tokens in its two 2-bit planes as the 2-bit
                 // planes above; code = low + 4 high, the high plane through a B scale of 2^2
-                const uint32_t x0 = cur.cx[cg][0], x1 = cur.cx[cg][1], x2 = cur.cx[cg][2 % NB], x3 = cur.cx[cg][3 % NB];
+                const uint32_t x0 = cur.cx[cg][0], x1 = cur.cx[cg][1 % NB], x2 = cur.cx[cg][2 % NB], x3 = cur.cx[cg][3 % NB];
                 const v8i_t blo = v8i_t{(int)(x0 & 0x33333333u), (int)(x1 & 0x33333333u), (int)(x2 & 0x33333333u),
                                         (int)(x3 & 0x33333333u), 0, 0, 0, 0};
                 const v8i_t bhi = v8i_t{(int)((x0 >> 2) & 0x33333333u), (int)((x1 >> 2) & 0x33333333u),
@@ -775,6 +793,7 @@ template <int WIN4, int WOUT4>
 hipError_t launch_decode_mfma_t(const DecodeArgs& a, hipStream_t s) {
     const bool r2 = decode_mfma_rowgroups(a.g) == 2;
     if (a.nbits == 4) return r2 ? launch_decode_mfma_r<WIN4, WOUT4, 2, 4>(a, s) : launch_decode_mfma_r<WIN4, WOUT4, 1, 4>(a, s);
+    if (a.nbits == 3) return r2 ? launch_decode_mfma_r<WIN4, WOUT4, 2, 3>(a, s) : launch_decode_mfma_r<WIN4, WOUT4, 1, 3>(a, s);
     return r2 ? launch_decode_mfma_r<WIN4, WOUT4, 2, 2>(a, s) : launch_decode_mfma_r<WIN4, WOUT4, 1, 2>(a, s);
 }
 

@@ -9,7 +9,7 @@
 // and the codes of 8 channels into LDS.  Phase 2: one thread per channel packs the tile's 32 codes of
 // its channel into nbits words (the channel-major tile the decode kernels read as matrix-core
 // operands; channel c is stream slot 8 (c % 16) + c / 16 of the tile; token j sits in field
-// code_field(j, nbits)).  A tile wholly inside the append is stored; a tile the append covers only in
+// code_field(j, nbits), or for 3-bit codes in the two planes described with code_field).  A tile wholly inside the append is stored; a tile the append covers only in
 // part is merged bit-exactly with two atomics per word (clear the appended fields, then set them), so
 // tokens outside [t0, t0 + T) keep their codes.
 //
@@ -83,13 +83,18 @@ __global__ __launch_bounds__(kValThreads) void quantize_values_kernel(ValueQuant
             const int i = 4 * q + e;
             const uint32_t code = (four >> (8 * e)) & 0xFFu;
             const bool in = p0 + i >= a.t0 && p0 + i < a.t0 + a.T;
-            constexpr uint32_t fm = (1u << NBITS) - 1u;
-            const int bp = NBITS * code_field(i, NBITS);
-            wd[bp >> 5] |= code << (bp & 31);
-            if (in) msk[bp >> 5] |= fm << (bp & 31);
-            if ((bp & 31) + NBITS > 32) {   // the field continues in the next word
-                wd[(bp >> 5) + 1] |= code >> (32 - (bp & 31));
-                if (in) msk[(bp >> 5) + 1] |= fm >> (32 - (bp & 31));
+            if constexpr (NBITS == 3) {
+                // two planes: the low two bits where a 2-bit stream keeps its code, the high bit in word 2
+                const int bl = 2 * i;
+                wd[bl >> 5] |= (code & 3u) << (bl & 31);
+                if (in) msk[bl >> 5] |= 3u << (bl & 31);
+                wd[2] |= (code >> 2) << hi3_bit(i);
+                if (in) msk[2] |= 1u << hi3_bit(i);
+            } else {
+                constexpr uint32_t fm = (1u << NBITS) - 1u;
+                const int bp = NBITS * code_field(i, NBITS);   // a 2- or 4-bit field never crosses a word
+                wd[bp >> 5] |= code << (bp & 31);
+                if (in) msk[bp >> 5] |= fm << (bp & 31);
             }
         }
     }

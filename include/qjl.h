@@ -42,11 +42,14 @@
  *   norms fp16  [B][Hkv][Ncap][2]: (|k_in|, |k_out|) as IEEE binary16 round-to-nearest-even.
  *   codes uint32 [B][Hkv][Ncap32/32][d][nbits], Ncap32 = Ncap rounded up to a multiple of 32: the
  *         positions are grouped in tiles of 32 (tile i covers positions 32 i .. 32 i + 31).  For each
- *         channel c a tile holds the codes of its 32 positions as an LSB-first bit stream of nbits
- *         words: for nbits 2 and 3, position 32 i + j in bits [nbits*j, nbits*j + nbits) of the
- *         stream; for nbits 4, word w holds positions 32 i + 16 floor(w/2) + 2 e + (w mod 2) in its
- *         nibbles e = 0..7 (so each 2-bit plane of a 4-bit word lists its positions in the same order
- *         as a 2-bit stream).  The stream of channel c is stream slot 8 (c mod 16) + floor(c / 16) of
+ *         channel c a tile holds the codes of its 32 positions in nbits words: for nbits 2, position
+ *         32 i + j in bits [2j, 2j + 2) of the LSB-first 64-bit stream; for nbits 4, word w holds
+ *         positions 32 i + 16 floor(w/2) + 2 e + (w mod 2) in its nibbles e = 0..7 (so each 2-bit
+ *         plane of a 4-bit word lists its positions in the same order as a 2-bit stream); for nbits 3,
+ *         words 0 and 1 hold the low two bits of every code exactly as a 2-bit stream holds its code
+ *         and word 2 the high bits, position 32 i + j at bit 4 floor((j mod 16)/2) + 2 floor(j/16) +
+ *         (j mod 2) (so (word 2 >> k) & 0x11111111 lists the same positions, nibble by nibble, as the
+ *         k-th 2-bit plane of words 0 and 1).  The stream of channel c is stream slot 8 (c mod 16) + floor(c / 16) of
  *         the tile (slot p holds channel 16 (p mod 8) + floor(p / 8)).  Channel-major tiles let the
  *         decode kernels feed the codes to the matrix cores directly, 8 channels per load.
  *   meta  fp16  [B][Hkv][Ncap][2]: (min, step) of the token's value vector.
@@ -160,7 +163,7 @@ size_t qjl_decode_workspace_size(int B, int Hq, int Hkv, int d, int64_t N, int m
  *   Q           [B][Hq][d] contiguous, dtype qdt; S_in / S_out / outlier_idx as for quantize (S in
  *               dtype qdt).
  *   bits, norms the key cache (capacity Ncap >= N).
- *   vmode       QJL_V_CODES: codes + meta (nbits 2, or 4 with m + m_out <= 512), V_f32 ignored;
+ *   vmode       QJL_V_CODES: codes + meta (nbits 2, or 3 or 4 with m + m_out <= 512), V_f32 ignored;
  *               QJL_V_F32: V_f32 [B][Hkv][Ncap][d] fp32, codes/meta ignored.
  *   sm_scale    softmax scale; <= 0 selects 1/sqrt(d).
  *   estimator   a qjl_estimator.  QJL_EST_TWO_SIDED is the variant the QJL summary contrasts with the
@@ -194,14 +197,14 @@ int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, 
  * T = 1 and t0 = N - 1, then qjl_decode_attention over N tokens (the new token is quantized on the
  * fly before the step's query attends to it, as the QJL summary describes for generated tokens,
  * "Approach"; the cache then holds the same bits, norms, codes and meta as after the separate calls).
- * On the matrix-core path (dt = QJL_BF16, 2- or 4-bit values, (m, m_out) in {(128, 0), (128, 128),
+ * On the matrix-core path (dt = QJL_BF16, 2-, 3- or 4-bit values, (m, m_out) in {(128, 0), (128, 128),
  * (256, 0), (256, 256), (512, 0)}) the appends and the query projections run in one launch before the
  * decode kernel; otherwise the three operations are enqueued one after the other.
  *   Q           [B][Hq][d] contiguous, dtype dt.
  *   K_new       new keys, element (b, h, c) at K_new[b*sK_b + h*sK_h + c] (the model layout of one
  *               token: [B][1][Hkv][d] with its strides), dtype dt; V_new likewise with (sV_b, sV_h).
  *   S_in, S_out, outlier_idx, n_out, m, m_out  as for qjl_quantize_keys (S in dtype dt).
- *   bits, norms, codes, meta  the cache (layout at the top) of capacity Ncap >= N; nbits 2 or 4 (as
+ *   bits, norms, codes, meta  the cache (layout at the top) of capacity Ncap >= N; nbits 2, 3 or 4 (as
  *               for qjl_decode_attention).
  *   N           context length after the append (N >= 1).
  *   sm_scale, estimator, out, scores_dbg, nsplit, workspace  as for qjl_decode_attention (same

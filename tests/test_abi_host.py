@@ -109,8 +109,9 @@ def decode_call(ws_bytes=None, **kw):
     (dict(N=2000), qjl.QJL_ERR_INVALID_ARG),
     (dict(m=384, m_out=384), qjl.QJL_ERR_UNSUPPORTED),
     (dict(m=256, m_out=128), qjl.QJL_ERR_UNSUPPORTED),
-    (dict(nbits=3), qjl.QJL_ERR_UNSUPPORTED),
-    (dict(nbits=4, m=512, m_out=512), qjl.QJL_ERR_UNSUPPORTED),   # 4-bit codes: matrix-core shapes only
+    (dict(nbits=5), qjl.QJL_ERR_UNSUPPORTED),
+    (dict(nbits=4, m=512, m_out=512), qjl.QJL_ERR_UNSUPPORTED),   # 3- and 4-bit codes: matrix-core shapes only
+    (dict(nbits=3, m=512, m_out=512), qjl.QJL_ERR_UNSUPPORTED),
     (dict(vmode=1), qjl.QJL_ERR_INVALID_ARG),          # fp32 values but V_f32 is null
     (dict(vmode=7), qjl.QJL_ERR_INVALID_ARG),
     (dict(estimator=2), qjl.QJL_ERR_INVALID_ARG),
@@ -166,7 +167,7 @@ def step_call(ws_bytes=None, **kw):
     (dict(dt=3), qjl.QJL_ERR_INVALID_ARG),
     (dict(Hq=9), qjl.QJL_ERR_INVALID_ARG),
     (dict(estimator=5), qjl.QJL_ERR_INVALID_ARG),
-    (dict(nbits=3), qjl.QJL_ERR_UNSUPPORTED),
+    (dict(nbits=5), qjl.QJL_ERR_UNSUPPORTED),
     (dict(m=256, m_out=128), qjl.QJL_ERR_UNSUPPORTED),
     (dict(K_new=0), qjl.QJL_ERR_INVALID_ARG),
     (dict(codes=0), qjl.QJL_ERR_INVALID_ARG),

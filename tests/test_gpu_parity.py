@@ -178,16 +178,18 @@ def test_decode_parity(name, nsplit):
 
 @pytest.mark.parametrize("name", ["llama2_7b_decode", "llama3_8b_gqa_decode", "llama31_70b_gqa_decode"])
 @pytest.mark.parametrize("nsplit", [0, 3])
-def test_decode_parity_four_bit_values(name, nsplit):
-    """4-bit token-wise value codes (two 2-bit planes on the matrix cores)."""
-    w = SCALED[name].scaled(nbits=4)
-    log(f"[decode 4-bit] {name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} nsplit={nsplit}")
+@pytest.mark.parametrize("nbits", [3, 4])
+def test_decode_parity_wider_values(name, nsplit, nbits):
+    """3- and 4-bit token-wise value codes (a 2-bit plane plus a high-bit plane, or two 2-bit planes, on
+    the matrix cores)."""
+    w = SCALED[name].scaled(nbits=nbits)
+    log(f"[decode {nbits}-bit] {name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} nsplit={nsplit}")
     x = inputs(w)
     kq = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
-    cache = {"bits": kq["bits"], "norms": kq["norms"], **oracle.quantize_values(x["V"], 4)}
+    cache = {"bits": kq["bits"], "norms": kq["norms"], **oracle.quantize_values(x["V"], nbits)}
     out, scores = run_decode(qjl, w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, w.N, nsplit=nsplit)
     units = [(b, hq) for b in range(w.B) for hq in range(w.Hq)]
-    check_decode(w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, w.N, out, scores, units, what=f"{name} 4-bit")
+    check_decode(w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, w.N, out, scores, units, what=f"{name} {nbits}-bit")
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "llama2_7b_decode", "llama3_8b_gqa_decode", "llama31_70b_gqa_decode",

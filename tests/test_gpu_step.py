@@ -38,6 +38,9 @@ CASES = {
     "fp32_separate_calls": W["tiny_fp32"].scaled(B=2, Hq=2, Hkv=1, N=300, vmode="codes"),
     "four_bit_values": L3.scaled(nbits=4, N=700),
     "four_bit_values_70b": W["llama31_70b_gqa_decode"].scaled(B=1, Hq=16, Hkv=2, N=450, nbits=4),
+    "three_bit_values": L3.scaled(nbits=3, N=701),
+    "three_bit_values_70b": W["llama31_70b_gqa_decode"].scaled(B=1, Hq=16, Hkv=2, N=430, nbits=3),
+    "three_bit_tile_start": L3.scaled(nbits=3, N=65),
 }
 BITS_SENTINEL = np.uint32(0xA5A5A5A5)
 HALF_SENTINEL = np.uint16(0x3C00)     # 1.0
@@ -220,7 +223,9 @@ def test_decode_step_rejects_bad_arguments():
     with pytest.raises(qjl.QJLError) as e:
         qjl.decode_step(Q, Kd[:, :1], Vd[:, :1], S_in, S_out, oidx, cache, 0, out)      # nothing to append to
     assert e.value.status == qjl.QJL_ERR_INVALID_ARG
-    c3 = qjl.alloc_cache(w.B, w.Hkv, 64, w.m, w.m_out, 3)               # 3-bit codes: quantize only
+    # 3-bit codes decode on the matrix-core sketch shapes only (m + m_out <= 512)
+    c3 = qjl.alloc_cache(w.B, w.Hkv, 64, 512, 512, 3)
+    S5 = torch.zeros((512, w.d), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(qjl.QJLError) as e:
-        qjl.decode_step(Q, Kd[:, :1], Vd[:, :1], S_in, S_out, oidx, c3, 10, out)        # 3-bit values
+        qjl.decode_step(Q, Kd[:, :1], Vd[:, :1], S5, S5, oidx, c3, 10, out)
     assert e.value.status == qjl.QJL_ERR_UNSUPPORTED

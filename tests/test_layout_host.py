@@ -8,14 +8,20 @@ layout = qjl.layout
 
 
 def tile_words_by_hand(codes, nbits, tile, ch):
-    """The nbits words of (tile, channel).  2 and 3 bits: position 32*tile + j in bits
-    [nbits*j, nbits*j + nbits) of an LSB-first stream.  4 bits: word w, nibble e holds position
-    32*tile + 16*(w // 2) + 2*e + (w % 2).  Positions past the end count as code 0."""
+    """The nbits words of (tile, channel).  2 bits: position 32*tile + j in bits [2j, 2j + 2) of an
+    LSB-first stream.  4 bits: word w, nibble e holds position 32*tile + 16*(w // 2) + 2*e + (w % 2).
+    3 bits: words 0 and 1 hold the low two bits of each code as the 2-bit stream does, word 2 the high
+    bit of position 32*tile + j at bit 4*((j % 16) // 2) + 2*(j // 16) + j % 2.  Positions past the end
+    count as code 0."""
     def code(j):
         p = 32 * tile + j
         return int(codes[p, ch]) if p < codes.shape[0] else 0
     if nbits == 4:
         return [sum(code(16 * (w // 2) + 2 * e + (w % 2)) << (4 * e) for e in range(8)) for w in range(4)]
+    if nbits == 3:
+        low = sum((code(j) & 3) << (2 * j) for j in range(32))
+        high = sum((code(j) >> 2) << (4 * ((j % 16) // 2) + 2 * (j // 16) + j % 2) for j in range(32))
+        return [low & 0xFFFFFFFF, low >> 32, high]
     stream = 0
     for j in range(32):
         c = code(j)
@@ -68,6 +74,28 @@ def test_four_bit_tile_by_example():
     codes[18, 0] = 0x2       # word 2, nibble 1
     t = layout.tiles_from_codes(codes, 4)
     assert [int(x) for x in t[0, 0]] == [0x9000000F, 0x3, 0x20, 0x50000000]
+
+
+def test_three_bit_tile_by_example():
+    """Channel 0 of a 3-bit tile, and the planes the decode reads: nibble n of (word 2 >> k) & 0x11111111
+    is the high bit of the position whose low bits nibble n of the k-th 2-bit plane holds."""
+    codes = np.zeros((32, 128), dtype=np.int64)
+    codes[5, 0] = 7          # low bits 10, 11 of word 0; high bit 4*2 + 0 + 1 = 9 of word 2
+    codes[20, 0] = 4         # low bits 0 (bits 8, 9 of word 1); high bit 4*2 + 2 + 0 = 10
+    codes[31, 0] = 6         # low 2 at bits 30, 31 of word 1; high bit 4*7 + 2 + 1 = 31
+    t = layout.tiles_from_codes(codes, 3)
+    assert [int(x) for x in t[0, 0]] == [0xC00, 0x80000000, (1 << 9) | (1 << 10) | (1 << 31)]
+    rng = np.random.default_rng(9)
+    c = rng.integers(0, 8, size=(32, 128))
+    w = layout.tiles_from_codes(c, 3)[0, 0].astype(np.int64)
+    planes = [w[0] & 0x33333333, (w[0] >> 2) & 0x33333333, w[1] & 0x33333333, (w[1] >> 2) & 0x33333333]
+    tokens = [[2 * n, 2 * n + 1, 16 + 2 * n, 17 + 2 * n] for n in range(8)]
+    for k in range(4):
+        hi = (w[2] >> k) & 0x11111111
+        for n in range(8):
+            j = tokens[n][k]
+            assert (planes[k] >> (4 * n)) & 3 == c[j, 0] & 3
+            assert (hi >> (4 * n)) & 1 == c[j, 0] >> 2
 
 
 def test_round_trip_with_leading_dims_and_int32_views():
