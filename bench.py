@@ -230,8 +230,8 @@ def main() -> int:
     if args.traffic_from:
         return write_traffic(*args.traffic_from, args.workload)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "sharding across GPUs is described in the design notes but not built", file=sys.stderr)
+        print(f"bench.py: the library and this benchmark run on one GPU only (asked for --gpus {args.gpus}); "
+              "how decode would shard across GPUs is described in the design notes, not implemented", file=sys.stderr)
         return 2
 
     import torch
