@@ -290,6 +290,7 @@ void quantize_keys_lds_kernel(KeyQuantArgs a) {
     __shared__ int s_oidx[kMaxOutliers];
     __shared__ uint32_t s_keep[2 * 32];          // keep masks of the 32 key words of each lane half
     __shared__ uint32_t s_goff[2 * 8];           // byte offsets of the gathered channels of each lane half
+    __shared__ int s_next;                       // next unclaimed 32-token block of the workgroup
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -301,6 +302,7 @@ void quantize_keys_lds_kernel(KeyQuantArgs a) {
     const int n_out = a.n_out;
 
     if (tid < n_out) s_oidx[tid] = a.oidx[h * n_out + tid] & (kD - 1);   // never index outside a row
+    if (tid == 0) s_next = kLWaves;              // blocks 0 .. kLWaves - 1 go to waves 0 .. kLWaves - 1
     __syncthreads();
     if (tid < 64) {
         // word w = 4 s + q of lane half hf holds channels 16 s + 8 hf + 2 q, + 1
@@ -396,8 +398,11 @@ void quantize_keys_lds_kernel(KeyQuantArgs a) {
         bg = make_uint4(g[0], g[1], g[2], g[3]);
     };
 
+    // Blocks are claimed one at a time from an LDS counter: the four waves of a SIMD progress at
+    // different rates, and with a fixed share per wave the workgroup would end with its slowest wave
+    // while the others sit idle (measured: 4 blocks per wave took 38 to 74 us).
     const int64_t nblk = (t_end - t_begin + 31) / 32;
-    for (int64_t blk = wave; blk < nblk; blk += kLWaves) {
+    for (int64_t blk = wave; blk < nblk;) {
         const int64_t t0b = t_begin + 32 * blk;
         const int64_t tk = t0b + tcol;
         // the mask tables are read per block, not held in registers across the loop
@@ -473,6 +478,9 @@ void quantize_keys_lds_kernel(KeyQuantArgs a) {
                 }
             }
         }
+        int claim = 0;
+        if (lane == 0) claim = atomicAdd(&s_next, 1);
+        blk = __builtin_amdgcn_readfirstlane(claim);
     }
 }
 
