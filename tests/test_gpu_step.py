@@ -188,8 +188,9 @@ def test_decode_step_split_counts(nsplit):
 
 
 def test_decode_step_consecutive_steps_share_workspace():
-    """Three steps in a row (N, N+1, N+2) with one workspace: the chunk counters the decode kernel
-    counts on are re-armed by every step's first launch."""
+    """Three steps in a row (N, N+1, N+2) with one workspace: nothing in the workspace carries over
+    from one step to the next (every step rewrites the query operands and the chunk partials it
+    reads)."""
     w = CASES["llama31_70b_gqa"].scaled(N=700)
     N0 = w.N - 2
     x = inputs(w)
