@@ -68,6 +68,20 @@ def test_quantize_keys_small_append(name, T, m, m_out):
     assert not bits[:, :, :9].any()
 
 
+@pytest.mark.parametrize("m,m_out", [(512, 512), (512, 0), (256, 256), (256, 0), (128, 128), (128, 0)])
+def test_quantize_keys_sketch_shapes(m, m_out):
+    """Every matrix-core sketch shape of the prefill quantizer (T > 16), three 32-token blocks and a
+    ragged fourth per (sequence, KV head)."""
+    base = SCALED["llama3_8b_gqa_decode"]
+    w = base.scaled(B=2, Hq=2, Hkv=2, N=100, m=m, m_out=m_out, n_out=base.n_out if m_out else 0)
+    log(f"[quantize_keys] sketch shape m={m} m_out={m_out} T={w.N}")
+    x = inputs(w)
+    cache = gpu_quantize_keys(qjl, w, x["K"], x["S_in"], x["S_out"], x["oidx"])
+    ref = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
+    compare_bits(bits_np(cache.bits, w.m, w.m_out), ref, f"m={m} m_out={m_out}", w.m + w.m_out)
+    compare_norms(cache.norms.cpu().numpy(), ref["norms"], f"m={m} m_out={m_out}")
+
+
 def test_quantize_keys_append_offset_and_strides():
     """Write T tokens at t0 of a larger cache from a strided (non-contiguous) key view."""
     w = SCALED["llama2_7b_decode"].scaled(N=70)
