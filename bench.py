@@ -184,6 +184,21 @@ def bench_quantize(qjl, torch, steps: int) -> dict:
     qjl.timer_enable(False)
     sel_s = mss / 1e3 / max(ns, 1)
     sel_bytes = float(K.numel() * K.element_size())
+    # token-wise value codes of the same prefill: V [1, 65536, 8, 128] bf16 -> 2-bit code tiles + (min, step)
+    V = torch.from_numpy(si.values(w)).cuda().to(torch.bfloat16)
+    for _ in range(3):
+        qjl.quantize_values(V, w.nbits, cache.codes, cache.meta)
+    torch.cuda.synchronize()
+    qjl.timer_enable(True)
+    qjl.timer_read("quantize_values")
+    for _ in range(steps):
+        qjl.quantize_values(V, w.nbits, cache.codes, cache.meta)
+    torch.cuda.synchronize()
+    nv, msv = qjl.timer_read("quantize_values")
+    qjl.timer_enable(False)
+    val_s = msv / 1e3 / max(nv, 1)
+    # per token and KV head: d bf16 values read, d b / 8 code bytes and the fp16 (min, step) pair written
+    val_bytes = float(w.B * w.N * w.Hkv * (2 * w.d + w.d * w.nbits // 8 + 4))
     tokens = w.B * w.N
     flops = 2.0 * w.d * w.m * tokens * w.Hkv          # inlier (d - n_out) m + outlier n_out m_out = d m MACs
     return {"workload": f"{w.name}: B={w.B} T={w.N} Hkv={w.Hkv} d={w.d} m=m_out={w.m} n_out={w.n_out}",
@@ -194,7 +209,10 @@ def bench_quantize(qjl, torch, steps: int) -> dict:
                      "flops_per_launch": flops},
             "select_outliers": {"kernel_ms": sel_s * 1e3, "bound": "hbm", "achieved": sel_bytes / sel_s / 1e9,
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": sel_bytes / sel_s / 1e9 / HBM_PEAK_GBS,
-                                "bytes_per_launch": sel_bytes}}
+                                "bytes_per_launch": sel_bytes},
+            "quantize_values": {"kernel_ms": val_s * 1e3, "tok_per_s": tokens / val_s, "bits": w.nbits, "bound": "hbm",
+                                "achieved": val_bytes / val_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": val_bytes / val_s / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": val_bytes}}
 
 
 def main() -> int:

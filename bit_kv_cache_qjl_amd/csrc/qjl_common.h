@@ -105,32 +105,54 @@ __device__ __forceinline__ uint32_t norm_pair(float ss_in, float ss_out) {
 // min and max over the row, step = fp16((max - min) / L), mn16 = fp16(min), and the codes
 // clamp(rint((v - mn16) / step), 0, L) of the lane's channels (all 0 when step is 0).  IEEE fp32
 // operations with no contraction.  Returns the meta word (mn16 | step16 << 16).
+// The quotient x / step is first taken as y = x * rcp(step) (v_rcp_f32, within 1 ulp; the product
+// rounded: y is within 2^-22 |y| of the exact quotient, the correctly rounded quotient within 2^-24),
+// so for |y| <= L + 1 rint(y) is the code unless y lies within 2^-20 (L + 2) of a half-integer (beyond
+// that range both quotients clamp to the same code).  A lane with such a value takes the correctly
+// rounded divides for its 8 values (one branch, rarely entered).  A step of 0 gives a reciprocal of
+// 0, so every code is 0 without a branch.
 template <int NBITS>
 __device__ __forceinline__ uint32_t value_codes16(const float (&v)[8], uint32_t (&code)[8]) {
 #pragma clang fp contract(off)
-    float mn = v[0], mx = v[0];
-#pragma unroll
-    for (int q = 1; q < 8; ++q) {
-        mn = fminf(mn, v[q]);
-        mx = fmaxf(mx, v[q]);
-    }
-    mn = row16_min(mn);   // min and max are exact in any order
+    // IEEE minimum / maximum (three-input instructions, no canonicalizing), in any order: exact
+    float mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(v[0], v[1]), v[2]);
+    float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[0], v[1]), v[2]);
+    mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, v[3]), v[4]);
+    mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, v[3]), v[4]);
+    mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, v[5]), v[6]);
+    mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, v[5]), v[6]);
+    mn = __builtin_elementwise_minimum(mn, v[7]);
+    mx = __builtin_elementwise_maximum(mx, v[7]);
+    mn = row16_min(mn);
     mx = row16_max(mx);
     constexpr int L = (1 << NBITS) - 1;
-    const float stepf = (mx - mn) / (float)L;
+    // fp16(fl32((mx - mn) / L)): the product with fl32(1 / L) is within 3 fp32 ulps of the correctly
+    // rounded quotient, so both round to the same fp16 unless their 13 dropped bits lie within 4 of
+    // the halfway pattern 0x1000, or the step is below the fp16 normal range; then divide.
+    const float rng = mx - mn;
+    float stepf = rng * (1.0f / (float)L);
+    const uint32_t dropped = __float_as_uint(stepf) & 0x1FFFu;
+    if (stepf < 0x1p-14f || (dropped >= 0x1000u - 4u && dropped <= 0x1000u + 4u)) stepf = rng / (float)L;
     const _Float16 step16 = (_Float16)stepf;
     const _Float16 mn16 = (_Float16)mn;
     const float step = (float)step16;
     const float base = (float)mn16;
+    const float rstep = step != 0.f ? __builtin_amdgcn_rcpf(step) : 0.f;
+    float x[8], r[8];
+    bool near_tie = false;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-        uint32_t c = 0;
-        if (step != 0.f) {
-            const float r = rintf((v[q] - base) / step);
-            c = (uint32_t)fminf(fmaxf(r, 0.f), (float)L);
-        }
-        code[q] = c;
+        x[q] = v[q] - base;
+        const float y = x[q] * rstep;
+        r[q] = rintf(y);
+        near_tie |= fabsf(y - r[q]) >= 0.5f - 0x1p-20f * (float)(L + 2);
     }
+    if (near_tie) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) r[q] = rintf(x[q] / step);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) code[q] = (uint32_t)fminf(fmaxf(r[q], 0.f), (float)L);
     return (uint32_t)__builtin_bit_cast(uint16_t, mn16) | ((uint32_t)__builtin_bit_cast(uint16_t, step16) << 16);
 }
 

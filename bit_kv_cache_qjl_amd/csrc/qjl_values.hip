@@ -6,12 +6,15 @@
 //
 // One workgroup per (sequence, KV head, 32-token code tile) touched by the append.  Phase 1: sixteen
 // threads own one value vector (8 channels each): a 16-lane min/max butterfly, the (min, step) meta,
-// and the codes of 8 channels into LDS.  Phase 2: one thread per channel packs the tile's 32 codes of
-// its channel into nbits words (the channel-major tile the decode kernels read as matrix-core
-// operands; channel c is stream slot 8 (c % 16) + c / 16 of the tile; token j sits in field
-// code_field(j, nbits), or for 3-bit codes in the two planes described with code_field).  A tile wholly inside the append is stored; a tile the append covers only in
-// part is merged bit-exactly with two atomics per word (clear the appended fields, then set them), so
-// tokens outside [t0, t0 + T) keep their codes.
+// and the codes of 8 channels into LDS, one byte per code.  Phase 2: one thread per channel packs
+// the tile's 32 codes of its channel into nbits words (the channel-major tile the decode kernels read
+// as matrix-core operands; channel c is stream slot 8 (c % 16) + c / 16 of the tile; token j sits in
+// field code_field(j, nbits), or for 3-bit codes in the two planes described with code_field).  In a
+// channel's LDS row, token j = 16 a + 4 e + f is byte 16 a + 4 f + e: 2-bit words then come from
+// three shift-or operations on the row's words (byte e of word f holds token 4 e + f, so
+// w0 | w1 << 2 | (w2 | w3 << 2) << 4 puts token 4 e + f at bits 8 e + 2 f).  A tile wholly inside the
+// append is stored; a tile the append covers only in part is merged bit-exactly with two atomics per
+// word (clear the appended fields, then set them), so tokens outside [t0, t0 + T) keep their codes.
 //
 // The decisions are IEEE fp32 operations with no contraction: subtract, correctly rounded divide,
 // fp16 round-to-nearest-even, rint (ties to even).
@@ -22,6 +25,20 @@ namespace {
 
 constexpr int kValThreads = kCodeTile * 16;   // 512
 constexpr int kRowPitch = kCodeTile + 4;      // bytes per channel row of the LDS code tile
+
+// byte of token j in a channel's LDS row, and the token held by byte p
+__host__ __device__ constexpr int code_byte(int j) { return 16 * (j >> 4) + 4 * (j & 3) + ((j & 15) >> 2); }
+__host__ __device__ constexpr int byte_token(int p) { return 16 * (p >> 4) + 4 * (p & 3) + ((p & 15) >> 2); }
+static_assert(byte_token(code_byte(13)) == 13 && byte_token(code_byte(22)) == 22, "inverse permutations");
+
+// 2-bit fields [a, b) of a 16-field word (a, b clamped to 0..16)
+__device__ __forceinline__ uint32_t field_mask2(int a, int b) {
+    a = a < 0 ? 0 : (a > 16 ? 16 : a);
+    b = b < 0 ? 0 : (b > 16 ? 16 : b);
+    const uint32_t hi = b >= 16 ? 0xFFFFFFFFu : ((1u << (2 * b)) - 1u);
+    const uint32_t lo = a >= 16 ? 0xFFFFFFFFu : ((1u << (2 * a)) - 1u);
+    return hi & ~lo;
+}
 
 template <typename VT>
 __device__ __forceinline__ void load8(const VT* p, float (&v)[8]);
@@ -64,42 +81,55 @@ __global__ __launch_bounds__(kValThreads) void quantize_values_kernel(ValueQuant
     uint32_t code[8];
     const uint32_t mt = value_codes16<NBITS>(v, code);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) cs[(8 * sub + q) * kRowPitch + tk] = (uint8_t)code[q];
+    for (int q = 0; q < 8; ++q) cs[(8 * sub + q) * kRowPitch + code_byte(tk)] = (uint8_t)code[q];
     if (valid && sub == 0) reinterpret_cast<uint32_t*>(a.meta)[bh * a.Ncap + pos] = mt;
     __syncthreads();
 
     if (tid >= kD) return;
     const int c = tid;
-    uint32_t wd[NBITS], msk[NBITS];
-#pragma unroll
-    for (int k = 0; k < NBITS; ++k) wd[k] = msk[k] = 0u;
     const int64_t p0 = tile * kCodeTile;
     const uint32_t* row = reinterpret_cast<const uint32_t*>(cs + c * kRowPitch);
+    uint32_t* dst = a.codes + ((size_t)bh * code_tiles(a.Ncap) + tile) * (kD * NBITS) + code_slot(c) * NBITS;
+    const bool full = p0 >= a.t0 && p0 + kCodeTile <= a.t0 + a.T;
+    // tokens of the tile inside the append: [ia, ib)
+    const int ia = (int)(a.t0 > p0 ? a.t0 - p0 : 0);
+    const int ib = (int)(a.t0 + a.T - p0 < kCodeTile ? a.t0 + a.T - p0 : kCodeTile);
+    uint32_t wd[NBITS], msk[NBITS];
+    if constexpr (NBITS == 2) {
+        uint32_t w[8];
 #pragma unroll
-    for (int q = 0; q < kCodeTile / 4; ++q) {
-        const uint32_t four = row[q];
+        for (int k = 0; k < 8; ++k) w[k] = row[k];
+        wd[0] = (w[0] | (w[1] << 2)) | ((w[2] | (w[3] << 2)) << 4);
+        wd[1] = (w[4] | (w[5] << 2)) | ((w[6] | (w[7] << 2)) << 4);
+        msk[0] = field_mask2(ia, ib);
+        msk[1] = field_mask2(ia - 16, ib - 16);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 4 * q + e;
-            const uint32_t code = (four >> (8 * e)) & 0xFFu;
-            const bool in = p0 + i >= a.t0 && p0 + i < a.t0 + a.T;
-            if constexpr (NBITS == 3) {
-                // two planes: the low two bits where a 2-bit stream keeps its code, the high bit in word 2
-                const int bl = 2 * i;
-                wd[bl >> 5] |= (code & 3u) << (bl & 31);
-                if (in) msk[bl >> 5] |= 3u << (bl & 31);
-                wd[2] |= (code >> 2) << hi3_bit(i);
-                if (in) msk[2] |= 1u << hi3_bit(i);
-            } else {
-                constexpr uint32_t fm = (1u << NBITS) - 1u;
-                const int bp = NBITS * code_field(i, NBITS);   // a 2- or 4-bit field never crosses a word
-                wd[bp >> 5] |= code << (bp & 31);
-                if (in) msk[bp >> 5] |= fm << (bp & 31);
+        for (int k = 0; k < NBITS; ++k) wd[k] = msk[k] = 0u;
+#pragma unroll
+        for (int q = 0; q < kCodeTile / 4; ++q) {
+            const uint32_t four = row[q];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = byte_token(4 * q + e);
+                const uint32_t code = (four >> (8 * e)) & 0xFFu;
+                const bool in = i >= ia && i < ib;
+                if constexpr (NBITS == 3) {
+                    // two planes: the low two bits where a 2-bit stream keeps its code, the high bit in word 2
+                    const int bl = 2 * i;
+                    wd[bl >> 5] |= (code & 3u) << (bl & 31);
+                    if (in) msk[bl >> 5] |= 3u << (bl & 31);
+                    wd[2] |= (code >> 2) << hi3_bit(i);
+                    if (in) msk[2] |= 1u << hi3_bit(i);
+                } else {
+                    constexpr uint32_t fm = (1u << NBITS) - 1u;
+                    const int bp = NBITS * code_field(i, NBITS);   // a 4-bit field never crosses a word
+                    wd[bp >> 5] |= code << (bp & 31);
+                    if (in) msk[bp >> 5] |= fm << (bp & 31);
+                }
             }
         }
     }
-    uint32_t* dst = a.codes + ((size_t)bh * code_tiles(a.Ncap) + tile) * (kD * NBITS) + code_slot(c) * NBITS;
-    const bool full = p0 >= a.t0 && p0 + kCodeTile <= a.t0 + a.T;
     if (full) {
 #pragma unroll
         for (int k = 0; k < NBITS; ++k) dst[k] = wd[k];

@@ -148,7 +148,38 @@ def test_quantize_values_parity(dtype, nbits):
     assert not cache.meta[:, :, :3].any(), "wrote meta before t0"
 
 
-@pytest.mark.parametrize("nbits", [2, 3])
+@pytest.mark.parametrize("nbits", [2, 3, 4])
+def test_quantize_values_half_integer_quotients(nbits):
+    """Values at and a few fp32 ulps around (k + 1/2) step, for steps that are not powers of two:
+    the quotients (v - min) / step sit on or next to the rounding ties, where a code must come from
+    the correctly rounded division and rint's ties to even."""
+    L = (1 << nbits) - 1
+    T, d = 96, 128
+    rng = np.random.default_rng(7)
+    V = np.zeros((1, T, 1, d), dtype=np.float32)
+    for t in range(T):
+        c = np.float32(rng.uniform(0.05, 3.0))
+        step16 = np.float32(np.float16(np.float32(np.float32(L) * c) / np.float32(L)))
+        row = [np.float32(0.0), np.float32(L) * c]
+        for k in range(L):
+            mid = np.float32((k + 0.5) * step16)
+            for j in range(-3, 4):
+                x = mid
+                for _ in range(abs(j)):
+                    x = np.nextafter(x, np.float32(np.inf if j > 0 else -np.inf), dtype=np.float32)
+                row.append(x)
+        row = np.array(row, dtype=np.float32)
+        V[0, t, 0, :] = np.resize(row, d)
+    log(f"[quantize_values] half-integer quotients nbits={nbits}")
+    cache = qjl.alloc_cache(1, 1, T, 256, 0, nbits)
+    qjl.quantize_values(to_dev(V, "f32"), nbits, cache.codes, cache.meta)
+    torch.cuda.synchronize()
+    ref = oracle.quantize_values(V, nbits)
+    np.testing.assert_array_equal(cache.meta.cpu().numpy().view(np.uint16), ref["meta"].view(np.uint16))
+    np.testing.assert_array_equal(code_rows_of_tiles(cache.codes, nbits, T), ref["codes"])
+
+
+@pytest.mark.parametrize("nbits", [2, 3, 4])
 def test_quantize_values_appends_keep_neighbours(nbits):
     """Appends that start and end inside code tiles (single tokens, short runs, a run across tiles)
     merge into the tiles without touching other positions; the result equals one bulk quantize."""
