@@ -101,30 +101,50 @@ __device__ __forceinline__ uint32_t norm_pair(float ss_in, float ss_out) {
     return (uint32_t)__builtin_bit_cast(uint16_t, ni) | ((uint32_t)__builtin_bit_cast(uint16_t, no) << 16);
 }
 
-// Token-wise quantization of one value vector held by a row of 16 lanes, 8 channels per lane (v):
-// min and max over the row, step = fp16((max - min) / L), mn16 = fp16(min), and the codes
-// clamp(rint((v - mn16) / step), 0, L) of the lane's channels (all 0 when step is 0).  IEEE fp32
-// operations with no contraction.  Returns the meta word (mn16 | step16 << 16).
+__device__ __forceinline__ float row8_max(float v) {
+    v = __builtin_elementwise_maximum(v, dpp_mov<0xB1>(v));
+    v = __builtin_elementwise_maximum(v, dpp_mov<0x4E>(v));
+    v = __builtin_elementwise_maximum(v, dpp_mov<0x141>(v));
+    return v;
+}
+__device__ __forceinline__ float row8_min(float v) {
+    v = __builtin_elementwise_minimum(v, dpp_mov<0xB1>(v));
+    v = __builtin_elementwise_minimum(v, dpp_mov<0x4E>(v));
+    v = __builtin_elementwise_minimum(v, dpp_mov<0x141>(v));
+    return v;
+}
+
+// Token-wise quantization of one value vector held by 128 / NV consecutive lanes (16 or 8, aligned),
+// NV channels per lane (v): min and max over those lanes, step = fp16((max - min) / L),
+// mn16 = fp16(min), and the codes clamp(rint((v - mn16) / step), 0, L) of the lane's channels (all 0
+// when step is 0).  IEEE fp32 operations with no contraction.  Returns the meta word
+// (mn16 | step16 << 16).
 // The quotient x / step is first taken as y = x * rcp(step) (v_rcp_f32, within 1 ulp; the product
 // rounded: y is within 2^-22 |y| of the exact quotient, the correctly rounded quotient within 2^-24),
 // so for |y| <= L + 1 rint(y) is the code unless y lies within 2^-20 (L + 2) of a half-integer (beyond
 // that range both quotients clamp to the same code).  A lane with such a value takes the correctly
-// rounded divides for its 8 values (one branch, rarely entered).  A step of 0 gives a reciprocal of
+// rounded divides for all its values (one branch, rarely entered).  A step of 0 gives a reciprocal of
 // 0, so every code is 0 without a branch.
-template <int NBITS>
-__device__ __forceinline__ uint32_t value_codes16(const float (&v)[8], uint32_t (&code)[8]) {
+template <int NBITS, int NV>
+__device__ __forceinline__ uint32_t value_codes(const float (&v)[NV], uint32_t (&code)[NV]) {
 #pragma clang fp contract(off)
+    static_assert(NV == 8 || NV == 16, "a vector of 128 channels over 16 or 8 lanes");
     // IEEE minimum / maximum (three-input instructions, no canonicalizing), in any order: exact
-    float mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(v[0], v[1]), v[2]);
-    float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[0], v[1]), v[2]);
-    mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, v[3]), v[4]);
-    mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, v[3]), v[4]);
-    mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, v[5]), v[6]);
-    mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, v[5]), v[6]);
-    mn = __builtin_elementwise_minimum(mn, v[7]);
-    mx = __builtin_elementwise_maximum(mx, v[7]);
-    mn = row16_min(mn);
-    mx = row16_max(mx);
+    float mn = v[0], mx = v[0];
+#pragma unroll
+    for (int q = 1; q + 1 < NV; q += 2) {
+        mn = __builtin_elementwise_minimum(__builtin_elementwise_minimum(mn, v[q]), v[q + 1]);
+        mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, v[q]), v[q + 1]);
+    }
+    mn = __builtin_elementwise_minimum(mn, v[NV - 1]);
+    mx = __builtin_elementwise_maximum(mx, v[NV - 1]);
+    if constexpr (NV == 8) {
+        mn = row16_min(mn);
+        mx = row16_max(mx);
+    } else {
+        mn = row8_min(mn);
+        mx = row8_max(mx);
+    }
     constexpr int L = (1 << NBITS) - 1;
     // fp16(fl32((mx - mn) / L)): the product with fl32(1 / L) is within 3 fp32 ulps of the correctly
     // rounded quotient, so both round to the same fp16 unless their 13 dropped bits lie within 4 of
@@ -138,10 +158,10 @@ __device__ __forceinline__ uint32_t value_codes16(const float (&v)[8], uint32_t 
     const float step = (float)step16;
     const float base = (float)mn16;
     const float rstep = step != 0.f ? __builtin_amdgcn_rcpf(step) : 0.f;
-    float x[8], r[8];
+    float x[NV], r[NV];
     bool near_tie = false;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < NV; ++q) {
         x[q] = v[q] - base;
         const float y = x[q] * rstep;
         r[q] = rintf(y);
@@ -149,10 +169,10 @@ __device__ __forceinline__ uint32_t value_codes16(const float (&v)[8], uint32_t 
     }
     if (near_tie) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) r[q] = rintf(x[q] / step);
+        for (int q = 0; q < NV; ++q) r[q] = rintf(x[q] / step);
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) code[q] = (uint32_t)fminf(fmaxf(r[q], 0.f), (float)L);
+    for (int q = 0; q < NV; ++q) code[q] = (uint32_t)fminf(fmaxf(r[q], 0.f), (float)L);
     return (uint32_t)__builtin_bit_cast(uint16_t, mn16) | ((uint32_t)__builtin_bit_cast(uint16_t, step16) << 16);
 }
 

@@ -246,7 +246,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs 
         }
         const int nb = a.nbits;
         uint32_t code[8];
-        const uint32_t mt = nb == 4 ? value_codes16<4>(v, code) : (nb == 3 ? value_codes16<3>(v, code) : value_codes16<2>(v, code));
+        const uint32_t mt = nb == 4 ? value_codes<4, 8>(v, code) : (nb == 3 ? value_codes<3, 8>(v, code) : value_codes<2, 8>(v, code));
         if (lane < 16) {
             if (lane == 0) reinterpret_cast<uint32_t*>(ap.meta)[(size_t)vunit * a.Ncap + ap.pos] = mt;
             const int64_t tile = ap.pos / kCodeTile;

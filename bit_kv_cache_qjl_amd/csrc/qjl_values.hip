@@ -4,15 +4,16 @@
 // (take the range of the vector, divide it into 2^b equally spaced values, round each number to the
 // nearest) and the QJL summary, "Limitations" (values use token-wise quantization).
 //
-// One workgroup per (sequence, KV head, 32-token code tile) touched by the append.  Phase 1: sixteen
-// threads own one value vector (8 channels each): a 16-lane min/max butterfly, the (min, step) meta,
-// and the codes of 8 channels into LDS, one byte per code.  Phase 2: one thread per channel packs
-// the tile's 32 codes of its channel into nbits words (the channel-major tile the decode kernels read
-// as matrix-core operands; channel c is stream slot 8 (c % 16) + c / 16 of the tile; token j sits in
-// field code_field(j, nbits), or for 3-bit codes in the two planes described with code_field).  In a
-// channel's LDS row, token j = 16 a + 4 e + f is byte 16 a + 4 f + e: 2-bit words then come from
-// three shift-or operations on the row's words (byte e of word f holds token 4 e + f, so
-// w0 | w1 << 2 | (w2 | w3 << 2) << 4 puts token 4 e + f at bits 8 e + 2 f).  A tile wholly inside the
+// One workgroup per (sequence, KV head, 32-token code tile) touched by the append.  Phase 1: eight
+// threads own one value vector (16 channels each): an 8-lane min/max butterfly, the (min, step)
+// meta, and the codes of 16 channels into LDS, one byte per code.  Phase 2: one thread per stream
+// slot p packs the tile's 32 codes of channel code_channel(p) into nbits words (the channel-major
+// tile the decode kernels read as matrix-core operands; channel c is stream slot 8 (c % 16) + c / 16
+// of the tile; token j sits in field code_field(j, nbits), or for 3-bit codes in the two planes
+// described with code_field).  LDS row p holds slot p (the 8 lanes of a token then write 8 rows that
+// fall on distinct banks).  In a row, token j = 16 a + 4 e + f is byte 16 a + 4 f + e: 2-bit words
+// then come from three shift-or operations on the row's words (byte e of word f holds token 4 e + f,
+// so w0 | w1 << 2 | (w2 | w3 << 2) << 4 puts token 4 e + f at bits 8 e + 2 f).  A tile wholly inside the
 // append is stored; a tile the append covers only in part is merged bit-exactly with two atomics per
 // word (clear the appended fields, then set them), so tokens outside [t0, t0 + T) keep their codes.
 //
@@ -23,7 +24,7 @@
 namespace qjl {
 namespace {
 
-constexpr int kValThreads = kCodeTile * 16;   // 512
+constexpr int kValThreads = kCodeTile * 8;    // 256: 8 threads per token, 16 channels each
 constexpr int kRowPitch = kCodeTile + 4;      // bytes per channel row of the LDS code tile
 
 // byte of token j in a channel's LDS row, and the token held by byte p
@@ -67,8 +68,8 @@ __global__ __launch_bounds__(kValThreads) void quantize_values_kernel(ValueQuant
 #pragma clang fp contract(off)
     __shared__ __attribute__((aligned(16))) uint8_t cs[kD * kRowPitch];   // [channel][token of the tile]
     const int tid = threadIdx.x;
-    const int sub = tid & 15;
-    const int tk = tid >> 4;
+    const int sub = tid & 7;
+    const int tk = tid >> 3;
     const int64_t bh = blockIdx.x / ntiles;           // b * Hkv + h
     const int64_t tile = tile_first + (int)(blockIdx.x % ntiles);
     const int h = (int)(bh % a.Hkv);
@@ -76,20 +77,31 @@ __global__ __launch_bounds__(kValThreads) void quantize_values_kernel(ValueQuant
     const int64_t pos = tile * kCodeTile + tk;        // cache position of this thread's token
     const bool valid = pos >= a.t0 && pos < a.t0 + a.T;
 
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (valid) load8<VT>(static_cast<const VT*>(a.V) + b * a.sVb + (pos - a.t0) * a.sVt + h * a.sVh + 8 * sub, v);
-    uint32_t code[8];
-    const uint32_t mt = value_codes16<NBITS>(v, code);
+    float v[16], lo[8], hi[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) cs[(8 * sub + q) * kRowPitch + code_byte(tk)] = (uint8_t)code[q];
+    for (int q = 0; q < 8; ++q) lo[q] = hi[q] = 0.f;
+    if (valid) {
+        const VT* src = static_cast<const VT*>(a.V) + b * a.sVb + (pos - a.t0) * a.sVt + h * a.sVh + 16 * sub;
+        load8<VT>(src, lo);
+        load8<VT>(src + 8, hi);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        v[q] = lo[q];
+        v[8 + q] = hi[q];
+    }
+    uint32_t code[16];
+    const uint32_t mt = value_codes<NBITS, 16>(v, code);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) cs[code_slot(16 * sub + q) * kRowPitch + code_byte(tk)] = (uint8_t)code[q];
     if (valid && sub == 0) reinterpret_cast<uint32_t*>(a.meta)[bh * a.Ncap + pos] = mt;
     __syncthreads();
 
     if (tid >= kD) return;
-    const int c = tid;
+    const int slot = tid;
     const int64_t p0 = tile * kCodeTile;
-    const uint32_t* row = reinterpret_cast<const uint32_t*>(cs + c * kRowPitch);
-    uint32_t* dst = a.codes + ((size_t)bh * code_tiles(a.Ncap) + tile) * (kD * NBITS) + code_slot(c) * NBITS;
+    const uint32_t* row = reinterpret_cast<const uint32_t*>(cs + slot * kRowPitch);
+    uint32_t* dst = a.codes + ((size_t)bh * code_tiles(a.Ncap) + tile) * (kD * NBITS) + slot * NBITS;
     const bool full = p0 >= a.t0 && p0 + kCodeTile <= a.t0 + a.T;
     // tokens of the tile inside the append: [ia, ib)
     const int ia = (int)(a.t0 > p0 ? a.t0 - p0 : 0);
