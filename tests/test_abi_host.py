@@ -91,6 +91,11 @@ def test_quantize_values_rejects(kw, status):
     assert values_call(**kw) == status
 
 
+def test_quantize_values_empty_is_noop():
+    assert values_call(T=0, V=0) == qjl.QJL_OK
+    assert values_call(B=0, V=0) == qjl.QJL_OK
+
+
 def decode_call(ws_bytes=None, **kw):
     a = dict(Q=FAKE, qdt=0, B=2, Hq=8, Hkv=2, d=128, N=1000, S_in=FAKE, m=256, S_out=FAKE, m_out=256, oidx=FAKE,
              n_out=3, bits=FAKE, norms=FAKE, Ncap=1024, vmode=0, codes=FAKE, meta=FAKE, V_f32=0, nbits=2,
