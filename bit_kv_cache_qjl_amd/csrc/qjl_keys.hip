@@ -339,21 +339,24 @@ void quantize_keys_lds_kernel(KeyQuantArgs a) {
             const int j = i / kOGRow, r = i % kOGRow;
             go[u] = r < n_out ? Sout[(size_t)j * kD + s_oidx[r]] : (uint16_t)0;
         }
+        // this thread's 8 channels 8 cgi .. 8 cgi + 7 are the same in every round: their keep masks
+        // (outlier channels zeroed) are built once, per lane, with no branch on the channel list
+        const int cgi = tid & 15;
+        uint32_t outl = 0;                               // bit e: channel 8 cgi + e is an outlier
+        for (int k = 0; k < n_out; ++k) {
+            const int c = s_oidx[k];
+            outl |= ((c >> 3) == cgi ? 1u : 0u) << (c & 7);
+        }
+        uint32_t keepw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            keepw[q] = (((outl >> (2 * q)) & 1u) ? 0xFFFF0000u : 0xFFFFFFFFu) & (((outl >> (2 * q + 1)) & 1u) ? 0x0000FFFFu : 0xFFFFFFFFu);
 #pragma unroll
         for (int u = 0; u < NSI; ++u) {
             const int i = tid + u * kLThreads;
-            const int r = i >> 4, cgi = i & 15;
-            uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-            for (int k = 0; k < n_out; ++k) {
-                const int c = s_oidx[k];
-                if ((c >> 3) == cgi) {
-                    const uint32_t m = (c & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (q == ((c & 7) >> 1)) w[q] &= m;
-                }
-            }
-            *reinterpret_cast<uint4*>(sl + r * kSRowL + 8 * cgi) = make_uint4(w[0], w[1], w[2], w[3]);
+            const int r = i >> 4;
+            *reinterpret_cast<uint4*>(sl + r * kSRowL + 8 * cgi) =
+                make_uint4(v[u].x & keepw[0], v[u].y & keepw[1], v[u].z & keepw[2], v[u].w & keepw[3]);
         }
 #pragma unroll
         for (int u = 0; u < NSO; ++u) {
