@@ -292,9 +292,8 @@ __global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs 
             for (int s = 0; s < 4; ++s)
                 sb[u][hf][s] = *reinterpret_cast<const uint4*>(S + (size_t)(16 * hf + (lane & 15)) * kD + 32 * s + 8 * (lane >> 4));
     }
-    bool is_out = false;
-    if (wave < 2)
-        for (int i = 0; i < a.n_out; ++i) is_out |= (a.oidx[h * a.n_out + i] & (kD - 1)) == tid;
+    // the KV head's outlier channels: one entry per lane of wave 0, all in one round trip
+    const int oc = (wave == 0 && lane < a.n_out) ? (a.oidx[h * a.n_out + lane] & (kD - 1)) : -1;
     const int sv = tid >> 4, cg = tid & 15;      // staging: vector sv of a pass, channels 8 cg .. 8 cg + 7
     auto load_vector = [&](int col) {
         if (col >= ncol) return make_uint4(0u, 0u, 0u, 0u);
@@ -302,12 +301,11 @@ __global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs 
         return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Q) + (head0 + col - (APPEND ? 1 : 0)) * kD + 8 * cg);
     };
     uint4 xv = load_vector(sv);
-    if (wave < 2) {                              // outlier mask of the KV head, 64 channels per wave
-        const uint64_t bm = __builtin_amdgcn_ballot_w64(is_out);
-        if (lane == 0) {
-            s_mask[2 * wave] = (uint32_t)bm;
-            s_mask[2 * wave + 1] = (uint32_t)(bm >> 32);
-        }
+    if (wave == 0) {
+        // outlier mask of the KV head (bit c % 32 of word c / 32): the LDS operations of a wave complete
+        // in order, so the words are cleared before the entries set their bits
+        if (lane < 4) s_mask[lane] = 0u;
+        if (oc >= 0) atomicOr(&s_mask[oc >> 5], 1u << (oc & 31));
     }
     __syncthreads();
 
