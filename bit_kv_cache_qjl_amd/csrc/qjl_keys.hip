@@ -508,11 +508,16 @@ void quantize_keys_rows_kernel(KeyQuantArgs a, int64_t rows) {
     const int64_t r0 = (int64_t)blockIdx.x * kTok;
 
     for (int hh = tid; hh < a.Hkv; hh += kThreads) {
+        // the head's outlier list as independent loads (one round trip), then its 128-bit mask
+        int cl[kMaxOutliers];
+#pragma unroll
+        for (int i = 0; i < kMaxOutliers; ++i) cl[i] = i < a.n_out ? (a.oidx[hh * a.n_out + i] & (kD - 1)) : -1;
         uint32_t mk[4] = {0u, 0u, 0u, 0u};
-        for (int i = 0; i < a.n_out; ++i) {
-            const int c = a.oidx[hh * a.n_out + i] & (kD - 1);
-            mk[c >> 5] |= 1u << (c & 31);
-        }
+#pragma unroll
+        for (int i = 0; i < kMaxOutliers; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (cl[i] >= 0 && (cl[i] >> 5) == q) mk[q] |= 1u << (cl[i] & 31);
 #pragma unroll
         for (int q = 0; q < 4; ++q) s_mask[hh * 4 + q] = mk[q];
     }
