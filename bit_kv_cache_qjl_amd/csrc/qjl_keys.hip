@@ -58,6 +58,31 @@ __device__ __forceinline__ uint32_t pack_signs(const f32x16& acc, int lane) {
     return ~(lo | (hi << 16));
 }
 
+// Signs of two 32x32 tiles at once: lane l < 32 gets tile a's word for token l, lane l + 32 tile b's
+// word for token l (same bit order as pack_signs).  The lane's 32 sign bits (b's in the upper half)
+// are swapped across the lane halves and one byte permute (sel: 0x05040100 in lanes 0..31,
+// 0x07060302 in lanes 32..63) joins each tile's two half-words.
+__device__ __forceinline__ uint32_t pack_sign_pair(const f32x16& a, const f32x16& b, uint32_t sel) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) w = __builtin_amdgcn_alignbit(w, __float_as_uint(b[r]), 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) w = __builtin_amdgcn_alignbit(w, __float_as_uint(a[r]), 31);
+    // x[0]: the word of lane l % 32, x[1]: the word of lane l % 32 + 32
+    const auto x = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return ~__builtin_amdgcn_perm(x[1], x[0], sel);
+}
+
+template <int N>
+__device__ __forceinline__ void store_words(uint32_t* dst, const uint32_t (&w)[N]) {
+    if constexpr (N == 1) dst[0] = w[0];
+    else if constexpr (N == 2) *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+    else {
+        static_assert(N == 4, "one, two or four words per lane");
+        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -268,8 +293,8 @@ void quantize_keys_bf16_kernel(KeyQuantArgs a) {
 // per row), loaded once.  Each wave then streams its own 32-token blocks with no further barrier:
 // the keys of a block go from global memory straight into the MFMA B operand (lane l: token l % 32,
 // channels 16 s + 8 (l / 32) .. + 7), the A operands (32 projections x 16 channels) come from LDS,
-// and a lane stores its token's sign words quarter-row group by group (the group's words are
-// consecutive slots of the stored row).  The norms come from the same registers: |k_in|^2 with the
+// and the two lanes of a token store its sign words quarter-row group by group (the group's words
+// are consecutive slots of the stored row).  The norms come from the same registers: |k_in|^2 with the
 // outlier channels masked out (S_in has zero columns there, so the projections need no masking),
 // |k_out|^2 from the gathered operand.
 constexpr int kOGRow = 16;                   // gathered S_out row (bf16)
@@ -369,8 +394,10 @@ void quantize_keys_lds_kernel(KeyQuantArgs a) {
     __syncthreads();
 
     const int tcol = lane & 31;
-    const int khalf = (lane >> 5) * 8;
+    const int hf = lane >> 5;
+    const int khalf = hf * 8;
     const int prow = tile_row(lane & 31);
+    const uint32_t psel = hf ? 0x07060302u : 0x05040100u;
     // this (sequence, head)'s key rows up to the end of the last valid token: loads of tokens past
     // t_end (and of the unused gathered ranks) fall outside and return zeros
     const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(static_cast<const uint16_t*>(a.K) + b * a.sKb + h * a.sKh,
@@ -435,50 +462,76 @@ void quantize_keys_lds_kernel(KeyQuantArgs a) {
         if (lane < 32 && tk < t_end) norms32[head_row0 + tk] = norm_pair(si, sg);
 
         // projections by quarter-row group g of the stored row (inlier words g WIN/4 .., then outlier
-        // words g WOUT/4 ..: consecutive slots g W/4 ..), two independent MFMA chains at a time
+        // words g WOUT/4 ..: consecutive slots g W/4 ..), two independent MFMA chains at a time.  Tiles
+        // are packed in pairs: lanes 0..31 keep the first tile's word, lanes 32..63 the second's.  With
+        // an outlier sketch, inlier tile p pairs with outlier tile p, so the lanes 0..31 of a token hold
+        // the group's inlier words and the lanes 32..63 its outlier words: one store per lane.
         constexpr int GI = WIN / 4, GO = WOUT / 4;
+        static_assert(GO == 0 || GO == GI, "outlier tiles pair with inlier tiles");
         uint32_t* row = a.bits + (head_row0 + tk) * W;
+        const bool live = tk < t_end;
 #pragma unroll 1
         for (int g = 0; g < 4; ++g) {
-            uint32_t gw[GI + GO];
+            uint32_t* dst = row + g * (W / 4);
+            if constexpr (GO > 0) {
+                uint32_t wd[GI];
 #pragma unroll
-            for (int jj = 0; jj < GI; jj += 2) {
-                const uint16_t* a0p = arow + 32 * (g * GI + jj) * kSRowL;
-                if constexpr (GI == 1) {
-                    f32x16 a0 = {};
+                for (int p = 0; p < GI; p += 2) {
+                    const uint16_t* a0p = arow + 32 * (g * GI + p) * kSRowL;
+                    const uint16_t* o0p = orow + 32 * (g * GO + p) * kOGRow;
+                    if constexpr (GI >= 2) {
+                        f32x16 a0 = {}, a1 = {};
 #pragma unroll
-                    for (int s = 0; s < 8; ++s)
-                        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const uint4*>(a0p + 16 * s)),
-                                                                     as_bf16x8(bk[s]), a0, 0, 0, 0);
-                    gw[jj] = pack_signs(a0, lane);
-                } else {
+                        for (int s = 0; s < 8; ++s) {
+                            a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const uint4*>(a0p + 16 * s)),
+                                                                         as_bf16x8(bk[s]), a0, 0, 0, 0);
+                            a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                as_bf16x8(*reinterpret_cast<const uint4*>(a0p + 32 * kSRowL + 16 * s)), as_bf16x8(bk[s]), a1, 0, 0, 0);
+                        }
+                        const f32x16 o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            as_bf16x8(*reinterpret_cast<const uint4*>(o0p)), as_bf16x8(bg), f32x16{}, 0, 0, 0);
+                        const f32x16 o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            as_bf16x8(*reinterpret_cast<const uint4*>(o0p + 32 * kOGRow)), as_bf16x8(bg), f32x16{}, 0, 0, 0);
+                        wd[p] = pack_sign_pair(a0, o0, psel);
+                        wd[p + 1] = pack_sign_pair(a1, o1, psel);
+                    } else {
+                        f32x16 a0 = {};
+#pragma unroll
+                        for (int s = 0; s < 8; ++s)
+                            a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const uint4*>(a0p + 16 * s)),
+                                                                         as_bf16x8(bk[s]), a0, 0, 0, 0);
+                        const f32x16 o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            as_bf16x8(*reinterpret_cast<const uint4*>(o0p)), as_bf16x8(bg), f32x16{}, 0, 0, 0);
+                        wd[p] = pack_sign_pair(a0, o0, psel);
+                    }
+                }
+                if (live) store_words<GI>(dst + hf * GI, wd);
+            } else if constexpr (GI >= 2) {
+                // pairs (p, p + GI/2): lanes 0..31 hold words 0 .. GI/2 - 1 of the group, 32..63 the rest
+                uint32_t wi[GI / 2];
+#pragma unroll
+                for (int p = 0; p < GI / 2; ++p) {
+                    const uint16_t* a0p = arow + 32 * (g * GI + p) * kSRowL;
+                    const uint16_t* a1p = a0p + 32 * (GI / 2) * kSRowL;
                     f32x16 a0 = {}, a1 = {};
 #pragma unroll
                     for (int s = 0; s < 8; ++s) {
                         a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const uint4*>(a0p + 16 * s)),
                                                                      as_bf16x8(bk[s]), a0, 0, 0, 0);
-                        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            as_bf16x8(*reinterpret_cast<const uint4*>(a0p + 32 * kSRowL + 16 * s)), as_bf16x8(bk[s]), a1, 0, 0, 0);
+                        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(*reinterpret_cast<const uint4*>(a1p + 16 * s)),
+                                                                     as_bf16x8(bk[s]), a1, 0, 0, 0);
                     }
-                    gw[jj] = pack_signs(a0, lane);
-                    gw[jj + 1] = pack_signs(a1, lane);
+                    wi[p] = pack_sign_pair(a0, a1, psel);
                 }
-            }
+                if (live) store_words<GI / 2>(dst + hf * (GI / 2), wi);
+            } else {
+                f32x16 a0 = {};
 #pragma unroll
-            for (int jj = 0; jj < GO; ++jj) {
-                const f32x16 ao = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    as_bf16x8(*reinterpret_cast<const uint4*>(orow + 32 * (g * GO + jj) * kOGRow)), as_bf16x8(bg), f32x16{}, 0, 0, 0);
-                gw[GI + jj] = pack_signs(ao, lane);
-            }
-            if (lane < 32 && tk < t_end) {
-                uint32_t* dst = row + g * (W / 4);
-                if constexpr (GI + GO == 1) dst[0] = gw[0];
-                else if constexpr (GI + GO == 2) *reinterpret_cast<uint2*>(dst) = make_uint2(gw[0], gw[1]);
-                else {
-#pragma unroll
-                    for (int q = 0; q < GI + GO; q += 4)
-                        *reinterpret_cast<uint4*>(dst + q) = make_uint4(gw[q], gw[q + 1], gw[q + 2], gw[q + 3]);
-                }
+                for (int s = 0; s < 8; ++s)
+                    a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        as_bf16x8(*reinterpret_cast<const uint4*>(arow + 32 * g * kSRowL + 16 * s)), as_bf16x8(bk[s]), a0, 0, 0, 0);
+                const uint32_t w = pack_signs(a0, lane);
+                if (lane < 32 && live) dst[0] = w;
             }
         }
         int claim = 0;
