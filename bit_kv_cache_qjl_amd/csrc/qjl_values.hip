@@ -1,4 +1,5 @@
-// Token-wise value quantization (memory-bound: 256 B read, 36 B written per token and KV head).
+// Token-wise value quantization (256 B read and, at 2 bits, 36 B written per token and KV head; the
+// kernel is bound by its vector instructions more than by HBM).
 //
 // Method: "2 numbers out of 128 destroy the entire KV cache", "The Obvious Fix: Use Fewer Bits"
 // (take the range of the vector, divide it into 2^b equally spaced values, round each number to the
@@ -17,8 +18,9 @@
 // append is stored; a tile the append covers only in part is merged bit-exactly with two atomics per
 // word (clear the appended fields, then set them), so tokens outside [t0, t0 + T) keep their codes.
 //
-// The decisions are IEEE fp32 operations with no contraction: subtract, correctly rounded divide,
-// fp16 round-to-nearest-even, rint (ties to even).
+// The decisions are those of IEEE fp32 operations with no contraction: subtract, correctly rounded
+// divide, fp16 round-to-nearest-even, rint (ties to even); value_codes reaches the same codes with
+// reciprocal products and falls back to the divides near rounding boundaries.
 #include "qjl_common.h"
 
 namespace qjl {
