@@ -464,8 +464,8 @@ void quantize_keys_lds_kernel(KeyQuantArgs a) {
         // projections by quarter-row group g of the stored row (inlier words g WIN/4 .., then outlier
         // words g WOUT/4 ..: consecutive slots g W/4 ..), two independent MFMA chains at a time.  Tiles
         // are packed in pairs: lanes 0..31 keep the first tile's word, lanes 32..63 the second's.  With
-        // an outlier sketch, inlier tile p pairs with outlier tile p, so the lanes 0..31 of a token hold
-        // the group's inlier words and the lanes 32..63 its outlier words: one store per lane.
+        // an outlier sketch, inlier tile p pairs with outlier tile p, so for token t of the block lane t
+        // holds the group's inlier words and lane t + 32 its outlier words: one store per lane.
         constexpr int GI = WIN / 4, GO = WOUT / 4;
         static_assert(GO == 0 || GO == GI, "outlier tiles pair with inlier tiles");
         uint32_t* row = a.bits + (head_row0 + tk) * W;
