@@ -249,7 +249,7 @@ def main() -> int:
         return write_traffic(*args.traffic_from, args.workload)
     if args.gpus != 1:
         print(f"bench.py: the library and this benchmark run on one GPU only (asked for --gpus {args.gpus}); "
-              "how decode would shard across GPUs is described in the design notes, not implemented", file=sys.stderr)
+              "sharding decode by (sequence, KV head) across GPUs is not implemented", file=sys.stderr)
         return 2
 
     import torch

@@ -18,7 +18,7 @@ Sources (page title, then section):
   [HARD]  "Why Compressing the KV Cache Is Hard" (TurboQuant slides, section 5) - "Just Round
           Everything - The Naive Approach", "A Worked Example: When Rounding Ruins Attention".
 
-Readings taken where the pages are silent (each is also listed in the design notes):
+Readings taken where the pages are silent:
   * estimator constant: score = sqrt(pi/2)/m * ||k|| * <S q, sign(S k)>; the pages only say the
     asymmetric estimator is unbiased [QJL "Approach"]; sqrt(pi/2) is what makes it unbiased for
     Gaussian S (E[<s,q> sign<s,k>] = sqrt(2/pi) <q,k>/||k||);
