@@ -526,3 +526,100 @@ def test_rotate_sign_closed_forms():
     ref = oracle.rotate_sign_scores(q, K, R)
     scale = np.linalg.norm(K, axis=1) * np.abs(R @ q).sum() / math.sqrt(d)
     assert np.all(np.abs(one - ref) <= 2 ** -11 * scale)
+
+
+# ----------------------------------------------------------------------------- exact attention
+
+def test_exact_attention_page_examples_and_closed_forms():
+    """Unquantized attention (reporting reference): the page's dot product Q . K_cat = 16.203
+    ("How Attention Computes a Score"); with two keys scoring 12.83 and 12.23 the weights are the
+    page's [0.65, 0.35] and the output its 0.65 V_cat + 0.35 V_mat ("Why Truncation Kills", "Keys
+    Select. Values Deliver."); one key returns its value; equal scores return the mean value; and an
+    explicit loop over the softmax definition on random inputs."""
+    g = golden("page1_one_bit_keys.json")
+    q = np.array(g["query_on"])
+    k_cat, v_cat, v_mat = (np.array(g["keys"]["cat"]), np.array(g["values"]["cat"]), np.array(g["values"]["mat"]))
+    # keys {k_cat, 0} with one-hot values: the first output channel is the softmax weight of cat,
+    # logistic(sm_scale * Q . K_cat); the page rounds each of its 8 products to 3 decimals (<= 0.004)
+    sm = 0.1
+    w_cat = oracle.exact_attention(q, np.stack([k_cat, np.zeros(8)]), np.eye(2), sm)[0]
+    dot = math.log(w_cat / (1.0 - w_cat)) / sm
+    assert dot == pytest.approx(g["score_on_cat_printed"], abs=4e-3)
+    # one key: the softmax weight is 1
+    np.testing.assert_allclose(oracle.exact_attention(q, k_cat[None], v_cat[None], 0.37), v_cat, rtol=0, atol=1e-15)
+    # two keys along q with the page's scores 12.83 and 12.23 (sm_scale 1)
+    K2 = np.stack([12.83 * q / (q @ q), 12.23 * q / (q @ q)])
+    out = oracle.exact_attention(q, K2, np.stack([v_cat, v_mat]), 1.0)
+    w = g["softmax_correct"]["weights_printed"]
+    np.testing.assert_allclose(out, w[0] * v_cat + w[1] * v_mat, atol=0.006 * np.abs(v_cat - v_mat).max())
+    wa = 1.0 / (1.0 + math.exp(-(12.83 - 12.23)))
+    np.testing.assert_allclose(out, wa * v_cat + (1 - wa) * v_mat, rtol=0, atol=1e-13)
+    # equal scores: every key orthogonal to q gives the mean of the values
+    rng = np.random.default_rng(11)
+    V = rng.standard_normal((9, 8))
+    qo = np.zeros(8)
+    qo[0] = 1.0
+    Ko = rng.standard_normal((9, 8))
+    Ko[:, 0] = 0.0
+    np.testing.assert_allclose(oracle.exact_attention(qo, Ko, V, 3.0), V.mean(axis=0), rtol=0, atol=1e-14)
+    # the definition written out as loops: scores <q, k_t>, scaled, max-subtracted exponentials
+    K = rng.standard_normal((13, 8))
+    V = rng.standard_normal((13, 8))
+    qr = rng.standard_normal(8)
+    sm = 0.6
+    z = [sm * sum(qr[c] * K[t, c] for c in range(8)) for t in range(13)]
+    mz = max(z)
+    e = [math.exp(x - mz) for x in z]
+    ref = [sum(e[t] * V[t, c] for t in range(13)) / sum(e) for c in range(8)]
+    np.testing.assert_allclose(oracle.exact_attention(qr, K, V, sm), ref, rtol=0, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------- batch and head routing
+
+def test_batch_and_kv_head_routing():
+    """Several sequences, KV heads and query heads per KV head (B = 3, Hkv = 2, g = 3), with a
+    different outlier channel set per KV head.  Query head hq reads KV head hq // g: heads 0, 1, 2 read
+    KV head 0 and heads 3, 4, 5 read KV head 1 (written out below, not computed).  Pinned three ways:
+      * values: every value vector of (b, h) is the constant c[b, h], so the output of (b, hq) is
+        exactly c[b, KV head of hq] whatever the scores are;
+      * keys: the keys of (b, h) live on the outlier channels of KV head h only, so their inlier norm
+        is 0, their inlier bits are all 1 (sign(0) = +1) and their outlier norm is the key's norm;
+      * scores: each (b, hq) equals the single-head estimator on the projection of its own query
+        with its KV head's outlier set, over that KV head's keys."""
+    B, Hkv, g, N, d, m, m_out = 3, 2, 3, 11, 16, 32, 32
+    Hq = Hkv * g
+    kv_of = [0, 0, 0, 1, 1, 1]
+    oidx = np.array([[1, 6], [9, 14]], dtype=np.int32)
+    rng = np.random.default_rng(21)
+    S_in, S_out = rng.standard_normal((m, d)), rng.standard_normal((m_out, d))
+    K = np.zeros((B, N, Hkv, d))
+    for h in range(Hkv):
+        K[:, :, h, oidx[h]] = rng.standard_normal((B, N, 2)) * 3.0
+    c = np.array([[1.0 + b + 0.25 * h for h in range(Hkv)] for b in range(B)])      # fp16-exact constants
+    V = np.broadcast_to(c[:, None, :, None], (B, N, Hkv, d)).astype(np.float32)
+    Q = rng.standard_normal((B, Hq, d))
+
+    kq = oracle.quantize_keys(K, S_in, S_out, oidx)
+    vq = oracle.quantize_values(V, 2)
+    for b in range(B):
+        for h in range(Hkv):
+            assert np.all(kq["norms"][b, h, :, 0] == 0)
+            full = np.linalg.norm(K[b, :, h, :], axis=1)
+            np.testing.assert_array_equal(kq["norms"][b, h, :, 1], oracle.fp16(full))
+            assert np.all(kq["bits"][b, h, :, : m // 32] == 0xFFFFFFFF)
+            # the unit equals the single-vector quantizer on its own keys and outlier set
+            r = oracle.quantize_key_vectors(K[b, :, h, :], S_in, S_out, oidx[h])
+            np.testing.assert_array_equal(kq["bits"][b, h], r["bits"])
+
+    res = oracle.decode_attention(Q, S_in, S_out, oidx, kq["bits"], kq["norms"], N, codes=vq["codes"],
+                                  meta=vq["meta"], nbits=2)
+    for b in range(B):
+        for hq in range(Hq):
+            h = kv_of[hq]
+            np.testing.assert_allclose(res["out"][b, hq], c[b, h], rtol=0, atol=1e-13)
+            sq_in, sq_out = oracle.project_query(Q[b, hq], S_in, S_out, oidx[h])
+            np.testing.assert_array_equal(res["scores"][b, hq],
+                                          oracle.estimator_scores(sq_in, sq_out, kq["bits"][b, h], kq["norms"][b, h]))
+    # the head routing is what distinguishes the KV heads here: a swap of the two heads' data changes
+    # every output, so the check above cannot pass by accident
+    assert np.all(c[:, 0] != c[:, 1])
