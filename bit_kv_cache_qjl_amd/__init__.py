@@ -28,6 +28,7 @@ QJL_V_CODES = 0
 QJL_V_F32 = 1
 QJL_EST_ONE_SIDED = 0
 QJL_EST_TWO_SIDED = 1
+NO_ALLOC_SCRATCH_BYTES = 8 << 20    # QJL_NO_ALLOC_SCRATCH_BYTES: the fixed workspace of qjl_decode_step_no_alloc
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python bit_kv_cache_qjl_amd/build.py`")
@@ -57,6 +58,9 @@ lib.qjl_decode_attention.argtypes = [_p, _i, _i, _i, _i, _i, _i64, _p, _i, _p, _
 lib.qjl_decode_step.restype = _i
 lib.qjl_decode_step.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _p, _i, _p, _i, _p, _i,
                                 _p, _p, _p, _p, _i64, _i, _f, _i, _p, _p, _i, _p, _sz, _p]
+lib.qjl_decode_step_no_alloc.restype = _i
+lib.qjl_decode_step_no_alloc.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _p, _i, _p, _i, _p,
+                                         _i, _p, _p, _p, _p, _i64, _i, _f, _i, _p, _p, _i, _p]
 lib.qjl_select_outliers_workspace_size.restype = _sz
 lib.qjl_select_outliers_workspace_size.argtypes = [_i, _i64, _i, _i]
 lib.qjl_select_outliers.restype = _i
@@ -212,10 +216,8 @@ def decode_attention(Q, S_in, S_out, outlier_idx, bits, norms, N: int, out, *, c
                                     _stream(stream)), "qjl_decode_attention")
 
 
-def decode_step(Q, K_new, V_new, S_in, S_out, outlier_idx, cache: Cache, N: int, out, *, sm_scale: float = 0.0,
-                estimator: int = 0, scores_dbg=None, nsplit: int = 0, workspace=None, stream=None) -> None:
-    """qjl_decode_step on torch tensors: append the new token (K_new, V_new [B, 1, Hkv, d], d contiguous)
-    at position N - 1 of the cache, then decode Q [B, Hq, d] over the first N positions into out."""
+def _step_args(Q, K_new, V_new, S_in, S_out, outlier_idx, cache: Cache, N: int, out, scores_dbg, workspace):
+    """Shapes, checks and the pointer arguments shared by qjl_decode_step and its no-alloc variant."""
     B, Hq, d = Q.shape
     if not Q.is_contiguous():
         raise ValueError("Q must be contiguous [B, Hq, d]")
@@ -230,6 +232,15 @@ def decode_step(Q, K_new, V_new, S_in, S_out, outlier_idx, cache: Cache, N: int,
     m = S_in.shape[0]
     m_out = 0 if S_out is None else S_out.shape[0]
     n_out = 0 if outlier_idx is None or outlier_idx.numel() == 0 else outlier_idx.shape[1]
+    return (B, Hq, Hkv, d, m, m_out, n_out)
+
+
+def decode_step(Q, K_new, V_new, S_in, S_out, outlier_idx, cache: Cache, N: int, out, *, sm_scale: float = 0.0,
+                estimator: int = 0, scores_dbg=None, nsplit: int = 0, workspace=None, stream=None) -> None:
+    """qjl_decode_step on torch tensors: append the new token (K_new, V_new [B, 1, Hkv, d], d contiguous)
+    at position N - 1 of the cache, then decode Q [B, Hq, d] over the first N positions into out."""
+    B, Hq, Hkv, d, m, m_out, n_out = _step_args(Q, K_new, V_new, S_in, S_out, outlier_idx, cache, N, out, scores_dbg,
+                                                workspace)
     if workspace is None:
         import torch
         workspace = torch.empty(max(1, decode_workspace_size(B, Hq, Hkv, N, m, m_out, nsplit, d)),
@@ -241,6 +252,23 @@ def decode_step(Q, K_new, V_new, S_in, S_out, outlier_idx, cache: Cache, N: int,
                                _ptr(cache.codes), _ptr(cache.meta), cache.Ncap, cache.nbits, sm_scale, estimator, _ptr(out),
                                _ptr(scores_dbg), nsplit, _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)), "qjl_decode_step")
+
+
+def decode_step_no_alloc(Q, K_new, V_new, S_in, S_out, outlier_idx, cache: Cache, N: int, out, *,
+                         sm_scale: float = 0.0, estimator: int = 0, scores_dbg=None, nsplit: int = 0,
+                         stream=None) -> None:
+    """qjl_decode_step_no_alloc on torch tensors: decode_step with the library's fixed device scratch as
+    its workspace (NO_ALLOC_SCRATCH_BYTES per GPU); nothing is allocated, by the library or here.  Calls
+    that overlap in time on one GPU race on the scratch."""
+    B, Hq, Hkv, d, m, m_out, n_out = _step_args(Q, K_new, V_new, S_in, S_out, outlier_idx, cache, N, out, scores_dbg,
+                                                None)
+    _check(lib.qjl_decode_step_no_alloc(_ptr(Q), _ptr(K_new), _ptr(V_new), _dtype_code(Q), B, Hq, Hkv, d, N,
+                                        K_new.stride(0), K_new.stride(2), V_new.stride(0), V_new.stride(2),
+                                        _ptr(S_in), m, _ptr(S_out) if m_out else 0, m_out,
+                                        _ptr(outlier_idx) if n_out else 0, n_out, _ptr(cache.bits), _ptr(cache.norms),
+                                        _ptr(cache.codes), _ptr(cache.meta), cache.Ncap, cache.nbits, sm_scale, estimator,
+                                        _ptr(out), _ptr(scores_dbg), nsplit, _stream(stream)),
+           "qjl_decode_step_no_alloc")
 
 
 def select_outliers(K, n_out: int, outlier_idx=None, *, workspace=None, stream=None):

@@ -254,8 +254,7 @@ WsLayout ws_layout(int B, int Hq, int d, int m, int m_out, int ns) {
 // Checks shared by the decode entry points (everything but the value arguments and the pointers),
 // then the launch descriptor.
 int prepare_decode(qjl::DecodeArgs& a, int qdt, int B, int Hq, int Hkv, int d, int64_t N, int m, int m_out, int n_out,
-                   int64_t Ncap, int vmode, int nbits, float sm_scale, int estimator, int nsplit, void* workspace,
-                   size_t ws_bytes) {
+                   int64_t Ncap, int vmode, int nbits, float sm_scale, int estimator, int nsplit) {
     if (qdt != QJL_BF16 && qdt != QJL_F32) return fail(QJL_ERR_INVALID_ARG, "qdt=%d is not a qjl_dtype", qdt);
     if (estimator != QJL_EST_ONE_SIDED && estimator != QJL_EST_TWO_SIDED)
         return fail(QJL_ERR_INVALID_ARG, "estimator=%d is not a qjl_estimator", estimator);
@@ -278,14 +277,7 @@ int prepare_decode(qjl::DecodeArgs& a, int qdt, int B, int Hq, int Hkv, int d, i
     if (nsplit > qjl::kMaxSplits) return fail(QJL_ERR_UNSUPPORTED, "nsplit=%d exceeds %d", nsplit, qjl::kMaxSplits);
     const int g = Hq / Hkv;
     const int ns = nsplit > 0 ? nsplit : qjl::decode_pick_nsplit(B, Hkv, g, N, m, m_out);
-    const WsLayout w = ws_layout(B, Hq, d, m, m_out, ns);
-    a.ws_need = w.total;
-    if (workspace) {
-        char* base = static_cast<char*>(workspace);
-        a.sq = reinterpret_cast<float*>(base + w.sq);
-        a.qconst = reinterpret_cast<float*>(base + w.qconst);
-        a.part = reinterpret_cast<float*>(base + w.part);
-    }
+    a.ws_need = ws_layout(B, Hq, d, m, m_out, ns).total;
     a.N = N;
     a.Ncap = Ncap;
     a.B = B;
@@ -304,11 +296,17 @@ int prepare_decode(qjl::DecodeArgs& a, int qdt, int B, int Hq, int Hkv, int d, i
     return QJL_OK;
 }
 
-// after the other pointer checks: the workspace the launch descriptor points into
-int check_workspace(const qjl::DecodeArgs& a, const void* workspace, size_t ws_bytes) {
+// after the other pointer checks: the workspace the launch descriptor points into (its regions are
+// laid out from the sizes prepare_decode recorded)
+int bind_workspace(qjl::DecodeArgs& a, void* workspace, size_t ws_bytes) {
     if (!workspace || ws_bytes < a.ws_need)
         return fail(QJL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", a.ws_need, workspace ? ws_bytes : (size_t)0);
     if (!aligned16(workspace)) return fail(QJL_ERR_MISALIGNED, "device pointers must be 16-byte aligned");
+    const WsLayout w = ws_layout(a.B, a.Hq, qjl::kD, a.m, a.m_out, a.nsplit);
+    char* base = static_cast<char*>(workspace);
+    a.sq = reinterpret_cast<float*>(base + w.sq);
+    a.qconst = reinterpret_cast<float*>(base + w.qconst);
+    a.part = reinterpret_cast<float*>(base + w.part);
     return QJL_OK;
 }
 
@@ -327,8 +325,7 @@ int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, 
                          int nsplit, void* workspace, size_t ws_bytes, hipStream_t stream) {
     g_last_error.clear();
     qjl::DecodeArgs a{};
-    int st = prepare_decode(a, qdt, B, Hq, Hkv, d, N, m, m_out, n_out, Ncap, vmode, nbits, sm_scale, estimator, nsplit, workspace,
-                            ws_bytes);
+    int st = prepare_decode(a, qdt, B, Hq, Hkv, d, N, m, m_out, n_out, Ncap, vmode, nbits, sm_scale, estimator, nsplit);
     if (st) return st;
     if (B == 0) return QJL_OK;
     if (!Q || !S_in || !bits || !norms || !out || (m_out && !S_out) || (n_out && !outlier_idx) ||
@@ -338,7 +335,7 @@ int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, 
         !aligned16(out) || (scores_dbg && !aligned16(scores_dbg)) ||
         (vmode == QJL_V_CODES && (!aligned16(codes) || !aligned16(meta))) || (vmode == QJL_V_F32 && !aligned16(V_f32)))
         return fail(QJL_ERR_MISALIGNED, "device pointers must be 16-byte aligned");
-    st = check_workspace(a, workspace, ws_bytes);
+    st = bind_workspace(a, workspace, ws_bytes);
     if (st) return st;
     a.Q = Q;
     a.S_in = S_in;
@@ -354,16 +351,48 @@ int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, 
     return hip_status(qjl::launch_decode(a, qdt, vmode, stream), "qjl_decode_attention launch");
 }
 
-int qjl_decode_step(const void* Q, const void* K_new, const void* V_new, int dt, int B, int Hq, int Hkv, int d, int64_t N,
-                    int64_t sK_b, int64_t sK_h, int64_t sV_b, int64_t sV_h, const void* S_in, int m, const void* S_out,
-                    int m_out, const int32_t* outlier_idx, int n_out, uint32_t* bits, uint16_t* norms, uint32_t* codes,
-                    uint16_t* meta, int64_t Ncap, int nbits, float sm_scale, int estimator, float* out, float* scores_dbg,
-                    int nsplit, void* workspace, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+// ------------------------------------------------------------------ allocation-free decode step
+// The workspace of qjl_decode_step_no_alloc: a fixed array in device memory, one copy per GPU.  In
+// host code `scratch` names a host-side stand-in, not device memory: its device address on each GPU
+// comes from hipGetSymbolAddress (with that GPU current) and only that address is ever passed on.
+static __device__ __align__(256) uint8_t scratch[QJL_NO_ALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+int scratch_of_current_device(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxScratchDevices) return fail(QJL_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxScratchDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(QJL_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return QJL_OK;
+}
+
+// qjl_decode_step and qjl_decode_step_no_alloc: every argument is checked first; then the workspace is
+// the caller's (no_alloc false) or the current device's scratch array (no_alloc true).
+int decode_step_impl(const void* Q, const void* K_new, const void* V_new, int dt, int B, int Hq, int Hkv, int d, int64_t N,
+                     int64_t sK_b, int64_t sK_h, int64_t sV_b, int64_t sV_h, const void* S_in, int m, const void* S_out,
+                     int m_out, const int32_t* outlier_idx, int n_out, uint32_t* bits, uint16_t* norms, uint32_t* codes,
+                     uint16_t* meta, int64_t Ncap, int nbits, float sm_scale, int estimator, float* out, float* scores_dbg,
+                     int nsplit, void* workspace, size_t ws_bytes, bool no_alloc, hipStream_t stream) {
     g_last_error.clear();
     if (N < 1) return fail(QJL_ERR_INVALID_ARG, "N=%lld: a decode step appends one token, so N >= 1", (long long)N);
     qjl::DecodeArgs a{};
-    int st = prepare_decode(a, dt, B, Hq, Hkv, d, N, m, m_out, n_out, Ncap, QJL_V_CODES, nbits, sm_scale, estimator, nsplit, workspace,
-                            ws_bytes);
+    int st = prepare_decode(a, dt, B, Hq, Hkv, d, N, m, m_out, n_out, Ncap, QJL_V_CODES, nbits, sm_scale, estimator, nsplit);
     if (st) return st;
     if (B == 0) return QJL_OK;
     if (!Q || !K_new || !V_new || !S_in || !bits || !norms || !codes || !meta || !out || (m_out && !S_out) ||
@@ -375,7 +404,15 @@ int qjl_decode_step(const void* Q, const void* K_new, const void* V_new, int dt,
         !aligned16(bits) || !aligned16(norms) || !aligned16(codes) || !aligned16(meta) || !aligned16(out) ||
         (scores_dbg && !aligned16(scores_dbg)) || sK_b % vec || sK_h % vec || sV_b % vec || sV_h % vec)
         return fail(QJL_ERR_MISALIGNED, "pointers must be 16-byte aligned and strides multiples of %lld elements", (long long)vec);
-    st = check_workspace(a, workspace, ws_bytes);
+    if (no_alloc) {
+        if (a.ws_need > QJL_NO_ALLOC_SCRATCH_BYTES)
+            return fail(QJL_ERR_WORKSPACE, "qjl_decode_step_no_alloc: these sizes need %zu bytes of workspace; the fixed scratch holds %zu",
+                        a.ws_need, (size_t)QJL_NO_ALLOC_SCRATCH_BYTES);
+        st = scratch_of_current_device(&workspace);
+        if (st) return st;
+        ws_bytes = QJL_NO_ALLOC_SCRATCH_BYTES;
+    }
+    st = bind_workspace(a, workspace, ws_bytes);
     if (st) return st;
     if (dt == QJL_BF16 && qjl::decode_uses_mfma(m, m_out, QJL_V_CODES, nbits)) {
         a.Q = Q;
@@ -411,6 +448,30 @@ int qjl_decode_step(const void* Q, const void* K_new, const void* V_new, int dt,
     return qjl_decode_attention(Q, dt, B, Hq, Hkv, d, N, S_in, m, S_out, m_out, outlier_idx, n_out, bits, norms, Ncap,
                                 QJL_V_CODES, codes, meta, nullptr, nbits, sm_scale, estimator, out, scores_dbg, nsplit, workspace,
                                 ws_bytes, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int qjl_decode_step(const void* Q, const void* K_new, const void* V_new, int dt, int B, int Hq, int Hkv, int d, int64_t N,
+                    int64_t sK_b, int64_t sK_h, int64_t sV_b, int64_t sV_h, const void* S_in, int m, const void* S_out,
+                    int m_out, const int32_t* outlier_idx, int n_out, uint32_t* bits, uint16_t* norms, uint32_t* codes,
+                    uint16_t* meta, int64_t Ncap, int nbits, float sm_scale, int estimator, float* out, float* scores_dbg,
+                    int nsplit, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    return decode_step_impl(Q, K_new, V_new, dt, B, Hq, Hkv, d, N, sK_b, sK_h, sV_b, sV_h, S_in, m, S_out, m_out, outlier_idx,
+                            n_out, bits, norms, codes, meta, Ncap, nbits, sm_scale, estimator, out, scores_dbg, nsplit, workspace,
+                            ws_bytes, false, stream);
+}
+
+int qjl_decode_step_no_alloc(const void* Q, const void* K_new, const void* V_new, int dt, int B, int Hq, int Hkv, int d,
+                             int64_t N, int64_t sK_b, int64_t sK_h, int64_t sV_b, int64_t sV_h, const void* S_in, int m,
+                             const void* S_out, int m_out, const int32_t* outlier_idx, int n_out, uint32_t* bits,
+                             uint16_t* norms, uint32_t* codes, uint16_t* meta, int64_t Ncap, int nbits, float sm_scale,
+                             int estimator, float* out, float* scores_dbg, int nsplit, hipStream_t stream) {
+    return decode_step_impl(Q, K_new, V_new, dt, B, Hq, Hkv, d, N, sK_b, sK_h, sV_b, sV_h, S_in, m, S_out, m_out, outlier_idx,
+                            n_out, bits, norms, codes, meta, Ncap, nbits, sm_scale, estimator, out, scores_dbg, nsplit, nullptr,
+                            0, true, stream);
 }
 
 size_t qjl_select_outliers_workspace_size(int B, int64_t T, int Hkv, int d) {

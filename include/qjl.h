@@ -220,6 +220,34 @@ int qjl_decode_step(const void* Q, const void* K_new, const void* V_new, int dt,
                     void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * qjl_decode_step_no_alloc - qjl_decode_step for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Same arguments, operations, results and errors as qjl_decode_step, except that there is no
+ * workspace argument: the workspace is a fixed device array inside the library of
+ * QJL_NO_ALLOC_SCRATCH_BYTES bytes, one per GPU, resolved on the first call on a device and held until
+ * the process ends.  A call whose workspace need (qjl_decode_workspace_size with the same sizes and
+ * nsplit) exceeds QJL_NO_ALLOC_SCRATCH_BYTES returns QJL_ERR_WORKSPACE before anything is enqueued.
+ * The call allocates nothing (no hipMalloc, no hipFree, no allocating library routine).
+ *   - The array belongs to the device that is current on the calling thread, which must be the
+ *     device of `stream`.
+ *   - Every call on one GPU uses the same array: calls that overlap in time on one GPU (different
+ *     streams, or threads) race on it and give undefined results; calls ordered on one stream are
+ *     safe.  The array keeps the last call's contents; no part of it needs to start at zero (every
+ *     byte a call reads was written earlier in the same call).
+ * For the Llama-3.1-70B decode shape (B = 16, Hq = 64, m = m_out = 256, library split choice) the
+ * workspace is about 3.2 MB.
+ */
+#define QJL_NO_ALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int qjl_decode_step_no_alloc(const void* Q, const void* K_new, const void* V_new, int dt, int B, int Hq, int Hkv, int d,
+                             int64_t N, int64_t sK_b, int64_t sK_h, int64_t sV_b, int64_t sV_h,
+                             const void* S_in, int m, const void* S_out, int m_out,
+                             const int32_t* outlier_idx, int n_out,
+                             uint32_t* bits, uint16_t* norms, uint32_t* codes, uint16_t* meta, int64_t Ncap, int nbits,
+                             float sm_scale, int estimator, float* out, float* scores_dbg, int nsplit,
+                             hipStream_t stream);
+
+/*
  * qjl_select_outliers - the outlier channels of every KV head, from prefill keys.
  *
  * The pages describe outlier channels as the few coordinates whose values are 10-100x those of the

@@ -228,3 +228,42 @@ def test_select_outliers_workspace_formula():
     assert qjl.lib.qjl_select_outliers_workspace_size(1, 65536, 8, 128) == 128 * 8 * 128 * 8
     assert qjl.lib.qjl_select_outliers_workspace_size(2, 100, 4, 128) == ((1 * 2 * 4 * 128 * 8 + 255) // 256) * 256
     assert qjl.lib.qjl_select_outliers_workspace_size(1, 10, 4, 64) == 0
+
+
+def step_no_alloc_call(**kw):
+    a = dict(Q=FAKE, K_new=FAKE, V_new=FAKE, dt=0, B=2, Hq=8, Hkv=2, d=128, N=1000, sK_b=2 * 128, sK_h=128,
+             sV_b=2 * 128, sV_h=128, S_in=FAKE, m=256, S_out=FAKE, m_out=256, oidx=FAKE, n_out=3, bits=FAKE,
+             norms=FAKE, codes=FAKE, meta=FAKE, Ncap=1024, nbits=2, sm_scale=0.0, estimator=0, out=FAKE, scores=0,
+             nsplit=0, stream=0)
+    a.update(kw)
+    return qjl.lib.qjl_decode_step_no_alloc(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), qjl.QJL_ERR_INVALID_ARG),
+    (dict(N=1025), qjl.QJL_ERR_INVALID_ARG),
+    (dict(Hq=9), qjl.QJL_ERR_INVALID_ARG),
+    (dict(nbits=5), qjl.QJL_ERR_UNSUPPORTED),
+    (dict(K_new=0), qjl.QJL_ERR_INVALID_ARG),
+    (dict(meta=MIS), qjl.QJL_ERR_MISALIGNED),
+    # 64 x 128 query heads: the query operands alone need 16 MiB, beyond the fixed 8 MiB scratch
+    (dict(B=64, Hq=128, Hkv=8), qjl.QJL_ERR_WORKSPACE),
+])
+def test_decode_step_no_alloc_rejects_before_touching_a_device(kw, status):
+    """Every argument error, and a workspace need beyond the fixed scratch, is reported before the
+    entry point looks for the device scratch (so no GPU is needed to see them)."""
+    assert step_no_alloc_call(**kw) == status
+    assert qjl.last_error() != ""
+    if status == qjl.QJL_ERR_WORKSPACE:
+        assert "fixed scratch" in qjl.last_error()
+        assert qjl.lib.qjl_decode_workspace_size(64, 128, 8, 128, 1000, 256, 256, 0) > qjl.NO_ALLOC_SCRATCH_BYTES
+
+
+def test_decode_step_no_alloc_empty_batch_is_noop():
+    assert step_no_alloc_call(B=0) == qjl.QJL_OK
+
+
+def test_no_alloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define QJL_NO_ALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == qjl.NO_ALLOC_SCRATCH_BYTES
