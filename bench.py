@@ -6,6 +6,10 @@ cache, then decode attention of every query head over all N cached tokens (query
 estimator scores, online softmax, value aggregation, split merge).  The cache of the first N-1
 tokens is built by the library's own prefill quantization before timing; inputs are resident in HBM.
 
+The headline workload is the largest single-GPU decode (Llama-3.1-70B shape: B=16, 64 query / 8 KV
+heads, N=131072); the Llama-2-7B and Llama-3-8B decode shapes are reported beside it, each with its own
+roofline, and the prefill quantize stream (65536 tokens x 8 KV heads) after them.
+
 Prints ONE JSON line.  value = keys scored per second = B * Hq * N / step time.
 """
 from __future__ import annotations
@@ -32,6 +36,13 @@ BYTES_PER_TOKEN_HEAD = 104          # 64 B signs + 4 B norms + 32 B codes + 4 B 
 DECODE_SOURCES = [os.path.join(ROOT, "bit_kv_cache_qjl_amd", "csrc", f) for f in
                   ("qjl_decode.hip", "qjl_decode_mfma.hip", "qjl_decode_common.h", "qjl_common.h")]
 DECODE_KERNEL = "decode_mfma_kernel"   # the dominant kernel of the 2-bit value decode workloads
+DECODE_KERNEL_VECTOR = "decode_kernel"  # the vector-unit (byte-table) decode
+HEADLINE = "llama31_70b_gqa_decode"
+DECODE_WORKLOADS = ("llama31_70b_gqa_decode", "llama2_7b_decode", "llama3_8b_gqa_decode")
+PATHS = {"auto": 0, "mfma": 1, "valu": 2}
+# the arithmetic each decode path computes in (bf16 keys, queries and JL matrices in; fp32 accumulation)
+DTYPE = {"mfma": "bf16 in; 1-bit keys x fp8e4m3x3 query, 2-bit values x fp8e4m3x3 weights on fp4 MFMA; fp32 acc",
+         "valu": "bf16 in; 1-bit keys x fp32 byte tables, 2-bit values x fp16 weights (v_dot2); fp32 acc"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_{}_traffic.json")
 
 
@@ -108,26 +119,66 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str) -> int:
     return 0
 
 
-def cpu_baseline(w: si.Workload, budget_s: float) -> dict:
-    """The oracle, as it stands, on a bounded sample of the same workload: whole (sequence, KV head)
-    units (quantize their keys and values, then decode every query head of the unit), until the
-    time budget is spent."""
-    import oracle
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        threads = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
+        return max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
     except Exception:  # pragma: no cover
-        threads = 1
+        return 1
+
+
+def _quality(s_est, s_exact, o_qjl, o_keys_only, o_exact) -> dict:
+    """Estimator quality of sampled heads against unquantized attention (reporting only)."""
+    s_est, s_exact = np.concatenate(s_est), np.concatenate(s_exact)
+    cos = lambda a, b: float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))  # noqa: E731
+    c_all = [cos(a, b) for a, b in zip(o_qjl, o_exact)]
+    c_keys = [cos(a, b) for a, b in zip(o_keys_only, o_exact)]
+    rmse = float(np.sqrt(np.mean((s_est - s_exact) ** 2)))
+    return {"score_rmse": rmse, "score_rmse_rel": rmse / float(np.sqrt(np.mean(s_exact ** 2))),
+            "score_corr": float(np.corrcoef(s_est, s_exact)[0, 1]),
+            "output_cosine_mean": float(np.mean(c_all)), "output_cosine_min": float(np.min(c_all)),
+            "output_cosine_keys_only_mean": float(np.mean(c_keys)), "heads": len(c_all), "keys": int(s_est.size)}
+
+
+def _unit_quality(w: si.Workload, oidx, S_in, S_out, Q, b: int, h: int, kq=None, vhat=None, k=None, v=None):
+    """Quality terms of one (sequence, KV head): estimator scores against <q, k>, and the decode output
+    (1-bit keys + quantized values; 1-bit keys + exact values) against exact attention."""
+    import oracle
+    k = si.key_slice(w, b, h, oidx) if k is None else k
+    v = si.value_slice(w, b, h) if v is None else v
+    if kq is None:
+        kq = oracle.quantize_key_vectors(k, S_in, S_out, oidx[h])
+        codes, meta = oracle.quantize_value_vectors(v, w.nbits)
+        vhat = oracle.dequantize_value_vectors(codes, meta)
+    sm = 1.0 / math.sqrt(w.d)
+    out = ([], [], [], [], [])
+    for i in range(w.g):
+        q = Q[b, h * w.g + i]
+        sq_in, sq_out = oracle.project_query(q, S_in, S_out, oidx[h])
+        s = oracle.estimator_scores(sq_in, sq_out, kq["bits"], kq["norms"])
+        out[0].append(s)
+        out[1].append(np.asarray(k, np.float64) @ np.asarray(q, np.float64))
+        out[2].append(oracle.attend(s, vhat, sm))
+        out[3].append(oracle.attend(s, v, sm))
+        out[4].append(oracle.exact_attention(q, k, v, sm))
+    return out
+
+
+def cpu_baseline(w: si.Workload, budget_s: float) -> tuple[dict, dict]:
+    """The oracle, as it stands, on a bounded sample of the same workload: whole (sequence, KV head)
+    units (quantize their keys and values, then decode every query head of the unit), until the
+    time budget is spent.  The estimator quality of those units is computed afterwards (untimed)."""
+    import oracle
     oidx = si.outlier_channels(w)
     S_in, S_out = si.jl_matrices(w)
     Q = si.queries(w)
     g = w.g
-    done_units = 0
-    t_start = time.perf_counter()
-    units = [(b, h) for b in range(w.B) for h in range(w.Hkv)]
-    for b, h in units:
+    done = []
+    elapsed = 0.0
+    for b, h in [(b, h) for b in range(w.B) for h in range(w.Hkv)]:
         k = si.key_slice(w, b, h, oidx)
         v = si.value_slice(w, b, h)
+        t0 = time.perf_counter()
         kq = oracle.quantize_key_vectors(k, S_in, S_out, oidx[h])
         codes, meta = oracle.quantize_value_vectors(v, w.nbits)
         vhat = oracle.dequantize_value_vectors(codes, meta)
@@ -135,74 +186,112 @@ def cpu_baseline(w: si.Workload, budget_s: float) -> dict:
             sq_in, sq_out = oracle.project_query(Q[b, h * g + i], S_in, S_out, oidx[h])
             s = oracle.estimator_scores(sq_in, sq_out, kq["bits"], kq["norms"])
             oracle.attend(s, vhat, 1.0 / math.sqrt(w.d))
-        done_units += 1
-        if time.perf_counter() - t_start >= budget_s and done_units >= 2:
+        elapsed += time.perf_counter() - t0
+        done.append((b, h, k, v, kq, vhat))
+        if elapsed >= budget_s and len(done) >= 2:
             break
-    elapsed = time.perf_counter() - t_start
-    keys = done_units * g * w.N
-    return {"value": keys / elapsed, "unit": "keys/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done_units} of {w.B * w.Hkv} (sequence, KV head) units of {w.name} "
+    keys = len(done) * g * w.N
+    terms = ([], [], [], [], [])
+    for b, h, k, v, kq, vhat in done[:2]:
+        for acc, part in zip(terms, _unit_quality(w, oidx, S_in, S_out, Q, b, h, kq, vhat, k, v)):
+            acc.extend(part)
+    base = {"value": keys / elapsed, "unit": "keys/s", "cores": _blas_threads(), "kind": "oracle",
+            "host_cores": len(os.sched_getaffinity(0)), "host_cpu_count": os.cpu_count(),
+            "sample": f"{len(done)} of {w.B * w.Hkv} (sequence, KV head) units of {w.name} "
                       f"(key + value quantization and decode of all {g} query heads over N={w.N}), "
-                      f"{elapsed:.1f} s"}
+                      f"{elapsed:.1f} s of oracle time; numpy fp64 with {_blas_threads()} BLAS threads for the "
+                      "matrix products, the rest on one core"}
+    return base, {w.name: {"units": [(b, h) for b, h, *_ in done[:2]], **_quality(*terms)}}
+
+
+def estimator_quality(w: si.Workload, unit=(0, 0)) -> dict:
+    """Quality of one sampled (sequence, KV head) unit of a workload (reporting only)."""
+    oidx = si.outlier_channels(w)
+    S_in, S_out = si.jl_matrices(w)
+    Q = si.queries(w)
+    terms = _unit_quality(w, oidx, S_in, S_out, Q, *unit)
+    return {"units": [list(unit)], **_quality(*terms)}
+
+
+def _timer_run(qjl, torch, names, run_one, steps: int) -> dict:
+    """HIP-event durations (recorded by the library on each launch's stream) over `steps` calls."""
+    qjl.timer_enable(True)
+    for k in names:
+        qjl.timer_read(k)
+    for _ in range(steps):
+        run_one()
+    torch.cuda.synchronize()
+    res = {k: qjl.timer_read(k) for k in names}
+    qjl.timer_enable(False)
+    return res
 
 
 def bench_quantize(qjl, torch, steps: int) -> dict:
-    """Prefill key-quantize stream: 65536 tokens x 8 KV heads, m = m_out = 512."""
+    """Prefill quantize stream: 65536 tokens x 8 KV heads, m = m_out = 512 (keys), 2-bit values.  Each
+    call takes the next of several input and output copies, so that no call finds its inputs (134 MB
+    of keys or values) or its outputs in the 256 MiB last-level cache."""
     w = si.WORKLOADS["prefill_quantize_64k"]
     oidx = si.outlier_channels(w)
     S_in, S_out = si.jl_matrices(w)
-    K = torch.from_numpy(si.keys(w, oidx)).cuda().to(torch.bfloat16)
+    K0 = torch.from_numpy(si.keys(w, oidx)).cuda().to(torch.bfloat16)
     Si = torch.from_numpy(S_in).cuda().to(torch.bfloat16)
     So = torch.from_numpy(S_out).cuda().to(torch.bfloat16)
     od = torch.from_numpy(oidx).cuda()
-    cache = qjl.alloc_cache(w.B, w.Hkv, w.N, w.m, w.m_out, w.nbits)
-    for _ in range(3):
-        qjl.quantize_keys(K, Si, So, od, cache.bits, cache.norms)
+    in_bytes = K0.numel() * K0.element_size()
+    copies = max(2, math.ceil(2 * MALL_BYTES / in_bytes))
+    Ks = [K0] + [K0.clone() for _ in range(copies - 1)]
+    caches = [qjl.alloc_cache(w.B, w.Hkv, w.N, w.m, w.m_out, w.nbits) for _ in range(copies)]
+    turn = [0]
+
+    def keys_once():
+        i = turn[0] % copies
+        turn[0] += 1
+        qjl.quantize_keys(Ks[i], Si, So, od, caches[i].bits, caches[i].norms)
+    for _ in range(2 * copies):
+        keys_once()
     torch.cuda.synchronize()
-    qjl.timer_enable(True)
-    qjl.timer_read("quantize_keys")
     t0 = time.perf_counter()
     for _ in range(steps):
-        qjl.quantize_keys(K, Si, So, od, cache.bits, cache.norms)
+        keys_once()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    n, ms = qjl.timer_read("quantize_keys")
-    qjl.timer_enable(False)
+    n, ms = _timer_run(qjl, torch, ["quantize_keys"], keys_once, steps)["quantize_keys"]
     kern_s = ms / 1e3 / max(n, 1)
     # outlier-channel selection over the same keys (one read of K, two launches)
     ws = torch.empty(qjl.lib.qjl_select_outliers_workspace_size(w.B, w.N, w.Hkv, w.d), dtype=torch.uint8, device="cuda")
     sel = torch.empty((w.Hkv, w.n_out), dtype=torch.int32, device="cuda")
-    for _ in range(3):
-        qjl.select_outliers(K, w.n_out, sel, workspace=ws)
+
+    def select_once():
+        i = turn[0] % copies
+        turn[0] += 1
+        qjl.select_outliers(Ks[i], w.n_out, sel, workspace=ws)
+    for _ in range(2 * copies):
+        select_once()
     torch.cuda.synchronize()
-    qjl.timer_enable(True)
-    qjl.timer_read("select_outliers")
-    for _ in range(steps):
-        qjl.select_outliers(K, w.n_out, sel, workspace=ws)
-    torch.cuda.synchronize()
-    ns, mss = qjl.timer_read("select_outliers")
-    qjl.timer_enable(False)
+    ns, mss = _timer_run(qjl, torch, ["select_outliers"], select_once, steps)["select_outliers"]
     sel_s = mss / 1e3 / max(ns, 1)
-    sel_bytes = float(K.numel() * K.element_size())
+    sel_bytes = float(in_bytes)
+    del Ks, K0
     # token-wise value codes of the same prefill: V [1, 65536, 8, 128] bf16 -> 2-bit code tiles + (min, step)
-    V = torch.from_numpy(si.values(w)).cuda().to(torch.bfloat16)
-    for _ in range(3):
-        qjl.quantize_values(V, w.nbits, cache.codes, cache.meta)
+    V0 = torch.from_numpy(si.values(w)).cuda().to(torch.bfloat16)
+    Vs = [V0] + [V0.clone() for _ in range(copies - 1)]
+
+    def values_once():
+        i = turn[0] % copies
+        turn[0] += 1
+        qjl.quantize_values(Vs[i], w.nbits, caches[i].codes, caches[i].meta)
+    for _ in range(2 * copies):
+        values_once()
     torch.cuda.synchronize()
-    qjl.timer_enable(True)
-    qjl.timer_read("quantize_values")
-    for _ in range(steps):
-        qjl.quantize_values(V, w.nbits, cache.codes, cache.meta)
-    torch.cuda.synchronize()
-    nv, msv = qjl.timer_read("quantize_values")
-    qjl.timer_enable(False)
+    nv, msv = _timer_run(qjl, torch, ["quantize_values"], values_once, steps)["quantize_values"]
     val_s = msv / 1e3 / max(nv, 1)
+    del Vs, V0
     # per token and KV head: d bf16 values read, d b / 8 code bytes and the fp16 (min, step) pair written
     val_bytes = float(w.B * w.N * w.Hkv * (2 * w.d + w.d * w.nbits // 8 + 4))
     tokens = w.B * w.N
     flops = 2.0 * w.d * w.m * tokens * w.Hkv          # inlier (d - n_out) m + outlier n_out m_out = d m MACs
     return {"workload": f"{w.name}: B={w.B} T={w.N} Hkv={w.Hkv} d={w.d} m=m_out={w.m} n_out={w.n_out}",
-            "tok_per_s": tokens / kern_s, "key_vectors_per_s": tokens * w.Hkv / kern_s,
+            "input_copies": copies, "tok_per_s": tokens / kern_s, "key_vectors_per_s": tokens * w.Hkv / kern_s,
             "kernel_ms": kern_s * 1e3, "wall_ms_per_call": wall * 1e3,
             "mfma": {"bound": "mfma", "achieved": flops / kern_s / 1e12, "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": flops / kern_s / 1e12 / BF16_MFMA_PEAK_TFLOPS,
@@ -215,57 +304,12 @@ def bench_quantize(qjl, torch, steps: int) -> dict:
                                 "frac": val_bytes / val_s / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": val_bytes}}
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama2_7b_decode",
-                    choices=["llama2_7b_decode", "llama3_8b_gqa_decode", "llama31_70b_gqa_decode"])
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0 = skip)")
-    ap.add_argument("--no-quantize", action="store_true", help="skip the prefill quantize measurement")
-    ap.add_argument("--graph", action="store_true",
-                    help="time the step captured once in a HIP graph and replayed (after checking that a replay "
-                         "reproduces the eager result) instead of eager launches")
-    ap.add_argument("--cache-copies", type=int, default=0,
-                    help="independent caches the steps rotate through (0: enough that consecutive steps never "
-                         f"find their cache in the {MALL_BYTES >> 20} MiB last-level cache)")
-    ap.add_argument("--value-bits", type=int, default=0, choices=[0, 2, 3, 4],
-                    help="token-wise value code width (0: the workload's, 2 bits)")
-    ap.add_argument("--nsplit", type=int, default=0,
-                    help="context chunks per (sequence, KV head) of the decode (0: the library's choice)")
-    ap.add_argument("--separate-calls", action="store_true",
-                    help="run the step as three calls (quantize keys, quantize values, decode attention) instead "
-                         "of the one decode-step call")
-    ap.add_argument("--quantize-only", action="store_true", help="only the prefill quantize measurement (profiling)")
-    ap.add_argument("--calibration-copy", action="store_true",
-                    help=f"run one plain {CALIB_BYTES >> 20} MiB device copy first (the reference kernel that "
-                         "scales the HBM byte counters of a --pmc profile)")
-    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a --calibration-copy "
-                         "run into the traffic record under profiles/, then exit")
-    args = ap.parse_args()
-    if args.traffic_from:
-        return write_traffic(*args.traffic_from, args.workload)
-    if args.gpus != 1:
-        print(f"bench.py: the library and this benchmark run on one GPU only (asked for --gpus {args.gpus}); "
-              "sharding decode by (sequence, KV head) across GPUs is not implemented", file=sys.stderr)
-        return 2
-
-    import torch
-    import bit_kv_cache_qjl_amd as qjl
-
-    if args.quantize_only:
-        print(json.dumps(bench_quantize(qjl, torch, args.steps)), flush=True)
-        return 0
-
-    w = si.WORKLOADS[args.workload]
-    if args.value_bits:
-        w = w.scaled(nbits=args.value_bits)
+def bench_decode(qjl, torch, w: si.Workload, args, path: str) -> dict:
+    """Time the serving step of one decode workload; returns its keys/s, step time and roofline."""
     N = w.N
     # algorithmic bytes per cached token and KV head: sign words, two fp16 norms, codes, fp16 (min, step)
     bytes_per_token_head = (w.m + w.m_out) // 8 + 4 + w.d * w.nbits // 8 + 4
-    log(f"bench: {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={N}; generating inputs")
+    log(f"bench: {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={N} ({path} decode); generating inputs")
     oidx = si.outlier_channels(w)
     S_in_np, S_out_np = si.jl_matrices(w)
     K = torch.from_numpy(si.keys(w, oidx)).cuda().to(torch.bfloat16)
@@ -283,7 +327,8 @@ def main() -> int:
         qjl.quantize_values(V[:, : N - 1], w.nbits, cache.codes, cache.meta, t0=0)
         caches.append(cache)
     log(f"bench: {copies} cache cop{'y' if copies == 1 else 'ies'} of {cache_bytes / 1e6:.0f} MB (steps rotate)")
-    k_new, v_new = K[:, N - 1:], V[:, N - 1:]
+    k_new, v_new = K[:, N - 1:].clone(), V[:, N - 1:].clone()
+    del K, V
     out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
     ws = torch.empty(qjl.decode_workspace_size(w.B, w.Hq, w.Hkv, N, w.m, w.m_out, args.nsplit), dtype=torch.uint8,
                      device="cuda")
@@ -293,7 +338,7 @@ def main() -> int:
         dst.copy_(src)
         del src, dst
     torch.cuda.synchronize()
-
+    pid = PATHS[path]
     turn = [0]
 
     def step():
@@ -303,9 +348,9 @@ def main() -> int:
             qjl.quantize_keys(k_new, S_in, S_out, od, cache.bits, cache.norms, t0=N - 1)
             qjl.quantize_values(v_new, w.nbits, cache.codes, cache.meta, t0=N - 1)
             qjl.decode_attention(Q, S_in, S_out, od, cache.bits, cache.norms, N, out, codes=cache.codes,
-                                 meta=cache.meta, nbits=w.nbits, nsplit=args.nsplit, workspace=ws)
+                                 meta=cache.meta, nbits=w.nbits, nsplit=args.nsplit, workspace=ws, path=pid)
         else:
-            qjl.decode_step(Q, k_new, v_new, S_in, S_out, od, cache, N, out, nsplit=args.nsplit, workspace=ws)
+            qjl.decode_step(Q, k_new, v_new, S_in, S_out, od, cache, N, out, nsplit=args.nsplit, workspace=ws, path=pid)
 
     log(f"bench: warmup {args.warmup}, timed {args.steps}")
     for _ in range(args.warmup):
@@ -358,50 +403,128 @@ def main() -> int:
             ms_per_step = timed(replay)
         else:
             log("bench: graph replay differs from the eager step; reporting eager timing")
-    # per-kernel durations (HIP events around each launch on its stream), in a separate eager pass
-    qjl.timer_enable(True)
-    for k in KERNELS:
-        qjl.timer_read(k)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    kernels = {k: qjl.timer_read(k) for k in KERNELS}
-    qjl.timer_enable(False)
+    # per-kernel durations: HIP events the library records around each launch on its stream, over
+    # another args.steps eager steps of the same rotation
+    kernels = _timer_run(qjl, torch, KERNELS, step, args.steps)
     keys_scored = w.B * w.Hq * N
     value = keys_scored / (ms_per_step / 1e3)
     n_dec, ms_dec = kernels["decode"]
     dec_s = ms_dec / 1e3 / max(n_dec, 1)
     bytes_alg = float(bytes_per_token_head) * w.B * w.Hkv * N
     achieved = bytes_alg / dec_s / 1e9
-    log("bench: kernel ms/launch " + ", ".join(f"{k}={v[1] / max(v[0], 1):.4f}" for k, v in kernels.items()))
-
-    result = {
-        "metric": METRIC, "value": value, "unit": "keys/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+    log(f"bench: {w.name} kernel ms/launch " + ", ".join(f"{k}={v[1] / max(v[0], 1):.4f}" for k, v in kernels.items()))
+    mfma_kernel = path != "valu"
+    return {
+        "value": value, "unit": "keys/s", "ms_per_step": ms_per_step,
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "N": N, "m": w.m,
                    "m_out": w.m_out, "n_out": w.n_out, "outlier_scale": w.outlier_scale, "value_bits": w.nbits,
+                   "decode_path": path,
                    "step": "append 1 token per sequence (key sketch + value codes) + decode attention over N",
                    "entry_points": ("qjl_quantize_keys + qjl_quantize_values + qjl_decode_attention"
-                                    if args.separate_calls else "qjl_decode_step")},
+                                    if args.separate_calls or path == "valu" else "qjl_decode_step")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(w.name) if w.nbits == 2 else None,   # counters: 2-bit runs
-                     "kernel": DECODE_KERNEL, "kernel_ms": dec_s * 1e3, "algorithmic_bytes": bytes_alg},
+                     # counters are taken for the 2-bit matrix-core decode
+                     "traffic": measured_traffic(w.name) if (w.nbits == 2 and mfma_kernel) else None,
+                     "kernel": DECODE_KERNEL if mfma_kernel else DECODE_KERNEL_VECTOR, "kernel_ms": dec_s * 1e3,
+                     "launches_timed": n_dec, "algorithmic_bytes": bytes_alg,
+                     "bytes_per_token_kv_head": bytes_per_token_head},
         "kernel_ms_per_launch": {k: v[1] / max(v[0], 1) for k, v in kernels.items()},
         "step_timing": {"mode": "hip_graph_replay" if (graph_ok and args.graph) else "eager",
                         "ms_per_step_eager": ms_eager, "graph_replay_matches_eager": graph_ok,
                         "cache_copies": copies, "cache_bytes": cache_bytes,
                         "nsplit": args.nsplit or "library choice"},
     }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE, choices=list(DECODE_WORKLOADS))
+    ap.add_argument("--extra-workloads", default=None,
+                    help="comma-separated decode workloads reported beside the headline (default: the other two; "
+                         "'' for none)")
+    ap.add_argument("--decode-path", default="auto", choices=list(PATHS),
+                    help="decode kernels: auto (matrix cores where the shape allows), mfma (matrix cores), valu "
+                         "(vector units, byte tables)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work (0 = skip)")
+    ap.add_argument("--no-quantize", action="store_true", help="skip the prefill quantize measurement")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the step captured once in a HIP graph and replayed (after checking that a replay "
+                         "reproduces the eager result) instead of eager launches")
+    ap.add_argument("--cache-copies", type=int, default=0,
+                    help="independent caches the steps rotate through (0: enough that consecutive steps never "
+                         f"find their cache in the {MALL_BYTES >> 20} MiB last-level cache)")
+    ap.add_argument("--value-bits", type=int, default=0, choices=[0, 2, 3, 4],
+                    help="token-wise value code width (0: the workload's, 2 bits)")
+    ap.add_argument("--nsplit", type=int, default=0,
+                    help="context chunks per (sequence, KV head) of the decode (0: the library's choice)")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="run the step as three calls (quantize keys, quantize values, decode attention) instead "
+                         "of the one decode-step call")
+    ap.add_argument("--quantize-only", action="store_true", help="only the prefill quantize measurement (profiling)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help=f"run one plain {CALIB_BYTES >> 20} MiB device copy first (the reference kernel that "
+                         "scales the HBM byte counters of a --pmc profile)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a --calibration-copy "
+                         "run into the traffic record under profiles/, then exit")
+    args = ap.parse_args()
+    if args.traffic_from:
+        return write_traffic(*args.traffic_from, args.workload)
+    if args.gpus != 1:
+        print(f"bench.py: the library and this benchmark run on one GPU only (asked for --gpus {args.gpus}); "
+              "sharding decode by (sequence, KV head) across GPUs is not implemented", file=sys.stderr)
+        return 2
+
+    import torch
+    import bit_kv_cache_qjl_amd as qjl
+
+    if args.quantize_only:
+        print(json.dumps(bench_quantize(qjl, torch, args.steps)), flush=True)
+        return 0
+
+    extras = ([x for x in DECODE_WORKLOADS if x != args.workload] if args.extra_workloads is None
+              else [x for x in args.extra_workloads.split(",") if x])
+    for x in extras:
+        if x not in DECODE_WORKLOADS:
+            raise SystemExit(f"bench.py: unknown workload {x!r}")
+
+    def workload(name):
+        w = si.WORKLOADS[name]
+        return w.scaled(nbits=args.value_bits) if args.value_bits else w
+
+    path = args.decode_path
+    kpath = "valu" if path == "valu" else "mfma"
+    head = bench_decode(qjl, torch, workload(args.workload), args, path)
+    torch.cuda.empty_cache()
+    result = {
+        "metric": METRIC, "value": head["value"], "unit": "keys/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": DTYPE[kpath], "data": "synthetic",
+        "config": head["config"], "roofline": head["roofline"],
+        "kernel_ms_per_launch": head["kernel_ms_per_launch"], "step_timing": head["step_timing"],
+    }
+    if extras:
+        result["other_decode_workloads"] = {}
+        for x in extras:
+            r = bench_decode(qjl, torch, workload(x), args, path)
+            torch.cuda.empty_cache()
+            result["other_decode_workloads"][x] = {k: r[k] for k in ("value", "unit", "ms_per_step", "roofline",
+                                                                     "kernel_ms_per_launch", "step_timing")}
     if not args.no_quantize:
         log("bench: prefill quantize stream")
-        del K, V
-        torch.cuda.empty_cache()
         result["quantize"] = bench_quantize(qjl, torch, max(5, args.steps // 2))
     if args.cpu_budget > 0:
-        log(f"bench: oracle on the host (~{args.cpu_budget:.0f} s)")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        log(f"bench: oracle on the host (~{args.cpu_budget:.0f} s), then estimator quality")
+        base, quality = cpu_baseline(workload(args.workload), args.cpu_budget)
+        for x in extras:
+            quality[x] = estimator_quality(workload(x))
+        result["cpu_baseline"] = base
+        result["estimator_quality"] = {"reference": "unquantized attention (exact <q, k> and fp32 values) on the "
+                                                    "same sampled units", **quality}
     print(json.dumps(result), flush=True)
     return 0
 

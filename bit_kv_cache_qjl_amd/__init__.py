@@ -28,6 +28,9 @@ QJL_V_CODES = 0
 QJL_V_F32 = 1
 QJL_EST_ONE_SIDED = 0
 QJL_EST_TWO_SIDED = 1
+QJL_PATH_AUTO = 0
+QJL_PATH_MATRIX = 1
+QJL_PATH_VECTOR = 2
 NO_ALLOC_SCRATCH_BYTES = 8 << 20    # QJL_NO_ALLOC_SCRATCH_BYTES: the fixed workspace of qjl_decode_step_no_alloc
 
 if not os.path.exists(LIB_PATH):
@@ -54,13 +57,13 @@ lib.qjl_decode_workspace_size.restype = _sz
 lib.qjl_decode_workspace_size.argtypes = [_i, _i, _i, _i, _i64, _i, _i, _i]
 lib.qjl_decode_attention.restype = _i
 lib.qjl_decode_attention.argtypes = [_p, _i, _i, _i, _i, _i, _i64, _p, _i, _p, _i, _p, _i, _p, _p, _i64,
-                                     _i, _p, _p, _p, _i, _f, _i, _p, _p, _i, _p, _sz, _p]
+                                     _i, _p, _p, _p, _i, _f, _i, _i, _p, _p, _i, _p, _sz, _p]
 lib.qjl_decode_step.restype = _i
 lib.qjl_decode_step.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _p, _i, _p, _i, _p, _i,
-                                _p, _p, _p, _p, _i64, _i, _f, _i, _p, _p, _i, _p, _sz, _p]
+                                _p, _p, _p, _p, _i64, _i, _f, _i, _i, _p, _p, _i, _p, _sz, _p]
 lib.qjl_decode_step_no_alloc.restype = _i
 lib.qjl_decode_step_no_alloc.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _p, _i, _p, _i, _p,
-                                         _i, _p, _p, _p, _p, _i64, _i, _f, _i, _p, _p, _i, _p]
+                                         _i, _p, _p, _p, _p, _i64, _i, _f, _i, _i, _p, _p, _i, _p]
 lib.qjl_select_outliers_workspace_size.restype = _sz
 lib.qjl_select_outliers_workspace_size.argtypes = [_i, _i64, _i, _i]
 lib.qjl_select_outliers.restype = _i
@@ -113,6 +116,70 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
 
 
+def _on_device(**tensors) -> None:
+    """Every array the C ABI receives is device memory of one GPU."""
+    devs = {t.device for t in tensors.values() if t is not None}
+    for name, t in tensors.items():
+        if t is not None and t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device (cuda) tensor, got {t.device}")
+    if len(devs) > 1:
+        raise ValueError(f"all tensors must be on one device, got {sorted(str(d) for d in devs)}")
+
+
+def _check_tensor(name: str, t, dtype, ndim: int | None = None, shape: dict | None = None) -> None:
+    """dtype, rank and the given {dimension: size} of one argument (TypeError / ValueError otherwise)."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    for dim, size in (shape or {}).items():
+        if t.shape[dim] != size:
+            raise ValueError(f"{name}: dimension {dim} must be {size}, got shape {tuple(t.shape)}")
+
+
+def _sketch_args(S_in, S_out, outlier_idx, dtype, Hkv: int, d: int) -> tuple[int, int, int]:
+    """JL matrices [m, d] / [m_out, d] of the key (or query) dtype and the int32 outlier list
+    [Hkv, n_out]; returns (m, m_out, n_out)."""
+    _check_tensor("S_in", S_in, dtype, 2, {1: d})
+    m_out = 0
+    if S_out is not None and S_out.numel():
+        _check_tensor("S_out", S_out, dtype, 2, {1: d})
+        m_out = int(S_out.shape[0])
+    n_out = 0
+    if outlier_idx is not None and outlier_idx.numel():
+        import torch
+        _check_tensor("outlier_idx", outlier_idx, torch.int32, 2, {0: Hkv})
+        n_out = int(outlier_idx.shape[1])
+    return int(S_in.shape[0]), m_out, n_out
+
+
+def _key_cache_args(bits, norms, B: int, Hkv: int, m: int, m_out: int) -> int:
+    """Sign words int32 [Bc, Hkv, Ncap, (m + m_out) / 32] and norms float16 [Bc, Hkv, Ncap, 2] with
+    Bc >= B; returns Ncap."""
+    import torch
+    _check_tensor("bits", bits, torch.int32, 4, {1: Hkv, 3: (m + m_out) // 32})
+    _check_tensor("norms", norms, torch.float16, 4, {0: bits.shape[0], 1: Hkv, 2: bits.shape[2], 3: 2})
+    if bits.shape[0] < B:
+        raise ValueError(f"the cache holds {bits.shape[0]} sequences, the call has {B}")
+    return int(bits.shape[2])
+
+
+def _value_cache_args(codes, meta, B: int, Hkv: int, nbits: int, d: int, Ncap: int | None = None) -> int:
+    """Code tiles int32 [Bc, Hkv, ceil(Ncap/32), d, nbits] and meta float16 [Bc, Hkv, Ncap, 2] with
+    Bc >= B; returns Ncap."""
+    import torch
+    if nbits not in (2, 3, 4):
+        raise ValueError(f"nbits must be 2, 3 or 4, got {nbits}")
+    Nc = int(meta.shape[2]) if meta.dim() == 4 else -1
+    _check_tensor("meta", meta, torch.float16, 4, {1: Hkv, 3: 2})
+    if Ncap is not None and Nc != Ncap:
+        raise ValueError(f"meta holds {Nc} positions, the key cache {Ncap}")
+    _check_tensor("codes", codes, torch.int32, 5, {0: meta.shape[0], 1: Hkv, 2: code_tiles(Nc), 3: d, 4: nbits})
+    if meta.shape[0] < B:
+        raise ValueError(f"the cache holds {meta.shape[0]} sequences, the call has {B}")
+    return Nc
+
+
 def status_string(status: int) -> str:
     return lib.qjl_status_string(status).decode()
 
@@ -155,30 +222,30 @@ def alloc_cache(B: int, Hkv: int, Ncap: int, m: int, m_out: int, nbits: int = 2,
 
 
 def quantize_keys(K, S_in, S_out, outlier_idx, bits, norms, t0: int = 0, stream=None) -> None:
-    """qjl_quantize_keys on torch tensors.  K [B, T, Hkv, d] (any strides with d contiguous)."""
+    """qjl_quantize_keys on torch tensors.  K [B, T, Hkv, d] (any strides with d contiguous); S_in, S_out
+    of K's dtype; outlier_idx int32 [Hkv, n_out]; bits / norms the key cache (alloc_cache)."""
+    if K.dim() != 4 or K.stride(3) != 1:
+        raise ValueError("K must be [B, T, Hkv, d] with the d channels contiguous")
     B, T, Hkv, d = K.shape
-    if K.stride(3) != 1:
-        raise ValueError("the d channels of K must be contiguous")
     _contiguous(S_in=S_in, S_out=S_out, outlier_idx=outlier_idx, bits=bits, norms=norms)
-    m = S_in.shape[0]
-    m_out = 0 if S_out is None else S_out.shape[0]
-    n_out = 0 if outlier_idx is None or outlier_idx.numel() == 0 else outlier_idx.shape[1]
+    _on_device(K=K, S_in=S_in, S_out=S_out, outlier_idx=outlier_idx, bits=bits, norms=norms)
+    m, m_out, n_out = _sketch_args(S_in, S_out, outlier_idx, K.dtype, Hkv, d)
+    Ncap = _key_cache_args(bits, norms, B, Hkv, m, m_out)
     _check(lib.qjl_quantize_keys(_ptr(K), _dtype_code(K), B, T, Hkv, d, K.stride(0), K.stride(1), K.stride(2),
                                  _ptr(S_in), m, _ptr(S_out) if m_out else 0, m_out,
                                  _ptr(outlier_idx) if n_out else 0, n_out, _ptr(bits), _ptr(norms),
-                                 bits.shape[2], t0, _stream(stream)), "qjl_quantize_keys")
+                                 Ncap, t0, _stream(stream)), "qjl_quantize_keys")
 
 
 def quantize_values(V, nbits: int, codes, meta, t0: int = 0, stream=None) -> None:
     """qjl_quantize_values on torch tensors.  V [B, T, Hkv, d] (d contiguous); codes are the code
-    tiles of a cache whose capacity is meta.shape[2]."""
+    tiles of a cache whose capacity is meta.shape[2] (alloc_cache with the same nbits)."""
+    if V.dim() != 4 or V.stride(3) != 1:
+        raise ValueError("V must be [B, T, Hkv, d] with the d channels contiguous")
     B, T, Hkv, d = V.shape
-    if V.stride(3) != 1:
-        raise ValueError("the d channels of V must be contiguous")
     _contiguous(codes=codes, meta=meta)
-    Ncap = meta.shape[2]
-    if codes.numel() * codes.element_size() < B * Hkv * code_tiles(Ncap) * d * nbits * 4:
-        raise ValueError("codes is smaller than the code tiles of a cache of this capacity")
+    _on_device(V=V, codes=codes, meta=meta)
+    Ncap = _value_cache_args(codes, meta, B, Hkv, nbits, d)
     _check(lib.qjl_quantize_values(_ptr(V), _dtype_code(V), B, T, Hkv, d, V.stride(0), V.stride(1), V.stride(2),
                                    nbits, _ptr(codes), _ptr(meta), Ncap, t0, _stream(stream)),
            "qjl_quantize_values")
@@ -190,37 +257,58 @@ def decode_workspace_size(B: int, Hq: int, Hkv: int, N: int, m: int, m_out: int,
 
 
 def decode_attention(Q, S_in, S_out, outlier_idx, bits, norms, N: int, out, *, codes=None, meta=None,
-                     V_f32=None, nbits: int = 2, sm_scale: float = 0.0, estimator: int = 0, scores_dbg=None,
-                     nsplit: int = 0, workspace=None, stream=None) -> None:
-    """qjl_decode_attention on torch tensors.  Q [B, Hq, d] contiguous; out [B, Hq, d] fp32.
-    estimator: QJL_EST_ONE_SIDED (0) or QJL_EST_TWO_SIDED (1)."""
-    B, Hq, d = Q.shape
-    if not Q.is_contiguous():
+                     V_f32=None, nbits: int | None = None, sm_scale: float = 0.0, estimator: int = 0, path: int = 0,
+                     scores_dbg=None, nsplit: int = 0, workspace=None, stream=None) -> None:
+    """qjl_decode_attention on torch tensors.  Q [B, Hq, d] contiguous; out [B, Hq, d] fp32; S_in, S_out
+    of Q's dtype; values as code tiles + meta (nbits taken from the tiles when not given) or fp32 V_f32
+    [B, Hkv, Ncap, d].  estimator: QJL_EST_ONE_SIDED (0) or QJL_EST_TWO_SIDED (1); path: QJL_PATH_AUTO (0),
+    QJL_PATH_MATRIX (1, matrix cores) or QJL_PATH_VECTOR (2, vector units)."""
+    import torch
+    if Q.dim() != 3 or not Q.is_contiguous():
         raise ValueError("Q must be contiguous [B, Hq, d]")
+    B, Hq, d = Q.shape
     _contiguous(S_in=S_in, S_out=S_out, outlier_idx=outlier_idx, bits=bits, norms=norms, out=out, codes=codes,
                 meta=meta, V_f32=V_f32, scores_dbg=scores_dbg, workspace=workspace)
-    Hkv = bits.shape[1]
-    m = S_in.shape[0]
-    m_out = 0 if S_out is None else S_out.shape[0]
-    n_out = 0 if outlier_idx is None or outlier_idx.numel() == 0 else outlier_idx.shape[1]
-    vmode = QJL_V_F32 if V_f32 is not None else QJL_V_CODES
+    _on_device(Q=Q, S_in=S_in, S_out=S_out, outlier_idx=outlier_idx, bits=bits, norms=norms, out=out, codes=codes,
+               meta=meta, V_f32=V_f32, scores_dbg=scores_dbg, workspace=workspace)
+    if bits.dim() != 4:
+        raise ValueError(f"bits must be [B, Hkv, Ncap, W], got shape {tuple(bits.shape)}")
+    Hkv = int(bits.shape[1])
+    m, m_out, n_out = _sketch_args(S_in, S_out, outlier_idx, Q.dtype, Hkv, d)
+    Ncap = _key_cache_args(bits, norms, B, Hkv, m, m_out)
+    _check_tensor("out", out, torch.float32, 3, {0: B, 1: Hq, 2: d})
+    if scores_dbg is not None:
+        _check_tensor("scores_dbg", scores_dbg, torch.float32, 3, {0: B, 1: Hq})
+        if N > 0 and scores_dbg.shape[2] != N:
+            raise ValueError(f"scores_dbg must be [B, Hq, N] with N = {N}, got shape {tuple(scores_dbg.shape)}")
+    if V_f32 is not None:
+        vmode = QJL_V_F32
+        _check_tensor("V_f32", V_f32, torch.float32, 4, {0: bits.shape[0], 1: Hkv, 2: Ncap, 3: d})
+        nbits = 2 if nbits is None else nbits
+    else:
+        vmode = QJL_V_CODES
+        if codes is None or meta is None:
+            raise ValueError("values: give codes and meta, or V_f32")
+        if nbits is None:
+            nbits = int(codes.shape[-1])
+        _value_cache_args(codes, meta, B, Hkv, nbits, d, Ncap)
     if workspace is None:
-        import torch
         workspace = torch.empty(max(1, decode_workspace_size(B, Hq, Hkv, N, m, m_out, nsplit, d)),
                                 dtype=torch.uint8, device=Q.device)
     _check(lib.qjl_decode_attention(_ptr(Q), _dtype_code(Q), B, Hq, Hkv, d, N, _ptr(S_in), m,
                                     _ptr(S_out) if m_out else 0, m_out, _ptr(outlier_idx) if n_out else 0, n_out,
-                                    _ptr(bits), _ptr(norms), bits.shape[2], vmode, _ptr(codes), _ptr(meta),
-                                    _ptr(V_f32), nbits, sm_scale, estimator, _ptr(out), _ptr(scores_dbg), nsplit,
+                                    _ptr(bits), _ptr(norms), Ncap, vmode, _ptr(codes), _ptr(meta),
+                                    _ptr(V_f32), nbits, sm_scale, estimator, path, _ptr(out), _ptr(scores_dbg), nsplit,
                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
                                     _stream(stream)), "qjl_decode_attention")
 
 
 def _step_args(Q, K_new, V_new, S_in, S_out, outlier_idx, cache: Cache, N: int, out, scores_dbg, workspace):
     """Shapes, checks and the pointer arguments shared by qjl_decode_step and its no-alloc variant."""
-    B, Hq, d = Q.shape
-    if not Q.is_contiguous():
+    import torch
+    if Q.dim() != 3 or not Q.is_contiguous():
         raise ValueError("Q must be contiguous [B, Hq, d]")
+    B, Hq, d = Q.shape
     for name, t in (("K_new", K_new), ("V_new", V_new)):
         if t.dim() != 4 or t.shape[1] != 1 or t.stride(3) != 1:
             raise ValueError(f"{name} must be [B, 1, Hkv, d] with the d channels contiguous")
@@ -228,15 +316,27 @@ def _step_args(Q, K_new, V_new, S_in, S_out, outlier_idx, cache: Cache, N: int, 
             raise TypeError(f"{name} must have the dtype of Q")
     _contiguous(S_in=S_in, S_out=S_out, outlier_idx=outlier_idx, bits=cache.bits, norms=cache.norms,
                 codes=cache.codes, meta=cache.meta, out=out, scores_dbg=scores_dbg, workspace=workspace)
-    Hkv = cache.bits.shape[1]
-    m = S_in.shape[0]
-    m_out = 0 if S_out is None else S_out.shape[0]
-    n_out = 0 if outlier_idx is None or outlier_idx.numel() == 0 else outlier_idx.shape[1]
+    _on_device(Q=Q, K_new=K_new, V_new=V_new, S_in=S_in, S_out=S_out, outlier_idx=outlier_idx, bits=cache.bits,
+               norms=cache.norms, codes=cache.codes, meta=cache.meta, out=out, scores_dbg=scores_dbg,
+               workspace=workspace)
+    Hkv = int(cache.bits.shape[1])
+    for name, t in (("K_new", K_new), ("V_new", V_new)):
+        if t.shape[0] != B or t.shape[2] != Hkv or t.shape[3] != d:
+            raise ValueError(f"{name} must be [B={B}, 1, Hkv={Hkv}, d={d}], got shape {tuple(t.shape)}")
+    m, m_out, n_out = _sketch_args(S_in, S_out, outlier_idx, Q.dtype, Hkv, d)
+    if (m, m_out) != (cache.m, cache.m_out):
+        raise ValueError(f"S_in / S_out give m={m}, m_out={m_out}; the cache was built for {cache.m}, {cache.m_out}")
+    Ncap = _key_cache_args(cache.bits, cache.norms, B, Hkv, m, m_out)
+    _value_cache_args(cache.codes, cache.meta, B, Hkv, cache.nbits, d, Ncap)
+    _check_tensor("out", out, torch.float32, 3, {0: B, 1: Hq, 2: d})
+    if scores_dbg is not None:
+        _check_tensor("scores_dbg", scores_dbg, torch.float32, 3, {0: B, 1: Hq, 2: N})
     return (B, Hq, Hkv, d, m, m_out, n_out)
 
 
 def decode_step(Q, K_new, V_new, S_in, S_out, outlier_idx, cache: Cache, N: int, out, *, sm_scale: float = 0.0,
-                estimator: int = 0, scores_dbg=None, nsplit: int = 0, workspace=None, stream=None) -> None:
+                estimator: int = 0, path: int = 0, scores_dbg=None, nsplit: int = 0, workspace=None,
+                stream=None) -> None:
     """qjl_decode_step on torch tensors: append the new token (K_new, V_new [B, 1, Hkv, d], d contiguous)
     at position N - 1 of the cache, then decode Q [B, Hq, d] over the first N positions into out."""
     B, Hq, Hkv, d, m, m_out, n_out = _step_args(Q, K_new, V_new, S_in, S_out, outlier_idx, cache, N, out, scores_dbg,
@@ -249,13 +349,14 @@ def decode_step(Q, K_new, V_new, S_in, S_out, outlier_idx, cache: Cache, N: int,
                                K_new.stride(0), K_new.stride(2), V_new.stride(0), V_new.stride(2),
                                _ptr(S_in), m, _ptr(S_out) if m_out else 0, m_out,
                                _ptr(outlier_idx) if n_out else 0, n_out, _ptr(cache.bits), _ptr(cache.norms),
-                               _ptr(cache.codes), _ptr(cache.meta), cache.Ncap, cache.nbits, sm_scale, estimator, _ptr(out),
+                               _ptr(cache.codes), _ptr(cache.meta), cache.Ncap, cache.nbits, sm_scale, estimator, path,
+                               _ptr(out),
                                _ptr(scores_dbg), nsplit, _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)), "qjl_decode_step")
 
 
 def decode_step_no_alloc(Q, K_new, V_new, S_in, S_out, outlier_idx, cache: Cache, N: int, out, *,
-                         sm_scale: float = 0.0, estimator: int = 0, scores_dbg=None, nsplit: int = 0,
+                         sm_scale: float = 0.0, estimator: int = 0, path: int = 0, scores_dbg=None, nsplit: int = 0,
                          stream=None) -> None:
     """qjl_decode_step_no_alloc on torch tensors: decode_step with the library's fixed device scratch as
     its workspace (NO_ALLOC_SCRATCH_BYTES per GPU); nothing is allocated, by the library or here.  Calls
@@ -267,7 +368,7 @@ def decode_step_no_alloc(Q, K_new, V_new, S_in, S_out, outlier_idx, cache: Cache
                                         _ptr(S_in), m, _ptr(S_out) if m_out else 0, m_out,
                                         _ptr(outlier_idx) if n_out else 0, n_out, _ptr(cache.bits), _ptr(cache.norms),
                                         _ptr(cache.codes), _ptr(cache.meta), cache.Ncap, cache.nbits, sm_scale, estimator,
-                                        _ptr(out), _ptr(scores_dbg), nsplit, _stream(stream)),
+                                        path, _ptr(out), _ptr(scores_dbg), nsplit, _stream(stream)),
            "qjl_decode_step_no_alloc")
 
 
@@ -275,12 +376,14 @@ def select_outliers(K, n_out: int, outlier_idx=None, *, workspace=None, stream=N
     """qjl_select_outliers on torch tensors: K [B, T, Hkv, d] (d contiguous) -> int32 [Hkv, n_out],
     the channels with the largest mean |k_c| of each KV head, ascending."""
     import torch
+    if K.dim() != 4 or K.stride(3) != 1:
+        raise ValueError("K must be [B, T, Hkv, d] with the d channels contiguous")
     B, T, Hkv, d = K.shape
-    if K.stride(3) != 1:
-        raise ValueError("the d channels of K must be contiguous")
     if outlier_idx is None:
         outlier_idx = torch.empty((Hkv, n_out), dtype=torch.int32, device=K.device)
     _contiguous(outlier_idx=outlier_idx, workspace=workspace)
+    _on_device(K=K, outlier_idx=outlier_idx, workspace=workspace)
+    _check_tensor("outlier_idx", outlier_idx, torch.int32, 2, {0: Hkv, 1: n_out})
     if workspace is None:
         workspace = torch.empty(max(1, int(lib.qjl_select_outliers_workspace_size(B, T, Hkv, d))), dtype=torch.uint8,
                                 device=K.device)

@@ -254,8 +254,10 @@ WsLayout ws_layout(int B, int Hq, int d, int m, int m_out, int ns) {
 // Checks shared by the decode entry points (everything but the value arguments and the pointers),
 // then the launch descriptor.
 int prepare_decode(qjl::DecodeArgs& a, int qdt, int B, int Hq, int Hkv, int d, int64_t N, int m, int m_out, int n_out,
-                   int64_t Ncap, int vmode, int nbits, float sm_scale, int estimator, int nsplit) {
+                   int64_t Ncap, int vmode, int nbits, float sm_scale, int estimator, int path, int nsplit) {
     if (qdt != QJL_BF16 && qdt != QJL_F32) return fail(QJL_ERR_INVALID_ARG, "qdt=%d is not a qjl_dtype", qdt);
+    if (path != QJL_PATH_AUTO && path != QJL_PATH_MATRIX && path != QJL_PATH_VECTOR)
+        return fail(QJL_ERR_INVALID_ARG, "path=%d is not a qjl_decode_path", path);
     if (estimator != QJL_EST_ONE_SIDED && estimator != QJL_EST_TWO_SIDED)
         return fail(QJL_ERR_INVALID_ARG, "estimator=%d is not a qjl_estimator", estimator);
     if (vmode != QJL_V_CODES && vmode != QJL_V_F32) return fail(QJL_ERR_INVALID_ARG, "vmode=%d is not a qjl_vmode", vmode);
@@ -274,6 +276,11 @@ int prepare_decode(qjl::DecodeArgs& a, int qdt, int B, int Hq, int Hkv, int d, i
     if (vmode == QJL_V_CODES && nbits != 2 && !qjl::decode_uses_mfma(m, m_out, QJL_V_CODES, nbits))
         return fail(QJL_ERR_UNSUPPORTED, "decode of %d-bit value codes needs m + m_out <= 512 (got m=%d m_out=%d)", nbits, m,
                     m_out);
+    if (path == QJL_PATH_MATRIX && !qjl::decode_uses_mfma(m, m_out, vmode, nbits))
+        return fail(QJL_ERR_UNSUPPORTED, "the matrix-core decode needs value codes and (m, m_out) in {(128|256|512, 0), "
+                    "(128, 128), (256, 256)}; got m=%d m_out=%d %s", m, m_out, vmode == QJL_V_CODES ? "codes" : "fp32 values");
+    if (path == QJL_PATH_VECTOR && vmode == QJL_V_CODES && nbits != 2)
+        return fail(QJL_ERR_UNSUPPORTED, "the vector-unit decode reads 2-bit value codes or fp32 values (got %d-bit codes)", nbits);
     if (nsplit > qjl::kMaxSplits) return fail(QJL_ERR_UNSUPPORTED, "nsplit=%d exceeds %d", nsplit, qjl::kMaxSplits);
     const int g = Hq / Hkv;
     const int ns = nsplit > 0 ? nsplit : qjl::decode_pick_nsplit(B, Hkv, g, N, m, m_out);
@@ -293,6 +300,7 @@ int prepare_decode(qjl::DecodeArgs& a, int qdt, int B, int Hq, int Hkv, int d, i
     const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)d);
     a.z_scale = scale * qjl::kLog2e;
     a.estimator = estimator;
+    a.path = path;
     return QJL_OK;
 }
 
@@ -321,11 +329,11 @@ size_t qjl_decode_workspace_size(int B, int Hq, int Hkv, int d, int64_t N, int m
 int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, int64_t N, const void* S_in, int m,
                          const void* S_out, int m_out, const int32_t* outlier_idx, int n_out, const uint32_t* bits,
                          const uint16_t* norms, int64_t Ncap, int vmode, const uint32_t* codes, const uint16_t* meta,
-                         const float* V_f32, int nbits, float sm_scale, int estimator, float* out, float* scores_dbg,
+                         const float* V_f32, int nbits, float sm_scale, int estimator, int path, float* out, float* scores_dbg,
                          int nsplit, void* workspace, size_t ws_bytes, hipStream_t stream) {
     g_last_error.clear();
     qjl::DecodeArgs a{};
-    int st = prepare_decode(a, qdt, B, Hq, Hkv, d, N, m, m_out, n_out, Ncap, vmode, nbits, sm_scale, estimator, nsplit);
+    int st = prepare_decode(a, qdt, B, Hq, Hkv, d, N, m, m_out, n_out, Ncap, vmode, nbits, sm_scale, estimator, path, nsplit);
     if (st) return st;
     if (B == 0) return QJL_OK;
     if (!Q || !S_in || !bits || !norms || !out || (m_out && !S_out) || (n_out && !outlier_idx) ||
@@ -387,12 +395,12 @@ int scratch_of_current_device(void** ptr) {
 int decode_step_impl(const void* Q, const void* K_new, const void* V_new, int dt, int B, int Hq, int Hkv, int d, int64_t N,
                      int64_t sK_b, int64_t sK_h, int64_t sV_b, int64_t sV_h, const void* S_in, int m, const void* S_out,
                      int m_out, const int32_t* outlier_idx, int n_out, uint32_t* bits, uint16_t* norms, uint32_t* codes,
-                     uint16_t* meta, int64_t Ncap, int nbits, float sm_scale, int estimator, float* out, float* scores_dbg,
-                     int nsplit, void* workspace, size_t ws_bytes, bool no_alloc, hipStream_t stream) {
+                     uint16_t* meta, int64_t Ncap, int nbits, float sm_scale, int estimator, int path, float* out,
+                     float* scores_dbg, int nsplit, void* workspace, size_t ws_bytes, bool no_alloc, hipStream_t stream) {
     g_last_error.clear();
     if (N < 1) return fail(QJL_ERR_INVALID_ARG, "N=%lld: a decode step appends one token, so N >= 1", (long long)N);
     qjl::DecodeArgs a{};
-    int st = prepare_decode(a, dt, B, Hq, Hkv, d, N, m, m_out, n_out, Ncap, QJL_V_CODES, nbits, sm_scale, estimator, nsplit);
+    int st = prepare_decode(a, dt, B, Hq, Hkv, d, N, m, m_out, n_out, Ncap, QJL_V_CODES, nbits, sm_scale, estimator, path, nsplit);
     if (st) return st;
     if (B == 0) return QJL_OK;
     if (!Q || !K_new || !V_new || !S_in || !bits || !norms || !codes || !meta || !out || (m_out && !S_out) ||
@@ -414,7 +422,7 @@ int decode_step_impl(const void* Q, const void* K_new, const void* V_new, int dt
     }
     st = bind_workspace(a, workspace, ws_bytes);
     if (st) return st;
-    if (dt == QJL_BF16 && qjl::decode_uses_mfma(m, m_out, QJL_V_CODES, nbits)) {
+    if (dt == QJL_BF16 && path != QJL_PATH_VECTOR && qjl::decode_uses_mfma(m, m_out, QJL_V_CODES, nbits)) {
         a.Q = Q;
         a.S_in = S_in;
         a.S_out = S_out;
@@ -439,15 +447,16 @@ int decode_step_impl(const void* Q, const void* K_new, const void* V_new, int dt
         ap.pos = N - 1;
         return hip_status(qjl::launch_decode_step_mfma(a, ap, stream), "qjl_decode_step launch");
     }
-    // other shapes and fp32: the three operations one after the other (arguments checked above)
+    // other shapes, fp32 and the vector-unit path: the three operations one after the other (arguments
+    // checked above)
     st = qjl_quantize_keys(K_new, dt, B, 1, Hkv, d, sK_b, 0, sK_h, S_in, m, S_out, m_out, outlier_idx, n_out, bits, norms,
                            Ncap, N - 1, stream);
     if (st) return st;
     st = qjl_quantize_values(V_new, dt, B, 1, Hkv, d, sV_b, 0, sV_h, nbits, codes, meta, Ncap, N - 1, stream);
     if (st) return st;
     return qjl_decode_attention(Q, dt, B, Hq, Hkv, d, N, S_in, m, S_out, m_out, outlier_idx, n_out, bits, norms, Ncap,
-                                QJL_V_CODES, codes, meta, nullptr, nbits, sm_scale, estimator, out, scores_dbg, nsplit, workspace,
-                                ws_bytes, stream);
+                                QJL_V_CODES, codes, meta, nullptr, nbits, sm_scale, estimator, path, out, scores_dbg, nsplit,
+                                workspace, ws_bytes, stream);
 }
 
 }  // namespace
@@ -457,21 +466,21 @@ extern "C" {
 int qjl_decode_step(const void* Q, const void* K_new, const void* V_new, int dt, int B, int Hq, int Hkv, int d, int64_t N,
                     int64_t sK_b, int64_t sK_h, int64_t sV_b, int64_t sV_h, const void* S_in, int m, const void* S_out,
                     int m_out, const int32_t* outlier_idx, int n_out, uint32_t* bits, uint16_t* norms, uint32_t* codes,
-                    uint16_t* meta, int64_t Ncap, int nbits, float sm_scale, int estimator, float* out, float* scores_dbg,
-                    int nsplit, void* workspace, size_t ws_bytes, hipStream_t stream) {
+                    uint16_t* meta, int64_t Ncap, int nbits, float sm_scale, int estimator, int path, float* out,
+                    float* scores_dbg, int nsplit, void* workspace, size_t ws_bytes, hipStream_t stream) {
     return decode_step_impl(Q, K_new, V_new, dt, B, Hq, Hkv, d, N, sK_b, sK_h, sV_b, sV_h, S_in, m, S_out, m_out, outlier_idx,
-                            n_out, bits, norms, codes, meta, Ncap, nbits, sm_scale, estimator, out, scores_dbg, nsplit, workspace,
-                            ws_bytes, false, stream);
+                            n_out, bits, norms, codes, meta, Ncap, nbits, sm_scale, estimator, path, out, scores_dbg, nsplit,
+                            workspace, ws_bytes, false, stream);
 }
 
 int qjl_decode_step_no_alloc(const void* Q, const void* K_new, const void* V_new, int dt, int B, int Hq, int Hkv, int d,
                              int64_t N, int64_t sK_b, int64_t sK_h, int64_t sV_b, int64_t sV_h, const void* S_in, int m,
                              const void* S_out, int m_out, const int32_t* outlier_idx, int n_out, uint32_t* bits,
                              uint16_t* norms, uint32_t* codes, uint16_t* meta, int64_t Ncap, int nbits, float sm_scale,
-                             int estimator, float* out, float* scores_dbg, int nsplit, hipStream_t stream) {
+                             int estimator, int path, float* out, float* scores_dbg, int nsplit, hipStream_t stream) {
     return decode_step_impl(Q, K_new, V_new, dt, B, Hq, Hkv, d, N, sK_b, sK_h, sV_b, sV_h, S_in, m, S_out, m_out, outlier_idx,
-                            n_out, bits, norms, codes, meta, Ncap, nbits, sm_scale, estimator, out, scores_dbg, nsplit, nullptr,
-                            0, true, stream);
+                            n_out, bits, norms, codes, meta, Ncap, nbits, sm_scale, estimator, path, out, scores_dbg, nsplit,
+                            nullptr, 0, true, stream);
 }
 
 size_t qjl_select_outliers_workspace_size(int B, int64_t T, int Hkv, int d) {

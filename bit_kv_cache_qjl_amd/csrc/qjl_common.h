@@ -257,6 +257,7 @@ struct DecodeArgs {
     int64_t chunk;                    // tokens per split (multiple of the tile)
     float z_scale;                    // sm_scale * log2(e)
     int estimator;                    // 0: one-sided (query unquantized); 1: two-sided (query signs)
+    int path;                         // qjl_decode_path: 0 auto, 1 matrix cores, 2 vector units
     size_t ws_need;                   // workspace bytes these sizes need (host-side check)
 };
 

@@ -90,6 +90,18 @@ typedef enum {
 } qjl_estimator;
 
 /*
+ * Which decode kernels score the keys and aggregate the values (both compute the same attention; see
+ * qjl_decode_attention for their operand formats).
+ */
+typedef enum {
+    QJL_PATH_AUTO = 0,    /* the matrix cores where the shape allows it, else the vector units          */
+    QJL_PATH_MATRIX = 1,  /* matrix cores: value codes of 2, 3 or 4 bits, m + m_out <= 512 with m in
+                             {128, 256, 512} and m_out in {0, m}; QJL_ERR_UNSUPPORTED otherwise          */
+    QJL_PATH_VECTOR = 2   /* vector units (byte tables of the projected query): 2-bit value codes or
+                             fp32 values, any supported sketch; QJL_ERR_UNSUPPORTED for 3- and 4-bit codes */
+} qjl_decode_path;
+
+/*
  * qjl_quantize_keys - sketch T new keys per (sequence, KV head) into the cache at positions
  * [t0, t0 + T).
  *
@@ -156,16 +168,27 @@ size_t qjl_decode_workspace_size(int B, int Hq, int Hkv, int d, int64_t N, int m
  * asymmetric estimator is unbiased for the inner product) and by softmax attention over the
  * estimated scores with a weighted sum of the dequantized values (page "Your Brain Already Runs on
  * 1-Bit Keys", "Keys Select. Values Deliver.").  Per (b, hq) with h = hq / (Hq/Hkv):
- *     Sq_in = S_in q_in, Sq_out = S_out q_out                         (fp32, unquantized)
+ *     Sq_in = S_in q_in, Sq_out = S_out q_out                         (fp32 sums of exact products)
  *     s_t   = score(q, k_t) from the sketch bits and fp16 norms      (formula at the top)
  *     out   = sum_t softmax(sm_scale * s)_t * v_t                    (fp32 accumulation)
  * where v_t = mn16 + step * code (QJL_V_CODES) or the fp32 value itself (QJL_V_F32).
+ * Operand formats (`path`):
+ *   matrix cores   each projected query value, times sm_scale log2(e) sqrt(pi/2)/m and a per-head power
+ *                  of two, is carried as the sum of three fp8 e4m3 pieces (round to nearest; the residual
+ *                  is below 2^-12 of the value), multiplied exactly with the sign bits as fp4 operands
+ *                  and summed in fp32, so a score is within 2^-12 of its magnitude scale
+ *                  sqrt(pi/2) (|k_in| |Sq_in|_1/m + |k_out| |Sq_out|_1/m_out) plus fp32 rounding; each
+ *                  softmax weight times its token's step is likewise carried as three e4m3 pieces
+ *                  against the codes, so the value term is within 2^-12 of the largest value range;
+ *   vector units   Sq in fp32, summed through byte tables in fp32; weights times step in fp16 against
+ *                  the codes (2^-11 relative).
  *   Q           [B][Hq][d] contiguous, dtype qdt; S_in / S_out / outlier_idx as for quantize (S in
  *               dtype qdt).
  *   bits, norms the key cache (capacity Ncap >= N).
  *   vmode       QJL_V_CODES: codes + meta (nbits 2, or 3 or 4 with m + m_out <= 512), V_f32 ignored;
  *               QJL_V_F32: V_f32 [B][Hkv][Ncap][d] fp32, codes/meta ignored.
  *   sm_scale    softmax scale; <= 0 selects 1/sqrt(d).
+ *   path        a qjl_decode_path.
  *   estimator   a qjl_estimator.  QJL_EST_TWO_SIDED is the variant the QJL summary contrasts with the
  *               one-sided estimator ("Surprising findings": quantizing both sides gives a biased
  *               estimate of the cosine): s_t = |q_in| n_in / m <sign(Sq_in), s_in> + |q_out| n_out /
@@ -186,7 +209,7 @@ int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, 
                          const int32_t* outlier_idx, int n_out,
                          const uint32_t* bits, const uint16_t* norms, int64_t Ncap,
                          int vmode, const uint32_t* codes, const uint16_t* meta, const float* V_f32,
-                         int nbits, float sm_scale, int estimator, float* out, float* scores_dbg, int nsplit,
+                         int nbits, float sm_scale, int estimator, int path, float* out, float* scores_dbg, int nsplit,
                          void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
@@ -207,8 +230,8 @@ int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, 
  *   bits, norms, codes, meta  the cache (layout at the top) of capacity Ncap >= N; nbits 2, 3 or 4 (as
  *               for qjl_decode_attention).
  *   N           context length after the append (N >= 1).
- *   sm_scale, estimator, out, scores_dbg, nsplit, workspace  as for qjl_decode_attention (same
- *               workspace size).
+ *   sm_scale, estimator, path, out, scores_dbg, nsplit, workspace  as for qjl_decode_attention (same
+ *               workspace size; QJL_PATH_VECTOR runs the three operations as separate launches).
  * Every argument is checked before anything is enqueued.
  */
 int qjl_decode_step(const void* Q, const void* K_new, const void* V_new, int dt, int B, int Hq, int Hkv, int d,
@@ -216,7 +239,7 @@ int qjl_decode_step(const void* Q, const void* K_new, const void* V_new, int dt,
                     const void* S_in, int m, const void* S_out, int m_out,
                     const int32_t* outlier_idx, int n_out,
                     uint32_t* bits, uint16_t* norms, uint32_t* codes, uint16_t* meta, int64_t Ncap, int nbits,
-                    float sm_scale, int estimator, float* out, float* scores_dbg, int nsplit,
+                    float sm_scale, int estimator, int path, float* out, float* scores_dbg, int nsplit,
                     void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
@@ -244,7 +267,7 @@ int qjl_decode_step_no_alloc(const void* Q, const void* K_new, const void* V_new
                              const void* S_in, int m, const void* S_out, int m_out,
                              const int32_t* outlier_idx, int n_out,
                              uint32_t* bits, uint16_t* norms, uint32_t* codes, uint16_t* meta, int64_t Ncap, int nbits,
-                             float sm_scale, int estimator, float* out, float* scores_dbg, int nsplit,
+                             float sm_scale, int estimator, int path, float* out, float* scores_dbg, int nsplit,
                              hipStream_t stream);
 
 /*

@@ -128,7 +128,7 @@ def two_sided_tolerance(q, S_in, S_out, channels, norms, m, m_out):
 
 
 def run_decode(qjl, w, Q, S_in, S_out, oidx, cache_np: dict, N: int, *, nsplit=0, with_scores=True, V_f32=None,
-               estimator=0):
+               estimator=0, path=0):
     """Upload an oracle-built cache, run the library decode, return (out, scores) as numpy."""
     torch = torch_mod()
     B, Hq, d = Q.shape
@@ -145,24 +145,48 @@ def run_decode(qjl, w, Q, S_in, S_out, oidx, cache_np: dict, N: int, *, nsplit=0
         kw["meta"] = torch.from_numpy(cache_np["meta"]).cuda()
     qjl.decode_attention(to_dev(Q, w.dtype), to_dev(S_in, w.dtype), to_dev(S_out, w.dtype) if w.m_out else None,
                          torch.from_numpy(oidx).cuda() if w.n_out else None, bits, norms, N, out,
-                         nbits=w.nbits, scores_dbg=scores, nsplit=nsplit, estimator=estimator, **kw)
+                         nbits=w.nbits, scores_dbg=scores, nsplit=nsplit, estimator=estimator, path=path, **kw)
     torch.cuda.synchronize()
     return out.cpu().numpy(), (scores.cpu().numpy()[:, :, :N] if with_scores else None)
 
 
+def device_cache_np(cache, w, N: int) -> dict:
+    """The first N positions of a cache the library wrote, read back in the oracle's formats: natural-order
+    sign words, fp16 norms, per-token packed code rows, fp16 (min, step)."""
+    return {"bits": bits_np(cache.bits, w.m, w.m_out)[:, :, :N], "norms": cache.norms.cpu().numpy()[:, :, :N],
+            "codes": code_rows_of_tiles(cache.codes, cache.nbits, N), "meta": cache.meta.cpu().numpy()[:, :, :N]}
+
+
+def output_tolerance(meta_unit, nbits: int) -> float:
+    """Max-abs output tolerance of one (sequence, KV head): 2e-3, or 1.25 * 2^-12 of the unit's largest
+    value range R = L * step where that is larger (R > 6.5).  Both error sources of the output scale with
+    the value range: the matrix-core path carries each softmax weight times step as three e4m3 pieces
+    (relative residual <= 2^-12, so the value term can be off by 2^-12 R), and a score error moves
+    weight between tokens whose values differ by up to R.  The 2e-3 bound is stated for the synthetic
+    N(0, 1) values (ranges of 5 to 7); wider ranges keep the same relative bound."""
+    if meta_unit is None or len(meta_unit) == 0:
+        return 2e-3
+    L = 2 ** nbits - 1
+    rng = float(np.max(meta_unit[:, 1].astype(np.float64))) * L
+    return max(2e-3, 1.25 * 2.0 ** -12 * rng)
+
+
 def check_decode(w, Q, S_in, S_out, oidx, cache_np, N, out_gpu, scores_gpu, units, V_f32=None, what="",
                  estimator="one_sided"):
-    """Compare sampled (b, hq) outputs (2e-3 max-abs) and scores (1e-3 of the estimator scale)."""
+    """Compare sampled (b, hq) outputs (2e-3 max-abs; output_tolerance for wide value ranges) and scores
+    (1e-3 of the estimator scale)."""
     ref = oracle.decode_attention(Q, S_in, S_out, oidx, cache_np["bits"], cache_np["norms"], N,
                                   codes=cache_np.get("codes"), meta=cache_np.get("meta"), V_f32=V_f32,
                                   nbits=w.nbits, units=units, estimator=estimator)
-    worst_o, worst_s = 0.0, 0.0
+    worst_o, worst_s, worst_raw = 0.0, 0.0, 0.0
     g = w.Hq // w.Hkv
     for b, hq in units:
         h = hq // g
         err = np.abs(out_gpu[b, hq] - ref["out"][b, hq]).max()
-        worst_o = max(worst_o, float(err))
-        assert err <= 2e-3, f"{what} out (b={b}, hq={hq}) max-abs {err:.3g} > 2e-3"
+        tol_o = 2e-3 if V_f32 is not None else output_tolerance(cache_np["meta"][b, h, :N], w.nbits)
+        worst_o = max(worst_o, float(err) / tol_o * 2e-3)
+        worst_raw = max(worst_raw, float(err))
+        assert err <= tol_o, f"{what} out (b={b}, hq={hq}) max-abs {err:.3g} > {tol_o:.3g}"
         if scores_gpu is not None and N:
             channels = oidx[h] if oidx.size else []
             if estimator == "one_sided":
@@ -174,5 +198,6 @@ def check_decode(w, Q, S_in, S_out, oidx, cache_np, N, out_gpu, scores_gpu, unit
             ratio = float((ds / tol).max())
             worst_s = max(worst_s, ratio)
             assert ratio <= 1.0, f"{what} scores (b={b}, hq={hq}) exceed tolerance by x{ratio:.3g}"
-    log(f"  {what}: out max-abs {worst_o:.2e} (<= 2e-3); worst score error {worst_s:.2e} of tolerance")
+    log(f"  {what}: out max-abs {worst_raw:.2e} ({worst_o / 2e-3:.2e} of its tolerance); worst score error "
+        f"{worst_s:.2e} of tolerance")
     return worst_o, worst_s

@@ -99,7 +99,7 @@ def test_quantize_values_empty_is_noop():
 def decode_call(ws_bytes=None, **kw):
     a = dict(Q=FAKE, qdt=0, B=2, Hq=8, Hkv=2, d=128, N=1000, S_in=FAKE, m=256, S_out=FAKE, m_out=256, oidx=FAKE,
              n_out=3, bits=FAKE, norms=FAKE, Ncap=1024, vmode=0, codes=FAKE, meta=FAKE, V_f32=0, nbits=2,
-             sm_scale=0.0, estimator=0, out=FAKE, scores=0, nsplit=0, ws=FAKE, ws_bytes=0, stream=0)
+             sm_scale=0.0, estimator=0, path=0, out=FAKE, scores=0, nsplit=0, ws=FAKE, ws_bytes=0, stream=0)
     a.update(kw)
     if ws_bytes is None:
         a["ws_bytes"] = qjl.lib.qjl_decode_workspace_size(a["B"], a["Hq"], a["Hkv"], 128, a["N"], a["m"], a["m_out"],
@@ -121,10 +121,18 @@ def decode_call(ws_bytes=None, **kw):
     (dict(vmode=7), qjl.QJL_ERR_INVALID_ARG),
     (dict(estimator=2), qjl.QJL_ERR_INVALID_ARG),
     (dict(estimator=-1), qjl.QJL_ERR_INVALID_ARG),
+    (dict(path=3), qjl.QJL_ERR_INVALID_ARG),
+    (dict(path=-1), qjl.QJL_ERR_INVALID_ARG),
+    (dict(path=1, m=512, m_out=512), qjl.QJL_ERR_UNSUPPORTED),     # matrix cores: sketches up to 512 bits
+    (dict(path=1, vmode=1, V_f32=FAKE), qjl.QJL_ERR_UNSUPPORTED),  # matrix cores: value codes only
+    (dict(path=2, nbits=3), qjl.QJL_ERR_UNSUPPORTED),              # vector units: 2-bit codes only
+    (dict(path=2, nbits=4), qjl.QJL_ERR_UNSUPPORTED),
     (dict(out=MIS), qjl.QJL_ERR_MISALIGNED),
     (dict(scores=MIS), qjl.QJL_ERR_MISALIGNED),
     (dict(nsplit=5000, ws_bytes=1 << 30), qjl.QJL_ERR_UNSUPPORTED),
     (dict(), qjl.QJL_ERR_WORKSPACE),                    # 4 bytes short
+    (dict(path=1), qjl.QJL_ERR_WORKSPACE),              # a valid path: the next check fails
+    (dict(path=2), qjl.QJL_ERR_WORKSPACE),
     (dict(ws=0), qjl.QJL_ERR_WORKSPACE),
 ])
 def test_decode_rejects(kw, status):
@@ -155,7 +163,7 @@ def test_timer_api():
 def step_call(ws_bytes=None, **kw):
     a = dict(Q=FAKE, K_new=FAKE, V_new=FAKE, dt=0, B=2, Hq=8, Hkv=2, d=128, N=1000, sK_b=2 * 128, sK_h=128,
              sV_b=2 * 128, sV_h=128, S_in=FAKE, m=256, S_out=FAKE, m_out=256, oidx=FAKE, n_out=3, bits=FAKE,
-             norms=FAKE, codes=FAKE, meta=FAKE, Ncap=1024, nbits=2, sm_scale=0.0, estimator=0, out=FAKE, scores=0,
+             norms=FAKE, codes=FAKE, meta=FAKE, Ncap=1024, nbits=2, sm_scale=0.0, estimator=0, path=0, out=FAKE, scores=0,
              nsplit=0, ws=FAKE, ws_bytes=0, stream=0)
     a.update(kw)
     if ws_bytes is None:
@@ -233,7 +241,7 @@ def test_select_outliers_workspace_formula():
 def step_no_alloc_call(**kw):
     a = dict(Q=FAKE, K_new=FAKE, V_new=FAKE, dt=0, B=2, Hq=8, Hkv=2, d=128, N=1000, sK_b=2 * 128, sK_h=128,
              sV_b=2 * 128, sV_h=128, S_in=FAKE, m=256, S_out=FAKE, m_out=256, oidx=FAKE, n_out=3, bits=FAKE,
-             norms=FAKE, codes=FAKE, meta=FAKE, Ncap=1024, nbits=2, sm_scale=0.0, estimator=0, out=FAKE, scores=0,
+             norms=FAKE, codes=FAKE, meta=FAKE, Ncap=1024, nbits=2, sm_scale=0.0, estimator=0, path=0, out=FAKE, scores=0,
              nsplit=0, stream=0)
     a.update(kw)
     return qjl.lib.qjl_decode_step_no_alloc(*a.values())

@@ -374,3 +374,128 @@ def test_decode_step_append_then_attend():
         o2, s2 = run_decode(qjl, w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache_np, N)
         units = [(b, hq) for b in range(w.B) for hq in range(w.Hq)]
         check_decode(w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache_np, N, o2, s2, units, what="pipeline")
+
+
+# ----------------------------------------------------------------------------- sketch shapes of the
+# VGPR-stationary key quantizer (T > 16 with m not in {128, 256, 512} or m_out not in {0, m}): one, two
+# and four 32-projection tiles per wave, outlier sketches narrower and wider than the inlier one
+
+@pytest.mark.parametrize("m,m_out", [(256, 128), (128, 256), (384, 384), (640, 0), (1024, 0), (512, 384)])
+def test_quantize_keys_vgpr_kernel_shapes(m, m_out):
+    base = SCALED["llama31_70b_gqa_decode"]
+    w = base.scaled(B=2, Hq=2, Hkv=2, N=100, m=m, m_out=m_out, n_out=base.n_out if m_out else 0)
+    log(f"[quantize_keys] VGPR kernel m={m} m_out={m_out} T={w.N} (64-token chunk + ragged 36), t0=5")
+    x = inputs(w)
+    cache = gpu_quantize_keys(qjl, w, x["K"], x["S_in"], x["S_out"], x["oidx"], Ncap=w.N + 12, t0=5)
+    ref = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
+    bits = bits_np(cache.bits, w.m, w.m_out)
+    compare_bits(bits[:, :, 5:5 + w.N], ref, f"m={m} m_out={m_out}", w.m + w.m_out)
+    compare_norms(cache.norms.cpu().numpy()[:, :, 5:5 + w.N], ref["norms"], f"m={m} m_out={m_out}")
+    assert not bits[:, :, :5].any() and not bits[:, :, 5 + w.N:].any(), "wrote outside [t0, t0 + T)"
+
+
+# ----------------------------------------------------------------------------- outlier lists in any order
+
+def _shuffled(oidx: np.ndarray, seed: int) -> np.ndarray:
+    """The same channel sets, each KV head's list in a seeded random order (never the sorted one)."""
+    rng = np.random.default_rng(seed)
+    out = oidx.copy()
+    for h in range(out.shape[0]):
+        while out.shape[1] > 1 and np.all(np.diff(out[h]) > 0):
+            out[h] = rng.permutation(oidx[h])
+    return out
+
+
+@pytest.mark.parametrize("kernel,T,m,m_out", [("lds", 100, 256, 256), ("rows", 3, 256, 256), ("vgpr", 100, 384, 384),
+                                              ("lds_512", 70, 512, 512)])
+def test_quantize_keys_unsorted_outlier_lists(kernel, T, m, m_out):
+    w = SCALED["llama31_70b_gqa_decode"].scaled(B=2, Hq=2, Hkv=2, N=T, m=m, m_out=m_out)
+    x = inputs(w)
+    oidx = _shuffled(x["oidx"], 5)
+    log(f"[quantize_keys] unsorted outlier lists ({kernel}) {oidx.tolist()}")
+    cache = gpu_quantize_keys(qjl, w, x["K"], x["S_in"], x["S_out"], oidx)
+    ref = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], oidx)
+    compare_bits(bits_np(cache.bits, w.m, w.m_out), ref, f"unsorted {kernel}", w.m + w.m_out)
+    compare_norms(cache.norms.cpu().numpy(), ref["norms"], f"unsorted {kernel}")
+
+
+@pytest.mark.parametrize("name", ["llama31_70b_gqa_decode", "llama3_8b_gqa_decode", "fp32_queries", "wide_sketch"])
+def test_decode_unsorted_outlier_lists(name):
+    """The matrix-core prologue (bf16), the fp32 query projection and the byte-table path (1024-bit
+    sketch) with each KV head's outlier list in a random order."""
+    if name == "wide_sketch":
+        w = WIDE
+    elif name == "fp32_queries":
+        w = SCALED["llama3_8b_gqa_decode"].scaled(dtype="f32")
+    else:
+        w = SCALED[name]
+    x = inputs(w)
+    oidx = _shuffled(x["oidx"], 9)
+    log(f"[decode] unsorted outlier lists {name}")
+    kq = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], oidx)
+    cache = {"bits": kq["bits"], "norms": kq["norms"], **oracle.quantize_values(x["V"], w.nbits)}
+    out, scores = run_decode(qjl, w, x["Q"], x["S_in"], x["S_out"], oidx, cache, w.N)
+    units = [(b, hq) for b in range(w.B) for hq in range(w.Hq)]
+    check_decode(w, x["Q"], x["S_in"], x["S_out"], oidx, cache, w.N, out, scores, units, what=f"unsorted {name}")
+
+
+# ----------------------------------------------------------------------------- values with outlier channels
+
+@pytest.mark.parametrize("nbits", [2, 3, 4])
+@pytest.mark.parametrize("scale", [20.0, 50.0])
+def test_decode_values_with_outlier_channels(nbits, scale):
+    """Value vectors with three channels scaled x20 / x50 (value ranges of ~60 / ~150 instead of ~6):
+    codes exact, and the decode output within output_tolerance, which grows with the value range (the
+    page's outlier example spans 99.4: "Why Outliers Destroy Quantization")."""
+    w = SCALED["llama31_70b_gqa_decode"].scaled(N=600, nbits=nbits)
+    x = inputs(w)
+    V = x["V"].copy()
+    V[:, :, :, [7, 70, 101]] *= np.float32(scale)
+    V = si.round_bf16(V)
+    vq = oracle.quantize_values(V, nbits)
+    # the library's codes for these values equal the oracle's
+    vd = qjl.alloc_cache(w.B, w.Hkv, w.N, w.m, w.m_out, nbits)
+    qjl.quantize_values(to_dev(V, w.dtype), nbits, vd.codes, vd.meta)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(code_rows_of_tiles(vd.codes, nbits, w.N), vq["codes"])
+    np.testing.assert_array_equal(vd.meta.cpu().numpy().view(np.uint16), vq["meta"].view(np.uint16))
+    kq = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
+    cache = {"bits": kq["bits"], "norms": kq["norms"], **vq}
+    rng_max = float(vq["meta"][..., 1].astype(np.float64).max()) * (2 ** nbits - 1)
+    log(f"[decode] values with x{scale:g} channels, {nbits}-bit: largest value range {rng_max:.1f}")
+    for nsplit in (0, 3):
+        out, scores = run_decode(qjl, w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, w.N, nsplit=nsplit)
+        units = [(b, hq) for b in range(w.B) for hq in range(w.Hq)]
+        check_decode(w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, w.N, out, scores, units,
+                     what=f"x{scale:g} values {nbits}-bit nsplit={nsplit}")
+
+
+# ----------------------------------------------------------------------------- the two decode paths
+
+@pytest.mark.parametrize("name", ["llama2_7b_decode", "llama3_8b_gqa_decode", "llama31_70b_gqa_decode"])
+@pytest.mark.parametrize("nsplit", [0, 3])
+@pytest.mark.parametrize("estimator", ["one_sided", "two_sided"])
+def test_decode_parity_vector_path(name, nsplit, estimator):
+    """The vector-unit decode (byte tables of the projected query, fp16 value weights) forced on the
+    2-bit matrix-core shapes, against the oracle."""
+    w = SCALED[name]
+    log(f"[decode vector path] {name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} N={w.N} nsplit={nsplit} {estimator}")
+    x = inputs(w)
+    kq = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
+    cache = {"bits": kq["bits"], "norms": kq["norms"], **oracle.quantize_values(x["V"], w.nbits)}
+    est = qjl.QJL_EST_ONE_SIDED if estimator == "one_sided" else qjl.QJL_EST_TWO_SIDED
+    out, scores = run_decode(qjl, w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, w.N, nsplit=nsplit,
+                             estimator=est, path=qjl.QJL_PATH_VECTOR)
+    units = [(b, hq) for b in range(w.B) for hq in range(w.Hq)]
+    check_decode(w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, w.N, out, scores, units,
+                 what=f"{name} vector path", estimator=estimator)
+
+
+def test_decode_paths_refuse_what_they_cannot_run():
+    w = SCALED["llama3_8b_gqa_decode"]
+    x = inputs(w.scaled(N=64))
+    kq = oracle.quantize_keys(x["K"][:, :64], x["S_in"], x["S_out"], x["oidx"])
+    cache = {"bits": kq["bits"], "norms": kq["norms"], **oracle.quantize_values(x["V"][:, :64], 3)}
+    with pytest.raises(qjl.QJLError) as e:
+        run_decode(qjl, w.scaled(nbits=3), x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, 64, path=qjl.QJL_PATH_VECTOR)
+    assert e.value.status == qjl.QJL_ERR_UNSUPPORTED
