@@ -772,6 +772,365 @@ __global__ __launch_bounds__(kMThreads, (R == 1 && NB == 2) ? 2 : 1) void decode
 
 }
 
+// ---------------------------------------------------------------------------- eight-wave decode
+// The same computation for 8 query heads per workgroup (two row groups) and 2-bit codes, with eight
+// waves, two per SIMD: one wave's vector instructions run while the other's matrix instructions do.
+// Registers allow that only without the two block buffers of decode_mfma_kernel, so a block's sign
+// quarter-rows, norms, meta and code words go from HBM straight into LDS (buffer loads with the LDS as
+// destination), one buffer per wave (norms and meta two), and are read from there when used:
+//   after the weight-tile stores of block i:  sign quarter-rows, norms and meta of block i + 1 (8 + 4 loads);
+//   after the values of block i:              code words of block i + 1 (4 loads).
+// Loads complete in issue order, so block i + 1 may start once at most the 4 code loads are
+// outstanding (vmcnt 4), and its values once at most the 12 loads issued after its weight stores are
+// (vmcnt 12).  These loads write no register, so the waits are explicit; the empty asm statements
+// that carry them also make the buffers escape, so the compiler does not take their contents as
+// never written.  Tokens past the chunk end read as zero (buffer bounds) and are masked as before.
+constexpr int kM8Waves = 8;
+constexpr int kM8Threads = 64 * kM8Waves;
+
+// 16 or 4 bytes per lane from a buffer into LDS (lane l at byte 16 l, or 4 l, of the destination), in
+// plain functions: with the size inside a kernel template the compiler's host pass drops the
+// kernel's launch stub
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t* lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, uint32_t* lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, 0, 0, 0);
+}
+
+template <int WIN4, int WOUT4, bool DBG>
+__global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs a, int groups, int hgroups) {
+    constexpr int R = 2, NB = 2;
+    constexpr int W4 = WIN4 + WOUT4;
+    constexpr int WB = 4 * W4;
+    constexpr int HPG = 4 * R;
+    static_assert(W4 == 1 || W4 == 4, "a sign quarter-row of 4 or 16 bytes: one LDS-destination load");
+    // separate arrays, so that the compiler's own wait analysis can tell the load destinations apart
+    __shared__ __attribute__((aligned(16))) uint8_t s_wtile[kM8Waves][2][16 * kWPitch];   // weight pieces
+    __shared__ __attribute__((aligned(16))) uint32_t s_sgn[kM8Waves][8][64][W4];         // sign quarter-rows
+    __shared__ __attribute__((aligned(16))) uint32_t s_cod[kM8Waves][4][64][4];          // code words
+    __shared__ __attribute__((aligned(16))) uint32_t s_nrm[kM8Waves][2][kMBlock];        // norms (two buffers)
+    __shared__ __attribute__((aligned(16))) uint32_t s_met[kM8Waves][2][kMBlock];        // (min, step) (two buffers)
+    __shared__ float s_red_m[kM8Waves][8], s_red_l[kM8Waves][8], s_red_mn[kM8Waves][8];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int t = lane & 15;
+    const int hh = lane >> 4;
+
+    const int lin = blockIdx.x;
+    const int xcd = lin & 7;
+    const int slot = lin >> 3;
+    const int hg = slot % hgroups;
+    const int64_t us = (int64_t)(slot / hgroups) * 8 + xcd;
+    if (us >= (int64_t)groups) return;
+    const int split = (int)(us % a.nsplit);
+    const int unit = (int)(us / a.nsplit);
+    const int b = unit / a.Hkv;
+    const int h = unit - b * a.Hkv;
+    const int t_begin = (int)((int64_t)split * a.chunk);
+    const int t_end = (int)min(a.N, (int64_t)t_begin + a.chunk);
+    const int head0 = b * a.Hq + h * a.g;
+
+    const int rh = t >> 2, pc = lane & 3;
+    v8i_t sA[R][W4];
+    int sc_in[R], sc_out[R];
+#pragma unroll
+    for (int rg = 0; rg < R; ++rg) {
+        const int qa_head = HPG * hg + 4 * rg + rh;
+        sc_in[rg] = sc_out[rg] = 127;
+        if (qa_head < a.g) {
+            const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.sq) +
+                                                              (size_t)(head0 + qa_head) * (128 * WB));
+#pragma unroll
+            for (int kb = 0; kb < W4; ++kb) {
+                const uint4 lo = src[kb * 32 + (pc * 4 + hh) * 2], hi = src[kb * 32 + (pc * 4 + hh) * 2 + 1];
+                sA[rg][kb] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
+            const float* c = a.qconst + (size_t)(head0 + qa_head) * 4;
+            sc_in[rg] = 127 - __float_as_int(c[2]) - 4 * pc;
+            sc_out[rg] = 127 - __float_as_int(c[3]) - 4 * pc;
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < W4; ++kb) sA[rg][kb] = v8i_t{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+    }
+    float cin[R], cout[R];
+    float* sdbg[R];
+#pragma unroll
+    for (int rg = 0; rg < R; ++rg) {
+        const int dhead = HPG * hg + 4 * rg + hh;
+        const bool ok = dhead < a.g;
+        cin[rg] = ok ? a.qconst[(size_t)(head0 + dhead) * 4] : 0.f;
+        cout[rg] = ok ? a.qconst[(size_t)(head0 + dhead) * 4 + 1] : 0.f;
+        sdbg[rg] = (DBG && ok) ? a.scores_dbg + (size_t)(head0 + dhead) * a.N : nullptr;
+    }
+
+    uint8_t* wt = &s_wtile[wave][0][0];
+    for (int i = lane; i < R * 16 * kWPitch / 16; i += 64) reinterpret_cast<uint4*>(wt)[i] = make_uint4(0, 0, 0, 0);
+    __builtin_amdgcn_wave_barrier();
+    const int woff = 32 * (2 * ((t >> 3) & 1) + ((t >> 2) & 1)) + 8 * (t & 1) + 4 * ((t >> 1) & 1);
+
+    const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(a.bits + (size_t)unit * a.Ncap * WB, (uint32_t)t_end * WB * 4u);
+    const __amdgpu_buffer_rsrc_t rn = buffer_rsrc(reinterpret_cast<const uint32_t*>(a.norms) + (size_t)unit * a.Ncap,
+                                                  (uint32_t)t_end * 4u);
+    const __amdgpu_buffer_rsrc_t rm = buffer_rsrc(reinterpret_cast<const uint32_t*>(a.meta) + (size_t)unit * a.Ncap,
+                                                  (uint32_t)t_end * 4u);
+    const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(a.codes + (size_t)unit * code_tiles(a.Ncap) * (kD * NB),
+                                                  (uint32_t)code_tiles(t_end) * (kD * NB * 4u));
+    const int off_bits = (mfma_token(0, t) * WB + hh * W4) * 4;        // sign quarter-row of sub-step 0
+    const int off_codes = hh * (kD * NB * 4) + t * (8 * NB * 4);       // channel streams 8 t .. of code tile hh
+    const float inv_z = 1.0f / a.z_scale;
+
+    // the loads of a block into this wave's LDS buffers (the block start s0 is wave-uniform)
+    auto load_signs_nm = [&](int s0, int nb) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int voff = off_bits + (s0 + 64 * (s >> 2) + 2 * (s & 3)) * WB * 4;
+            if constexpr (W4 == 4) lds_load16(rb, &s_sgn[wave][s][0][0], voff);
+            else lds_load4(rb, &s_sgn[wave][s][0][0], voff);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            lds_load4(rn, &s_nrm[wave][nb][64 * q], (s0 + 64 * q + lane) * 4);
+            lds_load4(rm, &s_met[wave][nb][64 * q], (s0 + 64 * q + lane) * 4);
+        }
+    };
+    auto load_codes = [&](int s0) {
+#pragma unroll
+        for (int q = 0; q < 2 * NB; ++q)
+            lds_load16(rc, &s_cod[wave][q][0][0], off_codes + s0 * (kD * NB * 4 / kCodeTile) + 16 * q);
+    };
+
+    float m_run[R], l_acc[R], mn_acc[R];
+    v4f_t dv[R][8];
+#pragma unroll
+    for (int rg = 0; rg < R; ++rg) {
+        m_run[rg] = -INFINITY;
+        l_acc[rg] = mn_acc[rg] = 0.f;
+#pragma unroll
+        for (int cg = 0; cg < 8; ++cg) dv[rg][cg] = v4f_t{0.f, 0.f, 0.f, 0.f};
+    }
+    uint32_t m8 = 0x88888888u, o1 = 0x11111111u;
+    asm volatile("" : "+v"(m8), "+v"(o1));
+
+    constexpr int kStep = kMBlock * kM8Waves;
+    const int s_first = t_begin + kMBlock * wave;
+    int nb = 0;
+    load_signs_nm(s_first, nb);
+    load_codes(s_first);
+    for (int s0 = s_first; s0 < t_end; s0 += kStep) {
+        // this block's sign quarter-rows, norms and meta have landed (only the 4 code loads may be pending)
+        if constexpr (DBG) asm volatile("s_waitcnt vmcnt(0)" ::"s"(s_sgn), "s"(s_cod), "s"(s_nrm), "s"(s_met) : "memory");
+        else asm volatile("s_waitcnt vmcnt(4)" ::"s"(s_sgn), "s"(s_cod), "s"(s_nrm), "s"(s_met) : "memory");
+        __builtin_amdgcn_wave_barrier();
+
+        float z[R][8];
+        uint32_t mtw[8];                               // meta of the 8 sub-steps, read before its buffer is reloaded
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            mtw[s] = s_met[wave][nb][mfma_token(s, t)];
+            const uint32_t nrm = s_nrm[wave][nb][mfma_token(s, t)];
+            const float n_in = (float)__builtin_bit_cast(_Float16, (uint16_t)(nrm & 0xFFFFu));
+            const float n_out = (float)__builtin_bit_cast(_Float16, (uint16_t)(nrm >> 16));
+            uint32_t w[W4];
+            if constexpr (W4 == 4) {
+                const uint4 x = *reinterpret_cast<const uint4*>(&s_sgn[wave][s][lane][0]);
+                w[0] = x.x; w[1 % W4] = x.y; w[2 % W4] = x.z; w[3 % W4] = x.w;
+            } else {
+                w[0] = s_sgn[wave][s][lane][0];
+            }
+            v8i_t bin[WIN4], bout[WOUT4 > 0 ? WOUT4 : 1];
+#pragma unroll
+            for (int kb = 0; kb < WIN4; ++kb) bin[kb] = sign_planes(w[kb], m8, o1);
+#pragma unroll
+            for (int kb = 0; kb < WOUT4; ++kb) bout[kb] = sign_planes(w[WIN4 + kb], m8, o1);
+#pragma unroll
+            for (int rg = 0; rg < R; ++rg) {
+                v4f_t din = v4f_t{cin[rg], 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < WIN4; ++kb)
+                    din = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sA[rg][kb], bin[kb], din, 0, 4, 0, sc_in[rg], 0, 127);
+                float zz = n_in * ((din[0] + din[1]) + din[2]);
+                if constexpr (WOUT4 > 0) {
+                    v4f_t dout = v4f_t{cout[rg], 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb < WOUT4; ++kb)
+                        dout = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sA[rg][WIN4 + kb], bout[kb], dout, 0, 4, 0,
+                                                                                sc_out[rg], 0, 127);
+                    zz = fmaf(n_out, (dout[0] + dout[1]) + dout[2], zz);
+                }
+                if constexpr (DBG) {
+                    const int P = s0 + mfma_token(s, t);
+                    if (sdbg[rg] && P < t_end) sdbg[rg][P] = zz * inv_z;
+                }
+                z[rg][s] = zz;
+            }
+        }
+        if (s0 + kMBlock > t_end) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const bool past = s0 + mfma_token(s, t) >= t_end;
+#pragma unroll
+                for (int rg = 0; rg < R; ++rg) z[rg][s] = past ? -INFINITY : z[rg][s];
+            }
+        }
+
+        float mxs = 0.f, stp[8], mnv[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const uint32_t mt = mtw[s];
+            mnv[s] = (float)__builtin_bit_cast(_Float16, (uint16_t)(mt & 0xFFFFu));
+            stp[s] = (float)__builtin_bit_cast(_Float16, (uint16_t)(mt >> 16));
+            mxs = fmaxf(mxs, stp[s]);
+        }
+        mxs = row16_max(mxs);
+        const int E = mxs > 0.f ? __builtin_amdgcn_frexp_expf(mxs) : 0;
+        float stpf[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) stpf[s] = ldexpf(stp[s], 8 - E);
+        bool rescale = false;
+        float alpha[R];
+#pragma unroll
+        for (int rg = 0; rg < R; ++rg) {
+            float mx = z[rg][0];
+#pragma unroll
+            for (int s = 1; s < 8; ++s) mx = fmaxf(mx, z[rg][s]);
+            mx = row16_max(mx);
+            const float m_new = fmaxf(m_run[rg], mx);
+            alpha[rg] = __builtin_amdgcn_exp2f(m_run[rg] - m_new);
+            rescale |= alpha[rg] != 1.f;
+            m_run[rg] = m_new;
+            l_acc[rg] *= alpha[rg];
+            mn_acc[rg] *= alpha[rg];
+            uint8_t* row0 = wt + rg * 16 * kWPitch + (4 * hh) * kWPitch + woff;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                float wgt[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int s = 4 * q + i;
+                    const float p = __builtin_amdgcn_exp2f(z[rg][s] - m_new);
+                    l_acc[rg] += p;
+                    mn_acc[rg] = fmaf(p, mnv[s], mn_acc[rg]);
+                    wgt[i] = p * stpf[s];
+                }
+                uint32_t k[3];
+                fp8_pieces(wgt, k);
+                uint8_t* row = row0 + 16 * q;
+                // three single stores (the empty asm keeps them from merging into paired stores, which the
+                // compiler's wait analysis cannot tell apart from the loads still writing the LDS buffers)
+                *reinterpret_cast<uint32_t*>(row) = k[0];
+                asm volatile("");
+                *reinterpret_cast<uint32_t*>(row + kWPitch) = k[1];
+                asm volatile("");
+                *reinterpret_cast<uint32_t*>(row + 2 * kWPitch) = k[2];
+                asm volatile("");
+            }
+        }
+        // the sign buffer is free once its reads are done: the next block's signs, norms and meta.  Issued
+        // after this block's LDS stores (the weight tiles above): the compiler waits for every load into
+        // LDS before an LDS store, whatever its address
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        load_signs_nm(s0 + kStep, nb ^ 1);
+        if (__builtin_amdgcn_ballot_w64(rescale)) {
+#pragma unroll
+            for (int rg = 0; rg < R; ++rg)
+#pragma unroll
+                for (int cg = 0; cg < 8; ++cg) dv[rg][cg] *= alpha[rg];
+        }
+        // this block's code words have landed (the 12 loads issued after the weight stores may be pending)
+        if constexpr (DBG) asm volatile("s_waitcnt vmcnt(0)" ::"s"(s_sgn), "s"(s_cod), "s"(s_nrm), "s"(s_met) : "memory");
+        else asm volatile("s_waitcnt vmcnt(12)" ::"s"(s_sgn), "s"(s_cod), "s"(s_nrm), "s"(s_met) : "memory");
+        __builtin_amdgcn_wave_barrier();
+
+        v8i_t aw[R];
+#pragma unroll
+        for (int rg = 0; rg < R; ++rg) {
+            const uint8_t* src = wt + rg * 16 * kWPitch + t * kWPitch + 32 * hh;
+            const uint4 alo = *reinterpret_cast<const uint4*>(src);
+            const uint4 ahi = *reinterpret_cast<const uint4*>(src + 16);
+            aw[rg] = v8i_t{(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
+        }
+        uint32_t cx[8][NB];
+#pragma unroll
+        for (int q = 0; q < 2 * NB; ++q) {
+            const uint4 x = *reinterpret_cast<const uint4*>(&s_cod[wave][q][lane][0]);
+            const uint32_t xe[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cx[(4 * q + e) / NB][(4 * q + e) % NB] = xe[e];
+        }
+        const int sc_w = 120 + E - 4 * pc;
+#pragma unroll
+        for (int cg = 0; cg < 8; ++cg) {
+            const uint32_t x0 = cx[cg][0], x1 = cx[cg][1];
+            const v8i_t bv = v8i_t{(int)(x0 & 0x33333333u), (int)((x0 >> 2) & 0x33333333u), (int)(x1 & 0x33333333u),
+                                   (int)((x1 >> 2) & 0x33333333u), 0, 0, 0, 0};
+#pragma unroll
+            for (int rg = 0; rg < R; ++rg)
+                dv[rg][cg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aw[rg], bv, dv[rg][cg], 0, 4, 0, sc_w, 0, 127);
+        }
+        // the code buffer and the weight tiles are free once their reads are done: the next block's codes
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_wave_barrier();
+        load_codes(s0 + kStep);
+        nb ^= 1;
+    }
+    // no load may still write this wave's buffers when the merge below reuses the LDS
+    asm volatile("s_waitcnt vmcnt(0)" ::"s"(s_sgn), "s"(s_cod), "s"(s_nrm), "s"(s_met) : "memory");
+
+    // ---- merge the eight wave streams of each head (the output rows go through the weight tiles)
+    float* red_o = reinterpret_cast<float*>(&s_wtile[0][0][0]);        // [wave][head][kD]
+    static_assert(sizeof(s_wtile) >= kM8Waves * HPG * kD * sizeof(float), "merge rows fit the weight tiles");
+    __syncthreads();
+#pragma unroll
+    for (int rg = 0; rg < R; ++rg) {
+        const float l_sum = row16_sum(l_acc[rg]), mn_sum = row16_sum(mn_acc[rg]);
+        if (t == 0) {
+            s_red_m[wave][4 * rg + hh] = m_run[rg];
+            s_red_l[wave][4 * rg + hh] = l_sum;
+            s_red_mn[wave][4 * rg + hh] = mn_sum;
+        }
+#pragma unroll
+        for (int cg = 0; cg < 8; ++cg)
+            red_o[(wave * HPG + 4 * rg + hh) * kD + 16 * cg + t] = (dv[rg][cg][0] + dv[rg][cg][1]) + dv[rg][cg][2];
+    }
+    __syncthreads();
+    const int c0 = 2 * (tid & 63);
+    for (int oh = tid >> 6; oh < HPG; oh += kM8Waves) {
+        if (HPG * hg + oh >= a.g) break;
+        float M = s_red_m[0][oh];
+#pragma unroll
+        for (int w = 1; w < kM8Waves; ++w) M = fmaxf(M, s_red_m[w][oh]);
+        float Ls = 0.f, o0 = 0.f, o1v = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < kM8Waves; ++w) {
+                const float mw = s_red_m[w][oh];
+                if (mw == -INFINITY) continue;
+                const float sc = exp2f(mw - M);
+                Ls = fmaf(sc, s_red_l[w][oh], Ls);
+                o0 = fmaf(sc, red_o[(w * HPG + oh) * kD + c0] + s_red_mn[w][oh], o0);
+                o1v = fmaf(sc, red_o[(w * HPG + oh) * kD + c0 + 1] + s_red_mn[w][oh], o1v);
+            }
+        }
+        if (a.nsplit == 1) {
+            float* o = a.out + (size_t)(head0 + HPG * hg + oh) * kD;
+            o[c0] = Ls > 0.f ? o0 / Ls : 0.f;
+            o[c0 + 1] = Ls > 0.f ? o1v / Ls : 0.f;
+            continue;
+        }
+        float* dst = a.part + ((size_t)(head0 + HPG * hg + oh) * a.nsplit + split) * (kD + 2);
+        dst[2 + c0] = o0;
+        dst[3 + c0] = o1v;
+        if ((tid & 63) == 0) {
+            dst[0] = M;
+            dst[1] = Ls;
+        }
+    }
+}
+
 template <int WIN4, int WOUT4, int R, int NB>
 hipError_t launch_decode_mfma_r(const DecodeArgs& a, hipStream_t s) {
     const int hgroups = (a.g + 4 * R - 1) / (4 * R);
@@ -779,10 +1138,18 @@ hipError_t launch_decode_mfma_r(const DecodeArgs& a, hipStream_t s) {
     const int slots = (groups + 7) / 8;
     const unsigned nblocks = (unsigned)slots * 8u * (unsigned)hgroups;
     timer_begin(TK_DECODE, s);
-    if (a.scores_dbg)
-        hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, R, true, NB>), dim3(nblocks), dim3(kMThreads), 0, s, a, groups, hgroups);
-    else
-        hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, R, false, NB>), dim3(nblocks), dim3(kMThreads), 0, s, a, groups, hgroups);
+    if constexpr (R == 2 && NB == 2 && (WIN4 + WOUT4 == 4 || WIN4 + WOUT4 == 1)) {
+        // eight waves (two per SIMD), block data through LDS
+        if (a.scores_dbg)
+            hipLaunchKernelGGL((decode_mfma8_kernel<WIN4, WOUT4, true>), dim3(nblocks), dim3(kM8Threads), 0, s, a, groups, hgroups);
+        else
+            hipLaunchKernelGGL((decode_mfma8_kernel<WIN4, WOUT4, false>), dim3(nblocks), dim3(kM8Threads), 0, s, a, groups, hgroups);
+    } else {
+        if (a.scores_dbg)
+            hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, R, true, NB>), dim3(nblocks), dim3(kMThreads), 0, s, a, groups, hgroups);
+        else
+            hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, R, false, NB>), dim3(nblocks), dim3(kMThreads), 0, s, a, groups, hgroups);
+    }
     timer_end(TK_DECODE, s);
     return hipGetLastError();
 }

@@ -499,3 +499,25 @@ def test_decode_paths_refuse_what_they_cannot_run():
     with pytest.raises(qjl.QJLError) as e:
         run_decode(qjl, w.scaled(nbits=3), x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, 64, path=qjl.QJL_PATH_VECTOR)
     assert e.value.status == qjl.QJL_ERR_UNSUPPORTED
+
+
+# ----------------------------------------------------------------------------- eight-wave decode (g > 4)
+
+@pytest.mark.parametrize("m,m_out", [(256, 256), (512, 0), (128, 0)])
+@pytest.mark.parametrize("N,nsplit", [(777, 0), (1500, 3), (2049, 1), (300, 40)])
+@pytest.mark.parametrize("with_scores", [True, False])
+def test_decode_parity_eight_wave_shapes(m, m_out, N, nsplit, with_scores):
+    """Query groups larger than 4 with 2-bit codes take the eight-wave kernel (block data staged in LDS
+    by loads that write LDS directly): every sketch shape it serves, ragged contexts, one chunk, several
+    and more chunks than blocks, with and without the score output (the benchmark's launch)."""
+    base = SCALED["llama31_70b_gqa_decode"]
+    w = base.scaled(B=2, Hq=16, Hkv=2, N=N, m=m, m_out=m_out, n_out=base.n_out if m_out else 0)
+    log(f"[decode eight-wave] m={m} m_out={m_out} N={N} nsplit={nsplit} scores={with_scores}")
+    x = inputs(w)
+    kq = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
+    cache = {"bits": kq["bits"], "norms": kq["norms"], **oracle.quantize_values(x["V"], w.nbits)}
+    out, scores = run_decode(qjl, w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, w.N, nsplit=nsplit,
+                             with_scores=with_scores)
+    units = [(b, hq) for b in range(w.B) for hq in range(w.Hq)]
+    check_decode(w, x["Q"], x["S_in"], x["S_out"], x["oidx"], cache, w.N, out, scores, units,
+                 what=f"eight-wave m={m} m_out={m_out} N={N}")
