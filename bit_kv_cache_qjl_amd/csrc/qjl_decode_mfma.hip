@@ -6,17 +6,18 @@
 // unquantized) and softmax attention over the estimated scores with the dequantized values ("Your
 // Brain Already Runs on 1-Bit Keys", "Keys Select. Values Deliver.").
 //
-// Scores on v_mfma_scale_f32_16x16x128_f8f6f4 (A fp8 e4m3, B fp4 e2m1): 16 tokens x 4 query heads
-// per instruction, 128 sign positions of one kind (inlier or outlier) per instruction.
+// Scores on v_mfma_scale_f32_16x16x128_f8f6f4 (A fp6 e2m3, B fp4 e2m1; with no 8-bit operand the
+// instruction issues at the fp4 rate, about 1.6x the fp8 one): 16 tokens x 4 query heads per
+// instruction, 128 sign positions of one kind (inlier or outlier) per instruction.
 //   B (sign bits): with b = 1 for a non-negative projection, a 32-bit sign word x gives four fp4
 //     operand words, one instruction each: x & 0x11111111, x & 0x22222222, x & 0x44444444 (nibble n
 //     holds bit 4n + i with the value 0.5 b, b, 2 b: e2m1 0001, 0010, 0100) and
 //     (x & 0x88888888) | 0x11111111 (e2m1 0001 or 1001: the value 0.5 - b of bit 4n + 3).
 //   A (query): x_k = 2 z_scale sqrt(pi/2)/m (S q)_k divided by its plane's bit coefficient (0.5, 1,
-//     2, -1) and scaled by a per-head power of two, split into three e4m3 pieces (each rounded to
-//     nearest, 4 significant bits, so the residual is below 2^-12 of the value); rows = (query head,
-//     piece), the fourth row of a head is zero, and the instruction's E8M0 row scales undo the powers
-//     of two.
+//     2, -1), split into four e2m3 pieces, each with its own power of two per 32 K indices (the
+//     E8M0 scale a lane supplies for its slice of the operand, 2^(s0 - 4 piece)); rows = (query
+//     head, piece).  After four pieces a value's error is at most 2^(s0 - 16), below 2^-17.9 of the
+//     largest magnitude of its 32-value slice.
 //   sign = 2b - 1, so <S q, sign> = 2 <S q, b> - sum (S q).  The plane-3 positions contribute
 //     x_k b_k - x_k / 2 by themselves; the accumulator starts at -sum x_k / 2 over the other
 //     positions, so z = |k_in| D_in + |k_out| D_out is the token's base-2 softmax logit.
@@ -79,79 +80,131 @@ __device__ __forceinline__ v8i_t sign_planes(uint32_t x, uint32_t m8, uint32_t o
                  (int)((x & m8) | o1), 0, 0, 0, 0};
 }
 
+// Score instruction: A = the query operand (fp6 e2m3) with the E8M0 scale in byte kb of sc, B = a
+// sign plane (fp4 e2m1).  The byte select is an instruction field, so kb is a constant once the
+// caller's loop over K blocks is unrolled.
+template <int KB>
+__device__ __forceinline__ v4f_t mfma_query_kb(const v8i_t& qa, const v8i_t& sb, v4f_t acc, int sc) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa, sb, acc, 2, 4, KB, sc, 0, 127);
+}
+__device__ __forceinline__ v4f_t mfma_query(int kb, const v8i_t& qa, const v8i_t& sb, v4f_t acc, int sc) {
+    switch (kb) {
+        case 0: return mfma_query_kb<0>(qa, sb, acc, sc);
+        case 1: return mfma_query_kb<1>(qa, sb, acc, sc);
+        case 2: return mfma_query_kb<2>(qa, sb, acc, sc);
+        default: return mfma_query_kb<3>(qa, sb, acc, sc);
+    }
+}
+
 // ---------------------------------------------------------------------------- query operand
+// fp6 e2m3 code of v, |v| <= 7.5, rounded to nearest even, and its value: magnitudes below 2 are the
+// multiples of 1/8 (codes 0..16), [2, 4) the multiples of 1/4 (codes 16..24), [4, 7.5] the multiples
+// of 1/2 (codes 24..31); bit 5 is the sign.
+__device__ __forceinline__ uint32_t e2m3_code(float v, float& value) {
+    const float a = fabsf(v);
+    const int k = a < 2.f ? 3 : (a < 4.f ? 2 : 1);          // the spacing is 2^-k
+    const float r = fminf(rintf(ldexpf(a, k)), k == 1 ? 15.f : 16.f);
+    const float d = ldexpf(r, -k);
+    value = v < 0.f ? -d : d;
+    const uint32_t c = (uint32_t)(8 * (3 - k)) + (uint32_t)r;
+    return v < 0.f ? (c | 32u) : c;
+}
+
+// The smallest power-of-two exponent s with mx <= 7.5 2^s (0 for mx = 0), within the E8M0 range.
+__device__ __forceinline__ int e2m3_scale_exp(float mx) {
+    if (!(mx > 0.f)) return 0;
+    const int e = __builtin_amdgcn_frexp_expf(mx);                // mx = f 2^e, f in [0.5, 1)
+    const int s = __builtin_amdgcn_frexp_mantf(mx) <= 0.9375f ? e - 3 : e - 2;
+    return s < -127 ? -127 : s;
+}
+
 // The matrix-core operand of one query head, built by one wave from the head's projections
 // x_j = 2 z_scale sqrt(pi/2)/m (S q)_j (inlier j < m, then outlier, natural order, in LDS; for the
-// two-sided estimator x_j = 2 z_scale |q_part|/m sign((S q)_j) instead): the
-// A-operand bytes in the order the decode kernel loads them, [K block kb][piece][lane group ga][32
-// bytes] (byte ea of lane group ga is K index k = 16 ga + ea % 16 + 64 (ea / 16) of the instruction,
-// and K index k pairs with bit 4n + i, n = (k % 32) % 8, i = (k % 32) / 8, of the sign word that B
-// lane group k / 32 supplies), and the per-head constants [-sum x_in / 2, -sum x_out / 2 (both over
-// the positions outside plane 3), e_in, e_out].
+// two-sided estimator x_j = 2 z_scale |q_part|/m sign((S q)_j) instead).
+// A K block kb is one instruction's 128 K indices; lane group ga of the instruction supplies K indices
+// 32 ga .. 32 ga + 31, which pair with the sign word of B lane group ga: K index 32 ga + j is bit
+// 4 (j % 8) + j / 8 of that word (plane j / 8).  Each value is divided by its plane's bit coefficient
+// (0.5, 1, 2, -1) and split into four fp6 e2m3 pieces with a power of two per (K block, piece, lane
+// group) (the instruction's E8M0 scale of that lane): piece p is the residual after pieces 0 .. p-1
+// at 2^(s0 - 4 p), where 2^s0 takes the 32 values' largest magnitude into (3.75, 7.5].
+// Output, per K block: [piece][lane group][8 words] = the 32 e2m3 codes packed from bit 0 (6 words),
+// the E8M0 byte 127 + s (word 6) and a zero word; then the per-head constants [-sum x_in / 2,
+// -sum x_out / 2 (both over the positions outside plane 3), 0, 0].
 __device__ void query_operand_wave(const float* xs, int m, int m_out, int win4, int wout4, uint32_t* dst, float* qc,
                                    int lane) {
-    // |x| divided by its plane's bit coefficient (0.5, 1, 2, -1 for position % 4 = 0, 1, 2, 3)
-    auto plane_abs = [](float x, int pos) {
-        const int i = pos & 3;
-        return fabsf(x) * (i == 0 ? 2.f : (i == 2 ? 0.5f : 1.f));
-    };
-    float sum_in = 0.f, sum_out = 0.f, mx_in = 0.f, mx_out = 0.f;
-    for (int j = lane; j < m; j += 64) {
-        const float x = xs[j];
-        if ((j & 3) != 3) sum_in += x;           // plane-3 positions carry their own -x/2
-        mx_in = fmaxf(mx_in, plane_abs(x, j));
-    }
-    for (int j = lane; j < m_out; j += 64) {   // m is a multiple of 4: position m + j is in plane j % 4
-        const float x = xs[m + j];
-        if ((j & 3) != 3) sum_out += x;
-        mx_out = fmaxf(mx_out, plane_abs(x, j));
-    }
+    float sum_in = 0.f, sum_out = 0.f;
+    for (int j = lane; j < m; j += 64)
+        if ((j & 3) != 3) sum_in += xs[j];        // plane-3 positions carry their own -x/2
+    for (int j = lane; j < m_out; j += 64)      // m is a multiple of 4: position m + j is in plane j % 4
+        if ((j & 3) != 3) sum_out += xs[m + j];
     sum_in = wave64_sum(sum_in);
     sum_out = wave64_sum(sum_out);
-    mx_in = wave64_max(mx_in);
-    mx_out = wave64_max(mx_out);
-    // the power of two that takes the largest operand value into [128, 256), kept within the E8M0
-    // range of the row scales 127 - e - 4 piece
-    auto pick_exp = [](float mx) {
-        if (!(mx > 0.f)) return 0;
-        const int e = 8 - __builtin_amdgcn_frexp_expf(mx);
-        return e > 114 ? 114 : (e < -120 ? -120 : e);
-    };
-    const int e_in = pick_exp(mx_in), e_out = pick_exp(mx_out);
     if (lane == 0) {
         qc[0] = -0.5f * sum_in;
         qc[1] = -0.5f * sum_out;
-        qc[2] = __int_as_float(e_in);
-        qc[3] = __int_as_float(e_out);
+        qc[2] = 0.f;
+        qc[3] = 0.f;
     }
-    // one task = 4 consecutive bytes e0 .. e0 + 3 of lane group ga in K block kb, all three pieces
-    // (words kb 128 + piece 32 + ga 8 + e0 / 4; the fourth piece's word is zero)
-    const int W = 4 * (win4 + wout4);
-    for (int task = lane; task < 8 * W; task += 64) {
-        const int kb = task >> 5;
-        const int ga = (task >> 3) & 3;
-        const int e0 = (task & 7) * 4;
-        const bool out = kb >= win4;
-        const int e = out ? e_out : e_in;
-        float y[4];
+    // eight lanes per (K block, lane group): lane j4 holds K indices 4 j4 .. 4 j4 + 3 of the group;
+    // blocks kb 4 + ga = lane / 8 and 8 + lane / 8 (at most 16: m + m_out <= 512) side by side, so the
+    // two dependency chains interleave.  Cross-lane steps are DPP moves within rows of 8 lanes.
+    const int W4 = win4 + wout4;
+    const int j4 = lane & 7;
+    float r[2][4];
+    bool live[2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int ea = e0 + q;
-            const int k = 16 * ga + (ea & 15) + 64 * (ea >> 4);
-            const int gb = k >> 5, eb = k & 31;
-            const int plane = eb >> 3, n = eb & 7;
-            const int word = out ? 4 * win4 + gb * wout4 + (kb - win4) : gb * win4 + kb;
-            // divided by the plane's bit coefficient and scaled by the head's power of two (exact)
-            const float v = ldexpf(xs[32 * word + 4 * n + plane], e + (plane == 0 ? 1 : (plane == 2 ? -1 : 0)));
-            y[q] = plane == 3 ? -v : v;
+    for (int hb = 0; hb < 2; ++hb) {
+        const int blk = 8 * hb + (lane >> 3);
+        live[hb] = blk < 4 * W4;
+        const int kb = blk >> 2, ga = blk & 3;
+        const bool out = kb >= win4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int jj = 4 * j4 + e;
+            const int plane = jj >> 3, n = jj & 7;
+            const int word = out ? 4 * win4 + ga * wout4 + (kb - win4) : ga * win4 + kb;
+            const float x = live[hb] ? xs[32 * word + 4 * n + plane] : 0.f;
+            const float v = ldexpf(x, plane == 0 ? 1 : (plane == 2 ? -1 : 0));
+            r[hb][e] = plane == 3 ? -v : v;
         }
-        uint32_t k[3];
-        fp8_pieces(y, k);
-        uint32_t* d = dst + kb * 128 + ga * 8 + (task & 7);
-        d[0] = k[0];
-        d[32] = k[1];
-        d[64] = k[2];
-        d[96] = 0u;
+    }
+    // the slice's largest magnitude sets 2^s0 (largest scaled value in (3.75, 7.5]); piece p uses
+    // 2^(s0 - 4 p): the residual after piece p is at most 2^(s0 - 2), 2^(s0 - 7), 2^(s0 - 12) (half a
+    // step of e2m3 at the piece's largest scaled value 7.5, 4, 2), so the next piece's scaled values
+    // are at most 4, 2, 1, and the error after the four pieces is at most 2^(s0 - 16)
+    int s0[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+        float mx = fmaxf(fmaxf(fabsf(r[hb][0]), fabsf(r[hb][1])), fmaxf(fabsf(r[hb][2]), fabsf(r[hb][3])));
+        mx = fmaxf(mx, dpp_mov<0xB1>(mx));     // quad_perm [1,0,3,2]
+        mx = fmaxf(mx, dpp_mov<0x4E>(mx));     // quad_perm [2,3,0,1]
+        mx = fmaxf(mx, dpp_mov<0x141>(mx));    // row_half_mirror: the other quad of the 8 lanes
+        s0[hb] = e2m3_scale_exp(mx);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            const int sc = s0[hb] - 4 * p < -127 ? -127 : s0[hb] - 4 * p;
+            uint32_t w24 = 0u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float d;
+                w24 |= e2m3_code(ldexpf(r[hb][e], -sc), d) << (6 * e);
+                r[hb][e] -= ldexpf(d, sc);           // exact: the piece holds the leading bits of r
+            }
+            // lane j4 covers bits 24 j4 .. 24 j4 + 23 of the group's 192; word w (0..5) is bits
+            // 8 (j4 % 4) .. of lanes j4 and j4 + 1 for j4 = 0, 1, 2, 4, 5, 6 (the next lane of the quad)
+            const uint32_t next = __builtin_bit_cast(uint32_t, dpp_mov<0xF9>(__builtin_bit_cast(float, w24)));  // quad_perm [1,2,3,3]
+            const uint64_t both = (uint64_t)w24 | ((uint64_t)next << 24);
+            const int blk = 8 * hb + (lane >> 3);
+            uint32_t* d = dst + (blk >> 2) * 128 + p * 32 + (blk & 3) * 8;
+            if (live[hb]) {
+                if ((j4 & 3) != 3) d[j4 - (j4 >> 2)] = (uint32_t)(both >> (8 * (j4 & 3)));
+                else if (j4 == 3) d[6] = (uint32_t)(127 + sc);
+                else d[7] = 0u;
+            }
+        }
     }
 }
 
@@ -481,22 +534,22 @@ __global__ __launch_bounds__(kMThreads, (R == 1 && NB == 2) ? 2 : 1) void decode
     //      K slice hh
     const int rh = t >> 2, pc = lane & 3;
     v8i_t sA[R][W4];
-    int sc_in[R], sc_out[R];
+    int sc[R];                                   // E8M0 scale of K block kb in byte kb
 #pragma unroll
     for (int rg = 0; rg < R; ++rg) {
         const int qa_head = HPG * hg + 4 * rg + rh;
-        sc_in[rg] = sc_out[rg] = 127;
+        sc[rg] = 0x7F7F7F7F;
         if (qa_head < a.g) {
             const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.sq) +
                                                               (size_t)(head0 + qa_head) * (128 * WB));
+            uint32_t bytes = 0u;
 #pragma unroll
             for (int kb = 0; kb < W4; ++kb) {
                 const uint4 lo = src[kb * 32 + (pc * 4 + hh) * 2], hi = src[kb * 32 + (pc * 4 + hh) * 2 + 1];
-                sA[rg][kb] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                sA[rg][kb] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, 0, 0};
+                bytes |= (hi.z & 0xFFu) << (8 * kb);
             }
-            const float* c = a.qconst + (size_t)(head0 + qa_head) * 4;
-            sc_in[rg] = 127 - __float_as_int(c[2]) - 4 * pc;
-            sc_out[rg] = 127 - __float_as_int(c[3]) - 4 * pc;
+            sc[rg] = (int)bytes;
         } else {
 #pragma unroll
             for (int kb = 0; kb < W4; ++kb) sA[rg][kb] = v8i_t{0, 0, 0, 0, 0, 0, 0, 0};
@@ -576,15 +629,14 @@ __global__ __launch_bounds__(kMThreads, (R == 1 && NB == 2) ? 2 : 1) void decode
                 v4f_t din = v4f_t{cin[rg], 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < WIN4; ++kb)
-                    din = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sA[rg][kb], bin[kb], din, 0, 4, 0, sc_in[rg], 0, 127);
-                float zz = n_in * ((din[0] + din[1]) + din[2]);
+                    din = mfma_query(kb, sA[rg][kb], bin[kb], din, sc[rg]);
+                float zz = n_in * ((din[0] + din[1]) + (din[2] + din[3]));
                 if constexpr (WOUT4 > 0) {
                     v4f_t dout = v4f_t{cout[rg], 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kb = 0; kb < WOUT4; ++kb)
-                        dout = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sA[rg][WIN4 + kb], bout[kb], dout, 0, 4, 0,
-                                                                                sc_out[rg], 0, 127);
-                    zz = fmaf(n_out, (dout[0] + dout[1]) + dout[2], zz);
+                        dout = mfma_query(WIN4 + kb, sA[rg][WIN4 + kb], bout[kb], dout, sc[rg]);
+                    zz = fmaf(n_out, (dout[0] + dout[1]) + (dout[2] + dout[3]), zz);
                 }
                 if constexpr (DBG) {
                     const int P = s0 + mfma_token(s, t);
@@ -835,22 +887,22 @@ __global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs 
 
     const int rh = t >> 2, pc = lane & 3;
     v8i_t sA[R][W4];
-    int sc_in[R], sc_out[R];
+    int sc[R];                                   // E8M0 scale of K block kb in byte kb
 #pragma unroll
     for (int rg = 0; rg < R; ++rg) {
         const int qa_head = HPG * hg + 4 * rg + rh;
-        sc_in[rg] = sc_out[rg] = 127;
+        sc[rg] = 0x7F7F7F7F;
         if (qa_head < a.g) {
             const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.sq) +
                                                               (size_t)(head0 + qa_head) * (128 * WB));
+            uint32_t bytes = 0u;
 #pragma unroll
             for (int kb = 0; kb < W4; ++kb) {
                 const uint4 lo = src[kb * 32 + (pc * 4 + hh) * 2], hi = src[kb * 32 + (pc * 4 + hh) * 2 + 1];
-                sA[rg][kb] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                sA[rg][kb] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, 0, 0};
+                bytes |= (hi.z & 0xFFu) << (8 * kb);
             }
-            const float* c = a.qconst + (size_t)(head0 + qa_head) * 4;
-            sc_in[rg] = 127 - __float_as_int(c[2]) - 4 * pc;
-            sc_out[rg] = 127 - __float_as_int(c[3]) - 4 * pc;
+            sc[rg] = (int)bytes;
         } else {
 #pragma unroll
             for (int kb = 0; kb < W4; ++kb) sA[rg][kb] = v8i_t{0, 0, 0, 0, 0, 0, 0, 0};
@@ -951,15 +1003,14 @@ __global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs 
                 v4f_t din = v4f_t{cin[rg], 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < WIN4; ++kb)
-                    din = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sA[rg][kb], bin[kb], din, 0, 4, 0, sc_in[rg], 0, 127);
-                float zz = n_in * ((din[0] + din[1]) + din[2]);
+                    din = mfma_query(kb, sA[rg][kb], bin[kb], din, sc[rg]);
+                float zz = n_in * ((din[0] + din[1]) + (din[2] + din[3]));
                 if constexpr (WOUT4 > 0) {
                     v4f_t dout = v4f_t{cout[rg], 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kb = 0; kb < WOUT4; ++kb)
-                        dout = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sA[rg][WIN4 + kb], bout[kb], dout, 0, 4, 0,
-                                                                                sc_out[rg], 0, 127);
-                    zz = fmaf(n_out, (dout[0] + dout[1]) + dout[2], zz);
+                        dout = mfma_query(WIN4 + kb, sA[rg][WIN4 + kb], bout[kb], dout, sc[rg]);
+                    zz = fmaf(n_out, (dout[0] + dout[1]) + (dout[2] + dout[3]), zz);
                 }
                 if constexpr (DBG) {
                     const int P = s0 + mfma_token(s, t);
