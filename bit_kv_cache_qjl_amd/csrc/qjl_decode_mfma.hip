@@ -97,113 +97,93 @@ __device__ __forceinline__ v4f_t mfma_query(int kb, const v8i_t& qa, const v8i_t
 }
 
 // ---------------------------------------------------------------------------- query operand
-// fp6 e2m3 code of v, |v| <= 7.5, rounded to nearest even, and its value: magnitudes below 2 are the
-// multiples of 1/8 (codes 0..16), [2, 4) the multiples of 1/4 (codes 16..24), [4, 7.5] the multiples
-// of 1/2 (codes 24..31); bit 5 is the sign.
-__device__ __forceinline__ uint32_t e2m3_code(float v, float& value) {
-    const float a = fabsf(v);
-    const int k = a < 2.f ? 3 : (a < 4.f ? 2 : 1);          // the spacing is 2^-k
-    const float r = fminf(rintf(ldexpf(a, k)), k == 1 ? 15.f : 16.f);
-    const float d = ldexpf(r, -k);
-    value = v < 0.f ? -d : d;
-    const uint32_t c = (uint32_t)(8 * (3 - k)) + (uint32_t)r;
-    return v < 0.f ? (c | 32u) : c;
-}
-
-// The smallest power-of-two exponent s with mx <= 7.5 2^s (0 for mx = 0), within the E8M0 range.
+// The smallest power-of-two exponent s with mx <= 7.5 2^s (0 for mx = 0), at least -126 (a normal
+// fp32 scale for the conversions, a valid E8M0 byte for the instruction).
 __device__ __forceinline__ int e2m3_scale_exp(float mx) {
     if (!(mx > 0.f)) return 0;
     const int e = __builtin_amdgcn_frexp_expf(mx);                // mx = f 2^e, f in [0.5, 1)
     const int s = __builtin_amdgcn_frexp_mantf(mx) <= 0.9375f ? e - 3 : e - 2;
-    return s < -127 ? -127 : s;
+    return s < -126 ? -126 : s;
 }
 
-// The matrix-core operand of one query head, built by one wave from the head's projections
-// x_j = 2 z_scale sqrt(pi/2)/m (S q)_j (inlier j < m, then outlier, natural order, in LDS; for the
-// two-sided estimator x_j = 2 z_scale |q_part|/m sign((S q)_j) instead).
-// A K block kb is one instruction's 128 K indices; lane group ga of the instruction supplies K indices
-// 32 ga .. 32 ga + 31, which pair with the sign word of B lane group ga: K index 32 ga + j is bit
-// 4 (j % 8) + j / 8 of that word (plane j / 8).  Each value is divided by its plane's bit coefficient
-// (0.5, 1, 2, -1) and split into four fp6 e2m3 pieces with a power of two per (K block, piece, lane
-// group) (the instruction's E8M0 scale of that lane): piece p is the residual after pieces 0 .. p-1
-// at 2^(s0 - 4 p), where 2^s0 takes the 32 values' largest magnitude into (3.75, 7.5].
+// The matrix-core operand of a query head from its projections x_j = 2 z_scale sqrt(pi/2)/m (S q)_j
+// (inlier j < m, then outlier, natural order, in LDS; for the two-sided estimator
+// x_j = 2 z_scale |q_part|/m sign((S q)_j) instead).  One lane per 32-value slice: a row of 16 lanes
+// (one DPP row) serves one head, lane slice = 4 kb + ga covers lane group ga of K block kb (one
+// instruction's 128 K indices; lane group ga supplies K indices 32 ga .. 32 ga + 31, which pair with
+// the sign word of B lane group ga: K index 32 ga + j is bit 4 (j % 8) + j / 8 of that word, plane
+// j / 8).  The 32 values of a slice are one sign word's projections, divided by their plane's bit
+// coefficient (0.5, 1, 2, -1) and split into four fp6 e2m3 pieces: piece p is the residual after
+// pieces 0 .. p-1 at the power of two 2^(s0 - 4 p) (the instruction's E8M0 scale of that lane),
+// where 2^s0 takes the slice's largest magnitude into (3.75, 7.5].  The residual after piece p is at
+// most 2^(s0 - 2), 2^(s0 - 7), 2^(s0 - 12) (half a step of e2m3 at the piece's largest scaled value
+// 7.5, 4, 2), so the next piece's scaled values are at most 4, 2, 1, and the error after the four
+// pieces is at most 2^(s0 - 16).  The pieces come from gfx950's packed conversions (32 values in one
+// instruction, nearest even; element 2i from the first source's i, 2i + 1 from the second's).
 // Output, per K block: [piece][lane group][8 words] = the 32 e2m3 codes packed from bit 0 (6 words),
 // the E8M0 byte 127 + s (word 6) and a zero word; then the per-head constants [-sum x_in / 2,
-// -sum x_out / 2 (both over the positions outside plane 3), 0, 0].
-__device__ void query_operand_wave(const float* xs, int m, int m_out, int win4, int wout4, uint32_t* dst, float* qc,
-                                   int lane) {
-    float sum_in = 0.f, sum_out = 0.f;
-    for (int j = lane; j < m; j += 64)
-        if ((j & 3) != 3) sum_in += xs[j];        // plane-3 positions carry their own -x/2
-    for (int j = lane; j < m_out; j += 64)      // m is a multiple of 4: position m + j is in plane j % 4
-        if ((j & 3) != 3) sum_out += xs[m + j];
-    sum_in = wave64_sum(sum_in);
-    sum_out = wave64_sum(sum_out);
-    if (lane == 0) {
-        qc[0] = -0.5f * sum_in;
-        qc[1] = -0.5f * sum_out;
+// -sum x_out / 2 (both over the positions outside plane 3), 0, 0] (written by the lane of slice 0).
+// Every lane of the row takes part (the sums are DPP row reductions); active is uniform per row.
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+typedef float v32f_t __attribute__((ext_vector_type(32)));
+typedef uint32_t v6u_t __attribute__((ext_vector_type(6)));
+__device__ void query_operand_slices(const float* xs, int win4, int wout4, int slice, bool active, uint32_t* dst,
+                                     float* qc) {
+    const int W4 = win4 + wout4;
+    const int kb = slice >> 2, ga = slice & 3;
+    const bool live = active && slice < 4 * W4;
+    const bool out = kb >= win4;
+    const int word = out ? 4 * win4 + ga * wout4 + (kb - win4) : ga * win4 + kb;
+    float x[32];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float4 v = live ? reinterpret_cast<const float4*>(xs + 32 * word)[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+        x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+    }
+    // position 4 n + plane; plane-3 positions carry their own -x/2 and stay out of the sums
+    float part = 0.f;
+#pragma unroll
+    for (int q = 0; q < 32; ++q)
+        if ((q & 3) != 3) part += x[q];
+    const float s_in = row16_sum(out ? 0.f : part), s_out = row16_sum(out ? part : 0.f);
+    if (active && slice == 0) {
+        qc[0] = -0.5f * s_in;
+        qc[1] = -0.5f * s_out;
         qc[2] = 0.f;
         qc[3] = 0.f;
     }
-    // eight lanes per (K block, lane group): lane j4 holds K indices 4 j4 .. 4 j4 + 3 of the group;
-    // blocks kb 4 + ga = lane / 8 and 8 + lane / 8 (at most 16: m + m_out <= 512) side by side, so the
-    // two dependency chains interleave.  Cross-lane steps are DPP moves within rows of 8 lanes.
-    const int W4 = win4 + wout4;
-    const int j4 = lane & 7;
-    float r[2][4];
-    bool live[2];
+    // K order j = 8 plane + n: element 2 i of the slice in ev[i], 2 i + 1 in od[i]
+    v16f_t ev, od;
+    float mx = 0.f;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-        const int blk = 8 * hb + (lane >> 3);
-        live[hb] = blk < 4 * W4;
-        const int kb = blk >> 2, ga = blk & 3;
-        const bool out = kb >= win4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int jj = 4 * j4 + e;
-            const int plane = jj >> 3, n = jj & 7;
-            const int word = out ? 4 * win4 + ga * wout4 + (kb - win4) : ga * win4 + kb;
-            const float x = live[hb] ? xs[32 * word + 4 * n + plane] : 0.f;
-            const float v = ldexpf(x, plane == 0 ? 1 : (plane == 2 ? -1 : 0));
-            r[hb][e] = plane == 3 ? -v : v;
-        }
+    for (int j = 0; j < 32; ++j) {
+        const int plane = j >> 3, n = j & 7;
+        const float v = x[4 * n + plane] * (plane == 0 ? 2.f : (plane == 1 ? 1.f : (plane == 2 ? 0.5f : -1.f)));
+        mx = fmaxf(mx, fabsf(v));
+        if (j & 1) od[j >> 1] = v;
+        else ev[j >> 1] = v;
     }
-    // the slice's largest magnitude sets 2^s0 (largest scaled value in (3.75, 7.5]); piece p uses
-    // 2^(s0 - 4 p): the residual after piece p is at most 2^(s0 - 2), 2^(s0 - 7), 2^(s0 - 12) (half a
-    // step of e2m3 at the piece's largest scaled value 7.5, 4, 2), so the next piece's scaled values
-    // are at most 4, 2, 1, and the error after the four pieces is at most 2^(s0 - 16)
-    int s0[2];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-        float mx = fmaxf(fmaxf(fabsf(r[hb][0]), fabsf(r[hb][1])), fmaxf(fabsf(r[hb][2]), fabsf(r[hb][3])));
-        mx = fmaxf(mx, dpp_mov<0xB1>(mx));     // quad_perm [1,0,3,2]
-        mx = fmaxf(mx, dpp_mov<0x4E>(mx));     // quad_perm [2,3,0,1]
-        mx = fmaxf(mx, dpp_mov<0x141>(mx));    // row_half_mirror: the other quad of the 8 lanes
-        s0[hb] = e2m3_scale_exp(mx);
-    }
+    const int s0 = e2m3_scale_exp(mx);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
+        const int sc = s0 - 4 * p < -126 ? -126 : s0 - 4 * p;
+        const float scale = ldexpf(1.f, sc);
+        const v6u_t pk = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, scale);
+        // the sources (and the scale) stay live across each conversion, so its destination cannot share
+        // their registers (the compiler would otherwise allow it, and the conversions read their
+        // sources after writing part of the destination)
+        asm volatile("" :: "v"(ev), "v"(od), "v"(scale));
+        const v32f_t d = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(pk, scale);
+        asm volatile("" :: "v"(pk), "v"(scale));
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-            const int sc = s0[hb] - 4 * p < -127 ? -127 : s0[hb] - 4 * p;
-            uint32_t w24 = 0u;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float d;
-                w24 |= e2m3_code(ldexpf(r[hb][e], -sc), d) << (6 * e);
-                r[hb][e] -= ldexpf(d, sc);           // exact: the piece holds the leading bits of r
-            }
-            // lane j4 covers bits 24 j4 .. 24 j4 + 23 of the group's 192; word w (0..5) is bits
-            // 8 (j4 % 4) .. of lanes j4 and j4 + 1 for j4 = 0, 1, 2, 4, 5, 6 (the next lane of the quad)
-            const uint32_t next = __builtin_bit_cast(uint32_t, dpp_mov<0xF9>(__builtin_bit_cast(float, w24)));  // quad_perm [1,2,3,3]
-            const uint64_t both = (uint64_t)w24 | ((uint64_t)next << 24);
-            const int blk = 8 * hb + (lane >> 3);
-            uint32_t* d = dst + (blk >> 2) * 128 + p * 32 + (blk & 3) * 8;
-            if (live[hb]) {
-                if ((j4 & 3) != 3) d[j4 - (j4 >> 2)] = (uint32_t)(both >> (8 * (j4 & 3)));
-                else if (j4 == 3) d[6] = (uint32_t)(127 + sc);
-                else d[7] = 0u;
-            }
+        for (int i = 0; i < 16; ++i) {
+            ev[i] -= d[2 * i];                   // exact: the piece holds the leading bits of the residual
+            od[i] -= d[2 * i + 1];
+        }
+        if (live) {
+            uint4* o = reinterpret_cast<uint4*>(dst + kb * 128 + p * 32 + ga * 8);
+            o[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+            o[1] = make_uint4(pk[4], pk[5], (uint32_t)(127 + sc), 0u);
         }
     }
 }
@@ -214,7 +194,7 @@ __global__ __launch_bounds__(256) void qproj_f32_kernel(DecodeArgs a, int win4, 
     __shared__ float qin[kD];
     __shared__ float qo[kMaxOutliers];
     __shared__ int so[kMaxOutliers];
-    __shared__ float xs[kMaxBits];
+    __shared__ __attribute__((aligned(16))) float xs[kMaxBits];
     const int tid = threadIdx.x;
     const int bh = blockIdx.x;
     const int hq = bh % a.Hq;
@@ -253,8 +233,8 @@ __global__ __launch_bounds__(256) void qproj_f32_kernel(DecodeArgs a, int win4, 
     }
     __syncthreads();
     if (tid < 64)
-        query_operand_wave(xs, a.m, a.m_out, win4, wout4, reinterpret_cast<uint32_t*>(a.sq) + (size_t)bh * (128 * (win4 + wout4)),
-                           a.qconst + (size_t)bh * 4, tid);
+        query_operand_slices(xs, win4, wout4, tid & 15, tid < 16,
+                             reinterpret_cast<uint32_t*>(a.sq) + (size_t)bh * (128 * (win4 + wout4)), a.qconst + (size_t)bh * 4);
 }
 
 // bf16: one workgroup per (sequence, KV head) projects the KV head's g query heads (and, for a decode
@@ -272,7 +252,7 @@ template <int WPW, bool APPEND>
 __global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs ap) {
     __shared__ __attribute__((aligned(16))) uint16_t vin[16 * kVRow];    // vectors, outlier channels zeroed
     __shared__ __attribute__((aligned(16))) uint16_t vout[16 * kVRow];   // vectors on the outlier channels only
-    __shared__ float xs[16 * kXPitch];
+    __shared__ __attribute__((aligned(16))) float xs[16 * kXPitch];
     __shared__ uint32_t s_mask[4];
     __shared__ float s_qn[16][2];                                         // vector norms (two-sided)
     typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -421,14 +401,15 @@ __global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs 
         }
         __syncthreads();
 
-        // ---- operands of this pass's query heads, one wave per head
-        for (int v = wave; v < 16; v += 4) {
+        // ---- operands of this pass's query heads: wave w serves columns w, w + 4, w + 8, w + 12, one
+        //      row of 16 lanes each
+        {
+            const int v = wave + 4 * (lane >> 4);
             const int col = c0 + v;
-            if (col >= ncol) break;
-            if (APPEND && col == 0) continue;
-            const int64_t hq = head0 + col - (APPEND ? 1 : 0);
-            query_operand_wave(xs + v * kXPitch, a.m, a.m_out, win4, wout4,
-                               reinterpret_cast<uint32_t*>(a.sq) + hq * (128 * (win4 + wout4)), a.qconst + hq * 4, lane);
+            const bool active = col < ncol && !(APPEND && col == 0);
+            const int64_t hq = active ? head0 + col - (APPEND ? 1 : 0) : 0;
+            query_operand_slices(xs + v * kXPitch, win4, wout4, lane & 15, active,
+                                 reinterpret_cast<uint32_t*>(a.sq) + hq * (128 * (win4 + wout4)), a.qconst + hq * 4);
         }
         __syncthreads();
     }
