@@ -35,13 +35,19 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0     # MI355X dense bf16
 BYTES_PER_TOKEN_HEAD = 104          # 64 B signs + 4 B norms + 32 B codes + 4 B (min, step)
 DECODE_SOURCES = [os.path.join(ROOT, "bit_kv_cache_qjl_amd", "csrc", f) for f in
                   ("qjl_decode.hip", "qjl_decode_mfma.hip", "qjl_decode_common.h", "qjl_common.h")]
-DECODE_KERNEL = "decode_mfma_kernel"   # the dominant kernel of the 2-bit value decode workloads
+DECODE_KERNEL = "decode_mfma"          # name prefix of the matrix-core decode kernels (counter records)
 DECODE_KERNEL_VECTOR = "decode_kernel"  # the vector-unit (byte-table) decode
+
+
+def mfma_decode_kernel(w: si.Workload) -> str:
+    """The matrix-core decode kernel a workload runs: eight waves over two row groups of four query
+    heads when a KV head has more than four (2-bit codes), else four waves."""
+    return "decode_mfma8_kernel" if (w.g > 4 and w.nbits == 2) else "decode_mfma_kernel"
 HEADLINE = "llama31_70b_gqa_decode"
 DECODE_WORKLOADS = ("llama31_70b_gqa_decode", "llama2_7b_decode", "llama3_8b_gqa_decode")
 PATHS = {"auto": 0, "mfma": 1, "valu": 2}
 # the arithmetic each decode path computes in (bf16 keys, queries and JL matrices in; fp32 accumulation)
-DTYPE = {"mfma": "bf16 in; 1-bit keys x fp8e4m3x3 query, 2-bit values x fp8e4m3x3 weights on fp4 MFMA; fp32 acc",
+DTYPE = {"mfma": "bf16 in; 1-bit keys x fp6e2m3x4 query, 2-bit values x fp8e4m3x3 weights on f8f6f4 MFMA; fp32 acc",
          "valu": "bf16 in; 1-bit keys x fp32 byte tables, 2-bit values x fp16 weights (v_dot2); fp32 acc"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_{}_traffic.json")
 
@@ -106,7 +112,8 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str) -> int:
     dec_f = statistics.mean(_per_dispatch(fetch_csv, "FETCH_SIZE", DECODE_KERNEL))
     dec_w = statistics.mean(_per_dispatch(write_csv, "WRITE_SIZE", DECODE_KERNEL))
     w = si.WORKLOADS[workload]
-    rec = {"workload": workload, "kernel": DECODE_KERNEL, "decode_source_sha256_16": source_hash(DECODE_SOURCES),
+    rec = {"workload": workload, "kernel": mfma_decode_kernel(si.WORKLOADS[workload]),
+           "decode_source_sha256_16": source_hash(DECODE_SOURCES),
            "fetch_kib_per_launch": dec_f, "write_kib_per_launch": dec_w,
            "copy_fetch_kib": big_f, "copy_write_kib": big_w, "copy_bytes": CALIB_BYTES,
            "read_scale": kf, "write_scale": kw,
@@ -426,7 +433,7 @@ def bench_decode(qjl, torch, w: si.Workload, args, path: str) -> dict:
                      "frac": achieved / HBM_PEAK_GBS,
                      # counters are taken for the 2-bit matrix-core decode
                      "traffic": measured_traffic(w.name) if (w.nbits == 2 and mfma_kernel) else None,
-                     "kernel": DECODE_KERNEL if mfma_kernel else DECODE_KERNEL_VECTOR, "kernel_ms": dec_s * 1e3,
+                     "kernel": mfma_decode_kernel(w) if mfma_kernel else DECODE_KERNEL_VECTOR, "kernel_ms": dec_s * 1e3,
                      "launches_timed": n_dec, "algorithmic_bytes": bytes_alg,
                      "bytes_per_token_kv_head": bytes_per_token_head},
         "kernel_ms_per_launch": {k: v[1] / max(v[0], 1) for k, v in kernels.items()},

@@ -173,13 +173,16 @@ size_t qjl_decode_workspace_size(int B, int Hq, int Hkv, int d, int64_t N, int m
  *     out   = sum_t softmax(sm_scale * s)_t * v_t                    (fp32 accumulation)
  * where v_t = mn16 + step * code (QJL_V_CODES) or the fp32 value itself (QJL_V_F32).
  * Operand formats (`path`):
- *   matrix cores   each projected query value, times sm_scale log2(e) sqrt(pi/2)/m and a per-head power
- *                  of two, is carried as the sum of three fp8 e4m3 pieces (round to nearest; the residual
- *                  is below 2^-12 of the value), multiplied exactly with the sign bits as fp4 operands
- *                  and summed in fp32, so a score is within 2^-12 of its magnitude scale
+ *   matrix cores   each projected query value, times sm_scale log2(e) sqrt(pi/2)/m and divided by its
+ *                  sign plane's coefficient, is carried as the sum of four fp6 e2m3 pieces with a power
+ *                  of two per 32 values (piece p at 2^(s - 4p), where 2^s takes the largest magnitude
+ *                  of the 32 into (3.75, 7.5]; round to nearest), so its error is at most 2^(s - 16),
+ *                  below 2^-17.9 of that largest magnitude; multiplied exactly with the sign bits as
+ *                  fp4 operands and summed in fp32, a score is within 5.9e-4 of its magnitude scale
  *                  sqrt(pi/2) (|k_in| |Sq_in|_1/m + |k_out| |Sq_out|_1/m_out) plus fp32 rounding; each
- *                  softmax weight times its token's step is likewise carried as three e4m3 pieces
- *                  against the codes, so the value term is within 2^-12 of the largest value range;
+ *                  softmax weight times its token's step is carried as three fp8 e4m3 pieces (round
+ *                  to nearest, residual below 2^-12 of the value) against the codes, so the value
+ *                  term is within 2^-12 of the largest value range;
  *   vector units   Sq in fp32, summed through byte tables in fp32; weights times step in fp16 against
  *                  the codes (2^-11 relative).
  *   Q           [B][Hq][d] contiguous, dtype qdt; S_in / S_out / outlier_idx as for quantize (S in
