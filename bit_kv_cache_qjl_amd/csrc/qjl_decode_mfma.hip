@@ -866,39 +866,48 @@ __global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs 
     const int t_end = (int)min(a.N, (int64_t)t_begin + a.chunk);
     const int head0 = b * a.Hq + h * a.g;
 
-    const int rh = t >> 2, pc = lane & 3;
-    v8i_t sA[R][W4];
-    int sc[R];                                   // E8M0 scale of K block kb in byte kb
+    // ---- score operands: A row t of both instructions is (head t / 2, slot t % 2) of the eight heads;
+    //      instruction pp carries piece 2 pp + slot, and both accumulate into the same rows, so D row
+    //      (head, slot) ends with pieces slot and 2 + slot summed.  Lane group hh then holds the rows of
+    //      heads 2 hh and 2 hh + 1 (the score heads of the lane, index j); its value rows stay those of
+    //      heads hh and 4 + hh (row group rg of the value instructions).
+    const int ah = t >> 1, aslot = t & 1;
+    const int pc = lane & 3;                     // value instructions: A row t is (head t / 4, piece t % 4)
+    v8i_t sA[2][W4];
+    int sc[2];                                   // E8M0 scale of K block kb in byte kb
 #pragma unroll
-    for (int rg = 0; rg < R; ++rg) {
-        const int qa_head = HPG * hg + 4 * rg + rh;
-        sc[rg] = 0x7F7F7F7F;
+    for (int pp = 0; pp < 2; ++pp) {
+        const int qa_head = HPG * hg + ah;
+        const int piece = 2 * pp + aslot;
+        sc[pp] = 0x7F7F7F7F;
         if (qa_head < a.g) {
             const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.sq) +
                                                               (size_t)(head0 + qa_head) * (128 * WB));
             uint32_t bytes = 0u;
 #pragma unroll
             for (int kb = 0; kb < W4; ++kb) {
-                const uint4 lo = src[kb * 32 + (pc * 4 + hh) * 2], hi = src[kb * 32 + (pc * 4 + hh) * 2 + 1];
-                sA[rg][kb] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, 0, 0};
+                const uint4 lo = src[kb * 32 + (piece * 4 + hh) * 2], hi = src[kb * 32 + (piece * 4 + hh) * 2 + 1];
+                sA[pp][kb] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, 0, 0};
                 bytes |= (hi.z & 0xFFu) << (8 * kb);
             }
-            sc[rg] = (int)bytes;
+            sc[pp] = (int)bytes;
         } else {
 #pragma unroll
-            for (int kb = 0; kb < W4; ++kb) sA[rg][kb] = v8i_t{0, 0, 0, 0, 0, 0, 0, 0};
+            for (int kb = 0; kb < W4; ++kb) sA[pp][kb] = v8i_t{0, 0, 0, 0, 0, 0, 0, 0};
         }
     }
-    float cin[R], cout[R];
-    float* sdbg[R];
+    float cin[2], cout[2];
+    float* sdbg[2];
 #pragma unroll
-    for (int rg = 0; rg < R; ++rg) {
-        const int dhead = HPG * hg + 4 * rg + hh;
+    for (int j = 0; j < 2; ++j) {
+        const int dhead = HPG * hg + 2 * hh + j;
         const bool ok = dhead < a.g;
-        cin[rg] = ok ? a.qconst[(size_t)(head0 + dhead) * 4] : 0.f;
-        cout[rg] = ok ? a.qconst[(size_t)(head0 + dhead) * 4 + 1] : 0.f;
-        sdbg[rg] = (DBG && ok) ? a.scores_dbg + (size_t)(head0 + dhead) * a.N : nullptr;
+        cin[j] = ok ? a.qconst[(size_t)(head0 + dhead) * 4] : 0.f;
+        cout[j] = ok ? a.qconst[(size_t)(head0 + dhead) * 4 + 1] : 0.f;
+        sdbg[j] = (DBG && ok) ? a.scores_dbg + (size_t)(head0 + dhead) * a.N : nullptr;
     }
+    // the lane group whose score heads include value head 4 rg + hh, as a ds_bpermute byte address
+    const int perm_addr[2] = {4 * (16 * (hh >> 1) + t), 4 * (16 * (2 + (hh >> 1)) + t)};
 
     uint8_t* wt = &s_wtile[wave][0][0];
     for (int i = lane; i < R * 16 * kWPitch / 16; i += 64) reinterpret_cast<uint4*>(wt)[i] = make_uint4(0, 0, 0, 0);
@@ -979,25 +988,30 @@ __global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs 
             for (int kb = 0; kb < WIN4; ++kb) bin[kb] = sign_planes(w[kb], m8, o1);
 #pragma unroll
             for (int kb = 0; kb < WOUT4; ++kb) bout[kb] = sign_planes(w[WIN4 + kb], m8, o1);
+            v4f_t din = v4f_t{cin[0], 0.f, cin[1], 0.f};
 #pragma unroll
-            for (int rg = 0; rg < R; ++rg) {
-                v4f_t din = v4f_t{cin[rg], 0.f, 0.f, 0.f};
+            for (int kb = 0; kb < WIN4; ++kb) {
+                din = mfma_query(kb, sA[0][kb], bin[kb], din, sc[0]);
+                din = mfma_query(kb, sA[1][kb], bin[kb], din, sc[1]);
+            }
+            float zz[2] = {n_in * (din[0] + din[1]), n_in * (din[2] + din[3])};
+            if constexpr (WOUT4 > 0) {
+                v4f_t dout = v4f_t{cout[0], 0.f, cout[1], 0.f};
 #pragma unroll
-                for (int kb = 0; kb < WIN4; ++kb)
-                    din = mfma_query(kb, sA[rg][kb], bin[kb], din, sc[rg]);
-                float zz = n_in * ((din[0] + din[1]) + (din[2] + din[3]));
-                if constexpr (WOUT4 > 0) {
-                    v4f_t dout = v4f_t{cout[rg], 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int kb = 0; kb < WOUT4; ++kb)
-                        dout = mfma_query(WIN4 + kb, sA[rg][WIN4 + kb], bout[kb], dout, sc[rg]);
-                    zz = fmaf(n_out, (dout[0] + dout[1]) + (dout[2] + dout[3]), zz);
+                for (int kb = 0; kb < WOUT4; ++kb) {
+                    dout = mfma_query(WIN4 + kb, sA[0][WIN4 + kb], bout[kb], dout, sc[0]);
+                    dout = mfma_query(WIN4 + kb, sA[1][WIN4 + kb], bout[kb], dout, sc[1]);
                 }
+                zz[0] = fmaf(n_out, dout[0] + dout[1], zz[0]);
+                zz[1] = fmaf(n_out, dout[2] + dout[3], zz[1]);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
                 if constexpr (DBG) {
                     const int P = s0 + mfma_token(s, t);
-                    if (sdbg[rg] && P < t_end) sdbg[rg][P] = zz * inv_z;
+                    if (sdbg[j] && P < t_end) sdbg[j][P] = zz[j] * inv_z;
                 }
-                z[rg][s] = zz;
+                z[j][s] = zz[j];
             }
         }
         if (s0 + kMBlock > t_end) {
@@ -1036,7 +1050,8 @@ __global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs 
             m_run[rg] = m_new;
             l_acc[rg] *= alpha[rg];
             mn_acc[rg] *= alpha[rg];
-            uint8_t* row0 = wt + rg * 16 * kWPitch + (4 * hh) * kWPitch + woff;
+            // score head 2 hh + rg: value row group hh / 2, rows 4 (2 (hh % 2) + rg) ..
+            uint8_t* row0 = wt + (hh >> 1) * 16 * kWPitch + (4 * (2 * (hh & 1) + rg)) * kWPitch + woff;
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 float wgt[4];
@@ -1067,10 +1082,16 @@ __global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs 
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         load_signs_nm(s0 + kStep, nb ^ 1);
         if (__builtin_amdgcn_ballot_w64(rescale)) {
+            // the value rows of head 4 rg + hh take that head's factor from the lane group scoring it
+            // (slot hh % 2 of group 2 rg + hh / 2)
 #pragma unroll
-            for (int rg = 0; rg < R; ++rg)
+            for (int rg = 0; rg < R; ++rg) {
+                const float f0 = __int_as_float(__builtin_amdgcn_ds_bpermute(perm_addr[rg], __float_as_int(alpha[0])));
+                const float f1 = __int_as_float(__builtin_amdgcn_ds_bpermute(perm_addr[rg], __float_as_int(alpha[1])));
+                const float av = (hh & 1) ? f1 : f0;
 #pragma unroll
-                for (int cg = 0; cg < 8; ++cg) dv[rg][cg] *= alpha[rg];
+                for (int cg = 0; cg < 8; ++cg) dv[rg][cg] *= av;
+            }
         }
         // this block's code words have landed (the 12 loads issued after the weight stores may be pending)
         if constexpr (DBG) asm volatile("s_waitcnt vmcnt(0)" ::"s"(s_sgn), "s"(s_cod), "s"(s_nrm), "s"(s_met) : "memory");
@@ -1119,10 +1140,10 @@ __global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs 
 #pragma unroll
     for (int rg = 0; rg < R; ++rg) {
         const float l_sum = row16_sum(l_acc[rg]), mn_sum = row16_sum(mn_acc[rg]);
-        if (t == 0) {
-            s_red_m[wave][4 * rg + hh] = m_run[rg];
-            s_red_l[wave][4 * rg + hh] = l_sum;
-            s_red_mn[wave][4 * rg + hh] = mn_sum;
+        if (t == 0) {                            // score head 2 hh + rg
+            s_red_m[wave][2 * hh + rg] = m_run[rg];
+            s_red_l[wave][2 * hh + rg] = l_sum;
+            s_red_mn[wave][2 * hh + rg] = mn_sum;
         }
 #pragma unroll
         for (int cg = 0; cg < 8; ++cg)
