@@ -158,21 +158,37 @@ __device__ __forceinline__ uint32_t value_codes(const float (&v)[NV], uint32_t (
     const float step = (float)step16;
     const float base = (float)mn16;
     const float rstep = step != 0.f ? __builtin_amdgcn_rcpf(step) : 0.f;
-    float x[NV], r[NV];
-    bool near_tie = false;
+    // y = v rstep + (1/2 - base rstep) in two fused multiply-adds approximates Q + 1/2, with Q the
+    // recipe's fl(fl(v - base) / step); the code is rint(Q) = floor(Q + 1/2) clamped to [0, L] unless Q
+    // is a tie.  Over the quotients that decide a code (0 <= Q <= L), |y - (Q + 1/2)| is below
+    // 2^-21 (L + 2 + |base rstep|): the two roundings of Q and the one-ulp reciprocal scale with Q, the
+    // offset's rounding with |base rstep|, the last fma's with |y|.  Outside twice that margin of an
+    // integer, floor(y) is the code; within it (exact ties: bf16 values over an fp16 step land on them
+    // often enough that some lane of a wave has one about every other wave) the quotient is recomputed
+    // with the divide, one value at a time, each behind a branch of its own.
+    const float off = fmaf(-base, rstep, 0.5f);
+    const float marg = 0x1p-20f * ((float)(L + 2) + fabsf(base * rstep));
+    float y[NV], f[NV];
+    float fmin = 1.f, fmax = 0.f;
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
-        x[q] = v[q] - base;
-        const float y = x[q] * rstep;
-        r[q] = rintf(y);
-        near_tie |= fabsf(y - r[q]) >= 0.5f - 0x1p-20f * (float)(L + 2);
+        y[q] = fmaf(v[q], rstep, off);
+        f[q] = __builtin_amdgcn_fractf(y[q]);
+        fmin = __builtin_elementwise_minimum(fmin, f[q]);
+        fmax = __builtin_elementwise_maximum(fmax, f[q]);
     }
-    if (near_tie) {
+    if (fmin <= marg || fmax >= 1.f - marg) {
 #pragma unroll
-        for (int q = 0; q < NV; ++q) r[q] = rintf(x[q] / step);
+        for (int q = 0; q < NV; ++q) {
+            if (f[q] <= marg || f[q] >= 1.f - marg) {
+                asm volatile("");                // keeps the divide behind its branch
+                y[q] = rintf((v[q] - base) / step) + 0.5f;
+            }
+        }
     }
+    // floor of y clamped to [0, L + 1/2] (med3 of values that are never NaN: no canonicalizing)
 #pragma unroll
-    for (int q = 0; q < NV; ++q) code[q] = (uint32_t)fminf(fmaxf(r[q], 0.f), (float)L);
+    for (int q = 0; q < NV; ++q) code[q] = (uint32_t)__builtin_amdgcn_fmed3f(y[q], 0.f, (float)L + 0.5f);
     return (uint32_t)__builtin_bit_cast(uint16_t, mn16) | ((uint32_t)__builtin_bit_cast(uint16_t, step16) << 16);
 }
 

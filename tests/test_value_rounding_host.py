@@ -56,3 +56,45 @@ def test_code_product_rounds_like_the_division(L, ulps):
         fast = np.clip(r, 0, L)
         assert np.array_equal(fast[~fallback], exact[~fallback])
     assert np.mean(np.abs((x_uni * rcp) - np.rint(x_uni * rcp)) >= 0.5 - 2.0 ** -20 * (L + 2)) < 1e-3
+
+
+def _fma32(a, b, c):
+    """float32 fused multiply-add: the float32 product is exact in float64, so the sum is rounded once to
+    float64 and once more to float32 (a second rounding that can move the result by one float32 ulp in
+    rare halfway cases, well inside the margin the kernels keep)."""
+    return (a.astype(np.float64) * b.astype(np.float64) + c.astype(np.float64)).astype(F32)
+
+
+@pytest.mark.parametrize("L", [3, 7, 15])
+@pytest.mark.parametrize("ulps", [-1, 0, 1])
+def test_offset_product_rounds_like_the_division(L, ulps):
+    """The kernels' fast path: y = fma(v, rcp, fma(-base, rcp, 1/2)), code = floor(y) clamped to [0, L],
+    unless the fraction of y lies within 2^-20 (L + 2 + |base rcp|) of 0 or 1 (then the divide)."""
+    g = np.random.default_rng(200 + L + ulps)
+    n = 300_000
+    step = np.float16(g.uniform(1e-3, 4.0, n)).astype(F32)
+    # minima over many magnitudes, both signs (an offset far from zero stresses the offset's rounding)
+    base = np.float16(g.choice([-1.0, 1.0], n) * g.uniform(0.0, 1.0, n) * 10.0 ** g.integers(-3, 4, n)).astype(F32)
+    v_uni = (base + (g.uniform(-0.3, L + 0.3, n) * step)).astype(F32)
+    k = g.integers(-1, L + 1, n).astype(F32)
+    mid = (base + (k + F32(0.5)) * step).astype(F32)
+    v_tie = (mid.view(np.int32) + g.integers(-3, 4, n).astype(np.int32)).view(F32)
+    rcp = (F32(1.0) / step).astype(F32)
+    rcp = (rcp.view(np.int32) + np.int32(ulps)).view(F32)
+    off = _fma32(-base, rcp, np.full(n, 0.5, F32))
+    marg = (F32(2.0 ** -20) * (F32(L + 2) + np.abs((base * rcp).astype(F32)))).astype(F32)
+    for v in (v_uni, v_tie):
+        v = np.where(np.isfinite(v), v, base)           # an integer nudge of a zero midpoint is not a value
+        exact = np.clip(np.rint(((v - base).astype(F32) / step).astype(F32)), 0, L)
+        y = _fma32(v, rcp, off)
+        f = (y - np.floor(y)).astype(F32)
+        fallback = (f <= marg) | (f >= F32(1.0) - marg)
+        fast = np.floor(np.clip(y, F32(0.0), F32(L + 0.5)))
+        assert np.array_equal(fast[~fallback], exact[~fallback])
+        # every exact tie takes the divide
+        ties = ((v - base).astype(F32) / step).astype(F32) - np.floor(((v - base).astype(F32) / step).astype(F32)) == F32(0.5)
+        assert np.all(fallback[ties & (exact > 0) & (exact < L)])
+    moderate = np.abs(base / step) < 64
+    y = _fma32(v_uni, rcp, off)
+    f = y - np.floor(y)
+    assert np.mean(((f <= marg) | (f >= 1 - marg))[moderate]) < 1e-3   # the divide stays rare
