@@ -5,7 +5,7 @@
 // (take the range of the vector, divide it into 2^b equally spaced values, round each number to the
 // nearest) and the QJL summary, "Limitations" (values use token-wise quantization).
 //
-// One workgroup per (sequence, KV head, 32-token code tile) touched by the append.  Phase 1: eight
+// One workgroup per (32-token code tile touched by the append, KV head, sequence).  Phase 1: eight
 // threads own one value vector (16 channels each): an 8-lane min/max butterfly, the (min, step)
 // meta, and the codes of 16 channels into LDS, one byte per code.  Phase 2: one thread per stream
 // slot p packs the tile's 32 codes of channel code_channel(p) into nbits words (the channel-major
@@ -65,25 +65,32 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
     v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
 }
 
+// grid: x = code tile of the append (from tile_first), y = KV head, z = sequence
 template <typename VT, int NBITS>
-__global__ __launch_bounds__(kValThreads) void quantize_values_kernel(ValueQuantArgs a, int64_t tile_first, int ntiles) {
+__global__ __launch_bounds__(kValThreads) void quantize_values_kernel(ValueQuantArgs a, int64_t tile_first) {
 #pragma clang fp contract(off)
     __shared__ __attribute__((aligned(16))) uint8_t cs[kD * kRowPitch];   // [channel][token of the tile]
     const int tid = threadIdx.x;
     const int sub = tid & 7;
     const int tk = tid >> 3;
-    const int64_t bh = blockIdx.x / ntiles;           // b * Hkv + h
-    const int64_t tile = tile_first + (int)(blockIdx.x % ntiles);
-    const int h = (int)(bh % a.Hkv);
-    const int64_t b = bh / a.Hkv;
-    const int64_t pos = tile * kCodeTile + tk;        // cache position of this thread's token
-    const bool valid = pos >= a.t0 && pos < a.t0 + a.T;
+    const int h = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int64_t bh = b * a.Hkv + h;
+    const int64_t tile = tile_first + blockIdx.x;
+    const int64_t p0 = tile * kCodeTile;
+    // tokens of the tile inside the append: [ia, ib) (uniform), so a lane's test is on its 32-bit index
+    const int ia = (int)(a.t0 > p0 ? a.t0 - p0 : 0);
+    const int ib = (int)(a.t0 + a.T - p0 < kCodeTile ? a.t0 + a.T - p0 : kCodeTile);
+    const int64_t pos = p0 + tk;                      // cache position of this thread's token
+    const bool valid = tk >= ia && tk < ib;
 
     float v[16], lo[8], hi[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) lo[q] = hi[q] = 0.f;
     if (valid) {
-        const VT* src = static_cast<const VT*>(a.V) + b * a.sVb + (pos - a.t0) * a.sVt + h * a.sVh + 16 * sub;
+        // the tile's first row in the value tensor (uniform), then this lane's row and channels
+        const VT* tile_row0 = static_cast<const VT*>(a.V) + b * a.sVb + h * a.sVh + (p0 - a.t0) * a.sVt;
+        const VT* src = tile_row0 + tk * a.sVt + 16 * sub;
         load8<VT>(src, lo);
         load8<VT>(src + 8, hi);
     }
@@ -101,13 +108,9 @@ __global__ __launch_bounds__(kValThreads) void quantize_values_kernel(ValueQuant
 
     if (tid >= kD) return;
     const int slot = tid;
-    const int64_t p0 = tile * kCodeTile;
     const uint32_t* row = reinterpret_cast<const uint32_t*>(cs + slot * kRowPitch);
     uint32_t* dst = a.codes + ((size_t)bh * code_tiles(a.Ncap) + tile) * (kD * NBITS) + slot * NBITS;
-    const bool full = p0 >= a.t0 && p0 + kCodeTile <= a.t0 + a.T;
-    // tokens of the tile inside the append: [ia, ib)
-    const int ia = (int)(a.t0 > p0 ? a.t0 - p0 : 0);
-    const int ib = (int)(a.t0 + a.T - p0 < kCodeTile ? a.t0 + a.T - p0 : kCodeTile);
+    const bool full = ia == 0 && ib == kCodeTile;
     uint32_t wd[NBITS], msk[NBITS];
     if constexpr (NBITS == 2) {
         uint32_t w[8];
@@ -163,11 +166,11 @@ hipError_t launch_typed(const ValueQuantArgs& a, hipStream_t s) {
     const int64_t first = a.t0 / kCodeTile;
     const int64_t last = (a.t0 + a.T - 1) / kCodeTile;
     const int ntiles = (int)(last - first + 1);
-    const dim3 grid((unsigned)((int64_t)a.B * a.Hkv * ntiles));
+    const dim3 grid((unsigned)ntiles, (unsigned)a.Hkv, (unsigned)a.B);
     switch (a.nbits) {
-        case 2: hipLaunchKernelGGL((quantize_values_kernel<VT, 2>), grid, dim3(kValThreads), 0, s, a, first, ntiles); break;
-        case 3: hipLaunchKernelGGL((quantize_values_kernel<VT, 3>), grid, dim3(kValThreads), 0, s, a, first, ntiles); break;
-        default: hipLaunchKernelGGL((quantize_values_kernel<VT, 4>), grid, dim3(kValThreads), 0, s, a, first, ntiles); break;
+        case 2: hipLaunchKernelGGL((quantize_values_kernel<VT, 2>), grid, dim3(kValThreads), 0, s, a, first); break;
+        case 3: hipLaunchKernelGGL((quantize_values_kernel<VT, 3>), grid, dim3(kValThreads), 0, s, a, first); break;
+        default: hipLaunchKernelGGL((quantize_values_kernel<VT, 4>), grid, dim3(kValThreads), 0, s, a, first); break;
     }
     return hipGetLastError();
 }
