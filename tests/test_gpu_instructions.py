@@ -1,0 +1,186 @@
+"""The gfx950 instruction forms the kernels rely on, checked on the GPU against exact host models.
+
+The decode kernels feed the query to v_mfma_scale_f32_16x16x128_f8f6f4 as fp6 e2m3 pieces with a
+scale byte per lane (selected by op_sel), build those pieces with the packed fp6 conversions, and stage
+block data through buffer loads with an LDS destination. These tests run each form in a small kernel
+(tests/probes/qjl_probes.hip) and compare every output with a model of the operand layout and the
+number formats written here; a stream-read kernel measures the HBM read rate the decode is compared
+with.
+"""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "probes", "libqjl_probes.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    assert os.path.exists(LIB_PATH), "tests/probes/libqjl_probes.so is not built (run __graft_entry__.build())"
+    lib = ctypes.CDLL(LIB_PATH)
+    for name in ("probe_mfma_f6f4", "probe_cvt_fp6", "probe_lds_dma", "probe_stream_read"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def e2m3(c: int) -> float:
+    """fp6 e2m3: sign bit 5, exponent bits 4..3 (bias 1), mantissa bits 2..0; exponent 0 = subnormal."""
+    s, e, m = (c >> 5) & 1, (c >> 3) & 3, c & 7
+    v = (1.0 + m / 8.0) * 2.0 ** (e - 1) if e else m / 8.0
+    return -v if s else v
+
+
+def e2m1(c: int) -> float:
+    """fp4 e2m1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0."""
+    s, e, m = (c >> 3) & 1, (c >> 1) & 3, c & 1
+    v = (1.0 + m / 2.0) * 2.0 ** (e - 1) if e else m / 2.0
+    return -v if s else v
+
+
+E2M3 = np.array([e2m3(c) for c in range(64)])
+
+
+def pack_bits(values, width: int, words: int) -> np.ndarray:
+    """values[i] at bits width*i of a little-endian run of 32-bit words."""
+    out = np.zeros(words, dtype=np.uint64)
+    for i, v in enumerate(values):
+        bit = width * i
+        out[bit // 32] |= (int(v) << (bit % 32)) & 0xFFFFFFFF
+        if bit % 32 + width > 32:
+            out[bit // 32 + 1] |= int(v) >> (32 - bit % 32)
+    return out.astype(np.uint32)
+
+
+def unpack_bits(words, width: int, count: int) -> list:
+    w = 0
+    for i, x in enumerate(words):
+        w |= int(x) << (32 * i)
+    return [(w >> (width * i)) & ((1 << width) - 1) for i in range(count)]
+
+
+@pytest.mark.parametrize("opsel", [0, 1, 2, 3])
+def test_fp6_times_fp4_operands_and_lane_scales(lib, opsel):
+    """A (16 x 128, fp6) row r, K slice g is supplied by lane 16 g + r as 32 values packed from bit 0,
+    scaled by byte opsel of that lane's scale word; B (128 x 16, fp4) column c, K slice g by lane 16 g + c;
+    lane l receives D rows 4 (l / 16) .. + 3 of column l % 16."""
+    rng = np.random.default_rng(40 + opsel)
+    A = rng.integers(0, 64, (16, 128))
+    Bm = rng.integers(0, 16, (128, 16))
+    exps = rng.integers(0, 3, (64, 4))            # scale exponents 0..2: every partial sum exact in fp32
+    a = np.zeros((64, 8), np.uint32)
+    b = np.zeros((64, 8), np.uint32)
+    sc = np.zeros(64, np.uint32)
+    for l in range(64):
+        g, r = l // 16, l % 16
+        a[l, :6] = pack_bits(A[r, 32 * g: 32 * g + 32], 6, 6)
+        b[l, :4] = pack_bits(Bm[32 * g: 32 * g + 32, r], 4, 4)
+        sc[l] = sum(int(127 + exps[l, q]) << (8 * q) for q in range(4))
+    Av = np.vectorize(e2m3)(A)
+    Bv = np.vectorize(e2m1)(Bm)
+    scale = np.zeros((16, 128))
+    for k in range(128):
+        for r in range(16):
+            scale[r, k] = 2.0 ** exps[16 * (k // 32) + r, opsel]
+    D = (Av * scale) @ Bv
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int32)).cuda()  # noqa: E731
+    d = torch.empty(256, dtype=torch.float32, device="cuda")
+    assert lib.probe_mfma_f6f4(_p(dev(a)), _p(dev(b)), _p(dev(sc)), opsel, _p(d), _stream()) == 0
+    torch.cuda.synchronize()
+    got = d.cpu().numpy().reshape(64, 4)
+    want = np.array([[D[4 * (l // 16) + i, l % 16] for i in range(4)] for l in range(64)])
+    np.testing.assert_array_equal(got, want.astype(np.float32))
+
+
+def _e2m3_nearest_even(v: float) -> int:
+    """The e2m3 code nearest to v, ties to the even code, magnitudes beyond 7.5 saturated."""
+    if abs(v) >= 7.5:
+        return 31 | (32 if v < 0 else 0)
+    best, err = 0, np.inf
+    for c in range(32):
+        e = abs(E2M3[c] - abs(v))
+        if e < err or (e == err and c % 2 == 0):
+            best, err = c, e
+    return best | (32 if (v < 0 and best) else 0)
+
+
+def test_packed_fp6_conversions(lib):
+    """v_cvt_scalef32_2xpk16_fp6_f32 rounds x / scale to the nearest e2m3 value (ties to even, saturating)
+    and places element i of its first source at position 2 i, of the second at 2 i + 1;
+    v_cvt_scalef32_pk32_f32_fp6 returns position j's value times scale."""
+    rng = np.random.default_rng(7)
+    x = np.zeros((64, 32), np.float32)
+    scale = np.zeros(64, np.float32)
+    for l in range(64):
+        scale[l] = np.float32(2.0 ** int(rng.integers(-20, 21)))
+        kind = rng.integers(0, 4, 32)
+        u = np.where(kind == 0, rng.uniform(0, 7.5, 32),
+                     np.where(kind == 1, rng.integers(1, 121, 32) / 16.0,          # many exact ties
+                              np.where(kind == 2, rng.uniform(0.01, 1.0, 32), rng.uniform(7.5, 9.5, 32))))
+        x[l] = (u * np.where(rng.random(32) < 0.5, -1, 1) * scale[l]).astype(np.float32)
+    packed = torch.empty(64 * 6, dtype=torch.int32, device="cuda")
+    back = torch.empty(64 * 32, dtype=torch.float32, device="cuda")
+    assert lib.probe_cvt_fp6(_p(torch.from_numpy(x.ravel()).cuda()), _p(torch.from_numpy(scale).cuda()), _p(packed),
+                             _p(back), _stream()) == 0
+    torch.cuda.synchronize()
+    pk = packed.cpu().numpy().view(np.uint32).reshape(64, 6)
+    bk = back.cpu().numpy().reshape(64, 32)
+    for l in range(64):
+        codes = unpack_bits(pk[l], 6, 32)
+        src = [x[l, j // 2] if j % 2 == 0 else x[l, 16 + j // 2] for j in range(32)]
+        want = [_e2m3_nearest_even(float(v) / float(scale[l])) for v in src]
+        zero = lambda c: 0 if c == 32 else c  # noqa: E731  (either sign of zero)
+        assert [zero(c) for c in codes] == [zero(c) for c in want], f"lane {l}: {codes} != {want}"
+        np.testing.assert_array_equal(bk[l], np.array([E2M3[c] * scale[l] for c in codes], np.float32))
+
+
+@pytest.mark.parametrize("size", [4, 16])
+def test_lds_destination_loads(lib, size):
+    """A buffer load with an LDS destination writes lane l's `size` bytes at LDS offset size * l
+    (after M0), whatever global offset the lane reads."""
+    rng = np.random.default_rng(size)
+    src = rng.integers(0, 2**32, 256, dtype=np.uint64).astype(np.uint32)
+    off = (rng.permutation(1024 // size)[:64] * size).astype(np.int32)
+    out = torch.empty(64 * size // 4, dtype=torch.int32, device="cuda")
+    assert lib.probe_lds_dma(_p(torch.from_numpy(src.view(np.int32)).cuda()), _p(torch.from_numpy(off).cuda()), size,
+                             _p(out), _stream()) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint32)
+    want = np.concatenate([src[o // 4: o // 4 + size // 4] for o in off])
+    np.testing.assert_array_equal(got, want)
+
+
+def test_stream_read_rate(lib):
+    """The HBM read rate of a plain 16-byte streaming read (the practical ceiling for a memory-bound
+    kernel on this GPU), printed; asserted only to be a sane fraction of the 8 TB/s peak."""
+    n16 = (2 << 30) // 16
+    buf = torch.ones(n16 * 4, dtype=torch.int32, device="cuda")
+    blocks = 8192
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        assert lib.probe_stream_read(_p(buf), n16, _p(sink), blocks, _stream()) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        lib.probe_stream_read(_p(buf), n16, _p(sink), blocks, _stream())
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = n16 * 16 * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    print(f"\n[stream read] 2 GiB, {blocks} workgroups x 256: {gbs:.0f} GB/s ({gbs / 8000 * 100:.1f}% of 8 TB/s)")
+    assert gbs > 3000
