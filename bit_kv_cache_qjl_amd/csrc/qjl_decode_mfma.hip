@@ -45,6 +45,9 @@ constexpr int kMWaves = kMThreads / 64;
 constexpr int kMBlock = 128;                 // tokens per wave step
 constexpr int kWPitch = 144;                 // bytes per row of a wave's weight tile (16-byte aligned;
                                              // rows of different heads land on different LDS banks)
+// cache policy of the loads that stream the cache (sign words, norms, meta, codes): non-temporal,
+// each byte is read once per launch (measured 4-5% faster on the Llama-2 and Llama-3 decodes)
+constexpr int kStream = 2;
 
 // 4 fp8 e4m3 bytes: a, b in the low half-word and c, d in the high one, rounded to nearest even
 __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
@@ -453,25 +456,25 @@ __device__ __forceinline__ void load_mblock(MBlock<WIN4, WOUT4, NB>& bl, __amdgp
         // token of sub-step s = token of sub-step 0 + 64 (s / 4) + 2 (s % 4)
         const int voff = (s < 4 ? vb0 : vb1) + 2 * (s & 3) * WB * 4;
         if constexpr (Q == 1) {
-            bl.w[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rb, voff, 0, 0);
+            bl.w[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rb, voff, 0, kStream);
         } else if constexpr (Q == 2) {
-            const auto x = __builtin_amdgcn_raw_buffer_load_b64(rb, voff, 0, 0);
+            const auto x = __builtin_amdgcn_raw_buffer_load_b64(rb, voff, 0, kStream);
             bl.w[s][0] = x[0]; bl.w[s][1 % Q] = x[1];
         } else {
-            const auto x = __builtin_amdgcn_raw_buffer_load_b128(rb, voff, 0, 0);
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(rb, voff, 0, kStream);
             bl.w[s][0] = x[0]; bl.w[s][1 % Q] = x[1]; bl.w[s][2 % Q] = x[2]; bl.w[s][3 % Q] = x[3];
         }
     }
     const int vn = o.nm + s0 * 4;
-    const auto n2 = __builtin_amdgcn_raw_buffer_load_b64(rn, vn, 0, 0);
-    const auto m2 = __builtin_amdgcn_raw_buffer_load_b64(rm, vn, 0, 0);
+    const auto n2 = __builtin_amdgcn_raw_buffer_load_b64(rn, vn, 0, kStream);
+    const auto m2 = __builtin_amdgcn_raw_buffer_load_b64(rm, vn, 0, kStream);
     bl.nm[0] = n2[0]; bl.nm[1] = m2[0]; bl.nm[2] = n2[1]; bl.nm[3] = m2[1];
     const int vc = o.codes + s0 * (kD * NB * 4 / kCodeTile);
     // the 8 channels' NB words each are 8 NB consecutive words: word 4 q + e is word (4 q + e) % NB of
     // channel group (4 q + e) / NB
 #pragma unroll
     for (int q = 0; q < 2 * NB; ++q) {
-        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rc, vc + 16 * q, 0, 0);
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rc, vc + 16 * q, 0, kStream);
 #pragma unroll
         for (int e = 0; e < 4; ++e) bl.cx[(4 * q + e) / NB][(4 * q + e) % NB] = x[e];
     }
@@ -825,10 +828,10 @@ constexpr int kM8Threads = 64 * kM8Waves;
 // plain functions: with the size inside a kernel template the compiler's host pass drops the
 // kernel's launch stub
 __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t* lds, int voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, kStream);
 }
 __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, uint32_t* lds, int voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, 0, 0, kStream);
 }
 
 template <int WIN4, int WOUT4, bool DBG>
