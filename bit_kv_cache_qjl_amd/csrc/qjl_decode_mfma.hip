@@ -27,7 +27,11 @@
 // high one through a B scale of 4.  The weights of a 128-token block are scaled
 // by 2^(8 - E), 2^E > the block's largest step, split into three e4m3 pieces, and transposed to the
 // A-operand order through LDS.  Each wave is an independent online-softmax stream over 128-token
-// blocks; the four waves of a workgroup merge at the end of the chunk.
+// blocks; the waves of a workgroup merge at the end of the chunk.  Two kernels: decode_mfma_kernel
+// (four waves, each streaming its blocks through registers; one or two row groups of four heads) and,
+// for more than four heads per KV head with 2-bit values, decode_mfma8_kernel (eight waves, two per
+// SIMD, block data staged through LDS by LDS-destination loads, score rows holding piece pairs of all
+// eight heads).
 #include <math.h>
 
 #include "qjl_decode_common.h"
