@@ -233,6 +233,21 @@ def _timer_run(qjl, torch, names, run_one, steps: int) -> dict:
     return res
 
 
+def _region_ms(torch, run_one, steps: int) -> float:
+    """Mean duration of one call over `steps` back-to-back calls: HIP events on the launch stream (torch's
+    current stream, which the binding launches on) bracket the whole run, so the figure is the rate a
+    stream of such calls sustains (the key quantizer's launches slow down over a run as the clock drops
+    under matrix-core load)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        run_one()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def bench_quantize(qjl, torch, steps: int) -> dict:
     """Prefill quantize stream: 65536 tokens x 8 KV heads, m = m_out = 512 (keys), 2-bit values.  Each
     call takes the next of several input and output copies, so that no call finds its inputs (134 MB
@@ -262,8 +277,7 @@ def bench_quantize(qjl, torch, steps: int) -> dict:
         keys_once()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    n, ms = _timer_run(qjl, torch, ["quantize_keys"], keys_once, steps)["quantize_keys"]
-    kern_s = ms / 1e3 / max(n, 1)
+    kern_s = _region_ms(torch, keys_once, steps) / 1e3
     # outlier-channel selection over the same keys (one read of K, two launches)
     ws = torch.empty(qjl.lib.qjl_select_outliers_workspace_size(w.B, w.N, w.Hkv, w.d), dtype=torch.uint8, device="cuda")
     sel = torch.empty((w.Hkv, w.n_out), dtype=torch.int32, device="cuda")
@@ -275,8 +289,7 @@ def bench_quantize(qjl, torch, steps: int) -> dict:
     for _ in range(2 * copies):
         select_once()
     torch.cuda.synchronize()
-    ns, mss = _timer_run(qjl, torch, ["select_outliers"], select_once, steps)["select_outliers"]
-    sel_s = mss / 1e3 / max(ns, 1)
+    sel_s = _region_ms(torch, select_once, steps) / 1e3
     sel_bytes = float(in_bytes)
     del Ks, K0
     # token-wise value codes of the same prefill: V [1, 65536, 8, 128] bf16 -> 2-bit code tiles + (min, step)
@@ -290,8 +303,7 @@ def bench_quantize(qjl, torch, steps: int) -> dict:
     for _ in range(2 * copies):
         values_once()
     torch.cuda.synchronize()
-    nv, msv = _timer_run(qjl, torch, ["quantize_values"], values_once, steps)["quantize_values"]
-    val_s = msv / 1e3 / max(nv, 1)
+    val_s = _region_ms(torch, values_once, steps) / 1e3
     del Vs, V0
     # per token and KV head: d bf16 values read, d b / 8 code bytes and the fp16 (min, step) pair written
     val_bytes = float(w.B * w.N * w.Hkv * (2 * w.d + w.d * w.nbits // 8 + 4))

@@ -370,44 +370,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 }
 
 // ------------------------------------------------------------------------------------ combine
-// One workgroup (256 threads) per (sequence, query head): log-sum-exp merge of the chunk partials
-// (max, sum, unnormalized output).  The split maxima and their scale factors go through LDS first,
-// so the output pass issues independent loads (two threads per channel, alternate splits).  A
-// separate launch: merging inside the decode kernel would need a device-scope release/acquire per
-// workgroup, which on MI355X writes back and invalidates the XCD's whole L2.
-__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
-    __shared__ float sc[kMaxSplits];
-    __shared__ float red[2][4];
-    __shared__ float ohalf[kD];
-    const int tid = threadIdx.x;
+// One workgroup per (sequence, query head), one thread per channel: the log-sum-exp merge of the
+// head's nsplit chunk partials (max, sum, unnormalized output) in one pass with a running maximum,
+// so a thread's loads do not wait on each other or on a barrier and the merge costs one round trip
+// to memory.  A separate launch: merging inside the decode kernel would need a device-scope
+// release/acquire per workgroup, which on MI355X writes back and invalidates the XCD's whole L2.
+__global__ __launch_bounds__(kD) void combine_kernel(DecodeArgs a) {
+    const int c = threadIdx.x;
     const int bhq = blockIdx.x;
     const int ns = a.nsplit;
     const float* src = a.part + (size_t)bhq * ns * (kD + 2);
-    float mx = -INFINITY;
-    for (int i = tid; i < ns; i += 256) mx = fmaxf(mx, src[(size_t)i * (kD + 2)]);
-    mx = wave64_max(mx);
-    if ((tid & 63) == 0) red[0][tid >> 6] = mx;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-    float l = 0.f;
-    for (int i = tid; i < ns; i += 256) {
-        const float mi = src[(size_t)i * (kD + 2)];
-        const float f = (mi == -INFINITY) ? 0.f : exp2f(mi - M);   // M is finite when any mi is
-        sc[i] = f;
-        l = fmaf(f, src[(size_t)i * (kD + 2) + 1], l);
-    }
-    l = wave64_sum(l);
-    if ((tid & 63) == 0) red[1][tid >> 6] = l;
-    __syncthreads();
-    const float L = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
-    const int c = tid & (kD - 1);
-    const int half = tid >> 7;
-    float o = 0.f;
+    float M = -INFINITY, L = 0.f, O = 0.f;
 #pragma unroll 4
-    for (int i = half; i < ns; i += 2) o = fmaf(sc[i], src[(size_t)i * (kD + 2) + 2 + c], o);
-    if (half) ohalf[c] = o;
-    __syncthreads();
-    if (!half) a.out[(size_t)bhq * kD + c] = L > 0.f ? (o + ohalf[c]) / L : 0.f;
+    for (int i = 0; i < ns; ++i) {
+        const float mi = src[(size_t)i * (kD + 2)];
+        const float li = src[(size_t)i * (kD + 2) + 1];
+        const float oi = src[(size_t)i * (kD + 2) + 2 + c];
+        if (mi == -INFINITY) continue;           // a chunk with no valid token
+        const float Mn = fmaxf(M, mi);
+        const float keep = exp2f(M - Mn);        // 0 while M is still -inf
+        const float f = exp2f(mi - Mn);
+        L = fmaf(f, li, L * keep);
+        O = fmaf(f, oi, O * keep);
+        M = Mn;
+    }
+    a.out[(size_t)bhq * kD + c] = L > 0.f ? O / L : 0.f;
 }
 
 }  // namespace
@@ -434,7 +421,7 @@ hipError_t launch_decode_v(const DecodeArgs& a, int vmode, hipStream_t s) {
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
     timer_begin(TK_COMBINE, s);
-    hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.Hq), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.Hq), dim3(kD), 0, s, a);
     timer_end(TK_COMBINE, s);
     return hipGetLastError();
 }

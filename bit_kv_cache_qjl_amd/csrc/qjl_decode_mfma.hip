@@ -838,6 +838,48 @@ __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, uint32_t* ld
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, 0, 0, kStream);
 }
 
+typedef uint32_t v2u_t __attribute__((ext_vector_type(2)));
+
+// The LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)reinterpret_cast<uintptr_t>(p); }
+
+// The (norm, meta) words of this lane's token in each of the eight sub-steps of a staged block: token
+// mfma_token(s, t) sits f(s) = 64 (s / 4) + 2 (s % 4) words after that of sub-step 0, the meta words 128
+// words after the norms.  The reads are waited for in the same statement.  They go through asm because
+// the compiler cannot tell this buffer from those that the block's code loads are still writing, and
+// would otherwise wait for every outstanding load (those of the next code words included) first; the
+// caller has waited for the loads into this buffer.
+__device__ __forceinline__ void read_nm8(uint32_t addr, v2u_t (&nm)[8]) {
+    asm volatile(
+        "ds_read2_b32 %0, %8 offset0:0 offset1:128\n\t"
+        "ds_read2_b32 %1, %8 offset0:2 offset1:130\n\t"
+        "ds_read2_b32 %2, %8 offset0:4 offset1:132\n\t"
+        "ds_read2_b32 %3, %8 offset0:6 offset1:134\n\t"
+        "ds_read2_b32 %4, %8 offset0:64 offset1:192\n\t"
+        "ds_read2_b32 %5, %8 offset0:66 offset1:194\n\t"
+        "ds_read2_b32 %6, %8 offset0:68 offset1:196\n\t"
+        "ds_read2_b32 %7, %8 offset0:70 offset1:198\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(nm[0]), "=&v"(nm[1]), "=&v"(nm[2]), "=&v"(nm[3]), "=&v"(nm[4]), "=&v"(nm[5]), "=&v"(nm[6]), "=&v"(nm[7])
+        : "v"(addr)
+        : "memory");
+}
+
+// The three e4m3 piece words of a weight quadruple into rows r, r + 1, r + 2 of a wave's weight tile.
+// Through asm for the same reason as read_nm8: the tile is not written by any load, but the compiler
+// would wait for every outstanding load into LDS before a store it can see.  The stores are in order
+// with the wave's later LDS reads of the tile.
+static_assert(kWPitch == 144, "row offsets of store_pieces");
+__device__ __forceinline__ void store_pieces(uint32_t addr, const uint32_t (&k)[3]) {
+    asm volatile(
+        "ds_write_b32 %0, %1\n\t"
+        "ds_write_b32 %0, %2 offset:144\n\t"
+        "ds_write_b32 %0, %3 offset:288"
+        :
+        : "v"(addr), "v"(k[0]), "v"(k[1]), "v"(k[2])
+        : "memory");
+}
+
 template <int WIN4, int WOUT4, bool DBG>
 __global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs a, int groups, int hgroups) {
     constexpr int R = 2, NB = 2;
@@ -849,8 +891,7 @@ __global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs 
     __shared__ __attribute__((aligned(16))) uint8_t s_wtile[kM8Waves][2][16 * kWPitch];   // weight pieces
     __shared__ __attribute__((aligned(16))) uint32_t s_sgn[kM8Waves][8][64][W4];         // sign quarter-rows
     __shared__ __attribute__((aligned(16))) uint32_t s_cod[kM8Waves][4][64][4];          // code words
-    __shared__ __attribute__((aligned(16))) uint32_t s_nrm[kM8Waves][2][kMBlock];        // norms (two buffers)
-    __shared__ __attribute__((aligned(16))) uint32_t s_met[kM8Waves][2][kMBlock];        // (min, step) (two buffers)
+    __shared__ __attribute__((aligned(16))) uint32_t s_nm[kM8Waves][2][2][kMBlock];      // [buffer][norm, meta][token]
     __shared__ float s_red_m[kM8Waves][8], s_red_l[kM8Waves][8], s_red_mn[kM8Waves][8];
 
     const int tid = threadIdx.x;
@@ -921,35 +962,46 @@ __global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs 
     __builtin_amdgcn_wave_barrier();
     const int woff = 32 * (2 * ((t >> 3) & 1) + ((t >> 2) & 1)) + 8 * (t & 1) + 4 * ((t >> 1) & 1);
 
-    const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(a.bits + (size_t)unit * a.Ncap * WB, (uint32_t)t_end * WB * 4u);
-    const __amdgpu_buffer_rsrc_t rn = buffer_rsrc(reinterpret_cast<const uint32_t*>(a.norms) + (size_t)unit * a.Ncap,
-                                                  (uint32_t)t_end * 4u);
-    const __amdgpu_buffer_rsrc_t rm = buffer_rsrc(reinterpret_cast<const uint32_t*>(a.meta) + (size_t)unit * a.Ncap,
-                                                  (uint32_t)t_end * 4u);
-    const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(a.codes + (size_t)unit * code_tiles(a.Ncap) * (kD * NB),
-                                                  (uint32_t)code_tiles(t_end) * (kD * NB * 4u));
+    const uint32_t* bits_u = a.bits + (size_t)unit * a.Ncap * WB;
+    const uint32_t* norms_u = reinterpret_cast<const uint32_t*>(a.norms) + (size_t)unit * a.Ncap;
+    const uint32_t* meta_u = reinterpret_cast<const uint32_t*>(a.meta) + (size_t)unit * a.Ncap;
+    const uint32_t* codes_u = a.codes + (size_t)unit * code_tiles(a.Ncap) * (kD * NB);
     const int off_bits = (mfma_token(0, t) * WB + hh * W4) * 4;        // sign quarter-row of sub-step 0
-    const int off_codes = hh * (kD * NB * 4) + t * (8 * NB * 4);       // channel streams 8 t .. of code tile hh
+    // code words: lane (t, hh) needs the 64 bytes of channel streams 8 t .. of code tile hh, as four
+    // 16-byte pieces.  Load q brings in all of tile q, 1 KB, so every cache line is whole within one load:
+    // its lane 16 p + u reads piece p of stream group u, which lands at slot 16 p + u of buffer q (for a
+    // given piece the 16 lanes of a lane group then read 16 consecutive slots, without bank conflicts)
+    const int off_codes = (8 * NB * 4) * (lane & 15) + 16 * (lane >> 4);
     const float inv_z = 1.0f / a.z_scale;
 
-    // the loads of a block into this wave's LDS buffers (the block start s0 is wave-uniform)
+    // the loads of a block into this wave's LDS buffers.  The block start s0 is wave-uniform: each
+    // block gets buffer descriptors based at its first token (scalar work), sized to the tokens left
+    // before t_end (none once s0 >= t_end: every load returns zeros), so the lane offsets stay the same
+    // from block to block and no vector instruction computes an address.
     auto load_signs_nm = [&](int s0, int nb) {
+        const uint32_t left = s0 < t_end ? (uint32_t)(t_end - s0) : 0u;
+        const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(bits_u + (size_t)s0 * WB, left * WB * 4u);
+        const __amdgpu_buffer_rsrc_t rn = buffer_rsrc(norms_u + s0, left * 4u);
+        const __amdgpu_buffer_rsrc_t rm = buffer_rsrc(meta_u + s0, left * 4u);
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            const int voff = off_bits + (s0 + 64 * (s >> 2) + 2 * (s & 3)) * WB * 4;
+            const int voff = off_bits + (64 * (s >> 2) + 2 * (s & 3)) * WB * 4;
             if constexpr (W4 == 4) lds_load16(rb, &s_sgn[wave][s][0][0], voff);
             else lds_load4(rb, &s_sgn[wave][s][0][0], voff);
         }
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            lds_load4(rn, &s_nrm[wave][nb][64 * q], (s0 + 64 * q + lane) * 4);
-            lds_load4(rm, &s_met[wave][nb][64 * q], (s0 + 64 * q + lane) * 4);
+            lds_load4(rn, &s_nm[wave][nb][0][64 * q], (64 * q + lane) * 4);
+            lds_load4(rm, &s_nm[wave][nb][1][64 * q], (64 * q + lane) * 4);
         }
     };
     auto load_codes = [&](int s0) {
+        // s0 is a multiple of the block, so the block starts a code tile
+        const int tile0 = s0 / kCodeTile, tiles = code_tiles(t_end);
+        const uint32_t left = tile0 < tiles ? (uint32_t)(tiles - tile0) : 0u;
+        const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(codes_u + (size_t)tile0 * (kD * NB), left * (kD * NB * 4u));
 #pragma unroll
-        for (int q = 0; q < 2 * NB; ++q)
-            lds_load16(rc, &s_cod[wave][q][0][0], off_codes + s0 * (kD * NB * 4 / kCodeTile) + 16 * q);
+        for (int q = 0; q < 2 * NB; ++q) lds_load16(rc, &s_cod[wave][q][0][0], off_codes + q * (kD * NB * 4));
     };
 
     float m_run[R], l_acc[R], mn_acc[R];
@@ -971,16 +1023,18 @@ __global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs 
     load_codes(s_first);
     for (int s0 = s_first; s0 < t_end; s0 += kStep) {
         // this block's sign quarter-rows, norms and meta have landed (only the 4 code loads may be pending)
-        if constexpr (DBG) asm volatile("s_waitcnt vmcnt(0)" ::"s"(s_sgn), "s"(s_cod), "s"(s_nrm), "s"(s_met) : "memory");
-        else asm volatile("s_waitcnt vmcnt(4)" ::"s"(s_sgn), "s"(s_cod), "s"(s_nrm), "s"(s_met) : "memory");
+        if constexpr (DBG) asm volatile("s_waitcnt vmcnt(0)" ::"s"(s_sgn), "s"(s_cod), "s"(s_nm) : "memory");
+        else asm volatile("s_waitcnt vmcnt(4)" ::"s"(s_sgn), "s"(s_cod), "s"(s_nm) : "memory");
         __builtin_amdgcn_wave_barrier();
 
         float z[R][8];
         uint32_t mtw[8];                               // meta of the 8 sub-steps, read before its buffer is reloaded
+        v2u_t nmw[8];
+        read_nm8(lds_addr(&s_nm[wave][nb][0][mfma_token(0, t)]), nmw);
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            mtw[s] = s_met[wave][nb][mfma_token(s, t)];
-            const uint32_t nrm = s_nrm[wave][nb][mfma_token(s, t)];
+            mtw[s] = nmw[s][1];
+            const uint32_t nrm = nmw[s][0];
             const float n_in = (float)__builtin_bit_cast(_Float16, (uint16_t)(nrm & 0xFFFFu));
             const float n_out = (float)__builtin_bit_cast(_Float16, (uint16_t)(nrm >> 16));
             uint32_t w[W4];
@@ -1072,15 +1126,7 @@ __global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs 
                 }
                 uint32_t k[3];
                 fp8_pieces(wgt, k);
-                uint8_t* row = row0 + 16 * q;
-                // three single stores (the empty asm keeps them from merging into paired stores, which the
-                // compiler's wait analysis cannot tell apart from the loads still writing the LDS buffers)
-                *reinterpret_cast<uint32_t*>(row) = k[0];
-                asm volatile("");
-                *reinterpret_cast<uint32_t*>(row + kWPitch) = k[1];
-                asm volatile("");
-                *reinterpret_cast<uint32_t*>(row + 2 * kWPitch) = k[2];
-                asm volatile("");
+                store_pieces(lds_addr(row0 + 16 * q), k);
             }
         }
         // the sign buffer is free once its reads are done: the next block's signs, norms and meta.  Issued
@@ -1101,8 +1147,8 @@ __global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs 
             }
         }
         // this block's code words have landed (the 12 loads issued after the weight stores may be pending)
-        if constexpr (DBG) asm volatile("s_waitcnt vmcnt(0)" ::"s"(s_sgn), "s"(s_cod), "s"(s_nrm), "s"(s_met) : "memory");
-        else asm volatile("s_waitcnt vmcnt(12)" ::"s"(s_sgn), "s"(s_cod), "s"(s_nrm), "s"(s_met) : "memory");
+        if constexpr (DBG) asm volatile("s_waitcnt vmcnt(0)" ::"s"(s_sgn), "s"(s_cod), "s"(s_nm) : "memory");
+        else asm volatile("s_waitcnt vmcnt(12)" ::"s"(s_sgn), "s"(s_cod), "s"(s_nm) : "memory");
         __builtin_amdgcn_wave_barrier();
 
         v8i_t aw[R];
@@ -1116,7 +1162,7 @@ __global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs 
         uint32_t cx[8][NB];
 #pragma unroll
         for (int q = 0; q < 2 * NB; ++q) {
-            const uint4 x = *reinterpret_cast<const uint4*>(&s_cod[wave][q][lane][0]);
+            const uint4 x = *reinterpret_cast<const uint4*>(&s_cod[wave][hh][16 * q + t][0]);
             const uint32_t xe[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) cx[(4 * q + e) / NB][(4 * q + e) % NB] = xe[e];
@@ -1138,7 +1184,7 @@ __global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs 
         nb ^= 1;
     }
     // no load may still write this wave's buffers when the merge below reuses the LDS
-    asm volatile("s_waitcnt vmcnt(0)" ::"s"(s_sgn), "s"(s_cod), "s"(s_nrm), "s"(s_met) : "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::"s"(s_sgn), "s"(s_cod), "s"(s_nm) : "memory");
 
     // ---- merge the eight wave streams of each head (the output rows go through the weight tiles)
     float* red_o = reinterpret_cast<float*>(&s_wtile[0][0][0]);        // [wave][head][kD]

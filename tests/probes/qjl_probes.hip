@@ -73,14 +73,100 @@ __global__ void lds_dma_kernel(const uint32_t* src, const int* off, int size, ui
     for (int i = l; i < 64 * size / 4; i += 64) out[i] = img[i];
 }
 
-// A streaming read of n 16-byte words (grid-stride), folded into one word per thread so the loads stay.
-__global__ void stream_read_kernel(const uint4* src, int64_t n, uint32_t* sink) {
+// A streaming read of n 16-byte words (grid-stride), folded into one word per thread so the loads stay;
+// NT: non-temporal loads.
+typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+template <bool NT>
+__global__ void stream_read_kernel(const v4u_t* src, int64_t n, uint32_t* sink) {
     uint32_t acc = 0u;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-        const uint4 v = src[i];
-        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+        const v4u_t v = NT ? __builtin_nontemporal_load(src + i) : src[i];
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
     }
     sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+// The cache-read pattern of the eight-wave decode with no arithmetic: one workgroup of 8 waves per
+// (unit, chunk) of U units of Ncap tokens split into nsplit chunks (workgroup L serves chunk 8 (L / 8) +
+// L % 8, as in the decode's grid), each wave taking 128-token blocks 1024 tokens apart; per token 64 B
+// of sign words, 4 B of norms, 4 B of meta and 32 B of codes, each stream stored unit after unit.  A
+// block's loads are all issued, then awaited, non-temporal.  LDS: the decode's LDS-destination loads
+// with its lane offsets (signs: 16-byte quarter-rows of token pairs; codes: 16-byte pieces of four
+// 32-token tiles); otherwise the same bytes go to registers as 16-byte (signs, codes) and 4-byte
+// (norms, meta) loads.  Every offset stays below the chunk's end, so the range checks never clip.
+struct DecodeStreams {
+    const uint8_t* sg;
+    const uint32_t* nr;
+    const uint32_t* mt;
+    const uint8_t* cd;
+    int64_t Ncap;
+    int U, nsplit;
+};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void nt_dma16(__amdgpu_buffer_rsrc_t r, uint32_t* lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, 2);
+}
+__device__ __forceinline__ void nt_dma4(__amdgpu_buffer_rsrc_t r, uint32_t* lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, 0, 0, 2);
+}
+template <bool LDS>
+__global__ __launch_bounds__(512, 1) void decode_stream_kernel(DecodeStreams d, uint32_t* sink) {
+    __shared__ __attribute__((aligned(16))) uint32_t s_sgn[8][8][64][4];
+    __shared__ __attribute__((aligned(16))) uint32_t s_cod[8][4][64][4];
+    __shared__ __attribute__((aligned(16))) uint32_t s_nm[8][2][128];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int t = lane & 15, hh = lane >> 4;
+    const int64_t us = (int64_t)(blockIdx.x >> 3) * 8 + (blockIdx.x & 7);
+    if (us >= (int64_t)d.U * d.nsplit) return;
+    const int split = (int)(us % d.nsplit), unit = (int)(us / d.nsplit);
+    const int chunk = (int)(d.Ncap / d.nsplit);
+    const int t_begin = split * chunk, t_end = t_begin + chunk;
+    const auto rs = rsrc(d.sg + (size_t)unit * d.Ncap * 64, (uint32_t)t_end * 64u);
+    const auto rn = rsrc(d.nr + (size_t)unit * d.Ncap, (uint32_t)t_end * 4u);
+    const auto rm = rsrc(d.mt + (size_t)unit * d.Ncap, (uint32_t)t_end * 4u);
+    const auto rc = rsrc(d.cd + (size_t)unit * d.Ncap * 32, (uint32_t)t_end * 32u);
+    // the decode's token of lane group (t, hh) in sub-step 0, its quarter-row and its code stream
+    const int tok0 = 32 * ((t >> 3) & 1) + 16 * ((t >> 2) & 1) + 8 * ((t >> 1) & 1) + (t & 1);
+    const int off_sg = (tok0 * 16 + hh * 4) * 4;
+    const int off_cd = hh * 1024 + t * 64;
+    uint32_t acc = 0u;
+    for (int s0 = t_begin + 128 * wave; s0 + 128 <= t_end; s0 += 1024) {
+        if (LDS) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) nt_dma16(rs, &s_sgn[wave][s][0][0], off_sg + (s0 + 64 * (s >> 2) + 2 * (s & 3)) * 64);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                nt_dma4(rn, &s_nm[wave][0][64 * q], (s0 + 64 * q + lane) * 4);
+                nt_dma4(rm, &s_nm[wave][1][64 * q], (s0 + 64 * q + lane) * 4);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) nt_dma16(rc, &s_cod[wave][q][0][0], off_cd + s0 * 32 + 16 * q);
+            // the loads write LDS behind the compiler's back: wait for them, and keep the buffers escaping
+            asm volatile("s_waitcnt vmcnt(0)" ::"s"(s_sgn), "s"(s_cod), "s"(s_nm) : "memory");
+            acc ^= s_sgn[wave][lane & 7][lane][0] ^ s_cod[wave][lane & 3][lane][1] ^ s_nm[wave][lane & 1][lane];
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        } else {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, s0 * 64 + 1024 * s + 16 * lane, 0, 2);
+                acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                acc ^= __builtin_amdgcn_raw_buffer_load_b32(rn, (s0 + 64 * q + lane) * 4, 0, 2);
+                acc ^= __builtin_amdgcn_raw_buffer_load_b32(rm, (s0 + 64 * q + lane) * 4, 0, 2);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, s0 * 32 + 1024 * q + 16 * lane, 0, 2);
+                acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+            }
+        }
+    }
+    sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
 }  // namespace
@@ -109,9 +195,25 @@ int probe_lds_dma(const uint32_t* src, const int* off, int size, uint32_t* out, 
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 
-int probe_stream_read(const void* src, int64_t n16, uint32_t* sink, int blocks, hipStream_t s) {
+// sink: blocks * 256 words
+int probe_stream_read(const void* src, int64_t n16, uint32_t* sink, int blocks, int nontemporal, hipStream_t s) {
     if (blocks <= 0 || n16 <= 0) return -1;
-    hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const uint4*>(src), n16, sink);
+    const v4u_t* p = static_cast<const v4u_t*>(src);
+    if (nontemporal) hipLaunchKernelGGL(stream_read_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, p, n16, sink);
+    else hipLaunchKernelGGL(stream_read_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, p, n16, sink);
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// signs: U * Ncap * 64 B, norms and meta: U * Ncap * 4 B, codes: U * Ncap * 32 B; Ncap a multiple of
+// 1024 * nsplit; sink: 512 words per workgroup (8 * ceil(U * nsplit / 8) workgroups)
+int probe_decode_stream(const void* signs, const void* norms, const void* meta, const void* codes, int64_t Ncap, int U,
+                        int nsplit, int lds, uint32_t* sink, hipStream_t s) {
+    if (U <= 0 || nsplit <= 0 || Ncap <= 0 || Ncap % (1024 * (int64_t)nsplit) != 0 || Ncap * 64 > 0xFFFFFFFFll) return -1;
+    const DecodeStreams d{static_cast<const uint8_t*>(signs), static_cast<const uint32_t*>(norms),
+                          static_cast<const uint32_t*>(meta), static_cast<const uint8_t*>(codes), Ncap, U, nsplit};
+    const unsigned blocks = (unsigned)((U * nsplit + 7) / 8 * 8);
+    if (lds) hipLaunchKernelGGL(decode_stream_kernel<true>, dim3(blocks), dim3(512), 0, s, d, sink);
+    else hipLaunchKernelGGL(decode_stream_kernel<false>, dim3(blocks), dim3(512), 0, s, d, sink);
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 

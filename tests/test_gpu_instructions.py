@@ -4,8 +4,8 @@ The decode kernels feed the query to v_mfma_scale_f32_16x16x128_f8f6f4 as fp6 e2
 scale byte per lane (selected by op_sel), build those pieces with the packed fp6 conversions, and stage
 block data through buffer loads with an LDS destination. These tests run each form in a small kernel
 (tests/probes/qjl_probes.hip) and compare every output with a model of the operand layout and the
-number formats written here; a stream-read kernel measures the HBM read rate the decode is compared
-with.
+number formats written here; read-only kernels measure the HBM read rates the decode is compared with
+(a plain streaming read, and the decode's own access pattern through its load path).
 """
 import ctypes
 import os
@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "probes", "l
 def lib():
     assert os.path.exists(LIB_PATH), "tests/probes/libqjl_probes.so is not built (run __graft_entry__.build())"
     lib = ctypes.CDLL(LIB_PATH)
-    for name in ("probe_mfma_f6f4", "probe_cvt_fp6", "probe_lds_dma", "probe_stream_read"):
+    for name in ("probe_mfma_f6f4", "probe_cvt_fp6", "probe_lds_dma", "probe_stream_read", "probe_decode_stream"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -165,22 +165,51 @@ def test_lds_destination_loads(lib, size):
     np.testing.assert_array_equal(got, want)
 
 
-def test_stream_read_rate(lib):
-    """The HBM read rate of a plain 16-byte streaming read (the practical ceiling for a memory-bound
-    kernel on this GPU), printed; asserted only to be a sane fraction of the 8 TB/s peak."""
-    n16 = (2 << 30) // 16
-    buf = torch.ones(n16 * 4, dtype=torch.int32, device="cuda")
-    blocks = 8192
-    sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+def _rate(launch, nbytes: int, reps: int = 10) -> float:
     for _ in range(2):
-        assert lib.probe_stream_read(_p(buf), n16, _p(sink), blocks, _stream()) == 0
+        assert launch() == 0
+    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 10
     e0.record()
     for _ in range(reps):
-        lib.probe_stream_read(_p(buf), n16, _p(sink), blocks, _stream())
+        launch()
     e1.record()
     torch.cuda.synchronize()
-    gbs = n16 * 16 * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
-    print(f"\n[stream read] 2 GiB, {blocks} workgroups x 256: {gbs:.0f} GB/s ({gbs / 8000 * 100:.1f}% of 8 TB/s)")
-    assert gbs > 3000
+    return nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+
+
+@pytest.mark.parametrize("blocks", [2048, 8192])
+def test_stream_read_rate(lib, blocks):
+    """The HBM read rate of a plain 16-byte streaming read, with ordinary and with non-temporal loads,
+    printed (the practical ceiling for a memory-bound kernel on this GPU); asserted only to be a sane
+    fraction of the 8 TB/s peak."""
+    n16 = (2 << 30) // 16
+    buf = torch.ones(n16 * 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    for nt in (0, 1):
+        gbs = _rate(lambda: lib.probe_stream_read(_p(buf), ctypes.c_int64(n16), _p(sink), blocks, nt, _stream()), n16 * 16)
+        kind = "non-temporal" if nt else "plain"
+        print(f"\n[stream read] 2 GiB, {blocks} workgroups x 256, {kind}: {gbs:.0f} GB/s ({gbs / 8000 * 100:.1f}% of 8 TB/s)")
+        assert gbs > 3000
+
+
+def test_decode_stream_rates(lib):
+    """The cache-read pattern of the eight-wave decode on its Llama-3.1-70B shape (128 (sequence, KV head)
+    units of 131072 tokens, two chunks each, 104 B per token: 1.745 GB), with no arithmetic: once through
+    LDS-destination loads with the decode's lane offsets, once into registers.  Printed; the first is the
+    ceiling of the decode's own load path."""
+    U, Ncap, ns = 128, 131072, 2
+    sg = torch.ones(U * Ncap * 16, dtype=torch.int32, device="cuda")
+    nr = torch.ones(U * Ncap, dtype=torch.int32, device="cuda")
+    mt = torch.ones(U * Ncap, dtype=torch.int32, device="cuda")
+    cd = torch.ones(U * Ncap * 8, dtype=torch.int32, device="cuda")
+    blocks = (U * ns + 7) // 8 * 8
+    sink = torch.empty(blocks * 512, dtype=torch.int32, device="cuda")
+    nbytes = U * Ncap * 104
+    for lds in (1, 0):
+        gbs = _rate(lambda: lib.probe_decode_stream(_p(sg), _p(nr), _p(mt), _p(cd), ctypes.c_int64(Ncap), U, ns, lds, _p(sink),
+                                                    _stream()), nbytes)
+        kind = "LDS-destination loads" if lds else "register loads"
+        print(f"\n[decode stream] 1.745 GB, {blocks} workgroups x 512, {kind}: {gbs:.0f} GB/s "
+              f"({gbs / 8000 * 100:.1f}% of 8 TB/s, {nbytes / gbs / 1e3:.1f} us)")
+        assert gbs > 3000
