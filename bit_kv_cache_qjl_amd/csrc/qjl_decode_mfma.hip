@@ -444,7 +444,7 @@ struct MBlock {
 struct MOffsets {
     int bits;    // sign quarter-row of sub-step 0
     int nm;      // (norm, meta) of tokens 2 lane, 2 lane + 1
-    int codes;   // channel streams 8 t .. 8 t + 7 of code tile hh
+    int codes;   // channel streams 8 t .. 8 t + 7 of code tile hh (2-bit codes: piece hh of stream group t)
 };
 
 template <int WIN4, int WOUT4, int NB>
@@ -475,12 +475,42 @@ __device__ __forceinline__ void load_mblock(MBlock<WIN4, WOUT4, NB>& bl, __amdgp
     bl.nm[0] = n2[0]; bl.nm[1] = m2[0]; bl.nm[2] = n2[1]; bl.nm[3] = m2[1];
     const int vc = o.codes + s0 * (kD * NB * 4 / kCodeTile);
     // the 8 channels' NB words each are 8 NB consecutive words: word 4 q + e is word (4 q + e) % NB of
-    // channel group (4 q + e) / NB
+    // channel group (4 q + e) / NB.  2-bit codes: load q is all of code tile q (lane 16 p + u: piece p of
+    // stream group u), and transpose_code_pieces later hands each lane its own pieces
 #pragma unroll
     for (int q = 0; q < 2 * NB; ++q) {
-        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rc, vc + 16 * q, 0, kStream);
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rc, vc + (NB == 2 ? q * (kD * NB * 4) : 16 * q), 0, kStream);
 #pragma unroll
         for (int e = 0; e < 4; ++e) bl.cx[(4 * q + e) / NB][(4 * q + e) % NB] = x[e];
+    }
+}
+
+// 2-bit codes loaded a whole tile per load: lane row p (lanes 16 p ..) holds in load q's four words
+// piece p of its stream group in tile q, which lane row q needs as its piece p.  Two exchange stages
+// transpose the 4 x 4 (row, load) blocks: v_permlane32_swap swaps the upper two rows of one register
+// with the lower two rows of another (row and load index exchange their high bits), v_permlane16_swap
+// the odd rows of one with the even rows of another (the low bits).  Afterwards register group p of
+// lane row hh is piece p of its stream group in tile hh, as the strided loads would have left it.
+__device__ __forceinline__ void transpose_code_pieces(uint32_t (&cx)[8][2]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        uint32_t r[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r[q] = cx[(4 * q + e) / 2][(4 * q + e) % 2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const auto x = __builtin_amdgcn_permlane32_swap(r[q], r[q + 2], false, false);
+            r[q] = x[0];
+            r[q + 2] = x[1];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; q += 2) {
+            const auto x = __builtin_amdgcn_permlane16_swap(r[q], r[q + 1], false, false);
+            r[q] = x[0];
+            r[q + 1] = x[1];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cx[(4 * q + e) / 2][(4 * q + e) % 2] = r[q];
     }
 }
 
@@ -570,7 +600,8 @@ __global__ __launch_bounds__(kMThreads, (R == 1 && NB == 2) ? 2 : 1) void decode
                                                   (uint32_t)t_end * 4u);
     const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(a.codes + (size_t)unit * code_tiles(a.Ncap) * (kD * NB),
                                                   (uint32_t)code_tiles(t_end) * (kD * NB * 4u));
-    const MOffsets offs{(mfma_token(0, t) * WB + hh * W4) * 4, 8 * lane, hh * (kD * NB * 4) + t * (8 * NB * 4)};
+    const MOffsets offs{(mfma_token(0, t) * WB + hh * W4) * 4, 8 * lane,
+                        NB == 2 ? (8 * NB * 4) * t + 16 * hh : hh * (kD * NB * 4) + t * (8 * NB * 4)};
     const float inv_z = 1.0f / a.z_scale;
 
     float m_run[R], l_acc[R], mn_acc[R];
@@ -710,10 +741,19 @@ __global__ __launch_bounds__(kMThreads, (R == 1 && NB == 2) ? 2 : 1) void decode
             aw[rg] = v8i_t{(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
         }
         const int sc_w = 120 + E - 4 * pc;   // 2^(E - 8 - 4 piece), times 2 for the nibble = code / 2
+        uint32_t cx2[8][2];
+        if constexpr (NB == 2) {
+#pragma unroll
+            for (int cg = 0; cg < 8; ++cg) {
+                cx2[cg][0] = cur.cx[cg][0];
+                cx2[cg][1] = cur.cx[cg][1 % NB];
+            }
+            transpose_code_pieces(cx2);
+        }
 #pragma unroll
         for (int cg = 0; cg < 8; ++cg) {
             if constexpr (NB == 2) {
-                const uint32_t x0 = cur.cx[cg][0], x1 = cur.cx[cg][1 % NB];
+                const uint32_t x0 = cx2[cg][0], x1 = cx2[cg][1];
                 const v8i_t bv = v8i_t{(int)(x0 & 0x33333333u), (int)((x0 >> 2) & 0x33333333u), (int)(x1 & 0x33333333u),
                                        (int)((x1 >> 2) & 0x33333333u), 0, 0, 0, 0};
 #pragma unroll

@@ -73,6 +73,18 @@ __global__ void lds_dma_kernel(const uint32_t* src, const int* off, int size, ui
     for (int i = l; i < 64 * size / 4; i += 64) out[i] = img[i];
 }
 
+// v_permlane16_swap and v_permlane32_swap of a = a0[l], b = b0[l] (lane l): out[0 .. 63] = the new a,
+// out[64 .. 127] = the new b of the 16-row swap; out[128 ..] and out[192 ..] the same for the 32-row swap.
+__global__ void permlane_swap_kernel(const uint32_t* a0, const uint32_t* b0, uint32_t* out) {
+    const int l = threadIdx.x;
+    const auto x = __builtin_amdgcn_permlane16_swap(a0[l], b0[l], false, false);
+    const auto y = __builtin_amdgcn_permlane32_swap(a0[l], b0[l], false, false);
+    out[l] = x[0];
+    out[64 + l] = x[1];
+    out[128 + l] = y[0];
+    out[192 + l] = y[1];
+}
+
 // A streaming read of n 16-byte words (grid-stride), folded into one word per thread so the loads stay;
 // NT: non-temporal loads.
 typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
@@ -192,6 +204,11 @@ int probe_cvt_fp6(const float* x, const float* scale, uint32_t* packed, float* b
 int probe_lds_dma(const uint32_t* src, const int* off, int size, uint32_t* out, hipStream_t s) {
     if (size != 4 && size != 16) return -1;
     hipLaunchKernelGGL(lds_dma_kernel, dim3(1), dim3(64), 0, s, src, off, size, out);
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+int probe_permlane_swaps(const uint32_t* a, const uint32_t* b, uint32_t* out, hipStream_t s) {
+    hipLaunchKernelGGL(permlane_swap_kernel, dim3(1), dim3(64), 0, s, a, b, out);
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 

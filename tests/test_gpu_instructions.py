@@ -26,7 +26,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "probes", "l
 def lib():
     assert os.path.exists(LIB_PATH), "tests/probes/libqjl_probes.so is not built (run __graft_entry__.build())"
     lib = ctypes.CDLL(LIB_PATH)
-    for name in ("probe_mfma_f6f4", "probe_cvt_fp6", "probe_lds_dma", "probe_stream_read", "probe_decode_stream"):
+    for name in ("probe_mfma_f6f4", "probe_cvt_fp6", "probe_lds_dma", "probe_permlane_swaps", "probe_stream_read",
+                 "probe_decode_stream"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -163,6 +164,31 @@ def test_lds_destination_loads(lib, size):
     got = out.cpu().numpy().view(np.uint32)
     want = np.concatenate([src[o // 4: o // 4 + size // 4] for o in off])
     np.testing.assert_array_equal(got, want)
+
+
+def test_permlane_swaps(lib):
+    """v_permlane16_swap(a, b) exchanges the odd 16-lane rows of a with the even rows of b (row r + 1 of
+    a <-> row r of b); v_permlane32_swap(a, b) the upper 32 lanes of a with the lower 32 of b.  The
+    four-wave decode transposes its code pieces across lane rows with these two."""
+    rng = np.random.default_rng(3)
+    a = rng.integers(0, 2**32, 64, dtype=np.uint64).astype(np.uint32)
+    b = rng.integers(0, 2**32, 64, dtype=np.uint64).astype(np.uint32)
+    out = torch.empty(256, dtype=torch.int32, device="cuda")
+    dev = lambda x: torch.from_numpy(x.view(np.int32)).cuda()  # noqa: E731
+    assert lib.probe_permlane_swaps(_p(dev(a)), _p(dev(b)), _p(out), _stream()) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint32).reshape(4, 64)
+    a16, b16, a32, b32 = a.copy(), b.copy(), a.copy(), b.copy()
+    for l in range(64):
+        if (l // 16) % 2 == 1:
+            a16[l] = b[l - 16]
+        else:
+            b16[l] = a[l + 16]
+        if l >= 32:
+            a32[l] = b[l - 32]
+        else:
+            b32[l] = a[l + 32]
+    np.testing.assert_array_equal(got, np.stack([a16, b16, a32, b32]))
 
 
 def _rate(launch, nbytes: int, reps: int = 10) -> float:
