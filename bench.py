@@ -233,19 +233,21 @@ def _timer_run(qjl, torch, names, run_one, steps: int) -> dict:
     return res
 
 
-def _region_ms(torch, run_one, steps: int) -> float:
+def _region_ms(torch, run_one, steps: int) -> tuple:
     """Mean duration of one call over `steps` back-to-back calls: HIP events on the launch stream (torch's
     current stream, which the binding launches on) bracket the whole run, so the figure is the rate a
     stream of such calls sustains (the key quantizer's launches slow down over a run as the clock drops
-    under matrix-core load)."""
+    under matrix-core load).  Returns (event ms, host wall-clock ms) per call of the same run."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
     e0.record()
     for _ in range(steps):
         run_one()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    return e0.elapsed_time(e1) / steps, wall
 
 
 def bench_quantize(qjl, torch, steps: int) -> dict:
@@ -271,13 +273,8 @@ def bench_quantize(qjl, torch, steps: int) -> dict:
         qjl.quantize_keys(Ks[i], Si, So, od, caches[i].bits, caches[i].norms)
     for _ in range(2 * copies):
         keys_once()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        keys_once()
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps
-    kern_s = _region_ms(torch, keys_once, steps) / 1e3
+    kern_ms, wall_ms = _region_ms(torch, keys_once, steps)
+    kern_s = kern_ms / 1e3
     # outlier-channel selection over the same keys (one read of K, two launches)
     ws = torch.empty(qjl.lib.qjl_select_outliers_workspace_size(w.B, w.N, w.Hkv, w.d), dtype=torch.uint8, device="cuda")
     sel = torch.empty((w.Hkv, w.n_out), dtype=torch.int32, device="cuda")
@@ -289,7 +286,7 @@ def bench_quantize(qjl, torch, steps: int) -> dict:
     for _ in range(2 * copies):
         select_once()
     torch.cuda.synchronize()
-    sel_s = _region_ms(torch, select_once, steps) / 1e3
+    sel_s = _region_ms(torch, select_once, steps)[0] / 1e3
     sel_bytes = float(in_bytes)
     del Ks, K0
     # token-wise value codes of the same prefill: V [1, 65536, 8, 128] bf16 -> 2-bit code tiles + (min, step)
@@ -303,7 +300,7 @@ def bench_quantize(qjl, torch, steps: int) -> dict:
     for _ in range(2 * copies):
         values_once()
     torch.cuda.synchronize()
-    val_s = _region_ms(torch, values_once, steps) / 1e3
+    val_s = _region_ms(torch, values_once, steps)[0] / 1e3
     del Vs, V0
     # per token and KV head: d bf16 values read, d b / 8 code bytes and the fp16 (min, step) pair written
     val_bytes = float(w.B * w.N * w.Hkv * (2 * w.d + w.d * w.nbits // 8 + 4))
@@ -311,7 +308,7 @@ def bench_quantize(qjl, torch, steps: int) -> dict:
     flops = 2.0 * w.d * w.m * tokens * w.Hkv          # inlier (d - n_out) m + outlier n_out m_out = d m MACs
     return {"workload": f"{w.name}: B={w.B} T={w.N} Hkv={w.Hkv} d={w.d} m=m_out={w.m} n_out={w.n_out}",
             "input_copies": copies, "tok_per_s": tokens / kern_s, "key_vectors_per_s": tokens * w.Hkv / kern_s,
-            "kernel_ms": kern_s * 1e3, "wall_ms_per_call": wall * 1e3,
+            "kernel_ms": kern_s * 1e3, "wall_ms_per_call": wall_ms,
             "mfma": {"bound": "mfma", "achieved": flops / kern_s / 1e12, "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": flops / kern_s / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                      "flops_per_launch": flops},

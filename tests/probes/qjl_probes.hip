@@ -102,10 +102,12 @@ __global__ void stream_read_kernel(const v4u_t* src, int64_t n, uint32_t* sink) 
 // (unit, chunk) of U units of Ncap tokens split into nsplit chunks (workgroup L serves chunk 8 (L / 8) +
 // L % 8, as in the decode's grid), each wave taking 128-token blocks 1024 tokens apart; per token 64 B
 // of sign words, 4 B of norms, 4 B of meta and 32 B of codes, each stream stored unit after unit.  A
-// block's loads are all issued, then awaited, non-temporal.  LDS: the decode's LDS-destination loads
-// with its lane offsets (signs: 16-byte quarter-rows of token pairs; codes: 16-byte pieces of four
-// 32-token tiles); otherwise the same bytes go to registers as 16-byte (signs, codes) and 4-byte
-// (norms, meta) loads.  Every offset stays below the chunk's end, so the range checks never clip.
+// block's loads are all issued, then awaited, non-temporal.  MODE 1: the decode's LDS-destination loads
+// with its lane offsets (signs: 16-byte quarter-rows of token pairs; codes: one whole 1 KB tile per load,
+// lane 16 p + u reading piece p of stream group u); MODE 2: the same, but each code load takes the 16-byte
+// piece q of every lane's own stream group in all four tiles (pieces 64 bytes apart); MODE 0: the same
+// bytes go to registers as contiguous 16-byte (signs, codes) and 4-byte (norms, meta) loads.  Every
+// offset stays below the chunk's end, so the range checks never clip.
 struct DecodeStreams {
     const uint8_t* sg;
     const uint32_t* nr;
@@ -123,7 +125,7 @@ __device__ __forceinline__ void nt_dma16(__amdgpu_buffer_rsrc_t r, uint32_t* lds
 __device__ __forceinline__ void nt_dma4(__amdgpu_buffer_rsrc_t r, uint32_t* lds, int voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, 0, 0, 2);
 }
-template <bool LDS>
+template <int MODE>
 __global__ __launch_bounds__(512, 1) void decode_stream_kernel(DecodeStreams d, uint32_t* sink) {
     __shared__ __attribute__((aligned(16))) uint32_t s_sgn[8][8][64][4];
     __shared__ __attribute__((aligned(16))) uint32_t s_cod[8][4][64][4];
@@ -143,10 +145,11 @@ __global__ __launch_bounds__(512, 1) void decode_stream_kernel(DecodeStreams d, 
     // the decode's token of lane group (t, hh) in sub-step 0, its quarter-row and its code stream
     const int tok0 = 32 * ((t >> 3) & 1) + 16 * ((t >> 2) & 1) + 8 * ((t >> 1) & 1) + (t & 1);
     const int off_sg = (tok0 * 16 + hh * 4) * 4;
-    const int off_cd = hh * 1024 + t * 64;
+    const int off_cd = MODE == 1 ? 64 * t + 16 * hh : hh * 1024 + t * 64;
+    const int step_cd = MODE == 1 ? 1024 : 16;
     uint32_t acc = 0u;
     for (int s0 = t_begin + 128 * wave; s0 + 128 <= t_end; s0 += 1024) {
-        if (LDS) {
+        if (MODE != 0) {
 #pragma unroll
             for (int s = 0; s < 8; ++s) nt_dma16(rs, &s_sgn[wave][s][0][0], off_sg + (s0 + 64 * (s >> 2) + 2 * (s & 3)) * 64);
 #pragma unroll
@@ -155,7 +158,7 @@ __global__ __launch_bounds__(512, 1) void decode_stream_kernel(DecodeStreams d, 
                 nt_dma4(rm, &s_nm[wave][1][64 * q], (s0 + 64 * q + lane) * 4);
             }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) nt_dma16(rc, &s_cod[wave][q][0][0], off_cd + s0 * 32 + 16 * q);
+            for (int q = 0; q < 4; ++q) nt_dma16(rc, &s_cod[wave][q][0][0], off_cd + s0 * 32 + step_cd * q);
             // the loads write LDS behind the compiler's back: wait for them, and keep the buffers escaping
             asm volatile("s_waitcnt vmcnt(0)" ::"s"(s_sgn), "s"(s_cod), "s"(s_nm) : "memory");
             acc ^= s_sgn[wave][lane & 7][lane][0] ^ s_cod[wave][lane & 3][lane][1] ^ s_nm[wave][lane & 1][lane];
@@ -224,13 +227,14 @@ int probe_stream_read(const void* src, int64_t n16, uint32_t* sink, int blocks, 
 // signs: U * Ncap * 64 B, norms and meta: U * Ncap * 4 B, codes: U * Ncap * 32 B; Ncap a multiple of
 // 1024 * nsplit; sink: 512 words per workgroup (8 * ceil(U * nsplit / 8) workgroups)
 int probe_decode_stream(const void* signs, const void* norms, const void* meta, const void* codes, int64_t Ncap, int U,
-                        int nsplit, int lds, uint32_t* sink, hipStream_t s) {
-    if (U <= 0 || nsplit <= 0 || Ncap <= 0 || Ncap % (1024 * (int64_t)nsplit) != 0 || Ncap * 64 > 0xFFFFFFFFll) return -1;
+                        int nsplit, int mode, uint32_t* sink, hipStream_t s) {
+    if (mode < 0 || mode > 2 || U <= 0 || nsplit <= 0 || Ncap <= 0 || Ncap % (1024 * (int64_t)nsplit) != 0 || Ncap * 64 > 0xFFFFFFFFll) return -1;
     const DecodeStreams d{static_cast<const uint8_t*>(signs), static_cast<const uint32_t*>(norms),
                           static_cast<const uint32_t*>(meta), static_cast<const uint8_t*>(codes), Ncap, U, nsplit};
     const unsigned blocks = (unsigned)((U * nsplit + 7) / 8 * 8);
-    if (lds) hipLaunchKernelGGL(decode_stream_kernel<true>, dim3(blocks), dim3(512), 0, s, d, sink);
-    else hipLaunchKernelGGL(decode_stream_kernel<false>, dim3(blocks), dim3(512), 0, s, d, sink);
+    if (mode == 1) hipLaunchKernelGGL(decode_stream_kernel<1>, dim3(blocks), dim3(512), 0, s, d, sink);
+    else if (mode == 2) hipLaunchKernelGGL(decode_stream_kernel<2>, dim3(blocks), dim3(512), 0, s, d, sink);
+    else hipLaunchKernelGGL(decode_stream_kernel<0>, dim3(blocks), dim3(512), 0, s, d, sink);
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 

@@ -221,9 +221,10 @@ def test_stream_read_rate(lib, blocks):
 
 def test_decode_stream_rates(lib):
     """The cache-read pattern of the eight-wave decode on its Llama-3.1-70B shape (128 (sequence, KV head)
-    units of 131072 tokens, two chunks each, 104 B per token: 1.745 GB), with no arithmetic: once through
-    LDS-destination loads with the decode's lane offsets, once into registers.  Printed; the first is the
-    ceiling of the decode's own load path."""
+    units of 131072 tokens, two chunks each, 104 B per token: 1.745 GB), with no arithmetic: through the
+    decode's LDS-destination loads (whole code tiles per load: the decode's own load path), the same with
+    the code words loaded as 16-byte pieces 64 bytes apart (the layout it replaced), and into registers.
+    Printed; asserted only to be a sane fraction of the 8 TB/s peak."""
     U, Ncap, ns = 128, 131072, 2
     sg = torch.ones(U * Ncap * 16, dtype=torch.int32, device="cuda")
     nr = torch.ones(U * Ncap, dtype=torch.int32, device="cuda")
@@ -232,10 +233,11 @@ def test_decode_stream_rates(lib):
     blocks = (U * ns + 7) // 8 * 8
     sink = torch.empty(blocks * 512, dtype=torch.int32, device="cuda")
     nbytes = U * Ncap * 104
-    for lds in (1, 0):
-        gbs = _rate(lambda: lib.probe_decode_stream(_p(sg), _p(nr), _p(mt), _p(cd), ctypes.c_int64(Ncap), U, ns, lds, _p(sink),
-                                                    _stream()), nbytes)
-        kind = "LDS-destination loads" if lds else "register loads"
+    kinds = {1: "LDS-destination loads, whole code tiles", 2: "LDS-destination loads, strided code pieces",
+             0: "register loads"}
+    for mode, kind in kinds.items():
+        gbs = _rate(lambda: lib.probe_decode_stream(_p(sg), _p(nr), _p(mt), _p(cd), ctypes.c_int64(Ncap), U, ns, mode,
+                                                    _p(sink), _stream()), nbytes)
         print(f"\n[decode stream] 1.745 GB, {blocks} workgroups x 512, {kind}: {gbs:.0f} GB/s "
               f"({gbs / 8000 * 100:.1f}% of 8 TB/s, {nbytes / gbs / 1e3:.1f} us)")
         assert gbs > 3000
