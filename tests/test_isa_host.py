@@ -86,7 +86,7 @@ def block_loop(kernel_asm: str) -> str:
 
 
 def test_block_loop_finds_the_last_loop():
-    fake = ("k:\n\ts_mov_b32 s0, 0\n.LBB0_1:  ; =>This Inner Loop Header: Depth=1\n\ts_waitcnt vmcnt(3)\n"
+    fake = ("\nk:\n\ts_mov_b32 s0, 0\n.LBB0_1:  ; =>This Inner Loop Header: Depth=1\n\ts_waitcnt vmcnt(3)\n"
             "\ts_cbranch_scc1 .LBB0_1\n.LBB0_2:  ; =>This Inner Loop Header: Depth=1\n\ts_waitcnt vmcnt(0)\n"
             "\tbuffer_load_dword v0, s[0:3], 0 offen lds\n\ts_cbranch_scc1 .LBB0_2\n\ts_endpgm\n")
     loop = block_loop(_kernel_asm(fake, "k:"))
