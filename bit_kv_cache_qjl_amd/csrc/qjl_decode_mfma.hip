@@ -317,9 +317,24 @@ __global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs 
     const int ncol = a.g + (APPEND ? 1 : 0);
     const int64_t head0 = (int64_t)b * a.Hq + (int64_t)h * a.g;
 
-    // ---- every global load that does not depend on another is issued first: this wave's S tiles
-    //      (B operands: projection row 16 hf + lane % 16 of word wn, channels 32 s + 8 (lane / 16) ..),
-    //      the outlier channels and the first pass's vectors
+    // ---- every global load that does not depend on another is issued first: the KV head's outlier
+    //      channels (one entry per lane of wave 0) and the first pass's vectors, then this wave's S tiles
+    //      (B operands: projection row 16 hf + lane % 16 of word wn, channels 32 s + 8 (lane / 16) ..).
+    //      Loads complete in order for the wait counter, so in this order the mask and the staging below
+    //      wait for their own loads while the S tiles are still in flight.
+    // (the raw entry, read only after the S tiles are issued: arithmetic on it next to its load would
+    // wait for the load there; the unused default is the lane index, not a constant that would let the
+    // compiler fold the arithmetic into the load's branch)
+    const bool has_oc = wave == 0 && lane < a.n_out;
+    int oc_raw = lane;
+    if (has_oc) oc_raw = a.oidx[h * a.n_out + lane];
+    const int sv = tid >> 4, cg = tid & 15;      // staging: vector sv of a pass, channels 8 cg .. 8 cg + 7
+    auto load_vector = [&](int col) {
+        if (col >= ncol) return make_uint4(0u, 0u, 0u, 0u);
+        if (APPEND && col == 0) return *reinterpret_cast<const uint4*>(ap.K + b * ap.sKb + h * ap.sKh + 8 * cg);
+        return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Q) + (head0 + col - (APPEND ? 1 : 0)) * kD + 8 * cg);
+    };
+    uint4 xv = load_vector(sv);
     uint4 sb[WPW][2][4];
 #pragma unroll
     for (int u = 0; u < WPW; ++u) {
@@ -332,20 +347,12 @@ __global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs 
             for (int s = 0; s < 4; ++s)
                 sb[u][hf][s] = *reinterpret_cast<const uint4*>(S + (size_t)(16 * hf + (lane & 15)) * kD + 32 * s + 8 * (lane >> 4));
     }
-    // the KV head's outlier channels: one entry per lane of wave 0, all in one round trip
-    const int oc = (wave == 0 && lane < a.n_out) ? (a.oidx[h * a.n_out + lane] & (kD - 1)) : -1;
-    const int sv = tid >> 4, cg = tid & 15;      // staging: vector sv of a pass, channels 8 cg .. 8 cg + 7
-    auto load_vector = [&](int col) {
-        if (col >= ncol) return make_uint4(0u, 0u, 0u, 0u);
-        if (APPEND && col == 0) return *reinterpret_cast<const uint4*>(ap.K + b * ap.sKb + h * ap.sKh + 8 * cg);
-        return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Q) + (head0 + col - (APPEND ? 1 : 0)) * kD + 8 * cg);
-    };
-    uint4 xv = load_vector(sv);
     if (wave == 0) {
         // outlier mask of the KV head (bit c % 32 of word c / 32): the LDS operations of a wave complete
         // in order, so the words are cleared before the entries set their bits
         if (lane < 4) s_mask[lane] = 0u;
-        if (oc >= 0) atomicOr(&s_mask[oc >> 5], 1u << (oc & 31));
+        const int oc = oc_raw & (kD - 1);        // never index outside a row
+        if (has_oc) atomicOr(&s_mask[oc >> 5], 1u << (oc & 31));
     }
     __syncthreads();
 
@@ -353,11 +360,12 @@ __global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs 
     const float c_out = a.m_out ? 2.f * a.z_scale * kSqrtHalfPi / (float)a.m_out : 0.f;
     const float c2_in = 2.f * a.z_scale / (float)a.m;
     const float c2_out = a.m_out ? 2.f * a.z_scale / (float)a.m_out : 0.f;
-    for (int c0 = 0; c0 < ncol; c0 += 16) {
+    // one pass per 16 vectors; the first pass is its own copy, so that its staging waits only for the
+    // vector loaded before the S tiles (a wait at a join with later passes would wait for all loads)
+    auto pass = [&](const int c0, const uint4 xv) {
         const bool key_pass = APPEND && c0 == 0;
         // ---- stage 16 vectors, split at the outlier channels
         {
-            if (c0) xv = load_vector(c0 + sv);
             const uint32_t om = (s_mask[cg >> 2] >> (8 * (cg & 3))) & 0xFFu;
             uint4 xi, xo;
             float ss_in = 0.f, ss_out = 0.f;
@@ -419,7 +427,9 @@ __global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs 
                                  reinterpret_cast<uint32_t*>(a.sq) + hq * (128 * (win4 + wout4)), a.qconst + hq * 4);
         }
         __syncthreads();
-    }
+    };
+    pass(0, xv);
+    for (int c0 = 16; c0 < ncol; c0 += 16) pass(c0, load_vector(c0 + sv));
 }
 
 // ---------------------------------------------------------------------------- decode
