@@ -85,6 +85,26 @@ __global__ void permlane_swap_kernel(const uint32_t* a0, const uint32_t* b0, uin
     out[192 + l] = y[1];
 }
 
+// v_mfma_f32_32x32x16_bf16 with register operands only: every wave runs four independent accumulator
+// chains for iters steps (operands from src, lane l: 16 bytes at 16 l, bf16); the accumulators are
+// folded into out[global thread index] so the instructions stay.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+__global__ __launch_bounds__(256) void mfma_rate_kernel(const uint4* src, int iters, float* out) {
+    const int l = threadIdx.x & 63;
+    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, src[l]);
+    const bf16x8_t b = __builtin_bit_cast(bf16x8_t, src[64 + l]);
+    v16f_t c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int i = 0; i < iters; ++i) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, b, c3, 0, 0, 0);
+    }
+    float acc = 0.f;
+    for (int r = 0; r < 16; ++r) acc += (c0[r] + c1[r]) + (c2[r] + c3[r]);
+    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
 // A streaming read of n 16-byte words (grid-stride), folded into one word per thread so the loads stay;
 // NT: non-temporal loads.
 typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
@@ -212,6 +232,13 @@ int probe_lds_dma(const uint32_t* src, const int* off, int size, uint32_t* out, 
 
 int probe_permlane_swaps(const uint32_t* a, const uint32_t* b, uint32_t* out, hipStream_t s) {
     hipLaunchKernelGGL(permlane_swap_kernel, dim3(1), dim3(64), 0, s, a, b, out);
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// src: 128 uint4 (bf16 operands), out: blocks * 256 floats
+int probe_mfma_rate(const void* src, int iters, int blocks, float* out, hipStream_t s) {
+    if (iters <= 0 || blocks <= 0) return -1;
+    hipLaunchKernelGGL(mfma_rate_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const uint4*>(src), iters, out);
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 

@@ -27,7 +27,7 @@ def lib():
     assert os.path.exists(LIB_PATH), "tests/probes/libqjl_probes.so is not built (run __graft_entry__.build())"
     lib = ctypes.CDLL(LIB_PATH)
     for name in ("probe_mfma_f6f4", "probe_cvt_fp6", "probe_lds_dma", "probe_permlane_swaps", "probe_stream_read",
-                 "probe_decode_stream"):
+                 "probe_decode_stream", "probe_mfma_rate"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -241,3 +241,23 @@ def test_decode_stream_rates(lib):
         print(f"\n[decode stream] 1.745 GB, {blocks} workgroups x 512, {kind}: {gbs:.0f} GB/s "
               f"({gbs / 8000 * 100:.1f}% of 8 TB/s, {nbytes / gbs / 1e3:.1f} us)")
         assert gbs > 3000
+
+
+def test_bf16_matrix_core_rate(lib):
+    """The rate of v_mfma_f32_32x32x16_bf16 with register operands only (four independent accumulator
+    chains per wave; 2, 4 and 8 waves per SIMD): the practical ceiling of a bf16 contraction such as the
+    key quantizer's, printed against the 2.5 PFLOP/s dense figure; asserted only to be sane."""
+    rng = np.random.default_rng(11)
+    vals = (rng.standard_normal(128 * 8) * 1e-2).astype(np.float32)
+    src = torch.from_numpy(vals).cuda().to(torch.bfloat16)
+    iters = 4096
+    best = 0.0
+    for blocks in (512, 1024, 2048):
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+        flops = blocks * 4 * iters * 4 * 2.0 * 32 * 32 * 16
+        tfs = _rate(lambda: lib.probe_mfma_rate(_p(src), iters, blocks, _p(out), _stream()), flops) / 1e3
+        print(f"\n[matrix cores] v_mfma_f32_32x32x16_bf16, register operands, {blocks * 4 // 1024} waves per SIMD: "
+              f"{tfs:.0f} TFLOP/s ({tfs / 2500 * 100:.1f}% of 2.5 PFLOP/s)")
+        assert torch.isfinite(out).all()
+        best = max(best, tfs)
+    assert best > 300
