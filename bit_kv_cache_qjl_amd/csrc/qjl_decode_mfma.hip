@@ -7,7 +7,7 @@
 // Brain Already Runs on 1-Bit Keys", "Keys Select. Values Deliver.").
 //
 // Scores on v_mfma_scale_f32_16x16x128_f8f6f4 (A fp6 e2m3, B fp4 e2m1; with no 8-bit operand the
-// instruction issues at the fp4 rate, about 1.6x the fp8 one): 16 tokens x 4 query heads per
+// instruction is faster: the fp8 x fp4 form takes 1.2x the time under full load): 16 tokens x 4 query heads per
 // instruction, 128 sign positions of one kind (inlier or outlier) per instruction.
 //   B (sign bits): with b = 1 for a non-negative projection, a 32-bit sign word x gives four fp4
 //     operand words, one instruction each: x & 0x11111111, x & 0x22222222, x & 0x44444444 (nibble n

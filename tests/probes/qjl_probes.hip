@@ -105,6 +105,26 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(const uint4* src, int it
     out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+template <int AFMT>
+__global__ __launch_bounds__(256) void f8f6f4_rate_kernel(const uint32_t* src, int iters, float* out) {
+    const int l = threadIdx.x & 63;
+    v8i_t a, b;
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (int)src[8 * l + i];
+        b[i] = (int)src[512 + 8 * l + i];
+    }
+    v4f_t c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int i = 0; i < iters; ++i) {
+        c0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c0, AFMT, 4, 0, 127, 0, 127);
+        c1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c1, AFMT, 4, 0, 127, 0, 127);
+        c2 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c2, AFMT, 4, 0, 127, 0, 127);
+        c3 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c3, AFMT, 4, 0, 127, 0, 127);
+    }
+    float acc = 0.f;
+    for (int r = 0; r < 4; ++r) acc += (c0[r] + c1[r]) + (c2[r] + c3[r]);
+    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
 // A streaming read of n 16-byte words (grid-stride), folded into one word per thread so the loads stay;
 // NT: non-temporal loads.
 typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
@@ -239,6 +259,17 @@ int probe_permlane_swaps(const uint32_t* a, const uint32_t* b, uint32_t* out, hi
 int probe_mfma_rate(const void* src, int iters, int blocks, float* out, hipStream_t s) {
     if (iters <= 0 || blocks <= 0) return -1;
     hipLaunchKernelGGL(mfma_rate_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const uint4*>(src), iters, out);
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// v_mfma_scale_f32_16x16x128_f8f6f4 with A in fp6 e2m3 (fp6 = 1) or fp8 e4m3 (fp6 = 0) and B in fp4 e2m1,
+// register operands only, four independent chains per wave, unit scales; src: 128 x 8 words of operand
+// bits (lane l: A = words 8 l .., B = words 512 + 8 l ..); out: blocks * 256 floats
+int probe_f8f6f4_rate(const void* src, int fp6, int iters, int blocks, float* out, hipStream_t s) {
+    if (iters <= 0 || blocks <= 0) return -1;
+    const uint32_t* p = static_cast<const uint32_t*>(src);
+    if (fp6) hipLaunchKernelGGL(f8f6f4_rate_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, p, iters, out);
+    else hipLaunchKernelGGL(f8f6f4_rate_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, s, p, iters, out);
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 

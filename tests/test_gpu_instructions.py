@@ -27,7 +27,7 @@ def lib():
     assert os.path.exists(LIB_PATH), "tests/probes/libqjl_probes.so is not built (run __graft_entry__.build())"
     lib = ctypes.CDLL(LIB_PATH)
     for name in ("probe_mfma_f6f4", "probe_cvt_fp6", "probe_lds_dma", "probe_permlane_swaps", "probe_stream_read",
-                 "probe_decode_stream", "probe_mfma_rate"):
+                 "probe_decode_stream", "probe_mfma_rate", "probe_f8f6f4_rate"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -261,3 +261,20 @@ def test_bf16_matrix_core_rate(lib):
         assert torch.isfinite(out).all()
         best = max(best, tfs)
     assert best > 300
+
+
+def test_fp6_and_fp8_query_operand_issue_rates(lib):
+    """v_mfma_scale_f32_16x16x128_f8f6f4 with B in fp4, A in fp6 e2m3 (the decode's score operand) or in
+    fp8 e4m3 (its value operand), register operands only, four independent chains per wave, 8 waves
+    per SIMD: printed as TFLOP/s and the fp8 / fp6 time ratio; asserted only that fp6 is not slower."""
+    rng = np.random.default_rng(12)
+    src = torch.from_numpy(rng.integers(0, 2**32, 1024, dtype=np.uint64).astype(np.uint32).view(np.int32)).cuda()
+    blocks, iters = 2048, 4096
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    flops = blocks * 4 * iters * 4 * 2.0 * 16 * 16 * 128
+    rates = {}
+    for fp6, name in ((1, "fp6 x fp4"), (0, "fp8 x fp4")):
+        rates[name] = _rate(lambda: lib.probe_f8f6f4_rate(_p(src), fp6, iters, blocks, _p(out), _stream()), flops) / 1e3
+        print(f"\n[matrix cores] v_mfma_scale_f32_16x16x128_f8f6f4, {name}: {rates[name]:.0f} TFLOP/s")
+    print(f"\n[matrix cores] fp8 x fp4 takes {rates['fp6 x fp4'] / rates['fp8 x fp4']:.2f}x the time of fp6 x fp4")
+    assert rates["fp6 x fp4"] >= 0.95 * rates["fp8 x fp4"]
