@@ -76,13 +76,17 @@ def _kernel_asm(asm: str, symbol_prefix: str) -> str:
     return asm[start:asm.index("s_endpgm", start)]
 
 
-def block_loop(kernel_asm: str) -> str:
-    """The body of the kernel's last loop (from its header label to the branch back to it)."""
+def block_loop(kernel_asm: str, marker: str = "") -> str:
+    """The body of the kernel's last loop that contains `marker` (from its header label to the branch
+    back to it; with no marker, the last loop)."""
     headers = re.findall(r"^(\.LBB\w+):.*Loop Header", kernel_asm, re.M)
     assert headers, "no loop found"
-    label = headers[-1]
-    body = kernel_asm[kernel_asm.index(label + ":"):]
-    return body[:body.rindex(label)]
+    for label in reversed(headers):
+        body = kernel_asm[kernel_asm.index(label + ":"):]
+        body = body[:body.rindex(label)]
+        if marker in body:
+            return body
+    return ""
 
 
 def test_block_loop_finds_the_last_loop():
@@ -100,7 +104,7 @@ def test_eight_wave_block_loop_waits_only_where_written(decode_asm):
     issued just before."""
     asm = decode_asm
     for sym in ("_ZN3qjl12_GLOBAL__N_119decode_mfma8_kernelILi2ELi2ELb0E", "_ZN3qjl12_GLOBAL__N_119decode_mfma8_kernelILi4ELi0ELb0E"):
-        loop = block_loop(_kernel_asm(asm, sym))
+        loop = block_loop(_kernel_asm(asm, sym), "v_mfma_scale_f32_16x16x128_f8f6f4")
         assert "v_mfma_scale_f32_16x16x128_f8f6f4" in loop and "lds" in loop, "not the block loop"
         waits = re.findall(r"s_waitcnt vmcnt\((\d+)\)", loop)
         assert waits and "0" not in waits, f"{sym}: vmcnt waits in the block loop: {waits}"
