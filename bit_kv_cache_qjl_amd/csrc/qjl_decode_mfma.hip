@@ -244,77 +244,82 @@ __global__ __launch_bounds__(256) void qproj_f32_kernel(DecodeArgs a, int win4, 
                              reinterpret_cast<uint32_t*>(a.sq) + (size_t)bh * (128 * (win4 + wout4)), a.qconst + (size_t)bh * 4);
 }
 
-// bf16: one workgroup per (sequence, KV head) projects the KV head's g query heads (and, for a decode
-// step, the new key) on the matrix cores: D (16 vectors x 16 projections) = A (vectors x channels,
-// from LDS) . B (S rows, straight from global memory), v_mfma_f32_16x16x32_bf16 (exact bf16 products,
-// fp32 sums).  Vector 0 of the first pass is the new key when APPEND; its signs are the sign bits of
-// the cache row (ballot of the D column), its norms and its value codes are computed as in the
-// quantize kernels.  Wave w owns sign words w WPW .. (w + 1) WPW - 1 (two 16-projection tiles per
-// word), so WPW = W / 4.  The query projections go to LDS, then one wave per head builds the operand.
+// ---------------------------------------------------------------------------- query projection (bf16)
 constexpr int kVRow = kD + 8;                // LDS row of a staged vector (bf16), 272 B
 constexpr int kMaxMfmaBits = 512;            // m + m_out on the matrix-core path
 constexpr int kXPitch = kMaxMfmaBits + 4;    // LDS row of a head's projections (floats)
 
-template <int WPW, bool APPEND>
-__global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs ap) {
-    __shared__ __attribute__((aligned(16))) uint16_t vin[16 * kVRow];    // vectors, outlier channels zeroed
-    __shared__ __attribute__((aligned(16))) uint16_t vout[16 * kVRow];   // vectors on the outlier channels only
-    __shared__ __attribute__((aligned(16))) float xs[16 * kXPitch];
-    __shared__ uint32_t s_mask[4];
-    __shared__ float s_qn[16][2];                                         // vector norms (two-sided)
-    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+// LDS of the projection phase: the staged vectors (outlier channels zeroed / outlier channels only),
+// their projections, the KV head's outlier mask and the vectors' part norms (two-sided estimator).
+struct ProjLds {
+    __attribute__((aligned(16))) uint16_t vin[16 * kVRow];
+    __attribute__((aligned(16))) uint16_t vout[16 * kVRow];
+    __attribute__((aligned(16))) float xs[16 * kXPitch];
+    uint32_t mask[4];
+    float qn[16][2];
+};
 
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nunits = a.B * a.Hkv;
-    if (APPEND && (int)blockIdx.x >= nunits) {
-        // ---- the new values, one (sequence, KV head) per wave in workgroups of their own (their atomic
-        //      round trips overlap the projections): a row of 16 lanes, 8 channels per lane; the 2- or
-        //      4-bit fields are merged into the tile words of position pos with atomic and/or, the rest
-        //      of the tile is kept
-        const int vunit = 4 * ((int)blockIdx.x - nunits) + wave;
-        if (vunit >= nunits) return;
-        const int vb = vunit / a.Hkv, vh = vunit - vb * a.Hkv;
-        uint4 vv = make_uint4(0u, 0u, 0u, 0u);
-        if (lane < 16) vv = *reinterpret_cast<const uint4*>(ap.V + vb * ap.sVb + vh * ap.sVh + 8 * lane);
-        const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-        float v[8];
+// The new value of a decode step (sequence, KV head vunit) into its code tile and meta at ap.pos: one
+// wave, a row of 16 lanes with 8 channels per lane; the 2- or 4-bit fields are merged into the tile
+// words with atomic and/or (the rest of the tile is kept), 3-bit codes into their two planes.
+__device__ __forceinline__ void append_value(const DecodeArgs& a, const AppendArgs& ap, int vunit, int lane) {
+    const int vb = vunit / a.Hkv, vh = vunit - vb * a.Hkv;
+    uint4 vv = make_uint4(0u, 0u, 0u, 0u);
+    if (lane < 16) vv = *reinterpret_cast<const uint4*>(ap.V + vb * ap.sVb + vh * ap.sVh + 8 * lane);
+    const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+    float v[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            v[2 * q] = __uint_as_float(w[q] << 16);
-            v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
-        }
-        const int nb = a.nbits;
-        uint32_t code[8];
-        const uint32_t mt = nb == 4 ? value_codes<4, 8>(v, code) : (nb == 3 ? value_codes<3, 8>(v, code) : value_codes<2, 8>(v, code));
-        if (lane < 16) {
-            if (lane == 0) reinterpret_cast<uint32_t*>(ap.meta)[(size_t)vunit * a.Ncap + ap.pos] = mt;
-            const int64_t tile = ap.pos / kCodeTile;
-            const int j = (int)(ap.pos % kCodeTile);
-            // a 2- or 4-bit field never crosses a word; 3-bit codes: the low two bits at the 2-bit
-            // field, the high bit in word 2 (two planes)
-            const int bit = nb == 3 ? 2 * j : nb * code_field(j, nb);
-            uint32_t* tw = ap.codes + ((size_t)vunit * code_tiles(a.Ncap) + tile) * (kD * nb);
-            const int sh = bit & 31;
-            const uint32_t fm = nb == 3 ? 3u : (1u << nb) - 1u;
+    for (int q = 0; q < 4; ++q) {
+        v[2 * q] = __uint_as_float(w[q] << 16);
+        v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+    }
+    const int nb = a.nbits;
+    uint32_t code[8];
+    const uint32_t mt = nb == 4 ? value_codes<4, 8>(v, code) : (nb == 3 ? value_codes<3, 8>(v, code) : value_codes<2, 8>(v, code));
+    if (lane < 16) {
+        if (lane == 0) reinterpret_cast<uint32_t*>(ap.meta)[(size_t)vunit * a.Ncap + ap.pos] = mt;
+        const int64_t tile = ap.pos / kCodeTile;
+        const int j = (int)(ap.pos % kCodeTile);
+        // a 2- or 4-bit field never crosses a word; 3-bit codes: the low two bits at the 2-bit
+        // field, the high bit in word 2 (two planes)
+        const int bit = nb == 3 ? 2 * j : nb * code_field(j, nb);
+        uint32_t* tw = ap.codes + ((size_t)vunit * code_tiles(a.Ncap) + tile) * (kD * nb);
+        const int sh = bit & 31;
+        const uint32_t fm = nb == 3 ? 3u : (1u << nb) - 1u;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                uint32_t* dst = tw + code_slot(8 * lane + q) * nb;
-                atomicAnd(dst + (bit >> 5), ~(fm << sh));
-                atomicOr(dst + (bit >> 5), (code[q] & fm) << sh);
-                if (nb == 3) {
-                    atomicAnd(dst + 2, ~(1u << hi3_bit(j)));
-                    atomicOr(dst + 2, (code[q] >> 2) << hi3_bit(j));
-                }
+        for (int q = 0; q < 8; ++q) {
+            uint32_t* dst = tw + code_slot(8 * lane + q) * nb;
+            atomicAnd(dst + (bit >> 5), ~(fm << sh));
+            atomicOr(dst + (bit >> 5), (code[q] & fm) << sh);
+            if (nb == 3) {
+                atomicAnd(dst + 2, ~(1u << hi3_bit(j)));
+                atomicOr(dst + 2, (code[q] >> 2) << hi3_bit(j));
             }
         }
-        return;
     }
-    const int unit = blockIdx.x;                 // b * Hkv + h
+}
+
+// One (sequence, KV head) on the matrix cores: D (16 vectors x 16 projections) = A (vectors x channels,
+// from LDS) . B (S rows, straight from global memory), v_mfma_f32_16x16x32_bf16 (exact bf16 products,
+// fp32 sums).  The vectors are the KV head's g query heads, preceded by the new key when app; the key's
+// signs are the sign bits of its cache row (ballot of the D column), its norms are computed as in the
+// quantize kernels.  Wave w < NPW owns sign words w WPW .. (w + 1) WPW - 1 (two 16-projection tiles per
+// word), so WPW = W / NPW.  The query projections go to LDS, then one wave per head builds its operand
+// at sq_dst + head (128 W/4) words and its constants at qc_dst + 4 head.  Threads 0..255 stage the
+// vectors and build the operands; every thread of the workgroup calls this (it holds the workgroup's
+// barriers).
+template <int WPW, int NPW>
+__device__ __forceinline__ void project_unit(const DecodeArgs& a, const AppendArgs& ap, int unit, bool app, ProjLds& L,
+                                             uint32_t* sq_dst, float* qc_dst) {
+    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool worker = tid < 256;               // staging and operands
+    const bool proj = wave < NPW;                // projections
     const int b = unit / a.Hkv, h = unit - b * a.Hkv;
     const int Win = a.m >> 5, Wout = a.m_out >> 5, W = Win + Wout;
     const int win4 = a.m >> 7, wout4 = a.m_out >> 7;
-    const int ncol = a.g + (APPEND ? 1 : 0);
+    const int ncol = a.g + (app ? 1 : 0);
     const int64_t head0 = (int64_t)b * a.Hq + (int64_t)h * a.g;
 
     // ---- every global load that does not depend on another is issued first: the KV head's outlier
@@ -328,31 +333,32 @@ __global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs 
     const bool has_oc = wave == 0 && lane < a.n_out;
     int oc_raw = lane;
     if (has_oc) oc_raw = a.oidx[h * a.n_out + lane];
-    const int sv = tid >> 4, cg = tid & 15;      // staging: vector sv of a pass, channels 8 cg .. 8 cg + 7
+    const int sv = (tid >> 4) & 15, cg = tid & 15;   // staging: vector sv of a pass, channels 8 cg .. 8 cg + 7
     auto load_vector = [&](int col) {
-        if (col >= ncol) return make_uint4(0u, 0u, 0u, 0u);
-        if (APPEND && col == 0) return *reinterpret_cast<const uint4*>(ap.K + b * ap.sKb + h * ap.sKh + 8 * cg);
-        return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Q) + (head0 + col - (APPEND ? 1 : 0)) * kD + 8 * cg);
+        if (!worker || col >= ncol) return make_uint4(0u, 0u, 0u, 0u);
+        if (app && col == 0) return *reinterpret_cast<const uint4*>(ap.K + b * ap.sKb + h * ap.sKh + 8 * cg);
+        return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.Q) + (head0 + col - (app ? 1 : 0)) * kD + 8 * cg);
     };
     uint4 xv = load_vector(sv);
     uint4 sb[WPW][2][4];
 #pragma unroll
     for (int u = 0; u < WPW; ++u) {
-        const int wn = WPW * wave + u;
+        const int wn = proj ? WPW * wave + u : 0;
         const uint16_t* S = wn < Win ? static_cast<const uint16_t*>(a.S_in) + (size_t)(32 * wn) * kD
                                      : static_cast<const uint16_t*>(a.S_out) + (size_t)(32 * (wn - Win)) * kD;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                sb[u][hf][s] = *reinterpret_cast<const uint4*>(S + (size_t)(16 * hf + (lane & 15)) * kD + 32 * s + 8 * (lane >> 4));
+                sb[u][hf][s] = proj ? *reinterpret_cast<const uint4*>(S + (size_t)(16 * hf + (lane & 15)) * kD + 32 * s + 8 * (lane >> 4))
+                                      : make_uint4(0u, 0u, 0u, 0u);
     }
     if (wave == 0) {
         // outlier mask of the KV head (bit c % 32 of word c / 32): the LDS operations of a wave complete
         // in order, so the words are cleared before the entries set their bits
-        if (lane < 4) s_mask[lane] = 0u;
+        if (lane < 4) L.mask[lane] = 0u;
         const int oc = oc_raw & (kD - 1);        // never index outside a row
-        if (has_oc) atomicOr(&s_mask[oc >> 5], 1u << (oc & 31));
+        if (has_oc) atomicOr(&L.mask[oc >> 5], 1u << (oc & 31));
     }
     __syncthreads();
 
@@ -363,15 +369,15 @@ __global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs 
     // one pass per 16 vectors; the first pass is its own copy, so that its staging waits only for the
     // vector loaded before the S tiles (a wait at a join with later passes would wait for all loads)
     auto pass = [&](const int c0, const uint4 xv) {
-        const bool key_pass = APPEND && c0 == 0;
+        const bool key_pass = app && c0 == 0;
         // ---- stage 16 vectors, split at the outlier channels
-        {
-            const uint32_t om = (s_mask[cg >> 2] >> (8 * (cg & 3))) & 0xFFu;
+        if (worker) {
+            const uint32_t om = (L.mask[cg >> 2] >> (8 * (cg & 3))) & 0xFFu;
             uint4 xi, xo;
             float ss_in = 0.f, ss_out = 0.f;
             split_key8(xv, om, xi, xo, ss_in, ss_out);
-            *reinterpret_cast<uint4*>(vin + sv * kVRow + 8 * cg) = xi;
-            *reinterpret_cast<uint4*>(vout + sv * kVRow + 8 * cg) = xo;
+            *reinterpret_cast<uint4*>(L.vin + sv * kVRow + 8 * cg) = xi;
+            *reinterpret_cast<uint4*>(L.vout + sv * kVRow + 8 * cg) = xo;
             if (key_pass || a.estimator) {
                 // squared norms of each vector's two parts: one DPP row of 16 lanes per vector
                 ss_in = row16_sum(ss_in);
@@ -380,56 +386,80 @@ __global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs 
             // the key is vector 0: lanes 0..15 of wave 0
             if (key_pass && tid == 0) reinterpret_cast<uint32_t*>(ap.norms)[(size_t)unit * a.Ncap + ap.pos] = norm_pair(ss_in, ss_out);
             if (a.estimator && cg == 0) {
-                s_qn[sv][0] = sqrtf(ss_in);
-                s_qn[sv][1] = sqrtf(ss_out);
+                L.qn[sv][0] = sqrtf(ss_in);
+                L.qn[sv][1] = sqrtf(ss_out);
             }
         }
         __syncthreads();
 
         // ---- projections: sign word wn = WPW wave + u is the pair of 16-projection tiles 2 wn, 2 wn + 1;
         //      D lane l holds projection 32 wn + 16 hf + l % 16 of vectors 4 (l / 16) + i
+        if (proj) {
 #pragma unroll
-        for (int u = 0; u < WPW; ++u) {
-            const int wn = WPW * wave + u;
-            const bool inl = wn < Win;
-            const uint16_t* vsrc = (inl ? vin : vout) + (lane & 15) * kVRow + 8 * (lane >> 4);
-            uint32_t word = 0;
+            for (int u = 0; u < WPW; ++u) {
+                const int wn = WPW * wave + u;
+                const bool inl = wn < Win;
+                const uint16_t* vsrc = (inl ? L.vin : L.vout) + (lane & 15) * kVRow + 8 * (lane >> 4);
+                uint32_t word = 0;
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                v4f_t acc = v4f_t{0.f, 0.f, 0.f, 0.f};
+                for (int hf = 0; hf < 2; ++hf) {
+                    v4f_t acc = v4f_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(vsrc + 32 * s)),
-                                                                  __builtin_bit_cast(bf16x8_t, sb[u][hf][s]), acc, 0, 0, 0);
-                if (key_pass) word |= ((uint32_t)__builtin_amdgcn_ballot_w64(acc[0] >= 0.f) & 0xFFFFu) << (16 * hf);
-                const int j = (inl ? 32 * wn : a.m + 32 * (wn - Win)) + 16 * hf + (lane & 15);
-                const float cs = inl ? c_in : c_out;
+                    for (int s = 0; s < 4; ++s)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(vsrc + 32 * s)),
+                                                                      __builtin_bit_cast(bf16x8_t, sb[u][hf][s]), acc, 0, 0, 0);
+                    if (key_pass) word |= ((uint32_t)__builtin_amdgcn_ballot_w64(acc[0] >= 0.f) & 0xFFFFu) << (16 * hf);
+                    const int j = (inl ? 32 * wn : a.m + 32 * (wn - Win)) + 16 * hf + (lane & 15);
+                    const float cs = inl ? c_in : c_out;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int vec = 4 * (lane >> 4) + i;
-                    // two-sided estimator: the projection's sign times the norm of the query part
-                    const float t = a.estimator ? s_qn[vec][inl ? 0 : 1] * (inl ? c2_in : c2_out) : 0.f;
-                    xs[vec * kXPitch + j] = a.estimator ? (acc[i] >= 0.f ? t : -t) : acc[i] * cs;
+                    for (int i = 0; i < 4; ++i) {
+                        const int vec = 4 * (lane >> 4) + i;
+                        // two-sided estimator: the projection's sign times the norm of the query part
+                        const float t = a.estimator ? L.qn[vec][inl ? 0 : 1] * (inl ? c2_in : c2_out) : 0.f;
+                        L.xs[vec * kXPitch + j] = a.estimator ? (acc[i] >= 0.f ? t : -t) : acc[i] * cs;
+                    }
                 }
+                if (key_pass && lane == 0) ap.bits[((size_t)unit * a.Ncap + ap.pos) * W + bits_slot(wn, Win, Wout)] = word;
             }
-            if (key_pass && lane == 0) ap.bits[((size_t)unit * a.Ncap + ap.pos) * W + bits_slot(wn, Win, Wout)] = word;
         }
         __syncthreads();
 
         // ---- operands of this pass's query heads: wave w serves columns w, w + 4, w + 8, w + 12, one
         //      row of 16 lanes each
-        {
+        if (worker) {
             const int v = wave + 4 * (lane >> 4);
             const int col = c0 + v;
-            const bool active = col < ncol && !(APPEND && col == 0);
-            const int64_t hq = active ? head0 + col - (APPEND ? 1 : 0) : 0;
-            query_operand_slices(xs + v * kXPitch, win4, wout4, lane & 15, active,
-                                 reinterpret_cast<uint32_t*>(a.sq) + hq * (128 * (win4 + wout4)), a.qconst + hq * 4);
+            const bool active = col < ncol && !(app && col == 0);
+            const int hl = active ? col - (app ? 1 : 0) : 0;
+            query_operand_slices(L.xs + v * kXPitch, win4, wout4, lane & 15, active, sq_dst + hl * (128 * (win4 + wout4)),
+                                 qc_dst + hl * 4);
         }
         __syncthreads();
     };
     pass(0, xv);
     for (int c0 = 16; c0 < ncol; c0 += 16) pass(c0, load_vector(c0 + sv));
+}
+
+// bf16: one workgroup per (sequence, KV head) projects the KV head's g query heads (and, for a decode
+// step, the new key) into the workspace; for a decode step, workgroups of their own append the new
+// values, one (sequence, KV head) per wave (their atomic round trips overlap the projections).
+template <int WPW, bool APPEND>
+__global__ __launch_bounds__(256) void prologue_kernel(DecodeArgs a, AppendArgs ap) {
+    __shared__ ProjLds L;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nunits = a.B * a.Hkv;
+    if (APPEND && (int)blockIdx.x >= nunits) {
+        const int vunit = 4 * ((int)blockIdx.x - nunits) + wave;
+        if (vunit >= nunits) return;
+        append_value(a, ap, vunit, tid & 63);
+        return;
+    }
+    const int unit = blockIdx.x;                 // b * Hkv + h
+    const int b = unit / a.Hkv, h = unit - b * a.Hkv;
+    const int64_t head0 = (int64_t)b * a.Hq + (int64_t)h * a.g;
+    project_unit<WPW, 4>(a, ap, unit, APPEND, L, reinterpret_cast<uint32_t*>(a.sq) + head0 * (128 * ((a.m + a.m_out) >> 7)),
+                      a.qconst + head0 * 4);
 }
 
 // ---------------------------------------------------------------------------- decode
@@ -934,19 +964,32 @@ __device__ __forceinline__ void store_pieces(uint32_t addr, const uint32_t (&k)[
         : "memory");
 }
 
-template <int WIN4, int WOUT4, bool DBG>
-__global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs a, int groups, int hgroups) {
+// FUSED: the workgroup projects its query heads itself (the KV head's g <= 8 heads: one head group),
+// into LDS, and the workgroup whose chunk holds the new token of a decode step (ap.pos; -1 for none)
+// appends it to the cache first; no projection launch precedes the decode.
+template <int WIN4, int WOUT4, bool DBG, bool FUSED>
+__global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs a, AppendArgs ap, int groups, int hgroups) {
     constexpr int R = 2, NB = 2;
     constexpr int W4 = WIN4 + WOUT4;
     constexpr int WB = 4 * W4;
     constexpr int HPG = 4 * R;
     static_assert(W4 == 1 || W4 == 4, "a sign quarter-row of 4 or 16 bytes: one LDS-destination load");
+    // projection phase (FUSED): ProjLds, then the query operands (HPG x 128 W4 words) and the per-head
+    // constants (HPG x 4); with 16-byte sign quarter-rows it lies over the sign buffers, which the
+    // block loads fill only after it
+    constexpr bool PJ_OVER = W4 == 4;
+    constexpr int PJ_BYTES = (int)sizeof(ProjLds) + HPG * 128 * W4 * 4 + HPG * 4 * 4;
+    __shared__ __attribute__((aligned(16))) uint8_t s_pj[(FUSED && !PJ_OVER) ? PJ_BYTES : 16];
     // separate arrays, so that the compiler's own wait analysis can tell the load destinations apart
     __shared__ __attribute__((aligned(16))) uint8_t s_wtile[kM8Waves][2][16 * kWPitch];   // weight pieces
     __shared__ __attribute__((aligned(16))) uint32_t s_sgn[kM8Waves][8][64][W4];         // sign quarter-rows
     __shared__ __attribute__((aligned(16))) uint32_t s_cod[kM8Waves][4][64][4];          // code words
     __shared__ __attribute__((aligned(16))) uint32_t s_nm[kM8Waves][2][2][kMBlock];      // [buffer][norm, meta][token]
     __shared__ float s_red_m[kM8Waves][8], s_red_l[kM8Waves][8], s_red_mn[kM8Waves][8];
+    static_assert(!FUSED || !PJ_OVER || sizeof(s_sgn) >= PJ_BYTES, "the projection phase fits the sign buffers");
+    uint8_t* const pj = PJ_OVER ? reinterpret_cast<uint8_t*>(&s_sgn[0][0][0][0]) : s_pj;
+    uint32_t* const s_sq = reinterpret_cast<uint32_t*>(pj + sizeof(ProjLds));
+    float* const s_qc = reinterpret_cast<float*>(pj + sizeof(ProjLds) + HPG * 128 * W4 * 4);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -967,6 +1010,19 @@ __global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs 
     const int t_begin = (int)((int64_t)split * a.chunk);
     const int t_end = (int)min(a.N, (int64_t)t_begin + a.chunk);
     const int head0 = b * a.Hq + h * a.g;
+    if constexpr (FUSED) {
+        // wave 4 appends the new value while waves 0..3 project (the key first, when this chunk holds it)
+        const bool app = ap.pos >= t_begin && ap.pos < t_end;
+        if (app && wave == 4) append_value(a, ap, unit, lane);
+        // eight projecting waves for 16 sign words per token (half the S tiles per wave), four for 4
+        project_unit<W4 == 4 ? 2 : 1, W4 == 4 ? 8 : 4>(a, ap, unit, app, *reinterpret_cast<ProjLds*>(pj), s_sq, s_qc);
+        // the appended row is in memory before any load of this workgroup's blocks
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+    const uint8_t* sq_base = FUSED ? reinterpret_cast<const uint8_t*>(s_sq)
+                                   : reinterpret_cast<const uint8_t*>(a.sq) + (size_t)head0 * (128 * WB);
+    const float* qc_base = FUSED ? s_qc : a.qconst + (size_t)head0 * 4;
 
     // ---- score operands: A row t of both instructions is (head t / 2, slot t % 2) of the eight heads;
     //      instruction pp carries piece 2 pp + slot, and both accumulate into the same rows, so D row
@@ -983,8 +1039,7 @@ __global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs 
         const int piece = 2 * pp + aslot;
         sc[pp] = 0x7F7F7F7F;
         if (qa_head < a.g) {
-            const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.sq) +
-                                                              (size_t)(head0 + qa_head) * (128 * WB));
+            const uint4* src = reinterpret_cast<const uint4*>(sq_base + (size_t)qa_head * (128 * WB));
             uint32_t bytes = 0u;
 #pragma unroll
             for (int kb = 0; kb < W4; ++kb) {
@@ -1004,10 +1059,12 @@ __global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs 
     for (int j = 0; j < 2; ++j) {
         const int dhead = HPG * hg + 2 * hh + j;
         const bool ok = dhead < a.g;
-        cin[j] = ok ? a.qconst[(size_t)(head0 + dhead) * 4] : 0.f;
-        cout[j] = ok ? a.qconst[(size_t)(head0 + dhead) * 4 + 1] : 0.f;
+        cin[j] = ok ? qc_base[dhead * 4] : 0.f;
+        cout[j] = ok ? qc_base[dhead * 4 + 1] : 0.f;
         sdbg[j] = (DBG && ok) ? a.scores_dbg + (size_t)(head0 + dhead) * a.N : nullptr;
     }
+    // every wave has its operands in registers before any block load writes over the projection phase
+    if constexpr (FUSED) __syncthreads();
     // the lane group whose score heads include value head 4 rg + hh, as a ds_bpermute byte address
     const int perm_addr[2] = {4 * (16 * (hh >> 1) + t), 4 * (16 * (2 + (hh >> 1)) + t)};
 
@@ -1292,19 +1349,31 @@ __global__ __launch_bounds__(kM8Threads, 1) void decode_mfma8_kernel(DecodeArgs 
 }
 
 template <int WIN4, int WOUT4, int R, int NB>
-hipError_t launch_decode_mfma_r(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_decode_mfma_r(const DecodeArgs& a, const AppendArgs* ap, hipStream_t s) {
     const int hgroups = (a.g + 4 * R - 1) / (4 * R);
     const int groups = a.B * a.Hkv * a.nsplit;
     const int slots = (groups + 7) / 8;
     const unsigned nblocks = (unsigned)slots * 8u * (unsigned)hgroups;
     timer_begin(TK_DECODE, s);
     if constexpr (R == 2 && NB == 2 && (WIN4 + WOUT4 == 4 || WIN4 + WOUT4 == 1)) {
-        // eight waves (two per SIMD), block data through LDS
-        if (a.scores_dbg)
-            hipLaunchKernelGGL((decode_mfma8_kernel<WIN4, WOUT4, true>), dim3(nblocks), dim3(kM8Threads), 0, s, a, groups, hgroups);
+        // eight waves (two per SIMD), block data through LDS; with ap, the projection (and the append of
+        // ap->pos, if >= 0) inside the kernel
+        const AppendArgs apv = ap ? *ap : AppendArgs{};
+        if (ap) {
+            if (a.scores_dbg)
+                hipLaunchKernelGGL((decode_mfma8_kernel<WIN4, WOUT4, true, true>), dim3(nblocks), dim3(kM8Threads), 0, s, a, apv, groups,
+                                   hgroups);
+            else
+                hipLaunchKernelGGL((decode_mfma8_kernel<WIN4, WOUT4, false, true>), dim3(nblocks), dim3(kM8Threads), 0, s, a, apv, groups,
+                                   hgroups);
+        } else if (a.scores_dbg)
+            hipLaunchKernelGGL((decode_mfma8_kernel<WIN4, WOUT4, true, false>), dim3(nblocks), dim3(kM8Threads), 0, s, a, apv, groups,
+                               hgroups);
         else
-            hipLaunchKernelGGL((decode_mfma8_kernel<WIN4, WOUT4, false>), dim3(nblocks), dim3(kM8Threads), 0, s, a, groups, hgroups);
+            hipLaunchKernelGGL((decode_mfma8_kernel<WIN4, WOUT4, false, false>), dim3(nblocks), dim3(kM8Threads), 0, s, a, apv, groups,
+                               hgroups);
     } else {
+        if (ap) return hipErrorInvalidValue;     // only the eight-wave kernel projects in-kernel
         if (a.scores_dbg)
             hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, R, true, NB>), dim3(nblocks), dim3(kMThreads), 0, s, a, groups, hgroups);
         else
@@ -1315,11 +1384,11 @@ hipError_t launch_decode_mfma_r(const DecodeArgs& a, hipStream_t s) {
 }
 
 template <int WIN4, int WOUT4>
-hipError_t launch_decode_mfma_t(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_decode_mfma_t(const DecodeArgs& a, const AppendArgs* ap, hipStream_t s) {
     const bool r2 = decode_mfma_rowgroups(a.g) == 2;
-    if (a.nbits == 4) return r2 ? launch_decode_mfma_r<WIN4, WOUT4, 2, 4>(a, s) : launch_decode_mfma_r<WIN4, WOUT4, 1, 4>(a, s);
-    if (a.nbits == 3) return r2 ? launch_decode_mfma_r<WIN4, WOUT4, 2, 3>(a, s) : launch_decode_mfma_r<WIN4, WOUT4, 1, 3>(a, s);
-    return r2 ? launch_decode_mfma_r<WIN4, WOUT4, 2, 2>(a, s) : launch_decode_mfma_r<WIN4, WOUT4, 1, 2>(a, s);
+    if (a.nbits == 4) return r2 ? launch_decode_mfma_r<WIN4, WOUT4, 2, 4>(a, ap, s) : launch_decode_mfma_r<WIN4, WOUT4, 1, 4>(a, ap, s);
+    if (a.nbits == 3) return r2 ? launch_decode_mfma_r<WIN4, WOUT4, 2, 3>(a, ap, s) : launch_decode_mfma_r<WIN4, WOUT4, 1, 3>(a, ap, s);
+    return r2 ? launch_decode_mfma_r<WIN4, WOUT4, 2, 2>(a, ap, s) : launch_decode_mfma_r<WIN4, WOUT4, 1, 2>(a, ap, s);
 }
 
 template <bool APPEND>
@@ -1334,20 +1403,35 @@ hipError_t launch_prologue(const DecodeArgs& a, const AppendArgs& ap, hipStream_
     return hipGetLastError();
 }
 
-hipError_t launch_decode_kernel(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_decode_kernel(const DecodeArgs& a, const AppendArgs* ap, hipStream_t s) {
     const int win4 = a.m >> 7, wout4 = a.m_out >> 7;
-    if (win4 == 1 && wout4 == 0) return launch_decode_mfma_t<1, 0>(a, s);
-    if (win4 == 1 && wout4 == 1) return launch_decode_mfma_t<1, 1>(a, s);
-    if (win4 == 2 && wout4 == 0) return launch_decode_mfma_t<2, 0>(a, s);
-    if (win4 == 2 && wout4 == 2) return launch_decode_mfma_t<2, 2>(a, s);
-    if (win4 == 4 && wout4 == 0) return launch_decode_mfma_t<4, 0>(a, s);
+    if (win4 == 1 && wout4 == 0) return launch_decode_mfma_t<1, 0>(a, ap, s);
+    if (win4 == 1 && wout4 == 1) return launch_decode_mfma_t<1, 1>(a, ap, s);
+    if (win4 == 2 && wout4 == 0) return launch_decode_mfma_t<2, 0>(a, ap, s);
+    if (win4 == 2 && wout4 == 2) return launch_decode_mfma_t<2, 2>(a, ap, s);
+    if (win4 == 4 && wout4 == 0) return launch_decode_mfma_t<4, 0>(a, ap, s);
     return hipErrorInvalidValue;
+}
+
+// The eight-wave kernel serves 5 to 8 query heads per KV head (one head group) with 2-bit codes and a
+// sign quarter-row of 4 or 16 bytes; for those shapes it projects the queries (and appends a decode
+// step's token) itself.
+bool decode_fuses_projection(const DecodeArgs& a) {
+    const int w4 = (a.m + a.m_out) >> 7;
+    return a.g > 4 && a.g <= 8 && a.nbits == 2 && (w4 == 1 || w4 == 4);
 }
 
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int qdt, hipStream_t s) {
     const int win4 = a.m >> 7, wout4 = a.m_out >> 7;
+    if (qdt == 0 && decode_fuses_projection(a)) {
+        AppendArgs none{};
+        none.pos = -1;
+        hipError_t e = launch_decode_kernel(a, &none, s);
+        if (e != hipSuccess || a.nsplit == 1) return e;
+        return launch_combine(a, s);
+    }
     timer_begin(TK_QPROJ, s);
     if (qdt == 0)
         (void)launch_prologue<false>(a, AppendArgs{}, s);
@@ -1356,17 +1440,22 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int qdt, hipStream_t s) {
     timer_end(TK_QPROJ, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_decode_kernel(a, s);
+    e = launch_decode_kernel(a, nullptr, s);
     if (e != hipSuccess || a.nsplit == 1) return e;
     return launch_combine(a, s);
 }
 
 hipError_t launch_decode_step_mfma(const DecodeArgs& a, const AppendArgs& ap, hipStream_t s) {
+    if (decode_fuses_projection(a)) {
+        hipError_t e = launch_decode_kernel(a, &ap, s);
+        if (e != hipSuccess || a.nsplit == 1) return e;
+        return launch_combine(a, s);
+    }
     timer_begin(TK_STEP, s);
     hipError_t e = launch_prologue<true>(a, ap, s);
     timer_end(TK_STEP, s);
     if (e != hipSuccess) return e;
-    e = launch_decode_kernel(a, s);
+    e = launch_decode_kernel(a, nullptr, s);
     if (e != hipSuccess || a.nsplit == 1) return e;
     return launch_combine(a, s);
 }
