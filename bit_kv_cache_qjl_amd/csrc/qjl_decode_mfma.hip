@@ -561,11 +561,20 @@ __device__ __forceinline__ void transpose_code_pieces(uint32_t (&cx)[8][2]) {
 // R = 1: one workgroup serves 4 query heads of a KV head; R = 2: 8 query heads as two row groups of
 // the same instructions' B operands (the sign and code planes are built once for both).
 // Two workgroups per CU for 4 query heads and 2-bit codes; one (the whole register file) otherwise.
-template <int WIN4, int WOUT4, int R, bool DBG, int NB>
-__global__ __launch_bounds__(kMThreads, (R == 1 && NB == 2) ? 2 : 1) void decode_mfma_kernel(DecodeArgs a, int groups, int hgroups) {
+// FUSED: as in the eight-wave kernel, the workgroup projects the KV head's query heads (g <= HPG: one
+// head group) into LDS, and the workgroup whose chunk holds the new token (ap.pos; -1 for none)
+// appends it first; no projection launch precedes the decode.
+template <int WIN4, int WOUT4, int R, bool DBG, int NB, bool FUSED>
+__global__ __launch_bounds__(kMThreads, (R == 1 && NB == 2) ? 2 : 1) void decode_mfma_kernel(DecodeArgs a, AppendArgs ap, int groups,
+                                                                                             int hgroups) {
     constexpr int W4 = WIN4 + WOUT4;             // instructions (K blocks of 128 sign positions) per token
     constexpr int WB = 4 * W4;                   // sign words per token
     constexpr int HPG = 4 * R;                   // query heads per workgroup
+    // projection phase (FUSED): ProjLds, the query operands (HPG x 128 W4 words), the per-head constants
+    constexpr int PJ_BYTES = (int)sizeof(ProjLds) + HPG * 128 * W4 * 4 + HPG * 4 * 4;
+    __shared__ __attribute__((aligned(16))) uint8_t pj[FUSED ? PJ_BYTES : 16];
+    uint32_t* const s_sq = reinterpret_cast<uint32_t*>(pj + sizeof(ProjLds));
+    float* const s_qc = reinterpret_cast<float*>(pj + sizeof(ProjLds) + HPG * 128 * W4 * 4);
     __shared__ __attribute__((aligned(16))) uint8_t wtile[kMWaves][R][16 * kWPitch];   // weight pieces
     __shared__ __attribute__((aligned(16))) uint32_t nmt[kMWaves][2 * kMBlock];        // (norm, meta) per token
     __shared__ float red_m[kMWaves][HPG], red_l[kMWaves][HPG], red_mn[kMWaves][HPG];
@@ -591,6 +600,18 @@ __global__ __launch_bounds__(kMThreads, (R == 1 && NB == 2) ? 2 : 1) void decode
     const int t_begin = (int)((int64_t)split * a.chunk);
     const int t_end = (int)min(a.N, (int64_t)t_begin + a.chunk);
     const int head0 = b * a.Hq + h * a.g;        // (b, first query head of KV head h)
+    if constexpr (FUSED) {
+        // wave 3 appends the new value first when this chunk holds the new token; all four waves project
+        const bool app = ap.pos >= t_begin && ap.pos < t_end;
+        if (app && wave == 3) append_value(a, ap, unit, lane);
+        project_unit<W4, 4>(a, ap, unit, app, *reinterpret_cast<ProjLds*>(pj), s_sq, s_qc);
+        // the appended row is in memory before any load of this workgroup's blocks
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+    const uint8_t* sq_base = FUSED ? reinterpret_cast<const uint8_t*>(s_sq)
+                                   : reinterpret_cast<const uint8_t*>(a.sq) + (size_t)head0 * (128 * WB);
+    const float* qc_base = FUSED ? s_qc : a.qconst + (size_t)head0 * 4;
 
     // ---- score A operands and scales: this lane's A row in row group rg is (head 4 rg + rh, piece pc),
     //      K slice hh
@@ -602,8 +623,7 @@ __global__ __launch_bounds__(kMThreads, (R == 1 && NB == 2) ? 2 : 1) void decode
         const int qa_head = HPG * hg + 4 * rg + rh;
         sc[rg] = 0x7F7F7F7F;
         if (qa_head < a.g) {
-            const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.sq) +
-                                                              (size_t)(head0 + qa_head) * (128 * WB));
+            const uint4* src = reinterpret_cast<const uint4*>(sq_base + (size_t)qa_head * (128 * WB));
             uint32_t bytes = 0u;
 #pragma unroll
             for (int kb = 0; kb < W4; ++kb) {
@@ -624,8 +644,8 @@ __global__ __launch_bounds__(kMThreads, (R == 1 && NB == 2) ? 2 : 1) void decode
     for (int rg = 0; rg < R; ++rg) {
         const int dhead = HPG * hg + 4 * rg + hh;
         const bool ok = dhead < a.g;
-        cin[rg] = ok ? a.qconst[(size_t)(head0 + dhead) * 4] : 0.f;
-        cout[rg] = ok ? a.qconst[(size_t)(head0 + dhead) * 4 + 1] : 0.f;
+        cin[rg] = ok ? qc_base[dhead * 4] : 0.f;
+        cout[rg] = ok ? qc_base[dhead * 4 + 1] : 0.f;
         sdbg[rg] = (DBG && ok) ? a.scores_dbg + (size_t)(head0 + dhead) * a.N : nullptr;
     }
 
@@ -1373,11 +1393,20 @@ hipError_t launch_decode_mfma_r(const DecodeArgs& a, const AppendArgs* ap, hipSt
             hipLaunchKernelGGL((decode_mfma8_kernel<WIN4, WOUT4, false, false>), dim3(nblocks), dim3(kM8Threads), 0, s, a, apv, groups,
                                hgroups);
     } else {
-        if (ap) return hipErrorInvalidValue;     // only the eight-wave kernel projects in-kernel
-        if (a.scores_dbg)
-            hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, R, true, NB>), dim3(nblocks), dim3(kMThreads), 0, s, a, groups, hgroups);
+        const AppendArgs apv = ap ? *ap : AppendArgs{};
+        if (ap) {
+            if (a.scores_dbg)
+                hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, R, true, NB, true>), dim3(nblocks), dim3(kMThreads), 0, s, a, apv,
+                                   groups, hgroups);
+            else
+                hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, R, false, NB, true>), dim3(nblocks), dim3(kMThreads), 0, s, a, apv,
+                                   groups, hgroups);
+        } else if (a.scores_dbg)
+            hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, R, true, NB, false>), dim3(nblocks), dim3(kMThreads), 0, s, a, apv,
+                               groups, hgroups);
         else
-            hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, R, false, NB>), dim3(nblocks), dim3(kMThreads), 0, s, a, groups, hgroups);
+            hipLaunchKernelGGL((decode_mfma_kernel<WIN4, WOUT4, R, false, NB, false>), dim3(nblocks), dim3(kMThreads), 0, s, a, apv,
+                               groups, hgroups);
     }
     timer_end(TK_DECODE, s);
     return hipGetLastError();
@@ -1413,13 +1442,9 @@ hipError_t launch_decode_kernel(const DecodeArgs& a, const AppendArgs* ap, hipSt
     return hipErrorInvalidValue;
 }
 
-// The eight-wave kernel serves 5 to 8 query heads per KV head (one head group) with 2-bit codes and a
-// sign quarter-row of 4 or 16 bytes; for those shapes it projects the queries (and appends a decode
-// step's token) itself.
-bool decode_fuses_projection(const DecodeArgs& a) {
-    const int w4 = (a.m + a.m_out) >> 7;
-    return a.g > 4 && a.g <= 8 && a.nbits == 2 && (w4 == 1 || w4 == 4);
-}
+// With at most 8 query heads per KV head a workgroup serves all of them (one head group), and the
+// decode kernels project the queries (and append a decode step's token) themselves.
+bool decode_fuses_projection(const DecodeArgs& a) { return a.g <= 8; }
 
 }  // namespace
 
