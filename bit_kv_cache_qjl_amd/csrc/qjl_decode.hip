@@ -375,24 +375,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 // so a thread's loads do not wait on each other or on a barrier and the merge costs one round trip
 // to memory.  A separate launch: merging inside the decode kernel would need a device-scope
 // release/acquire per workgroup, which on MI355X writes back and invalidates the XCD's whole L2.
+// One chunk's partials into the running (M, L, O); a chunk with no valid token (mi = -inf) leaves them
+// as they are.  Branch-free, so that the loads of every chunk can be in flight before the first merge.
+__device__ __forceinline__ void merge_chunk(float mi, float li, float oi, float& M, float& L, float& O) {
+    const bool skip = mi == -INFINITY;
+    const float Mn = fmaxf(M, mi);
+    const float keep = exp2f(M - Mn);            // 0 while M is still -inf
+    const float f = exp2f(mi - Mn);
+    L = skip ? L : fmaf(f, li, L * keep);
+    O = skip ? O : fmaf(f, oi, O * keep);
+    M = skip ? M : Mn;
+}
+
 __global__ __launch_bounds__(kD) void combine_kernel(DecodeArgs a) {
+    constexpr int kFew = 16;                     // chunks whose partials are all requested before the merge
     const int c = threadIdx.x;
     const int bhq = blockIdx.x;
     const int ns = a.nsplit;
     const float* src = a.part + (size_t)bhq * ns * (kD + 2);
     float M = -INFINITY, L = 0.f, O = 0.f;
+    if (ns <= kFew) {
+        // one round trip: every chunk's (max, sum, value) is loaded first, then merged in chunk order
+        float mi[kFew], li[kFew], oi[kFew];
+#pragma unroll
+        for (int i = 0; i < kFew; ++i) {
+            const float* pi = src + (size_t)(i < ns ? i : ns - 1) * (kD + 2);   // past ns: a repeat, skipped
+            const float m_ld = pi[0];
+            mi[i] = i < ns ? m_ld : -INFINITY;
+            li[i] = pi[1];
+            oi[i] = pi[2 + c];
+        }
+#pragma unroll
+        for (int i = 0; i < kFew; ++i) merge_chunk(mi[i], li[i], oi[i], M, L, O);
+    } else {
 #pragma unroll 4
-    for (int i = 0; i < ns; ++i) {
-        const float mi = src[(size_t)i * (kD + 2)];
-        const float li = src[(size_t)i * (kD + 2) + 1];
-        const float oi = src[(size_t)i * (kD + 2) + 2 + c];
-        if (mi == -INFINITY) continue;           // a chunk with no valid token
-        const float Mn = fmaxf(M, mi);
-        const float keep = exp2f(M - Mn);        // 0 while M is still -inf
-        const float f = exp2f(mi - Mn);
-        L = fmaf(f, li, L * keep);
-        O = fmaf(f, oi, O * keep);
-        M = Mn;
+        for (int i = 0; i < ns; ++i)
+            merge_chunk(src[(size_t)i * (kD + 2)], src[(size_t)i * (kD + 2) + 1], src[(size_t)i * (kD + 2) + 2 + c], M, L, O);
     }
     a.out[(size_t)bhq * kD + c] = L > 0.f ? O / L : 0.f;
 }
