@@ -185,6 +185,32 @@ def test_decode_step_split_counts(nsplit):
                  what=f"nsplit={nsplit}")
 
 
+@pytest.mark.parametrize("name,N,nsplit", [
+    # chunks are multiples of 512 tokens
+    ("llama31_70b_gqa", 513, 2),    # the new token is the only token of chunk 1
+    ("llama31_70b_gqa", 1024, 2),   # the new token closes chunk 1
+    ("llama3_gqa", 1025, 3),        # the new token is the only token of chunk 2
+    ("llama3_gqa", 1024, 3),        # the new token closes chunk 1, chunk 2 is empty
+])
+def test_decode_step_new_token_at_chunk_edges(name, N, nsplit):
+    """The decode kernel's own append: the workgroup whose chunk holds position N - 1 appends the new
+    token before it reads the cache; the token at either end of a chunk, alone in one, or next to an
+    empty chunk gives the oracle's row and output."""
+    w = CASES[name].scaled(N=N)
+    Ncap = N + 3
+    log(f"[decode_step chunk edge] {name} N={N} nsplit={nsplit}")
+    x = inputs(w)
+    kq = oracle.quantize_keys(x["K"], x["S_in"], x["S_out"], x["oidx"])
+    vq = oracle.quantize_values(x["V"], w.nbits)
+    cache = dev_cache(w, kq, vq, N - 1, Ncap)
+    scores = torch.full((w.B, w.Hq, N), float("nan"), dtype=torch.float32, device="cuda")
+    out = run_step(w, x, cache, N, scores=scores, nsplit=nsplit)
+    check_row(w, cache, kq, vq, N - 1, Ncap, f"{name} N={N} nsplit={nsplit}")
+    units = [(b, hq) for b in range(w.B) for hq in range(w.Hq)]
+    check_decode(w, x["Q"], x["S_in"], x["S_out"], x["oidx"], device_cache_np(cache, w, N), N, out,
+                 scores.cpu().numpy(), units, what=f"{name} N={N} nsplit={nsplit}")
+
+
 def test_decode_step_consecutive_steps_share_workspace():
     """Three steps in a row (N, N+1, N+2) with one workspace: nothing in the workspace carries over
     from one step to the next (every step rewrites the query operands and the chunk partials it
