@@ -103,7 +103,9 @@ def test_eight_wave_block_loop_waits_only_where_written(decode_asm):
     (vmcnt(0)) inserted before an LDS access it sees would also wait for the next block's code loads,
     issued just before."""
     asm = decode_asm
-    for sym in ("_ZN3qjl12_GLOBAL__N_119decode_mfma8_kernelILi2ELi2ELb0E", "_ZN3qjl12_GLOBAL__N_119decode_mfma8_kernelILi4ELi0ELb0E"):
+    # both sketch widths, with the query projection in the kernel (Lb1E) and after a projection launch (Lb0E)
+    for sym in ("_ZN3qjl12_GLOBAL__N_119decode_mfma8_kernelILi2ELi2ELb0ELb1E", "_ZN3qjl12_GLOBAL__N_119decode_mfma8_kernelILi4ELi0ELb0ELb1E",
+                "_ZN3qjl12_GLOBAL__N_119decode_mfma8_kernelILi2ELi2ELb0ELb0E", "_ZN3qjl12_GLOBAL__N_119decode_mfma8_kernelILi4ELi0ELb0ELb0E"):
         loop = block_loop(_kernel_asm(asm, sym), "v_mfma_scale_f32_16x16x128_f8f6f4")
         assert "v_mfma_scale_f32_16x16x128_f8f6f4" in loop and "lds" in loop, "not the block loop"
         waits = re.findall(r"s_waitcnt vmcnt\((\d+)\)", loop)
