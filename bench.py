@@ -79,6 +79,7 @@ def measured_traffic(workload: str):
 KERNELS = ("decode", "append_project", "quantize_keys", "quantize_values", "query_project", "combine")
 CALIB_BYTES = 1 << 30               # plain copy kernel used to scale FETCH_SIZE / WRITE_SIZE
 MALL_BYTES = 256 << 20              # MI355X last-level (Infinity) cache
+QUANT_CALLS = 25                    # back-to-back calls per prefill quantize figure (after 8 warm-up calls)
 
 
 def _counter_rows(path: str):
@@ -456,8 +457,10 @@ def bench_decode(qjl, torch, w: si.Workload, args, path: str) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # decode steps: the first tens of back-to-back launches ride the GPU's clock transient (they slow down,
+    # then settle), so the default warm-up runs past it and the timed steps see the sustained rate
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=HEADLINE, choices=list(DECODE_WORKLOADS))
     ap.add_argument("--extra-workloads", default=None,
                     help="comma-separated decode workloads reported beside the headline (default: the other two; "
@@ -532,7 +535,7 @@ def main() -> int:
                                                                      "kernel_ms_per_launch", "step_timing")}
     if not args.no_quantize:
         log("bench: prefill quantize stream")
-        result["quantize"] = bench_quantize(qjl, torch, max(5, args.steps // 2))
+        result["quantize"] = bench_quantize(qjl, torch, QUANT_CALLS)
     if args.cpu_budget > 0:
         log(f"bench: oracle on the host (~{args.cpu_budget:.0f} s), then estimator quality")
         base, quality = cpu_baseline(workload(args.workload), args.cpu_budget)
