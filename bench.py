@@ -79,7 +79,9 @@ def measured_traffic(workload: str):
 KERNELS = ("decode", "append_project", "quantize_keys", "quantize_values", "query_project", "combine")
 CALIB_BYTES = 1 << 30               # plain copy kernel used to scale FETCH_SIZE / WRITE_SIZE
 MALL_BYTES = 256 << 20              # MI355X last-level (Infinity) cache
-QUANT_CALLS = 25                    # back-to-back calls per prefill quantize figure (after 8 warm-up calls)
+QUANT_CALLS = 25                    # back-to-back calls per prefill quantize figure
+QUANT_WARM_S = 0.040                # each quantize stream first runs this long on its own kernel (>= 8 calls):
+                                    # its first tens of launches ride the GPU's clock transient
 
 
 def _counter_rows(path: str):
@@ -251,6 +253,18 @@ def _region_ms(torch, run_one, steps: int) -> tuple:
     return e0.elapsed_time(e1) / steps, wall
 
 
+def _warm(torch, run_one, min_calls: int) -> int:
+    """Back-to-back calls of one stream until QUANT_WARM_S of its work has run (at least min_calls)."""
+    torch.cuda.synchronize()
+    t0, n = time.perf_counter(), 0
+    while n < min_calls or time.perf_counter() - t0 < QUANT_WARM_S:
+        for _ in range(8):
+            run_one()
+        n += 8
+        torch.cuda.synchronize()
+    return n
+
+
 def bench_quantize(qjl, torch, steps: int) -> dict:
     """Prefill quantize stream: 65536 tokens x 8 KV heads, m = m_out = 512 (keys), 2-bit values.  Each
     call takes the next of several input and output copies, so that no call finds its inputs (134 MB
@@ -272,8 +286,7 @@ def bench_quantize(qjl, torch, steps: int) -> dict:
         i = turn[0] % copies
         turn[0] += 1
         qjl.quantize_keys(Ks[i], Si, So, od, caches[i].bits, caches[i].norms)
-    for _ in range(2 * copies):
-        keys_once()
+    _warm(torch, keys_once, 2 * copies)
     kern_ms, wall_ms = _region_ms(torch, keys_once, steps)
     kern_s = kern_ms / 1e3
     # outlier-channel selection over the same keys (one read of K, two launches)
@@ -284,9 +297,7 @@ def bench_quantize(qjl, torch, steps: int) -> dict:
         i = turn[0] % copies
         turn[0] += 1
         qjl.select_outliers(Ks[i], w.n_out, sel, workspace=ws)
-    for _ in range(2 * copies):
-        select_once()
-    torch.cuda.synchronize()
+    _warm(torch, select_once, 2 * copies)
     sel_s = _region_ms(torch, select_once, steps)[0] / 1e3
     sel_bytes = float(in_bytes)
     del Ks, K0
@@ -298,9 +309,7 @@ def bench_quantize(qjl, torch, steps: int) -> dict:
         i = turn[0] % copies
         turn[0] += 1
         qjl.quantize_values(Vs[i], w.nbits, caches[i].codes, caches[i].meta)
-    for _ in range(2 * copies):
-        values_once()
-    torch.cuda.synchronize()
+    _warm(torch, values_once, 2 * copies)
     val_s = _region_ms(torch, values_once, steps)[0] / 1e3
     del Vs, V0
     # per token and KV head: d bf16 values read, d b / 8 code bytes and the fp16 (min, step) pair written
