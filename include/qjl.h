@@ -224,8 +224,10 @@ int qjl_decode_attention(const void* Q, int qdt, int B, int Hq, int Hkv, int d, 
  * fly before the step's query attends to it, as the QJL summary describes for generated tokens,
  * "Approach"; the cache then holds the same bits, norms, codes and meta as after the separate calls).
  * On the matrix-core path (dt = QJL_BF16, 2-, 3- or 4-bit values, (m, m_out) in {(128, 0), (128, 128),
- * (256, 0), (256, 256), (512, 0)}) the appends and the query projections run in one launch before the
- * decode kernel; otherwise the three operations are enqueued one after the other.
+ * (256, 0), (256, 256), (512, 0)}) the decode kernel itself appends the token and projects the queries
+ * when a KV head serves at most 8 query heads (one launch, plus the chunk merge when the context is
+ * split), and one launch does the appends and projections before the decode kernel when it serves more;
+ * otherwise the three operations are enqueued one after the other.
  *   Q           [B][Hq][d] contiguous, dtype dt.
  *   K_new       new keys, element (b, h, c) at K_new[b*sK_b + h*sK_h + c] (the model layout of one
  *               token: [B][1][Hkv][d] with its strides), dtype dt; V_new likewise with (sV_b, sV_h).
@@ -304,7 +306,8 @@ const char* qjl_last_error(void);
 /*
  * Kernel timing for measurement harnesses.  While enabled, every launch of the named kernel
  * ("decode", "quantize_keys", "quantize_values", "query_project", "combine", "append_project": the
- * append + query-projection launch of qjl_decode_step, "select_outliers") is bracketed by HIP
+ * append + query-projection launch of qjl_decode_step where it is a launch of its own, "select_outliers";
+ * where the decode kernel projects the queries itself, "decode" includes that work) is bracketed by HIP
  * events recorded on the launch stream.  qjl_timer_read synchronizes on the recorded events and
  * returns the number of launches timed and their total duration in milliseconds, then clears the
  * record.  Disabled by default; enabling it does not change results.
