@@ -224,6 +224,50 @@ __global__ __launch_bounds__(512, 1) void decode_stream_kernel(DecodeStreams d, 
     sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+
+// The three e4m3 pieces of 4 values, two ways: "scaled" with gfx950's scaled fp8 conversions (the power of
+// two of the scale divides before rounding and multiplies after decoding; the form the decode kernels
+// use for the softmax weights), "plain" with the unscaled conversions on 16 r1 and 256 r2.  Thread i
+// takes x[4 i ..] and writes three words to each output.
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+typedef short v2s_t __attribute__((ext_vector_type(2)));
+__device__ uint32_t probe_fp8x4(float a, float b, float c, float d) {
+    const uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)r, true);
+}
+__device__ float probe_e4m3_value(uint32_t w, int byte) {
+    const v2f_t p = byte >= 2 ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true) : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    return p[byte & 1];
+}
+__global__ void fp8_pieces_kernel(const float* x, int n4, uint32_t* scaled, uint32_t* plain) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n4) return;
+    float v[4];
+    for (int q = 0; q < 4; ++q) v[q] = x[4 * i + q];
+    // scaled form
+    uint32_t k0 = probe_fp8x4(v[0], v[1], v[2], v[3]);
+    v2f_t lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)k0, 1.0f, false);
+    v2f_t hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)k0, 1.0f, true);
+    float r0 = v[0] - lo[0], r1 = v[1] - lo[1], r2 = v[2] - hi[0], r3 = v[3] - hi[1];
+    v2s_t q = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s_t{0, 0}, r0, r1, 0.0625f, false);
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(q, r2, r3, 0.0625f, true);
+    const uint32_t k1 = (uint32_t)(uint16_t)q[0] | ((uint32_t)(uint16_t)q[1] << 16);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)k1, 0.0625f, false);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)k1, 0.0625f, true);
+    r0 -= lo[0]; r1 -= lo[1]; r2 -= hi[0]; r3 -= hi[1];
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s_t{0, 0}, r0, r1, 0.00390625f, false);
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(q, r2, r3, 0.00390625f, true);
+    const uint32_t k2 = (uint32_t)(uint16_t)q[0] | ((uint32_t)(uint16_t)q[1] << 16);
+    scaled[3 * i] = k0; scaled[3 * i + 1] = k1; scaled[3 * i + 2] = k2;
+    // plain form: unscaled conversions of 16 r1 and 256 r2
+    float s1[4], s2[4];
+    for (int e = 0; e < 4; ++e) s1[e] = v[e] - probe_e4m3_value(k0, e);
+    const uint32_t p1 = probe_fp8x4(16.f * s1[0], 16.f * s1[1], 16.f * s1[2], 16.f * s1[3]);
+    for (int e = 0; e < 4; ++e) s2[e] = s1[e] - probe_e4m3_value(p1, e) * 0.0625f;
+    const uint32_t p2 = probe_fp8x4(256.f * s2[0], 256.f * s2[1], 256.f * s2[2], 256.f * s2[3]);
+    plain[3 * i] = k0; plain[3 * i + 1] = p1; plain[3 * i + 2] = p2;
+}
+
 }  // namespace
 
 extern "C" {
@@ -293,6 +337,11 @@ int probe_decode_stream(const void* signs, const void* norms, const void* meta, 
     if (mode == 1) hipLaunchKernelGGL(decode_stream_kernel<1>, dim3(blocks), dim3(512), 0, s, d, sink);
     else if (mode == 2) hipLaunchKernelGGL(decode_stream_kernel<2>, dim3(blocks), dim3(512), 0, s, d, sink);
     else hipLaunchKernelGGL(decode_stream_kernel<0>, dim3(blocks), dim3(512), 0, s, d, sink);
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+int probe_fp8_pieces(const float* x, int n4, uint32_t* scaled, uint32_t* plain, hipStream_t s) {
+    hipLaunchKernelGGL(fp8_pieces_kernel, dim3((n4 + 255) / 256), dim3(256), 0, s, x, n4, scaled, plain);
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 

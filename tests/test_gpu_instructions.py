@@ -27,7 +27,7 @@ def lib():
     assert os.path.exists(LIB_PATH), "tests/probes/libqjl_probes.so is not built (run __graft_entry__.build())"
     lib = ctypes.CDLL(LIB_PATH)
     for name in ("probe_mfma_f6f4", "probe_cvt_fp6", "probe_lds_dma", "probe_permlane_swaps", "probe_stream_read",
-                 "probe_decode_stream", "probe_mfma_rate", "probe_f8f6f4_rate"):
+                 "probe_decode_stream", "probe_mfma_rate", "probe_f8f6f4_rate", "probe_fp8_pieces"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -148,6 +148,47 @@ def test_packed_fp6_conversions(lib):
         zero = lambda c: 0 if c == 32 else c  # noqa: E731  (either sign of zero)
         assert [zero(c) for c in codes] == [zero(c) for c in want], f"lane {l}: {codes} != {want}"
         np.testing.assert_array_equal(bk[l], np.array([E2M3[c] * scale[l] for c in codes], np.float32))
+
+
+def _e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """fp8 e4m3 (sign bit 7, exponent bits 6..3 with bias 7, mantissa bits 2..0; exponent 0 subnormal, step
+    2^-9) of float32 values with |x| <= 448, rounded to nearest, ties to even."""
+    a = np.abs(x.astype(np.float64))
+    _, ex = np.frexp(a)                          # a in [2^(ex-1), 2^ex)
+    e = np.maximum(ex - 1, -6)
+    q = np.round(a / np.exp2(e - 3.0))           # exact quotient; numpy rounds half to even
+    carry = q >= 16
+    e, q = np.where(carry, e + 1, e), np.where(carry, 8, q)
+    normal = q >= 8
+    field = np.where(normal, e + 7, 0).astype(np.uint32)
+    mant = np.where(normal, q - 8, q).astype(np.uint32)
+    return (np.signbit(x).astype(np.uint32) << 7) | (field << 3) | mant
+
+
+def test_fp8_pieces_scaled_conversions(lib):
+    """The three e4m3 pieces of the decode's softmax weights come from gfx950's scaled conversions (the
+    scale's power of two divides before rounding and multiplies after decoding).  On 4M values (uniform
+    weights in [0, 256), magnitudes from 2^-12 to 2^8 of either sign, exact e4m3 ties) they equal the
+    pieces of the unscaled conversions of v, 16 r1 and 256 r2, bit for bit, and the first piece is
+    e4m3(v) rounded to nearest even by the host model."""
+    rng = np.random.default_rng(21)
+    n = 1 << 22
+    kind = rng.integers(0, 3, n)
+    uni = rng.uniform(0.0, 256.0, n)
+    wide = np.exp2(rng.uniform(-12.0, 8.0, n)) * np.where(rng.random(n) < 0.5, -1.0, 1.0)
+    tie = (rng.integers(8, 16, n) + 0.5) * np.exp2(rng.integers(-6, 8, n) - 3.0)
+    x = np.where(kind == 0, uni, np.where(kind == 1, wide, tie)).astype(np.float32)
+    x[x == 0] = np.float32(1.0)
+    xd = torch.from_numpy(x).cuda()
+    scaled = torch.empty(3 * n // 4, dtype=torch.int32, device="cuda")
+    plain = torch.empty(3 * n // 4, dtype=torch.int32, device="cuda")
+    assert lib.probe_fp8_pieces(_p(xd), n // 4, _p(scaled), _p(plain), _stream()) == 0
+    torch.cuda.synchronize()
+    sw = scaled.cpu().numpy().view(np.uint32).reshape(-1, 3)
+    pw = plain.cpu().numpy().view(np.uint32).reshape(-1, 3)
+    first = np.stack([(sw[:, 0] >> (8 * j)) & 0xFF for j in range(4)], axis=1).ravel()
+    np.testing.assert_array_equal(first, _e4m3_bits(x))
+    np.testing.assert_array_equal(sw, pw)
 
 
 @pytest.mark.parametrize("size", [4, 16])
