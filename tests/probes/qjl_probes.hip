@@ -268,6 +268,33 @@ __global__ void fp8_pieces_kernel(const float* x, int n4, uint32_t* scaled, uint
     plain[3 * i] = k0; plain[3 * i + 1] = p1; plain[3 * i + 2] = p2;
 }
 
+
+// LDS read rate of the key quantizer's A-fragment pattern: 16 waves per workgroup, lane l reads the
+// 16 bytes at row l % 32, offset 16 (l / 32) + 32 s (s = 0..7) of 32 rows of `pitch` bytes, `iters`
+// times over; wave 0 reads the shader clock (s_memtime) around the loop between two barriers.  Each
+// workgroup writes its clocks; sink keeps the reads alive.
+__global__ __launch_bounds__(1024) void lds_rate_kernel(int iters, int pitch, uint64_t* clocks, uint32_t* sink) {
+    __shared__ __attribute__((aligned(16))) uint32_t buf[32 * 272 / 4];
+    const int tid = threadIdx.x, lane = tid & 63;
+    for (int i = tid; i < 32 * 272 / 4; i += 1024) buf[i] = (uint32_t)i * 2654435761u;
+    __syncthreads();
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(buf) + (lane & 31) * pitch + 16 * (lane >> 5);
+    uint4 acc = make_uint4(0u, 0u, 0u, 0u);
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const uint4 v = *reinterpret_cast<const uint4*>(base + 32 * s);
+            acc.x ^= v.x; acc.y += v.y; acc.z ^= v.z; acc.w += v.w;
+        }
+        asm volatile("" : "+v"(acc.x), "+v"(acc.y), "+v"(acc.z), "+v"(acc.w));
+    }
+    __syncthreads();
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    if (tid == 0) clocks[blockIdx.x] = t1 - t0;
+    if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) sink[blockIdx.x] = acc.x;
+}
+
 }  // namespace
 
 extern "C" {
@@ -342,6 +369,12 @@ int probe_decode_stream(const void* signs, const void* norms, const void* meta, 
 
 int probe_fp8_pieces(const float* x, int n4, uint32_t* scaled, uint32_t* plain, hipStream_t s) {
     hipLaunchKernelGGL(fp8_pieces_kernel, dim3((n4 + 255) / 256), dim3(256), 0, s, x, n4, scaled, plain);
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+int probe_lds_rate(int iters, int pitch, int blocks, uint64_t* clocks, uint32_t* sink, hipStream_t s) {
+    if (pitch < 256 || pitch > 272 || pitch % 16) return -1;
+    hipLaunchKernelGGL(lds_rate_kernel, dim3(blocks), dim3(1024), 0, s, iters, pitch, clocks, sink);
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 

@@ -27,7 +27,7 @@ def lib():
     assert os.path.exists(LIB_PATH), "tests/probes/libqjl_probes.so is not built (run __graft_entry__.build())"
     lib = ctypes.CDLL(LIB_PATH)
     for name in ("probe_mfma_f6f4", "probe_cvt_fp6", "probe_lds_dma", "probe_permlane_swaps", "probe_stream_read",
-                 "probe_decode_stream", "probe_mfma_rate", "probe_f8f6f4_rate", "probe_fp8_pieces"):
+                 "probe_decode_stream", "probe_mfma_rate", "probe_f8f6f4_rate", "probe_fp8_pieces", "probe_lds_rate"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -189,6 +189,25 @@ def test_fp8_pieces_scaled_conversions(lib):
     first = np.stack([(sw[:, 0] >> (8 * j)) & 0xFF for j in range(4)], axis=1).ravel()
     np.testing.assert_array_equal(first, _e4m3_bits(x))
     np.testing.assert_array_equal(sw, pw)
+
+
+def test_lds_read_rate_of_the_key_fragments(lib):
+    """64-lane 16-byte LDS reads in the key quantizer's A-fragment pattern (lane l: row l % 32, bytes
+    16 (l / 32) + 32 s of its row), 16 waves per workgroup: with the kernel's 272-byte row pitch the 32
+    rows of a read fall on distinct banks and it runs at the full LDS rate; with 256-byte rows every
+    lane of a half-wave hits the same banks.  Bytes per shader clock per CU (`pytest -s` prints them)."""
+    iters, blocks = 2000, 256
+    rate = {}
+    for pitch in (272, 256):
+        clocks = torch.zeros(blocks, dtype=torch.int64, device="cuda")
+        sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+        for _ in range(2):                       # the second launch is timed
+            assert lib.probe_lds_rate(iters, pitch, blocks, _p(clocks), _p(sink), _stream()) == 0
+        torch.cuda.synchronize()
+        rate[pitch] = 16 * iters * 8 * 1024 / float(np.median(clocks.cpu().numpy()))
+    print(f"LDS read rate, bytes per clock per CU: {rate[272]:.0f} with 272-byte rows, {rate[256]:.0f} with 256-byte rows")
+    assert rate[272] >= 4.0 * rate[256]          # measured 237 against 16
+    assert rate[272] >= 160.0
 
 
 @pytest.mark.parametrize("size", [4, 16])
